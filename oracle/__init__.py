@@ -1,0 +1,173 @@
+"""Python face of the fp64 CPU oracle (``msa_oracle.c``).
+
+TEST INFRASTRUCTURE: only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the HIP path; its only common dependency is the seeded input generator
+(``synth``), which holds none of the method's arithmetic.
+
+The C library is built with gcc (``-O2 -fopenmp``, no fast-math) on first use,
+or by ``build()``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(_HERE, "liboracle.so")
+SRC = os.path.join(_HERE, "msa_oracle.c")
+_lib = None
+
+_u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+_i64, _i32, _f64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+
+
+def build(force: bool = False) -> str:
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", SRC, "-o", tmp, "-lm"],
+                       check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(LIB)
+        lib.oracle_pool.argtypes = [_u16p, _i64, _i64p, _u16p, _i64, _i32, _i32, _f64p, _i64]
+        lib.oracle_select.argtypes = [_f64p, _i64, _i64, _i64p, _i32, _i32, _i32p]
+        lib.oracle_attend.argtypes = [_u16p, _i64, _i64p, _i32p, _i32, _i32, _u16p, _u16p, _i64, _i32, _i32,
+                                      _f64, _f64p, _f64p]
+        lib.oracle_dense_gqa.argtypes = [_u16p, _i64, _i64p, _i32, _u16p, _u16p, _i64, _i32, _f64, _f64p, _f64p]
+        lib.oracle_merge.argtypes = [_f64p, _f64p, _i64, _i32, _i32, _f64p, _f64p]
+        for f in (lib.oracle_pool, lib.oracle_select, lib.oracle_attend, lib.oracle_dense_gqa, lib.oracle_merge):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"{what}: invalid argument")
+
+
+def _u16(a):
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
+def pool(iq_rows, pos, ik, bk: int) -> np.ndarray:
+    """Pooled index scores [nrows, n_blk] (NaN after each row's local block).
+
+    iq_rows [nrows, d_idx] bf16 bits; pos [nrows]; ik [n_kv, d_idx] bf16 bits.
+    """
+    iq_rows, ik = _u16(iq_rows), _u16(ik)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    n_kv, d_idx = ik.shape
+    n_blk = -(-n_kv // bk)
+    out = np.full((len(pos), n_blk), np.nan)
+    _check(_L().oracle_pool(iq_rows, len(pos), pos, ik, n_kv, d_idx, bk, out, n_blk), "oracle_pool")
+    return out
+
+
+def select(pooled, pos, bk: int, k: int) -> np.ndarray:
+    """Selected blocks [nrows, k] int32: ascending, local included, -1 padded."""
+    pooled = np.ascontiguousarray(pooled, dtype=np.float64)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    out = np.empty((len(pos), k), np.int32)
+    _check(_L().oracle_select(pooled, pooled.shape[1], len(pos), pos, bk, k, out), "oracle_select")
+    return out
+
+
+def attend(q_rows, pos, sel, K, V, bk: int, scale: float):
+    """Main-branch attention on a given block set.
+
+    q_rows [nrows, G, d]; sel [nrows, k]; K, V [n_kv, d] -> (out [nrows, G, d], lse [nrows, G]).
+    """
+    q_rows, K, V = _u16(q_rows), _u16(K), _u16(V)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    n, G, d = q_rows.shape
+    out = np.empty((n, G, d))
+    lse = np.empty((n, G))
+    _check(_L().oracle_attend(q_rows, n, pos, sel, sel.shape[1], G, K, V, K.shape[0], d, bk, scale, out, lse),
+           "oracle_attend")
+    return out, lse
+
+
+def dense_gqa(q_rows, pos, K, V, scale: float):
+    """Dense causal GQA attention over every key j <= p."""
+    q_rows, K, V = _u16(q_rows), _u16(K), _u16(V)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    n, G, d = q_rows.shape
+    out = np.empty((n, G, d))
+    lse = np.empty((n, G))
+    _check(_L().oracle_dense_gqa(q_rows, n, pos, G, K, V, K.shape[0], d, scale, out, lse), "oracle_dense_gqa")
+    return out, lse
+
+
+def merge(o_parts, lse_parts):
+    """LSE merge of partial results: o_parts [n, P, d], lse_parts [n, P] -> (o [n, d], lse [n])."""
+    o_parts = np.ascontiguousarray(o_parts, dtype=np.float64)
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    n, P, d = o_parts.shape
+    o = np.empty((n, d))
+    lse = np.empty(n)
+    _check(_L().oracle_merge(o_parts, lse_parts, n, P, d, o, lse), "oracle_merge")
+    return o, lse
+
+
+# ---------------------------------------------------------------- workload rows
+def inputs_for_rows(w, b: int, g: int, rows, plant=None):
+    """Host inputs of one (sequence, group) for the given query rows.
+
+    Returns dict(pos, iq [n, d_idx], q [n, G, d], ik [pmax+1, d_idx]).
+    """
+    import synth
+    rows = np.asarray(rows, dtype=np.int64)
+    plant = synth.plant_spec(w) if plant is None else plant
+    pos = w.offset + rows
+    G = w.group
+    iq = synth.host_iq_rows(w, b, rows, plant)[:, g, :]
+    q = synth.host_q_rows(w, b, rows)[:, g * G:(g + 1) * G, :]
+    ik = synth.host_ik(w, b, 0, int(pos.max()) + 1, plant)
+    return {"pos": pos, "iq": np.ascontiguousarray(iq), "q": np.ascontiguousarray(q), "ik": ik}
+
+
+def kv_for_blocks(w, b: int, g: int, sel):
+    """K and V of one (sequence, group) with only the selected blocks filled.
+
+    The arrays are full-length (so token positions keep their meaning) but are
+    allocated with calloc, so untouched blocks cost no memory.
+    """
+    import synth
+    K = np.zeros((w.n_kv, w.head_dim), np.uint16)
+    V = np.zeros((w.n_kv, w.head_dim), np.uint16)
+    blocks = np.unique(np.asarray(sel)[np.asarray(sel) >= 0])
+    for t in blocks:
+        j0, j1 = int(t) * w.block_size, min((int(t) + 1) * w.block_size, w.n_kv)
+        K[j0:j1] = synth.host_kv(w, "k", b, g, j0, j1)
+        V[j0:j1] = synth.host_kv(w, "v", b, g, j0, j1)
+    return K, V
+
+
+def forward_rows(w, b: int, g: int, rows, sel_given=None, plant=None):
+    """The whole forward pass for some query rows of one (sequence, group).
+
+    Returns dict(pos, pooled, sel, out [n, G, d], lse [n, G]); when ``sel_given``
+    is passed, attention runs on that block set instead of the oracle's own.
+    """
+    x = inputs_for_rows(w, b, g, rows, plant)
+    pooled = pool(x["iq"], x["pos"], x["ik"], w.block_size)
+    sel = select(pooled, x["pos"], w.block_size, w.topk)
+    use = sel if sel_given is None else np.asarray(sel_given, dtype=np.int32)
+    K, V = kv_for_blocks(w, b, g, use)
+    out, lse = attend(x["q"], x["pos"], use, K, V, w.block_size, w.scale)
+    return {"pos": x["pos"], "pooled": pooled, "sel": sel, "out": out, "lse": lse}
