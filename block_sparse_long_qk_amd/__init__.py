@@ -1,0 +1,168 @@
+"""MiniMax Sparse Attention (MSA) forward pass on AMD MI355X (gfx950).
+
+Thin ctypes binding of ``include/msa.h`` (``libmsa.so``): argument marshalling
+only.  Every step of the computation runs in the library's HIP kernels; torch
+supplies device memory and the stream.  If the library has not been built the
+import of a compute entry point raises; nothing falls back to another path.
+
+Entry points (same names as the C ABI, without the ``msa_`` prefix):
+``index_scores``, ``block_topk``, ``sparse_attn_fwd``, ``forward``,
+``workspace_size``; ``Problem`` mirrors ``msa_problem``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
+OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN, OP_FORWARD = range(4)
+
+EXPORTS = ("msa_workspace_size", "msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
+           "msa_status_string")
+
+
+class Problem(ctypes.Structure):
+    """msa_problem: one MSA problem instance (see include/msa.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32),
+        ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("index_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("q_offset", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+    @classmethod
+    def make(cls, batch, n_q, n_kv, h_q, h_kv, head_dim=128, index_dim=128, block_size=128, topk=16,
+             q_offset=-1, softmax_scale=None):
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(head_dim)
+        return cls(batch, n_q, n_kv, h_q, h_kv, head_dim, index_dim, block_size, topk, q_offset, softmax_scale)
+
+    @property
+    def offset(self) -> int:
+        return self.n_kv - self.n_q if self.q_offset == -1 else self.q_offset
+
+    @property
+    def n_blk(self) -> int:
+        return -(-self.n_kv // self.block_size)
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m block_sparse_long_qk_amd.build`")
+        lib = ctypes.CDLL(path)
+        P = ctypes.POINTER(Problem)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lib.msa_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz)]
+        lib.msa_index_scores.argtypes = [P, vp, vp, vp, vp]
+        lib.msa_block_topk.argtypes = [P, vp, vp, vp]
+        lib.msa_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.msa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name in EXPORTS[:-1]:
+            getattr(lib, name).restype = ctypes.c_int
+        lib.msa_status_string.argtypes = [ctypes.c_int]
+        lib.msa_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().msa_status_string(status).decode()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream, like=None):
+    if stream is None:
+        import torch
+        dev = like.device if like is not None and hasattr(like, "device") else None
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(x):
+    return 0 if x is None else (x.numel() * x.element_size() if hasattr(x, "numel") else 0)
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise MsaError(rc, what)
+
+
+def workspace_size(p: Problem, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().msa_workspace_size(ctypes.byref(p), op, ctypes.byref(n)), "msa_workspace_size")
+    return n.value
+
+
+def index_scores(p: Problem, index_q, index_k, pooled, stream=None):
+    """pooled[b, g, i, t] = max over visible j in block t of index_q[b, i, g] . index_k[b, j]."""
+    _check(library().msa_index_scores(ctypes.byref(p), _ptr(index_q), _ptr(index_k), _ptr(pooled),
+                                      _stream(stream, pooled)), "msa_index_scores")
+    return pooled
+
+
+def block_topk(p: Problem, pooled, block_idx, stream=None):
+    """block_idx[b, g, i] = local block + top-(k-1) other visible blocks, ascending, -1 padded."""
+    _check(library().msa_block_topk(ctypes.byref(p), _ptr(pooled), _ptr(block_idx), _stream(stream, pooled)),
+           "msa_block_topk")
+    return block_idx
+
+
+def sparse_attn_fwd(p: Problem, q, k, v, block_idx, out, lse=None, workspace=None, workspace_bytes=None,
+                    stream=None):
+    """Softmax attention of every query head over its group's selected blocks."""
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(library().msa_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out),
+                                         _ptr(lse), _ptr(workspace), nb, _stream(stream, q)), "msa_sparse_attn_fwd")
+    return out
+
+
+def forward(p: Problem, q, k, v, index_q, index_k, out, block_idx, lse=None, workspace=None, workspace_bytes=None,
+            stream=None):
+    """The whole MSA forward pass: index scores, block top-k, sparse attention."""
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(library().msa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(index_q), _ptr(index_k), _ptr(out),
+                                 _ptr(block_idx), _ptr(lse), _ptr(workspace), nb, _stream(stream, q)), "msa_forward")
+    return out
+
+
+# ---------------------------------------------------------------- allocation helpers (torch)
+def alloc_outputs(p: Problem, device="cuda", lse: bool = True, op: int = OP_FORWARD) -> dict:
+    """Output tensors and the workspace of one call, allocated with torch."""
+    import torch
+    o = {
+        "out": torch.empty((p.batch, p.n_q, p.h_q, p.head_dim), dtype=torch.bfloat16, device=device),
+        "block_idx": torch.empty((p.batch, p.h_kv, p.n_q, p.topk), dtype=torch.int32, device=device),
+        "lse": torch.empty((p.batch, p.h_q, p.n_q), dtype=torch.float32, device=device) if lse else None,
+    }
+    if op == OP_INDEX_SCORES:
+        o = {"pooled": torch.empty((p.batch, p.h_kv, p.n_q, p.n_blk), dtype=torch.float32, device=device)}
+    nbytes = workspace_size(p, op)
+    o["workspace"] = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return o

@@ -1,0 +1,205 @@
+// The C ABI of include/msa.h: argument validation, workspace layout and
+// dispatch.  Every check runs on the host before any HIP call, so a rejected
+// call enqueues nothing.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/msa.h"
+#include "launch.h"
+
+namespace {
+
+using msa::AttnWs;
+using msa::Dims;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Validate a problem and derive the kernels' view of it.
+msa_status derive(const msa_problem* p, Dims* D) {
+  if (!p) return MSA_ERR_INVALID_ARGUMENT;
+  if (p->batch < 1 || p->n_q < 1 || p->n_kv < 1 || p->h_q < 1 || p->h_kv < 1 || p->head_dim < 1 ||
+      p->index_dim < 1 || p->block_size < 1 || p->topk < 1)
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (p->h_q % p->h_kv != 0) return MSA_ERR_INVALID_ARGUMENT;
+  if (p->q_offset < -1) return MSA_ERR_INVALID_ARGUMENT;
+  const int64_t offset = p->q_offset == -1 ? (int64_t)p->n_kv - p->n_q : p->q_offset;
+  if (offset < 0 || offset + p->n_q > p->n_kv) return MSA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->softmax_scale)) return MSA_ERR_INVALID_ARGUMENT;
+  const int64_t G = p->h_q / p->h_kv;
+  const int64_t n_blk = ((int64_t)p->n_kv + p->block_size - 1) / p->block_size;
+  // index ranges the kernels keep in 32 bits
+  const int64_t rows = (int64_t)p->batch * p->h_kv * p->n_q;
+  if (rows * p->topk > INT32_MAX || (int64_t)p->batch * p->h_kv * n_blk > INT32_MAX ||
+      (int64_t)p->n_q * p->topk > INT32_MAX || (int64_t)p->n_q * p->h_kv > INT32_MAX)
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (p->head_dim != msa::kHeadDim || (p->index_dim != 64 && p->index_dim != 128) || p->block_size != msa::kBk ||
+      p->topk > msa::kMaxTopk || G > msa::kTileRows)
+    return MSA_ERR_UNSUPPORTED;
+  int pt = 1;
+  while (pt * 2 * G <= msa::kTileRows) pt *= 2;
+  // launch-grid limits: y/z dims of 65535, 2^32 threads along x
+  const int64_t max_tiles = (rows * p->topk + pt - 1) / pt + (int64_t)p->batch * p->h_kv * n_blk;
+  if ((int64_t)p->batch * p->h_kv > 65535 || max_tiles * 256 >= (int64_t(1) << 32) ||
+      rows * 64 >= (int64_t(1) << 32))
+    return MSA_ERR_UNSUPPORTED;
+  D->B = p->batch;
+  D->n_q = p->n_q;
+  D->n_kv = p->n_kv;
+  D->h_q = p->h_q;
+  D->h_kv = p->h_kv;
+  D->G = (int32_t)G;
+  D->d = p->head_dim;
+  D->d_idx = p->index_dim;
+  D->k = p->topk;
+  D->n_blk = (int32_t)n_blk;
+  D->pt = pt;
+  D->offset = offset;
+  D->scale = p->softmax_scale;
+  D->scale_log2 = (float)((double)p->softmax_scale * 1.4426950408889634);
+  return MSA_OK;
+}
+
+// Carve the sparse-attention workspace out of `base` (nullptr: sizing only).
+size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
+  const int64_t nbgt = (int64_t)D.B * D.h_kv * D.n_blk;
+  const int64_t slots = (int64_t)D.B * D.h_kv * D.n_q * D.k;
+  const int64_t max_tiles = (slots + D.pt - 1) / D.pt + nbgt;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + at : nullptr;
+    at += round256(bytes);
+    return p;
+  };
+  // cnt and cursor are contiguous (one clear covers both)
+  char* cnt_cursor = take(sizeof(int32_t) * 2 * nbgt);
+  char* off = take(sizeof(int32_t) * (nbgt + 1));
+  char* tile_off = take(sizeof(int32_t) * (nbgt + 1));
+  char* list = take(sizeof(int32_t) * slots);
+  char* tile_desc = take(sizeof(int32_t) * 2 * max_tiles);
+  char* part_lse = take(sizeof(float) * slots * D.G);
+  char* part_o = take(sizeof(uint16_t) * slots * D.G * msa::kHeadDim);
+  if (ws) {
+    ws->cnt = reinterpret_cast<int32_t*>(cnt_cursor);
+    ws->cursor = reinterpret_cast<int32_t*>(cnt_cursor) + nbgt;
+    ws->off = reinterpret_cast<int32_t*>(off);
+    ws->tile_off = reinterpret_cast<int32_t*>(tile_off);
+    ws->list = reinterpret_cast<int32_t*>(list);
+    ws->tile_desc = reinterpret_cast<int32_t*>(tile_desc);
+    ws->part_lse = reinterpret_cast<float*>(part_lse);
+    ws->part_o = reinterpret_cast<uint16_t*>(part_o);
+    ws->max_tiles = max_tiles;
+  }
+  return at;
+}
+
+size_t pooled_bytes(const Dims& D) { return round256(sizeof(float) * (size_t)D.B * D.h_kv * D.n_q * D.n_blk); }
+
+msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
+  if (!bytes) return MSA_ERR_INVALID_ARGUMENT;
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  switch (op) {
+    case MSA_OP_INDEX_SCORES:
+    case MSA_OP_BLOCK_TOPK:
+      *bytes = 0;
+      return MSA_OK;
+    case MSA_OP_SPARSE_ATTN:
+      *bytes = attn_ws_layout(D, nullptr, nullptr);
+      return MSA_OK;
+    case MSA_OP_FORWARD:
+      *bytes = pooled_bytes(D) + attn_ws_layout(D, nullptr, nullptr);
+      return MSA_OK;
+    default:
+      return MSA_ERR_INVALID_ARGUMENT;
+  }
+}
+
+msa_status msa_index_scores(const msa_problem* p, const void* index_q, const void* index_k, float* pooled,
+                            hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!index_q || !index_k || !pooled) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(index_q) || !aligned16(index_k) || !aligned16(pooled)) return MSA_ERR_INVALID_ARGUMENT;
+  return hip_status(msa::launch_index_scores(static_cast<const uint16_t*>(index_q),
+                                             static_cast<const uint16_t*>(index_k), pooled, D, stream));
+}
+
+msa_status msa_block_topk(const msa_problem* p, const float* pooled, int32_t* block_idx, hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!pooled || !block_idx) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(pooled) || !aligned16(block_idx)) return MSA_ERR_INVALID_ARGUMENT;
+  return hip_status(msa::launch_block_topk(pooled, block_idx, D, stream));
+}
+
+msa_status msa_sparse_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !block_idx || !out || !workspace) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(out) ||
+      !aligned16(workspace) || (lse && !aligned16(lse)))
+    return MSA_ERR_INVALID_ARGUMENT;
+  AttnWs ws;
+  if (attn_ws_layout(D, static_cast<char*>(workspace), &ws) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(msa::launch_sparse_attn(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                            static_cast<const uint16_t*>(v), block_idx,
+                                            static_cast<uint16_t*>(out), lse, ws, D, stream));
+}
+
+msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const void* v, const void* index_q,
+                       const void* index_k, void* out, int32_t* block_idx, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !index_q || !index_k || !out || !block_idx || !workspace) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(index_q) || !aligned16(index_k) ||
+      !aligned16(out) || !aligned16(block_idx) || !aligned16(workspace) || (lse && !aligned16(lse)))
+    return MSA_ERR_INVALID_ARGUMENT;
+  const size_t pb = pooled_bytes(D);
+  AttnWs ws;
+  if (pb + attn_ws_layout(D, static_cast<char*>(workspace) + pb, &ws) > workspace_bytes)
+    return MSA_ERR_WORKSPACE_TOO_SMALL;
+  float* pooled = static_cast<float*>(workspace);
+  hipError_t e = msa::launch_index_scores(static_cast<const uint16_t*>(index_q),
+                                          static_cast<const uint16_t*>(index_k), pooled, D, stream);
+  if (e != hipSuccess) return MSA_ERR_HIP;
+  e = msa::launch_block_topk(pooled, block_idx, D, stream);
+  if (e != hipSuccess) return MSA_ERR_HIP;
+  e = msa::launch_sparse_attn(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                              static_cast<const uint16_t*>(v), block_idx, static_cast<uint16_t*>(out), lse, ws, D,
+                              stream);
+  return hip_status(e);
+}
+
+const char* msa_status_string(msa_status s) {
+  switch (s) {
+    case MSA_OK:
+      return "ok";
+    case MSA_ERR_INVALID_ARGUMENT:
+      return "invalid argument";
+    case MSA_ERR_UNSUPPORTED:
+      return "unsupported configuration";
+    case MSA_ERR_WORKSPACE_TOO_SMALL:
+      return "workspace too small";
+    case MSA_ERR_HIP:
+      return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Shared device helpers and launch descriptors of the MSA kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kBk = 128;        // block size the kernels are built for
+constexpr int kHeadDim = 128;   // main-branch head dim
+constexpr int kMaxTopk = 64;    // one selection per wavefront lane at most
+constexpr int kTileRows = 128;  // query rows (positions x heads) per attention tile
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Problem dimensions as the kernels see them (all derived on the host).
+struct Dims {
+  int32_t B, n_q, n_kv, h_q, h_kv, G, d, d_idx, k, n_blk;
+  int32_t pt;          // query positions per attention tile (power of two, pt * G <= 128)
+  int64_t offset;      // position of query row 0
+  float scale;         // softmax scale
+  float scale_log2;    // softmax scale * log2(e)
+};
+
+// Workspace carve-up of the sparse attention stage (device pointers).
+struct AttnWs {
+  int32_t* cnt;        // [B*h_kv*n_blk]   gathered query rows per (b, g, block)
+  int32_t* cursor;     // [B*h_kv*n_blk]   fill cursors
+  int32_t* off;        // [B*h_kv*n_blk+1] exclusive scan of cnt
+  int32_t* tile_off;   // [B*h_kv*n_blk+1] exclusive scan of ceil(cnt / pt); last = tile count
+  int32_t* list;       // [edges]          row-slot ids (i * k + s), grouped by (b, g, block)
+  int32_t* tile_desc;  // [max_tiles][2]   (b*h_kv*n_blk + block, first list entry)
+  float* part_lse;     // [B*h_kv*n_q*k][G]     base-2 log-sum-exp of each partial
+  uint16_t* part_o;    // [B*h_kv*n_q*k][G][d]  normalised partial outputs, bf16
+  int64_t max_tiles;
+};
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Operands are 8 packed bf16 per lane.
+__device__ __forceinline__ f32x16 mfma_32x32x16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// A 32x32 MFMA accumulator register e of lane l holds row 8*(e/4) + 4*(l/32) + e%4,
+// column l%32.
+__device__ __forceinline__ int acc_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
+}  // namespace msa

@@ -1,0 +1,170 @@
+// Index Branch, part 1: index scores against the shared index-key head with
+// the block max-pool fused into the MFMA epilogue.
+//
+// Page "MiniMax 发布 MSA 稀疏注意力方法，开源推理内核并推出 MiniMax-M3 模型", section
+// 两个分支如何工作: one index-query head per GQA group, one shared index-key head;
+// the visible key tokens are scored and the scores max-pooled to blocks.
+//
+// All groups share the index keys, so the (query, group) rows of one sequence
+// form a single GEMM [n_q*h_kv, d_idx] x [d_idx, n_kv].  A workgroup owns 256
+// consecutive rows (4 waves x 64) and streams 128-key blocks of index_k through
+// double-buffered LDS.  Each wave computes S^T = K * Q^T with the gfx950
+// 32x32x16 bf16 MFMA, so that a lane's accumulators hold 16 keys of a single
+// query column: the max-pool is in-lane plus one exchange between the two
+// half-waves, and each lane ends every block with exactly one pooled value
+// (its own row).  Products of bf16 values are exact in fp32; accumulation is
+// fp32.  Causal masking (key j > p -> -inf) is applied only on blocks that
+// reach past the wave's first position.
+#include "launch.h"
+
+namespace msa {
+namespace {
+
+template <int DIDX>
+struct IdxCfg {
+  static constexpr int KS = DIDX / 16;              // MFMA k-steps per key row
+  static constexpr int PITCH = DIDX + 8;            // LDS row pitch (bf16), 16-byte pad
+  static constexpr int CHUNKS = kBk * DIDX / 8;     // 16-byte chunks per key block
+  static constexpr int PER_THREAD = CHUNKS / 256;
+  static constexpr int CPR = DIDX / 8;              // chunks per key row
+};
+
+template <int DIDX>
+__global__ __launch_bounds__(256) void k_index_scores(const uint16_t* __restrict__ iq,
+                                                      const uint16_t* __restrict__ ik, float* __restrict__ pooled,
+                                                      Dims D, int32_t blocks_per_split) {
+  using C = IdxCfg<DIDX>;
+  __shared__ __align__(16) uint16_t lds[2][kBk * C::PITCH];
+  const float NEG_INF = -__builtin_huge_valf();
+
+  const int b = blockIdx.z;
+  const int rows_total = D.n_q * D.h_kv;
+  const int tile = gridDim.x - 1 - blockIdx.x;     // heaviest (latest) rows first
+  const int row0 = tile * 256;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int half = lane >> 5, col = lane & 31;
+
+  const int last_row = min(row0 + 255, rows_total - 1);
+  const int t_last = (int)((D.offset + last_row / D.h_kv) / kBk);
+  const int t_begin = blockIdx.y * blocks_per_split;
+  const int t_end = min(t_begin + blocks_per_split, t_last + 1);
+  if (t_begin >= t_end) return;  // uniform over the workgroup
+
+  const int wrow0 = row0 + wave * 64;
+  const bool wave_active = wrow0 < rows_total;
+  const int64_t p_wave_min = D.offset + (int64_t)(wave_active ? wrow0 : 0) / D.h_kv;
+
+  // B operand: this lane's query columns (n-tile 0: row wrow0+col, n-tile 1: +32),
+  // 8 bf16 of the index dim per k-step.
+  int64_t pc[2];
+  uint4 qb[2][C::KS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = wrow0 + 32 * nt + col;
+    if (r < rows_total) {
+      pc[nt] = D.offset + r / D.h_kv;
+      const uint16_t* src = iq + ((int64_t)b * rows_total + r) * DIDX + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) qb[nt][ks] = *reinterpret_cast<const uint4*>(src + 16 * ks);
+    } else {
+      pc[nt] = -1;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) qb[nt][ks] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // The row this lane writes: lane < 32 -> n-tile 0 column `lane`, else n-tile 1.
+  const int r_out = wrow0 + lane;
+  int64_t out_base = -1;
+  int l_out = -1;
+  if (r_out < rows_total) {
+    const int i = r_out / D.h_kv, g = r_out % D.h_kv;
+    out_base = (((int64_t)b * D.h_kv + g) * D.n_q + i) * D.n_blk;
+    l_out = (int)((D.offset + i) / kBk);
+  }
+
+  const uint16_t* ikb = ik + (int64_t)b * D.n_kv * DIDX;
+  uint4 stage[C::PER_THREAD];
+  auto load_block = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < C::PER_THREAD; ++u) {
+      const int c = threadIdx.x + 256 * u;
+      const int64_t j = (int64_t)t * kBk + c / C::CPR;
+      stage[u] = (j < D.n_kv) ? *reinterpret_cast<const uint4*>(ikb + j * DIDX + (c % C::CPR) * 8)
+                              : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < C::PER_THREAD; ++u) {
+      const int c = threadIdx.x + 256 * u;
+      *reinterpret_cast<uint4*>(&lds[buf][(c / C::CPR) * C::PITCH + (c % C::CPR) * 8]) = stage[u];
+    }
+  };
+
+  load_block(t_begin);
+  store_block(0);
+  __syncthreads();
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    if (t + 1 < t_end) load_block(t + 1);
+    if (wave_active) {
+      const bool need_mask = (int64_t)t * kBk + kBk - 1 > p_wave_min;
+      float run0 = NEG_INF, run1 = NEG_INF;
+#pragma unroll 1
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x16 a0 = {}, a1 = {};
+        const uint16_t* arow = &lds[buf][(32 * mt + col) * C::PITCH + 8 * half];
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const uint4 a = *reinterpret_cast<const uint4*>(arow + 16 * ks);
+          a0 = mfma_32x32x16(a, qb[0][ks], a0);
+          a1 = mfma_32x32x16(a, qb[1][ks], a1);
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t key = (int64_t)t * kBk + 32 * mt + acc_row(e, lane);
+            if (key > pc[0]) a0[e] = NEG_INF;
+            if (key > pc[1]) a1[e] = NEG_INF;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          run0 = fmaxf(run0, a0[e]);
+          run1 = fmaxf(run1, a1[e]);
+        }
+      }
+      run0 = fmaxf(run0, wave_xor32(run0));
+      run1 = fmaxf(run1, wave_xor32(run1));
+      const float v = half ? run1 : run0;
+      if (out_base >= 0 && t <= l_out) pooled[out_base + t] = v;
+    }
+    if (t + 1 < t_end) store_block(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_index_scores(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
+                               hipStream_t stream) {
+  const int64_t rows_total = (int64_t)D.n_q * D.h_kv;
+  const int row_tiles = (int)((rows_total + 255) / 256);
+  const int t_max = (int)((D.offset + D.n_q - 1) / kBk) + 1;  // blocks the last row needs
+  // Split the key range when there are too few row tiles to fill the chip.
+  const int64_t want = 2048;
+  int64_t nsplit = (want + (int64_t)row_tiles * D.B - 1) / ((int64_t)row_tiles * D.B);
+  if (nsplit < 1) nsplit = 1;
+  if (nsplit > t_max) nsplit = t_max;
+  const int per = (int)((t_max + nsplit - 1) / nsplit);
+  nsplit = (t_max + per - 1) / per;
+  dim3 grid(row_tiles, (unsigned)nsplit, D.B);
+  if (D.d_idx == 128)
+    hipLaunchKernelGGL(k_index_scores<128>, grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+  else
+    hipLaunchKernelGGL(k_index_scores<64>, grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,21 @@
+// Kernel launchers of the MSA forward pass (host side, internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace msa {
+
+// Index scores + block max-pool: pooled[B][h_kv][n_q][n_blk] (fp32).
+hipError_t launch_index_scores(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
+                               hipStream_t stream);
+
+// Exp-free block top-k with the forced local block: block_idx[B][h_kv][n_q][k].
+hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims& D, hipStream_t stream);
+
+// Gather plan + gathered non-local tiles + local tiles with the merge.
+hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
+                              uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,149 @@
+/*
+ * msa.h -- C ABI of the MiniMax Sparse Attention (MSA) forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (page "MiniMax 发布 MSA 稀疏注意力方法，开源推理内核并推出 MiniMax-M3
+ * 模型", sections 什么是 MSA and 两个分支如何工作): an Index Branch scores every
+ * causally visible key with one index-query head per GQA group against one
+ * shared index-key head, max-pools the scores to blocks of Bk tokens and keeps
+ * the top-k blocks per query and group, the query's own (local) block always
+ * taking one slot; a Main Branch then runs exact scaled dot-product softmax
+ * attention, per query head, over the causally visible tokens of its group's
+ * selected blocks.  The same page's "运行 Kernel" section shows the three calls
+ * of the released library (a max-score proxy pass, sparse_topk_select, a
+ * sparse attention pass); the entry points below follow that split.
+ *
+ * Notation: B batch, n_q query rows per call, n_kv key/value tokens,
+ * H_q query heads, H_kv key/value heads (= GQA groups), G = H_q / H_kv,
+ * d head dim, d_idx index dim, Bk block size, k blocks kept,
+ * n_blk = ceil(n_kv / Bk).  Query row i sits at position p_i = q_offset + i,
+ * its local block is l_i = floor(p_i / Bk), key j is visible to it iff
+ * j <= p_i.  Query head h belongs to group g = floor(h / G).
+ *
+ * Tensor layouts (all dense, row-major, contiguous):
+ *   q, out     [B][n_q][H_q][d]        bf16
+ *   k, v       [B][H_kv][n_kv][d]      bf16  (each 128-token block of one head
+ *                                             is one contiguous 32 KiB run)
+ *   index_q    [B][n_q][H_kv][d_idx]   bf16  (one index-query head per group)
+ *   index_k    [B][n_kv][d_idx]        bf16  (one shared index-key head)
+ *   pooled     [B][H_kv][n_q][n_blk]   fp32
+ *   block_idx  [B][H_kv][n_q][k]       int32
+ *   lse        [B][H_q][n_q]           fp32, natural log (optional output)
+ *
+ * Ownership and execution: the caller owns every buffer (device memory) and
+ * the workspace.  The library allocates no device memory, keeps no state
+ * between calls and may be called concurrently on different streams with
+ * different workspaces.  Each call validates its arguments on the host, then
+ * only enqueues kernels on `stream` and returns; results are valid once the
+ * stream has been synchronised.
+ *
+ * Errors: argument checks run before any HIP call.  On failure nothing is
+ * enqueued and the call returns MSA_ERR_INVALID_ARGUMENT (bad shapes, null or
+ * misaligned pointers, q_offset + n_q > n_kv, k < 1, H_q % H_kv != 0, index
+ * overflow) or MSA_ERR_UNSUPPORTED (shapes the kernels are not built for:
+ * d != 128, d_idx not in {64, 128}, Bk != 128, k > 64, G > 128).  A failed
+ * kernel launch returns MSA_ERR_HIP.  No C++ exception crosses the ABI.
+ * All device pointers must be 16-byte aligned; NaN inputs are not supported.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARGUMENT = 1,
+  MSA_ERR_UNSUPPORTED = 2,
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MSA_ERR_HIP = 4
+} msa_status;
+
+/* One problem instance.  q_offset = -1 means bottom-right alignment,
+ * q_offset = n_kv - n_q (prefill: n_q = n_kv gives 0; decode: n_q = 1 puts the
+ * query on the last cached token, whose block is its local block). */
+typedef struct {
+  int32_t batch, n_q, n_kv;
+  int32_t h_q, h_kv;
+  int32_t head_dim, index_dim;
+  int32_t block_size, topk;
+  int64_t q_offset;
+  float softmax_scale; /* 1/sqrt(d) in the standard configuration */
+} msa_problem;
+
+/* Which call a workspace is sized for. */
+typedef enum {
+  MSA_OP_INDEX_SCORES = 0,
+  MSA_OP_BLOCK_TOPK = 1,
+  MSA_OP_SPARSE_ATTN = 2,
+  MSA_OP_FORWARD = 3
+} msa_op;
+
+/* Bytes of device workspace the call `op` needs for problem `p` (0 for the
+ * calls that take none).  Host only; enqueues nothing. */
+msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes);
+
+/*
+ * Index Branch, scoring and block max-pool (section 两个分支如何工作: score the
+ * visible keys with the group's index-query head against the shared index-key
+ * head, then max-pool to blocks; reading R1: the score is the raw dot product).
+ *   pooled[b][g][i][t] = max_{j in block t, j <= p_i} sum_c index_q[b][i][g][c] * index_k[b][j][c]
+ * for t = 0 .. l_i, computed with fp32 accumulation of exact bf16 products.
+ * Entries with t > l_i are not written (their contents are unspecified).
+ */
+msa_status msa_index_scores(const msa_problem* p, const void* index_q, const void* index_k, float* pooled,
+                            hipStream_t stream);
+
+/*
+ * Index Branch, exp-free block top-k (section 两个分支如何工作: top-k per query
+ * and group with the local block always included; section 内核协同设计: softmax
+ * keeps the order, so the raw pooled scores are ranked directly).
+ *   block_idx[b][g][i][:] = { l_i } U top_(k-1) of { 0 .. l_i - 1 } by
+ *   (pooled desc, block index asc), written in ascending order; when
+ *   l_i + 1 <= k every visible block is kept and the tail is -1.
+ * Equal scores (including -0 vs +0) go to the lower block index; the result is
+ * a deterministic function of the fp32 input.
+ */
+msa_status msa_block_topk(const msa_problem* p, const float* pooled, int32_t* block_idx, hipStream_t stream);
+
+/*
+ * Main Branch on a given block set (section 两个分支如何工作: gather the causally
+ * visible tokens of the selected blocks and run scaled dot-product softmax per
+ * query head, the group's block set shared by its heads; section 内核协同设计:
+ * KV-outer iteration with gathered queries and a separate merge stage).
+ *   out[b][i][h] = sum_{j in T} softmax_j(scale * q[b][i][h] . k[b][g][j]) v[b][g][j],
+ *   T = { j <= p_i : floor(j / Bk) in S }, S = the valid entries of
+ *   block_idx[b][g][i] together with l_i.
+ * Each block_idx row must be ascending with entries in [0, l_i] followed by -1
+ * padding (as msa_block_topk writes it); the local block l_i is always
+ * attended, listed or not.  out is bf16 (rounded to nearest even from fp32);
+ * lse (nullable) gets ln sum_{j in T} exp(scale * q . k_j).
+ * Needs workspace of msa_workspace_size(p, MSA_OP_SPARSE_ATTN).
+ */
+msa_status msa_sparse_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The whole forward pass: index scores, block top-k, sparse attention.
+ * Writes out, block_idx and (when non-null) lse exactly as the three calls
+ * above would.  Needs workspace of msa_workspace_size(p, MSA_OP_FORWARD).
+ */
+msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const void* v, const void* index_q,
+                       const void* index_k, void* out, int32_t* block_idx, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* msa_status_string(msa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -137,8 +137,22 @@ def inputs_for_rows(w, b: int, g: int, rows, plant=None):
     G = w.group
     iq = synth.host_iq_rows(w, b, rows, plant)[:, g, :]
     q = synth.host_q_rows(w, b, rows)[:, g * G:(g + 1) * G, :]
-    ik = synth.host_ik(w, b, 0, int(pos.max()) + 1, plant)
+    ik = _index_keys(w, b, plant)[:int(pos.max()) + 1]
     return {"pos": pos, "iq": np.ascontiguousarray(iq), "q": np.ascontiguousarray(q), "ik": ik}
+
+
+_ik_cache = {}
+
+
+def _index_keys(w, b: int, plant):
+    """index_k of one sequence (all n_kv tokens); the last one is kept, since
+    every group and row of a sequence reads the same keys."""
+    import synth
+    key = (w, b)
+    if key not in _ik_cache:
+        _ik_cache.clear()
+        _ik_cache[key] = synth.host_ik(w, b, 0, w.n_kv, plant)
+    return _ik_cache[key]
 
 
 def kv_for_blocks(w, b: int, g: int, sel):

@@ -1,0 +1,112 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/msa.h declares, sizes workspaces, and rejects bad arguments on the
+host before any HIP call (so these calls never reach the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_long_qk_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = msa.library()
+    names = declared_functions()
+    assert set(names) == set(msa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert msa.status_string(msa.OK) == "ok"
+    assert "workspace" in msa.status_string(msa.ERR_WORKSPACE_TOO_SMALL)
+    assert msa.status_string(99) == "unknown status"
+
+
+def prob(**kw):
+    base = dict(batch=1, n_q=4096, n_kv=4096, h_q=4, h_kv=1, head_dim=128, index_dim=64, block_size=128, topk=16)
+    base.update(kw)
+    return msa.Problem.make(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h_q=6, h_kv=4), msa.ERR_INVALID_ARGUMENT),          # H_q % H_kv != 0
+    (dict(n_q=10, n_kv=8), msa.ERR_INVALID_ARGUMENT),         # q_offset + n_q > n_kv
+    (dict(q_offset=5, n_q=4092), msa.ERR_INVALID_ARGUMENT),
+    (dict(q_offset=-2), msa.ERR_INVALID_ARGUMENT),
+    (dict(topk=0), msa.ERR_INVALID_ARGUMENT),
+    (dict(batch=0), msa.ERR_INVALID_ARGUMENT),
+    (dict(softmax_scale=float("inf")), msa.ERR_INVALID_ARGUMENT),
+    (dict(head_dim=64), msa.ERR_UNSUPPORTED),
+    (dict(index_dim=96), msa.ERR_UNSUPPORTED),
+    (dict(block_size=64), msa.ERR_UNSUPPORTED),
+    (dict(topk=65), msa.ERR_UNSUPPORTED),
+    (dict(h_q=256, h_kv=1), msa.ERR_UNSUPPORTED),             # G > 128
+    (dict(batch=64, n_q=262144, n_kv=262144, h_kv=8, h_q=64, topk=64), msa.ERR_INVALID_ARGUMENT),  # int32 overflow
+])
+def test_invalid_problems_rejected(kw, status):
+    p = prob(**kw)
+    n = ctypes.c_size_t(0)
+    assert msa.library().msa_workspace_size(ctypes.byref(p), msa.OP_FORWARD, ctypes.byref(n)) == status
+    # the compute entry points reject it before touching the device
+    fake = 1 << 20
+    assert msa.library().msa_index_scores(ctypes.byref(p), fake, fake, fake, None) == status
+    assert msa.library().msa_block_topk(ctypes.byref(p), fake, fake, None) == status
+
+
+def test_null_and_misaligned_pointers_rejected():
+    p = prob()
+    lib = msa.library()
+    ok = 1 << 20
+    assert lib.msa_index_scores(ctypes.byref(p), None, ok, ok, None) == msa.ERR_INVALID_ARGUMENT
+    assert lib.msa_index_scores(ctypes.byref(p), ok + 2, ok, ok, None) == msa.ERR_INVALID_ARGUMENT
+    assert lib.msa_block_topk(ctypes.byref(p), ok, ok + 4, None) == msa.ERR_INVALID_ARGUMENT
+    assert lib.msa_sparse_attn_fwd(ctypes.byref(p), ok, ok, ok, ok, ok, None, None, 1 << 30,
+                                   None) == msa.ERR_INVALID_ARGUMENT
+    assert lib.msa_sparse_attn_fwd(ctypes.byref(p), ok, ok, ok, ok, ok, ok + 8, ok, 1 << 30,
+                                   None) == msa.ERR_INVALID_ARGUMENT
+    assert lib.msa_forward(None, ok, ok, ok, ok, ok, ok, ok, None, ok, 1 << 30, None) == msa.ERR_INVALID_ARGUMENT
+    n = ctypes.c_size_t(0)
+    assert lib.msa_workspace_size(ctypes.byref(p), 7, ctypes.byref(n)) == msa.ERR_INVALID_ARGUMENT
+    assert lib.msa_workspace_size(ctypes.byref(p), 0, None) == msa.ERR_INVALID_ARGUMENT
+
+
+def test_workspace_too_small_rejected():
+    p = prob()
+    need = msa.workspace_size(p, msa.OP_FORWARD)
+    ok = 1 << 20
+    lib = msa.library()
+    assert lib.msa_forward(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, None, ok, need - 1,
+                           None) == msa.ERR_WORKSPACE_TOO_SMALL
+    need_a = msa.workspace_size(p, msa.OP_SPARSE_ATTN)
+    assert lib.msa_sparse_attn_fwd(ctypes.byref(p), ok, ok, ok, ok, ok, None, ok, need_a - 1,
+                                   None) == msa.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_sizes():
+    p = prob()
+    assert msa.workspace_size(p, msa.OP_INDEX_SCORES) == 0
+    assert msa.workspace_size(p, msa.OP_BLOCK_TOPK) == 0
+    a = msa.workspace_size(p, msa.OP_SPARSE_ATTN)
+    f = msa.workspace_size(p, msa.OP_FORWARD)
+    pooled = 4 * p.batch * p.h_kv * p.n_q * p.n_blk
+    assert f >= a + pooled
+    # partial outputs dominate: one bf16 [G, d] slab per (row, slot)
+    assert a >= 2 * p.batch * p.h_kv * p.n_q * p.topk * (p.h_q // p.h_kv) * 128
+    big = msa.Problem.make(1, 131072, 131072, 64, 8)
+    assert msa.workspace_size(big, msa.OP_FORWARD) < 64 << 30   # fits one MI355X comfortably
+
+
+def test_decode_and_chunked_offsets_accepted():
+    assert msa.workspace_size(msa.Problem.make(64, 1, 262144, 64, 8), msa.OP_FORWARD) > 0
+    assert msa.workspace_size(msa.Problem.make(1, 8192, 1048576, 64, 8, q_offset=1040384), msa.OP_FORWARD) > 0

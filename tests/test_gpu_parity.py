@@ -1,0 +1,141 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, for the five workloads and the edge cases."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import (Stats, check_forward_matches_stages, check_rows, problem, run_gpu, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _release():
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+EDGE = [
+    # ragged tail (n_kv % 128 != 0), batch 2, two groups of 4, index dim 64
+    synth.Workload("edge_ragged", 2, 1000, 1000, 8, 2, index_dim=64, topk=4, seed=2001),
+    # chunk of queries at an explicit offset into a ragged cache
+    synth.Workload("edge_chunk", 1, 300, 1000, 8, 2, topk=4, q_offset=700, seed=2002),
+    # only the local block (k = 1)
+    synth.Workload("edge_k1", 1, 700, 700, 4, 1, topk=1, seed=2003),
+    # the widest selection the kernels take (k = 64)
+    synth.Workload("edge_k64", 1, 8269, 8269, 8, 1, topk=64, seed=2004),
+    # one head per group (MHA-shaped), and wide groups
+    synth.Workload("edge_g1", 1, 1536, 1536, 4, 4, topk=3, seed=2005),
+    synth.Workload("edge_g16", 1, 2048, 2048, 32, 2, topk=5, seed=2006),
+    synth.Workload("edge_g128", 1, 512, 512, 128, 1, topk=2, seed=2007),
+    # decode against a ragged cache, and the one-token cache
+    synth.Workload("edge_decode", 3, 1, 5000, 16, 2, topk=8, seed=2008),
+    synth.Workload("edge_one_token", 2, 1, 1, 8, 1, seed=2009),
+    # a group size that does not divide 128 (96-row tiles)
+    synth.Workload("edge_g3", 1, 1200, 1200, 6, 2, topk=6, seed=2010),
+    # planted blocks in a small prefill
+    synth.Workload("edge_planted", 1, 4096, 4096, 16, 2, topk=6, seed=2011, plant_m=3,
+                   plant_alpha=2 * 128 ** 0.25, plant_beta=2 * 128 ** 0.25),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=[w.name for w in EDGE])
+def test_edge_cases(w):
+    res = run_gpu(w)
+    check_forward_matches_stages(res)
+    st = Stats()
+    rows = np.arange(w.n_q) if w.n_q <= 2048 else sample_rows(w, 256, seed=w.seed, whole_blocks=3)
+    for b in range(w.batch):
+        for g in range(w.h_kv):
+            check_rows(w, res, b, g, rows, st)
+    st.check()
+    del res
+    _release()
+
+
+def test_prefill_4k_all_rows():
+    w = synth.WORKLOADS["prefill_4k"]
+    res = run_gpu(w)
+    check_forward_matches_stages(res)
+    st = Stats()
+    check_rows(w, res, 0, 0, np.arange(w.n_q), st)
+    st.check()
+    # the planted blocks are picked by the queries aligned with the planted direction
+    p = synth.plant_spec(w)
+    sel = res["block_idx"][0, 0].cpu().numpy()
+    hits = np.mean([np.isin(p.blocks[0], s).sum() for s in sel[2048:]])
+    say(f"    planted blocks selected per late query: {hits:.2f} of 3")
+    assert hits > 1.0
+    del res
+    _release()
+
+
+def test_prefill_32k_sampled_rows():
+    w = synth.WORKLOADS["prefill_32k"]
+    res = run_gpu(w)
+    check_forward_matches_stages(res)
+    st = Stats()
+    plant = synth.plant_spec(w)
+    rows = sample_rows(w, 48, seed=32, whole_blocks=2)
+    for g in range(w.h_kv):
+        check_rows(w, res, 0, g, rows, st, plant)
+    st.check()
+    # every group keeps its planted blocks for late queries
+    sel = res["block_idx"][0, :, -1].cpu().numpy()
+    for g in range(w.h_kv):
+        assert np.isin(plant.blocks[g], sel[g]).all()
+    del res
+    _release()
+
+
+def test_prefill_128k_sampled_rows():
+    w = synth.WORKLOADS["prefill_128k"]
+    res = run_gpu(w, with_forward=False)
+    st = Stats()
+    rows = sample_rows(w, 24, seed=128, whole_blocks=0)
+    for g in range(w.h_kv):
+        check_rows(w, res, 0, g, rows, st)
+    st.check()
+    del res
+    _release()
+
+
+def test_decode_256k_sampled_sequences():
+    w = synth.WORKLOADS["decode_256k"]
+    res = run_gpu(w, with_forward=True)
+    check_forward_matches_stages(res)
+    st = Stats()
+    for b in (0, 37, 63):
+        for g in range(w.h_kv):
+            check_rows(w, res, b, g, [0], st)
+    st.check()
+    del res
+    _release()
+
+
+def test_chunked_1m_sampled_rows():
+    w = synth.WORKLOADS["chunked_1m"]
+    res = run_gpu(w, with_forward=True)
+    check_forward_matches_stages(res)
+    st = Stats()
+    plant = synth.plant_spec(w)
+    rows = sample_rows(w, 6, seed=1024, whole_blocks=0)
+    for g in range(w.h_kv):
+        check_rows(w, res, 0, g, rows, st, plant)
+    st.check()
+    sel = res["block_idx"][0, :, -1].cpu().numpy()
+    for g in range(w.h_kv):
+        assert np.isin(plant.blocks[g], sel[g]).all()
+    del res
+    _release()
+
+
+def test_forward_is_deterministic():
+    import torch
+    w = synth.Workload("det", 1, 4096, 4096, 16, 2, topk=8, seed=2100)
+    a = run_gpu(w)
+    b = run_gpu(w, inputs=a["inputs"])
+    assert torch.equal(a["fwd"]["block_idx"], b["fwd"]["block_idx"])
+    assert torch.equal(a["fwd"]["out"].view(torch.int16), b["fwd"]["out"].view(torch.int16))
+    assert torch.equal(a["fwd"]["lse"], b["fwd"]["lse"])
+    _release()

@@ -1,0 +1,86 @@
+"""msa_block_topk alone on crafted fp32 score tensors: every row must equal the
+oracle's selection on the same values, bit for bit (ties, signed zeros, rows
+that defeat the kernel's fast threshold, rows of every visible length)."""
+import numpy as np
+import pytest
+
+import block_sparse_long_qk_amd as msa
+import oracle
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_topk(pooled_np, n_q, n_kv, h_kv, k, q_offset=-1):
+    import torch
+    p = msa.Problem.make(1, n_q, n_kv, 8 * h_kv, h_kv, topk=k, q_offset=q_offset)
+    pooled = torch.from_numpy(pooled_np.astype(np.float32)).cuda()
+    bidx = torch.full((1, h_kv, n_q, k), -7, dtype=torch.int32, device="cuda")
+    msa.block_topk(p, pooled, bidx)
+    torch.cuda.synchronize()
+    return bidx.cpu().numpy()
+
+
+def check(pooled_np, n_q, n_kv, h_kv, k, q_offset=-1, name=""):
+    say(f"[gpu] top-k {name}: n_q={n_q} n_kv={n_kv} h_kv={h_kv} k={k}")
+    got = run_topk(pooled_np, n_q, n_kv, h_kv, k, q_offset)
+    off = n_kv - n_q if q_offset == -1 else q_offset
+    pos = off + np.arange(n_q)
+    n_blk = pooled_np.shape[-1]
+    vis = np.arange(n_blk)[None, :] <= (pos // 128)[:, None]
+    for g in range(h_kv):
+        ref = oracle.select(np.where(vis, pooled_np[0, g].astype(np.float64), np.nan), pos, 128, k)
+        bad = np.nonzero(np.any(ref != got[0, g], axis=1))[0]
+        assert bad.size == 0, f"group {g} rows {bad[:5]}: got {got[0, g, bad[0]]} want {ref[bad[0]]}"
+
+
+N = 128 * 300
+
+
+@pytest.mark.parametrize("k", [1, 2, 16, 64])
+def test_random_scores(k):
+    rng = np.random.default_rng(3000 + k)
+    pooled = rng.standard_normal((1, 2, N, N // 128)).astype(np.float32) * 30
+    check(pooled, N, N, 2, k, name="random")
+
+
+def test_heavy_ties():
+    rng = np.random.default_rng(3100)
+    pooled = rng.integers(-2, 3, size=(1, 2, N, N // 128)).astype(np.float32)
+    check(pooled, N, N, 2, 16, name="ties")
+
+
+def test_signed_zeros():
+    rng = np.random.default_rng(3200)
+    pooled = np.where(rng.random((1, 1, N, N // 128)) < 0.5, np.float32(-0.0), np.float32(0.0))
+    pooled[..., ::7] = -1.0
+    check(pooled.astype(np.float32), N, N, 1, 16, name="signed zeros")
+
+
+def test_all_equal():
+    pooled = np.full((1, 1, N, N // 128), 3.25, np.float32)
+    check(pooled, N, N, 1, 16, name="all equal")
+
+
+def test_periodic_rows_take_the_exact_path():
+    """Scores that depend only on the lane a block falls in: hundreds of
+    blocks pass the lane-maxima threshold, so the exact search runs."""
+    t = np.arange(N // 128)
+    row = -(t % 64).astype(np.float32)
+    pooled = np.broadcast_to(row, (1, 1, N, N // 128)).copy()
+    check(pooled, N, N, 1, 16, name="periodic")
+
+
+def test_long_rows_8192_blocks():
+    rng = np.random.default_rng(3300)
+    n_kv, n_q = 1 << 20, 256
+    pooled = rng.standard_normal((1, 2, n_q, n_kv // 128)).astype(np.float32)
+    pooled[0, 1, :, :] = np.round(pooled[0, 1] * 2)        # ties in the second group
+    check(pooled, n_q, n_kv, 2, 16, name="8192 blocks")
+
+
+def test_chunk_with_offset():
+    rng = np.random.default_rng(3400)
+    n_kv, n_q, off = 50000, 777, 30001
+    pooled = rng.standard_normal((1, 1, n_q, -(-n_kv // 128))).astype(np.float32)
+    check(pooled, n_q, n_kv, 1, 16, q_offset=off, name="chunk")
