@@ -42,7 +42,7 @@ msa_status derive(const msa_problem* p, Dims* D) {
   // launch-grid limits: y/z dims of 65535, 2^32 threads along x
   const int64_t max_tiles = (rows * p->topk + pt - 1) / pt + (int64_t)p->batch * p->h_kv * n_blk;
   if ((int64_t)p->batch * p->h_kv > 65535 || max_tiles * 256 >= (int64_t(1) << 32) ||
-      rows * 64 >= (int64_t(1) << 32))
+      rows * 64 >= (int64_t(1) << 32) || rows > 65535LL * 65535LL)
     return MSA_ERR_UNSUPPORTED;
   D->B = p->batch;
   D->n_q = p->n_q;
@@ -72,8 +72,9 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
     at += round256(bytes);
     return p;
   };
-  // cnt and cursor are contiguous (one clear covers both)
-  char* cnt_cursor = take(sizeof(int32_t) * 2 * nbgt);
+  char* hist = take(sizeof(int32_t) * nbgt * msa::plan_chunks(D));
+  char* cnt = take(sizeof(int32_t) * nbgt);
+  char* bsum = take(sizeof(int32_t) * 2 * msa::plan_scan_blocks(D));
   char* off = take(sizeof(int32_t) * (nbgt + 1));
   char* tile_off = take(sizeof(int32_t) * (nbgt + 1));
   char* list = take(sizeof(int32_t) * slots);
@@ -81,8 +82,9 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
   char* part_lse = take(sizeof(float) * slots * D.G);
   char* part_o = take(sizeof(uint16_t) * slots * D.G * msa::kHeadDim);
   if (ws) {
-    ws->cnt = reinterpret_cast<int32_t*>(cnt_cursor);
-    ws->cursor = reinterpret_cast<int32_t*>(cnt_cursor) + nbgt;
+    ws->hist = reinterpret_cast<int32_t*>(hist);
+    ws->cnt = reinterpret_cast<int32_t*>(cnt);
+    ws->bsum = reinterpret_cast<int32_t*>(bsum);
     ws->off = reinterpret_cast<int32_t*>(off);
     ws->tile_off = reinterpret_cast<int32_t*>(tile_off);
     ws->list = reinterpret_cast<int32_t*>(list);
@@ -92,6 +94,34 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
     ws->max_tiles = max_tiles;
   }
   return at;
+}
+
+// The gather plan keeps one LDS histogram bin per block (n_kv <= 2M tokens);
+// the query-outer path of decode-shaped calls has no such limit.
+bool attn_path_ok(const Dims& D) { return msa::use_attn_rows(D) || D.n_blk <= msa::kMaxPlanBlocks; }
+
+size_t attn_bytes(const Dims& D) {
+  return msa::use_attn_rows(D) ? round256(msa::attn_rows_partial_bytes(D)) : attn_ws_layout(D, nullptr, nullptr);
+}
+
+hipError_t run_attention(const Dims& D, const void* q, const void* k, const void* v, const int32_t* block_idx,
+                         void* out, float* lse, char* ws_base, hipStream_t stream) {
+  auto q16 = static_cast<const uint16_t*>(q);
+  auto k16 = static_cast<const uint16_t*>(k);
+  auto v16 = static_cast<const uint16_t*>(v);
+  auto o16 = static_cast<uint16_t*>(out);
+  if (msa::use_attn_rows(D))
+    return msa::launch_attn_rows(q16, k16, v16, block_idx, o16, lse, reinterpret_cast<float*>(ws_base), D, stream);
+  AttnWs ws;
+  attn_ws_layout(D, ws_base, &ws);
+  return msa::launch_sparse_attn(q16, k16, v16, block_idx, o16, lse, ws, D, stream);
+}
+
+hipError_t run_index(const Dims& D, const void* index_q, const void* index_k, float* pooled, hipStream_t stream) {
+  auto iq = static_cast<const uint16_t*>(index_q);
+  auto ik = static_cast<const uint16_t*>(index_k);
+  return msa::use_index_small(D) ? msa::launch_index_small(iq, ik, pooled, D, stream)
+                                 : msa::launch_index_scores(iq, ik, pooled, D, stream);
 }
 
 size_t pooled_bytes(const Dims& D) { return round256(sizeof(float) * (size_t)D.B * D.h_kv * D.n_q * D.n_blk); }
@@ -113,10 +143,12 @@ msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
       *bytes = 0;
       return MSA_OK;
     case MSA_OP_SPARSE_ATTN:
-      *bytes = attn_ws_layout(D, nullptr, nullptr);
+      if (!attn_path_ok(D)) return MSA_ERR_UNSUPPORTED;
+      *bytes = attn_bytes(D);
       return MSA_OK;
     case MSA_OP_FORWARD:
-      *bytes = pooled_bytes(D) + attn_ws_layout(D, nullptr, nullptr);
+      if (!attn_path_ok(D)) return MSA_ERR_UNSUPPORTED;
+      *bytes = pooled_bytes(D) + attn_bytes(D);
       return MSA_OK;
     default:
       return MSA_ERR_INVALID_ARGUMENT;
@@ -130,8 +162,7 @@ msa_status msa_index_scores(const msa_problem* p, const void* index_q, const voi
   if (st != MSA_OK) return st;
   if (!index_q || !index_k || !pooled) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(index_q) || !aligned16(index_k) || !aligned16(pooled)) return MSA_ERR_INVALID_ARGUMENT;
-  return hip_status(msa::launch_index_scores(static_cast<const uint16_t*>(index_q),
-                                             static_cast<const uint16_t*>(index_k), pooled, D, stream));
+  return hip_status(run_index(D, index_q, index_k, pooled, stream));
 }
 
 msa_status msa_block_topk(const msa_problem* p, const float* pooled, int32_t* block_idx, hipStream_t stream) {
@@ -153,11 +184,9 @@ msa_status msa_sparse_attn_fwd(const msa_problem* p, const void* q, const void* 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(out) ||
       !aligned16(workspace) || (lse && !aligned16(lse)))
     return MSA_ERR_INVALID_ARGUMENT;
-  AttnWs ws;
-  if (attn_ws_layout(D, static_cast<char*>(workspace), &ws) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
-  return hip_status(msa::launch_sparse_attn(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                            static_cast<const uint16_t*>(v), block_idx,
-                                            static_cast<uint16_t*>(out), lse, ws, D, stream));
+  if (!attn_path_ok(D)) return MSA_ERR_UNSUPPORTED;
+  if (attn_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(run_attention(D, q, k, v, block_idx, out, lse, static_cast<char*>(workspace), stream));
 }
 
 msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const void* v, const void* index_q,
@@ -170,20 +199,15 @@ msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(index_q) || !aligned16(index_k) ||
       !aligned16(out) || !aligned16(block_idx) || !aligned16(workspace) || (lse && !aligned16(lse)))
     return MSA_ERR_INVALID_ARGUMENT;
+  if (!attn_path_ok(D)) return MSA_ERR_UNSUPPORTED;
   const size_t pb = pooled_bytes(D);
-  AttnWs ws;
-  if (pb + attn_ws_layout(D, static_cast<char*>(workspace) + pb, &ws) > workspace_bytes)
-    return MSA_ERR_WORKSPACE_TOO_SMALL;
+  if (pb + attn_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
   float* pooled = static_cast<float*>(workspace);
-  hipError_t e = msa::launch_index_scores(static_cast<const uint16_t*>(index_q),
-                                          static_cast<const uint16_t*>(index_k), pooled, D, stream);
+  hipError_t e = run_index(D, index_q, index_k, pooled, stream);
   if (e != hipSuccess) return MSA_ERR_HIP;
   e = msa::launch_block_topk(pooled, block_idx, D, stream);
   if (e != hipSuccess) return MSA_ERR_HIP;
-  e = msa::launch_sparse_attn(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                              static_cast<const uint16_t*>(v), block_idx, static_cast<uint16_t*>(out), lse, ws, D,
-                              stream);
-  return hip_status(e);
+  return hip_status(run_attention(D, q, k, v, block_idx, out, lse, static_cast<char*>(workspace) + pb, stream));
 }
 
 const char* msa_status_string(msa_status s) {

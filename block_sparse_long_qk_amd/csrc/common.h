@@ -9,6 +9,10 @@ constexpr int kBk = 128;        // block size the kernels are built for
 constexpr int kHeadDim = 128;   // main-branch head dim
 constexpr int kMaxTopk = 64;    // one selection per wavefront lane at most
 constexpr int kTileRows = 128;  // query rows (positions x heads) per attention tile
+constexpr int kChunkRows = 1024;   // query rows per gather-plan workgroup
+constexpr int kMaxPlanBlocks = 16384;  // LDS histogram bins of the gather plan (n_kv <= 2M)
+constexpr int kRowsMaxQ = 4;           // query rows per sequence up to which attention runs query-outer
+constexpr int kRowsPart = 16 * kHeadDim + 16;  // floats per query-outer partial: o[16][d], lse[16]
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -24,16 +28,25 @@ struct Dims {
 
 // Workspace carve-up of the sparse attention stage (device pointers).
 struct AttnWs {
+  int32_t* hist;       // [B*h_kv][n_ch][n_blk] per-chunk block histograms, then chunk offsets
   int32_t* cnt;        // [B*h_kv*n_blk]   gathered query rows per (b, g, block)
-  int32_t* cursor;     // [B*h_kv*n_blk]   fill cursors
+  int32_t* bsum;       // [2 * scan blocks] block sums of the two-level scan
   int32_t* off;        // [B*h_kv*n_blk+1] exclusive scan of cnt
   int32_t* tile_off;   // [B*h_kv*n_blk+1] exclusive scan of ceil(cnt / pt); last = tile count
   int32_t* list;       // [edges]          row-slot ids (i * k + s), grouped by (b, g, block)
   int32_t* tile_desc;  // [max_tiles][2]   (b*h_kv*n_blk + block, first list entry)
   float* part_lse;     // [B*h_kv*n_q*k][G]     base-2 log-sum-exp of each partial
-  uint16_t* part_o;    // [B*h_kv*n_q*k][G][d]  normalised partial outputs, bf16
+  uint16_t* part_o;    // [B*h_kv*n_q*k][G][d]  normalised partial outputs, bf16, lane order
   int64_t max_tiles;
 };
+
+// Is slot s of a block_idx row a non-local block with a partial of its own?
+// Rows are ascending; a repeated entry is ignored; the local block and
+// anything past it carry no partial.
+__device__ __forceinline__ bool nonlocal_slot(const int32_t* row, int s, int local) {
+  const int t = row[s];
+  return t >= 0 && t < local && (s == 0 || row[s - 1] != t);
+}
 
 // 32x32x16 bf16 MFMA, fp32 accumulate.  Operands are 8 packed bf16 per lane.
 __device__ __forceinline__ f32x16 mfma_32x32x16(uint4 a, uint4 b, f32x16 c) {

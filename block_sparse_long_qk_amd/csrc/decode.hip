@@ -1,0 +1,318 @@
+// Decode-shaped calls: a few query rows per sequence against a long cache.
+//
+// Page "MiniMax 发布 MSA 稀疏注意力方法，开源推理内核并推出 MiniMax-M3 模型":
+// section 两个分支如何工作 (index scores of the visible keys, max-pooled to
+// blocks; softmax attention over the selected blocks) and section 优势与不足
+// (decode at long context).  With one new token per sequence the index branch
+// must stream every index key once: it is bound by HBM, not by the MFMA.
+//
+// k_index_small: (query, group) rows of one sequence (at most 16) form the
+//   MFMA B operand in registers; every wave streams its own range of 128-key
+//   blocks of index_k straight from HBM into 16x16x32 bf16 MFMA A operands (no
+//   LDS, no barriers) and max-pools each block in registers.
+// k_attn_rows: query-outer attention.  One wave per (row, slot): it loads the
+//   slot's K block as MFMA B operands, computes the G x 128 scores, the block's
+//   softmax statistics, and P V on the VALU from coalesced V rows; it writes an
+//   fp32 partial and its base-2 log-sum-exp.
+// k_merge_rows: LSE merge of a row's partials into bf16 out and the lse.
+#include "launch.h"
+
+namespace msa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// Index-dim mapping of both MFMA operands: lane group c (= lane / 16) and
+// k-step ks hold dims (DIDX/4)*c + 8*ks .. +8, so each lane reads one
+// contiguous DIDX/2-byte run of its row.
+template <int DIDX>
+__global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict__ iq,
+                                                     const uint16_t* __restrict__ ik, float* __restrict__ pooled,
+                                                     Dims D, int32_t blocks_per_wave) {
+  constexpr int KS = DIDX / 32;
+  const float NEG_INF = -__builtin_huge_valf();
+  const int b = blockIdx.y;
+  const int R = D.n_q * D.h_kv;  // <= 16
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, c = lane >> 4;
+  const int t_last = (int)((D.offset + D.n_q - 1) / kBk);
+  const int t0 = ((int)blockIdx.x * 4 + wave) * blocks_per_wave;
+  const int t1 = min(t0 + blocks_per_wave, t_last + 1);
+  if (t0 >= t1) return;
+
+  uint4 qb[KS];
+  const bool row_ok = n < R;
+  const int64_t pc = row_ok ? D.offset + n / D.h_kv : -1;
+  const int l_row = row_ok ? (int)(pc / kBk) : -1;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qb[ks] = row_ok ? *reinterpret_cast<const uint4*>(iq + ((int64_t)b * R + n) * DIDX + (DIDX / 4) * c + 8 * ks)
+                    : make_uint4(0, 0, 0, 0);
+  int64_t out_base = -1;
+  if (row_ok && c == 0) {
+    const int i = n / D.h_kv, g = n % D.h_kv;
+    out_base = (((int64_t)b * D.h_kv + g) * D.n_q + i) * D.n_blk;
+  }
+  const uint16_t* ikb = ik + (int64_t)b * D.n_kv * DIDX + (DIDX / 4) * c;
+  const int64_t p_min = D.offset;
+
+  for (int t = t0; t < t1; ++t) {
+    uint4 a[8][KS];
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      const int64_t key = (int64_t)t * kBk + 16 * T + n;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        a[T][ks] = key < D.n_kv ? *reinterpret_cast<const uint4*>(ikb + key * DIDX + 8 * ks) : make_uint4(0, 0, 0, 0);
+    }
+    const bool need_mask = (int64_t)t * kBk + kBk - 1 > p_min;
+    float m = NEG_INF;
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma_16x16x32(a[T][ks], qb[ks], acc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x = acc[j];
+        if (need_mask && (int64_t)t * kBk + 16 * T + 4 * c + j > pc) x = NEG_INF;
+        m = fmaxf(m, x);
+      }
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (out_base >= 0 && t <= l_row) pooled[out_base + t] = m;
+  }
+}
+
+// Is slot s of a row a block to attend?  Slot k stands for the local block
+// when the row does not list it.
+__device__ __forceinline__ int slot_block(const int32_t* row, int s, int k, int local) {
+  if (s == k) {
+    for (int u = 0; u < k; ++u)
+      if (row[u] == local) return -1;
+    return local;
+  }
+  const int t = row[s];
+  return (t >= 0 && t <= local && (s == 0 || row[s - 1] != t)) ? t : -1;
+}
+
+// One wave per (row, slot); GMAX (8 or 16) >= G query heads of the row's group.
+template <int GMAX>
+__global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ v,
+                                                   const int32_t* __restrict__ block_idx, float* __restrict__ part,
+                                                   Dims D) {
+  __shared__ float P[4][kBk][GMAX];  // per wave: probabilities [key][head]
+  const float NEG_INF = -__builtin_huge_valf();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t r = blockIdx.x;  // row = (b*h_kv + g)*n_q + i
+  const int s = blockIdx.y * 4 + wave;
+  if (s > D.k) return;  // slots 0..k (k = the unlisted local block)
+  const int64_t bg = r / D.n_q;
+  const int i = (int)(r % D.n_q);
+  const int g = (int)(bg % D.h_kv), b = (int)(bg / D.h_kv);
+  const int64_t p = D.offset + i;
+  const int local = (int)(p / kBk);
+  const int t = slot_block(block_idx + r * D.k, s, D.k, local);  // same for the whole wave
+  float* dst = part + (r * (D.k + 1) + s) * (int64_t)kRowsPart;  // o [16][d], then lse [16]
+  if (t < 0) {
+    if (lane < 16) dst[16 * kHeadDim + lane] = NEG_INF;
+    return;
+  }
+  const int n = lane & 15, c = lane >> 4;
+  const int64_t key0 = (int64_t)t * kBk;
+  const uint16_t* kb = k + ((int64_t)bg * D.n_kv + key0) * kHeadDim;
+  const uint16_t* vb = v + ((int64_t)bg * D.n_kv + key0) * kHeadDim;
+
+  // scores S[h][key] with MFMA: A = Q (rows = heads), B = K^T (columns = keys);
+  // lane group c and k-step ks hold head dims 32*c + 8*ks .. +8.
+  uint4 qa[4];
+  const bool head_ok = n < D.G;
+  const uint16_t* qrow = q + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + (head_ok ? n : 0)) * kHeadDim + 32 * c;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qa[ks] = head_ok ? *reinterpret_cast<const uint4*>(qrow + 8 * ks) : make_uint4(0, 0, 0, 0);
+  f32x4 sc[8];
+#pragma unroll
+  for (int T = 0; T < 8; ++T) {
+    const int key = 16 * T + n;
+    uint4 kf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[ks] = key0 + key < D.n_kv ? *reinterpret_cast<const uint4*>(kb + key * kHeadDim + 32 * c + 8 * ks)
+                                   : make_uint4(0, 0, 0, 0);
+    sc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) sc[T] = mfma_16x16x32(qa[ks], kf[ks], sc[T]);
+  }
+  // lane (column key = 16T + n, group c) holds heads 4c + j; keys past p or n_kv drop
+  float mx[4], sm[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float m = NEG_INF;
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      const int64_t key = key0 + 16 * T + n;
+      float x = sc[T][j] * D.scale_log2;
+      if (key > p || key >= D.n_kv) x = NEG_INF;
+      sc[T][j] = x;
+      m = fmaxf(m, x);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float mref = m == NEG_INF ? 0.f : m;
+    float sum = 0.f;
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      const float e = __builtin_amdgcn_exp2f(sc[T][j] - mref);
+      sum += e;
+      if (4 * c + j < GMAX) P[wave][16 * T + n][4 * c + j] = e;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+    mx[j] = m;
+    sm[j] = sum;
+  }
+  // per-head statistics to every lane (head h lives in lane group h / 4, register h % 4)
+  float lh[GMAX], mh[GMAX];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    lh[h] = __shfl(sm[h & 3], 16 * (h >> 2), 64);
+    mh[h] = __shfl(mx[h & 3], 16 * (h >> 2), 64);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // O[h][8*dc .. +8] over keys kr, kr+4, ...: lane = (dc = lane % 16, kr = lane / 16)
+  const int dc = lane & 15, kr = lane >> 4;
+  float acc[GMAX][8];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  const int n_keys = (int)min((int64_t)kBk, (int64_t)D.n_kv - key0);
+  for (int kk = kr; kk < n_keys; kk += 4) {
+    const uint4 w = *reinterpret_cast<const uint4*>(vb + kk * kHeadDim + 8 * dc);
+    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+    float vv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vv[2 * e] = __uint_as_float(x[e] << 16);
+      vv[2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      const float ph = P[wave][kk][h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += ph * vv[e];
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[h][e];
+      x += __shfl_xor(x, 16, 64);
+      x += __shfl_xor(x, 32, 64);
+      acc[h][e] = x;
+    }
+  if (kr == 0) {
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      if (h < D.G) {
+        const float inv = 1.f / lh[h];
+        float4* o4 = reinterpret_cast<float4*>(dst + h * kHeadDim + 8 * dc);
+        o4[0] = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
+        o4[1] = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h)
+    if (lane == h && h < D.G) dst[16 * kHeadDim + h] = mh[h] + __log2f(lh[h]);
+}
+
+// One workgroup per row: out[b][i][g*G + h][d] and lse from the row's partials.
+__global__ __launch_bounds__(256) void k_merge_rows(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                    float* __restrict__ lse_out, Dims D) {
+  const float NEG_INF = -__builtin_huge_valf();
+  const int64_t r = blockIdx.x;
+  const int64_t bg = r / D.n_q;
+  const int i = (int)(r % D.n_q);
+  const int g = (int)(bg % D.h_kv), b = (int)(bg / D.h_kv);
+  const int nslot = D.k + 1;
+  const float* base = part + r * nslot * (int64_t)kRowsPart;
+  for (int x = threadIdx.x; x < D.G * (kHeadDim / 4); x += blockDim.x) {
+    const int h = x / (kHeadDim / 4), d4 = x % (kHeadDim / 4);
+    float m = NEG_INF;
+    for (int s = 0; s < nslot; ++s) m = fmaxf(m, base[s * kRowsPart + 16 * kHeadDim + h]);
+    float wsum = 0.f;
+    for (int s = 0; s < nslot; ++s) {
+      const float ls = base[s * kRowsPart + 16 * kHeadDim + h];
+      if (ls > NEG_INF) wsum += __builtin_amdgcn_exp2f(ls - m);
+    }
+    const float tot = m + __log2f(wsum);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < nslot; ++s) {
+      const float* ps = base + s * kRowsPart;
+      const float ls = ps[16 * kHeadDim + h];
+      if (!(ls > NEG_INF)) continue;
+      const float cw = __builtin_amdgcn_exp2f(ls - tot);
+      const float4 w = *reinterpret_cast<const float4*>(ps + h * kHeadDim + 4 * d4);
+      o.x += cw * w.x;
+      o.y += cw * w.y;
+      o.z += cw * w.z;
+      o.w += cw * w.w;
+    }
+    uint16_t* dst = out + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + h) * kHeadDim + 4 * d4;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+    if (lse_out && d4 == 0) lse_out[((int64_t)b * D.h_q + g * D.G + h) * D.n_q + i] = tot * 0.69314718055994531f;
+  }
+}
+
+}  // namespace
+
+bool use_index_small(const Dims& D) { return (int64_t)D.n_q * D.h_kv <= 16; }
+
+bool use_attn_rows(const Dims& D) { return D.n_q <= kRowsMaxQ && D.G <= 16; }
+
+size_t attn_rows_partial_bytes(const Dims& D) {
+  return sizeof(float) * (size_t)D.B * D.h_kv * D.n_q * (D.k + 1) * kRowsPart;
+}
+
+hipError_t launch_index_small(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
+                              hipStream_t stream) {
+  const int t_max = (int)((D.offset + D.n_q - 1) / kBk) + 1;
+  // about 2048 workgroups of 4 waves over the whole batch, at least one block per wave
+  int64_t waves_per_b = (8192 + D.B - 1) / D.B;
+  if (waves_per_b > t_max) waves_per_b = t_max;
+  const int per = (int)((t_max + waves_per_b - 1) / waves_per_b);
+  const int wgs = (int)(((t_max + per - 1) / per + 3) / 4);
+  dim3 grid(wgs, D.B);
+  if (D.d_idx == 128)
+    hipLaunchKernelGGL(k_index_small<128>, grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+  else
+    hipLaunchKernelGGL(k_index_small<64>, grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
+                            uint16_t* out, float* lse, float* part, const Dims& D, hipStream_t stream) {
+  const int64_t rows = (int64_t)D.B * D.h_kv * D.n_q;
+  dim3 grid((unsigned)rows, (D.k + 1 + 3) / 4);
+  if (D.G <= 8)
+    hipLaunchKernelGGL(k_attn_rows<8>, grid, dim3(256), 0, stream, q, k, v, block_idx, part, D);
+  else
+    hipLaunchKernelGGL(k_attn_rows<16>, grid, dim3(256), 0, stream, q, k, v, block_idx, part, D);
+  hipLaunchKernelGGL(k_merge_rows, dim3((unsigned)rows), dim3(256), 0, stream, part, out, lse, D);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,217 @@
+// Gather plan of the KV-outer attention (page "MiniMax 发布 MSA 稀疏注意力方法，开源推理
+// 内核并推出 MiniMax-M3 模型", section 内核协同设计: iterate over KV blocks and gather
+// the query positions that selected each one).
+//
+// Input: block_idx rows (one per sequence, group, query).  Output: for every
+// (sequence b, group g, block t) the list of row-slot ids i*k + s that picked t
+// as a non-local block, the lists stored back to back in (b, g, t) order, and a
+// tile list cutting each list into runs of `pt` query positions.
+//
+// A counting sort without global atomics:
+//   1. hist:  one workgroup per chunk of kChunkRows rows of one (b, g) counts its
+//             entries per block in LDS and writes the chunk's histogram;
+//   2. colscan: per (b, g, t), exclusive scan of the chunk histograms (the chunk's
+//             start inside the block's list) and the list length;
+//   3. scan:  exclusive scans of the list lengths and of their tile counts over
+//             all (b, g, t) (two-level: block sums, one-workgroup scan, apply);
+//   4. fill:  each chunk workgroup re-reads its rows and scatters row-slot ids
+//             with LDS cursors;
+//   5. tiles: one descriptor (b*h_kv*n_blk + t, first entry) per tile.
+// Entries inside one list appear in no fixed order; every row's attention is
+// independent of the other rows of its tile, so results do not depend on it.
+#include "launch.h"
+
+namespace msa {
+namespace {
+
+constexpr int kScanPer = 4096;  // elements per workgroup in the two-level scan
+
+__global__ __launch_bounds__(256) void k_plan_hist(const int32_t* __restrict__ block_idx,
+                                                   int32_t* __restrict__ hist, Dims D, int32_t n_ch) {
+  extern __shared__ int32_t lh[];  // [n_blk]
+  const int ch = blockIdx.x, bg = blockIdx.y;
+  for (int t = threadIdx.x; t < D.n_blk; t += blockDim.x) lh[t] = 0;
+  __syncthreads();
+  const int i0 = ch * kChunkRows, i1 = min(D.n_q, i0 + kChunkRows);
+  for (int i = i0 + (int)threadIdx.x; i < i1; i += blockDim.x) {
+    const int local = (int)((D.offset + i) / kBk);
+    const int32_t* row = block_idx + ((int64_t)bg * D.n_q + i) * D.k;
+    for (int s = 0; s < D.k; ++s)
+      if (nonlocal_slot(row, s, local)) atomicAdd(&lh[row[s]], 1);
+  }
+  __syncthreads();
+  int32_t* dst = hist + ((int64_t)bg * n_ch + ch) * D.n_blk;
+  for (int t = threadIdx.x; t < D.n_blk; t += blockDim.x) dst[t] = lh[t];
+}
+
+// hist[bg][ch][t] <- exclusive prefix over ch; cnt[bg][t] <- total.
+__global__ void k_plan_colscan(int32_t* __restrict__ hist, int32_t* __restrict__ cnt, Dims D, int32_t n_ch) {
+  const int64_t nbgt = (int64_t)D.B * D.h_kv * D.n_blk;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < nbgt; x += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bg = x / D.n_blk, t = x % D.n_blk;
+    int32_t acc = 0;
+    for (int ch = 0; ch < n_ch; ++ch) {
+      int32_t* h = hist + (bg * n_ch + ch) * D.n_blk + t;
+      const int32_t v = *h;
+      *h = acc;
+      acc += v;
+    }
+    cnt[x] = acc;
+  }
+}
+
+__device__ __forceinline__ int32_t tiles_of(int32_t c, int32_t pt) { return (c + pt - 1) / pt; }
+
+// Block-wide inclusive scan of two values (256 threads).
+__device__ __forceinline__ void block_scan2(int32_t& a, int32_t& b, int32_t* sa, int32_t* sb) {
+  const int tid = threadIdx.x;
+  sa[tid] = a;
+  sb[tid] = b;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int32_t ya = tid >= o ? sa[tid - o] : 0, yb = tid >= o ? sb[tid - o] : 0;
+    __syncthreads();
+    sa[tid] += ya;
+    sb[tid] += yb;
+    __syncthreads();
+  }
+  a = sa[tid];
+  b = sb[tid];
+}
+
+__global__ __launch_bounds__(256) void k_scan_reduce(const int32_t* __restrict__ cnt, int32_t* __restrict__ bsum,
+                                                     int64_t n, int32_t pt) {
+  __shared__ int32_t sa[256], sb[256];
+  const int64_t a0 = (int64_t)blockIdx.x * kScanPer;
+  int32_t e = 0, t = 0;
+  for (int64_t x = a0 + threadIdx.x; x < min(n, a0 + kScanPer); x += 256) {
+    e += cnt[x];
+    t += tiles_of(cnt[x], pt);
+  }
+  block_scan2(e, t, sa, sb);
+  if (threadIdx.x == 255) {
+    bsum[2 * blockIdx.x] = e;
+    bsum[2 * blockIdx.x + 1] = t;
+  }
+}
+
+// One workgroup: exclusive scan of the (edges, tiles) block sums in place;
+// writes the grand totals to off[n] and tile_off[n].
+__global__ __launch_bounds__(256) void k_scan_blocks(int32_t* __restrict__ bsum, int32_t nb, int32_t* __restrict__ off,
+                                                     int32_t* __restrict__ tile_off, int64_t n) {
+  __shared__ int32_t sa[256], sb[256];
+  const int per = (nb + 255) / 256;
+  const int a0 = threadIdx.x * per, a1 = min(nb, a0 + per);
+  int32_t e = 0, t = 0;
+  for (int x = a0; x < a1; ++x) {
+    e += bsum[2 * x];
+    t += bsum[2 * x + 1];
+  }
+  const int32_t e_own = e, t_own = t;
+  block_scan2(e, t, sa, sb);
+  int32_t re = e - e_own, rt = t - t_own;
+  for (int x = a0; x < a1; ++x) {
+    const int32_t ve = bsum[2 * x], vt = bsum[2 * x + 1];
+    bsum[2 * x] = re;
+    bsum[2 * x + 1] = rt;
+    re += ve;
+    rt += vt;
+  }
+  if (threadIdx.x == 255) {
+    off[n] = e;
+    tile_off[n] = t;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_scan_apply(const int32_t* __restrict__ cnt, const int32_t* __restrict__ bsum,
+                                                    int32_t* __restrict__ off, int32_t* __restrict__ tile_off,
+                                                    int64_t n, int32_t pt) {
+  __shared__ int32_t sa[256], sb[256];
+  const int64_t a0 = (int64_t)blockIdx.x * kScanPer;
+  constexpr int kPer = kScanPer / 256;  // contiguous elements per thread
+  const int64_t b0 = a0 + (int64_t)threadIdx.x * kPer;
+  int32_t e = 0, t = 0;
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t x = b0 + u;
+    if (x < n) {
+      e += cnt[x];
+      t += tiles_of(cnt[x], pt);
+    }
+  }
+  const int32_t e_own = e, t_own = t;
+  block_scan2(e, t, sa, sb);
+  int32_t re = bsum[2 * blockIdx.x] + e - e_own, rt = bsum[2 * blockIdx.x + 1] + t - t_own;
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t x = b0 + u;
+    if (x < n) {
+      off[x] = re;
+      tile_off[x] = rt;
+      re += cnt[x];
+      rt += tiles_of(cnt[x], pt);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ block_idx,
+                                                   const int32_t* __restrict__ hist, const int32_t* __restrict__ off,
+                                                   int32_t* __restrict__ list, Dims D, int32_t n_ch) {
+  extern __shared__ int32_t cursor[];  // [n_blk]
+  const int ch = blockIdx.x, bg = blockIdx.y;
+  const int32_t* h = hist + ((int64_t)bg * n_ch + ch) * D.n_blk;
+  const int32_t* o = off + (int64_t)bg * D.n_blk;
+  for (int t = threadIdx.x; t < D.n_blk; t += blockDim.x) cursor[t] = o[t] + h[t];
+  __syncthreads();
+  const int i0 = ch * kChunkRows, i1 = min(D.n_q, i0 + kChunkRows);
+  for (int i = i0 + (int)threadIdx.x; i < i1; i += blockDim.x) {
+    const int local = (int)((D.offset + i) / kBk);
+    const int32_t* row = block_idx + ((int64_t)bg * D.n_q + i) * D.k;
+    for (int s = 0; s < D.k; ++s)
+      if (nonlocal_slot(row, s, local)) list[atomicAdd(&cursor[row[s]], 1)] = i * D.k + s;
+  }
+}
+
+__global__ void k_plan_tiles(const int32_t* __restrict__ cnt, const int32_t* __restrict__ tile_off,
+                             int32_t* __restrict__ tile_desc, int64_t n, int32_t pt) {
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
+    const int nt = tiles_of(cnt[x], pt);
+    const int64_t t0 = tile_off[x];
+    for (int j = 0; j < nt; ++j) {
+      tile_desc[2 * (t0 + j)] = (int32_t)x;
+      tile_desc[2 * (t0 + j) + 1] = j * pt;
+    }
+  }
+}
+
+unsigned grid_for(int64_t n, int threads) {
+  int64_t g = (n + threads - 1) / threads;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+int64_t plan_chunks(const Dims& D) { return (D.n_q + kChunkRows - 1) / kChunkRows; }
+
+int64_t plan_scan_blocks(const Dims& D) {
+  return ((int64_t)D.B * D.h_kv * D.n_blk + kScanPer - 1) / kScanPer;
+}
+
+hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const Dims& D, hipStream_t stream) {
+  const int64_t nbgt = (int64_t)D.B * D.h_kv * D.n_blk;
+  const int n_ch = (int)plan_chunks(D);
+  const int nb = (int)plan_scan_blocks(D);
+  const size_t lds = sizeof(int32_t) * D.n_blk;
+  dim3 cgrid(n_ch, D.B * D.h_kv);
+  hipLaunchKernelGGL(k_plan_hist, cgrid, dim3(256), lds, stream, block_idx, ws.hist, D, n_ch);
+  hipLaunchKernelGGL(k_plan_colscan, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.hist, ws.cnt, D, n_ch);
+  hipLaunchKernelGGL(k_scan_reduce, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, nbgt, D.pt);
+  hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(256), 0, stream, ws.bsum, nb, ws.off, ws.tile_off, nbgt);
+  hipLaunchKernelGGL(k_scan_apply, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, ws.off, ws.tile_off, nbgt, D.pt);
+  hipLaunchKernelGGL(k_plan_fill, cgrid, dim3(256), lds, stream, block_idx, ws.hist, ws.off, ws.list, D, n_ch);
+  hipLaunchKernelGGL(k_plan_tiles, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.cnt, ws.tile_off,
+                     ws.tile_desc, nbgt, D.pt);
+  return hipGetLastError();
+}
+
+}  // namespace msa

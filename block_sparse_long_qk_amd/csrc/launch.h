@@ -14,8 +14,22 @@ hipError_t launch_index_scores(const uint16_t* index_q, const uint16_t* index_k,
 // Exp-free block top-k with the forced local block: block_idx[B][h_kv][n_q][k].
 hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims& D, hipStream_t stream);
 
+// Gather plan: per (b, g, block) lists of row-slot ids and the tile list.
+hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const Dims& D, hipStream_t stream);
+int64_t plan_chunks(const Dims& D);       // chunk workgroups per (b, g)
+int64_t plan_scan_blocks(const Dims& D);  // workgroups of the two-level scan
+
 // Gather plan + gathered non-local tiles + local tiles with the merge.
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream);
+
+// Decode-shaped calls (few query rows per sequence).
+bool use_index_small(const Dims& D);   // at most 16 (query, group) rows per sequence
+bool use_attn_rows(const Dims& D);     // query-outer attention
+size_t attn_rows_partial_bytes(const Dims& D);
+hipError_t launch_index_small(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
+                              hipStream_t stream);
+hipError_t launch_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
+                            uint16_t* out, float* lse, float* part, const Dims& D, hipStream_t stream);
 
 }  // namespace msa

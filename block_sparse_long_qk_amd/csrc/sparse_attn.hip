@@ -7,14 +7,16 @@
 // queries, packing gathered query positions into 128x128 score tiles; attention
 // and merge run as two separate stages).
 //
-// Stage A, gather plan: for every (sequence, group, block) the list of query
-//   rows that selected it as a non-local block (histogram, scan, scatter), cut
-//   into tiles of `pt` positions (pt * G <= 128 rows).
-// Stage B, non-local tiles (KV-outer): one workgroup per tile loads the 128-key
-//   K block and V block once into LDS, gathers the tile's query rows and
-//   computes S^T = K Q^T and O^T = V^T P^T with 32x32x16 bf16 MFMA.  A
-//   non-local block lies wholly before the query, so no mask is needed.  Each
-//   (row, slot) writes a normalised bf16 partial and its base-2 log-sum-exp.
+// Stage A, gather plan (gather_plan.hip): for every (sequence, group, block)
+//   the list of query rows that selected it as a non-local block, cut into
+//   tiles of `pt` positions (pt * G <= 128 rows).
+// Stage B, non-local tiles (KV-outer): persistent workgroups walk contiguous
+//   runs of tiles; the 128-key K block and V block sit in LDS while the run
+//   stays on one (b, g, block), the tile's query rows are gathered into
+//   registers (the next tile's while the current one computes), and S^T = K Q^T
+//   and O^T = V^T P^T run on 32x32x16 bf16 MFMA.  A non-local block lies wholly
+//   before the query, so no mask is needed.  Each (row, slot) writes a
+//   normalised bf16 partial and its base-2 log-sum-exp.
 // Stage C, local tiles + merge: one workgroup per run of `pt` consecutive
 //   positions, which share their local block; it computes that block with the
 //   causal mask, then merges the row's partials (LSE weighting) and writes the
@@ -22,6 +24,8 @@
 //
 // Lane layout: a wave owns 32 rows (one MFMA n-tile); lane l holds column
 // l % 32, so all softmax statistics of a row live in one lane pair (l, l ^ 32).
+#include <algorithm>
+
 #include "launch.h"
 
 namespace msa {
@@ -29,94 +33,6 @@ namespace {
 
 constexpr int KP = kHeadDim + 8;   // LDS pitch of K rows (bf16): 16-byte pad
 constexpr int VP = kBk + 4;        // LDS pitch of V^T rows (bf16): 8-byte pad
-
-// Is slot s of a block_idx row a non-local block with its own partial?
-// (Rows are ascending; a repeated entry is ignored; the local block and
-// anything past it carry no partial.)
-__device__ __forceinline__ bool nonlocal_slot(const int32_t* row, int s, int local) {
-  const int t = row[s];
-  return t >= 0 && t < local && (s == 0 || row[s - 1] != t);
-}
-
-__global__ void k_fill_zero(int32_t* __restrict__ p, int64_t n) {
-  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x)
-    p[x] = 0;
-}
-
-__global__ void k_plan_count(const int32_t* __restrict__ block_idx, int32_t* __restrict__ cnt, Dims D) {
-  const int64_t nrows = (int64_t)D.B * D.h_kv * D.n_q;
-  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < nrows; r += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t bg = r / D.n_q;
-    const int i = (int)(r % D.n_q);
-    const int local = (int)((D.offset + i) / kBk);
-    const int32_t* row = block_idx + r * D.k;
-    for (int s = 0; s < D.k; ++s)
-      if (nonlocal_slot(row, s, local)) atomicAdd(&cnt[bg * D.n_blk + row[s]], 1);
-  }
-}
-
-// Exclusive scans of cnt and of ceil(cnt / pt) by one workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ cnt, int32_t* __restrict__ off,
-                                                    int32_t* __restrict__ tile_off, int64_t n, int32_t pt) {
-  __shared__ int32_t s_e[1024], s_t[1024];
-  const int tid = threadIdx.x;
-  const int64_t chunk = (n + 1023) / 1024;
-  const int64_t a = tid * chunk, z = min(n, a + chunk);
-  int32_t se = 0, st = 0;
-  for (int64_t x = a; x < z; ++x) {
-    se += cnt[x];
-    st += (cnt[x] + pt - 1) / pt;
-  }
-  s_e[tid] = se;
-  s_t[tid] = st;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
-    const int32_t ye = tid >= o ? s_e[tid - o] : 0, yt = tid >= o ? s_t[tid - o] : 0;
-    __syncthreads();
-    s_e[tid] += ye;
-    s_t[tid] += yt;
-    __syncthreads();
-  }
-  int32_t re = s_e[tid] - se, rt = s_t[tid] - st;
-  for (int64_t x = a; x < z; ++x) {
-    off[x] = re;
-    tile_off[x] = rt;
-    re += cnt[x];
-    rt += (cnt[x] + pt - 1) / pt;
-  }
-  if (tid == 1023) {
-    off[n] = s_e[1023];
-    tile_off[n] = s_t[1023];
-  }
-}
-
-__global__ void k_plan_fill(const int32_t* __restrict__ block_idx, int32_t* __restrict__ cursor,
-                            const int32_t* __restrict__ off, int32_t* __restrict__ list, Dims D) {
-  const int64_t nrows = (int64_t)D.B * D.h_kv * D.n_q;
-  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < nrows; r += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t bg = r / D.n_q;
-    const int i = (int)(r % D.n_q);
-    const int local = (int)((D.offset + i) / kBk);
-    const int32_t* row = block_idx + r * D.k;
-    for (int s = 0; s < D.k; ++s) {
-      if (!nonlocal_slot(row, s, local)) continue;
-      const int64_t bgt = bg * D.n_blk + row[s];
-      const int at = atomicAdd(&cursor[bgt], 1);
-      list[off[bgt] + at] = i * D.k + s;
-    }
-  }
-}
-
-__global__ void k_plan_tiles(const int32_t* __restrict__ cnt, const int32_t* __restrict__ tile_off,
-                             int32_t* __restrict__ tile_desc, int64_t n, int32_t pt) {
-  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
-    const int nt = (cnt[x] + pt - 1) / pt;
-    for (int j = 0; j < nt; ++j) {
-      tile_desc[2 * (int64_t)(tile_off[x] + j)] = (int32_t)x;
-      tile_desc[2 * (int64_t)(tile_off[x] + j) + 1] = j * pt;
-    }
-  }
-}
 
 // Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS.
 // Keys at or past n_valid are zero-filled.
@@ -220,56 +136,98 @@ __device__ __forceinline__ void attn_block(const uint16_t* Ks, const uint16_t* V
   l = sum;
 }
 
-__global__ __launch_bounds__(256) void k_attn_nonlocal(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+// Where the gathered row `r` of a tile comes from: query i, slot s of its
+// block_idx row.
+struct TileRow {
+  int bgt, start, npos;
+  bool valid;
+  int i, s;
+};
+
+__device__ __forceinline__ TileRow tile_row(const AttnWs& ws, const Dims& D, int tile, int ps) {
+  TileRow tr;
+  tr.bgt = ws.tile_desc[2 * (int64_t)tile];
+  tr.start = ws.tile_desc[2 * (int64_t)tile + 1];
+  tr.npos = min(D.pt, ws.cnt[tr.bgt] - tr.start);
+  tr.valid = ps < tr.npos;
+  tr.i = 0;
+  tr.s = 0;
+  if (tr.valid) {
+    const int e = ws.list[ws.off[tr.bgt] + tr.start + ps];
+    tr.i = e / D.k;
+    tr.s = e % D.k;
+  }
+  return tr;
+}
+
+// Store one row's normalised partial in lane order: lane (q, half) owns 64
+// contiguous bf16 of its row, in accumulator order.
+__device__ __forceinline__ void store_partial(uint16_t* dst, const f32x16 (&o)[4], float inv) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int Dt = u >> 1, e0 = (u & 1) * 8;
+    const uint4 w = make_uint4(pack_bf16x2(o[Dt][e0 + 0] * inv, o[Dt][e0 + 1] * inv),
+                               pack_bf16x2(o[Dt][e0 + 2] * inv, o[Dt][e0 + 3] * inv),
+                               pack_bf16x2(o[Dt][e0 + 4] * inv, o[Dt][e0 + 5] * inv),
+                               pack_bf16x2(o[Dt][e0 + 6] * inv, o[Dt][e0 + 7] * inv));
+    *reinterpret_cast<uint4*>(dst + 8 * u) = w;
+  }
+}
+
+// Persistent: workgroup w owns a contiguous run of tiles; the K/V block in LDS
+// is reloaded only when the run moves to another (b, g, block), and the next
+// tile's query rows are fetched while the current tile computes.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_nonlocal(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v, AttnWs ws, Dims D) {
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
   const int64_t nbgt = (int64_t)D.B * D.h_kv * D.n_blk;
-  const int tile = blockIdx.x;
-  if (tile >= ws.tile_off[nbgt]) return;  // uniform over the workgroup
-  const int bgt = ws.tile_desc[2 * (int64_t)tile];
-  const int start = ws.tile_desc[2 * (int64_t)tile + 1];
-  const int t = bgt % D.n_blk;
-  const int bg = bgt / D.n_blk;
-  const int g = bg % D.h_kv, b = bg / D.h_kv;
-  const int npos = min(D.pt, ws.cnt[bgt] - start);
-
-  const int64_t kv0 = ((int64_t)bg * D.n_kv + (int64_t)t * kBk) * kHeadDim;
-  stage_kv(Ks, Vt, k + kv0, v + kv0, kBk);
+  const int total = ws.tile_off[nbgt];
+  const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int t0 = (int)blockIdx.x * per, t1 = min(total, t0 + per);
+  if (t0 >= t1) return;  // uniform over the workgroup
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
   const int r = wave * 32 + col;
   const int ps = r / D.G, hh = r % D.G;
-  const bool valid = ps < npos;
-  int i = 0, s = 0;
-  if (valid) {
-    const int e = ws.list[ws.off[bgt] + start + ps];
-    i = e / D.k;
-    s = e % D.k;
-  }
-  uint4 qb[8];
-  load_q_row(qb, q + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + hh) * kHeadDim, valid, half);
-  __syncthreads();
-  if (wave * 32 >= npos * D.G) return;  // no rows for this wave
 
-  f32x16 o[4];
-  float m2, l;
-  attn_block(Ks, Vt, qb, lane, D.scale_log2, false, 0, 0, o, m2, l);
-  if (!valid) return;
-  const int64_t pidx = ((((int64_t)bg * D.n_q + i) * D.k + s) * D.G + hh);
-  if (half == 0) ws.part_lse[pidx] = m2 + __log2f(l);
-  const float inv = 1.f / l;
-  uint16_t* dst = ws.part_o + pidx * kHeadDim;
-#pragma unroll
-  for (int Dt = 0; Dt < 4; ++Dt) {
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = 32 * Dt + 8 * i4 + 4 * half;
-      const uint2 w = make_uint2(pack_bf16x2(o[Dt][4 * i4 + 0] * inv, o[Dt][4 * i4 + 1] * inv),
-                                 pack_bf16x2(o[Dt][4 * i4 + 2] * inv, o[Dt][4 * i4 + 3] * inv));
-      *reinterpret_cast<uint2*>(dst + d0) = w;
+  TileRow cur = tile_row(ws, D, t0, ps);
+  uint4 qb[8], qn[8];
+  {
+    const int bg = cur.bgt / D.n_blk, g = bg % D.h_kv, b = bg / D.h_kv;
+    load_q_row(qb, q + (((int64_t)b * D.n_q + cur.i) * D.h_q + g * D.G + hh) * kHeadDim, cur.valid, half);
+  }
+  int staged = -1;
+  for (int tile = t0; tile < t1; ++tile) {
+    const int bg = cur.bgt / D.n_blk;
+    const int t = cur.bgt % D.n_blk;
+    if (cur.bgt != staged) {  // uniform: every lane reads the same descriptor
+      if (staged >= 0) __syncthreads();
+      const int64_t kv0 = ((int64_t)bg * D.n_kv + (int64_t)t * kBk) * kHeadDim;
+      stage_kv(Ks, Vt, k + kv0, v + kv0, kBk);
+      __syncthreads();
+      staged = cur.bgt;
     }
+    TileRow nxt = cur;
+    if (tile + 1 < t1) {
+      nxt = tile_row(ws, D, tile + 1, ps);
+      const int nbg = nxt.bgt / D.n_blk, ng = nbg % D.h_kv, nb = nbg / D.h_kv;
+      load_q_row(qn, q + (((int64_t)nb * D.n_q + nxt.i) * D.h_q + ng * D.G + hh) * kHeadDim, nxt.valid, half);
+    }
+    if (wave * 32 < cur.npos * D.G) {
+      f32x16 o[4];
+      float m2, l;
+      attn_block(Ks, Vt, qb, lane, D.scale_log2, false, 0, 0, o, m2, l);
+      if (cur.valid) {
+        const int64_t pidx = ((((int64_t)bg * D.n_q + cur.i) * D.k + cur.s) * D.G + hh);
+        if (half == 0) ws.part_lse[pidx] = m2 + __log2f(l);
+        store_partial(ws.part_o + pidx * kHeadDim + half * 64, o, 1.f / l);
+      }
+    }
+    cur = nxt;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) qb[u] = qn[u];
   }
 }
 
@@ -322,20 +280,23 @@ __global__ __launch_bounds__(256) void k_attn_local_merge(const uint16_t* __rest
   const float c_loc = __builtin_amdgcn_exp2f(lse_loc - lse_tot) / l;
 #pragma unroll
   for (int Dt = 0; Dt < 4; ++Dt) o[Dt] *= c_loc;
+#pragma unroll 2
   for (int s = 0; s < D.k; ++s) {
     if (!nonlocal_slot(row, s, lblk)) continue;
     const int64_t pidx = pbase + (int64_t)s * D.G;
     const float c = __builtin_amdgcn_exp2f(ws.part_lse[pidx] - lse_tot);
-    const uint16_t* src = ws.part_o + pidx * kHeadDim;
+    const uint4* src = reinterpret_cast<const uint4*>(ws.part_o + pidx * kHeadDim + half * 64);
+    uint4 w[8];
 #pragma unroll
-    for (int Dt = 0; Dt < 4; ++Dt) {
+    for (int u = 0; u < 8; ++u) w[u] = src[u];
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const uint2 w = *reinterpret_cast<const uint2*>(src + 32 * Dt + 8 * i4 + 4 * half);
-        o[Dt][4 * i4 + 0] += c * bf16_to_f32(w.x & 0xFFFFu);
-        o[Dt][4 * i4 + 1] += c * bf16_to_f32(w.x >> 16);
-        o[Dt][4 * i4 + 2] += c * bf16_to_f32(w.y & 0xFFFFu);
-        o[Dt][4 * i4 + 3] += c * bf16_to_f32(w.y >> 16);
+    for (int u = 0; u < 8; ++u) {
+      const int Dt = u >> 1, e0 = (u & 1) * 8;
+      const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int h2 = 0; h2 < 4; ++h2) {
+        o[Dt][e0 + 2 * h2] += c * __uint_as_float(x[h2] << 16);
+        o[Dt][e0 + 2 * h2 + 1] += c * __uint_as_float(x[h2] & 0xFFFF0000u);
       }
     }
   }
@@ -353,29 +314,26 @@ __global__ __launch_bounds__(256) void k_attn_local_merge(const uint16_t* __rest
     lse_out[((int64_t)b * D.h_q + g * D.G + hh) * D.n_q + i] = lse_tot * 0.69314718055994531f;
 }
 
-unsigned grid_for(int64_t n, int threads) {
-  int64_t g = (n + threads - 1) / threads;
-  if (g < 1) g = 1;
-  if (g > 65536) g = 65536;
-  return (unsigned)g;
+int persistent_grid() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
+  }
+  return 2 * cus;  // two 68 KB-LDS workgroups fit one CU
 }
 
 }  // namespace
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream) {
-  const int64_t nbgt = (int64_t)D.B * D.h_kv * D.n_blk;
-  const int64_t nrows = (int64_t)D.B * D.h_kv * D.n_q;
-  // cnt and cursor are adjacent in the workspace: clear both with one fill kernel
-  hipLaunchKernelGGL(k_fill_zero, dim3(grid_for(2 * nbgt, 256)), dim3(256), 0, stream, ws.cnt, 2 * nbgt);
-  hipLaunchKernelGGL(k_plan_count, dim3(grid_for(nrows, 256)), dim3(256), 0, stream, block_idx, ws.cnt, D);
-  hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, stream, ws.cnt, ws.off, ws.tile_off, nbgt, D.pt);
-  hipLaunchKernelGGL(k_plan_fill, dim3(grid_for(nrows, 256)), dim3(256), 0, stream, block_idx, ws.cursor, ws.off,
-                     ws.list, D);
-  hipLaunchKernelGGL(k_plan_tiles, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.cnt, ws.tile_off,
-                     ws.tile_desc, nbgt, D.pt);
-  if (ws.max_tiles > 0)
-    hipLaunchKernelGGL(k_attn_nonlocal, dim3((unsigned)ws.max_tiles), dim3(256), 0, stream, q, k, v, ws, D);
+  hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
+  if (e != hipSuccess) return e;
+  const int grid = (int)std::min<int64_t>(persistent_grid(), ws.max_tiles);
+  hipLaunchKernelGGL(k_attn_nonlocal, dim3(grid), dim3(256), 0, stream, q, k, v, ws, D);
   const int64_t a0 = D.offset / D.pt;
   const int64_t a1 = (D.offset + D.n_q - 1) / D.pt;
   hipLaunchKernelGGL(k_attn_local_merge, dim3((unsigned)(a1 - a0 + 1), (unsigned)(D.B * D.h_kv)), dim3(256), 0,

@@ -33,6 +33,11 @@ EDGE = [
     synth.Workload("edge_one_token", 2, 1, 1, 8, 1, seed=2009),
     # a group size that does not divide 128 (96-row tiles)
     synth.Workload("edge_g3", 1, 1200, 1200, 6, 2, topk=6, seed=2010),
+    # a few query rows per sequence (query-outer attention, small-row index kernel)
+    synth.Workload("edge_rows_nq4", 2, 4, 3000, 16, 2, topk=6, seed=2012),
+    synth.Workload("edge_rows_g16", 1, 2, 2000, 32, 2, topk=5, seed=2013),
+    # decode with wide groups (gather-plan path)
+    synth.Workload("edge_decode_g32", 2, 1, 3000, 64, 2, topk=7, seed=2014),
     # planted blocks in a small prefill
     synth.Workload("edge_planted", 1, 4096, 4096, 16, 2, topk=6, seed=2011, plant_m=3,
                    plant_alpha=2 * 128 ** 0.25, plant_beta=2 * 128 ** 0.25),
@@ -144,3 +149,44 @@ def test_forward_is_deterministic():
     assert torch.equal(a["fwd"]["out"].view(torch.int16), b["fwd"]["out"].view(torch.int16))
     assert torch.equal(a["fwd"]["lse"], b["fwd"]["lse"])
     _release()
+
+
+@pytest.mark.parametrize("w", [synth.Workload("unlisted_prefill", 1, 1500, 1500, 16, 2, topk=5, seed=2200),
+                               synth.Workload("unlisted_decode", 4, 1, 4000, 16, 2, topk=5, seed=2201)],
+                         ids=["gather-plan", "query-outer"])
+def test_local_block_attended_when_unlisted(w):
+    """msa_sparse_attn_fwd attends the local block even when a row omits it."""
+    import torch
+    import block_sparse_long_qk_amd as msa
+    import oracle
+    res = run_gpu(w, with_forward=False)
+    bidx = res["block_idx"].clone()
+    pos = w.offset + torch.arange(w.n_q, device=bidx.device)
+    local = (pos // w.block_size).view(1, 1, -1, 1)
+    bidx = torch.where(bidx == local, torch.full_like(bidx, -1), bidx)
+    # keep rows ascending with the -1 padding at the tail
+    bidx = torch.where(bidx < 0, torch.full_like(bidx, 1 << 30), bidx).sort(dim=-1).values
+    bidx = torch.where(bidx == (1 << 30), torch.full_like(bidx, -1), bidx).contiguous()
+    p = problem(w)
+    x = res["inputs"]
+    out = torch.empty_like(res["out"])
+    ws = torch.empty(max(msa.workspace_size(p, msa.OP_SPARSE_ATTN), 256), dtype=torch.uint8, device="cuda")
+    msa.sparse_attn_fwd(p, x["q"], x["k"], x["v"], bidx, out, None, ws)
+    torch.cuda.synchronize()
+    # same block set as the listed rows (the merge order may differ in the last bit)
+    assert torch.max(torch.abs(out.float() - res["out"].float())).item() <= 1e-2
+    # and it agrees with the oracle on S + {local}
+    st = Stats()
+    rows = np.arange(w.n_q) if w.n_q <= 64 else np.arange(0, w.n_q, 7)
+    for b in range(w.batch):
+        for g in range(w.h_kv):
+            xr = oracle.inputs_for_rows(w, b, g, rows)
+            sel = bidx[b, g].cpu().numpy()[rows]
+            sel_full = np.concatenate([sel, (xr["pos"] // w.block_size)[:, None]], axis=1).astype(np.int32)
+            sel_full = np.sort(np.where(sel_full < 0, 1 << 30, sel_full), axis=1)
+            sel_full = np.where(sel_full == (1 << 30), -1, sel_full).astype(np.int32)
+            K, V = oracle.kv_for_blocks(w, b, g, sel_full)
+            ref, _ = oracle.attend(xr["q"], xr["pos"], sel_full, K, V, w.block_size, w.scale)
+            got = out[b].index_select(0, torch.from_numpy(rows).cuda())[:, g * w.group:(g + 1) * w.group].float()
+            st.add_out(got.cpu().numpy(), ref)
+    st.check()
