@@ -151,6 +151,13 @@ def main():
     import synth
     torch.cuda.init()
     stream = torch.cuda.current_stream()
+    # copy probe: 1 GiB device-to-device copy of known size, so that HBM byte
+    # counters (FETCH_SIZE, WRITE_SIZE) can be scaled against a known transfer
+    probe_src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    probe_dst = torch.empty_like(probe_src)
+    probe_dst.copy_(probe_src)
+    torch.cuda.synchronize()
+    del probe_src, probe_dst
     w = synth.WORKLOADS[args.workload]
     g = gpu_leg(w, args.steps, args.warmup, stream)
     f_idx, f_attn, topk_bytes, _ = algorithmic_work(w)

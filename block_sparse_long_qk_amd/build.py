@@ -20,6 +20,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
          # keep the compiler from emitting packed fp32 arithmetic
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # inputs are NaN-free by contract: max/min need no NaN quieting
+         "-fno-honor-nans",
+         # MFMA results in VGPRs (no AGPR round trips before the VALU epilogues)
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

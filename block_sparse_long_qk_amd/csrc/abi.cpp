@@ -40,7 +40,9 @@ msa_status derive(const msa_problem* p, Dims* D) {
   int pt = 1;
   while (pt * 2 * G <= msa::kTileRows) pt *= 2;
   // launch-grid limits: y/z dims of 65535, 2^32 threads along x
-  const int64_t max_tiles = (rows * p->topk + pt - 1) / pt + (int64_t)p->batch * p->h_kv * n_blk;
+  const int64_t n_groups = ((int64_t)p->n_q + msa::kChunkRows * msa::kGroupChunks - 1) /
+                           (msa::kChunkRows * msa::kGroupChunks);
+  const int64_t max_tiles = (rows * p->topk + pt - 1) / pt + (int64_t)p->batch * p->h_kv * n_groups * n_blk;
   if ((int64_t)p->batch * p->h_kv > 65535 || max_tiles * 256 >= (int64_t(1) << 32) ||
       rows * 64 >= (int64_t(1) << 32) || rows > 65535LL * 65535LL)
     return MSA_ERR_UNSUPPORTED;
@@ -63,7 +65,7 @@ msa_status derive(const msa_problem* p, Dims* D) {
 
 // Carve the sparse-attention workspace out of `base` (nullptr: sizing only).
 size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
-  const int64_t nbgt = (int64_t)D.B * D.h_kv * D.n_blk;
+  const int64_t nbgt = msa::plan_bins(D);
   const int64_t slots = (int64_t)D.B * D.h_kv * D.n_q * D.k;
   const int64_t max_tiles = (slots + D.pt - 1) / D.pt + nbgt;
   size_t at = 0;
@@ -72,7 +74,7 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
     at += round256(bytes);
     return p;
   };
-  char* hist = take(sizeof(int32_t) * nbgt * msa::plan_chunks(D));
+  char* hist = take(sizeof(int32_t) * (int64_t)D.B * D.h_kv * D.n_blk * msa::plan_chunks(D));
   char* cnt = take(sizeof(int32_t) * nbgt);
   char* bsum = take(sizeof(int32_t) * 2 * msa::plan_scan_blocks(D));
   char* off = take(sizeof(int32_t) * (nbgt + 1));
@@ -92,6 +94,8 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
     ws->part_lse = reinterpret_cast<float*>(part_lse);
     ws->part_o = reinterpret_cast<uint16_t*>(part_o);
     ws->max_tiles = max_tiles;
+    ws->n_bins = nbgt;
+    ws->n_groups = (int32_t)msa::plan_groups(D);
   }
   return at;
 }
@@ -203,9 +207,14 @@ msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const
   const size_t pb = pooled_bytes(D);
   if (pb + attn_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
   float* pooled = static_cast<float*>(workspace);
-  hipError_t e = run_index(D, index_q, index_k, pooled, stream);
-  if (e != hipSuccess) return MSA_ERR_HIP;
-  e = msa::launch_block_topk(pooled, block_idx, D, stream);
+  hipError_t e;
+  if (!msa::use_index_small(D) && msa::index_topk_fusable(D)) {
+    e = msa::launch_index_topk(static_cast<const uint16_t*>(index_q), static_cast<const uint16_t*>(index_k),
+                               block_idx, D, stream);
+  } else {
+    e = run_index(D, index_q, index_k, pooled, stream);
+    if (e == hipSuccess) e = msa::launch_block_topk(pooled, block_idx, D, stream);
+  }
   if (e != hipSuccess) return MSA_ERR_HIP;
   return hip_status(run_attention(D, q, k, v, block_idx, out, lse, static_cast<char*>(workspace) + pb, stream));
 }

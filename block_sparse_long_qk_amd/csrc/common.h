@@ -10,7 +10,9 @@ constexpr int kHeadDim = 128;   // main-branch head dim
 constexpr int kMaxTopk = 64;    // one selection per wavefront lane at most
 constexpr int kTileRows = 128;  // query rows (positions x heads) per attention tile
 constexpr int kChunkRows = 1024;   // query rows per gather-plan workgroup
+constexpr int kGroupChunks = 8;    // plan chunks per gather-list group (8192 query rows)
 constexpr int kMaxPlanBlocks = 16384;  // LDS histogram bins of the gather plan (n_kv <= 2M)
+constexpr int kPoolStage = 8;          // pooled scores a lane stages before one 32-byte store
 constexpr int kRowsMaxQ = 4;           // query rows per sequence up to which attention runs query-outer
 constexpr int kRowsPart = 16 * kHeadDim + 16;  // floats per query-outer partial: o[16][d], lse[16]
 
@@ -29,15 +31,17 @@ struct Dims {
 // Workspace carve-up of the sparse attention stage (device pointers).
 struct AttnWs {
   int32_t* hist;       // [B*h_kv][n_ch][n_blk] per-chunk block histograms, then chunk offsets
-  int32_t* cnt;        // [B*h_kv*n_blk]   gathered query rows per (b, g, block)
+  int32_t* cnt;        // [bins]   gathered rows per bin (b, g, query group, block)
   int32_t* bsum;       // [2 * scan blocks] block sums of the two-level scan
-  int32_t* off;        // [B*h_kv*n_blk+1] exclusive scan of cnt
-  int32_t* tile_off;   // [B*h_kv*n_blk+1] exclusive scan of ceil(cnt / pt); last = tile count
-  int32_t* list;       // [edges]          row-slot ids (i * k + s), grouped by (b, g, block)
-  int32_t* tile_desc;  // [max_tiles][2]   (b*h_kv*n_blk + block, first list entry)
+  int32_t* off;        // [bins+1] exclusive scan of cnt
+  int32_t* tile_off;   // [bins+1] exclusive scan of ceil(cnt / pt); last = tile count
+  int32_t* list;       // [edges]  row-slot ids (i * k + s), grouped by bin
+  int32_t* tile_desc;  // [max_tiles][2]   (bin, first list entry)
   float* part_lse;     // [B*h_kv*n_q*k][G]     base-2 log-sum-exp of each partial
   uint16_t* part_o;    // [B*h_kv*n_q*k][G][d]  normalised partial outputs, bf16, lane order
   int64_t max_tiles;
+  int64_t n_bins;      // B * h_kv * query groups * n_blk
+  int32_t n_groups;    // query groups per (b, g)
 };
 
 // Is slot s of a block_idx row a non-local block with a partial of its own?
@@ -56,14 +60,13 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(uint4 a, uint4 b, f32x16 c) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }

@@ -3,20 +3,23 @@
 // the query positions that selected each one).
 //
 // Input: block_idx rows (one per sequence, group, query).  Output: for every
-// (sequence b, group g, block t) the list of row-slot ids i*k + s that picked t
-// as a non-local block, the lists stored back to back in (b, g, t) order, and a
-// tile list cutting each list into runs of `pt` query positions.
+// bin (sequence b, group g, query chunk group c of kGroupRows rows, block t)
+// the list of row-slot ids i*k + s of the rows in c that picked t as a
+// non-local block, the lists stored back to back in (b, g, c, t) order, and a
+// tile list cutting each list into runs of `pt` query positions.  Binning by
+// chunk group keeps the query rows that consecutive tiles gather within
+// kGroupRows positions.
 //
 // A counting sort without global atomics:
 //   1. hist:  one workgroup per chunk of kChunkRows rows of one (b, g) counts its
 //             entries per block in LDS and writes the chunk's histogram;
-//   2. colscan: per (b, g, t), exclusive scan of the chunk histograms (the chunk's
-//             start inside the block's list) and the list length;
+//   2. colscan: per bin, exclusive scan of its chunks' histograms (the chunk's
+//             start inside the list) and the list length;
 //   3. scan:  exclusive scans of the list lengths and of their tile counts over
-//             all (b, g, t) (two-level: block sums, one-workgroup scan, apply);
+//             all bins (two-level: block sums, one-workgroup scan, apply);
 //   4. fill:  each chunk workgroup re-reads its rows and scatters row-slot ids
 //             with LDS cursors;
-//   5. tiles: one descriptor (b*h_kv*n_blk + t, first entry) per tile.
+//   5. tiles: one descriptor (bin, first entry) per tile.
 // Entries inside one list appear in no fixed order; every row's attention is
 // independent of the other rows of its tile, so results do not depend on it.
 #include "launch.h"
@@ -44,13 +47,18 @@ __global__ __launch_bounds__(256) void k_plan_hist(const int32_t* __restrict__ b
   for (int t = threadIdx.x; t < D.n_blk; t += blockDim.x) dst[t] = lh[t];
 }
 
-// hist[bg][ch][t] <- exclusive prefix over ch; cnt[bg][t] <- total.
+// hist[bg][ch][t] <- exclusive prefix over the chunks of ch's group;
+// cnt[(bg*n_cg + cg)*n_blk + t] <- the group's total.
 __global__ void k_plan_colscan(int32_t* __restrict__ hist, int32_t* __restrict__ cnt, Dims D, int32_t n_ch) {
-  const int64_t nbgt = (int64_t)D.B * D.h_kv * D.n_blk;
-  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < nbgt; x += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t bg = x / D.n_blk, t = x % D.n_blk;
+  const int n_cg = (n_ch + kGroupChunks - 1) / kGroupChunks;
+  const int64_t nbins = (int64_t)D.B * D.h_kv * n_cg * D.n_blk;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < nbins; x += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = x % D.n_blk;
+    const int64_t cg = (x / D.n_blk) % n_cg;
+    const int64_t bg = x / ((int64_t)D.n_blk * n_cg);
     int32_t acc = 0;
-    for (int ch = 0; ch < n_ch; ++ch) {
+    const int ch1 = min(n_ch, (int)(cg + 1) * kGroupChunks);
+    for (int ch = (int)cg * kGroupChunks; ch < ch1; ++ch) {
       int32_t* h = hist + (bg * n_ch + ch) * D.n_blk + t;
       const int32_t v = *h;
       *h = acc;
@@ -157,8 +165,9 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ b
                                                    int32_t* __restrict__ list, Dims D, int32_t n_ch) {
   extern __shared__ int32_t cursor[];  // [n_blk]
   const int ch = blockIdx.x, bg = blockIdx.y;
+  const int n_cg = (n_ch + kGroupChunks - 1) / kGroupChunks;
   const int32_t* h = hist + ((int64_t)bg * n_ch + ch) * D.n_blk;
-  const int32_t* o = off + (int64_t)bg * D.n_blk;
+  const int32_t* o = off + ((int64_t)bg * n_cg + ch / kGroupChunks) * D.n_blk;
   for (int t = threadIdx.x; t < D.n_blk; t += blockDim.x) cursor[t] = o[t] + h[t];
   __syncthreads();
   const int i0 = ch * kChunkRows, i1 = min(D.n_q, i0 + kChunkRows);
@@ -193,12 +202,14 @@ unsigned grid_for(int64_t n, int threads) {
 
 int64_t plan_chunks(const Dims& D) { return (D.n_q + kChunkRows - 1) / kChunkRows; }
 
-int64_t plan_scan_blocks(const Dims& D) {
-  return ((int64_t)D.B * D.h_kv * D.n_blk + kScanPer - 1) / kScanPer;
-}
+int64_t plan_groups(const Dims& D) { return (plan_chunks(D) + kGroupChunks - 1) / kGroupChunks; }
+
+int64_t plan_bins(const Dims& D) { return (int64_t)D.B * D.h_kv * plan_groups(D) * D.n_blk; }
+
+int64_t plan_scan_blocks(const Dims& D) { return (plan_bins(D) + kScanPer - 1) / kScanPer; }
 
 hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const Dims& D, hipStream_t stream) {
-  const int64_t nbgt = (int64_t)D.B * D.h_kv * D.n_blk;
+  const int64_t nbgt = plan_bins(D);
   const int n_ch = (int)plan_chunks(D);
   const int nb = (int)plan_scan_blocks(D);
   const size_t lds = sizeof(int32_t) * D.n_blk;

@@ -29,12 +29,46 @@ struct IdxCfg {
   static constexpr int CPR = DIDX / 8;              // chunks per key row
 };
 
-template <int DIDX>
+// Sort the KK selected block ids of a lane ascending (bitonic network over a
+// power-of-two padding; unused slots carry INT_MAX).
+template <int KK>
+__device__ __forceinline__ void sort_ids(int (&ti)[KK]) {
+  constexpr int N = KK <= 8 ? 8 : 16;
+  int x[N];
+#pragma unroll
+  for (int s = 0; s < N; ++s) x[s] = s < KK ? ti[s] : 0x7FFFFFFF;
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int s = 0; s < N; ++s) {
+        const int o = s ^ stride;
+        if (o > s) {
+          const bool asc = (s & size) == 0;
+          const int lo = min(x[s], x[o]), hi = max(x[s], x[o]);
+          x[s] = asc ? lo : hi;
+          x[o] = asc ? hi : lo;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < KK; ++s) ti[s] = x[s];
+}
+
+// KK == 0: write the pooled scores.  KK > 0: the launch covers every block of
+// every row (no key split); each lane keeps its row's best KK non-local blocks
+// by (score desc, index asc) in registers and writes the block_idx row (k = KK+1)
+// exactly as the standalone top-k does from the same fp32 scores.
+template <int DIDX, int KK>
 __global__ __launch_bounds__(256) void k_index_scores(const uint16_t* __restrict__ iq,
                                                       const uint16_t* __restrict__ ik, float* __restrict__ pooled,
-                                                      Dims D, int32_t blocks_per_split) {
+                                                      int32_t* __restrict__ block_idx, Dims D,
+                                                      int32_t blocks_per_split) {
   using C = IdxCfg<DIDX>;
   __shared__ __align__(16) uint16_t lds[2][kBk * C::PITCH];
+  __shared__ __align__(16) float pstage[KK == 0 ? 4 : 1][64][kPoolStage];  // per-lane pooled staging
   const float NEG_INF = -__builtin_huge_valf();
 
   const int b = blockIdx.z;
@@ -73,14 +107,21 @@ __global__ __launch_bounds__(256) void k_index_scores(const uint16_t* __restrict
     }
   }
 
-  // The row this lane writes: lane < 32 -> n-tile 0 column `lane`, else n-tile 1.
+  // The row this lane owns: lane < 32 -> n-tile 0 column `lane`, else n-tile 1.
   const int r_out = wrow0 + lane;
-  int64_t out_base = -1;
+  int64_t out_row = -1;  // (b, g, i) row index
   int l_out = -1;
   if (r_out < rows_total) {
     const int i = r_out / D.h_kv, g = r_out % D.h_kv;
-    out_base = (((int64_t)b * D.h_kv + g) * D.n_q + i) * D.n_blk;
+    out_row = ((int64_t)b * D.h_kv + g) * D.n_q + i;
     l_out = (int)((D.offset + i) / kBk);
+  }
+  float tv[KK > 0 ? KK : 1];
+  int ti[KK > 0 ? KK : 1];
+#pragma unroll
+  for (int s = 0; s < (KK > 0 ? KK : 1); ++s) {
+    tv[s] = NEG_INF;
+    ti[s] = -1;
   }
 
   const uint16_t* ikb = ik + (int64_t)b * D.n_kv * DIDX;
@@ -122,48 +163,138 @@ __global__ __launch_bounds__(256) void k_index_scores(const uint16_t* __restrict
           a1 = mfma_32x32x16(a, qb[1][ks], a1);
         }
         if (need_mask) {
+          // key (t*Bk + 32*mt + row) is visible to column position p iff row <= p - (t*Bk + 32*mt)
+          const int64_t base = (int64_t)t * kBk + 32 * mt;
+          const int rel0 = (int)max<int64_t>(-1, min<int64_t>(64, pc[0] - base)) - 4 * half;
+          const int rel1 = (int)max<int64_t>(-1, min<int64_t>(64, pc[1] - base)) - 4 * half;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int64_t key = (int64_t)t * kBk + 32 * mt + acc_row(e, lane);
-            if (key > pc[0]) a0[e] = NEG_INF;
-            if (key > pc[1]) a1[e] = NEG_INF;
+            const int row = 8 * (e >> 2) + (e & 3);
+            if (row > rel0) a0[e] = NEG_INF;
+            if (row > rel1) a1[e] = NEG_INF;
           }
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          run0 = fmaxf(run0, a0[e]);
-          run1 = fmaxf(run1, a1[e]);
+        for (int e = 0; e < 16; e += 2) {
+          run0 = fmaxf(run0, fmaxf(a0[e], a0[e + 1]));
+          run1 = fmaxf(run1, fmaxf(a1[e], a1[e + 1]));
         }
       }
       run0 = fmaxf(run0, wave_xor32(run0));
       run1 = fmaxf(run1, wave_xor32(run1));
       const float v = half ? run1 : run0;
-      if (out_base >= 0 && t <= l_out) pooled[out_base + t] = v;
+      if constexpr (KK == 0) {
+        // stage per lane; flush kPoolStage consecutive blocks of the row at once
+        const int j = (t - t_begin) % kPoolStage;
+        pstage[wave][lane][j] = v;
+        if ((j == kPoolStage - 1 || t == t_end - 1) && out_row >= 0) {
+          const int tb = t - j;
+          const int n = min(j + 1, l_out - tb + 1);
+          float* dst = pooled + out_row * D.n_blk + tb;
+          if (n == kPoolStage && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+            const float4* srcv = reinterpret_cast<const float4*>(&pstage[wave][lane][0]);
+#pragma unroll
+            for (int u = 0; u < kPoolStage / 4; ++u) reinterpret_cast<float4*>(dst)[u] = srcv[u];
+          } else {
+            for (int u = 0; u < n; ++u) dst[u] = pstage[wave][lane][u];
+          }
+        }
+      } else {
+        // running top-KK of the non-local blocks (t < l_out); an equal score
+        // never displaces an earlier block
+        if (t < l_out && v > tv[KK - 1]) {
+          bool ge[KK];
+#pragma unroll
+          for (int s = 0; s < KK; ++s) ge[s] = tv[s] >= v;
+#pragma unroll
+          for (int s = KK - 1; s >= 0; --s) {
+            const bool here = s == 0 || ge[s - 1];
+            const float sv = here ? v : tv[s > 0 ? s - 1 : 0];
+            const int si = here ? t : ti[s > 0 ? s - 1 : 0];
+            tv[s] = ge[s] ? tv[s] : sv;
+            ti[s] = ge[s] ? ti[s] : si;
+          }
+        }
+      }
     }
     if (t + 1 < t_end) store_block(buf ^ 1);
     __syncthreads();
+  }
+
+  if constexpr (KK > 0) {
+    if (out_row >= 0) {
+      int32_t* dst = block_idx + out_row * (KK + 1);
+      if (l_out <= KK) {  // every visible block is kept
+#pragma unroll
+        for (int s = 0; s <= KK; ++s) dst[s] = s <= l_out ? s : -1;
+      } else {
+        sort_ids<KK>(ti);
+#pragma unroll
+        for (int s = 0; s < KK; ++s) dst[s] = ti[s];
+        dst[KK] = l_out;
+      }
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_index_scores(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
-                               hipStream_t stream) {
-  const int64_t rows_total = (int64_t)D.n_q * D.h_kv;
-  const int row_tiles = (int)((rows_total + 255) / 256);
-  const int t_max = (int)((D.offset + D.n_q - 1) / kBk) + 1;  // blocks the last row needs
-  // Split the key range when there are too few row tiles to fill the chip.
-  const int64_t want = 2048;
+// Key-range splits so that row tiles x splits fill the chip (two workgroups per CU).
+static int index_splits(const Dims& D, int row_tiles, int t_max, int* per) {
+  const int64_t want = 512;
   int64_t nsplit = (want + (int64_t)row_tiles * D.B - 1) / ((int64_t)row_tiles * D.B);
   if (nsplit < 1) nsplit = 1;
   if (nsplit > t_max) nsplit = t_max;
-  const int per = (int)((t_max + nsplit - 1) / nsplit);
-  nsplit = (t_max + per - 1) / per;
-  dim3 grid(row_tiles, (unsigned)nsplit, D.B);
+  int p = (int)((t_max + nsplit - 1) / nsplit);
+  p = (p + kPoolStage - 1) / kPoolStage * kPoolStage;  // splits start on a staging boundary
+  *per = p;
+  return (int)((t_max + p - 1) / p);
+}
+
+static void index_grid(const Dims& D, dim3* grid, int* per) {
+  const int64_t rows_total = (int64_t)D.n_q * D.h_kv;
+  const int row_tiles = (int)((rows_total + 255) / 256);
+  const int t_max = (int)((D.offset + D.n_q - 1) / kBk) + 1;  // blocks the last row needs
+  const int nsplit = index_splits(D, row_tiles, t_max, per);
+  *grid = dim3(row_tiles, (unsigned)nsplit, D.B);
+}
+
+hipError_t launch_index_scores(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
+                               hipStream_t stream) {
+  dim3 grid;
+  int per;
+  index_grid(D, &grid, &per);
   if (D.d_idx == 128)
-    hipLaunchKernelGGL(k_index_scores<128>, grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+    hipLaunchKernelGGL((k_index_scores<128, 0>), grid, dim3(256), 0, stream, index_q, index_k, pooled, nullptr, D,
+                       per);
   else
-    hipLaunchKernelGGL(k_index_scores<64>, grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+    hipLaunchKernelGGL((k_index_scores<64, 0>), grid, dim3(256), 0, stream, index_q, index_k, pooled, nullptr, D,
+                       per);
+  return hipGetLastError();
+}
+
+bool index_topk_fusable(const Dims& D) {
+  if (D.k != 8 && D.k != 16) return false;
+  dim3 grid;
+  int per;
+  index_grid(D, &grid, &per);
+  return grid.y == 1;
+}
+
+hipError_t launch_index_topk(const uint16_t* index_q, const uint16_t* index_k, int32_t* block_idx, const Dims& D,
+                             hipStream_t stream) {
+  dim3 grid;
+  int per;
+  index_grid(D, &grid, &per);
+#define MSA_IDX_TOPK(DI, KK)                                                                                      \
+  hipLaunchKernelGGL((k_index_scores<DI, KK>), grid, dim3(256), 0, stream, index_q, index_k, nullptr, block_idx, D, \
+                     per)
+  if (D.d_idx == 128) {
+    if (D.k == 16) MSA_IDX_TOPK(128, 15); else MSA_IDX_TOPK(128, 7);
+  } else {
+    if (D.k == 16) MSA_IDX_TOPK(64, 15); else MSA_IDX_TOPK(64, 7);
+  }
+#undef MSA_IDX_TOPK
   return hipGetLastError();
 }
 

@@ -11,6 +11,12 @@ namespace msa {
 hipError_t launch_index_scores(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
                                hipStream_t stream);
 
+// Index scores with the block top-k fused into the epilogue (no pooled
+// round-trip); possible when one launch covers every block of every row.
+bool index_topk_fusable(const Dims& D);
+hipError_t launch_index_topk(const uint16_t* index_q, const uint16_t* index_k, int32_t* block_idx, const Dims& D,
+                             hipStream_t stream);
+
 // Exp-free block top-k with the forced local block: block_idx[B][h_kv][n_q][k].
 hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims& D, hipStream_t stream);
 
@@ -18,6 +24,8 @@ hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims
 hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const Dims& D, hipStream_t stream);
 int64_t plan_chunks(const Dims& D);       // chunk workgroups per (b, g)
 int64_t plan_scan_blocks(const Dims& D);  // workgroups of the two-level scan
+int64_t plan_groups(const Dims& D);       // query groups (kGroupChunks chunks) per (b, g)
+int64_t plan_bins(const Dims& D);         // (b, g, query group, block) bins
 
 // Gather plan + gathered non-local tiles + local tiles with the merge.
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,

@@ -32,6 +32,8 @@ namespace msa {
 namespace {
 
 constexpr int KP = kHeadDim + 8;   // LDS pitch of K rows (bf16): 16-byte pad
+constexpr int kXcds = 8;           // XCDs of an MI355X; workgroups are dealt round-robin over them
+constexpr int kRun = 8;            // consecutive tiles one workgroup takes before moving on
 constexpr int VP = kBk + 4;        // LDS pitch of V^T rows (bf16): 8-byte pad
 
 // Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS.
@@ -92,12 +94,14 @@ __device__ __forceinline__ void attn_block(const uint16_t* Ks, const uint16_t* V
     for (int ks = 0; ks < 8; ++ks) s[T] = mfma_32x32x16(*reinterpret_cast<const uint4*>(krow + 16 * ks), qb[ks], s[T]);
   }
   float mx = NEG_INF;
+  // key key0 + 32*T + row is visible iff 32*T + row <= p - key0
+  const int rel = (masked ? (int)max<int64_t>(-1, min<int64_t>(kBk, p - key0)) : kBk) - 4 * half;
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float x = s[T][e] * scale_log2;
-      if (masked && key0 + 32 * T + acc_row(e, lane) > p) x = NEG_INF;
+      if (32 * T + 8 * (e >> 2) + (e & 3) > rel) x = NEG_INF;
       s[T][e] = x;
       mx = fmaxf(mx, x);
     }
@@ -174,45 +178,67 @@ __device__ __forceinline__ void store_partial(uint16_t* dst, const f32x16 (&o)[4
   }
 }
 
-// Persistent: workgroup w owns a contiguous run of tiles; the K/V block in LDS
-// is reloaded only when the run moves to another (b, g, block), and the next
-// tile's query rows are fetched while the current tile computes.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_nonlocal(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ v, AttnWs ws, Dims D) {
+// Persistent and XCD-aware.  Workgroup w runs on XCD w % kXcds (the hardware
+// deals workgroups round-robin over the XCDs); XCD x owns the contiguous
+// x-th slice of the tile list, and its workgroups walk that slice in runs of
+// kRun consecutive tiles (same (b, g, group, block) as a rule), run r going to
+// the workgroup r % (grid / kXcds).  So the K/V block in LDS is reused across
+// a run, concurrent workgroups of one XCD share K/V blocks through its L2, and
+// the query rows all XCDs gather at a time come from at most kXcds chunk groups
+// of queries.  The next tile's query rows are fetched while the current tile
+// computes.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_nonlocal(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, AttnWs ws,
+    Dims D) {
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
-  const int64_t nbgt = (int64_t)D.B * D.h_kv * D.n_blk;
-  const int total = ws.tile_off[nbgt];
-  const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int t0 = (int)blockIdx.x * per, t1 = min(total, t0 + per);
-  if (t0 >= t1) return;  // uniform over the workgroup
+  const int total = ws.tile_off[ws.n_bins];
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = gridDim.x / kXcds;
+  const int lo = (int)((int64_t)total * xcd / kXcds), hi = (int)((int64_t)total * (xcd + 1) / kXcds);
+  const int stride = per_xcd * kRun;  // >= kRun
+  int run_start = lo + slot * kRun;
+  int tile = run_start;
+  if (tile >= hi) return;  // uniform over the workgroup
+  int run_end = min(run_start + kRun, hi);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
   const int r = wave * 32 + col;
   const int ps = r / D.G, hh = r % D.G;
+  const int64_t bins_per_bg = (int64_t)ws.n_groups * D.n_blk;
 
-  TileRow cur = tile_row(ws, D, t0, ps);
+  TileRow cur = tile_row(ws, D, tile, ps);
   uint4 qb[8], qn[8];
   {
-    const int bg = cur.bgt / D.n_blk, g = bg % D.h_kv, b = bg / D.h_kv;
+    const int bg = (int)(cur.bgt / bins_per_bg), g = bg % D.h_kv, b = bg / D.h_kv;
     load_q_row(qb, q + (((int64_t)b * D.n_q + cur.i) * D.h_q + g * D.G + hh) * kHeadDim, cur.valid, half);
   }
-  int staged = -1;
-  for (int tile = t0; tile < t1; ++tile) {
-    const int bg = cur.bgt / D.n_blk;
+  int staged_bg = -1, staged_t = -1;
+  while (tile < hi) {
+    const int bg = (int)(cur.bgt / bins_per_bg);
     const int t = cur.bgt % D.n_blk;
-    if (cur.bgt != staged) {  // uniform: every lane reads the same descriptor
-      if (staged >= 0) __syncthreads();
+    if (bg != staged_bg || t != staged_t) {  // uniform: every lane reads the same descriptor
+      if (staged_bg >= 0) __syncthreads();
       const int64_t kv0 = ((int64_t)bg * D.n_kv + (int64_t)t * kBk) * kHeadDim;
       stage_kv(Ks, Vt, k + kv0, v + kv0, kBk);
       __syncthreads();
-      staged = cur.bgt;
+      staged_bg = bg;
+      staged_t = t;
+    }
+    // the tile after this one: the next of the run, else the start of this
+    // workgroup's next run (strictly increasing, so the loop ends at hi)
+    int nt, n_run_start = run_start, n_run_end = run_end;
+    if (tile + 1 < run_end) {
+      nt = tile + 1;
+    } else {
+      n_run_start = run_start + stride;
+      nt = n_run_start < hi ? n_run_start : hi;
+      n_run_end = min(n_run_start + kRun, hi);
     }
     TileRow nxt = cur;
-    if (tile + 1 < t1) {
-      nxt = tile_row(ws, D, tile + 1, ps);
-      const int nbg = nxt.bgt / D.n_blk, ng = nbg % D.h_kv, nb = nbg / D.h_kv;
+    if (nt < hi) {
+      nxt = tile_row(ws, D, nt, ps);
+      const int nbg = (int)(nxt.bgt / bins_per_bg), ng = nbg % D.h_kv, nb = nbg / D.h_kv;
       load_q_row(qn, q + (((int64_t)nb * D.n_q + nxt.i) * D.h_q + ng * D.G + hh) * kHeadDim, nxt.valid, half);
     }
     if (wave * 32 < cur.npos * D.G) {
@@ -225,6 +251,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         store_partial(ws.part_o + pidx * kHeadDim + half * 64, o, 1.f / l);
       }
     }
+    tile = nt;
+    run_start = n_run_start;
+    run_end = n_run_end;
     cur = nxt;
 #pragma unroll
     for (int u = 0; u < 8; ++u) qb[u] = qn[u];
@@ -314,7 +343,7 @@ __global__ __launch_bounds__(256) void k_attn_local_merge(const uint16_t* __rest
     lse_out[((int64_t)b * D.h_q + g * D.G + hh) * D.n_q + i] = lse_tot * 0.69314718055994531f;
 }
 
-int persistent_grid() {
+int persistent_grid() {  // a multiple of kXcds
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, n = 0;
@@ -323,7 +352,7 @@ int persistent_grid() {
       n = 256;
     cus = n;
   }
-  return 2 * cus;  // two 68 KB-LDS workgroups fit one CU
+  return (2 * cus + kXcds - 1) / kXcds * kXcds;  // two 68 KB-LDS workgroups fit one CU
 }
 
 }  // namespace
@@ -332,7 +361,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream) {
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
   if (e != hipSuccess) return e;
-  const int grid = (int)std::min<int64_t>(persistent_grid(), ws.max_tiles);
+  const int grid = persistent_grid();
   hipLaunchKernelGGL(k_attn_nonlocal, dim3(grid), dim3(256), 0, stream, q, k, v, ws, D);
   const int64_t a0 = D.offset / D.pt;
   const int64_t a1 = (D.offset + D.n_q - 1) / D.pt;

@@ -38,6 +38,9 @@ EDGE = [
     synth.Workload("edge_rows_g16", 1, 2, 2000, 32, 2, topk=5, seed=2013),
     # decode with wide groups (gather-plan path)
     synth.Workload("edge_decode_g32", 2, 1, 3000, 64, 2, topk=7, seed=2014),
+    # enough (query, group) rows for one launch over all key blocks: the fused
+    # scoring + top-k path of msa_forward with k = 8
+    synth.Workload("edge_fused_k8", 1, 8192, 8192, 128, 16, topk=8, seed=2015),
     # planted blocks in a small prefill
     synth.Workload("edge_planted", 1, 4096, 4096, 16, 2, topk=6, seed=2011, plant_m=3,
                    plant_alpha=2 * 128 ** 0.25, plant_beta=2 * 128 ** 0.25),
