@@ -81,8 +81,9 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
   char* tile_off = take(sizeof(int32_t) * (nbgt + 1));
   char* list = take(sizeof(int32_t) * slots);
   char* tile_desc = take(sizeof(int32_t) * 2 * max_tiles);
-  char* part_lse = take(sizeof(float) * slots * D.G);
-  char* part_o = take(sizeof(uint16_t) * slots * D.G * msa::kHeadDim);
+  const int64_t pslots = (int64_t)D.B * D.h_kv * D.n_q * (D.k + 1);  // + the local slot
+  char* part_lse = take(sizeof(float) * pslots * D.G);
+  char* part_o = take(sizeof(uint16_t) * pslots * D.G * msa::kHeadDim);
   if (ws) {
     ws->hist = reinterpret_cast<int32_t*>(hist);
     ws->cnt = reinterpret_cast<int32_t*>(cnt);

@@ -37,8 +37,8 @@ struct AttnWs {
   int32_t* tile_off;   // [bins+1] exclusive scan of ceil(cnt / pt); last = tile count
   int32_t* list;       // [edges]  row-slot ids (i * k + s), grouped by bin
   int32_t* tile_desc;  // [max_tiles][2]   (bin, first list entry)
-  float* part_lse;     // [B*h_kv*n_q*k][G]     base-2 log-sum-exp of each partial
-  uint16_t* part_o;    // [B*h_kv*n_q*k][G][d]  normalised partial outputs, bf16, lane order
+  float* part_lse;     // [B*h_kv*n_q*(k+1)][G]     base-2 log-sum-exp of each partial (slot k: local)
+  uint16_t* part_o;    // [B*h_kv*n_q*(k+1)][G][d]  normalised partial outputs, bf16, lane order
   int64_t max_tiles;
   int64_t n_bins;      // B * h_kv * query groups * n_blk
   int32_t n_groups;    // query groups per (b, g)

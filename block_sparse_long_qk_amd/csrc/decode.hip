@@ -27,14 +27,30 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(uint4 a, uint4 b, f32x4 c) {
                                                  0, 0, 0);
 }
 
-// Index-dim mapping of both MFMA operands: lane group c (= lane / 16) and
-// k-step ks hold dims (DIDX/4)*c + 8*ks .. +8, so each lane reads one
-// contiguous DIDX/2-byte run of its row.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Each wave streams its own range of 128-key blocks in steps of 32 keys: the
+// step's 32*DIDX*2 bytes are read with fully coalesced 16-byte loads (64 lanes
+// cover one contiguous 1 KB span per instruction), parked in a per-wave LDS
+// buffer with padded key rows, and read back as 16x16x32 MFMA A operands
+// (lane = key, lane group c = 8 index dims of each k-step).  The next step's
+// loads are in flight while the current step computes.  Only wave-level
+// ordering is needed: no workgroup barrier.
 template <int DIDX>
 __global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict__ iq,
                                                      const uint16_t* __restrict__ ik, float* __restrict__ pooled,
                                                      Dims D, int32_t blocks_per_wave) {
-  constexpr int KS = DIDX / 32;
+  constexpr int KS = DIDX / 32;            // MFMA k-steps per key
+  constexpr int ROW = DIDX * 2;            // bytes per key
+  constexpr int PITCH = ROW + 16;          // LDS bytes per key (pad: conflict-free operand reads)
+  constexpr int STEP_KEYS = 32;
+  constexpr int LOADS = STEP_KEYS * ROW / 1024;  // 16-byte loads per lane per step
+  constexpr int KEYS_PER_LOAD = 1024 / ROW;      // keys one load instruction covers
+  __shared__ __align__(16) unsigned char lds[4][STEP_KEYS * PITCH];
   const float NEG_INF = -__builtin_huge_valf();
   const int b = blockIdx.y;
   const int R = D.n_q * D.h_kv;  // <= 16
@@ -51,42 +67,63 @@ __global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict_
   const int l_row = row_ok ? (int)(pc / kBk) : -1;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qb[ks] = row_ok ? *reinterpret_cast<const uint4*>(iq + ((int64_t)b * R + n) * DIDX + (DIDX / 4) * c + 8 * ks)
+    qb[ks] = row_ok ? *reinterpret_cast<const uint4*>(iq + ((int64_t)b * R + n) * DIDX + 8 * (KS * c + ks))
                     : make_uint4(0, 0, 0, 0);
   int64_t out_base = -1;
   if (row_ok && c == 0) {
     const int i = n / D.h_kv, g = n % D.h_kv;
     out_base = (((int64_t)b * D.h_kv + g) * D.n_q + i) * D.n_blk;
   }
-  const uint16_t* ikb = ik + (int64_t)b * D.n_kv * DIDX + (DIDX / 4) * c;
-  const int64_t p_min = D.offset;
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(ik + (int64_t)b * D.n_kv * DIDX);
+  const int64_t key_end = D.n_kv;
+  unsigned char* buf = lds[wave];
+  // this lane's slot in a load: key (u*KEYS_PER_LOAD + lane*16/ROW), byte offset (lane*16) % ROW
+  const int lk = (lane * 16) / ROW, lo = (lane * 16) % ROW;
 
-  for (int t = t0; t < t1; ++t) {
-    uint4 a[8][KS];
+  const int steps = (t1 - t0) * (kBk / STEP_KEYS);
+  uint4 cur[LOADS];
+  auto fetch = [&](int st, uint4 (&x)[LOADS]) {
+    const int64_t key0 = (int64_t)t0 * kBk + (int64_t)st * STEP_KEYS;
 #pragma unroll
-    for (int T = 0; T < 8; ++T) {
-      const int64_t key = (int64_t)t * kBk + 16 * T + n;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        a[T][ks] = key < D.n_kv ? *reinterpret_cast<const uint4*>(ikb + key * DIDX + 8 * ks) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < LOADS; ++u) {
+      const int64_t key = key0 + u * KEYS_PER_LOAD + lk;
+      x[u] = key < key_end ? *reinterpret_cast<const uint4*>(src + key * ROW + lo) : make_uint4(0, 0, 0, 0);
     }
-    const bool need_mask = (int64_t)t * kBk + kBk - 1 > p_min;
-    float m = NEG_INF;
+  };
+  fetch(0, cur);
+  float m = NEG_INF;
+  for (int st = 0; st < steps; ++st) {
+    const int t = t0 + st / (kBk / STEP_KEYS);
+    // park this step's keys in LDS, then start the next step's loads
 #pragma unroll
-    for (int T = 0; T < 8; ++T) {
+    for (int u = 0; u < LOADS; ++u)
+      *reinterpret_cast<uint4*>(buf + (u * KEYS_PER_LOAD + lk) * PITCH + lo) = cur[u];
+    wave_lds_fence();
+    if (st + 1 < steps) fetch(st + 1, cur);
+    const int64_t skey0 = (int64_t)t * kBk + (st % (kBk / STEP_KEYS)) * STEP_KEYS;
+    const bool need_mask = skey0 + STEP_KEYS - 1 > D.offset;
+#pragma unroll
+    for (int T = 0; T < STEP_KEYS / 16; ++T) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma_16x16x32(a[T][ks], qb[ks], acc);
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(buf + (16 * T + n) * PITCH + 16 * (KS * c + ks));
+        acc = mfma_16x16x32(a, qb[ks], acc);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float x = acc[j];
-        if (need_mask && (int64_t)t * kBk + 16 * T + 4 * c + j > pc) x = NEG_INF;
+        if (need_mask && skey0 + 16 * T + 4 * c + j > pc) x = NEG_INF;
         m = fmaxf(m, x);
       }
     }
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    if (out_base >= 0 && t <= l_row) pooled[out_base + t] = m;
+    wave_lds_fence();  // the buffer is rewritten next step
+    if ((st + 1) % (kBk / STEP_KEYS) == 0) {  // block t complete
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (out_base >= 0 && t <= l_row) pooled[out_base + t] = m;
+      m = NEG_INF;
+    }
   }
 }
 

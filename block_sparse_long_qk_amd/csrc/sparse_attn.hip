@@ -10,17 +10,16 @@
 // Stage A, gather plan (gather_plan.hip): for every (sequence, group, block)
 //   the list of query rows that selected it as a non-local block, cut into
 //   tiles of `pt` positions (pt * G <= 128 rows).
-// Stage B, non-local tiles (KV-outer): persistent workgroups walk contiguous
-//   runs of tiles; the 128-key K block and V block sit in LDS while the run
-//   stays on one (b, g, block), the tile's query rows are gathered into
-//   registers (the next tile's while the current one computes), and S^T = K Q^T
-//   and O^T = V^T P^T run on 32x32x16 bf16 MFMA.  A non-local block lies wholly
-//   before the query, so no mask is needed.  Each (row, slot) writes a
+// Stage B, tiles (KV-outer): persistent workgroups walk runs of tiles; the
+//   128-key K block and V block sit in LDS while the run stays on one
+//   (b, g, block), the tile's query rows are gathered into registers (the next
+//   tile's while the current one computes), and S^T = K Q^T and O^T = V^T P^T
+//   run on 32x32x16 bf16 MFMA.  Non-local tiles need no mask (the block lies
+//   wholly before the query); local tiles (pt consecutive positions sharing
+//   their local block) apply the causal mask.  Each (row, slot) writes a
 //   normalised bf16 partial and its base-2 log-sum-exp.
-// Stage C, local tiles + merge: one workgroup per run of `pt` consecutive
-//   positions, which share their local block; it computes that block with the
-//   causal mask, then merges the row's partials (LSE weighting) and writes the
-//   bf16 output and the natural-log lse.
+// Stage C, merge: LSE weighting of each row's partials into the bf16 output
+//   and the natural-log lse.
 //
 // Lane layout: a wave owns 32 rows (one MFMA n-tile); lane l holds column
 // l % 32, so all softmax statistics of a row live in one lane pair (l, l ^ 32).
@@ -34,6 +33,7 @@ namespace {
 constexpr int KP = kHeadDim + 8;   // LDS pitch of K rows (bf16): 16-byte pad
 constexpr int kXcds = 8;           // XCDs of an MI355X; workgroups are dealt round-robin over them
 constexpr int kRun = 8;            // consecutive tiles one workgroup takes before moving on
+constexpr int kMergeBatch = 8;     // partial slots whose loads the merge issues together
 constexpr int VP = kBk + 4;        // LDS pitch of V^T rows (bf16): 8-byte pad
 
 // Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS.
@@ -140,26 +140,52 @@ __device__ __forceinline__ void attn_block(const uint16_t* Ks, const uint16_t* V
   l = sum;
 }
 
-// Where the gathered row `r` of a tile comes from: query i, slot s of its
-// block_idx row.
+// One lane's row of a tile.  Non-local tiles come from the gather lists (row
+// = query i, slot s of its block_idx row); local tiles are runs of pt
+// consecutive positions that share their local block (slot k).
 struct TileRow {
-  int bgt, start, npos;
-  bool valid;
-  int i, s;
+  int bg, t;      // (b * h_kv + g), KV block
+  int npos;       // positions the tile uses
+  bool valid;     // this lane's row exists
+  bool local;     // the masked local-block tile
+  int i, s;       // query row, partial slot (k = the local block)
+  int64_t p;      // position of the row's query
 };
 
-__device__ __forceinline__ TileRow tile_row(const AttnWs& ws, const Dims& D, int tile, int ps) {
+__device__ __forceinline__ TileRow tile_row(const AttnWs& ws, const Dims& D, int tile, int ps, int n_nonlocal) {
   TileRow tr;
-  tr.bgt = ws.tile_desc[2 * (int64_t)tile];
-  tr.start = ws.tile_desc[2 * (int64_t)tile + 1];
-  tr.npos = min(D.pt, ws.cnt[tr.bgt] - tr.start);
-  tr.valid = ps < tr.npos;
   tr.i = 0;
   tr.s = 0;
-  if (tr.valid) {
-    const int e = ws.list[ws.off[tr.bgt] + tr.start + ps];
-    tr.i = e / D.k;
-    tr.s = e % D.k;
+  tr.p = -1;
+  if (tile < n_nonlocal) {
+    const int bin = ws.tile_desc[2 * (int64_t)tile];
+    const int start = ws.tile_desc[2 * (int64_t)tile + 1];
+    tr.bg = bin / (ws.n_groups * D.n_blk);
+    tr.t = bin % D.n_blk;
+    tr.npos = min(D.pt, ws.cnt[bin] - start);
+    tr.valid = ps < tr.npos;
+    tr.local = false;
+    if (tr.valid) {
+      const int e = ws.list[ws.off[bin] + start + ps];
+      tr.i = e / D.k;
+      tr.s = e % D.k;
+    }
+  } else {
+    const int64_t a0 = D.offset / D.pt;
+    const int n_loc = (int)((D.offset + D.n_q - 1) / D.pt - a0 + 1);
+    const int L = tile - n_nonlocal;
+    tr.bg = L / n_loc;
+    const int64_t p0 = (a0 + L % n_loc) * D.pt;
+    tr.t = (int)(p0 / kBk);
+    tr.npos = D.pt;
+    tr.local = true;
+    const int64_t p = p0 + ps;
+    tr.valid = ps < D.pt && p >= D.offset && p < D.offset + D.n_q;
+    if (tr.valid) {
+      tr.i = (int)(p - D.offset);
+      tr.s = D.k;
+      tr.p = p;
+    }
   }
   return tr;
 }
@@ -178,21 +204,25 @@ __device__ __forceinline__ void store_partial(uint16_t* dst, const f32x16 (&o)[4
   }
 }
 
-// Persistent and XCD-aware.  Workgroup w runs on XCD w % kXcds (the hardware
-// deals workgroups round-robin over the XCDs); XCD x owns the contiguous
-// x-th slice of the tile list, and its workgroups walk that slice in runs of
-// kRun consecutive tiles (same (b, g, group, block) as a rule), run r going to
-// the workgroup r % (grid / kXcds).  So the K/V block in LDS is reused across
-// a run, concurrent workgroups of one XCD share K/V blocks through its L2, and
-// the query rows all XCDs gather at a time come from at most kXcds chunk groups
-// of queries.  The next tile's query rows are fetched while the current tile
-// computes.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_nonlocal(
+// Persistent and XCD-aware tile kernel: the gathered non-local tiles, then the
+// local tiles.  Workgroup w runs on XCD w % kXcds (the hardware deals
+// workgroups round-robin over the XCDs); XCD x owns the contiguous x-th slice
+// of the tile list, and its workgroups walk that slice in runs of kRun
+// consecutive tiles (same (b, g, block) as a rule), run r going to workgroup
+// r % (grid / kXcds).  So the K/V block in LDS is reused across a run,
+// concurrent workgroups of one XCD share K/V blocks through its L2, and the
+// query rows gathered at any time come from at most kXcds query groups.  The
+// next tile's query rows are fetched while the current tile computes.  Every
+// (row, slot) writes a normalised bf16 partial and its base-2 log-sum-exp.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_tiles(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, AttnWs ws,
     Dims D) {
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
-  const int total = ws.tile_off[ws.n_bins];
+  const int n_nonlocal = ws.tile_off[ws.n_bins];
+  const int64_t a0 = D.offset / D.pt;
+  const int n_loc = (int)((D.offset + D.n_q - 1) / D.pt - a0 + 1);
+  const int total = n_nonlocal + D.B * D.h_kv * n_loc;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = gridDim.x / kXcds;
   const int lo = (int)((int64_t)total * xcd / kXcds), hi = (int)((int64_t)total * (xcd + 1) / kXcds);
   const int stride = per_xcd * kRun;  // >= kRun
@@ -205,25 +235,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int col = lane & 31, half = lane >> 5;
   const int r = wave * 32 + col;
   const int ps = r / D.G, hh = r % D.G;
-  const int64_t bins_per_bg = (int64_t)ws.n_groups * D.n_blk;
 
-  TileRow cur = tile_row(ws, D, tile, ps);
+  TileRow cur = tile_row(ws, D, tile, ps, n_nonlocal);
   uint4 qb[8], qn[8];
   {
-    const int bg = (int)(cur.bgt / bins_per_bg), g = bg % D.h_kv, b = bg / D.h_kv;
+    const int g = cur.bg % D.h_kv, b = cur.bg / D.h_kv;
     load_q_row(qb, q + (((int64_t)b * D.n_q + cur.i) * D.h_q + g * D.G + hh) * kHeadDim, cur.valid, half);
   }
   int staged_bg = -1, staged_t = -1;
   while (tile < hi) {
-    const int bg = (int)(cur.bgt / bins_per_bg);
-    const int t = cur.bgt % D.n_blk;
-    if (bg != staged_bg || t != staged_t) {  // uniform: every lane reads the same descriptor
+    if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform: every lane reads the same descriptor
       if (staged_bg >= 0) __syncthreads();
-      const int64_t kv0 = ((int64_t)bg * D.n_kv + (int64_t)t * kBk) * kHeadDim;
-      stage_kv(Ks, Vt, k + kv0, v + kv0, kBk);
+      const int64_t key0 = (int64_t)cur.t * kBk;
+      const int64_t kv0 = ((int64_t)cur.bg * D.n_kv + key0) * kHeadDim;
+      stage_kv(Ks, Vt, k + kv0, v + kv0, (int)min((int64_t)kBk, (int64_t)D.n_kv - key0));
       __syncthreads();
-      staged_bg = bg;
-      staged_t = t;
+      staged_bg = cur.bg;
+      staged_t = cur.t;
     }
     // the tile after this one: the next of the run, else the start of this
     // workgroup's next run (strictly increasing, so the loop ends at hi)
@@ -237,16 +265,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     TileRow nxt = cur;
     if (nt < hi) {
-      nxt = tile_row(ws, D, nt, ps);
-      const int nbg = (int)(nxt.bgt / bins_per_bg), ng = nbg % D.h_kv, nb = nbg / D.h_kv;
+      nxt = tile_row(ws, D, nt, ps, n_nonlocal);
+      const int ng = nxt.bg % D.h_kv, nb = nxt.bg / D.h_kv;
       load_q_row(qn, q + (((int64_t)nb * D.n_q + nxt.i) * D.h_q + ng * D.G + hh) * kHeadDim, nxt.valid, half);
     }
     if (wave * 32 < cur.npos * D.G) {
       f32x16 o[4];
       float m2, l;
-      attn_block(Ks, Vt, qb, lane, D.scale_log2, false, 0, 0, o, m2, l);
+      attn_block(Ks, Vt, qb, lane, D.scale_log2, cur.local, (int64_t)cur.t * kBk, cur.p, o, m2, l);
       if (cur.valid) {
-        const int64_t pidx = ((((int64_t)bg * D.n_q + cur.i) * D.k + cur.s) * D.G + hh);
+        const int64_t pidx = ((((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s) * D.G + hh);
         if (half == 0) ws.part_lse[pidx] = m2 + __log2f(l);
         store_partial(ws.part_o + pidx * kHeadDim + half * 64, o, 1.f / l);
       }
@@ -260,87 +288,75 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-__global__ __launch_bounds__(256) void k_attn_local_merge(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v,
-                                                          const int32_t* __restrict__ block_idx, AttnWs ws,
-                                                          uint16_t* __restrict__ out, float* __restrict__ lse_out,
-                                                          Dims D, int64_t a0) {
-  __shared__ __align__(16) uint16_t Ks[kBk * KP];
-  __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
-  const int bg = blockIdx.y;
-  const int g = bg % D.h_kv, b = bg / D.h_kv;
-  const int64_t p0 = (a0 + blockIdx.x) * (int64_t)D.pt;  // first position of this run
-  const int lblk = (int)(p0 / kBk);
-  const int64_t key0 = (int64_t)lblk * kBk;
-  const int n_valid = (int)min((int64_t)kBk, (int64_t)D.n_kv - key0);
-
-  const int64_t kv0 = ((int64_t)bg * D.n_kv + key0) * kHeadDim;
-  stage_kv(Ks, Vt, k + kv0, v + kv0, n_valid);
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = lane & 31, half = lane >> 5;
-  const int r = wave * 32 + col;
-  const int ps = r / D.G, hh = r % D.G;
-  const int64_t p = p0 + ps;
-  const bool valid = ps < D.pt && p >= D.offset && p < D.offset + D.n_q;
-  const int i = valid ? (int)(p - D.offset) : 0;
-  uint4 qb[8];
-  load_q_row(qb, q + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + hh) * kHeadDim, valid, half);
-  __syncthreads();
-  if (wave * 32 >= D.pt * D.G) return;
-
-  f32x16 o[4];
-  float m2, l;
-  attn_block(Ks, Vt, qb, lane, D.scale_log2, true, key0, valid ? p : -1, o, m2, l);
-  if (!valid) return;
-
-  // merge with the partials of the row's non-local blocks
-  const float lse_loc = m2 + __log2f(l);
-  const int32_t* row = block_idx + ((int64_t)bg * D.n_q + i) * D.k;
-  const int64_t pbase = (((int64_t)bg * D.n_q + i) * D.k) * D.G + hh;  // + s * G
-  float mtot = lse_loc;
-  for (int s = 0; s < D.k; ++s)
-    if (nonlocal_slot(row, s, lblk)) mtot = fmaxf(mtot, ws.part_lse[pbase + (int64_t)s * D.G]);
-  float wsum = __builtin_amdgcn_exp2f(lse_loc - mtot);
-  for (int s = 0; s < D.k; ++s)
-    if (nonlocal_slot(row, s, lblk)) wsum += __builtin_amdgcn_exp2f(ws.part_lse[pbase + (int64_t)s * D.G] - mtot);
-  const float lse_tot = mtot + __log2f(wsum);
-  const float c_loc = __builtin_amdgcn_exp2f(lse_loc - lse_tot) / l;
+// LSE merge of every row's partials (its non-local slots and the local slot
+// k).  One thread per 8 output values of one (row, head): a row-head's 16
+// threads read each slot's 256-byte partial contiguously; all slot loads are
+// independent, and the kernel holds few registers, so many loads are in flight.
+__global__ __launch_bounds__(256) void k_attn_merge(const int32_t* __restrict__ block_idx, AttnWs ws,
+                                                    uint16_t* __restrict__ out, float* __restrict__ lse_out, Dims D) {
+  const float NEG_INF = -__builtin_huge_valf();
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int u = (int)(gid & 15);
+  const int64_t rh = gid >> 4;
+  const int h = (int)(rh % D.G);
+  const int64_t row = rh / D.G;  // (b * h_kv + g) * n_q + i
+  if (row >= (int64_t)D.B * D.h_kv * D.n_q) return;
+  const int i = (int)(row % D.n_q);
+  const int64_t bg = row / D.n_q;
+  const int local = (int)((D.offset + i) / kBk);
+  const int32_t* brow = block_idx + row * D.k;
+  const int64_t pbase = row * (D.k + 1) * D.G + h;  // + s * G
+  // slots in groups of kMergeBatch with every load issued before any use;
+  // a slot without a partial reads the local slot's data with weight zero
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float m = NEG_INF, wsum = 0.f;
+  for (int s0 = 0; s0 <= D.k; s0 += kMergeBatch) {
+    float ls[kMergeBatch];
+    uint4 x[kMergeBatch];
+    bool use[kMergeBatch];
 #pragma unroll
-  for (int Dt = 0; Dt < 4; ++Dt) o[Dt] *= c_loc;
-#pragma unroll 2
-  for (int s = 0; s < D.k; ++s) {
-    if (!nonlocal_slot(row, s, lblk)) continue;
-    const int64_t pidx = pbase + (int64_t)s * D.G;
-    const float c = __builtin_amdgcn_exp2f(ws.part_lse[pidx] - lse_tot);
-    const uint4* src = reinterpret_cast<const uint4*>(ws.part_o + pidx * kHeadDim + half * 64);
-    uint4 w[8];
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int s = s0 + j;
+      use[j] = s == D.k || (s < D.k && nonlocal_slot(brow, s, local));
+      const int64_t pidx = pbase + (int64_t)(use[j] ? s : D.k) * D.G;
+      ls[j] = ws.part_lse[pidx];
+      x[j] = *reinterpret_cast<const uint4*>(ws.part_o + pidx * kHeadDim + 8 * u);
+    }
+    float mb = m;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) w[u] = src[u];
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (use[j]) mb = fmaxf(mb, ls[j]);
+    // nothing seen yet (mb = -inf): keep the zeros; else shift to the new max
+    const float rescale = mb == NEG_INF ? 1.f : __builtin_amdgcn_exp2f(m - mb);
+    wsum *= rescale;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int Dt = u >> 1, e0 = (u & 1) * 8;
-      const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+    for (int c = 0; c < 8; ++c) acc[c] *= rescale;
+    m = mb;
 #pragma unroll
-      for (int h2 = 0; h2 < 4; ++h2) {
-        o[Dt][e0 + 2 * h2] += c * __uint_as_float(x[h2] << 16);
-        o[Dt][e0 + 2 * h2 + 1] += c * __uint_as_float(x[h2] & 0xFFFF0000u);
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float w = use[j] ? __builtin_amdgcn_exp2f(ls[j] - m) : 0.f;
+      wsum += w;
+      const uint32_t xs[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[2 * c] += w * __uint_as_float(xs[c] << 16);
+        acc[2 * c + 1] += w * __uint_as_float(xs[c] & 0xFFFF0000u);
       }
     }
   }
-  uint16_t* dst = out + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + hh) * kHeadDim;
-#pragma unroll
-  for (int Dt = 0; Dt < 4; ++Dt) {
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = 32 * Dt + 8 * i4 + 4 * half;
-      *reinterpret_cast<uint2*>(dst + d0) = make_uint2(pack_bf16x2(o[Dt][4 * i4 + 0], o[Dt][4 * i4 + 1]),
-                                                       pack_bf16x2(o[Dt][4 * i4 + 2], o[Dt][4 * i4 + 3]));
-    }
-  }
-  if (lse_out && half == 0)
-    lse_out[((int64_t)b * D.h_q + g * D.G + hh) * D.n_q + i] = lse_tot * 0.69314718055994531f;
+  const float inv = 1.f / wsum;
+  // lane order -> head dims: value n = 8*(u%8) + c of half u/8 sits at
+  // d = 32*(n/16) + 8*((n%16)/4) + 4*half + n%4
+  const int half = u >> 3, v8 = u & 7;
+  const int d0 = 32 * (v8 >> 1) + 16 * (v8 & 1) + 4 * half;
+  const int g = (int)(bg % D.h_kv), b = (int)(bg / D.h_kv);
+  uint16_t* dst = out + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + h) * kHeadDim;
+  *reinterpret_cast<uint2*>(dst + d0) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                                  pack_bf16x2(acc[2] * inv, acc[3] * inv));
+  *reinterpret_cast<uint2*>(dst + d0 + 8) = make_uint2(pack_bf16x2(acc[4] * inv, acc[5] * inv),
+                                                      pack_bf16x2(acc[6] * inv, acc[7] * inv));
+  if (lse_out && u == 0)
+    lse_out[((int64_t)b * D.h_q + g * D.G + h) * D.n_q + i] = (m + __log2f(wsum)) * 0.69314718055994531f;
 }
 
 int persistent_grid() {  // a multiple of kXcds
@@ -361,12 +377,10 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream) {
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
   if (e != hipSuccess) return e;
-  const int grid = persistent_grid();
-  hipLaunchKernelGGL(k_attn_nonlocal, dim3(grid), dim3(256), 0, stream, q, k, v, ws, D);
-  const int64_t a0 = D.offset / D.pt;
-  const int64_t a1 = (D.offset + D.n_q - 1) / D.pt;
-  hipLaunchKernelGGL(k_attn_local_merge, dim3((unsigned)(a1 - a0 + 1), (unsigned)(D.B * D.h_kv)), dim3(256), 0,
-                     stream, q, k, v, block_idx, ws, out, lse, D, a0);
+  hipLaunchKernelGGL(k_attn_tiles, dim3(persistent_grid()), dim3(256), 0, stream, q, k, v, ws, D);
+  const int64_t threads = (int64_t)D.B * D.h_kv * D.n_q * D.G * 16;
+  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, block_idx, ws, out,
+                     lse, D);
   return hipGetLastError();
 }
 
