@@ -10,6 +10,7 @@
 //     (order-preserving bits of the fp32 score, -0 folded onto +0) << 32 | ~t
 // so a single unsigned compare ranks by (score desc, index asc) and all keys of
 // a row are distinct.  Selection:
+//   0. rows of up to 2048 blocks are loaded into registers once;
 //   1. each lane takes the max key of its strided share of the row;
 //   2. a bitonic sort of the 64 lane maxima gives tau, the (k-1)-th largest of
 //      them; at least k-1 keys of the row are >= tau, and for score rows of any
@@ -71,6 +72,9 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// PER > 0: the row's candidates (at most 64*PER) are loaded once into
+// registers and every pass runs on them; PER == 0: passes re-read the row.
+template <int PER>
 __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ pooled, int32_t* __restrict__ out,
                                                     Dims D, int64_t nrows) {
   __shared__ uint64_t cand[4][64];
@@ -93,10 +97,25 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
     return;
   }
 
+  constexpr int NREG = PER > 0 ? PER : 1;
+  uint64_t reg[NREG];  // keys of t = lane + 64*j (0 = no candidate)
+  if constexpr (PER > 0) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int t = lane + 64 * j;
+      reg[j] = t < local ? sel_key(src[t], t) : 0;
+    }
+  }
+  auto key_at = [&](int j, int t) -> uint64_t {
+    if constexpr (PER > 0) return reg[j];
+    else return t < local ? sel_key(src[t], t) : 0;
+  };
+  const int nj = PER > 0 ? PER : (local + 63) / 64;
+
   // 1. lane maxima
   uint64_t mx = 0;
-  for (int t = lane; t < local; t += 64) {
-    const uint64_t c = sel_key(src[t], t);
+  for (int j = 0; j < nj; ++j) {
+    const uint64_t c = key_at(j, lane + 64 * j);
     mx = c > mx ? c : mx;
   }
   // 2. tau = kk-th largest lane maximum (lanes without candidates hold 0)
@@ -104,7 +123,7 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
 
   // 3. compact the keys >= tau and find the exact kk-th largest key
   int mine = 0;
-  for (int t = lane; t < local; t += 64) mine += sel_key(src[t], t) >= tau;
+  for (int j = 0; j < nj; ++j) mine += key_at(j, lane + 64 * j) >= tau;
   int incl = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -115,8 +134,8 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
   uint64_t thr;
   if (total <= 64) {
     int at = incl - mine;
-    for (int t = lane; t < local; t += 64) {
-      const uint64_t c = sel_key(src[t], t);
+    for (int j = 0; j < nj; ++j) {
+      const uint64_t c = key_at(j, lane + 64 * j);
       if (c >= tau) cand[wave][at++] = c;
     }
     wave_lds_sync();
@@ -128,7 +147,7 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
     for (int bit = 63; bit >= 0; --bit) {
       const uint64_t trial = prefix | (1ull << bit);
       int c = 0;
-      for (int t = lane; t < local; t += 64) c += sel_key(src[t], t) >= trial;
+      for (int j = 0; j < nj; ++j) c += key_at(j, lane + 64 * j) >= trial;
       if (wave_sum(c) >= kk) prefix = trial;
     }
     thr = prefix;
@@ -136,9 +155,9 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
 
   // 4. ascending output: rank by ballot over the strided slots
   int base = 0;
-  for (int t0 = 0; t0 < local; t0 += 64) {
-    const int t = t0 + lane;
-    const bool take = t < local && sel_key(src[t], t) >= thr;
+  for (int j = 0; j < nj; ++j) {
+    const int t = lane + 64 * j;
+    const bool take = t < local && key_at(j, t) >= thr;
     const uint64_t m = __ballot(take);
     if (take) dst[base + __popcll(m & ((1ull << lane) - 1ull))] = t;
     base += __popcll(m);
@@ -151,7 +170,12 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
 hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims& D, hipStream_t stream) {
   const int64_t nrows = (int64_t)D.B * D.h_kv * D.n_q;
   const int64_t blocks = (nrows + 3) / 4;
-  hipLaunchKernelGGL(k_block_topk, dim3((unsigned)blocks), dim3(256), 0, stream, pooled, block_idx, D, nrows);
+  if (D.n_blk <= 64 * 16)
+    hipLaunchKernelGGL(k_block_topk<16>, dim3((unsigned)blocks), dim3(256), 0, stream, pooled, block_idx, D, nrows);
+  else if (D.n_blk <= 64 * 32)
+    hipLaunchKernelGGL(k_block_topk<32>, dim3((unsigned)blocks), dim3(256), 0, stream, pooled, block_idx, D, nrows);
+  else
+    hipLaunchKernelGGL(k_block_topk<0>, dim3((unsigned)blocks), dim3(256), 0, stream, pooled, block_idx, D, nrows);
   return hipGetLastError();
 }
 

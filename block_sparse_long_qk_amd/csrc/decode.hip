@@ -146,6 +146,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
                                                    const int32_t* __restrict__ block_idx, float* __restrict__ part,
                                                    Dims D) {
   __shared__ float P[4][kBk][GMAX];  // per wave: probabilities [key][head]
+  __shared__ __align__(16) unsigned char Kst[4][32 * (kHeadDim * 2 + 16)];  // per wave: one 32-key step of K
   const float NEG_INF = -__builtin_huge_valf();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t r = blockIdx.x;  // row = (b*h_kv + g)*n_q + i
@@ -175,18 +176,42 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     qa[ks] = head_ok ? *reinterpret_cast<const uint4*>(qrow + 8 * ks) : make_uint4(0, 0, 0, 0);
+  // K in four 32-key steps: fully coalesced 16-byte loads (4 keys per
+  // instruction) parked in this wave's padded LDS buffer, read back as MFMA B
+  // operands; the next step's loads are in flight while this one computes.
+  constexpr int KPITCH = kHeadDim * 2 + 16;  // bytes per key row in LDS
+  unsigned char* kbuf = Kst[wave];
+  const int lk = lane >> 4, lo = (lane & 15) * 16;
+  const int n_keys = (int)min((int64_t)kBk, (int64_t)D.n_kv - key0);
+  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kb);
+  uint4 kx[8];
+  auto fetch_k = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int key = 32 * st + 4 * u + lk;
+      kx[u] = key < n_keys ? *reinterpret_cast<const uint4*>(kbytes + key * (kHeadDim * 2) + lo)
+                           : make_uint4(0, 0, 0, 0);
+    }
+  };
   f32x4 sc[8];
+  fetch_k(0);
 #pragma unroll
-  for (int T = 0; T < 8; ++T) {
-    const int key = 16 * T + n;
-    uint4 kf[4];
+  for (int st = 0; st < 4; ++st) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      kf[ks] = key0 + key < D.n_kv ? *reinterpret_cast<const uint4*>(kb + key * kHeadDim + 32 * c + 8 * ks)
-                                   : make_uint4(0, 0, 0, 0);
-    sc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(kbuf + (4 * u + lk) * KPITCH + lo) = kx[u];
+    wave_lds_fence();
+    if (st + 1 < 4) fetch_k(st + 1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) sc[T] = mfma_16x16x32(qa[ks], kf[ks], sc[T]);
+    for (int T2 = 0; T2 < 2; ++T2) {
+      const int T = 2 * st + T2;
+      sc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 kf = *reinterpret_cast<const uint4*>(kbuf + (16 * T2 + n) * KPITCH + 16 * (4 * c + ks));
+        sc[T] = mfma_16x16x32(qa[ks], kf, sc[T]);
+      }
+    }
+    wave_lds_fence();
   }
   // lane (column key = 16T + n, group c) holds heads 4c + j; keys past p or n_kv drop
   float mx[4], sm[4];
@@ -234,21 +259,31 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
   for (int h = 0; h < GMAX; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  const int n_keys = (int)min((int64_t)kBk, (int64_t)D.n_kv - key0);
-  for (int kk = kr; kk < n_keys; kk += 4) {
-    const uint4 w = *reinterpret_cast<const uint4*>(vb + kk * kHeadDim + 8 * dc);
-    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-    float vv[8];
+  // rows kr, kr+4, ...: eight rows' loads issued before their FMAs
+#pragma unroll 1
+  for (int kb8 = 0; kb8 < kBk; kb8 += 32) {
+    uint4 w8[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vv[2 * e] = __uint_as_float(x[e] << 16);
-      vv[2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
+    for (int u = 0; u < 8; ++u) {
+      const int kk = kb8 + 4 * u + kr;
+      w8[u] = kk < n_keys ? *reinterpret_cast<const uint4*>(vb + kk * kHeadDim + 8 * dc) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-      const float ph = P[wave][kk][h];
+    for (int u = 0; u < 8; ++u) {
+      const int kk = kb8 + 4 * u + kr;
+      const uint32_t x[4] = {w8[u].x, w8[u].y, w8[u].z, w8[u].w};
+      float vv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += ph * vv[e];
+      for (int e = 0; e < 4; ++e) {
+        vv[2 * e] = __uint_as_float(x[e] << 16);
+        vv[2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        const float ph = P[wave][kk][h];  // zero past n_keys
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] += ph * vv[e];
+      }
     }
   }
 #pragma unroll
