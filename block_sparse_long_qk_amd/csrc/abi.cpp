@@ -43,7 +43,7 @@ msa_status derive(const msa_problem* p, Dims* D) {
   const int64_t n_groups = ((int64_t)p->n_q + msa::kChunkRows * msa::kGroupChunks - 1) /
                            (msa::kChunkRows * msa::kGroupChunks);
   const int64_t max_tiles = (rows * p->topk + pt - 1) / pt + (int64_t)p->batch * p->h_kv * n_groups * n_blk;
-  if ((int64_t)p->batch * p->h_kv > 65535 || max_tiles * 256 >= (int64_t(1) << 32) ||
+  if ((int64_t)p->batch * p->h_kv > 65535 || max_tiles * 256 >= (int64_t(1) << 32) || max_tiles * pt > INT32_MAX ||
       rows * 64 >= (int64_t(1) << 32) || rows > 65535LL * 65535LL)
     return MSA_ERR_UNSUPPORTED;
   D->B = p->batch;
@@ -79,8 +79,8 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
   char* bsum = take(sizeof(int32_t) * 2 * msa::plan_scan_blocks(D));
   char* off = take(sizeof(int32_t) * (nbgt + 1));
   char* tile_off = take(sizeof(int32_t) * (nbgt + 1));
-  char* list = take(sizeof(int32_t) * slots);
-  char* tile_desc = take(sizeof(int32_t) * 2 * max_tiles);
+  char* list = take(sizeof(int32_t) * max_tiles * D.pt);
+  char* tile_desc = take(sizeof(int32_t) * max_tiles);
   const int64_t pslots = (int64_t)D.B * D.h_kv * D.n_q * (D.k + 1);  // + the local slot
   char* part_lse = take(sizeof(float) * pslots * D.G);
   char* part_o = take(sizeof(uint16_t) * pslots * D.G * msa::kHeadDim);

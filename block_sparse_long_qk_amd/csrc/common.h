@@ -35,8 +35,8 @@ struct AttnWs {
   int32_t* bsum;       // [2 * scan blocks] block sums of the two-level scan
   int32_t* off;        // [bins+1] exclusive scan of cnt
   int32_t* tile_off;   // [bins+1] exclusive scan of ceil(cnt / pt); last = tile count
-  int32_t* list;       // [edges]  row-slot ids (i * k + s), grouped by bin
-  int32_t* tile_desc;  // [max_tiles][2]   (bin, first list entry)
+  int32_t* list;       // [max_tiles * pt] row-slot ids (i * k + s), tile-major, -1 = empty
+  int32_t* tile_desc;  // [max_tiles] the bin of each tile
   float* part_lse;     // [B*h_kv*n_q*(k+1)][G]     base-2 log-sum-exp of each partial (slot k: local)
   uint16_t* part_o;    // [B*h_kv*n_q*(k+1)][G][d]  normalised partial outputs, bf16, lane order
   int64_t max_tiles;

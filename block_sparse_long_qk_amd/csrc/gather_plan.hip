@@ -18,8 +18,11 @@
 //   3. scan:  exclusive scans of the list lengths and of their tile counts over
 //             all bins (two-level: block sums, one-workgroup scan, apply);
 //   4. fill:  each chunk workgroup re-reads its rows and scatters row-slot ids
-//             with LDS cursors;
-//   5. tiles: one descriptor (bin, first entry) per tile.
+//             with LDS cursors into the tile-major list: bin b owns list slots
+//             [tile_off[b] * pt, tile_off[b+1] * pt), so tile j's rows are
+//             list[j * pt .. j * pt + pt);
+//   5. tiles: the bin of every tile, and -1 in the unused slots of each bin's
+//             last tile.
 // Entries inside one list appear in no fixed order; every row's attention is
 // independent of the other rows of its tile, so results do not depend on it.
 #include "launch.h"
@@ -161,14 +164,15 @@ __global__ __launch_bounds__(256) void k_scan_apply(const int32_t* __restrict__ 
 }
 
 __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ block_idx,
-                                                   const int32_t* __restrict__ hist, const int32_t* __restrict__ off,
-                                                   int32_t* __restrict__ list, Dims D, int32_t n_ch) {
+                                                   const int32_t* __restrict__ hist,
+                                                   const int32_t* __restrict__ tile_off, int32_t* __restrict__ list,
+                                                   Dims D, int32_t n_ch) {
   extern __shared__ int32_t cursor[];  // [n_blk]
   const int ch = blockIdx.x, bg = blockIdx.y;
   const int n_cg = (n_ch + kGroupChunks - 1) / kGroupChunks;
   const int32_t* h = hist + ((int64_t)bg * n_ch + ch) * D.n_blk;
-  const int32_t* o = off + ((int64_t)bg * n_cg + ch / kGroupChunks) * D.n_blk;
-  for (int t = threadIdx.x; t < D.n_blk; t += blockDim.x) cursor[t] = o[t] + h[t];
+  const int32_t* o = tile_off + ((int64_t)bg * n_cg + ch / kGroupChunks) * D.n_blk;
+  for (int t = threadIdx.x; t < D.n_blk; t += blockDim.x) cursor[t] = o[t] * D.pt + h[t];
   __syncthreads();
   const int i0 = ch * kChunkRows, i1 = min(D.n_q, i0 + kChunkRows);
   for (int i = i0 + (int)threadIdx.x; i < i1; i += blockDim.x) {
@@ -180,14 +184,13 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ b
 }
 
 __global__ void k_plan_tiles(const int32_t* __restrict__ cnt, const int32_t* __restrict__ tile_off,
-                             int32_t* __restrict__ tile_desc, int64_t n, int32_t pt) {
+                             int32_t* __restrict__ tile_bin, int32_t* __restrict__ list, int64_t n, int32_t pt) {
   for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
-    const int nt = tiles_of(cnt[x], pt);
+    const int c = cnt[x];
+    const int nt = tiles_of(c, pt);
     const int64_t t0 = tile_off[x];
-    for (int j = 0; j < nt; ++j) {
-      tile_desc[2 * (t0 + j)] = (int32_t)x;
-      tile_desc[2 * (t0 + j) + 1] = j * pt;
-    }
+    for (int j = 0; j < nt; ++j) tile_bin[t0 + j] = (int32_t)x;
+    for (int sl = c; sl < nt * pt; ++sl) list[t0 * pt + sl] = -1;
   }
 }
 
@@ -219,9 +222,10 @@ hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const 
   hipLaunchKernelGGL(k_scan_reduce, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, nbgt, D.pt);
   hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(256), 0, stream, ws.bsum, nb, ws.off, ws.tile_off, nbgt);
   hipLaunchKernelGGL(k_scan_apply, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, ws.off, ws.tile_off, nbgt, D.pt);
-  hipLaunchKernelGGL(k_plan_fill, cgrid, dim3(256), lds, stream, block_idx, ws.hist, ws.off, ws.list, D, n_ch);
+  hipLaunchKernelGGL(k_plan_fill, cgrid, dim3(256), lds, stream, block_idx, ws.hist, ws.tile_off, ws.list, D,
+                     n_ch);
   hipLaunchKernelGGL(k_plan_tiles, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.cnt, ws.tile_off,
-                     ws.tile_desc, nbgt, D.pt);
+                     ws.tile_desc, ws.list, nbgt, D.pt);
   return hipGetLastError();
 }
 

@@ -15,6 +15,8 @@
 // (its own row).  Products of bf16 values are exact in fp32; accumulation is
 // fp32.  Causal masking (key j > p -> -inf) is applied only on blocks that
 // reach past the wave's first position.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace msa {
@@ -125,30 +127,45 @@ __global__ __launch_bounds__(256) void k_index_scores(const uint16_t* __restrict
   }
 
   const uint16_t* ikb = ik + (int64_t)b * D.n_kv * DIDX;
-  uint4 stage[C::PER_THREAD];
-  auto load_block = [&](int t) {
+  // two register stages: block t+2 is fetched while block t computes, so a
+  // load has two block-iterations to arrive before it is parked in LDS
+  uint4 stage[2][C::PER_THREAD];
+  auto load_block = [&](int t, uint4 (&st)[C::PER_THREAD]) {
+    const int64_t j0 = (int64_t)t * kBk;
+    if (j0 + kBk <= D.n_kv) {  // whole block inside the cache: no per-key test
 #pragma unroll
-    for (int u = 0; u < C::PER_THREAD; ++u) {
-      const int c = threadIdx.x + 256 * u;
-      const int64_t j = (int64_t)t * kBk + c / C::CPR;
-      stage[u] = (j < D.n_kv) ? *reinterpret_cast<const uint4*>(ikb + j * DIDX + (c % C::CPR) * 8)
-                              : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < C::PER_THREAD; ++u) {
+        const int c = threadIdx.x + 256 * u;
+        st[u] = *reinterpret_cast<const uint4*>(ikb + (j0 + c / C::CPR) * DIDX + (c % C::CPR) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < C::PER_THREAD; ++u) {
+        const int c = threadIdx.x + 256 * u;
+        const int64_t j = j0 + c / C::CPR;
+        st[u] = (j < D.n_kv) ? *reinterpret_cast<const uint4*>(ikb + j * DIDX + (c % C::CPR) * 8)
+                             : make_uint4(0, 0, 0, 0);
+      }
     }
   };
-  auto store_block = [&](int buf) {
+  auto store_block = [&](int buf, const uint4 (&st)[C::PER_THREAD]) {
 #pragma unroll
     for (int u = 0; u < C::PER_THREAD; ++u) {
       const int c = threadIdx.x + 256 * u;
-      *reinterpret_cast<uint4*>(&lds[buf][(c / C::CPR) * C::PITCH + (c % C::CPR) * 8]) = stage[u];
+      *reinterpret_cast<uint4*>(&lds[buf][(c / C::CPR) * C::PITCH + (c % C::CPR) * 8]) = st[u];
     }
   };
 
-  load_block(t_begin);
-  store_block(0);
+  load_block(t_begin, stage[0]);
+  if (t_begin + 1 < t_end) load_block(t_begin + 1, stage[1]);
+  store_block(0, stage[0]);
   __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    if (t + 1 < t_end) load_block(t + 1);
+  // one block: compute block t from LDS buffer SG, fetch block t+2 into
+  // stage[SG], park block t+1 (stage[SG^1]) into the other buffer
+  auto process = [&](int t, auto sg_c) {
+    constexpr int sg = decltype(sg_c)::value;
+    constexpr int buf = sg;
+    if (t + 2 < t_end) load_block(t + 2, stage[sg]);
     if (wave_active) {
       const bool need_mask = (int64_t)t * kBk + kBk - 1 > p_wave_min;
       float run0 = NEG_INF, run1 = NEG_INF;
@@ -217,8 +234,12 @@ __global__ __launch_bounds__(256) void k_index_scores(const uint16_t* __restrict
         }
       }
     }
-    if (t + 1 < t_end) store_block(buf ^ 1);
+    if (t + 1 < t_end) store_block(buf ^ 1, stage[sg ^ 1]);
     __syncthreads();
+  };
+  for (int t = t_begin; t < t_end; t += 2) {
+    process(t, std::integral_constant<int, 0>{});
+    if (t + 1 < t_end) process(t + 1, std::integral_constant<int, 1>{});
   }
 
   if constexpr (KK > 0) {

@@ -140,35 +140,46 @@ __device__ __forceinline__ void attn_block(const uint16_t* Ks, const uint16_t* V
   l = sum;
 }
 
-// One lane's row of a tile.  Non-local tiles come from the gather lists (row
-// = query i, slot s of its block_idx row); local tiles are runs of pt
-// consecutive positions that share their local block (slot k).
+// One lane's row of a tile.  Non-local tiles come from the tile-major gather
+// lists (row = query i, slot s of its block_idx row); local tiles are runs of
+// pt consecutive positions that share their local block (slot k).
 struct TileRow {
   int bg, t;      // (b * h_kv + g), KV block
-  int npos;       // positions the tile uses
   bool valid;     // this lane's row exists
   bool local;     // the masked local-block tile
   int i, s;       // query row, partial slot (k = the local block)
-  int64_t p;      // position of the row's query
+  int64_t p;      // position of the row's query (local tiles)
 };
 
-__device__ __forceinline__ TileRow tile_row(const AttnWs& ws, const Dims& D, int tile, int ps, int n_nonlocal) {
+// The loads that describe a non-local tile: its bin and this lane's list entry
+// (independent of each other, issued early and decoded later).
+struct TileRaw {
+  int bin, e;
+};
+
+__device__ __forceinline__ TileRaw tile_raw(const AttnWs& ws, const Dims& D, int tile, int ps, int n_nonlocal) {
+  TileRaw r{0, -1};
+  if (tile < n_nonlocal) {
+    r.bin = ws.tile_desc[tile];
+    r.e = ps < D.pt ? ws.list[(int64_t)tile * D.pt + ps] : -1;
+  }
+  return r;
+}
+
+__device__ __forceinline__ TileRow tile_row(const TileRaw& raw, const Dims& D, const AttnWs& ws, int tile, int ps,
+                                            int n_nonlocal) {
   TileRow tr;
   tr.i = 0;
   tr.s = 0;
   tr.p = -1;
   if (tile < n_nonlocal) {
-    const int bin = ws.tile_desc[2 * (int64_t)tile];
-    const int start = ws.tile_desc[2 * (int64_t)tile + 1];
-    tr.bg = bin / (ws.n_groups * D.n_blk);
-    tr.t = bin % D.n_blk;
-    tr.npos = min(D.pt, ws.cnt[bin] - start);
-    tr.valid = ps < tr.npos;
+    tr.bg = raw.bin / (ws.n_groups * D.n_blk);
+    tr.t = raw.bin % D.n_blk;
     tr.local = false;
+    tr.valid = raw.e >= 0;
     if (tr.valid) {
-      const int e = ws.list[ws.off[bin] + start + ps];
-      tr.i = e / D.k;
-      tr.s = e % D.k;
+      tr.i = raw.e / D.k;
+      tr.s = raw.e % D.k;
     }
   } else {
     const int64_t a0 = D.offset / D.pt;
@@ -177,7 +188,6 @@ __device__ __forceinline__ TileRow tile_row(const AttnWs& ws, const Dims& D, int
     tr.bg = L / n_loc;
     const int64_t p0 = (a0 + L % n_loc) * D.pt;
     tr.t = (int)(p0 / kBk);
-    tr.npos = D.pt;
     tr.local = true;
     const int64_t p = p0 + ps;
     tr.valid = ps < D.pt && p >= D.offset && p < D.offset + D.n_q;
@@ -188,6 +198,24 @@ __device__ __forceinline__ TileRow tile_row(const AttnWs& ws, const Dims& D, int
     }
   }
   return tr;
+}
+
+// Walk of one workgroup over its tiles: runs of kRun consecutive tiles,
+// successive runs `stride` apart, inside [.., hi).
+struct Walk {
+  int tile, run_start, run_end;
+};
+
+__device__ __forceinline__ Walk walk_next(const Walk& w, int stride, int hi) {
+  Walk n = w;
+  if (w.tile + 1 < w.run_end) {
+    n.tile = w.tile + 1;
+  } else {
+    n.run_start = w.run_start + stride;  // stride >= kRun: strictly increasing
+    n.tile = n.run_start < hi ? n.run_start : hi;
+    n.run_end = min(n.run_start + kRun, hi);
+  }
+  return n;
 }
 
 // Store one row's normalised partial in lane order: lane (q, half) owns 64
@@ -226,25 +254,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = gridDim.x / kXcds;
   const int lo = (int)((int64_t)total * xcd / kXcds), hi = (int)((int64_t)total * (xcd + 1) / kXcds);
   const int stride = per_xcd * kRun;  // >= kRun
-  int run_start = lo + slot * kRun;
-  int tile = run_start;
-  if (tile >= hi) return;  // uniform over the workgroup
-  int run_end = min(run_start + kRun, hi);
+  Walk w0{lo + slot * kRun, lo + slot * kRun, min(lo + slot * kRun + kRun, hi)};
+  if (w0.tile >= hi) return;  // uniform over the workgroup
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
   const int r = wave * 32 + col;
   const int ps = r / D.G, hh = r % D.G;
+  auto q_row = [&](const TileRow& tr) {
+    const int g = tr.bg % D.h_kv, b = tr.bg / D.h_kv;
+    return q + (((int64_t)b * D.n_q + tr.i) * D.h_q + g * D.G + hh) * kHeadDim;
+  };
 
-  TileRow cur = tile_row(ws, D, tile, ps, n_nonlocal);
+  // pipeline: rows of tile n+2 and the query rows of tile n+1 load while tile n computes
+  TileRow cur = tile_row(tile_raw(ws, D, w0.tile, ps, n_nonlocal), D, ws, w0.tile, ps, n_nonlocal);
   uint4 qb[8], qn[8];
-  {
-    const int g = cur.bg % D.h_kv, b = cur.bg / D.h_kv;
-    load_q_row(qb, q + (((int64_t)b * D.n_q + cur.i) * D.h_q + g * D.G + hh) * kHeadDim, cur.valid, half);
-  }
+  load_q_row(qb, q_row(cur), cur.valid, half);
+  Walk w1 = walk_next(w0, stride, hi);
+  TileRaw raw1 = w1.tile < hi ? tile_raw(ws, D, w1.tile, ps, n_nonlocal) : TileRaw{0, -1};
   int staged_bg = -1, staged_t = -1;
-  while (tile < hi) {
-    if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform: every lane reads the same descriptor
+  while (w0.tile < hi) {
+    if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform: every lane decodes the same tile
       if (staged_bg >= 0) __syncthreads();
       const int64_t key0 = (int64_t)cur.t * kBk;
       const int64_t kv0 = ((int64_t)cur.bg * D.n_kv + key0) * kHeadDim;
@@ -253,23 +283,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       staged_bg = cur.bg;
       staged_t = cur.t;
     }
-    // the tile after this one: the next of the run, else the start of this
-    // workgroup's next run (strictly increasing, so the loop ends at hi)
-    int nt, n_run_start = run_start, n_run_end = run_end;
-    if (tile + 1 < run_end) {
-      nt = tile + 1;
-    } else {
-      n_run_start = run_start + stride;
-      nt = n_run_start < hi ? n_run_start : hi;
-      n_run_end = min(n_run_start + kRun, hi);
-    }
     TileRow nxt = cur;
-    if (nt < hi) {
-      nxt = tile_row(ws, D, nt, ps, n_nonlocal);
-      const int ng = nxt.bg % D.h_kv, nb = nxt.bg / D.h_kv;
-      load_q_row(qn, q + (((int64_t)nb * D.n_q + nxt.i) * D.h_q + ng * D.G + hh) * kHeadDim, nxt.valid, half);
+    if (w1.tile < hi) {
+      nxt = tile_row(raw1, D, ws, w1.tile, ps, n_nonlocal);
+      load_q_row(qn, q_row(nxt), nxt.valid, half);
     }
-    if (wave * 32 < cur.npos * D.G) {
+    const Walk w2 = w1.tile < hi ? walk_next(w1, stride, hi) : w1;
+    const TileRaw raw2 = w2.tile < hi ? tile_raw(ws, D, w2.tile, ps, n_nonlocal) : TileRaw{0, -1};
+    // waves whose 32 rows are all empty skip the math
+    if (__ballot(cur.valid) != 0ull) {
       f32x16 o[4];
       float m2, l;
       attn_block(Ks, Vt, qb, lane, D.scale_log2, cur.local, (int64_t)cur.t * kBk, cur.p, o, m2, l);
@@ -279,9 +301,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         store_partial(ws.part_o + pidx * kHeadDim + half * 64, o, 1.f / l);
       }
     }
-    tile = nt;
-    run_start = n_run_start;
-    run_end = n_run_end;
+    w0 = w1;
+    w1 = w2;
+    raw1 = raw2;
     cur = nxt;
 #pragma unroll
     for (int u = 0; u < 8; ++u) qb[u] = qn[u];
