@@ -56,5 +56,39 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def resource_report() -> dict:
+    """Per-kernel register, LDS, scratch and occupancy figures from the compiler
+    (kernel-resource-usage remarks), keyed by mangled kernel name."""
+    import re
+    report = {}
+
+    def one(src):
+        if not src.endswith(".hip"):
+            return ""
+        cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", os.devnull,
+               "-Rpass-analysis=kernel-resource-usage"]
+        return subprocess.run(cmd, capture_output=True, text=True).stderr
+
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        outs = list(ex.map(one, SOURCES))
+    for text in outs:
+        name = None
+        for line in text.splitlines():
+            m = re.search(r"remark:\s+(.*?)\s*\[-Rpass", line)
+            if not m:
+                continue
+            body = m.group(1)
+            if body.startswith("Function Name:"):
+                name = body.split(":", 1)[1].strip()
+                report[name] = {}
+            elif name and ":" in body:
+                k, v = body.split(":", 1)
+                try:
+                    report[name][k.strip()] = int(v.strip())
+                except ValueError:
+                    pass
+    return report
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -218,17 +218,55 @@ __device__ __forceinline__ Walk walk_next(const Walk& w, int stride, int hi) {
   return n;
 }
 
-// Store one row's normalised partial in lane order: lane (q, half) owns 64
-// contiguous bf16 of its row, in accumulator order.
-__device__ __forceinline__ void store_partial(uint16_t* dst, const f32x16 (&o)[4], float inv) {
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int64_t shfl_i64(int64_t x, int src) {
+  const uint32_t lo = __shfl((uint32_t)x, src, 64);
+  const uint32_t hi = __shfl((uint32_t)((uint64_t)x >> 32), src, 64);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Store the wave's 32 normalised partials (bf16, lane order: row q's 128
+// values are lane q's 64 then lane q+32's 64, in accumulator order).  Stored
+// straight from the MFMA layout, one instruction would scatter 64 pieces of
+// 16 bytes over 32 rows; instead the rows go through the wave's 2 KB LDS
+// buffer eight at a time and 16 consecutive lanes write each 256-byte row.
+__device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, unsigned char* stage,
+                                               const f32x16 (&o)[4], float inv, bool valid, int64_t pidx,
+                                               int lane) {
+  const int col = lane & 31, half = lane >> 5;
+  uint4 w[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int Dt = u >> 1, e0 = (u & 1) * 8;
-    const uint4 w = make_uint4(pack_bf16x2(o[Dt][e0 + 0] * inv, o[Dt][e0 + 1] * inv),
-                               pack_bf16x2(o[Dt][e0 + 2] * inv, o[Dt][e0 + 3] * inv),
-                               pack_bf16x2(o[Dt][e0 + 4] * inv, o[Dt][e0 + 5] * inv),
-                               pack_bf16x2(o[Dt][e0 + 6] * inv, o[Dt][e0 + 7] * inv));
-    *reinterpret_cast<uint4*>(dst + 8 * u) = w;
+    w[u] = make_uint4(pack_bf16x2(o[Dt][e0 + 0] * inv, o[Dt][e0 + 1] * inv),
+                      pack_bf16x2(o[Dt][e0 + 2] * inv, o[Dt][e0 + 3] * inv),
+                      pack_bf16x2(o[Dt][e0 + 4] * inv, o[Dt][e0 + 5] * inv),
+                      pack_bf16x2(o[Dt][e0 + 6] * inv, o[Dt][e0 + 7] * inv));
+  }
+#pragma unroll
+  for (int rho = 0; rho < 4; ++rho) {
+    if ((col >> 3) == rho) {
+      unsigned char* dst = stage + (col & 7) * 256 + half * 128;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(dst + 16 * u) = w[u];
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int chunk = 64 * j + lane;            // 128 chunks of 16 bytes: 8 rows x 256 bytes
+      const int rr = chunk >> 4, c16 = chunk & 15;
+      const int owner = 8 * rho + rr;             // lane (column) holding that row
+      const int64_t rp = shfl_i64(pidx, owner);
+      const bool rv = __shfl((int)valid, owner, 64) != 0;
+      const uint4 x = *reinterpret_cast<const uint4*>(stage + rr * 256 + c16 * 16);
+      if (rv) *reinterpret_cast<uint4*>(part_o + rp * kHeadDim + c16 * 8) = x;
+    }
+    wave_lds_fence();
   }
 }
 
@@ -247,6 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     Dims D) {
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
+  __shared__ __align__(16) unsigned char Pst[4][2048];  // per wave: 8 partial rows on their way out
   const int n_nonlocal = ws.tile_off[ws.n_bins];
   const int64_t a0 = D.offset / D.pt;
   const int n_loc = (int)((D.offset + D.n_q - 1) / D.pt - a0 + 1);
@@ -295,11 +334,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       f32x16 o[4];
       float m2, l;
       attn_block(Ks, Vt, qb, lane, D.scale_log2, cur.local, (int64_t)cur.t * kBk, cur.p, o, m2, l);
-      if (cur.valid) {
-        const int64_t pidx = ((((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s) * D.G + hh);
-        if (half == 0) ws.part_lse[pidx] = m2 + __log2f(l);
-        store_partial(ws.part_o + pidx * kHeadDim + half * 64, o, 1.f / l);
-      }
+      const int64_t pidx = ((((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s) * D.G + hh);
+      if (cur.valid && half == 0) ws.part_lse[pidx] = m2 + __log2f(l);
+      store_partials(ws.part_o, Pst[wave], o, 1.f / l, cur.valid, pidx, lane);
     }
     w0 = w1;
     w1 = w2;
