@@ -79,8 +79,7 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
   char* bsum = take(sizeof(int32_t) * 2 * msa::plan_scan_blocks(D));
   char* off = take(sizeof(int32_t) * (nbgt + 1));
   char* tile_off = take(sizeof(int32_t) * (nbgt + 1));
-  char* list = take(sizeof(int32_t) * max_tiles * D.pt);
-  char* tile_desc = take(sizeof(int32_t) * max_tiles);
+  char* list = take(sizeof(int2) * max_tiles * D.pt);
   const int64_t pslots = (int64_t)D.B * D.h_kv * D.n_q * (D.k + 1);  // + the local slot
   char* part_lse = take(sizeof(float) * pslots * D.G);
   char* part_o = take(sizeof(uint16_t) * pslots * D.G * msa::kHeadDim);
@@ -90,8 +89,7 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
     ws->bsum = reinterpret_cast<int32_t*>(bsum);
     ws->off = reinterpret_cast<int32_t*>(off);
     ws->tile_off = reinterpret_cast<int32_t*>(tile_off);
-    ws->list = reinterpret_cast<int32_t*>(list);
-    ws->tile_desc = reinterpret_cast<int32_t*>(tile_desc);
+    ws->list = reinterpret_cast<int2*>(list);
     ws->part_lse = reinterpret_cast<float*>(part_lse);
     ws->part_o = reinterpret_cast<uint16_t*>(part_o);
     ws->max_tiles = max_tiles;

@@ -35,8 +35,7 @@ struct AttnWs {
   int32_t* bsum;       // [2 * scan blocks] block sums of the two-level scan
   int32_t* off;        // [bins+1] exclusive scan of cnt
   int32_t* tile_off;   // [bins+1] exclusive scan of ceil(cnt / pt); last = tile count
-  int32_t* list;       // [max_tiles * pt] row-slot ids (i * k + s), tile-major, -1 = empty
-  int32_t* tile_desc;  // [max_tiles] the bin of each tile
+  int2* list;          // [max_tiles * pt] {row-slot id i * k + s (-1 = empty), bin of the tile}, tile-major
   float* part_lse;     // [B*h_kv*n_q*(k+1)][G]     base-2 log-sum-exp of each partial (slot k: local)
   uint16_t* part_o;    // [B*h_kv*n_q*(k+1)][G][d]  normalised partial outputs, bf16, lane order
   int64_t max_tiles;

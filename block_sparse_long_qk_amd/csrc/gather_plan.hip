@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void k_scan_apply(const int32_t* __restrict__ 
 
 __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ block_idx,
                                                    const int32_t* __restrict__ hist,
-                                                   const int32_t* __restrict__ tile_off, int32_t* __restrict__ list,
+                                                   const int32_t* __restrict__ tile_off, int2* __restrict__ list,
                                                    Dims D, int32_t n_ch) {
   extern __shared__ int32_t cursor[];  // [n_blk]
   const int ch = blockIdx.x, bg = blockIdx.y;
@@ -179,18 +179,20 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ b
     const int local = (int)((D.offset + i) / kBk);
     const int32_t* row = block_idx + ((int64_t)bg * D.n_q + i) * D.k;
     for (int s = 0; s < D.k; ++s)
-      if (nonlocal_slot(row, s, local)) list[atomicAdd(&cursor[row[s]], 1)] = i * D.k + s;
+      if (nonlocal_slot(row, s, local)) list[atomicAdd(&cursor[row[s]], 1)].x = i * D.k + s;
   }
 }
 
+// Every entry of a bin's tiles gets the bin (padding entries too), and the
+// padding entries get the empty id -1.
 __global__ void k_plan_tiles(const int32_t* __restrict__ cnt, const int32_t* __restrict__ tile_off,
-                             int32_t* __restrict__ tile_bin, int32_t* __restrict__ list, int64_t n, int32_t pt) {
+                             int2* __restrict__ list, int64_t n, int32_t pt) {
   for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
     const int c = cnt[x];
     const int nt = tiles_of(c, pt);
-    const int64_t t0 = tile_off[x];
-    for (int j = 0; j < nt; ++j) tile_bin[t0 + j] = (int32_t)x;
-    for (int sl = c; sl < nt * pt; ++sl) list[t0 * pt + sl] = -1;
+    int2* l = list + (int64_t)tile_off[x] * pt;
+    for (int sl = 0; sl < c; ++sl) l[sl].y = (int32_t)x;
+    for (int sl = c; sl < nt * pt; ++sl) l[sl] = make_int2(-1, (int32_t)x);
   }
 }
 
@@ -224,8 +226,8 @@ hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const 
   hipLaunchKernelGGL(k_scan_apply, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, ws.off, ws.tile_off, nbgt, D.pt);
   hipLaunchKernelGGL(k_plan_fill, cgrid, dim3(256), lds, stream, block_idx, ws.hist, ws.tile_off, ws.list, D,
                      n_ch);
-  hipLaunchKernelGGL(k_plan_tiles, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.cnt, ws.tile_off,
-                     ws.tile_desc, ws.list, nbgt, D.pt);
+  hipLaunchKernelGGL(k_plan_tiles, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.cnt, ws.tile_off, ws.list,
+                     nbgt, D.pt);
   return hipGetLastError();
 }
 

@@ -37,30 +37,38 @@ constexpr int kMergeBatch = 8;     // partial slots whose loads the merge issues
 constexpr int VP = kBk + 4;        // LDS pitch of V^T rows (bf16): 8-byte pad
 
 // Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS.
-// Keys at or past n_valid are zero-filled.
+// Keys at or past n_valid (n_valid >= 1) repeat key n_valid - 1: finite data
+// that the causal mask drops, so the block needs no zero fill.  All sixteen
+// loads are issued before the first LDS write.
 __device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint16_t* __restrict__ kb,
                                          const uint16_t* __restrict__ vb, int n_valid) {
   const int tid = threadIdx.x;
+  uint4 kr[8], vr[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {  // K: 2048 chunks of 16 B
     const int c = tid + 256 * u;
-    const int key = c >> 4, oc = c & 15;
-    const uint4 x = key < n_valid ? *reinterpret_cast<const uint4*>(kb + key * kHeadDim + oc * 8)
-                                  : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(Ks + key * KP + oc * 8) = x;
+    const int key = min(c >> 4, n_valid - 1), oc = c & 15;
+    kr[u] = *reinterpret_cast<const uint4*>(kb + key * kHeadDim + oc * 8);
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {  // V: 512 units of 4 keys x 8 dims, written transposed
+  for (int u = 0; u < 2; ++u) {  // V: 512 units of 4 keys x 8 dims
     const int c = tid + 256 * u;
     const int kq = c >> 4, od = c & 15;
-    uint4 r[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int key = kq * 4 + q;
-      r[q] = key < n_valid ? *reinterpret_cast<const uint4*>(vb + key * kHeadDim + od * 8) : make_uint4(0, 0, 0, 0);
-    }
-    const uint32_t* w[4] = {reinterpret_cast<const uint32_t*>(&r[0]), reinterpret_cast<const uint32_t*>(&r[1]),
-                            reinterpret_cast<const uint32_t*>(&r[2]), reinterpret_cast<const uint32_t*>(&r[3])};
+    for (int q = 0; q < 4; ++q)
+      vr[4 * u + q] = *reinterpret_cast<const uint4*>(vb + min(kq * 4 + q, n_valid - 1) * kHeadDim + od * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = tid + 256 * u;
+    *reinterpret_cast<uint4*>(Ks + (c >> 4) * KP + (c & 15) * 8) = kr[u];
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {  // written transposed: Vt[d][key]
+    const int c = tid + 256 * u;
+    const int kq = c >> 4, od = c & 15;
+    const uint32_t* w[4] = {reinterpret_cast<const uint32_t*>(&vr[4 * u + 0]), reinterpret_cast<const uint32_t*>(&vr[4 * u + 1]),
+                            reinterpret_cast<const uint32_t*>(&vr[4 * u + 2]), reinterpret_cast<const uint32_t*>(&vr[4 * u + 3])};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int sh = (e & 1) * 16;
@@ -71,52 +79,94 @@ __device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint1
   }
 }
 
-__device__ __forceinline__ void load_q_row(uint4 (&qb)[8], const uint16_t* __restrict__ qrow, bool valid, int half) {
+// This lane's half of a query row (its 8 k-steps of 8 dims); rows that do not
+// exist read a stand-in row (finite data whose results are never stored).
+__device__ __forceinline__ void load_q_row(uint4 (&qb)[8], const uint16_t* __restrict__ qrow, int half) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    qb[ks] = valid ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * half) : make_uint4(0, 0, 0, 0);
+  for (int ks = 0; ks < 8; ++ks) qb[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * half);
 }
 
-// One wave, 32 query rows x one 128-key block.  Returns the unnormalised O^T
-// accumulators, the row max m2 and sum l in base-2 units (score*scale*log2 e).
-// With `masked`, key key0+j is dropped for rows whose position p < key0+j.
-__device__ __forceinline__ void attn_block(const uint16_t* Ks, const uint16_t* Vt, const uint4 (&qb)[8], int lane,
-                                           float scale_log2, bool masked, int64_t key0, int64_t p, f32x16 (&o)[4],
-                                           float& m2, float& l) {
+// S^T = K Q^T for one wave: the 128 keys of the staged block (4 row tiles of
+// 32) against the wave's 32 query rows, raw dot products.  k-steps outer, so
+// the four accumulator chains interleave.
+__device__ __forceinline__ void qk_block(const uint16_t* Ks, const uint4 (&qb)[8], int lane, f32x16 (&s)[4]) {
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) s[T] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+      s[T] = mfma_32x32x16(*reinterpret_cast<const uint4*>(Ks + (32 * T + col) * KP + 8 * half + 16 * ks), qb[ks],
+                           s[T]);
+  }
+}
+
+// Softmax of one wave's raw scores (in place) and the unnormalised
+// O^T = V^T P^T.  Returns the row max m2 and sum l in base-2 units
+// (score * scale * log2 e).  MASKED drops key key0 + j for rows whose position
+// p < key0 + j (local tiles); unmasked tiles see all 128 keys, so the max of
+// c * s is c times the max (c >= 0) or the min (c < 0) of the raw scores and
+// one fma per score forms the exponent.
+template <bool MASKED>
+__device__ __forceinline__ void softmax_pv(const uint16_t* Vt, f32x16 (&s)[4], int lane, float c, int64_t key0,
+                                           int64_t p, f32x16 (&o)[4], float& m2, float& l) {
   const float NEG_INF = -__builtin_huge_valf();
   const int col = lane & 31, half = lane >> 5;
-  f32x16 s[4];
+  if constexpr (MASKED) {
+    // key key0 + 32*T + row is visible iff 32*T + row <= p - key0
+    const int rel = (int)max<int64_t>(-1, min<int64_t>(kBk, p - key0)) - 4 * half;
+    float mx = NEG_INF;
 #pragma unroll
-  for (int T = 0; T < 4; ++T) {
-    s[T] = f32x16{};
-    const uint16_t* krow = Ks + (32 * T + col) * KP + 8 * half;
+    for (int T = 0; T < 4; ++T) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) s[T] = mfma_32x32x16(*reinterpret_cast<const uint4*>(krow + 16 * ks), qb[ks], s[T]);
-  }
-  float mx = NEG_INF;
-  // key key0 + 32*T + row is visible iff 32*T + row <= p - key0
-  const int rel = (masked ? (int)max<int64_t>(-1, min<int64_t>(kBk, p - key0)) : kBk) - 4 * half;
-#pragma unroll
-  for (int T = 0; T < 4; ++T) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float x = s[T][e] * scale_log2;
-      if (32 * T + 8 * (e >> 2) + (e & 3) > rel) x = NEG_INF;
-      s[T][e] = x;
-      mx = fmaxf(mx, x);
+      for (int e = 0; e < 16; ++e) {
+        float x = s[T][e] * c;
+        if (32 * T + 8 * (e >> 2) + (e & 3) > rel) x = NEG_INF;
+        s[T][e] = x;
+        mx = fmaxf(mx, x);
+      }
     }
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float mref = mx == NEG_INF ? 0.f : mx;  // rows with nothing visible (padding rows)
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[T][e] = __builtin_amdgcn_exp2f(s[T][e] - mref);
+    }
+    m2 = mx;
+  } else {
+    float ext;
+    if (c >= 0.f) {
+      ext = NEG_INF;
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ext = fmaxf(ext, s[T][e]);
+      }
+      ext = fmaxf(ext, wave_xor32(ext));
+    } else {
+      ext = -NEG_INF;
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ext = fminf(ext, s[T][e]);
+      }
+      ext = fminf(ext, wave_xor32(ext));
+    }
+    const float mref = ext * c;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[T][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[T][e], c, -mref));
+    }
+    m2 = mref;
   }
-  mx = fmaxf(mx, wave_xor32(mx));
-  const float mref = mx == NEG_INF ? 0.f : mx;  // rows with nothing visible (padding rows)
   float sum = 0.f;
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(s[T][e] - mref);
-      s[T][e] = pe;
-      sum += pe;
-    }
+    for (int e = 0; e < 16; ++e) sum += s[T][e];
   }
   sum += wave_xor32(sum);
 #pragma unroll
@@ -136,47 +186,47 @@ __device__ __forceinline__ void attn_block(const uint16_t* Ks, const uint16_t* V
       }
     }
   }
-  m2 = mx;
   l = sum;
 }
 
 // One lane's row of a tile.  Non-local tiles come from the tile-major gather
 // lists (row = query i, slot s of its block_idx row); local tiles are runs of
 // pt consecutive positions that share their local block (slot k).
-struct TileRow {
+struct TileRow {   // five ints, no padding bytes (which would keep the struct in memory)
   int bg, t;      // (b * h_kv + g), KV block
-  bool valid;     // this lane's row exists
-  bool local;     // the masked local-block tile
-  int i, s;       // query row, partial slot (k = the local block)
-  int64_t p;      // position of the row's query (local tiles)
+  int valid;      // this lane's row exists
+  int i, s;       // query row (position offset + i), partial slot (k = the local block)
 };
 
-// The loads that describe a non-local tile: its bin and this lane's list entry
-// (independent of each other, issued early and decoded later).
+// What a lane loads to describe its row of a non-local tile: its list entry,
+// which also carries the tile's bin.  Each lane reads its own entry (lanes past
+// pt read entry pt - 1), so the bin arrives per lane and nothing waits for it
+// until the tile is decoded, a step later.
 struct TileRaw {
-  int bin, e;
+  int e, bin;
 };
 
-__device__ __forceinline__ TileRaw tile_raw(const AttnWs& ws, const Dims& D, int tile, int ps, int n_nonlocal) {
-  TileRaw r{0, -1};
-  if (tile < n_nonlocal) {
-    r.bin = ws.tile_desc[tile];
-    r.e = ps < D.pt ? ws.list[(int64_t)tile * D.pt + ps] : -1;
+template <bool LOCAL>
+__device__ __forceinline__ TileRaw tile_raw(const AttnWs& ws, const Dims& D, int tile, int ps) {
+  TileRaw r{-1, 0};
+  if constexpr (!LOCAL) {
+    const int2 x = ws.list[(int64_t)tile * D.pt + min(ps, D.pt - 1)];
+    r.e = x.x;
+    r.bin = x.y;
   }
   return r;
 }
 
-__device__ __forceinline__ TileRow tile_row(const TileRaw& raw, const Dims& D, const AttnWs& ws, int tile, int ps,
-                                            int n_nonlocal) {
+template <bool LOCAL>
+__device__ __forceinline__ TileRow tile_row(const TileRaw& raw, const Dims& D, const AttnWs& ws, int tile, int ps) {
   TileRow tr;
   tr.i = 0;
   tr.s = 0;
-  tr.p = -1;
-  if (tile < n_nonlocal) {
-    tr.bg = raw.bin / (ws.n_groups * D.n_blk);
-    tr.t = raw.bin % D.n_blk;
-    tr.local = false;
-    tr.valid = raw.e >= 0;
+  if constexpr (!LOCAL) {
+    const int bin = __builtin_amdgcn_readfirstlane(raw.bin);  // equal over the tile
+    tr.bg = bin / (ws.n_groups * D.n_blk);
+    tr.t = bin % D.n_blk;
+    tr.valid = ps < D.pt && raw.e >= 0;
     if (tr.valid) {
       tr.i = raw.e / D.k;
       tr.s = raw.e % D.k;
@@ -184,17 +234,14 @@ __device__ __forceinline__ TileRow tile_row(const TileRaw& raw, const Dims& D, c
   } else {
     const int64_t a0 = D.offset / D.pt;
     const int n_loc = (int)((D.offset + D.n_q - 1) / D.pt - a0 + 1);
-    const int L = tile - n_nonlocal;
-    tr.bg = L / n_loc;
-    const int64_t p0 = (a0 + L % n_loc) * D.pt;
+    tr.bg = tile / n_loc;
+    const int64_t p0 = (a0 + tile % n_loc) * D.pt;
     tr.t = (int)(p0 / kBk);
-    tr.local = true;
     const int64_t p = p0 + ps;
     tr.valid = ps < D.pt && p >= D.offset && p < D.offset + D.n_q;
     if (tr.valid) {
       tr.i = (int)(p - D.offset);
       tr.s = D.k;
-      tr.p = p;
     }
   }
   return tr;
@@ -230,16 +277,9 @@ __device__ __forceinline__ int64_t shfl_i64(int64_t x, int src) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Store the wave's 32 normalised partials (bf16, lane order: row q's 128
-// values are lane q's 64 then lane q+32's 64, in accumulator order).  Stored
-// straight from the MFMA layout, one instruction would scatter 64 pieces of
-// 16 bytes over 32 rows; instead the rows go through the wave's 2 KB LDS
-// buffer eight at a time and 16 consecutive lanes write each 256-byte row.
-__device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, unsigned char* stage,
-                                               const f32x16 (&o)[4], float inv, bool valid, int64_t pidx,
-                                               int lane) {
-  const int col = lane & 31, half = lane >> 5;
-  uint4 w[8];
+// The wave's 32 normalised partials, bf16 in lane order: row q's 128 values
+// are lane q's 64 then lane q+32's 64, in accumulator order.
+__device__ __forceinline__ void pack_partial(const f32x16 (&o)[4], float inv, uint4 (&w)[8]) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int Dt = u >> 1, e0 = (u & 1) * 8;
@@ -248,6 +288,17 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, un
                       pack_bf16x2(o[Dt][e0 + 4] * inv, o[Dt][e0 + 5] * inv),
                       pack_bf16x2(o[Dt][e0 + 6] * inv, o[Dt][e0 + 7] * inv));
   }
+}
+
+// Store packed partials and their log-sum-exps.  Stored straight from the MFMA
+// layout, one instruction would scatter 64 pieces of 16 bytes over 32 rows;
+// instead the rows go through the wave's 2 KB LDS buffer eight at a time and 16
+// consecutive lanes write each 256-byte row.
+__device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
+                                               unsigned char* stage, const uint4 (&w)[8], float lse, bool valid,
+                                               int64_t pidx, int lane) {
+  const int col = lane & 31, half = lane >> 5;
+  if (valid && half == 0) part_lse[pidx] = lse;
 #pragma unroll
   for (int rho = 0; rho < 4; ++rho) {
     if ((col >> 3) == rho) {
@@ -270,8 +321,9 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, un
   }
 }
 
-// Persistent and XCD-aware tile kernel: the gathered non-local tiles, then the
-// local tiles.  Workgroup w runs on XCD w % kXcds (the hardware deals
+// Persistent and XCD-aware tile kernel, launched once over the gathered
+// non-local tiles and once (LOCAL) over the masked local tiles.  Workgroup w
+// runs on XCD w % kXcds (the hardware deals
 // workgroups round-robin over the XCDs); XCD x owns the contiguous x-th slice
 // of the tile list, and its workgroups walk that slice in runs of kRun
 // consecutive tiles (same (b, g, block) as a rule), run r going to workgroup
@@ -280,16 +332,20 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, un
 // query rows gathered at any time come from at most kXcds query groups.  The
 // next tile's query rows are fetched while the current tile computes.  Every
 // (row, slot) writes a normalised bf16 partial and its base-2 log-sum-exp.
+template <bool LOCAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_tiles(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, AttnWs ws,
     Dims D) {
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
   __shared__ __align__(16) unsigned char Pst[4][2048];  // per wave: 8 partial rows on their way out
-  const int n_nonlocal = ws.tile_off[ws.n_bins];
-  const int64_t a0 = D.offset / D.pt;
-  const int n_loc = (int)((D.offset + D.n_q - 1) / D.pt - a0 + 1);
-  const int total = n_nonlocal + D.B * D.h_kv * n_loc;
+  int total;
+  if constexpr (LOCAL) {
+    const int64_t a0 = D.offset / D.pt;
+    total = D.B * D.h_kv * (int)((D.offset + D.n_q - 1) / D.pt - a0 + 1);
+  } else {
+    total = ws.tile_off[ws.n_bins];
+  }
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = gridDim.x / kXcds;
   const int lo = (int)((int64_t)total * xcd / kXcds), hi = (int)((int64_t)total * (xcd + 1) / kXcds);
   const int stride = per_xcd * kRun;  // >= kRun
@@ -300,51 +356,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int col = lane & 31, half = lane >> 5;
   const int r = wave * 32 + col;
   const int ps = r / D.G, hh = r % D.G;
-  auto q_row = [&](const TileRow& tr) {
+  auto q_row = [&](const TileRow& tr) {  // rows that do not exist read row 0 of the group
     const int g = tr.bg % D.h_kv, b = tr.bg / D.h_kv;
-    return q + (((int64_t)b * D.n_q + tr.i) * D.h_q + g * D.G + hh) * kHeadDim;
+    const int i = tr.valid ? tr.i : 0;
+    return q + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + hh) * kHeadDim;
   };
 
-  // pipeline: rows of tile n+2 and the query rows of tile n+1 load while tile n computes
-  TileRow cur = tile_row(tile_raw(ws, D, w0.tile, ps, n_nonlocal), D, ws, w0.tile, ps, n_nonlocal);
-  uint4 qb[8], qn[8];
-  load_q_row(qb, q_row(cur), cur.valid, half);
+  // pipeline: the next tile's query rows load into qb once this tile's
+  // scores are done with it; the list entries of the tile after that load a
+  // step earlier still
+  TileRow cur = tile_row<LOCAL>(tile_raw<LOCAL>(ws, D, w0.tile, ps), D, ws, w0.tile, ps);
+  uint4 qb[8];
+  load_q_row(qb, q_row(cur), half);
   Walk w1 = walk_next(w0, stride, hi);
-  TileRaw raw1 = w1.tile < hi ? tile_raw(ws, D, w1.tile, ps, n_nonlocal) : TileRaw{0, -1};
-  int staged_bg = -1, staged_t = -1;
+  TileRaw raw1 = tile_raw<LOCAL>(ws, D, min(w1.tile, hi - 1), ps);
+  // A tile's partials are stored one step late, right after the next tile's
+  // scores: one counter tracks vector loads and stores alike, so a wait for a
+  // load waits for every store issued before it.  Issued there, the stores have
+  // a whole softmax and P.V to drain before the wait for the following tile's
+  // query rows; the list entries needed next are consumed before them.
+  uint4 pw[8];
+  int64_t ppidx = 0;
+  float plse = 0.f;
+  bool pvalid = false, have = false;  // have: a packed partial waits in pw (uniform)
+  // outer loop: one staged K/V block; inner loop: the tiles that use it
   while (w0.tile < hi) {
-    if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform: every lane decodes the same tile
-      if (staged_bg >= 0) __syncthreads();
+    {
       const int64_t key0 = (int64_t)cur.t * kBk;
       const int64_t kv0 = ((int64_t)cur.bg * D.n_kv + key0) * kHeadDim;
       stage_kv(Ks, Vt, k + kv0, v + kv0, (int)min((int64_t)kBk, (int64_t)D.n_kv - key0));
       __syncthreads();
-      staged_bg = cur.bg;
-      staged_t = cur.t;
     }
-    TileRow nxt = cur;
-    if (w1.tile < hi) {
-      nxt = tile_row(raw1, D, ws, w1.tile, ps, n_nonlocal);
-      load_q_row(qn, q_row(nxt), nxt.valid, half);
-    }
-    const Walk w2 = w1.tile < hi ? walk_next(w1, stride, hi) : w1;
-    const TileRaw raw2 = w2.tile < hi ? tile_raw(ws, D, w2.tile, ps, n_nonlocal) : TileRaw{0, -1};
-    // waves whose 32 rows are all empty skip the math
-    if (__ballot(cur.valid) != 0ull) {
+    const int staged_bg = cur.bg, staged_t = cur.t;
+    bool same;
+    do {
+      f32x16 s[4];
+      qk_block(Ks, qb, lane, s);
+      const bool more = w1.tile < hi;
+      // past the last tile: a stand-in decode of the last one (loads stay in bounds, results unused)
+      const TileRow nxt = tile_row<LOCAL>(raw1, D, ws, min(w1.tile, hi - 1), ps);  // before the stores: see above
+      __builtin_amdgcn_sched_barrier(0);
+      if (have) store_partials(ws.part_o, ws.part_lse, Pst[wave], pw, plse, pvalid, ppidx, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      load_q_row(qb, q_row(nxt), half);
+      Walk w2 = w1;
+      if (more) w2 = walk_next(w1, stride, hi);
+      const TileRaw raw2 = tile_raw<LOCAL>(ws, D, min(w2.tile, hi - 1), ps);
       f32x16 o[4];
       float m2, l;
-      attn_block(Ks, Vt, qb, lane, D.scale_log2, cur.local, (int64_t)cur.t * kBk, cur.p, o, m2, l);
-      const int64_t pidx = ((((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s) * D.G + hh);
-      if (cur.valid && half == 0) ws.part_lse[pidx] = m2 + __log2f(l);
-      store_partials(ws.part_o, Pst[wave], o, 1.f / l, cur.valid, pidx, lane);
-    }
-    w0 = w1;
-    w1 = w2;
-    raw1 = raw2;
-    cur = nxt;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) qb[u] = qn[u];
+      softmax_pv<LOCAL>(Vt, s, lane, D.scale_log2, (int64_t)cur.t * kBk, D.offset + cur.i, o, m2, l);
+      pack_partial(o, 1.f / l, pw);
+      ppidx = ((((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s) * D.G + hh);
+      plse = m2 + __log2f(l);
+      pvalid = cur.valid;
+      have = true;
+      w0 = w1;
+      w1 = w2;
+      raw1 = raw2;
+      cur = nxt;
+      same = more && cur.bg == staged_bg && cur.t == staged_t;  // uniform
+    } while (same);
+    __syncthreads();  // every wave is done with the staged block
   }
+  if (have) store_partials(ws.part_o, ws.part_lse, Pst[wave], pw, plse, pvalid, ppidx, lane);
 }
 
 // LSE merge of every row's partials (its non-local slots and the local slot
@@ -436,7 +510,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream) {
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_tiles, dim3(persistent_grid()), dim3(256), 0, stream, q, k, v, ws, D);
+  hipLaunchKernelGGL(k_attn_tiles<false>, dim3(persistent_grid()), dim3(256), 0, stream, q, k, v, ws, D);
+  hipLaunchKernelGGL(k_attn_tiles<true>, dim3(persistent_grid()), dim3(256), 0, stream, q, k, v, ws, D);
   const int64_t threads = (int64_t)D.B * D.h_kv * D.n_q * D.G * 16;
   hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, block_idx, ws, out,
                      lse, D);
