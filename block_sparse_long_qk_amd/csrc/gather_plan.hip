@@ -23,6 +23,9 @@
 //             list[j * pt .. j * pt + pt);
 //   5. tiles: the bin of every tile, and -1 in the unused slots of each bin's
 //             last tile.
+// Step 4 also marks every slot that carries no partial (a padding entry, a
+// repeat, the local block or a block past it) with a log-sum-exp of -inf, so
+// that the merge needs no block_idx.
 // Entries inside one list appear in no fixed order; every row's attention is
 // independent of the other rows of its tile, so results do not depend on it.
 #include "launch.h"
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(256) void k_scan_apply(const int32_t* __restrict__ 
 __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ block_idx,
                                                    const int32_t* __restrict__ hist,
                                                    const int32_t* __restrict__ tile_off, int2* __restrict__ list,
-                                                   Dims D, int32_t n_ch) {
+                                                   float* __restrict__ part_lse, Dims D, int32_t n_ch) {
   extern __shared__ int32_t cursor[];  // [n_blk]
   const int ch = blockIdx.x, bg = blockIdx.y;
   const int n_cg = (n_ch + kGroupChunks - 1) / kGroupChunks;
@@ -178,8 +181,14 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ b
   for (int i = i0 + (int)threadIdx.x; i < i1; i += blockDim.x) {
     const int local = (int)((D.offset + i) / kBk);
     const int32_t* row = block_idx + ((int64_t)bg * D.n_q + i) * D.k;
-    for (int s = 0; s < D.k; ++s)
-      if (nonlocal_slot(row, s, local)) list[atomicAdd(&cursor[row[s]], 1)].x = i * D.k + s;
+    float* lse_row = part_lse + ((int64_t)bg * D.n_q + i) * (D.k + 1) * D.G;
+    for (int s = 0; s < D.k; ++s) {
+      if (nonlocal_slot(row, s, local)) {
+        list[atomicAdd(&cursor[row[s]], 1)].x = i * D.k + s;
+      } else {
+        for (int h = 0; h < D.G; ++h) lse_row[s * D.G + h] = -__builtin_huge_valf();
+      }
+    }
   }
 }
 
@@ -224,8 +233,8 @@ hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const 
   hipLaunchKernelGGL(k_scan_reduce, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, nbgt, D.pt);
   hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(256), 0, stream, ws.bsum, nb, ws.off, ws.tile_off, nbgt);
   hipLaunchKernelGGL(k_scan_apply, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, ws.off, ws.tile_off, nbgt, D.pt);
-  hipLaunchKernelGGL(k_plan_fill, cgrid, dim3(256), lds, stream, block_idx, ws.hist, ws.tile_off, ws.list, D,
-                     n_ch);
+  hipLaunchKernelGGL(k_plan_fill, cgrid, dim3(256), lds, stream, block_idx, ws.hist, ws.tile_off, ws.list,
+                     ws.part_lse, D, n_ch);
   hipLaunchKernelGGL(k_plan_tiles, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.cnt, ws.tile_off, ws.list,
                      nbgt, D.pt);
   return hipGetLastError();

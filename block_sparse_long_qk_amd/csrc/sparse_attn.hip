@@ -33,8 +33,9 @@ namespace {
 constexpr int KP = kHeadDim + 8;   // LDS pitch of K rows (bf16): 16-byte pad
 constexpr int kXcds = 8;           // XCDs of an MI355X; workgroups are dealt round-robin over them
 constexpr int kRun = 8;            // consecutive tiles one workgroup takes before moving on
-constexpr int kMergeBatch = 8;     // partial slots whose loads the merge issues together
+constexpr int kMergeBatch = 9;     // partial slots whose loads the merge issues together (k = 8: one batch, 16: two)
 constexpr int VP = kBk + 4;        // LDS pitch of V^T rows (bf16): 8-byte pad
+constexpr int kPstPitch = 272;     // LDS pitch (bytes) of a partial row being stored: 16-byte pad
 
 // Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS.
 // Keys at or past n_valid (n_valid >= 1) repeat key n_valid - 1: finite data
@@ -292,8 +293,10 @@ __device__ __forceinline__ void pack_partial(const f32x16 (&o)[4], float inv, ui
 
 // Store packed partials and their log-sum-exps.  Stored straight from the MFMA
 // layout, one instruction would scatter 64 pieces of 16 bytes over 32 rows;
-// instead the rows go through the wave's 2 KB LDS buffer eight at a time and 16
-// consecutive lanes write each 256-byte row.
+// instead the rows go through the wave's LDS buffer eight at a time and 16
+// consecutive lanes write each 256-byte row.  The buffer's rows are padded to
+// 272 bytes: the eight rows then start on different banks, and neither the
+// writes (16 lanes, one 128-byte half row each) nor the reads conflict.
 __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
                                                unsigned char* stage, const uint4 (&w)[8], float lse, bool valid,
                                                int64_t pidx, int lane) {
@@ -302,7 +305,7 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, fl
 #pragma unroll
   for (int rho = 0; rho < 4; ++rho) {
     if ((col >> 3) == rho) {
-      unsigned char* dst = stage + (col & 7) * 256 + half * 128;
+      unsigned char* dst = stage + (col & 7) * kPstPitch + half * 128;
 #pragma unroll
       for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(dst + 16 * u) = w[u];
     }
@@ -314,7 +317,7 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, fl
       const int owner = 8 * rho + rr;             // lane (column) holding that row
       const int64_t rp = shfl_i64(pidx, owner);
       const bool rv = __shfl((int)valid, owner, 64) != 0;
-      const uint4 x = *reinterpret_cast<const uint4*>(stage + rr * 256 + c16 * 16);
+      const uint4 x = *reinterpret_cast<const uint4*>(stage + rr * kPstPitch + c16 * 16);
       if (rv) *reinterpret_cast<uint4*>(part_o + rp * kHeadDim + c16 * 8) = x;
     }
     wave_lds_fence();
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     Dims D) {
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
-  __shared__ __align__(16) unsigned char Pst[4][2048];  // per wave: 8 partial rows on their way out
+  __shared__ __align__(16) unsigned char Pst[4][8 * kPstPitch];  // per wave: 8 partial rows on their way out
   int total;
   if constexpr (LOCAL) {
     const int64_t a0 = D.offset / D.pt;
@@ -423,10 +426,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // LSE merge of every row's partials (its non-local slots and the local slot
 // k).  One thread per 8 output values of one (row, head): a row-head's 16
-// threads read each slot's 256-byte partial contiguously; all slot loads are
-// independent, and the kernel holds few registers, so many loads are in flight.
-__global__ __launch_bounds__(256) void k_attn_merge(const int32_t* __restrict__ block_idx, AttnWs ws,
-                                                    uint16_t* __restrict__ out, float* __restrict__ lse_out, Dims D) {
+// threads read each slot's 256-byte partial contiguously.  Slots without a
+// partial carry a log-sum-exp of -inf (set by the gather plan) and weight 0;
+// their partial memory is never written, so it is zeroed after the load rather
+// than multiplied.  The loads of a batch of slots are all issued before any use.
+__global__ __launch_bounds__(256) void k_attn_merge(AttnWs ws, uint16_t* __restrict__ out, float* __restrict__ lse_out,
+                                                    Dims D) {
   const float NEG_INF = -__builtin_huge_valf();
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int u = (int)(gid & 15);
@@ -436,29 +441,26 @@ __global__ __launch_bounds__(256) void k_attn_merge(const int32_t* __restrict__ 
   if (row >= (int64_t)D.B * D.h_kv * D.n_q) return;
   const int i = (int)(row % D.n_q);
   const int64_t bg = row / D.n_q;
-  const int local = (int)((D.offset + i) / kBk);
-  const int32_t* brow = block_idx + row * D.k;
-  const int64_t pbase = row * (D.k + 1) * D.G + h;  // + s * G
-  // slots in groups of kMergeBatch with every load issued before any use;
-  // a slot without a partial reads the local slot's data with weight zero
+  const float* lse_p = ws.part_lse + row * (D.k + 1) * D.G + h;   // slot s at s * G
+  const uint16_t* o_p = ws.part_o + (row * (D.k + 1) * D.G + h) * kHeadDim + 8 * u;  // slot s at s * G * 128
+  const int64_t o_stride = (int64_t)D.G * kHeadDim;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float m = NEG_INF, wsum = 0.f;
   for (int s0 = 0; s0 <= D.k; s0 += kMergeBatch) {
     float ls[kMergeBatch];
     uint4 x[kMergeBatch];
-    bool use[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const int s = s0 + j;
-      use[j] = s == D.k || (s < D.k && nonlocal_slot(brow, s, local));
-      const int64_t pidx = pbase + (int64_t)(use[j] ? s : D.k) * D.G;
-      ls[j] = ws.part_lse[pidx];
-      x[j] = *reinterpret_cast<const uint4*>(ws.part_o + pidx * kHeadDim + 8 * u);
+      const int s = min(s0 + j, D.k);  // past slot k: a repeat of slot k, dropped below
+      ls[j] = lse_p[s * D.G];
+      x[j] = *reinterpret_cast<const uint4*>(o_p + s * o_stride);
     }
-    float mb = m;
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j)
-      if (use[j]) mb = fmaxf(mb, ls[j]);
+      if (s0 + j > D.k) ls[j] = NEG_INF;
+    float mb = m;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, ls[j]);
     // nothing seen yet (mb = -inf): keep the zeros; else shift to the new max
     const float rescale = mb == NEG_INF ? 1.f : __builtin_amdgcn_exp2f(m - mb);
     wsum *= rescale;
@@ -467,9 +469,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(const int32_t* __restrict__ 
     m = mb;
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const float w = use[j] ? __builtin_amdgcn_exp2f(ls[j] - m) : 0.f;
+      const bool use = ls[j] != NEG_INF;
+      const float w = use ? __builtin_amdgcn_exp2f(ls[j] - m) : 0.f;
       wsum += w;
-      const uint32_t xs[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+      const uint32_t xs[4] = {use ? x[j].x : 0u, use ? x[j].y : 0u, use ? x[j].z : 0u, use ? x[j].w : 0u};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         acc[2 * c] += w * __uint_as_float(xs[c] << 16);
@@ -513,8 +516,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
   hipLaunchKernelGGL(k_attn_tiles<false>, dim3(persistent_grid()), dim3(256), 0, stream, q, k, v, ws, D);
   hipLaunchKernelGGL(k_attn_tiles<true>, dim3(persistent_grid()), dim3(256), 0, stream, q, k, v, ws, D);
   const int64_t threads = (int64_t)D.B * D.h_kv * D.n_q * D.G * 16;
-  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, block_idx, ws, out,
-                     lse, D);
+  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, ws, out, lse, D);
   return hipGetLastError();
 }
 
