@@ -35,10 +35,12 @@ msa_status derive(const msa_problem* p, Dims* D) {
       (int64_t)p->n_q * p->topk > INT32_MAX || (int64_t)p->n_q * p->h_kv > INT32_MAX)
     return MSA_ERR_INVALID_ARGUMENT;
   if (p->head_dim != msa::kHeadDim || (p->index_dim != 64 && p->index_dim != 128) || p->block_size != msa::kBk ||
-      p->topk > msa::kMaxTopk || G > msa::kTileRows)
+      p->topk > msa::kMaxTopk || G > msa::kMaxGroup)
     return MSA_ERR_UNSUPPORTED;
   int pt = 1;
-  while (pt * 2 * G <= msa::kTileRows) pt *= 2;
+  // positions per attention tile: pt * G rows fill the tile; pt <= Bk keeps a
+  // local tile's positions inside one block
+  while (pt * 2 * G <= msa::kTileRows && pt * 2 <= msa::kBk) pt *= 2;
   // launch-grid limits: y/z dims of 65535, 2^32 threads along x
   const int64_t n_groups = ((int64_t)p->n_q + msa::kChunkRows * msa::kGroupChunks - 1) /
                            (msa::kChunkRows * msa::kGroupChunks);

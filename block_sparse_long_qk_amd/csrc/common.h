@@ -8,7 +8,8 @@ namespace msa {
 constexpr int kBk = 128;        // block size the kernels are built for
 constexpr int kHeadDim = 128;   // main-branch head dim
 constexpr int kMaxTopk = 64;    // one selection per wavefront lane at most
-constexpr int kTileRows = 128;  // query rows (positions x heads) per attention tile
+constexpr int kTileRows = 256;  // query rows (positions x heads) per attention tile (8 waves x 32)
+constexpr int kMaxGroup = 128;  // query heads per KV head
 constexpr int kChunkRows = 1024;   // query rows per gather-plan workgroup
 constexpr int kGroupChunks = 8;    // plan chunks per gather-list group (8192 query rows)
 constexpr int kMaxPlanBlocks = 16384;  // LDS histogram bins of the gather plan (n_kv <= 2M)
@@ -22,7 +23,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Problem dimensions as the kernels see them (all derived on the host).
 struct Dims {
   int32_t B, n_q, n_kv, h_q, h_kv, G, d, d_idx, k, n_blk;
-  int32_t pt;          // query positions per attention tile (power of two, pt * G <= 128)
+  int32_t pt;          // query positions per attention tile (power of two, pt * G <= 256, pt <= 128)
   int64_t offset;      // position of query row 0
   float scale;         // softmax scale
   float scale_log2;    // softmax scale * log2(e)

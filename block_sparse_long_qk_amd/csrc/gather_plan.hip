@@ -178,13 +178,19 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ b
   for (int t = threadIdx.x; t < D.n_blk; t += blockDim.x) cursor[t] = o[t] * D.pt + h[t];
   __syncthreads();
   const int i0 = ch * kChunkRows, i1 = min(D.n_q, i0 + kChunkRows);
+  const int bin0 = (bg * n_cg + ch / kGroupChunks) * D.n_blk;  // bin of block 0 in this chunk's group
+  const float4 neg4 = make_float4(-__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf(),
+                                  -__builtin_huge_valf());
   for (int i = i0 + (int)threadIdx.x; i < i1; i += blockDim.x) {
     const int local = (int)((D.offset + i) / kBk);
     const int32_t* row = block_idx + ((int64_t)bg * D.n_q + i) * D.k;
     float* lse_row = part_lse + ((int64_t)bg * D.n_q + i) * (D.k + 1) * D.G;
     for (int s = 0; s < D.k; ++s) {
       if (nonlocal_slot(row, s, local)) {
-        list[atomicAdd(&cursor[row[s]], 1)].x = i * D.k + s;
+        list[atomicAdd(&cursor[row[s]], 1)] = make_int2(i * D.k + s, bin0 + row[s]);
+      } else if ((D.G & 3) == 0) {  // 16-byte aligned runs of G floats
+        float4* dst = reinterpret_cast<float4*>(lse_row + s * D.G);
+        for (int h = 0; h < D.G / 4; ++h) dst[h] = neg4;
       } else {
         for (int h = 0; h < D.G; ++h) lse_row[s * D.G + h] = -__builtin_huge_valf();
       }
@@ -192,15 +198,14 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ b
   }
 }
 
-// Every entry of a bin's tiles gets the bin (padding entries too), and the
-// padding entries get the empty id -1.
+// The padding entries of each bin's last tile: the empty id -1 and the bin
+// (every entry of a tile carries its bin; step 4 wrote the others).
 __global__ void k_plan_tiles(const int32_t* __restrict__ cnt, const int32_t* __restrict__ tile_off,
                              int2* __restrict__ list, int64_t n, int32_t pt) {
   for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
     const int c = cnt[x];
     const int nt = tiles_of(c, pt);
     int2* l = list + (int64_t)tile_off[x] * pt;
-    for (int sl = 0; sl < c; ++sl) l[sl].y = (int32_t)x;
     for (int sl = c; sl < nt * pt; ++sl) l[sl] = make_int2(-1, (int32_t)x);
   }
 }

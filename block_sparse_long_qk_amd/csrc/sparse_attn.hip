@@ -9,15 +9,16 @@
 //
 // Stage A, gather plan (gather_plan.hip): for every (sequence, group, block)
 //   the list of query rows that selected it as a non-local block, cut into
-//   tiles of `pt` positions (pt * G <= 128 rows).
-// Stage B, tiles (KV-outer): persistent workgroups walk runs of tiles; the
-//   128-key K block and V block sit in LDS while the run stays on one
-//   (b, g, block), the tile's query rows are gathered into registers (the next
-//   tile's while the current one computes), and S^T = K Q^T and O^T = V^T P^T
-//   run on 32x32x16 bf16 MFMA.  Non-local tiles need no mask (the block lies
-//   wholly before the query); local tiles (pt consecutive positions sharing
-//   their local block) apply the causal mask.  Each (row, slot) writes a
-//   normalised bf16 partial and its base-2 log-sum-exp.
+//   tiles of `pt` positions (pt * G <= 256 rows, pt <= 128).
+// Stage B, tiles (KV-outer): persistent workgroups of 8 waves walk runs of
+//   tiles; the 128-key K block and V block sit in LDS while the run stays on
+//   one (b, g, block); each wave owns 32 of the tile's 256 rows.  A wave's
+//   query rows arrive in its own LDS region by direct global-to-LDS loads
+//   issued one tile ahead, and S^T = K Q^T and O^T = V^T P^T run on 32x32x16
+//   bf16 MFMA.  Non-local tiles need no mask (the block lies wholly before the
+//   query); local tiles (pt consecutive positions sharing their local block)
+//   apply the causal mask.  Each (row, slot) writes a normalised bf16 partial
+//   and its base-2 log-sum-exp.
 // Stage C, merge: LSE weighting of each row's partials into the bf16 output
 //   and the natural-log lse.
 //
@@ -33,40 +34,46 @@ namespace {
 constexpr int KP = kHeadDim + 8;   // LDS pitch of K rows (bf16): 16-byte pad
 constexpr int kXcds = 8;           // XCDs of an MI355X; workgroups are dealt round-robin over them
 constexpr int kRun = 8;            // consecutive tiles one workgroup takes before moving on
-constexpr int kMergeBatch = 9;     // partial slots whose loads the merge issues together (k = 8: one batch, 16: two)
 constexpr int VP = kBk + 4;        // LDS pitch of V^T rows (bf16): 8-byte pad
 constexpr int kPstPitch = 272;     // LDS pitch (bytes) of a partial row being stored: 16-byte pad
+constexpr int kWaves = 8;          // waves per tile workgroup (kWaves * 32 = 256 rows per tile)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQRegion = 32 * 256; // LDS bytes of one wave's 32 query rows
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F; // lgkmcnt(0)
 
-// Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS.
-// Keys at or past n_valid (n_valid >= 1) repeat key n_valid - 1: finite data
-// that the causal mask drops, so the block needs no zero fill.  All sixteen
-// loads are issued before the first LDS write.
+// Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS
+// with the workgroup's kThreads threads.  Keys at or past n_valid (n_valid >= 1)
+// repeat key n_valid - 1: finite data that the causal mask drops, so the block
+// needs no zero fill.  All loads are issued before the first LDS write.
 __device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint16_t* __restrict__ kb,
                                          const uint16_t* __restrict__ vb, int n_valid) {
+  constexpr int KPER = 2048 / kThreads, VPER = 512 / kThreads;  // 16-byte K chunks, 4-key V units
   const int tid = threadIdx.x;
-  uint4 kr[8], vr[8];
+  uint4 kr[KPER], vr[4 * VPER];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {  // K: 2048 chunks of 16 B
-    const int c = tid + 256 * u;
+  for (int u = 0; u < KPER; ++u) {
+    const int c = tid + kThreads * u;
     const int key = min(c >> 4, n_valid - 1), oc = c & 15;
     kr[u] = *reinterpret_cast<const uint4*>(kb + key * kHeadDim + oc * 8);
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {  // V: 512 units of 4 keys x 8 dims
-    const int c = tid + 256 * u;
+  for (int u = 0; u < VPER; ++u) {
+    const int c = tid + kThreads * u;
     const int kq = c >> 4, od = c & 15;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       vr[4 * u + q] = *reinterpret_cast<const uint4*>(vb + min(kq * 4 + q, n_valid - 1) * kHeadDim + od * 8);
   }
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int c = tid + 256 * u;
+  for (int u = 0; u < KPER; ++u) {
+    const int c = tid + kThreads * u;
     *reinterpret_cast<uint4*>(Ks + (c >> 4) * KP + (c & 15) * 8) = kr[u];
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {  // written transposed: Vt[d][key]
-    const int c = tid + 256 * u;
+  for (int u = 0; u < VPER; ++u) {  // written transposed: Vt[d][key]
+    const int c = tid + kThreads * u;
     const int kq = c >> 4, od = c & 15;
     const uint32_t* w[4] = {reinterpret_cast<const uint32_t*>(&vr[4 * u + 0]), reinterpret_cast<const uint32_t*>(&vr[4 * u + 1]),
                             reinterpret_cast<const uint32_t*>(&vr[4 * u + 2]), reinterpret_cast<const uint32_t*>(&vr[4 * u + 3])};
@@ -80,27 +87,54 @@ __device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint1
   }
 }
 
-// This lane's half of a query row (its 8 k-steps of 8 dims); rows that do not
-// exist read a stand-in row (finite data whose results are never stored).
-__device__ __forceinline__ void load_q_row(uint4 (&qb)[8], const uint16_t* __restrict__ qrow, int half) {
+// A wave's query rows live in its 8 KB LDS region chunk-major: 16-byte chunk
+// c (dims 8c..8c+7) of row r (0..31) at c * 512 + r * 16, so the 32 lanes that
+// read one chunk of 32 rows read 512 consecutive bytes.  The rows are fetched
+// with direct global-to-LDS loads, which place lane l's 16 bytes at l * 16 past
+// the instruction's LDS address: instruction u has lane (col, half) fetch
+// chunk 2u + half of its own row, which lands exactly there.  Rows that do not
+// exist point at a stand-in row whose results are never stored.
+__device__ __forceinline__ void fetch_q_rows(unsigned char* qw, const uint16_t* mine, int half) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qb[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * half);
+  for (int u = 0; u < 8; ++u)
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(mine + 8 * (2 * u + half)),
+                                     (__attribute__((address_space(3))) void*)(qw + 1024 * u), 16, 0, 0);
 }
 
 // S^T = K Q^T for one wave: the 128 keys of the staged block (4 row tiles of
-// 32) against the wave's 32 query rows, raw dot products.  k-steps outer, so
-// the four accumulator chains interleave.
-__device__ __forceinline__ void qk_block(const uint16_t* Ks, const uint4 (&qb)[8], int lane, f32x16 (&s)[4]) {
+// 32) against the wave's 32 query rows (from its LDS region), raw dot
+// products.  k-steps outer, so the four accumulator chains interleave; the
+// operands of k-step ks+1 are read from LDS while the MFMAs of k-step ks run.
+__device__ __forceinline__ void qk_block(const uint16_t* Ks, const unsigned char* qw, int lane, f32x16 (&s)[4]) {
   const int col = lane & 31, half = lane >> 5;
+  const uint16_t* kbase = Ks + col * KP + 8 * half;
+  const unsigned char* qbase = qw + half * 512 + col * 16;
+  uint4 kf[2][4], qf[2];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) kf[0][T] = *reinterpret_cast<const uint4*>(kbase + 32 * T * KP);
+  qf[0] = *reinterpret_cast<const uint4*>(qbase);
 #pragma unroll
   for (int T = 0; T < 4; ++T) s[T] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
+    const int cb = ks & 1, nb = cb ^ 1;
+    if (ks + 1 < 8) {
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
-      s[T] = mfma_32x32x16(*reinterpret_cast<const uint4*>(Ks + (32 * T + col) * KP + 8 * half + 16 * ks), qb[ks],
-                           s[T]);
+      for (int T = 0; T < 4; ++T) kf[nb][T] = *reinterpret_cast<const uint4*>(kbase + 32 * T * KP + 16 * (ks + 1));
+      qf[nb] = *reinterpret_cast<const uint4*>(qbase + (ks + 1) * 1024);
+    }
+#pragma unroll
+    for (int T = 0; T < 4; ++T) s[T] = mfma_32x32x16(kf[cb][T], qf[cb], s[T]);
   }
+  // issue order: the first operands, then per k-step the next operands ahead
+  // of that step's four MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+#pragma unroll
+  for (int ks = 0; ks < 7; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 // Softmax of one wave's raw scores (in place) and the unnormalised
@@ -172,21 +206,37 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* Vt, f32x16 (&s)[4], i
   sum += wave_xor32(sum);
 #pragma unroll
   for (int D = 0; D < 4; ++D) o[D] = f32x16{};
+  // k-step j = 2T + u covers keys 32T + 16u .. +15; its V^T operands are read
+  // from LDS while the MFMAs of k-step j-1 run
+  const uint16_t* vbase = Vt + col * VP + 4 * half;
+  uint4 vf[2][4];
+  auto read_v = [&](int j, uint4 (&dst)[4]) {
 #pragma unroll
-  for (int T = 0; T < 4; ++T) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint4 pb = make_uint4(pack_bf16x2(s[T][8 * u + 0], s[T][8 * u + 1]), pack_bf16x2(s[T][8 * u + 2], s[T][8 * u + 3]),
-                                  pack_bf16x2(s[T][8 * u + 4], s[T][8 * u + 5]), pack_bf16x2(s[T][8 * u + 6], s[T][8 * u + 7]));
-#pragma unroll
-      for (int D = 0; D < 4; ++D) {
-        const uint16_t* vrow = Vt + (32 * D + col) * VP + 32 * T + 16 * u + 4 * half;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-        o[D] = mfma_32x32x16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[D]);
-      }
+    for (int D = 0; D < 4; ++D) {
+      const uint16_t* vrow = vbase + 32 * D * VP + 16 * j;
+      const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+      dst[D] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
+  };
+  read_v(0, vf[0]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int T = j >> 1, u = j & 1;
+    if (j + 1 < 8) read_v(j + 1, vf[(j + 1) & 1]);
+    const uint4 pb = make_uint4(pack_bf16x2(s[T][8 * u + 0], s[T][8 * u + 1]), pack_bf16x2(s[T][8 * u + 2], s[T][8 * u + 3]),
+                                pack_bf16x2(s[T][8 * u + 4], s[T][8 * u + 5]), pack_bf16x2(s[T][8 * u + 6], s[T][8 * u + 7]));
+#pragma unroll
+    for (int D = 0; D < 4; ++D) o[D] = mfma_32x32x16(vf[j & 1][D], pb, o[D]);
   }
+  // issue order of the LDS reads and MFMAs (the VALU work interleaves freely)
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   l = sum;
 }
 
@@ -325,23 +375,30 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, fl
 }
 
 // Persistent and XCD-aware tile kernel, launched once over the gathered
-// non-local tiles and once (LOCAL) over the masked local tiles.  Workgroup w
-// runs on XCD w % kXcds (the hardware deals
-// workgroups round-robin over the XCDs); XCD x owns the contiguous x-th slice
-// of the tile list, and its workgroups walk that slice in runs of kRun
-// consecutive tiles (same (b, g, block) as a rule), run r going to workgroup
-// r % (grid / kXcds).  So the K/V block in LDS is reused across a run,
-// concurrent workgroups of one XCD share K/V blocks through its L2, and the
-// query rows gathered at any time come from at most kXcds query groups.  The
-// next tile's query rows are fetched while the current tile computes.  Every
-// (row, slot) writes a normalised bf16 partial and its base-2 log-sum-exp.
+// non-local tiles and once (LOCAL) over the masked local tiles.  One
+// workgroup of kWaves waves per CU (2 waves per SIMD); workgroup w runs on XCD
+// w % kXcds (the hardware deals workgroups round-robin over the XCDs); XCD x
+// owns the contiguous x-th slice of the tile list, and its workgroups walk
+// that slice in runs of kRun consecutive tiles (same (b, g, block) as a rule),
+// run r going to workgroup r % (grid / kXcds).  So the K/V block in LDS is
+// reused across a run, and the query rows gathered at any time come from at
+// most kXcds query groups.
+//
+// Per tile and wave: scores from the query rows in LDS; decode of the next
+// tile's list entries; stores of the previous tile's partials; the next
+// tile's query rows fetched into the (now free) LDS region; softmax and P.V;
+// the partial packed for storing one tile later.  One counter (vmcnt) tracks
+// vector loads and stores alike, so a wait for loads waits for every store
+// issued before them: issued where they are, the stores and the next rows
+// have a whole softmax and P.V to land before the next tile waits for them.
+// The wave's LDS region doubles as the staging buffer of the stores.
 template <bool LOCAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_tiles(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_tiles(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, AttnWs ws,
     Dims D) {
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
-  __shared__ __align__(16) unsigned char Pst[4][8 * kPstPitch];  // per wave: 8 partial rows on their way out
+  __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];  // per wave: its query rows, or partials on their way out
   int total;
   if constexpr (LOCAL) {
     const int64_t a0 = D.offset / D.pt;
@@ -359,25 +416,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int col = lane & 31, half = lane >> 5;
   const int r = wave * 32 + col;
   const int ps = r / D.G, hh = r % D.G;
+  unsigned char* qw = Qs[wave];
   auto q_row = [&](const TileRow& tr) {  // rows that do not exist read row 0 of the group
     const int g = tr.bg % D.h_kv, b = tr.bg / D.h_kv;
     const int i = tr.valid ? tr.i : 0;
     return q + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + hh) * kHeadDim;
   };
 
-  // pipeline: the next tile's query rows load into qb once this tile's
-  // scores are done with it; the list entries of the tile after that load a
-  // step earlier still
   TileRow cur = tile_row<LOCAL>(tile_raw<LOCAL>(ws, D, w0.tile, ps), D, ws, w0.tile, ps);
-  uint4 qb[8];
-  load_q_row(qb, q_row(cur), half);
+  fetch_q_rows(qw, q_row(cur), half);
   Walk w1 = walk_next(w0, stride, hi);
   TileRaw raw1 = tile_raw<LOCAL>(ws, D, min(w1.tile, hi - 1), ps);
-  // A tile's partials are stored one step late, right after the next tile's
-  // scores: one counter tracks vector loads and stores alike, so a wait for a
-  // load waits for every store issued before it.  Issued there, the stores have
-  // a whole softmax and P.V to drain before the wait for the following tile's
-  // query rows; the list entries needed next are consumed before them.
   uint4 pw[8];
   int64_t ppidx = 0;
   float plse = 0.f;
@@ -394,14 +443,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     bool same;
     do {
       f32x16 s[4];
-      qk_block(Ks, qb, lane, s);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this tile's query rows have landed in LDS
+      __builtin_amdgcn_sched_barrier(0);
+      qk_block(Ks, qw, lane, s);
+      __builtin_amdgcn_sched_barrier(0);
       const bool more = w1.tile < hi;
       // past the last tile: a stand-in decode of the last one (loads stay in bounds, results unused)
-      const TileRow nxt = tile_row<LOCAL>(raw1, D, ws, min(w1.tile, hi - 1), ps);  // before the stores: see above
+      const TileRow nxt = tile_row<LOCAL>(raw1, D, ws, min(w1.tile, hi - 1), ps);
       __builtin_amdgcn_sched_barrier(0);
-      if (have) store_partials(ws.part_o, ws.part_lse, Pst[wave], pw, plse, pvalid, ppidx, lane);
+      if (have) store_partials(ws.part_o, ws.part_lse, qw, pw, plse, pvalid, ppidx, lane);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // LDS reads of the region are done before it is refilled
       __builtin_amdgcn_sched_barrier(0);
-      load_q_row(qb, q_row(nxt), half);
+      fetch_q_rows(qw, q_row(nxt), half);
       Walk w2 = w1;
       if (more) w2 = walk_next(w1, stride, hi);
       const TileRaw raw2 = tile_raw<LOCAL>(ws, D, min(w2.tile, hi - 1), ps);
@@ -421,78 +474,121 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } while (same);
     __syncthreads();  // every wave is done with the staged block
   }
-  if (have) store_partials(ws.part_o, ws.part_lse, Pst[wave], pw, plse, pvalid, ppidx, lane);
+  if (have) store_partials(ws.part_o, ws.part_lse, qw, pw, plse, pvalid, ppidx, lane);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the last (unused) row fetch has landed before the workgroup ends
 }
 
-// LSE merge of every row's partials (its non-local slots and the local slot
-// k).  One thread per 8 output values of one (row, head): a row-head's 16
-// threads read each slot's 256-byte partial contiguously.  Slots without a
-// partial carry a log-sum-exp of -inf (set by the gather plan) and weight 0;
-// their partial memory is never written, so it is zeroed after the load rather
-// than multiplied.  The loads of a batch of slots are all issued before any use.
-__global__ __launch_bounds__(256) void k_attn_merge(AttnWs ws, uint16_t* __restrict__ out, float* __restrict__ lse_out,
-                                                    Dims D) {
+// Local tiles fused with the merge.  Each workgroup walks the local tiles (pt
+// consecutive positions sharing their local block; XCD-aware runs as above).
+// Per tile and wave: the query rows arrive by direct loads into the wave's LDS
+// region, the masked local block gives the unnormalised O^T, its max and sum
+// in registers, and the row's non-local partials (lse -inf: no partial) are
+// folded in two slots at a time with a running max.  Normalised, the result is
+// written to `out` (bf16) and `lse` (natural log).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_local_merge(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, AttnWs ws,
+    uint16_t* __restrict__ out, float* __restrict__ lse_out, Dims D) {
+  __shared__ __align__(16) uint16_t Ks[kBk * KP];
+  __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
+  __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];
   const float NEG_INF = -__builtin_huge_valf();
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int u = (int)(gid & 15);
-  const int64_t rh = gid >> 4;
-  const int h = (int)(rh % D.G);
-  const int64_t row = rh / D.G;  // (b * h_kv + g) * n_q + i
-  if (row >= (int64_t)D.B * D.h_kv * D.n_q) return;
-  const int i = (int)(row % D.n_q);
-  const int64_t bg = row / D.n_q;
-  const float* lse_p = ws.part_lse + row * (D.k + 1) * D.G + h;   // slot s at s * G
-  const uint16_t* o_p = ws.part_o + (row * (D.k + 1) * D.G + h) * kHeadDim + 8 * u;  // slot s at s * G * 128
-  const int64_t o_stride = (int64_t)D.G * kHeadDim;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float m = NEG_INF, wsum = 0.f;
-  for (int s0 = 0; s0 <= D.k; s0 += kMergeBatch) {
-    float ls[kMergeBatch];
-    uint4 x[kMergeBatch];
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int s = min(s0 + j, D.k);  // past slot k: a repeat of slot k, dropped below
-      ls[j] = lse_p[s * D.G];
-      x[j] = *reinterpret_cast<const uint4*>(o_p + s * o_stride);
+  const int64_t a0 = D.offset / D.pt;
+  const int total = D.B * D.h_kv * (int)((D.offset + D.n_q - 1) / D.pt - a0 + 1);
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = gridDim.x / kXcds;
+  const int lo = (int)((int64_t)total * xcd / kXcds), hi = (int)((int64_t)total * (xcd + 1) / kXcds);
+  const int stride = per_xcd * kRun;
+  Walk w{lo + slot * kRun, lo + slot * kRun, min(lo + slot * kRun + kRun, hi)};
+  if (w.tile >= hi) return;  // uniform over the workgroup
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int r = wave * 32 + col;
+  const int ps = r / D.G, hh = r % D.G;
+  unsigned char* qw = Qs[wave];
+  int staged_bg = -1, staged_t = -1;
+  for (; w.tile < hi; w = walk_next(w, stride, hi)) {
+    const TileRow cur = tile_row<true>(TileRaw{-1, 0}, D, ws, w.tile, ps);
+    const int g = cur.bg % D.h_kv, b = cur.bg / D.h_kv;
+    const int64_t qoff = (((int64_t)b * D.n_q + (cur.valid ? cur.i : 0)) * D.h_q + g * D.G + hh) * kHeadDim;
+    fetch_q_rows(qw, q + qoff, half);
+    if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform
+      if (staged_bg >= 0) __syncthreads();
+      const int64_t key0 = (int64_t)cur.t * kBk;
+      const int64_t kv0 = ((int64_t)cur.bg * D.n_kv + key0) * kHeadDim;
+      stage_kv(Ks, Vt, k + kv0, v + kv0, (int)min((int64_t)kBk, (int64_t)D.n_kv - key0));
+      __syncthreads();
+      staged_bg = cur.bg;
+      staged_t = cur.t;
     }
+    f32x16 sc[4], o[4];
+    float m2, l;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the query rows have landed in LDS
+    __builtin_amdgcn_sched_barrier(0);
+    qk_block(Ks, qw, lane, sc);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_pv<true>(Vt, sc, lane, D.scale_log2, (int64_t)cur.t * kBk, D.offset + cur.i, o, m2, l);
+
+    // fold in the non-local partials: this lane's 64 values of each are the
+    // 128 bytes at half * 128 of the row's 256, in accumulator order
+    const int64_t prow = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1);
+    const float* lse_p = ws.part_lse + prow * D.G + hh;                       // slot s at s * G
+    const uint16_t* o_p = ws.part_o + (prow * D.G + hh) * kHeadDim + 64 * half;  // slot s at s * G * 128
+    float M = m2, L = l;
+    for (int s0 = 0; s0 < D.k; s0 += 2) {
+      float ls[2];
+      uint4 x[2][8];
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j)
-      if (s0 + j > D.k) ls[j] = NEG_INF;
-    float mb = m;
+      for (int j = 0; j < 2; ++j) {
+        const int sl = min(s0 + j, D.k - 1);
+        ls[j] = lse_p[(int64_t)sl * D.G];
+        const uint16_t* src = o_p + (int64_t)sl * D.G * kHeadDim;
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, ls[j]);
-    // nothing seen yet (mb = -inf): keep the zeros; else shift to the new max
-    const float rescale = mb == NEG_INF ? 1.f : __builtin_amdgcn_exp2f(m - mb);
-    wsum *= rescale;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] *= rescale;
-    m = mb;
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const bool use = ls[j] != NEG_INF;
-      const float w = use ? __builtin_amdgcn_exp2f(ls[j] - m) : 0.f;
-      wsum += w;
-      const uint32_t xs[4] = {use ? x[j].x : 0u, use ? x[j].y : 0u, use ? x[j].z : 0u, use ? x[j].w : 0u};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        acc[2 * c] += w * __uint_as_float(xs[c] << 16);
-        acc[2 * c + 1] += w * __uint_as_float(xs[c] & 0xFFFF0000u);
+        for (int u = 0; u < 8; ++u) x[j][u] = *reinterpret_cast<const uint4*>(src + 8 * u);
       }
+      if (s0 + 1 >= D.k) ls[1] = NEG_INF;
+      const float Mn = fmaxf(M, fmaxf(ls[0], ls[1]));
+      const float rs = __builtin_amdgcn_exp2f(M - Mn);
+      L *= rs;
+#pragma unroll
+      for (int D4 = 0; D4 < 4; ++D4) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[D4][e] *= rs;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool use = ls[j] != NEG_INF;
+        const float wgt = use ? __builtin_amdgcn_exp2f(ls[j] - Mn) : 0.f;
+        L += wgt;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t xs[4] = {use ? x[j][u].x : 0u, use ? x[j][u].y : 0u, use ? x[j][u].z : 0u,
+                                  use ? x[j][u].w : 0u};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = (u & 1) * 8 + 2 * c;
+            o[u >> 1][e] += wgt * __uint_as_float(xs[c] << 16);
+            o[u >> 1][e + 1] += wgt * __uint_as_float(xs[c] & 0xFFFF0000u);
+          }
+        }
+      }
+      M = Mn;
+    }
+    if (cur.valid) {
+      const float inv = 1.f / L;
+      // accumulator (D4, e) of lane (col, half) is head dim 32*D4 + 8*(e/4) + 4*half + e%4
+      uint16_t* dst = out + qoff + 4 * half;
+#pragma unroll
+      for (int D4 = 0; D4 < 4; ++D4) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<uint2*>(dst + 32 * D4 + 8 * a) =
+              make_uint2(pack_bf16x2(o[D4][4 * a] * inv, o[D4][4 * a + 1] * inv),
+                         pack_bf16x2(o[D4][4 * a + 2] * inv, o[D4][4 * a + 3] * inv));
+      }
+      if (lse_out && half == 0)
+        lse_out[((int64_t)b * D.h_q + g * D.G + hh) * D.n_q + cur.i] = (M + __log2f(L)) * 0.69314718055994531f;
     }
   }
-  const float inv = 1.f / wsum;
-  // lane order -> head dims: value n = 8*(u%8) + c of half u/8 sits at
-  // d = 32*(n/16) + 8*((n%16)/4) + 4*half + n%4
-  const int half = u >> 3, v8 = u & 7;
-  const int d0 = 32 * (v8 >> 1) + 16 * (v8 & 1) + 4 * half;
-  const int g = (int)(bg % D.h_kv), b = (int)(bg / D.h_kv);
-  uint16_t* dst = out + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + h) * kHeadDim;
-  *reinterpret_cast<uint2*>(dst + d0) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
-                                                  pack_bf16x2(acc[2] * inv, acc[3] * inv));
-  *reinterpret_cast<uint2*>(dst + d0 + 8) = make_uint2(pack_bf16x2(acc[4] * inv, acc[5] * inv),
-                                                      pack_bf16x2(acc[6] * inv, acc[7] * inv));
-  if (lse_out && u == 0)
-    lse_out[((int64_t)b * D.h_q + g * D.G + h) * D.n_q + i] = (m + __log2f(wsum)) * 0.69314718055994531f;
 }
 
 int persistent_grid() {  // a multiple of kXcds
@@ -504,7 +600,7 @@ int persistent_grid() {  // a multiple of kXcds
       n = 256;
     cus = n;
   }
-  return (2 * cus + kXcds - 1) / kXcds * kXcds;  // two 68 KB-LDS workgroups fit one CU
+  return (cus + kXcds - 1) / kXcds * kXcds;  // one 131 KB-LDS workgroup of 8 waves per CU
 }
 
 }  // namespace
@@ -513,10 +609,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream) {
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_tiles<false>, dim3(persistent_grid()), dim3(256), 0, stream, q, k, v, ws, D);
-  hipLaunchKernelGGL(k_attn_tiles<true>, dim3(persistent_grid()), dim3(256), 0, stream, q, k, v, ws, D);
-  const int64_t threads = (int64_t)D.B * D.h_kv * D.n_q * D.G * 16;
-  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, ws, out, lse, D);
+  hipLaunchKernelGGL(k_attn_tiles<false>, dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws, D);
+  hipLaunchKernelGGL(k_attn_local_merge, dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws, out, lse, D);
   return hipGetLastError();
 }
 

@@ -4,7 +4,7 @@ import pytest
 
 from block_sparse_long_qk_amd import build
 
-HOT = ("k_index_scores", "k_attn_tiles", "k_index_small", "k_attn_rows", "k_block_topk", "k_attn_merge")
+HOT = ("k_index_scores", "k_attn_tiles", "k_index_small", "k_attn_rows", "k_block_topk", "k_attn_local_merge")
 
 
 @pytest.fixture(scope="module")
