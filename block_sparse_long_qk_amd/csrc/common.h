@@ -19,6 +19,11 @@ constexpr int kRowsPart = 16 * kHeadDim + 16;  // floats per query-outer partial
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
 // Problem dimensions as the kernels see them (all derived on the host).
 struct Dims {

@@ -25,10 +25,12 @@ namespace {
 template <int DIDX>
 struct IdxCfg {
   static constexpr int KS = DIDX / 16;              // MFMA k-steps per key row
-  static constexpr int PITCH = DIDX + 8;            // LDS row pitch (bf16), 16-byte pad
-  static constexpr int CHUNKS = kBk * DIDX / 8;     // 16-byte chunks per key block
-  static constexpr int PER_THREAD = CHUNKS / 256;
-  static constexpr int CPR = DIDX / 8;              // chunks per key row
+  static constexpr int CPR = DIDX / 8;              // 16-byte chunks per key row
+  static constexpr int RPI = 1024 / (2 * DIDX);     // key rows per 1 KB direct-to-LDS instruction
+  static constexpr int NI = kBk / RPI / 4;          // such instructions per wave per block
+  // slot of chunk c of key row r is c ^ swz(r): the 16 lanes reading one chunk
+  // of 16 consecutive rows then cover all 64 banks once
+  static __device__ __forceinline__ int swz(int r) { return DIDX == 128 ? (r & 15) : ((r >> 1) & 7); }
 };
 
 // Sort the KK selected block ids of a lane ascending (bitonic network over a
@@ -64,12 +66,16 @@ __device__ __forceinline__ void sort_ids(int (&ti)[KK]) {
 // by (score desc, index asc) in registers and writes the block_idx row (k = KK+1)
 // exactly as the standalone top-k does from the same fp32 scores.
 template <int DIDX, int KK>
-__global__ __launch_bounds__(256) void k_index_scores(const uint16_t* __restrict__ iq,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_index_scores(const uint16_t* __restrict__ iq,
                                                       const uint16_t* __restrict__ ik, float* __restrict__ pooled,
                                                       int32_t* __restrict__ block_idx, Dims D,
                                                       int32_t blocks_per_split) {
   using C = IdxCfg<DIDX>;
-  __shared__ __align__(16) uint16_t lds[2][kBk * C::PITCH];
+  // two key blocks (rows unpadded, chunks swizzled) as two separate arrays, each
+  // named statically where it is used: the compiler can then tell a read of
+  // one from the direct-to-LDS loads filling the other and does not wait for them
+  __shared__ __align__(16) uint16_t lds0[kBk * DIDX];
+  __shared__ __align__(16) uint16_t lds1[kBk * DIDX];
   __shared__ __align__(16) float pstage[KK == 0 ? 4 : 1][64][kPoolStage];  // per-lane pooled staging
   const float NEG_INF = -__builtin_huge_valf();
 
@@ -127,58 +133,56 @@ __global__ __launch_bounds__(256) void k_index_scores(const uint16_t* __restrict
   }
 
   const uint16_t* ikb = ik + (int64_t)b * D.n_kv * DIDX;
-  // two register stages: block t+2 is fetched while block t computes, so a
-  // load has two block-iterations to arrive before it is parked in LDS
-  uint4 stage[2][C::PER_THREAD];
-  auto load_block = [&](int t, uint4 (&st)[C::PER_THREAD]) {
+  // Key blocks arrive by direct global-to-LDS loads one block ahead: the
+  // hardware writes lane l's 16 bytes at l * 16 past the instruction's LDS
+  // address, so lane l of instruction i fetches the chunk that belongs in slot
+  // l % CPR of row RPI * i + l / CPR.  Keys past the cache end repeat its last
+  // key: finite values the causal mask drops (they follow every row's
+  // position), so the loads need no per-key branch.
+  auto fetch_block = [&](int t, uint16_t* dst) {
     const int64_t j0 = (int64_t)t * kBk;
-    if (j0 + kBk <= D.n_kv) {  // whole block inside the cache: no per-key test
 #pragma unroll
-      for (int u = 0; u < C::PER_THREAD; ++u) {
-        const int c = threadIdx.x + 256 * u;
-        st[u] = *reinterpret_cast<const uint4*>(ikb + (j0 + c / C::CPR) * DIDX + (c % C::CPR) * 8);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < C::PER_THREAD; ++u) {
-        const int c = threadIdx.x + 256 * u;
-        const int64_t j = j0 + c / C::CPR;
-        st[u] = (j < D.n_kv) ? *reinterpret_cast<const uint4*>(ikb + j * DIDX + (c % C::CPR) * 8)
-                             : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_block = [&](int buf, const uint4 (&st)[C::PER_THREAD]) {
-#pragma unroll
-    for (int u = 0; u < C::PER_THREAD; ++u) {
-      const int c = threadIdx.x + 256 * u;
-      *reinterpret_cast<uint4*>(&lds[buf][(c / C::CPR) * C::PITCH + (c % C::CPR) * 8]) = st[u];
+    for (int u = 0; u < C::NI; ++u) {
+      const int i = wave * C::NI + u;
+      const int row = C::RPI * i + lane / C::CPR, sl = lane % C::CPR;
+      const int64_t j = min(j0 + row, (int64_t)D.n_kv - 1);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ikb + j * DIDX + 8 * (sl ^ C::swz(row))),
+                                       (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, 0, 0);
     }
   };
 
-  load_block(t_begin, stage[0]);
-  if (t_begin + 1 < t_end) load_block(t_begin + 1, stage[1]);
-  store_block(0, stage[0]);
-  __syncthreads();
-  // one block: compute block t from LDS buffer SG, fetch block t+2 into
-  // stage[SG], park block t+1 (stage[SG^1]) into the other buffer
-  auto process = [&](int t, auto sg_c) {
-    constexpr int sg = decltype(sg_c)::value;
-    constexpr int buf = sg;
-    if (t + 2 < t_end) load_block(t + 2, stage[sg]);
+  fetch_block(t_begin, lds0);
+  auto process = [&](int t, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const uint16_t* cur = buf == 0 ? lds0 : lds1;
+    // this wave's part of block t has landed; after the barrier every part has,
+    // and every wave is done with block t-1, whose buffer takes block t+1
+    // (past the end: a repeat of the last block, never used, so that every
+    // path issues the same loads)
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    fetch_block(min(t + 1, t_end - 1), buf == 0 ? lds1 : lds0);
     if (wave_active) {
       const bool need_mask = (int64_t)t * kBk + kBk - 1 > p_wave_min;
       float run0 = NEG_INF, run1 = NEG_INF;
 #pragma unroll 1
       for (int mt = 0; mt < 4; ++mt) {
         f32x16 a0 = {}, a1 = {};
-        const uint16_t* arow = &lds[buf][(32 * mt + col) * C::PITCH + 8 * half];
+        const int arow_i = 32 * mt + col;
+        const uint16_t* arow = cur + arow_i * DIDX;
+        const int asw = C::swz(arow_i);
+        // all fragments of the 32 keys read up front (8 LDS reads in flight),
+        // then the two MFMA chains
+        uint4 af[C::KS];
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) af[ks] = *reinterpret_cast<const uint4*>(arow + 8 * ((2 * ks + half) ^ asw));
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          const uint4 a = *reinterpret_cast<const uint4*>(arow + 16 * ks);
-          a0 = mfma_32x32x16(a, qb[0][ks], a0);
-          a1 = mfma_32x32x16(a, qb[1][ks], a1);
+          a0 = mfma_32x32x16(af[ks], qb[0][ks], a0);
+          a1 = mfma_32x32x16(af[ks], qb[1][ks], a1);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, C::KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KS, 0);
         if (need_mask) {
           // key (t*Bk + 32*mt + row) is visible to column position p iff row <= p - (t*Bk + 32*mt)
           const int64_t base = (int64_t)t * kBk + 32 * mt;
@@ -234,13 +238,12 @@ __global__ __launch_bounds__(256) void k_index_scores(const uint16_t* __restrict
         }
       }
     }
-    if (t + 1 < t_end) store_block(buf ^ 1, stage[sg ^ 1]);
-    __syncthreads();
   };
   for (int t = t_begin; t < t_end; t += 2) {
     process(t, std::integral_constant<int, 0>{});
     if (t + 1 < t_end) process(t + 1, std::integral_constant<int, 1>{});
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the last (unused) block fetch has landed before the workgroup ends
 
   if constexpr (KK > 0) {
     if (out_row >= 0) {

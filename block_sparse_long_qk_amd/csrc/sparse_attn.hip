@@ -39,9 +39,6 @@ constexpr int kPstPitch = 272;     // LDS pitch (bytes) of a partial row being s
 constexpr int kWaves = 8;          // waves per tile workgroup (kWaves * 32 = 256 rows per tile)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQRegion = 32 * 256; // LDS bytes of one wave's 32 query rows
-// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
-constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
-constexpr int kWaitLgkm0 = 0xC07F; // lgkmcnt(0)
 
 // Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS
 // with the workgroup's kThreads threads.  Keys at or past n_valid (n_valid >= 1)
