@@ -42,8 +42,8 @@ struct AttnWs {
   int32_t* off;        // [bins+1] exclusive scan of cnt
   int32_t* tile_off;   // [bins+1] exclusive scan of ceil(cnt / pt); last = tile count
   int2* list;          // [max_tiles * pt] {row-slot id i * k + s (-1 = empty), bin of the tile}, tile-major
-  float* part_lse;     // [B*h_kv*n_q*(k+1)][G]     base-2 log-sum-exp of each partial (slot k: local)
-  uint16_t* part_o;    // [B*h_kv*n_q*(k+1)][G][d]  normalised partial outputs, bf16, lane order
+  float* part_lse;     // [B*h_kv*n_q*(k+1)][G]     base-2 log-sum-exp of each non-local partial (-inf: none)
+  uint16_t* part_o;    // [B*h_kv*n_q*(k+1)][16][G][8] normalised partials, bf16, chunk-major per block
   int64_t max_tiles;
   int64_t n_bins;      // B * h_kv * query groups * n_blk
   int32_t n_groups;    // query groups per (b, g)

@@ -35,7 +35,6 @@ constexpr int KP = kHeadDim + 8;   // LDS pitch of K rows (bf16): 16-byte pad
 constexpr int kXcds = 8;           // XCDs of an MI355X; workgroups are dealt round-robin over them
 constexpr int kRun = 8;            // consecutive tiles one workgroup takes before moving on
 constexpr int VP = kBk + 4;        // LDS pitch of V^T rows (bf16): 8-byte pad
-constexpr int kPstPitch = 272;     // LDS pitch (bytes) of a partial row being stored: 16-byte pad
 constexpr int kWaves = 8;          // waves per tile workgroup (kWaves * 32 = 256 rows per tile)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQRegion = 32 * 256; // LDS bytes of one wave's 32 query rows
@@ -313,18 +312,6 @@ __device__ __forceinline__ Walk walk_next(const Walk& w, int stride, int hi) {
   return n;
 }
 
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ int64_t shfl_i64(int64_t x, int src) {
-  const uint32_t lo = __shfl((uint32_t)x, src, 64);
-  const uint32_t hi = __shfl((uint32_t)((uint64_t)x >> 32), src, 64);
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 // The wave's 32 normalised partials, bf16 in lane order: row q's 128 values
 // are lane q's 64 then lane q+32's 64, in accumulator order.
 __device__ __forceinline__ void pack_partial(const f32x16 (&o)[4], float inv, uint4 (&w)[8]) {
@@ -338,36 +325,21 @@ __device__ __forceinline__ void pack_partial(const f32x16 (&o)[4], float inv, ui
   }
 }
 
-// Store packed partials and their log-sum-exps.  Stored straight from the MFMA
-// layout, one instruction would scatter 64 pieces of 16 bytes over 32 rows;
-// instead the rows go through the wave's LDS buffer eight at a time and 16
-// consecutive lanes write each 256-byte row.  The buffer's rows are padded to
-// 272 bytes: the eight rows then start on different banks, and neither the
-// writes (16 lanes, one 128-byte half row each) nor the reads conflict.
+// Store a wave's packed partials and their log-sum-exps.  The partials of one
+// (sequence, group, query, slot) form a block of G x 128 bf16 laid out
+// chunk-major: 16-byte chunk c of head h at (c * G + h) * 16 bytes, chunk
+// 8 * half + u holding w[u] of lane (column, half).  A wave's 32 rows are
+// whole query positions (all G heads) whenever G divides 32, so for each u
+// the lanes of one position write (or, in the merge, read) consecutive 16-byte
+// chunks straight from the MFMA layout, with no transposition.
 __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-                                               unsigned char* stage, const uint4 (&w)[8], float lse, bool valid,
-                                               int64_t pidx, int lane) {
-  const int col = lane & 31, half = lane >> 5;
-  if (valid && half == 0) part_lse[pidx] = lse;
+                                               const uint4 (&w)[8], float lse, bool valid, int64_t pblk, int hh,
+                                               int G, int half) {
+  if (valid) {
+    if (half == 0) part_lse[pblk * G + hh] = lse;
+    uint16_t* dst = part_o + pblk * G * kHeadDim + hh * 8;
 #pragma unroll
-  for (int rho = 0; rho < 4; ++rho) {
-    if ((col >> 3) == rho) {
-      unsigned char* dst = stage + (col & 7) * kPstPitch + half * 128;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(dst + 16 * u) = w[u];
-    }
-    wave_lds_fence();
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int chunk = 64 * j + lane;            // 128 chunks of 16 bytes: 8 rows x 256 bytes
-      const int rr = chunk >> 4, c16 = chunk & 15;
-      const int owner = 8 * rho + rr;             // lane (column) holding that row
-      const int64_t rp = shfl_i64(pidx, owner);
-      const bool rv = __shfl((int)valid, owner, 64) != 0;
-      const uint4 x = *reinterpret_cast<const uint4*>(stage + rr * kPstPitch + c16 * 16);
-      if (rv) *reinterpret_cast<uint4*>(part_o + rp * kHeadDim + c16 * 8) = x;
-    }
-    wave_lds_fence();
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(dst + (8 * half + u) * G * 8) = w[u];
   }
 }
 
@@ -388,14 +360,13 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, fl
 // vector loads and stores alike, so a wait for loads waits for every store
 // issued before them: issued where they are, the stores and the next rows
 // have a whole softmax and P.V to land before the next tile waits for them.
-// The wave's LDS region doubles as the staging buffer of the stores.
 template <bool LOCAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_tiles(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, AttnWs ws,
     Dims D) {
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
-  __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];  // per wave: its query rows, or partials on their way out
+  __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];  // per wave: its query rows
   int total;
   if constexpr (LOCAL) {
     const int64_t a0 = D.offset / D.pt;
@@ -425,7 +396,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   Walk w1 = walk_next(w0, stride, hi);
   TileRaw raw1 = tile_raw<LOCAL>(ws, D, min(w1.tile, hi - 1), ps);
   uint4 pw[8];
-  int64_t ppidx = 0;
+  int64_t ppblk = 0;
   float plse = 0.f;
   bool pvalid = false, have = false;  // have: a packed partial waits in pw (uniform)
   // outer loop: one staged K/V block; inner loop: the tiles that use it
@@ -448,7 +419,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // past the last tile: a stand-in decode of the last one (loads stay in bounds, results unused)
       const TileRow nxt = tile_row<LOCAL>(raw1, D, ws, min(w1.tile, hi - 1), ps);
       __builtin_amdgcn_sched_barrier(0);
-      if (have) store_partials(ws.part_o, ws.part_lse, qw, pw, plse, pvalid, ppidx, lane);
+      if (have) store_partials(ws.part_o, ws.part_lse, pw, plse, pvalid, ppblk, hh, D.G, half);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // LDS reads of the region are done before it is refilled
       __builtin_amdgcn_sched_barrier(0);
       fetch_q_rows(qw, q_row(nxt), half);
@@ -459,7 +430,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       float m2, l;
       softmax_pv<LOCAL>(Vt, s, lane, D.scale_log2, (int64_t)cur.t * kBk, D.offset + cur.i, o, m2, l);
       pack_partial(o, 1.f / l, pw);
-      ppidx = ((((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s) * D.G + hh);
+      ppblk = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s;
       plse = m2 + __log2f(l);
       pvalid = cur.valid;
       have = true;
@@ -471,7 +442,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     } while (same);
     __syncthreads();  // every wave is done with the staged block
   }
-  if (have) store_partials(ws.part_o, ws.part_lse, qw, pw, plse, pvalid, ppidx, lane);
+  if (have) store_partials(ws.part_o, ws.part_lse, pw, plse, pvalid, ppblk, hh, D.G, half);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the last (unused) row fetch has landed before the workgroup ends
 }
 
@@ -525,36 +496,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_sched_barrier(0);
     softmax_pv<true>(Vt, sc, lane, D.scale_log2, (int64_t)cur.t * kBk, D.offset + cur.i, o, m2, l);
 
-    // fold in the non-local partials: this lane's 64 values of each are the
-    // 128 bytes at half * 128 of the row's 256, in accumulator order
+    // fold in the non-local partials (chunk-major blocks, see store_partials):
+    // this lane's 64 values of each are chunks 8 * half .. 8 * half + 7 of its
+    // head, in accumulator order.  The max
+    // over all slots comes first (lse loads only), so the fold never rescales;
+    // partial loads run one batch of two slots ahead of the fold.
     const int64_t prow = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1);
     const float* lse_p = ws.part_lse + prow * D.G + hh;                       // slot s at s * G
-    const uint16_t* o_p = ws.part_o + (prow * D.G + hh) * kHeadDim + 64 * half;  // slot s at s * G * 128
-    float M = m2, L = l;
-    for (int s0 = 0; s0 < D.k; s0 += 2) {
-      float ls[2];
-      uint4 x[2][8];
+    const uint16_t* o_p = ws.part_o + prow * D.G * kHeadDim + (8 * half * D.G + hh) * 8;  // slot s at s * G * 128
+    float M = m2;
+    for (int s0 = 0; s0 < D.k; s0 += 8) {
+      float lv[8];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int sl = min(s0 + j, D.k - 1);
-        ls[j] = lse_p[(int64_t)sl * D.G];
-        const uint16_t* src = o_p + (int64_t)sl * D.G * kHeadDim;
+      for (int j = 0; j < 8; ++j) lv[j] = lse_p[(int64_t)min(s0 + j, D.k - 1) * D.G];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[j][u] = *reinterpret_cast<const uint4*>(src + 8 * u);
-      }
-      if (s0 + 1 >= D.k) ls[1] = NEG_INF;
-      const float Mn = fmaxf(M, fmaxf(ls[0], ls[1]));
-      const float rs = __builtin_amdgcn_exp2f(M - Mn);
-      L *= rs;
+      for (int j = 0; j < 8; ++j) M = fmaxf(M, lv[j]);
+    }
+    {
+      const float rs = __builtin_amdgcn_exp2f(m2 - M);
 #pragma unroll
       for (int D4 = 0; D4 < 4; ++D4) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[D4][e] *= rs;
       }
+      l *= rs;
+    }
+    float L = l;
+    auto load_batch = [&](int s0, float (&ls)[2], uint4 (&x)[2][8]) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int sl = min(s0 + j, D.k - 1);
+        ls[j] = s0 + j < D.k ? lse_p[(int64_t)sl * D.G] : NEG_INF;
+        const uint16_t* src = o_p + (int64_t)sl * D.G * kHeadDim;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[j][u] = *reinterpret_cast<const uint4*>(src + u * D.G * 8);
+      }
+    };
+    auto fold = [&](const float (&ls)[2], const uint4 (&x)[2][8]) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const bool use = ls[j] != NEG_INF;
-        const float wgt = use ? __builtin_amdgcn_exp2f(ls[j] - Mn) : 0.f;
+        const float wgt = use ? __builtin_amdgcn_exp2f(ls[j] - M) : 0.f;
         L += wgt;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -568,7 +550,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           }
         }
       }
-      M = Mn;
+    };
+    {
+      float la[2], lb[2];
+      uint4 xa[2][8], xb[2][8];
+      load_batch(0, la, xa);
+      for (int s0 = 0; s0 < D.k; s0 += 4) {
+        load_batch(s0 + 2, lb, xb);
+        fold(la, xa);
+        if (s0 + 2 >= D.k) break;
+        load_batch(s0 + 4, la, xa);
+        fold(lb, xb);
+      }
     }
     if (cur.valid) {
       const float inv = 1.f / L;
