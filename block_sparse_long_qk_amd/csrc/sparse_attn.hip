@@ -83,18 +83,33 @@ __device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint1
   }
 }
 
-// A wave's query rows live in its 8 KB LDS region chunk-major: 16-byte chunk
-// c (dims 8c..8c+7) of row r (0..31) at c * 512 + r * 16, so the 32 lanes that
-// read one chunk of 32 rows read 512 consecutive bytes.  The rows are fetched
-// with direct global-to-LDS loads, which place lane l's 16 bytes at l * 16 past
-// the instruction's LDS address: instruction u has lane (col, half) fetch
-// chunk 2u + half of its own row, which lands exactly there.  Rows that do not
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
+  const uint32_t lo = __shfl((uint32_t)x, src, 64);
+  const uint32_t hi = __shfl((uint32_t)(x >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// A wave's query rows live in its 8 KB LDS region row-major: row r (0..31) at
+// r * 256 bytes, its 16-byte chunk c (dims 8c..8c+7) in slot c ^ (r % 16), so
+// that the 16 lanes reading one chunk of 16 rows hit 16 different bank groups.
+// The rows are fetched with direct global-to-LDS loads, which place lane l's
+// 16 bytes at l * 16 past the instruction's LDS address: instruction u fills
+// rows 4u..4u+3, the 16 lanes of a row fetching its 16 chunks (permuted), so
+// every load instruction reads whole 256-byte rows.  `mine` is the row this
+// lane's column owns (lanes l and l ^ 32 own the same one); rows that do not
 // exist point at a stand-in row whose results are never stored.
-__device__ __forceinline__ void fetch_q_rows(unsigned char* qw, const uint16_t* mine, int half) {
+__device__ __forceinline__ void fetch_q_rows(unsigned char* qw, const uint16_t* mine, int lane) {
+  const uint64_t me = reinterpret_cast<uint64_t>(mine);
+  uint64_t row[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(mine + 8 * (2 * u + half)),
+  for (int u = 0; u < 8; ++u) row[u] = shfl_u64(me, 4 * u + (lane >> 4));
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int r = 4 * u + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(row[u] + 16 * c),
                                      (__attribute__((address_space(3))) void*)(qw + 1024 * u), 16, 0, 0);
+  }
 }
 
 // S^T = K Q^T for one wave: the 128 keys of the staged block (4 row tiles of
@@ -104,11 +119,12 @@ __device__ __forceinline__ void fetch_q_rows(unsigned char* qw, const uint16_t* 
 __device__ __forceinline__ void qk_block(const uint16_t* Ks, const unsigned char* qw, int lane, f32x16 (&s)[4]) {
   const int col = lane & 31, half = lane >> 5;
   const uint16_t* kbase = Ks + col * KP + 8 * half;
-  const unsigned char* qbase = qw + half * 512 + col * 16;
+  const unsigned char* qbase = qw + col * 256;
+  const int qsw = col & 15;
   uint4 kf[2][4], qf[2];
 #pragma unroll
   for (int T = 0; T < 4; ++T) kf[0][T] = *reinterpret_cast<const uint4*>(kbase + 32 * T * KP);
-  qf[0] = *reinterpret_cast<const uint4*>(qbase);
+  qf[0] = *reinterpret_cast<const uint4*>(qbase + 16 * (half ^ qsw));
 #pragma unroll
   for (int T = 0; T < 4; ++T) s[T] = f32x16{};
 #pragma unroll
@@ -117,7 +133,7 @@ __device__ __forceinline__ void qk_block(const uint16_t* Ks, const unsigned char
     if (ks + 1 < 8) {
 #pragma unroll
       for (int T = 0; T < 4; ++T) kf[nb][T] = *reinterpret_cast<const uint4*>(kbase + 32 * T * KP + 16 * (ks + 1));
-      qf[nb] = *reinterpret_cast<const uint4*>(qbase + (ks + 1) * 1024);
+      qf[nb] = *reinterpret_cast<const uint4*>(qbase + 16 * ((2 * (ks + 1) + half) ^ qsw));
     }
 #pragma unroll
     for (int T = 0; T < 4; ++T) s[T] = mfma_32x32x16(kf[cb][T], qf[cb], s[T]);
@@ -392,7 +408,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
 
   TileRow cur = tile_row<LOCAL>(tile_raw<LOCAL>(ws, D, w0.tile, ps), D, ws, w0.tile, ps);
-  fetch_q_rows(qw, q_row(cur), half);
+  fetch_q_rows(qw, q_row(cur), lane);
   Walk w1 = walk_next(w0, stride, hi);
   TileRaw raw1 = tile_raw<LOCAL>(ws, D, min(w1.tile, hi - 1), ps);
   uint4 pw[8];
@@ -422,7 +438,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (have) store_partials(ws.part_o, ws.part_lse, pw, plse, pvalid, ppblk, hh, D.G, half);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // LDS reads of the region are done before it is refilled
       __builtin_amdgcn_sched_barrier(0);
-      fetch_q_rows(qw, q_row(nxt), half);
+      fetch_q_rows(qw, q_row(nxt), lane);
       Walk w2 = w1;
       if (more) w2 = walk_next(w1, stride, hi);
       const TileRaw raw2 = tile_raw<LOCAL>(ws, D, min(w2.tile, hi - 1), ps);
@@ -478,7 +494,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const TileRow cur = tile_row<true>(TileRaw{-1, 0}, D, ws, w.tile, ps);
     const int g = cur.bg % D.h_kv, b = cur.bg / D.h_kv;
     const int64_t qoff = (((int64_t)b * D.n_q + (cur.valid ? cur.i : 0)) * D.h_q + g * D.G + hh) * kHeadDim;
-    fetch_q_rows(qw, q + qoff, half);
+    fetch_q_rows(qw, q + qoff, lane);
     if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform
       if (staged_bg >= 0) __syncthreads();
       const int64_t key0 = (int64_t)cur.t * kBk;
