@@ -495,6 +495,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int g = cur.bg % D.h_kv, b = cur.bg / D.h_kv;
     const int64_t qoff = (((int64_t)b * D.n_q + (cur.valid ? cur.i : 0)) * D.h_q + g * D.G + hh) * kHeadDim;
     fetch_q_rows(qw, q + qoff, lane);
+    // The row's non-local partials (chunk-major blocks, see store_partials):
+    // this lane's 64 values of each are chunks 8 * half .. 8 * half + 7 of its
+    // head, in accumulator order.  Their log-sum-exps are requested before the
+    // local block is computed, so the max over all slots is known before the
+    // fold, which therefore never rescales; partial loads run one slot ahead of
+    // the fold.
+    const int64_t prow = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1);
+    const float* lse_p = ws.part_lse + prow * D.G + hh;                       // slot s at s * G
+    const uint16_t* o_p = ws.part_o + prow * D.G * kHeadDim + (8 * half * D.G + hh) * 8;  // slot s at s * G * 128
+    auto load_slot = [&](int s0, float& ls, uint4 (&x)[8]) {  // past slot k-1: weight 0
+      const int sl = min(s0, D.k - 1);
+      ls = s0 < D.k ? lse_p[(int64_t)sl * D.G] : NEG_INF;
+      const uint16_t* src = o_p + (int64_t)sl * D.G * kHeadDim;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const uint4*>(src + u * D.G * 8);
+    };
+    float lv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float x = lse_p[(int64_t)min(j, D.k - 1) * D.G];
+      lv[j] = j < D.k ? x : NEG_INF;
+    }
+
     if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform
       if (staged_bg >= 0) __syncthreads();
       const int64_t key0 = (int64_t)cur.t * kBk;
@@ -507,27 +530,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     f32x16 sc[4], o[4];
     float m2, l;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the query rows have landed in LDS
+
+    float M = NEG_INF;  // the lse loads were issued after the row fetch: landed too
+#pragma unroll
+    for (int j = 0; j < 16; ++j) M = fmaxf(M, lv[j]);
     __builtin_amdgcn_sched_barrier(0);
     qk_block(Ks, qw, lane, sc);
     __builtin_amdgcn_sched_barrier(0);
-    softmax_pv<true>(Vt, sc, lane, D.scale_log2, (int64_t)cur.t * kBk, D.offset + cur.i, o, m2, l);
-
-    // fold in the non-local partials (chunk-major blocks, see store_partials):
-    // this lane's 64 values of each are chunks 8 * half .. 8 * half + 7 of its
-    // head, in accumulator order.  The max
-    // over all slots comes first (lse loads only), so the fold never rescales;
-    // partial loads run one batch of two slots ahead of the fold.
-    const int64_t prow = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1);
-    const float* lse_p = ws.part_lse + prow * D.G + hh;                       // slot s at s * G
-    const uint16_t* o_p = ws.part_o + prow * D.G * kHeadDim + (8 * half * D.G + hh) * 8;  // slot s at s * G * 128
-    float M = m2;
-    for (int s0 = 0; s0 < D.k; s0 += 8) {
-      float lv[8];
+    for (int s0 = 16; s0 < D.k; s0 += 8) {  // k > 16
+      float lw[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) lv[j] = lse_p[(int64_t)min(s0 + j, D.k - 1) * D.G];
+      for (int j = 0; j < 8; ++j) lw[j] = lse_p[(int64_t)min(s0 + j, D.k - 1) * D.G];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) M = fmaxf(M, lv[j]);
+      for (int j = 0; j < 8; ++j) M = fmaxf(M, lw[j]);
     }
+    softmax_pv<true>(Vt, sc, lane, D.scale_log2, (int64_t)cur.t * kBk, D.offset + cur.i, o, m2, l);
+    M = fmaxf(M, m2);
     {
       const float rs = __builtin_amdgcn_exp2f(m2 - M);
 #pragma unroll
@@ -538,44 +556,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       l *= rs;
     }
     float L = l;
-    auto load_batch = [&](int s0, float (&ls)[2], uint4 (&x)[2][8]) {
+    auto fold = [&](float ls, const uint4 (&x)[8]) {
+      const bool use = ls != NEG_INF;
+      const float wgt = use ? __builtin_amdgcn_exp2f(ls - M) : 0.f;
+      L += wgt;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int sl = min(s0 + j, D.k - 1);
-        ls[j] = s0 + j < D.k ? lse_p[(int64_t)sl * D.G] : NEG_INF;
-        const uint16_t* src = o_p + (int64_t)sl * D.G * kHeadDim;
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t xs[4] = {use ? x[u].x : 0u, use ? x[u].y : 0u, use ? x[u].z : 0u, use ? x[u].w : 0u};
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[j][u] = *reinterpret_cast<const uint4*>(src + u * D.G * 8);
-      }
-    };
-    auto fold = [&](const float (&ls)[2], const uint4 (&x)[2][8]) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bool use = ls[j] != NEG_INF;
-        const float wgt = use ? __builtin_amdgcn_exp2f(ls[j] - M) : 0.f;
-        L += wgt;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t xs[4] = {use ? x[j][u].x : 0u, use ? x[j][u].y : 0u, use ? x[j][u].z : 0u,
-                                  use ? x[j][u].w : 0u};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int e = (u & 1) * 8 + 2 * c;
-            o[u >> 1][e] += wgt * __uint_as_float(xs[c] << 16);
-            o[u >> 1][e + 1] += wgt * __uint_as_float(xs[c] & 0xFFFF0000u);
-          }
+        for (int c = 0; c < 4; ++c) {
+          const int e = (u & 1) * 8 + 2 * c;
+          o[u >> 1][e] += wgt * __uint_as_float(xs[c] << 16);
+          o[u >> 1][e + 1] += wgt * __uint_as_float(xs[c] & 0xFFFF0000u);
         }
       }
     };
     {
-      float la[2], lb[2];
-      uint4 xa[2][8], xb[2][8];
-      load_batch(0, la, xa);
-      for (int s0 = 0; s0 < D.k; s0 += 4) {
-        load_batch(s0 + 2, lb, xb);
+      float la, lb;
+      uint4 xa[8], xb[8];
+      load_slot(0, la, xa);
+      for (int s0 = 0; s0 < D.k; s0 += 2) {
+        load_slot(s0 + 1, lb, xb);
         fold(la, xa);
-        if (s0 + 2 >= D.k) break;
-        load_batch(s0 + 4, la, xa);
+        if (s0 + 1 >= D.k) break;
+        load_slot(s0 + 2, la, xa);
         fold(lb, xb);
       }
     }
