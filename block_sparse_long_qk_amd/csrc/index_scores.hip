@@ -66,7 +66,7 @@ __device__ __forceinline__ void sort_ids(int (&ti)[KK]) {
 // by (score desc, index asc) in registers and writes the block_idx row (k = KK+1)
 // exactly as the standalone top-k does from the same fp32 scores.
 template <int DIDX, int KK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_index_scores(const uint16_t* __restrict__ iq,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_index_scores(const uint16_t* __restrict__ iq,
                                                       const uint16_t* __restrict__ ik, float* __restrict__ pooled,
                                                       int32_t* __restrict__ block_idx, Dims D,
                                                       int32_t blocks_per_split) {
