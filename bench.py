@@ -139,7 +139,7 @@ def main():
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--decode-workload", default="decode_256k")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-positions", type=int, default=256)
+    ap.add_argument("--cpu-positions", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
