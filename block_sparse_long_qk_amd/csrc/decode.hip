@@ -8,8 +8,10 @@
 //
 // k_index_small: (query, group) rows of one sequence (at most 16) form the
 //   MFMA B operand in registers; every wave streams its own range of 128-key
-//   blocks of index_k straight from HBM into 16x16x32 bf16 MFMA A operands (no
-//   LDS, no barriers) and max-pools each block in registers.
+//   blocks of index_k with coalesced loads into a register ring one block
+//   deep, parks each 32-key step in a per-wave LDS buffer, reads it back as
+//   16x16x32 bf16 MFMA A operands (no workgroup barriers) and max-pools each
+//   block in registers.
 // k_attn_rows: query-outer attention.  One wave per (row, slot): it loads the
 //   slot's K block as MFMA B operands, computes the G x 128 scores, the block's
 //   softmax statistics, and P V on the VALU from coalesced V rows; it writes an
@@ -33,24 +35,31 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Each wave streams its own range of 128-key blocks in steps of 32 keys: the
-// step's 32*DIDX*2 bytes are read with fully coalesced 16-byte loads (64 lanes
-// cover one contiguous 1 KB span per instruction), parked in a per-wave LDS
-// buffer with padded key rows, and read back as 16x16x32 MFMA A operands
-// (lane = key, lane group c = 8 index dims of each k-step).  The next step's
-// loads are in flight while the current step computes.  Only wave-level
-// ordering is needed: no workgroup barrier.
+// Each wave streams its own range of 128-key blocks in steps of 32 keys.  A
+// step's 32 * DIDX * 2 bytes are read with fully coalesced 16-byte loads (64
+// lanes cover one contiguous 1 KB span per instruction) into a register ring
+// one block (four steps) deep, so 32 KB per wave are always in flight; each
+// step is parked in the wave's LDS buffer (padded key rows), read back as
+// 16x16x32 MFMA A operands (lane = key, lane group c = 8 index dims of each
+// k-step) and max-pooled, and its ring slot is refilled with the same step of
+// the next block.  Only wave-level ordering is needed: no workgroup barrier.
+// Loads past the cache end repeat its last key (masked: it follows every
+// row's position).  Pooled values wait in LDS and leave in batches, so stores
+// rarely interrupt the load stream.
 template <int DIDX>
 __global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict__ iq,
                                                      const uint16_t* __restrict__ ik, float* __restrict__ pooled,
                                                      Dims D, int32_t blocks_per_wave) {
-  constexpr int KS = DIDX / 32;            // MFMA k-steps per key
+  constexpr int KS = DIDX / 32;            // MFMA k-steps per key (16x16x32)
   constexpr int ROW = DIDX * 2;            // bytes per key
   constexpr int PITCH = ROW + 16;          // LDS bytes per key (pad: conflict-free operand reads)
   constexpr int STEP_KEYS = 32;
+  constexpr int NSTEP = kBk / STEP_KEYS;   // steps per block = ring depth
   constexpr int LOADS = STEP_KEYS * ROW / 1024;  // 16-byte loads per lane per step
   constexpr int KEYS_PER_LOAD = 1024 / ROW;      // keys one load instruction covers
+  constexpr int FLUSH = 16;                // pooled values staged per row before a store batch
   __shared__ __align__(16) unsigned char lds[4][STEP_KEYS * PITCH];
+  __shared__ float pst[4][16][FLUSH];
   const float NEG_INF = -__builtin_huge_valf();
   const int b = blockIdx.y;
   const int R = D.n_q * D.h_kv;  // <= 16
@@ -70,61 +79,79 @@ __global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict_
     qb[ks] = row_ok ? *reinterpret_cast<const uint4*>(iq + ((int64_t)b * R + n) * DIDX + 8 * (KS * c + ks))
                     : make_uint4(0, 0, 0, 0);
   int64_t out_base = -1;
-  if (row_ok && c == 0) {
+  if (row_ok) {
     const int i = n / D.h_kv, g = n % D.h_kv;
     out_base = (((int64_t)b * D.h_kv + g) * D.n_q + i) * D.n_blk;
   }
   const unsigned char* src = reinterpret_cast<const unsigned char*>(ik + (int64_t)b * D.n_kv * DIDX);
-  const int64_t key_end = D.n_kv;
+  const int64_t last_key = (int64_t)D.n_kv - 1;
   unsigned char* buf = lds[wave];
-  // this lane's slot in a load: key (u*KEYS_PER_LOAD + lane*16/ROW), byte offset (lane*16) % ROW
+  // this lane's slot in a load: key u*KEYS_PER_LOAD + lk, byte offset lo
   const int lk = (lane * 16) / ROW, lo = (lane * 16) % ROW;
-
-  const int steps = (t1 - t0) * (kBk / STEP_KEYS);
-  uint4 cur[LOADS];
-  auto fetch = [&](int st, uint4 (&x)[LOADS]) {
-    const int64_t key0 = (int64_t)t0 * kBk + (int64_t)st * STEP_KEYS;
+  auto fetch = [&](int t, int st, u32x4 (&x)[LOADS]) {
+    const int64_t key0 = (int64_t)t * kBk + st * STEP_KEYS;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int64_t key = key0 + u * KEYS_PER_LOAD + lk;
-      x[u] = key < key_end ? *reinterpret_cast<const uint4*>(src + key * ROW + lo) : make_uint4(0, 0, 0, 0);
+      const int64_t key = min(key0 + u * KEYS_PER_LOAD + lk, last_key);
+      x[u] = *reinterpret_cast<const u32x4*>(src + key * ROW + lo);
     }
   };
-  fetch(0, cur);
-  float m = NEG_INF;
-  for (int st = 0; st < steps; ++st) {
-    const int t = t0 + st / (kBk / STEP_KEYS);
-    // park this step's keys in LDS, then start the next step's loads
+  u32x4 ring[NSTEP][LOADS];  // native vectors: whole-register copies, no memcpy
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      *reinterpret_cast<uint4*>(buf + (u * KEYS_PER_LOAD + lk) * PITCH + lo) = cur[u];
-    wave_lds_fence();
-    if (st + 1 < steps) fetch(st + 1, cur);
-    const int64_t skey0 = (int64_t)t * kBk + (st % (kBk / STEP_KEYS)) * STEP_KEYS;
-    const bool need_mask = skey0 + STEP_KEYS - 1 > D.offset;
-#pragma unroll
-    for (int T = 0; T < STEP_KEYS / 16; ++T) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(buf + (16 * T + n) * PITCH + 16 * (KS * c + ks));
-        acc = mfma_16x16x32(a, qb[ks], acc);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x = acc[j];
-        if (need_mask && skey0 + 16 * T + 4 * c + j > pc) x = NEG_INF;
-        m = fmaxf(m, x);
-      }
+  for (int st = 0; st < NSTEP; ++st) {  // in slot order, as the loop refills them
+    fetch(t0, st, ring[st]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  auto flush = [&](int tb, int cnt) {
+    if (c == 0 && out_base >= 0) {
+      for (int j = 0; j < cnt; ++j)
+        if (tb + j <= l_row) pooled[out_base + tb + j] = pst[wave][n][j];
     }
-    wave_lds_fence();  // the buffer is rewritten next step
-    if ((st + 1) % (kBk / STEP_KEYS) == 0) {  // block t complete
-      m = fmaxf(m, __shfl_xor(m, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      if (out_base >= 0 && t <= l_row) pooled[out_base + t] = m;
-      m = NEG_INF;
+  };
+  int tb = t0;
+  for (int t = t0; t < t1; ++t) {
+    const int tn = min(t + 1, t1 - 1);  // next block (past the end: a repeat, never used)
+    float m = NEG_INF;
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      // park step st, refill its slot with the next block's step st
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u)
+        *reinterpret_cast<u32x4*>(buf + (u * KEYS_PER_LOAD + lk) * PITCH + lo) = ring[st][u];
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(tn, st, ring[st]);
+      __builtin_amdgcn_sched_barrier(0);
+      wave_lds_fence();
+      const int64_t skey0 = (int64_t)t * kBk + st * STEP_KEYS;
+      const bool need_mask = skey0 + STEP_KEYS - 1 > D.offset;
+#pragma unroll
+      for (int T = 0; T < STEP_KEYS / 16; ++T) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 a = *reinterpret_cast<const uint4*>(buf + (16 * T + n) * PITCH + 16 * (KS * c + ks));
+          acc = mfma_16x16x32(a, qb[ks], acc);
+        }
+        // accumulator j of lane (n, c) is key skey0 + 16*T + 4*c + j against row n
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x = acc[j];
+          if (need_mask && skey0 + 16 * T + 4 * c + j > pc) x = NEG_INF;
+          m = fmaxf(m, x);
+        }
+      }
+      wave_lds_fence();  // the buffer is rewritten next step
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (c == 0) pst[wave][n][t - tb] = m;
+    if (t - tb == FLUSH - 1) {
+      flush(tb, FLUSH);
+      tb = t + 1;
     }
   }
+  if (t1 > tb) flush(tb, t1 - tb);
 }
 
 // Is slot s of a row a block to attend?  Slot k stands for the local block
