@@ -389,8 +389,18 @@ size_t attn_rows_partial_bytes(const Dims& D) {
 hipError_t launch_index_small(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
                               hipStream_t stream) {
   const int t_max = (int)((D.offset + D.n_q - 1) / kBk) + 1;
-  // about 2048 workgroups of 4 waves over the whole batch, at least one block per wave
-  int64_t waves_per_b = (8192 + D.B - 1) / D.B;
+  // one resident round of waves over the whole batch (8 waves per CU: the
+  // kernel holds two waves per SIMD), at least one block per wave, so every
+  // wave fills its load ring once and then streams a long range
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+      ncu = 256;
+    cus = ncu;
+  }
+  int64_t waves_per_b = (8LL * cus + D.B - 1) / D.B;
   if (waves_per_b > t_max) waves_per_b = t_max;
   const int per = (int)((t_max + waves_per_b - 1) / waves_per_b);
   const int wgs = (int)(((t_max + per - 1) / per + 3) / 4);
