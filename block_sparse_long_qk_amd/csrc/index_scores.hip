@@ -165,41 +165,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (wave_active) {
       const bool need_mask = (int64_t)t * kBk + kBk - 1 > p_wave_min;
       float run0 = NEG_INF, run1 = NEG_INF;
+      // two 32-key row tiles per iteration: four MFMA chains of 8 k-steps (32
+      // MFMAs) between epilogues, each LDS fragment feeding two MFMAs
 #pragma unroll 1
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x16 a0 = {}, a1 = {};
-        const int arow_i = 32 * mt + col;
-        const uint16_t* arow = cur + arow_i * DIDX;
-        const int asw = C::swz(arow_i);
-        // all fragments of the 32 keys read up front (8 LDS reads in flight),
-        // then the two MFMA chains
-        uint4 af[C::KS];
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) af[ks] = *reinterpret_cast<const uint4*>(arow + 8 * ((2 * ks + half) ^ asw));
+      for (int mp = 0; mp < 2; ++mp) {
+        f32x16 a00 = {}, a01 = {}, a10 = {}, a11 = {};
+        const int r0 = 64 * mp + col, r1 = r0 + 32;
+        const uint16_t* arow0 = cur + r0 * DIDX;
+        const uint16_t* arow1 = cur + r1 * DIDX;
+        const int sw0 = C::swz(r0), sw1 = C::swz(r1);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          a0 = mfma_32x32x16(af[ks], qb[0][ks], a0);
-          a1 = mfma_32x32x16(af[ks], qb[1][ks], a1);
+          const uint4 f0 = *reinterpret_cast<const uint4*>(arow0 + 8 * ((2 * ks + half) ^ sw0));
+          const uint4 f1 = *reinterpret_cast<const uint4*>(arow1 + 8 * ((2 * ks + half) ^ sw1));
+          a00 = mfma_32x32x16(f0, qb[0][ks], a00);
+          a01 = mfma_32x32x16(f0, qb[1][ks], a01);
+          a10 = mfma_32x32x16(f1, qb[0][ks], a10);
+          a11 = mfma_32x32x16(f1, qb[1][ks], a11);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, C::KS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KS, 0);
-        if (need_mask) {
-          // key (t*Bk + 32*mt + row) is visible to column position p iff row <= p - (t*Bk + 32*mt)
-          const int64_t base = (int64_t)t * kBk + 32 * mt;
-          const int rel0 = (int)max<int64_t>(-1, min<int64_t>(64, pc[0] - base)) - 4 * half;
-          const int rel1 = (int)max<int64_t>(-1, min<int64_t>(64, pc[1] - base)) - 4 * half;
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int row = 8 * (e >> 2) + (e & 3);
-            if (row > rel0) a0[e] = NEG_INF;
-            if (row > rel1) a1[e] = NEG_INF;
+        for (int ks = 0; ks < C::KS; ++ks) {
+          if (ks + 2 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        auto pool = [&](f32x16& x0, f32x16& x1, int mt) {
+          if (need_mask) {
+            // key (t*Bk + 32*mt + row) is visible to column position p iff row <= p - (t*Bk + 32*mt)
+            const int64_t base = (int64_t)t * kBk + 32 * mt;
+            const int rel0 = (int)max<int64_t>(-1, min<int64_t>(64, pc[0] - base)) - 4 * half;
+            const int rel1 = (int)max<int64_t>(-1, min<int64_t>(64, pc[1] - base)) - 4 * half;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int row = 8 * (e >> 2) + (e & 3);
+              if (row > rel0) x0[e] = NEG_INF;
+              if (row > rel1) x1[e] = NEG_INF;
+            }
           }
-        }
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          run0 = fmaxf(run0, fmaxf(a0[e], a0[e + 1]));
-          run1 = fmaxf(run1, fmaxf(a1[e], a1[e + 1]));
-        }
+          for (int e = 0; e < 16; e += 2) {
+            run0 = fmaxf(run0, fmaxf(x0[e], x0[e + 1]));
+            run1 = fmaxf(run1, fmaxf(x1[e], x1[e + 1]));
+          }
+        };
+        pool(a00, a01, 2 * mp);
+        pool(a10, a11, 2 * mp + 1);
       }
       run0 = fmaxf(run0, wave_xor32(run0));
       run1 = fmaxf(run1, wave_xor32(run1));
