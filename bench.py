@@ -24,7 +24,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x2, calibrated on a 1 GiB copy) + WRITE_SIZE (x1); see
 # profiles/prefill_128k_attention_index_counters.md.  Valid for this kernel
 # version only: re-measure (or set None) when the kernel changes.
-INDEX_TRAFFIC_BYTES = (2.804e6 * 2 + 2.138e6) * 1024
+INDEX_TRAFFIC_BYTES = None  # kernel changed since the last counter run
 # The same for one msa_sparse_attn_fwd at 128K: k_attn_tiles<false> plus
 # k_attn_local_merge (the plan kernels add under 1%).
 ATTN_TRAFFIC_BYTES = ((1.770e7 + 1.865e7) * 2 + 3.172e7 + 2.285e6) * 1024
@@ -175,7 +175,7 @@ def main():
     idx_tflops = f_idx / (g["ms_index"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "k_index_scores", "achieved": round(idx_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(idx_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": INDEX_TRAFFIC_BYTES if w.name == "prefill_128k" else None}
+                "traffic": INDEX_TRAFFIC_BYTES if (w.name == "prefill_128k" and INDEX_TRAFFIC_BYTES) else None}
     stages = {
         "index_scores": {"ms": round(g["ms_index"], 4), "tflops": round(idx_tflops, 1),
                          "frac_mfma": round(idx_tflops / PEAK_BF16_TFLOPS, 4)},
