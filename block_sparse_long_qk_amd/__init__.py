@@ -7,7 +7,10 @@ import of a compute entry point raises; nothing falls back to another path.
 
 Entry points (same names as the C ABI, without the ``msa_`` prefix):
 ``index_scores``, ``block_topk``, ``sparse_attn_fwd``, ``forward``,
-``workspace_size``; ``Problem`` mirrors ``msa_problem``.
+``workspace_size``; ``Problem`` mirrors ``msa_problem``.  Each compute call
+takes an optional ``varlen`` (a ``Varlen``, mirroring ``msa_varlen``: per
+sequence query and cache lengths, packed query rows, a page table); given,
+the ``*_v`` variant of the C call is used.
 """
 from __future__ import annotations
 
@@ -22,7 +25,7 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = ra
 OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN, OP_FORWARD = range(4)
 
 EXPORTS = ("msa_workspace_size", "msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
-           "msa_status_string")
+           "msa_index_scores_v", "msa_block_topk_v", "msa_sparse_attn_fwd_v", "msa_forward_v", "msa_status_string")
 
 
 class Problem(ctypes.Structure):
@@ -52,6 +55,23 @@ class Problem(ctypes.Structure):
         return -(-self.n_kv // self.block_size)
 
 
+class Varlen(ctypes.Structure):
+    """msa_varlen: variable-length batches and paged caches (device pointers)."""
+    _fields_ = [
+        ("qo_lens", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p), ("q_starts", ctypes.c_void_p),
+        ("total_q", ctypes.c_int32),
+        ("page_table", ctypes.c_void_p), ("pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+    ]
+
+    @classmethod
+    def make(cls, qo_lens=None, kv_lens=None, q_starts=None, total_q=0, page_table=None, num_pages=0):
+        """From int32 device tensors (or None); page_table is [batch, pages_per_seq]."""
+        pps = int(page_table.shape[1]) if page_table is not None else 0
+        v = cls(_ptr(qo_lens), _ptr(kv_lens), _ptr(q_starts), int(total_q), _ptr(page_table), pps, int(num_pages))
+        v._keep = (qo_lens, kv_lens, q_starts, page_table)  # the tensors must outlive the calls
+        return v
+
+
 class MsaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -75,6 +95,11 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.msa_block_topk.argtypes = [P, vp, vp, vp]
         lib.msa_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        V = ctypes.POINTER(Varlen)
+        lib.msa_index_scores_v.argtypes = [P, V, vp, vp, vp, vp]
+        lib.msa_block_topk_v.argtypes = [P, V, vp, vp, vp]
+        lib.msa_sparse_attn_fwd_v.argtypes = [P, V, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.msa_forward_v.argtypes = [P, V, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTS[:-1]:
             getattr(lib, name).restype = ctypes.c_int
         lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -120,35 +145,55 @@ def workspace_size(p: Problem, op: int) -> int:
     return n.value
 
 
-def index_scores(p: Problem, index_q, index_k, pooled, stream=None):
+def index_scores(p: Problem, index_q, index_k, pooled, stream=None, varlen: Varlen | None = None):
     """pooled[b, g, i, t] = max over visible j in block t of index_q[b, i, g] . index_k[b, j]."""
-    _check(library().msa_index_scores(ctypes.byref(p), _ptr(index_q), _ptr(index_k), _ptr(pooled),
-                                      _stream(stream, pooled)), "msa_index_scores")
+    L, st = library(), _stream(stream, pooled)
+    if varlen is None:
+        rc = L.msa_index_scores(ctypes.byref(p), _ptr(index_q), _ptr(index_k), _ptr(pooled), st)
+    else:
+        rc = L.msa_index_scores_v(ctypes.byref(p), ctypes.byref(varlen), _ptr(index_q), _ptr(index_k), _ptr(pooled),
+                                  st)
+    _check(rc, "msa_index_scores")
     return pooled
 
 
-def block_topk(p: Problem, pooled, block_idx, stream=None):
+def block_topk(p: Problem, pooled, block_idx, stream=None, varlen: Varlen | None = None):
     """block_idx[b, g, i] = local block + top-(k-1) other visible blocks, ascending, -1 padded."""
-    _check(library().msa_block_topk(ctypes.byref(p), _ptr(pooled), _ptr(block_idx), _stream(stream, pooled)),
-           "msa_block_topk")
+    L, st = library(), _stream(stream, pooled)
+    if varlen is None:
+        rc = L.msa_block_topk(ctypes.byref(p), _ptr(pooled), _ptr(block_idx), st)
+    else:
+        rc = L.msa_block_topk_v(ctypes.byref(p), ctypes.byref(varlen), _ptr(pooled), _ptr(block_idx), st)
+    _check(rc, "msa_block_topk")
     return block_idx
 
 
 def sparse_attn_fwd(p: Problem, q, k, v, block_idx, out, lse=None, workspace=None, workspace_bytes=None,
-                    stream=None):
+                    stream=None, varlen: Varlen | None = None):
     """Softmax attention of every query head over its group's selected blocks."""
     nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
-    _check(library().msa_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out),
-                                         _ptr(lse), _ptr(workspace), nb, _stream(stream, q)), "msa_sparse_attn_fwd")
+    L, st = library(), _stream(stream, q)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(workspace), nb, st)
+    if varlen is None:
+        rc = L.msa_sparse_attn_fwd(ctypes.byref(p), *args)
+    else:
+        rc = L.msa_sparse_attn_fwd_v(ctypes.byref(p), ctypes.byref(varlen), *args)
+    _check(rc, "msa_sparse_attn_fwd")
     return out
 
 
 def forward(p: Problem, q, k, v, index_q, index_k, out, block_idx, lse=None, workspace=None, workspace_bytes=None,
-            stream=None):
+            stream=None, varlen: Varlen | None = None):
     """The whole MSA forward pass: index scores, block top-k, sparse attention."""
     nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
-    _check(library().msa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(index_q), _ptr(index_k), _ptr(out),
-                                 _ptr(block_idx), _ptr(lse), _ptr(workspace), nb, _stream(stream, q)), "msa_forward")
+    L, st = library(), _stream(stream, q)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(index_q), _ptr(index_k), _ptr(out), _ptr(block_idx), _ptr(lse),
+            _ptr(workspace), nb, st)
+    if varlen is None:
+        rc = L.msa_forward(ctypes.byref(p), *args)
+    else:
+        rc = L.msa_forward_v(ctypes.byref(p), ctypes.byref(varlen), *args)
+    _check(rc, "msa_forward")
     return out
 
 

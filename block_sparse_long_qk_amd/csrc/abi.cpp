@@ -62,6 +62,27 @@ msa_status derive(const msa_problem* p, Dims* D) {
   D->offset = offset;
   D->scale = p->softmax_scale;
   D->scale_log2 = (float)((double)p->softmax_scale * 1.4426950408889634);
+  D->qo_lens = D->kv_lens = D->q_starts = D->pages = nullptr;
+  D->pages_per_seq = D->num_pages = 0;
+  D->total_q = 0;
+  return MSA_OK;
+}
+
+// derive() plus the variable-length / paged description (vl may be null).
+msa_status derive_v(const msa_problem* p, const msa_varlen* vl, Dims* D) {
+  const msa_status st = derive(p, D);
+  if (st != MSA_OK || !vl) return st;
+  if ((vl->qo_lens || vl->kv_lens) && p->q_offset != -1) return MSA_ERR_INVALID_ARGUMENT;
+  if (vl->q_starts && vl->total_q < 1) return MSA_ERR_INVALID_ARGUMENT;
+  if (vl->page_table && (vl->num_pages < 1 || vl->pages_per_seq < D->n_blk)) return MSA_ERR_INVALID_ARGUMENT;
+  if (vl->page_table && (int64_t)vl->num_pages * p->h_kv * msa::kBk > INT32_MAX) return MSA_ERR_INVALID_ARGUMENT;
+  D->qo_lens = vl->qo_lens;
+  D->kv_lens = vl->kv_lens;
+  D->q_starts = vl->q_starts;
+  D->total_q = vl->q_starts ? vl->total_q : 0;
+  D->pages = vl->page_table;
+  D->pages_per_seq = vl->page_table ? vl->pages_per_seq : 0;
+  D->num_pages = vl->page_table ? vl->num_pages : 0;
   return MSA_OK;
 }
 
@@ -160,30 +181,31 @@ msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
   }
 }
 
-msa_status msa_index_scores(const msa_problem* p, const void* index_q, const void* index_k, float* pooled,
-                            hipStream_t stream) {
+msa_status msa_index_scores_v(const msa_problem* p, const msa_varlen* vl, const void* index_q, const void* index_k,
+                              float* pooled, hipStream_t stream) {
   Dims D;
-  const msa_status st = derive(p, &D);
+  const msa_status st = derive_v(p, vl, &D);
   if (st != MSA_OK) return st;
   if (!index_q || !index_k || !pooled) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(index_q) || !aligned16(index_k) || !aligned16(pooled)) return MSA_ERR_INVALID_ARGUMENT;
   return hip_status(run_index(D, index_q, index_k, pooled, stream));
 }
 
-msa_status msa_block_topk(const msa_problem* p, const float* pooled, int32_t* block_idx, hipStream_t stream) {
+msa_status msa_block_topk_v(const msa_problem* p, const msa_varlen* vl, const float* pooled, int32_t* block_idx,
+                            hipStream_t stream) {
   Dims D;
-  const msa_status st = derive(p, &D);
+  const msa_status st = derive_v(p, vl, &D);
   if (st != MSA_OK) return st;
   if (!pooled || !block_idx) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(pooled) || !aligned16(block_idx)) return MSA_ERR_INVALID_ARGUMENT;
   return hip_status(msa::launch_block_topk(pooled, block_idx, D, stream));
 }
 
-msa_status msa_sparse_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v,
-                               const int32_t* block_idx, void* out, float* lse, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+msa_status msa_sparse_attn_fwd_v(const msa_problem* p, const msa_varlen* vl, const void* q, const void* k,
+                                 const void* v, const int32_t* block_idx, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
   Dims D;
-  const msa_status st = derive(p, &D);
+  const msa_status st = derive_v(p, vl, &D);
   if (st != MSA_OK) return st;
   if (!q || !k || !v || !block_idx || !out || !workspace) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(out) ||
@@ -194,11 +216,11 @@ msa_status msa_sparse_attn_fwd(const msa_problem* p, const void* q, const void* 
   return hip_status(run_attention(D, q, k, v, block_idx, out, lse, static_cast<char*>(workspace), stream));
 }
 
-msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const void* v, const void* index_q,
-                       const void* index_k, void* out, int32_t* block_idx, float* lse, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+msa_status msa_forward_v(const msa_problem* p, const msa_varlen* vl, const void* q, const void* k, const void* v,
+                         const void* index_q, const void* index_k, void* out, int32_t* block_idx, float* lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Dims D;
-  const msa_status st = derive(p, &D);
+  const msa_status st = derive_v(p, vl, &D);
   if (st != MSA_OK) return st;
   if (!q || !k || !v || !index_q || !index_k || !out || !block_idx || !workspace) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(index_q) || !aligned16(index_k) ||
@@ -218,6 +240,28 @@ msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const
   }
   if (e != hipSuccess) return MSA_ERR_HIP;
   return hip_status(run_attention(D, q, k, v, block_idx, out, lse, static_cast<char*>(workspace) + pb, stream));
+}
+
+msa_status msa_index_scores(const msa_problem* p, const void* index_q, const void* index_k, float* pooled,
+                            hipStream_t stream) {
+  return msa_index_scores_v(p, nullptr, index_q, index_k, pooled, stream);
+}
+
+msa_status msa_block_topk(const msa_problem* p, const float* pooled, int32_t* block_idx, hipStream_t stream) {
+  return msa_block_topk_v(p, nullptr, pooled, block_idx, stream);
+}
+
+msa_status msa_sparse_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  return msa_sparse_attn_fwd_v(p, nullptr, q, k, v, block_idx, out, lse, workspace, workspace_bytes, stream);
+}
+
+msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const void* v, const void* index_q,
+                       const void* index_k, void* out, int32_t* block_idx, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  return msa_forward_v(p, nullptr, q, k, v, index_q, index_k, out, block_idx, lse, workspace, workspace_bytes,
+                       stream);
 }
 
 const char* msa_status_string(msa_status s) {

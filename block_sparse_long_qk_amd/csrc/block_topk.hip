@@ -82,7 +82,9 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= nrows) return;  // whole wave; no workgroup barrier below
   const int i = (int)(row % D.n_q);
-  const int local = (int)((D.offset + i) / kBk);
+  const int b = (int)(row / ((int64_t)D.h_kv * D.n_q));
+  if (i >= seq_nq(D, b)) return;  // a row past this sequence's queries (variable lengths)
+  const int local = (int)((seq_offset(D, b) + i) / kBk);
   const float* src = pooled + row * D.n_blk;
   int32_t* dst = out + row * D.k;
   const int k = D.k;

@@ -29,10 +29,80 @@ constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 struct Dims {
   int32_t B, n_q, n_kv, h_q, h_kv, G, d, d_idx, k, n_blk;
   int32_t pt;          // query positions per attention tile (power of two, pt * G <= 256, pt <= 128)
-  int64_t offset;      // position of query row 0
+  int64_t offset;      // position of query row 0 (uniform batches)
   float scale;         // softmax scale
   float scale_log2;    // softmax scale * log2(e)
+  // Variable-length batches and paged caches.  All null: every sequence has
+  // n_q query rows at positions offset .. offset + n_q - 1 and n_kv cached
+  // tokens, each tensor contiguous.  Otherwise n_q and n_kv are maxima, per-row
+  // outputs keep n_q rows per (sequence, group) of which the first qo_len are
+  // written, and a sequence's queries sit at the end of its cache.
+  const int32_t* qo_lens;   // [B] query rows per sequence (null: n_q each)
+  const int32_t* kv_lens;   // [B] cached tokens per sequence (null: n_kv each)
+  const int32_t* q_starts;  // [B] first row of each sequence in the packed q, index_q, out (null: b * n_q)
+  const int32_t* pages;     // [B][pages_per_seq] physical page (= block) of each logical block (null: contiguous)
+  int32_t pages_per_seq;
+  int32_t num_pages;        // pages in the k, v and index_k pools
+  int32_t total_q;          // rows of the packed q, index_q and out
 };
+
+// Per-sequence view.  Lengths are clamped to the maxima the launch was sized
+// for and an out-of-range page to the pool, so malformed length or page data
+// gives wrong results for that sequence but never an access outside the
+// buffers.
+__device__ __forceinline__ int seq_nkv(const Dims& D, int b) {
+  return D.kv_lens ? max(0, min(D.kv_lens[b], D.n_kv)) : D.n_kv;
+}
+__device__ __forceinline__ int seq_nq(const Dims& D, int b) {
+  return D.qo_lens ? max(0, min(min(D.qo_lens[b], D.n_q), seq_nkv(D, b))) : D.n_q;
+}
+// position of the sequence's query row 0
+__device__ __forceinline__ int64_t seq_offset(const Dims& D, int b) {
+  return D.qo_lens || D.kv_lens ? (int64_t)seq_nkv(D, b) - seq_nq(D, b) : D.offset;
+}
+// row of query i of sequence b in the packed q / index_q / out
+__device__ __forceinline__ int64_t q_row(const Dims& D, int b, int i) {
+  if (!D.q_starts) return (int64_t)b * D.n_q + i;
+  return min((int64_t)max(D.q_starts[b], 0) + i, (int64_t)D.total_q - 1);
+}
+// physical page of logical block t of sequence b
+__device__ __forceinline__ int64_t kv_page(const Dims& D, int b, int t) {
+  const int tt = min(max(t, 0), D.pages_per_seq - 1);
+  return min(max(D.pages[(int64_t)b * D.pages_per_seq + tt], 0), D.num_pages - 1);
+}
+// element offset of the first key of block t, KV head g, in k / v
+__device__ __forceinline__ int64_t kv_block_off(const Dims& D, int b, int g, int t) {
+  if (D.pages) return (kv_page(D, b, t) * D.h_kv + g) * (int64_t)kBk * kHeadDim;
+  return (((int64_t)b * D.h_kv + g) * D.n_kv + (int64_t)t * kBk) * kHeadDim;
+}
+// element offset of the first key of block t in index_k
+__device__ __forceinline__ int64_t ik_block_off(const Dims& D, int b, int t) {
+  if (D.pages) return kv_page(D, b, t) * (int64_t)kBk * D.d_idx;
+  return ((int64_t)b * D.n_kv + (int64_t)t * kBk) * D.d_idx;
+}
+
+// The same views for kernels instantiated twice: VL = false is the uniform,
+// contiguous case with no per-sequence lookups at all.
+inline bool dims_varlen(const Dims& D) { return D.qo_lens || D.kv_lens || D.q_starts || D.pages; }
+template <bool VL> __device__ __forceinline__ int nq_of(const Dims& D, int b) {
+  if constexpr (VL) return seq_nq(D, b); else return D.n_q;
+}
+template <bool VL> __device__ __forceinline__ int nkv_of(const Dims& D, int b) {
+  if constexpr (VL) return seq_nkv(D, b); else return D.n_kv;
+}
+template <bool VL> __device__ __forceinline__ int64_t off_of(const Dims& D, int b) {
+  if constexpr (VL) return seq_offset(D, b); else return D.offset;
+}
+template <bool VL> __device__ __forceinline__ int64_t qrow_of(const Dims& D, int b, int i) {
+  if constexpr (VL) return q_row(D, b, i); else return (int64_t)b * D.n_q + i;
+}
+template <bool VL> __device__ __forceinline__ int64_t kvoff_of(const Dims& D, int b, int g, int t) {
+  if constexpr (VL) return kv_block_off(D, b, g, t);
+  else return (((int64_t)b * D.h_kv + g) * D.n_kv + (int64_t)t * kBk) * kHeadDim;
+}
+template <bool VL> __device__ __forceinline__ int64_t ikoff_of(const Dims& D, int b, int t) {
+  if constexpr (VL) return ik_block_off(D, b, t); else return ((int64_t)b * D.n_kv + (int64_t)t * kBk) * D.d_idx;
+}
 
 // Workspace carve-up of the sparse attention stage (device pointers).
 struct AttnWs {

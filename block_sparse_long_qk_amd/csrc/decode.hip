@@ -46,7 +46,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 // Loads past the cache end repeat its last key (masked: it follows every
 // row's position).  Pooled values wait in LDS and leave in batches, so stores
 // rarely interrupt the load stream.
-template <int DIDX>
+template <int DIDX, bool VL>
 __global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict__ iq,
                                                      const uint16_t* __restrict__ ik, float* __restrict__ pooled,
                                                      Dims D, int32_t blocks_per_wave) {
@@ -62,38 +62,44 @@ __global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict_
   __shared__ float pst[4][16][FLUSH];
   const float NEG_INF = -__builtin_huge_valf();
   const int b = blockIdx.y;
-  const int R = D.n_q * D.h_kv;  // <= 16
+  const int nq_b = nq_of<VL>(D, b);
+  if (nq_b == 0) return;          // uniform over the workgroup
+  const int R = nq_b * D.h_kv;    // <= 16
+  const int64_t off_b = off_of<VL>(D, b);
+  const int nkv_b = nkv_of<VL>(D, b);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, c = lane >> 4;
-  const int t_last = (int)((D.offset + D.n_q - 1) / kBk);
+  const int t_last = (int)((off_b + nq_b - 1) / kBk);
   const int t0 = ((int)blockIdx.x * 4 + wave) * blocks_per_wave;
   const int t1 = min(t0 + blocks_per_wave, t_last + 1);
   if (t0 >= t1) return;
 
   uint4 qb[KS];
   const bool row_ok = n < R;
-  const int64_t pc = row_ok ? D.offset + n / D.h_kv : -1;
+  const int64_t pc = row_ok ? off_b + n / D.h_kv : -1;
   const int l_row = row_ok ? (int)(pc / kBk) : -1;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qb[ks] = row_ok ? *reinterpret_cast<const uint4*>(iq + ((int64_t)b * R + n) * DIDX + 8 * (KS * c + ks))
+    qb[ks] = row_ok ? *reinterpret_cast<const uint4*>(iq + (qrow_of<VL>(D, b, n / D.h_kv) * D.h_kv + n % D.h_kv) * DIDX +
+                                                      8 * (KS * c + ks))
                     : make_uint4(0, 0, 0, 0);
   int64_t out_base = -1;
   if (row_ok) {
     const int i = n / D.h_kv, g = n % D.h_kv;
     out_base = (((int64_t)b * D.h_kv + g) * D.n_q + i) * D.n_blk;
   }
-  const unsigned char* src = reinterpret_cast<const unsigned char*>(ik + (int64_t)b * D.n_kv * DIDX);
-  const int64_t last_key = (int64_t)D.n_kv - 1;
   unsigned char* buf = lds[wave];
   // this lane's slot in a load: key u*KEYS_PER_LOAD + lk, byte offset lo
   const int lk = (lane * 16) / ROW, lo = (lane * 16) % ROW;
   auto fetch = [&](int t, int st, u32x4 (&x)[LOADS]) {
-    const int64_t key0 = (int64_t)t * kBk + st * STEP_KEYS;
+    // the block's keys are contiguous (a page when paged); past the cache end
+    // its last key repeats
+    const unsigned char* blk = reinterpret_cast<const unsigned char*>(ik + ikoff_of<VL>(D, b, t));
+    const int last = nkv_b - 1 - t * kBk;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int64_t key = min(key0 + u * KEYS_PER_LOAD + lk, last_key);
-      x[u] = *reinterpret_cast<const u32x4*>(src + key * ROW + lo);
+      const int key = min(st * STEP_KEYS + u * KEYS_PER_LOAD + lk, last);
+      x[u] = *reinterpret_cast<const u32x4*>(blk + key * ROW + lo);
     }
   };
   u32x4 ring[NSTEP][LOADS];  // native vectors: whole-register copies, no memcpy
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict_
       __builtin_amdgcn_sched_barrier(0);
       wave_lds_fence();
       const int64_t skey0 = (int64_t)t * kBk + st * STEP_KEYS;
-      const bool need_mask = skey0 + STEP_KEYS - 1 > D.offset;
+      const bool need_mask = skey0 + STEP_KEYS - 1 > off_b;
 #pragma unroll
       for (int T = 0; T < STEP_KEYS / 16; ++T) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -167,7 +173,7 @@ __device__ __forceinline__ int slot_block(const int32_t* row, int s, int k, int 
 }
 
 // One wave per (row, slot); GMAX (8 or 16) >= G query heads of the row's group.
-template <int GMAX>
+template <int GMAX, bool VL>
 __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v,
                                                    const int32_t* __restrict__ block_idx, float* __restrict__ part,
@@ -182,7 +188,9 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
   const int64_t bg = r / D.n_q;
   const int i = (int)(r % D.n_q);
   const int g = (int)(bg % D.h_kv), b = (int)(bg / D.h_kv);
-  const int64_t p = D.offset + i;
+  if (i >= nq_of<VL>(D, b)) return;  // a row past this sequence's queries (whole workgroup)
+  const int nkv_b = nkv_of<VL>(D, b);
+  const int64_t p = off_of<VL>(D, b) + i;
   const int local = (int)(p / kBk);
   const int t = slot_block(block_idx + r * D.k, s, D.k, local);  // same for the whole wave
   float* dst = part + (r * (D.k + 1) + s) * (int64_t)kRowsPart;  // o [16][d], then lse [16]
@@ -192,14 +200,14 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
   }
   const int n = lane & 15, c = lane >> 4;
   const int64_t key0 = (int64_t)t * kBk;
-  const uint16_t* kb = k + ((int64_t)bg * D.n_kv + key0) * kHeadDim;
-  const uint16_t* vb = v + ((int64_t)bg * D.n_kv + key0) * kHeadDim;
+  const uint16_t* kb = k + kvoff_of<VL>(D, b, g, t);
+  const uint16_t* vb = v + kvoff_of<VL>(D, b, g, t);
 
   // scores S[h][key] with MFMA: A = Q (rows = heads), B = K^T (columns = keys);
   // lane group c and k-step ks hold head dims 32*c + 8*ks .. +8.
   uint4 qa[4];
   const bool head_ok = n < D.G;
-  const uint16_t* qrow = q + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + (head_ok ? n : 0)) * kHeadDim + 32 * c;
+  const uint16_t* qrow = q + (qrow_of<VL>(D, b, i) * D.h_q + g * D.G + (head_ok ? n : 0)) * kHeadDim + 32 * c;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     qa[ks] = head_ok ? *reinterpret_cast<const uint4*>(qrow + 8 * ks) : make_uint4(0, 0, 0, 0);
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
   constexpr int KPITCH = kHeadDim * 2 + 16;  // bytes per key row in LDS
   unsigned char* kbuf = Kst[wave];
   const int lk = lane >> 4, lo = (lane & 15) * 16;
-  const int n_keys = (int)min((int64_t)kBk, (int64_t)D.n_kv - key0);
+  const int n_keys = (int)min((int64_t)kBk, (int64_t)nkv_b - key0);
   const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kb);
   uint4 kx[8];
   auto fetch_k = [&](int st) {
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
     for (int T = 0; T < 8; ++T) {
       const int64_t key = key0 + 16 * T + n;
       float x = sc[T][j] * D.scale_log2;
-      if (key > p || key >= D.n_kv) x = NEG_INF;
+      if (key > p || key >= nkv_b) x = NEG_INF;
       sc[T][j] = x;
       m = fmaxf(m, x);
     }
@@ -339,6 +347,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
 }
 
 // One workgroup per row: out[b][i][g*G + h][d] and lse from the row's partials.
+template <bool VL>
 __global__ __launch_bounds__(256) void k_merge_rows(const float* __restrict__ part, uint16_t* __restrict__ out,
                                                     float* __restrict__ lse_out, Dims D) {
   const float NEG_INF = -__builtin_huge_valf();
@@ -346,6 +355,7 @@ __global__ __launch_bounds__(256) void k_merge_rows(const float* __restrict__ pa
   const int64_t bg = r / D.n_q;
   const int i = (int)(r % D.n_q);
   const int g = (int)(bg % D.h_kv), b = (int)(bg / D.h_kv);
+  if (i >= nq_of<VL>(D, b)) return;  // a row past this sequence's queries (whole workgroup)
   const int nslot = D.k + 1;
   const float* base = part + r * nslot * (int64_t)kRowsPart;
   for (int x = threadIdx.x; x < D.G * (kHeadDim / 4); x += blockDim.x) {
@@ -370,7 +380,7 @@ __global__ __launch_bounds__(256) void k_merge_rows(const float* __restrict__ pa
       o.z += cw * w.z;
       o.w += cw * w.w;
     }
-    uint16_t* dst = out + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + h) * kHeadDim + 4 * d4;
+    uint16_t* dst = out + (qrow_of<VL>(D, b, i) * D.h_q + g * D.G + h) * kHeadDim + 4 * d4;
     *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
     if (lse_out && d4 == 0) lse_out[((int64_t)b * D.h_q + g * D.G + h) * D.n_q + i] = tot * 0.69314718055994531f;
   }
@@ -405,10 +415,14 @@ hipError_t launch_index_small(const uint16_t* index_q, const uint16_t* index_k, 
   const int per = (int)((t_max + waves_per_b - 1) / waves_per_b);
   const int wgs = (int)(((t_max + per - 1) / per + 3) / 4);
   dim3 grid(wgs, D.B);
-  if (D.d_idx == 128)
-    hipLaunchKernelGGL(k_index_small<128>, grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
-  else
-    hipLaunchKernelGGL(k_index_small<64>, grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+  const bool vl = dims_varlen(D);
+  if (D.d_idx == 128) {
+    if (vl) hipLaunchKernelGGL((k_index_small<128, true>), grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+    else hipLaunchKernelGGL((k_index_small<128, false>), grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+  } else {
+    if (vl) hipLaunchKernelGGL((k_index_small<64, true>), grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+    else hipLaunchKernelGGL((k_index_small<64, false>), grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+  }
   return hipGetLastError();
 }
 
@@ -416,11 +430,19 @@ hipError_t launch_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t
                             uint16_t* out, float* lse, float* part, const Dims& D, hipStream_t stream) {
   const int64_t rows = (int64_t)D.B * D.h_kv * D.n_q;
   dim3 grid((unsigned)rows, (D.k + 1 + 3) / 4);
-  if (D.G <= 8)
-    hipLaunchKernelGGL(k_attn_rows<8>, grid, dim3(256), 0, stream, q, k, v, block_idx, part, D);
+#define MSA_ROWS(GM, VL)                                                                                  \
+  hipLaunchKernelGGL((k_attn_rows<GM, VL>), grid, dim3(256), 0, stream, q, k, v, block_idx, part, D)
+  const bool vl = dims_varlen(D);
+  if (D.G <= 8) {
+    if (vl) MSA_ROWS(8, true); else MSA_ROWS(8, false);
+  } else {
+    if (vl) MSA_ROWS(16, true); else MSA_ROWS(16, false);
+  }
+#undef MSA_ROWS
+  if (vl)
+    hipLaunchKernelGGL(k_merge_rows<true>, dim3((unsigned)rows), dim3(256), 0, stream, part, out, lse, D);
   else
-    hipLaunchKernelGGL(k_attn_rows<16>, grid, dim3(256), 0, stream, q, k, v, block_idx, part, D);
-  hipLaunchKernelGGL(k_merge_rows, dim3((unsigned)rows), dim3(256), 0, stream, part, out, lse, D);
+    hipLaunchKernelGGL(k_merge_rows<false>, dim3((unsigned)rows), dim3(256), 0, stream, part, out, lse, D);
   return hipGetLastError();
 }
 

@@ -41,9 +41,11 @@ __global__ __launch_bounds__(256) void k_plan_hist(const int32_t* __restrict__ b
   const int ch = blockIdx.x, bg = blockIdx.y;
   for (int t = threadIdx.x; t < D.n_blk; t += blockDim.x) lh[t] = 0;
   __syncthreads();
-  const int i0 = ch * kChunkRows, i1 = min(D.n_q, i0 + kChunkRows);
+  const int b = bg / D.h_kv;
+  const int64_t off_b = seq_offset(D, b);
+  const int i0 = ch * kChunkRows, i1 = min(seq_nq(D, b), i0 + kChunkRows);
   for (int i = i0 + (int)threadIdx.x; i < i1; i += blockDim.x) {
-    const int local = (int)((D.offset + i) / kBk);
+    const int local = (int)((off_b + i) / kBk);
     const int32_t* row = block_idx + ((int64_t)bg * D.n_q + i) * D.k;
     for (int s = 0; s < D.k; ++s)
       if (nonlocal_slot(row, s, local)) atomicAdd(&lh[row[s]], 1);
@@ -177,12 +179,14 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ b
   const int32_t* o = tile_off + ((int64_t)bg * n_cg + ch / kGroupChunks) * D.n_blk;
   for (int t = threadIdx.x; t < D.n_blk; t += blockDim.x) cursor[t] = o[t] * D.pt + h[t];
   __syncthreads();
-  const int i0 = ch * kChunkRows, i1 = min(D.n_q, i0 + kChunkRows);
+  const int b = bg / D.h_kv;
+  const int64_t off_b = seq_offset(D, b);
+  const int i0 = ch * kChunkRows, i1 = min(seq_nq(D, b), i0 + kChunkRows);
   const int bin0 = (bg * n_cg + ch / kGroupChunks) * D.n_blk;  // bin of block 0 in this chunk's group
   const float4 neg4 = make_float4(-__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf(),
                                   -__builtin_huge_valf());
   for (int i = i0 + (int)threadIdx.x; i < i1; i += blockDim.x) {
-    const int local = (int)((D.offset + i) / kBk);
+    const int local = (int)((off_b + i) / kBk);
     const int32_t* row = block_idx + ((int64_t)bg * D.n_q + i) * D.k;
     float* lse_row = part_lse + ((int64_t)bg * D.n_q + i) * (D.k + 1) * D.G;
     for (int s = 0; s < D.k; ++s) {

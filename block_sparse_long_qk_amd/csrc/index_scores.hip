@@ -65,7 +65,7 @@ __device__ __forceinline__ void sort_ids(int (&ti)[KK]) {
 // every row (no key split); each lane keeps its row's best KK non-local blocks
 // by (score desc, index asc) in registers and writes the block_idx row (k = KK+1)
 // exactly as the standalone top-k does from the same fp32 scores.
-template <int DIDX, int KK>
+template <int DIDX, int KK, bool VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_index_scores(const uint16_t* __restrict__ iq,
                                                       const uint16_t* __restrict__ ik, float* __restrict__ pooled,
                                                       int32_t* __restrict__ block_idx, Dims D,
@@ -80,21 +80,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const float NEG_INF = -__builtin_huge_valf();
 
   const int b = blockIdx.z;
-  const int rows_total = D.n_q * D.h_kv;
+  const int rows_total = nq_of<VL>(D, b) * D.h_kv;    // this sequence's (query, group) rows
+  const int64_t off_b = off_of<VL>(D, b);
+  const int nkv_b = nkv_of<VL>(D, b);
   const int tile = gridDim.x - 1 - blockIdx.x;     // heaviest (latest) rows first
   const int row0 = tile * 256;
+  if (VL && row0 >= rows_total) return;            // uniform over the workgroup
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
 
   const int last_row = min(row0 + 255, rows_total - 1);
-  const int t_last = (int)((D.offset + last_row / D.h_kv) / kBk);
+  const int t_last = (int)((off_b + last_row / D.h_kv) / kBk);
   const int t_begin = blockIdx.y * blocks_per_split;
   const int t_end = min(t_begin + blocks_per_split, t_last + 1);
   if (t_begin >= t_end) return;  // uniform over the workgroup
 
   const int wrow0 = row0 + wave * 64;
   const bool wave_active = wrow0 < rows_total;
-  const int64_t p_wave_min = D.offset + (int64_t)(wave_active ? wrow0 : 0) / D.h_kv;
+  const int64_t p_wave_min = off_b + (int64_t)(wave_active ? wrow0 : 0) / D.h_kv;
 
   // B operand: this lane's query columns (n-tile 0: row wrow0+col, n-tile 1: +32),
   // 8 bf16 of the index dim per k-step.
@@ -104,8 +107,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int nt = 0; nt < 2; ++nt) {
     const int r = wrow0 + 32 * nt + col;
     if (r < rows_total) {
-      pc[nt] = D.offset + r / D.h_kv;
-      const uint16_t* src = iq + ((int64_t)b * rows_total + r) * DIDX + 8 * half;
+      pc[nt] = off_b + r / D.h_kv;
+      const int64_t qr = VL ? qrow_of<VL>(D, b, r / D.h_kv) * D.h_kv + r % D.h_kv : (int64_t)b * rows_total + r;
+      const uint16_t* src = iq + qr * DIDX + 8 * half;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) qb[nt][ks] = *reinterpret_cast<const uint4*>(src + 16 * ks);
     } else {
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   if (r_out < rows_total) {
     const int i = r_out / D.h_kv, g = r_out % D.h_kv;
     out_row = ((int64_t)b * D.h_kv + g) * D.n_q + i;
-    l_out = (int)((D.offset + i) / kBk);
+    l_out = (int)((off_b + i) / kBk);
   }
   float tv[KK > 0 ? KK : 1];
   int ti[KK > 0 ? KK : 1];
@@ -132,21 +136,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     ti[s] = -1;
   }
 
-  const uint16_t* ikb = ik + (int64_t)b * D.n_kv * DIDX;
   // Key blocks arrive by direct global-to-LDS loads one block ahead: the
   // hardware writes lane l's 16 bytes at l * 16 past the instruction's LDS
   // address, so lane l of instruction i fetches the chunk that belongs in slot
   // l % CPR of row RPI * i + l / CPR.  Keys past the cache end repeat its last
   // key: finite values the causal mask drops (they follow every row's
   // position), so the loads need no per-key branch.
+  const uint16_t* ikb = ik + (int64_t)b * D.n_kv * DIDX;  // uniform case: sequence b's keys
   auto fetch_block = [&](int t, uint16_t* dst) {
-    const int64_t j0 = (int64_t)t * kBk;
+    // the block's keys are contiguous (a page when paged); past its last cached
+    // key the last one repeats
+    const uint16_t* blk;
+    int last;
+    if constexpr (VL) {
+      blk = ik + ikoff_of<VL>(D, b, t);
+      last = nkv_b - 1 - t * kBk;
+    } else {
+      blk = ikb;
+      last = D.n_kv - 1;
+    }
+    const int j0 = VL ? 0 : t * kBk;
 #pragma unroll
     for (int u = 0; u < C::NI; ++u) {
       const int i = wave * C::NI + u;
       const int row = C::RPI * i + lane / C::CPR, sl = lane % C::CPR;
-      const int64_t j = min(j0 + row, (int64_t)D.n_kv - 1);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ikb + j * DIDX + 8 * (sl ^ C::swz(row))),
+      const int64_t jr = min(j0 + row, last);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(blk + jr * DIDX + 8 * (sl ^ C::swz(row))),
                                        (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, 0, 0);
     }
   };
@@ -298,12 +313,15 @@ hipError_t launch_index_scores(const uint16_t* index_q, const uint16_t* index_k,
   dim3 grid;
   int per;
   index_grid(D, &grid, &per);
-  if (D.d_idx == 128)
-    hipLaunchKernelGGL((k_index_scores<128, 0>), grid, dim3(256), 0, stream, index_q, index_k, pooled, nullptr, D,
-                       per);
-  else
-    hipLaunchKernelGGL((k_index_scores<64, 0>), grid, dim3(256), 0, stream, index_q, index_k, pooled, nullptr, D,
-                       per);
+  const bool vl = dims_varlen(D);
+#define MSA_IDX(DI, VL) \
+  hipLaunchKernelGGL((k_index_scores<DI, 0, VL>), grid, dim3(256), 0, stream, index_q, index_k, pooled, nullptr, D, per)
+  if (D.d_idx == 128) {
+    if (vl) MSA_IDX(128, true); else MSA_IDX(128, false);
+  } else {
+    if (vl) MSA_IDX(64, true); else MSA_IDX(64, false);
+  }
+#undef MSA_IDX
   return hipGetLastError();
 }
 
@@ -320,9 +338,15 @@ hipError_t launch_index_topk(const uint16_t* index_q, const uint16_t* index_k, i
   dim3 grid;
   int per;
   index_grid(D, &grid, &per);
-#define MSA_IDX_TOPK(DI, KK)                                                                                      \
-  hipLaunchKernelGGL((k_index_scores<DI, KK>), grid, dim3(256), 0, stream, index_q, index_k, nullptr, block_idx, D, \
-                     per)
+#define MSA_IDX_TOPK(DI, KK)                                                                          \
+  do {                                                                                                \
+    if (dims_varlen(D))                                                                               \
+      hipLaunchKernelGGL((k_index_scores<DI, KK, true>), grid, dim3(256), 0, stream, index_q, index_k, \
+                         nullptr, block_idx, D, per);                                                 \
+    else                                                                                              \
+      hipLaunchKernelGGL((k_index_scores<DI, KK, false>), grid, dim3(256), 0, stream, index_q, index_k, \
+                         nullptr, block_idx, D, per);                                                 \
+  } while (0)
   if (D.d_idx == 128) {
     if (D.k == 16) MSA_IDX_TOPK(128, 15); else MSA_IDX_TOPK(128, 7);
   } else {

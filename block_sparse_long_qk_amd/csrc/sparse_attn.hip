@@ -252,6 +252,15 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* Vt, f32x16 (&s)[4], i
   l = sum;
 }
 
+// Local tiles per (sequence, group): runs of pt consecutive positions (aligned
+// to pt) covering the sequence's query positions; with variable lengths an upper
+// bound, the tiles past a sequence's rows having no valid row.
+template <bool VL>
+__device__ __forceinline__ int local_tiles(const Dims& D) {
+  if (VL && (D.qo_lens || D.kv_lens)) return (D.n_q + D.pt - 1) / D.pt + 1;
+  return (int)((D.offset + D.n_q - 1) / D.pt - D.offset / D.pt + 1);
+}
+
 // One lane's row of a tile.  Non-local tiles come from the tile-major gather
 // lists (row = query i, slot s of its block_idx row); local tiles are runs of
 // pt consecutive positions that share their local block (slot k).
@@ -280,7 +289,7 @@ __device__ __forceinline__ TileRaw tile_raw(const AttnWs& ws, const Dims& D, int
   return r;
 }
 
-template <bool LOCAL>
+template <bool LOCAL, bool VL>
 __device__ __forceinline__ TileRow tile_row(const TileRaw& raw, const Dims& D, const AttnWs& ws, int tile, int ps) {
   TileRow tr;
   tr.i = 0;
@@ -295,15 +304,16 @@ __device__ __forceinline__ TileRow tile_row(const TileRaw& raw, const Dims& D, c
       tr.s = raw.e % D.k;
     }
   } else {
-    const int64_t a0 = D.offset / D.pt;
-    const int n_loc = (int)((D.offset + D.n_q - 1) / D.pt - a0 + 1);
+    const int n_loc = local_tiles<VL>(D);
     tr.bg = tile / n_loc;
-    const int64_t p0 = (a0 + tile % n_loc) * D.pt;
-    tr.t = (int)(p0 / kBk);
+    const int b = tr.bg / D.h_kv;
+    const int64_t off_b = off_of<VL>(D, b);
+    const int64_t p0 = (off_b / D.pt + tile % n_loc) * D.pt;
+    tr.t = (int)min(p0 / kBk, (int64_t)D.n_blk - 1);  // tiles past the sequence's rows stay in bounds
     const int64_t p = p0 + ps;
-    tr.valid = ps < D.pt && p >= D.offset && p < D.offset + D.n_q;
+    tr.valid = ps < D.pt && p >= off_b && p < off_b + nq_of<VL>(D, b);
     if (tr.valid) {
-      tr.i = (int)(p - D.offset);
+      tr.i = (int)(p - off_b);
       tr.s = D.k;
     }
   }
@@ -376,7 +386,7 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, fl
 // vector loads and stores alike, so a wait for loads waits for every store
 // issued before them: issued where they are, the stores and the next rows
 // have a whole softmax and P.V to land before the next tile waits for them.
-template <bool LOCAL>
+template <bool LOCAL, bool VL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_tiles(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, AttnWs ws,
     Dims D) {
@@ -385,8 +395,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];  // per wave: its query rows
   int total;
   if constexpr (LOCAL) {
-    const int64_t a0 = D.offset / D.pt;
-    total = D.B * D.h_kv * (int)((D.offset + D.n_q - 1) / D.pt - a0 + 1);
+    total = D.B * D.h_kv * local_tiles<VL>(D);
   } else {
     total = ws.tile_off[ws.n_bins];
   }
@@ -401,14 +410,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int r = wave * 32 + col;
   const int ps = r / D.G, hh = r % D.G;
   unsigned char* qw = Qs[wave];
-  auto q_row = [&](const TileRow& tr) {  // rows that do not exist read row 0 of the group
+  auto q_ptr = [&](const TileRow& tr) {  // rows that do not exist read row 0 of the group
     const int g = tr.bg % D.h_kv, b = tr.bg / D.h_kv;
     const int i = tr.valid ? tr.i : 0;
-    return q + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + hh) * kHeadDim;
+    return q + (qrow_of<VL>(D, b, i) * D.h_q + g * D.G + hh) * kHeadDim;
   };
 
-  TileRow cur = tile_row<LOCAL>(tile_raw<LOCAL>(ws, D, w0.tile, ps), D, ws, w0.tile, ps);
-  fetch_q_rows(qw, q_row(cur), lane);
+  TileRow cur = tile_row<LOCAL, VL>(tile_raw<LOCAL>(ws, D, w0.tile, ps), D, ws, w0.tile, ps);
+  fetch_q_rows(qw, q_ptr(cur), lane);
   Walk w1 = walk_next(w0, stride, hi);
   TileRaw raw1 = tile_raw<LOCAL>(ws, D, min(w1.tile, hi - 1), ps);
   uint4 pw[8];
@@ -418,9 +427,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // outer loop: one staged K/V block; inner loop: the tiles that use it
   while (w0.tile < hi) {
     {
-      const int64_t key0 = (int64_t)cur.t * kBk;
-      const int64_t kv0 = ((int64_t)cur.bg * D.n_kv + key0) * kHeadDim;
-      stage_kv(Ks, Vt, k + kv0, v + kv0, (int)min((int64_t)kBk, (int64_t)D.n_kv - key0));
+      const int sb = cur.bg / D.h_kv;
+      const int64_t kv0 = kvoff_of<VL>(D, sb, cur.bg % D.h_kv, cur.t);
+      stage_kv(Ks, Vt, k + kv0, v + kv0, max(1, min(kBk, nkv_of<VL>(D, sb) - cur.t * kBk)));
       __syncthreads();
     }
     const int staged_bg = cur.bg, staged_t = cur.t;
@@ -433,18 +442,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       __builtin_amdgcn_sched_barrier(0);
       const bool more = w1.tile < hi;
       // past the last tile: a stand-in decode of the last one (loads stay in bounds, results unused)
-      const TileRow nxt = tile_row<LOCAL>(raw1, D, ws, min(w1.tile, hi - 1), ps);
+      const TileRow nxt = tile_row<LOCAL, VL>(raw1, D, ws, min(w1.tile, hi - 1), ps);
       __builtin_amdgcn_sched_barrier(0);
       if (have) store_partials(ws.part_o, ws.part_lse, pw, plse, pvalid, ppblk, hh, D.G, half);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // LDS reads of the region are done before it is refilled
       __builtin_amdgcn_sched_barrier(0);
-      fetch_q_rows(qw, q_row(nxt), lane);
+      fetch_q_rows(qw, q_ptr(nxt), lane);
       Walk w2 = w1;
       if (more) w2 = walk_next(w1, stride, hi);
       const TileRaw raw2 = tile_raw<LOCAL>(ws, D, min(w2.tile, hi - 1), ps);
       f32x16 o[4];
       float m2, l;
-      softmax_pv<LOCAL>(Vt, s, lane, D.scale_log2, (int64_t)cur.t * kBk, D.offset + cur.i, o, m2, l);
+      softmax_pv<LOCAL>(Vt, s, lane, D.scale_log2, (int64_t)cur.t * kBk, off_of<VL>(D, cur.bg / D.h_kv) + cur.i, o, m2,
+                        l);
       pack_partial(o, 1.f / l, pw);
       ppblk = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s;
       plse = m2 + __log2f(l);
@@ -469,6 +479,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // in registers, and the row's non-local partials (lse -inf: no partial) are
 // folded in two slots at a time with a running max.  Normalised, the result is
 // written to `out` (bf16) and `lse` (natural log).
+template <bool VL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_local_merge(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, AttnWs ws,
     uint16_t* __restrict__ out, float* __restrict__ lse_out, Dims D) {
@@ -476,8 +487,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
   __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];
   const float NEG_INF = -__builtin_huge_valf();
-  const int64_t a0 = D.offset / D.pt;
-  const int total = D.B * D.h_kv * (int)((D.offset + D.n_q - 1) / D.pt - a0 + 1);
+  const int total = D.B * D.h_kv * local_tiles<VL>(D);
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = gridDim.x / kXcds;
   const int lo = (int)((int64_t)total * xcd / kXcds), hi = (int)((int64_t)total * (xcd + 1) / kXcds);
   const int stride = per_xcd * kRun;
@@ -491,9 +501,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   unsigned char* qw = Qs[wave];
   int staged_bg = -1, staged_t = -1;
   for (; w.tile < hi; w = walk_next(w, stride, hi)) {
-    const TileRow cur = tile_row<true>(TileRaw{-1, 0}, D, ws, w.tile, ps);
+    const TileRow cur = tile_row<true, VL>(TileRaw{-1, 0}, D, ws, w.tile, ps);
     const int g = cur.bg % D.h_kv, b = cur.bg / D.h_kv;
-    const int64_t qoff = (((int64_t)b * D.n_q + (cur.valid ? cur.i : 0)) * D.h_q + g * D.G + hh) * kHeadDim;
+    const int64_t qoff = (qrow_of<VL>(D, b, cur.valid ? cur.i : 0) * D.h_q + g * D.G + hh) * kHeadDim;
     fetch_q_rows(qw, q + qoff, lane);
     // The row's non-local partials (chunk-major blocks, see store_partials):
     // this lane's 64 values of each are chunks 8 * half .. 8 * half + 7 of its
@@ -520,9 +530,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform
       if (staged_bg >= 0) __syncthreads();
-      const int64_t key0 = (int64_t)cur.t * kBk;
-      const int64_t kv0 = ((int64_t)cur.bg * D.n_kv + key0) * kHeadDim;
-      stage_kv(Ks, Vt, k + kv0, v + kv0, (int)min((int64_t)kBk, (int64_t)D.n_kv - key0));
+      const int sb = cur.bg / D.h_kv;
+      const int64_t kv0 = kvoff_of<VL>(D, sb, cur.bg % D.h_kv, cur.t);
+      stage_kv(Ks, Vt, k + kv0, v + kv0, max(1, min(kBk, nkv_of<VL>(D, sb) - cur.t * kBk)));
       __syncthreads();
       staged_bg = cur.bg;
       staged_t = cur.t;
@@ -544,7 +554,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int j = 0; j < 8; ++j) M = fmaxf(M, lw[j]);
     }
-    softmax_pv<true>(Vt, sc, lane, D.scale_log2, (int64_t)cur.t * kBk, D.offset + cur.i, o, m2, l);
+    softmax_pv<true>(Vt, sc, lane, D.scale_log2, (int64_t)cur.t * kBk, off_of<VL>(D, b) + cur.i, o, m2, l);
     M = fmaxf(M, m2);
     {
       const float rs = __builtin_amdgcn_exp2f(m2 - M);
@@ -619,8 +629,16 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream) {
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_tiles<false>, dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws, D);
-  hipLaunchKernelGGL(k_attn_local_merge, dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws, out, lse, D);
+  if (dims_varlen(D)) {
+    hipLaunchKernelGGL((k_attn_tiles<false, true>), dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws, D);
+    hipLaunchKernelGGL(k_attn_local_merge<true>, dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws, out,
+                       lse, D);
+  } else {
+    hipLaunchKernelGGL((k_attn_tiles<false, false>), dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws,
+                       D);
+    hipLaunchKernelGGL(k_attn_local_merge<false>, dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws, out,
+                       lse, D);
+  }
   return hipGetLastError();
 }
 

@@ -139,6 +139,50 @@ msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const
                        const void* index_k, void* out, int32_t* block_idx, float* lse, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Variable-length batches and paged caches (section 运行 Kernel: the kernels
+ * take per-sequence query and cache lengths and K/V held in pages of
+ * block_size tokens addressed through a page table).  All pointers are device
+ * memory; each may be NULL on its own, meaning the uniform case:
+ *   qo_lens[b]    query rows of sequence b (NULL: p->n_q each);
+ *   kv_lens[b]    cached tokens of sequence b (NULL: p->n_kv each);
+ *   q_starts[b]   first row of sequence b in the packed q, index_q and out,
+ *                 which then hold total_q rows (NULL: row b * n_q + i);
+ *   page_table    [batch][pages_per_seq]: the physical page holding logical
+ *                 block t of sequence b (NULL: contiguous caches).
+ * With qo_lens or kv_lens given, p->q_offset must be -1 and the queries of a
+ * sequence sit at the end of its cache: p_i = kv_len - qo_len + i; p->n_q and
+ * p->n_kv are the maxima (qo_len <= n_q, kv_len <= n_kv, qo_len <= kv_len) and
+ * size the launches and the workspace.  Per-row outputs (pooled, block_idx,
+ * lse) keep p->n_q rows per (sequence, group or head); rows i >= qo_len are
+ * left untouched.  With a page table, k and v are page pools
+ * [num_pages][h_kv][block_size][head_dim] and index_k is
+ * [num_pages][block_size][index_dim]; pages_per_seq >= ceil(n_kv / block_size).
+ * Lengths above the maxima, starts past total_q and page ids outside the pool
+ * are clamped (wrong results for that sequence, but no access outside the
+ * buffers).  The calls below equal the plain calls when vl is NULL.
+ */
+typedef struct {
+  const int32_t* qo_lens;
+  const int32_t* kv_lens;
+  const int32_t* q_starts;
+  int32_t total_q;
+  const int32_t* page_table;
+  int32_t pages_per_seq;
+  int32_t num_pages;
+} msa_varlen;
+
+msa_status msa_index_scores_v(const msa_problem* p, const msa_varlen* vl, const void* index_q, const void* index_k,
+                              float* pooled, hipStream_t stream);
+msa_status msa_block_topk_v(const msa_problem* p, const msa_varlen* vl, const float* pooled, int32_t* block_idx,
+                            hipStream_t stream);
+msa_status msa_sparse_attn_fwd_v(const msa_problem* p, const msa_varlen* vl, const void* q, const void* k,
+                                 const void* v, const int32_t* block_idx, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+msa_status msa_forward_v(const msa_problem* p, const msa_varlen* vl, const void* q, const void* k, const void* v,
+                         const void* index_q, const void* index_k, void* out, int32_t* block_idx, float* lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* msa_status_string(msa_status s);
 

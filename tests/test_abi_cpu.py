@@ -110,3 +110,32 @@ def test_workspace_sizes():
 def test_decode_and_chunked_offsets_accepted():
     assert msa.workspace_size(msa.Problem.make(64, 1, 262144, 64, 8), msa.OP_FORWARD) > 0
     assert msa.workspace_size(msa.Problem.make(1, 8192, 1048576, 64, 8, q_offset=1040384), msa.OP_FORWARD) > 0
+
+
+@pytest.mark.parametrize("p_kw,vl_kw", [
+    (dict(q_offset=0), dict(qo_lens=1 << 20)),                       # lengths need bottom-right alignment
+    (dict(q_offset=0), dict(kv_lens=1 << 20)),
+    (dict(), dict(q_starts=1 << 20, total_q=0)),                       # packed rows need their count
+    (dict(), dict(page_table=1 << 20, pages_per_seq=31, num_pages=64)),  # fewer page slots than blocks (32)
+    (dict(), dict(page_table=1 << 20, pages_per_seq=32, num_pages=0)),
+])
+def test_invalid_varlen_rejected(p_kw, vl_kw):
+    p = prob(**p_kw)
+    vl = msa.Varlen(**vl_kw)
+    lib = msa.library()
+    fake = 1 << 20
+    V = ctypes.byref(vl)
+    assert lib.msa_index_scores_v(ctypes.byref(p), V, fake, fake, fake, None) == msa.ERR_INVALID_ARGUMENT
+    assert lib.msa_block_topk_v(ctypes.byref(p), V, fake, fake, None) == msa.ERR_INVALID_ARGUMENT
+    assert lib.msa_sparse_attn_fwd_v(ctypes.byref(p), V, fake, fake, fake, fake, fake, None, fake, 1 << 40,
+                                     None) == msa.ERR_INVALID_ARGUMENT
+    assert lib.msa_forward_v(ctypes.byref(p), V, fake, fake, fake, fake, fake, fake, fake, None, fake, 1 << 40,
+                             None) == msa.ERR_INVALID_ARGUMENT
+
+
+def test_null_varlen_is_the_plain_call():
+    # same rejection as the plain call for a bad problem, and no crash on NULL
+    p = prob(h_q=6, h_kv=4)
+    lib = msa.library()
+    fake = 1 << 20
+    assert lib.msa_block_topk_v(ctypes.byref(p), None, fake, fake, None) == msa.ERR_INVALID_ARGUMENT
