@@ -6,7 +6,9 @@ gather plan, sparse attention, merge) over the 128K-token causal prefill
 k 16), inputs seeded and synthetic, resident in HBM before timing starts.
 Prints one JSON line: prefill tokens/s (the value), the decode rate at a
 256K-token cache (64 sequences), per-stage times, the roofline of the dominant
-kernel and the oracle's CPU rate on a bounded sample of the same workload.
+kernel, the same two steps with the caches in a shuffled page pool
+(msa_forward_v) and the oracle's CPU rate on a bounded sample of the same
+workload.
 """
 import argparse
 import json
@@ -24,10 +26,10 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x2, calibrated on a 1 GiB copy) + WRITE_SIZE (x1); see
 # profiles/prefill_128k_attention_index_counters.md.  Valid for this kernel
 # version only: re-measure (or set None) when the kernel changes.
-INDEX_TRAFFIC_BYTES = None  # kernel changed since the last counter run
+INDEX_TRAFFIC_BYTES = (2.9366e6 * 2 + 2.1467e6) * 1024
 # The same for one msa_sparse_attn_fwd at 128K: k_attn_tiles<false> plus
 # k_attn_local_merge (the plan kernels add under 1%).
-ATTN_TRAFFIC_BYTES = ((1.770e7 + 1.865e7) * 2 + 3.172e7 + 2.285e6) * 1024
+ATTN_TRAFFIC_BYTES = ((1.7700e7 + 1.8653e7) * 2 + 3.1715e7 + 2.2894e6) * 1024
 
 
 def algorithmic_work(w):
@@ -74,7 +76,7 @@ class Timer:
         return self.a.elapsed_time(self.b) / n
 
 
-def gpu_leg(w, steps, warmup, stream):
+def gpu_leg(w, steps, warmup, stream, paged=False):
     import torch
     import block_sparse_long_qk_amd as msa
     import synth
@@ -107,9 +109,57 @@ def gpu_leg(w, steps, warmup, stream):
     ms_topk = t.run(lambda: msa.block_topk(p, pooled, f["block_idx"], sp), steps)
     ms_attn = t.run(lambda: msa.sparse_attn_fwd(p, x["q"], x["k"], x["v"], f["block_idx"], f["out"], f["lse"],
                                                 attn_ws, stream=sp), steps)
-    del attn_ws, x, f
+    res = {"ms_step": ms_step, "wall_ms_step": wall, "ms_index": ms_idx, "ms_topk": ms_topk, "ms_attn": ms_attn}
+    del attn_ws
+    if paged:
+        # the same step through msa_forward_v, the caches re-laid as a shuffled page pool
+        ref = {key: f[key].clone() for key in ("out", "block_idx", "lse")}
+        vl, kp, vp, ikp = to_pages(w, x, seed=w.seed)
+        print(f"[bench] timing {steps} paged steps of {w.name}", file=sys.stderr, flush=True)
+
+        def paged_step():
+            msa.forward(p, x["q"], kp, vp, x["iq"], ikp, f["out"], f["block_idx"], f["lse"], f["workspace"],
+                        stream=sp, varlen=vl)
+
+        for _ in range(warmup):
+            paged_step()
+        res["ms_step_paged"] = t.run(paged_step, steps)
+        res["paged_equal"] = (torch.equal(ref["block_idx"], f["block_idx"]) and torch.equal(ref["lse"], f["lse"])
+                              and torch.equal(ref["out"].view(torch.int16), f["out"].view(torch.int16)))
+        del ref, kp, vp, ikp, vl
+    del x, f
     torch.cuda.empty_cache()
-    return {"ms_step": ms_step, "wall_ms_step": wall, "ms_index": ms_idx, "ms_topk": ms_topk, "ms_attn": ms_attn}
+    return res
+
+
+def to_pages(w, x, seed):
+    """Re-lay the contiguous caches of x as a page pool in the paged layout
+    (k/v [pages][h_kv][Bk][d], index_k [pages][Bk][d_idx]) with a seeded random
+    page permutation, and describe it with a Varlen of uniform lengths.  The
+    contiguous k, v and index_k are released from x as they are copied."""
+    import numpy as np
+    import torch
+    import block_sparse_long_qk_amd as msa
+    B, hk, bk, d, di, pps = w.batch, w.h_kv, w.block_size, w.head_dim, w.index_dim, w.n_blk
+    assert w.n_kv == pps * bk, "the paged bench leg takes whole blocks"
+    dev = x["q"].device
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(B * pps)).to(dev)
+    pool = {}
+    for name, page_shape in (("k", (hk, bk, d)), ("v", (hk, bk, d)), ("ik", (bk, di))):
+        dst = torch.empty((B * pps,) + page_shape, dtype=torch.bfloat16, device=dev)
+        for b in range(B):
+            src = x[name][b].view(hk, pps, bk, d).transpose(0, 1) if name != "ik" else x[name][b].view(pps, bk, di)
+            dst.index_copy_(0, perm[b * pps:(b + 1) * pps], src)
+        x[name] = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        pool[name] = dst
+    i32 = lambda a: a.to(torch.int32).contiguous()
+    vl = msa.Varlen.make(qo_lens=i32(torch.full((B,), w.n_q, device=dev)),
+                         kv_lens=i32(torch.full((B,), w.n_kv, device=dev)),
+                         q_starts=i32(torch.arange(B, device=dev) * w.n_q), total_q=B * w.n_q,
+                         page_table=i32(perm.view(B, pps)), num_pages=B * pps)
+    return vl, pool["k"], pool["v"], pool["ik"]
 
 
 def cpu_leg(w, n_positions, seed=0):
@@ -149,6 +199,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache (msa_forward_v) legs")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; the multi-GPU sharding is a design note, "
@@ -167,7 +218,7 @@ def main():
     torch.cuda.synchronize()
     del probe_src, probe_dst
     w = synth.WORKLOADS[args.workload]
-    g = gpu_leg(w, args.steps, args.warmup, stream)
+    g = gpu_leg(w, args.steps, args.warmup, stream, paged=not args.no_paged)
     f_idx, f_attn, topk_bytes, _ = algorithmic_work(w)
     tok_s = w.batch * w.n_q / (g["ms_step"] * 1e-3)
 
@@ -207,7 +258,7 @@ def main():
 
     if not args.no_decode:
         wd = synth.WORKLOADS[args.decode_workload]
-        gd = gpu_leg(wd, args.steps, args.warmup, stream)
+        gd = gpu_leg(wd, args.steps, args.warmup, stream, paged=not args.no_paged)
         db = decode_bytes(wd)
         line["decode"] = {
             "workload": wd.name, "tokens_per_s": round(wd.batch / (gd["ms_step"] * 1e-3), 1),
@@ -217,6 +268,20 @@ def main():
             "stages_ms": {"index_scores": round(gd["ms_index"], 4), "block_topk": round(gd["ms_topk"], 4),
                           "sparse_attn": round(gd["ms_attn"], 4)},
         }
+
+    if not args.no_paged:
+        # the same steps with the caches in a shuffled page pool (msa_forward_v, uniform lengths)
+        line["paged"] = {"prefill_ms_per_step": round(g["ms_step_paged"], 4),
+                         "prefill_tokens_per_s": round(w.batch * w.n_q / (g["ms_step_paged"] * 1e-3), 1),
+                         "prefill_vs_contiguous": round(g["ms_step"] / g["ms_step_paged"], 4),
+                         "prefill_bitwise_equal": g["paged_equal"]}
+        if not args.no_decode:
+            line["paged"].update({
+                "decode_ms_per_step": round(gd["ms_step_paged"], 4),
+                "decode_tokens_per_s": round(wd.batch / (gd["ms_step_paged"] * 1e-3), 1),
+                "decode_frac_hbm": round(db / (gd["ms_step_paged"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "decode_vs_contiguous": round(gd["ms_step"] / gd["ms_step_paged"], 4),
+                "decode_bitwise_equal": gd["paged_equal"]})
 
     if not args.no_cpu_baseline:
         print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
