@@ -22,6 +22,7 @@ SRC = os.path.join(_HERE, "msa_oracle.c")
 _lib = None
 
 _u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
 _i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
@@ -48,7 +49,10 @@ def _L():
                                       _f64, _f64p, _f64p]
         lib.oracle_dense_gqa.argtypes = [_u16p, _i64, _i64p, _i32, _u16p, _u16p, _i64, _i32, _f64, _f64p, _f64p]
         lib.oracle_merge.argtypes = [_f64p, _f64p, _i64, _i32, _i32, _f64p, _f64p]
-        for f in (lib.oracle_pool, lib.oracle_select, lib.oracle_attend, lib.oracle_dense_gqa, lib.oracle_merge):
+        lib.oracle_e4m3_decode.argtypes = [_u8p, _i64, _f64p]
+        lib.oracle_pool_f8.argtypes = [_u8p, _i64, _i64p, _u8p, _i64, _i32, _i32, _f64p, _i64]
+        for f in (lib.oracle_pool, lib.oracle_select, lib.oracle_attend, lib.oracle_dense_gqa, lib.oracle_merge,
+                  lib.oracle_e4m3_decode, lib.oracle_pool_f8):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -74,6 +78,26 @@ def pool(iq_rows, pos, ik, bk: int) -> np.ndarray:
     n_blk = -(-n_kv // bk)
     out = np.full((len(pos), n_blk), np.nan)
     _check(_L().oracle_pool(iq_rows, len(pos), pos, ik, n_kv, d_idx, bk, out, n_blk), "oracle_pool")
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP E4M3 codes (uint8) -> their values in fp64 (NaN for 0x7F / 0xFF)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _check(_L().oracle_e4m3_decode(c.reshape(-1), c.size, out.reshape(-1)), "oracle_e4m3_decode")
+    return out
+
+
+def pool_f8(iq_rows, pos, ik, bk: int) -> np.ndarray:
+    """pool() with E4M3 index inputs (uint8 codes)."""
+    iq_rows = np.ascontiguousarray(iq_rows, dtype=np.uint8)
+    ik = np.ascontiguousarray(ik, dtype=np.uint8)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    n_kv, d_idx = ik.shape
+    n_blk = -(-n_kv // bk)
+    out = np.full((len(pos), n_blk), np.nan)
+    _check(_L().oracle_pool_f8(iq_rows, len(pos), pos, ik, n_kv, d_idx, bk, out, n_blk), "oracle_pool_f8")
     return out
 
 

@@ -28,7 +28,8 @@
  *      other visible blocks;
  *   R6 with at most k visible blocks, all are selected; unused slots are -1;
  *   R7 equal pooled scores: the lower block index wins (-0 equals +0);
- *   R8 the selected indices are emitted in ascending order.
+ *   R8 the selected indices are emitted in ascending order;
+ *   R13 FP8 index inputs are OCP E4M3 (see oracle_pool_f8).
  *
  * Every function works on a batch of independent "rows" (one query position of
  * one sequence and one GQA group); the caller slices the tensors.  bf16 inputs
@@ -71,6 +72,58 @@ int oracle_pool(const uint16_t* iq, int64_t nrows, const int64_t* pos, const uin
       for (int64_t j = t * bk; j < j_end; ++j) {
         double s = 0.0;
         for (int32_t c = 0; c < d_idx; ++c) s += bf(iq[r * d_idx + c]) * bf(ik[j * d_idx + c]);
+        if (s > best) best = s;
+      }
+      pooled[r * ld + t] = best;
+    }
+  }
+  return 0;
+}
+
+/*
+ * FP8 index inputs.  The released kernels take FP8 as well as BF16 (page
+ * "MiniMax lança MSA…", section "Kernel open source e MiniMax-M3"; page
+ * "MiniMax 发布 MSA…", section 内核协同设计, the paragraph on the open-source
+ * kernel).  The pages do not name the 8-bit format; the reading taken (R13) is
+ * OCP E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, NaN only for exponent and mantissa all ones, largest finite
+ * value 448; exponent field 0 holds the subnormals m/8 * 2^-6.
+ */
+static double e4m3(uint8_t c) {
+  const int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m, -9)          /* (m/8) * 2^(1-7) */
+                            : ldexp(8.0 + (double)m, e - 10); /* (1 + m/8) * 2^(e-7) */
+  return sign ? -mag : mag;
+}
+
+/* Decode n E4M3 codes (exposed so that the decoder can be pinned on its own). */
+int oracle_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
+  if (n < 0) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3(codes[i]);
+  return 0;
+}
+
+/*
+ * The index scores and block max-pool of oracle_pool with E4M3 index inputs:
+ * the same definition on the decoded values (R1: raw dot product, no scale).
+ *   iq [nrows][d_idx] and ik [n_kv][d_idx] are E4M3 codes; the rest as above.
+ */
+int oracle_pool_f8(const uint8_t* iq, int64_t nrows, const int64_t* pos, const uint8_t* ik,
+                   int64_t n_kv, int32_t d_idx, int32_t bk, double* pooled, int64_t ld) {
+  if (nrows < 0 || d_idx <= 0 || bk <= 0 || ld < (n_kv + bk - 1) / bk) return -1;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (pos[r] < 0 || pos[r] >= n_kv) return -1;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t p = pos[r];
+    const int64_t local = p / bk;
+    for (int64_t t = 0; t <= local; ++t) {
+      const int64_t j_end = (t + 1) * bk < p + 1 ? (t + 1) * bk : p + 1;
+      double best = -INFINITY;
+      for (int64_t j = t * bk; j < j_end; ++j) {
+        double s = 0.0;
+        for (int32_t c = 0; c < d_idx; ++c) s += e4m3(iq[r * d_idx + c]) * e4m3(ik[j * d_idx + c]);
         if (s > best) best = s;
       }
       pooled[r * ld + t] = best;
