@@ -7,8 +7,8 @@ k 16), inputs seeded and synthetic, resident in HBM before timing starts.
 Prints one JSON line: prefill tokens/s (the value), the decode rate at a
 256K-token cache (64 sequences), per-stage times, the roofline of the dominant
 kernel, the same two steps with the caches in a shuffled page pool
-(msa_forward_v) and the oracle's CPU rate on a bounded sample of the same
-workload.
+(msa_forward_v), the same two steps with FP8 (E4M3) index inputs, and the
+oracle's CPU rate on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # HBM bytes of one standalone k_index_scores<128, 0> launch at 128K, from
 # rocprofv3 FETCH_SIZE (x2, calibrated on a 1 GiB copy) + WRITE_SIZE (x1); see
@@ -50,9 +51,11 @@ def decode_bytes(w):
     """HBM bytes one decode step must move: every index key once, the K/V of the
     selected tokens, Q, index-q, the output and the block indices."""
     _, _, _, t_size = algorithmic_work(w)
-    ik = 2.0 * w.batch * w.n_kv * w.index_dim
+    eb = 1.0 if w.index_dtype == "fp8" else 2.0   # bytes per index element
+    ik = eb * w.batch * w.n_kv * w.index_dim
     kv = 2.0 * 2 * w.head_dim * w.h_kv * w.batch * float(t_size.sum())
-    small = 2.0 * w.batch * w.n_q * (2 * w.h_q * w.head_dim + w.h_kv * w.index_dim) + 4.0 * w.batch * w.h_kv * w.topk
+    small = (2.0 * w.batch * w.n_q * 2 * w.h_q * w.head_dim + eb * w.batch * w.n_q * w.h_kv * w.index_dim
+             + 4.0 * w.batch * w.h_kv * w.topk)
     return ik + kv + small
 
 
@@ -83,7 +86,8 @@ def gpu_leg(w, steps, warmup, stream, paged=False):
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     x = synth.device_inputs(w)
     p = msa.Problem.make(w.batch, w.n_q, w.n_kv, w.h_q, w.h_kv, w.head_dim, w.index_dim, w.block_size, w.topk,
-                         w.q_offset, w.scale)
+                         w.q_offset, w.scale,
+                         index_dtype=msa.DTYPE_FP8_E4M3 if w.index_dtype == "fp8" else msa.DTYPE_BF16)
     f = msa.alloc_outputs(p)
     sp = stream.cuda_stream
 
@@ -200,6 +204,7 @@ def main():
     ap.add_argument("--cpu-positions", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache (msa_forward_v) legs")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) index-input legs")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; the multi-GPU sharding is a design note, "
@@ -282,6 +287,26 @@ def main():
                 "decode_frac_hbm": round(db / (gd["ms_step_paged"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 "decode_vs_contiguous": round(gd["ms_step"] / gd["ms_step_paged"], 4),
                 "decode_bitwise_equal": gd["paged_equal"]})
+
+    if not args.no_fp8:
+        # the same steps with E4M3 index inputs (the main branch stays bf16)
+        wf = w.replace(name=w.name + "_fp8_index", index_dtype="fp8")
+        gf = gpu_leg(wf, args.steps, args.warmup, stream)
+        f8_tflops = f_idx / (gf["ms_index"] * 1e-3) / 1e12
+        line["fp8_index"] = {"prefill_ms_per_step": round(gf["ms_step"], 4),
+                             "prefill_tokens_per_s": round(w.batch * w.n_q / (gf["ms_step"] * 1e-3), 1),
+                             "index_scores_ms": round(gf["ms_index"], 4), "index_tflops": round(f8_tflops, 1),
+                             "index_frac_fp8_mfma": round(f8_tflops / PEAK_FP8_TFLOPS, 4)}
+        if not args.no_decode:
+            wdf = wd.replace(name=wd.name + "_fp8_index", index_dtype="fp8")
+            gdf = gpu_leg(wdf, args.steps, args.warmup, stream)
+            dbf = decode_bytes(wdf)
+            line["fp8_index"].update({
+                "decode_ms_per_step": round(gdf["ms_step"], 4),
+                "decode_tokens_per_s": round(wdf.batch / (gdf["ms_step"] * 1e-3), 1),
+                "decode_bytes_per_step": dbf,
+                "decode_frac_hbm": round(dbf / (gdf["ms_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "decode_index_ms": round(gdf["ms_index"], 4)})
 
     if not args.no_cpu_baseline:
         print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)

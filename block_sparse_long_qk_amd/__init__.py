@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN, OP_FORWARD = range(4)
+DTYPE_BF16, DTYPE_FP8_E4M3 = range(2)  # msa_dtype: element type of index_q / index_k
 
 EXPORTS = ("msa_workspace_size", "msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
            "msa_index_scores_v", "msa_block_topk_v", "msa_sparse_attn_fwd_v", "msa_forward_v", "msa_status_string")
@@ -37,14 +38,16 @@ class Problem(ctypes.Structure):
         ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
         ("q_offset", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float),
+        ("index_dtype", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, batch, n_q, n_kv, h_q, h_kv, head_dim=128, index_dim=128, block_size=128, topk=16,
-             q_offset=-1, softmax_scale=None):
+             q_offset=-1, softmax_scale=None, index_dtype=DTYPE_BF16):
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(head_dim)
-        return cls(batch, n_q, n_kv, h_q, h_kv, head_dim, index_dim, block_size, topk, q_offset, softmax_scale)
+        return cls(batch, n_q, n_kv, h_q, h_kv, head_dim, index_dim, block_size, topk, q_offset, softmax_scale,
+                   index_dtype)
 
     @property
     def offset(self) -> int:

@@ -27,6 +27,7 @@ msa_status derive(const msa_problem* p, Dims* D) {
   const int64_t offset = p->q_offset == -1 ? (int64_t)p->n_kv - p->n_q : p->q_offset;
   if (offset < 0 || offset + p->n_q > p->n_kv) return MSA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(p->softmax_scale)) return MSA_ERR_INVALID_ARGUMENT;
+  if (p->index_dtype != MSA_DTYPE_BF16 && p->index_dtype != MSA_DTYPE_FP8_E4M3) return MSA_ERR_INVALID_ARGUMENT;
   const int64_t G = p->h_q / p->h_kv;
   const int64_t n_blk = ((int64_t)p->n_kv + p->block_size - 1) / p->block_size;
   // index ranges the kernels keep in 32 bits
@@ -56,6 +57,7 @@ msa_status derive(const msa_problem* p, Dims* D) {
   D->G = (int32_t)G;
   D->d = p->head_dim;
   D->d_idx = p->index_dim;
+  D->idx_eb = p->index_dtype == MSA_DTYPE_FP8_E4M3 ? 1 : 2;
   D->k = p->topk;
   D->n_blk = (int32_t)n_blk;
   D->pt = pt;
@@ -144,10 +146,8 @@ hipError_t run_attention(const Dims& D, const void* q, const void* k, const void
 }
 
 hipError_t run_index(const Dims& D, const void* index_q, const void* index_k, float* pooled, hipStream_t stream) {
-  auto iq = static_cast<const uint16_t*>(index_q);
-  auto ik = static_cast<const uint16_t*>(index_k);
-  return msa::use_index_small(D) ? msa::launch_index_small(iq, ik, pooled, D, stream)
-                                 : msa::launch_index_scores(iq, ik, pooled, D, stream);
+  return msa::use_index_small(D) ? msa::launch_index_small(index_q, index_k, pooled, D, stream)
+                                 : msa::launch_index_scores(index_q, index_k, pooled, D, stream);
 }
 
 size_t pooled_bytes(const Dims& D) { return round256(sizeof(float) * (size_t)D.B * D.h_kv * D.n_q * D.n_blk); }
@@ -232,8 +232,7 @@ msa_status msa_forward_v(const msa_problem* p, const msa_varlen* vl, const void*
   float* pooled = static_cast<float*>(workspace);
   hipError_t e;
   if (!msa::use_index_small(D) && msa::index_topk_fusable(D)) {
-    e = msa::launch_index_topk(static_cast<const uint16_t*>(index_q), static_cast<const uint16_t*>(index_k),
-                               block_idx, D, stream);
+    e = msa::launch_index_topk(index_q, index_k, block_idx, D, stream);
   } else {
     e = run_index(D, index_q, index_k, pooled, stream);
     if (e == hipSuccess) e = msa::launch_block_topk(pooled, block_idx, D, stream);

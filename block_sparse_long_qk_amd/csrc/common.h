@@ -1,5 +1,6 @@
 // Shared device helpers and launch descriptors of the MSA kernels (gfx950).
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,6 +33,7 @@ struct Dims {
   int64_t offset;      // position of query row 0 (uniform batches)
   float scale;         // softmax scale
   float scale_log2;    // softmax scale * log2(e)
+  int32_t idx_eb;      // bytes per index_q / index_k element: 2 (bf16) or 1 (FP8 E4M3)
   // Variable-length batches and paged caches.  All null: every sequence has
   // n_q query rows at positions offset .. offset + n_q - 1 and n_kv cached
   // tokens, each tensor contiguous.  Otherwise n_q and n_kv are maxima, per-row
@@ -134,6 +136,25 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(uint4 a, uint4 b, f32x16 c) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// FP8 (OCP E4M3) operands: 32 packed values per lane.  The gfx950 f8f6f4 MFMAs
+// with format code 0 for both operands and no block scale: products of E4M3
+// values are exact in fp32, accumulation is fp32.  Lane l supplies row (or
+// column) l % M and bytes [32 * (l / M), 32 * (l / M) + 32) of the k-step, with
+// the same k-order in A and B; the accumulator layout is that of the bf16 MFMA
+// of the same M.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x16 mfma_f8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// Two 16-byte pieces as one 32-byte operand.
+__device__ __forceinline__ i32x8 join32(u32x4 lo, u32x4 hi) {
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));

@@ -22,7 +22,6 @@
 namespace msa {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -45,13 +44,17 @@ __device__ __forceinline__ void wave_lds_fence() {
 // the next block.  Only wave-level ordering is needed: no workgroup barrier.
 // Loads past the cache end repeat its last key (masked: it follows every
 // row's position).  Pooled values wait in LDS and leave in batches, so stores
-// rarely interrupt the load stream.
-template <int DIDX, bool VL>
-__global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict__ iq,
-                                                     const uint16_t* __restrict__ ik, float* __restrict__ pooled,
+// rarely interrupt the load stream.  EB = 1 (FP8 E4M3 index inputs) uses the
+// 16x16x128 E4M3 MFMA instead: lane group c supplies bytes [32c, 32c + 32) of
+// a key and of a query row, one MFMA per 16 keys (index dim 64: groups 2 and 3
+// supply zeros).
+template <int DIDX, bool VL, int EB>
+__global__ __launch_bounds__(256) void k_index_small(const unsigned char* __restrict__ iq,
+                                                     const unsigned char* __restrict__ ik, float* __restrict__ pooled,
                                                      Dims D, int32_t blocks_per_wave) {
-  constexpr int KS = DIDX / 32;            // MFMA k-steps per key (16x16x32)
-  constexpr int ROW = DIDX * 2;            // bytes per key
+  constexpr bool F8 = EB == 1;
+  constexpr int KS = F8 ? 1 : DIDX / 32;   // MFMA k-steps per key (16x16x32 bf16, 16x16x128 E4M3)
+  constexpr int ROW = DIDX * EB;           // bytes per key
   constexpr int PITCH = ROW + 16;          // LDS bytes per key (pad: conflict-free operand reads)
   constexpr int STEP_KEYS = 32;
   constexpr int NSTEP = kBk / STEP_KEYS;   // steps per block = ring depth
@@ -74,15 +77,26 @@ __global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict_
   const int t1 = min(t0 + blocks_per_wave, t_last + 1);
   if (t0 >= t1) return;
 
-  uint4 qb[KS];
+  using Frag = std::conditional_t<F8, i32x8, uint4>;
+  Frag qb[KS];
   const bool row_ok = n < R;
   const int64_t pc = row_ok ? off_b + n / D.h_kv : -1;
   const int l_row = row_ok ? (int)(pc / kBk) : -1;
+  // E4M3 with index dim 64: lane groups 2 and 3 hold no index dims
+  const bool c_ok = !F8 || 32 * c < ROW;
+  {
+    const unsigned char* qrow =
+        iq + (row_ok ? (qrow_of<VL>(D, b, n / D.h_kv) * D.h_kv + n % D.h_kv) * ROW : 0);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qb[ks] = row_ok ? *reinterpret_cast<const uint4*>(iq + (qrow_of<VL>(D, b, n / D.h_kv) * D.h_kv + n % D.h_kv) * DIDX +
-                                                      8 * (KS * c + ks))
-                    : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (F8)
+        qb[ks] = row_ok && c_ok ? join32(*reinterpret_cast<const u32x4*>(qrow + 32 * c),
+                                         *reinterpret_cast<const u32x4*>(qrow + 32 * c + 16))
+                                : i32x8{};
+      else
+        qb[ks] = row_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * (KS * c + ks)) : make_uint4(0, 0, 0, 0);
+    }
+  }
   int64_t out_base = -1;
   if (row_ok) {
     const int i = n / D.h_kv, g = n % D.h_kv;
@@ -94,7 +108,7 @@ __global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict_
   auto fetch = [&](int t, int st, u32x4 (&x)[LOADS]) {
     // the block's keys are contiguous (a page when paged); past the cache end
     // its last key repeats
-    const unsigned char* blk = reinterpret_cast<const unsigned char*>(ik + ikoff_of<VL>(D, b, t));
+    const unsigned char* blk = ik + ikoff_of<VL>(D, b, t) * EB;
     const int last = nkv_b - 1 - t * kBk;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
@@ -134,10 +148,18 @@ __global__ __launch_bounds__(256) void k_index_small(const uint16_t* __restrict_
 #pragma unroll
       for (int T = 0; T < STEP_KEYS / 16; ++T) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const unsigned char* krow = buf + (16 * T + n) * PITCH;
+        if constexpr (F8) {
+          const i32x8 a = c_ok ? join32(*reinterpret_cast<const u32x4*>(krow + 32 * c),
+                                        *reinterpret_cast<const u32x4*>(krow + 32 * c + 16))
+                               : i32x8{};
+          acc = mfma_f8_16x16x128(a, qb[0], acc);
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 a = *reinterpret_cast<const uint4*>(buf + (16 * T + n) * PITCH + 16 * (KS * c + ks));
-          acc = mfma_16x16x32(a, qb[ks], acc);
+          for (int ks = 0; ks < KS; ++ks) {
+            const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * (KS * c + ks));
+            acc = mfma_16x16x32(a, qb[ks], acc);
+          }
         }
         // accumulator j of lane (n, c) is key skey0 + 16*T + 4*c + j against row n
 #pragma unroll
@@ -396,7 +418,7 @@ size_t attn_rows_partial_bytes(const Dims& D) {
   return sizeof(float) * (size_t)D.B * D.h_kv * D.n_q * (D.k + 1) * kRowsPart;
 }
 
-hipError_t launch_index_small(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
+hipError_t launch_index_small(const void* index_q, const void* index_k, float* pooled, const Dims& D,
                               hipStream_t stream) {
   const int t_max = (int)((D.offset + D.n_q - 1) / kBk) + 1;
   // one resident round of waves over the whole batch (8 waves per CU: the
@@ -415,13 +437,25 @@ hipError_t launch_index_small(const uint16_t* index_q, const uint16_t* index_k, 
   const int per = (int)((t_max + waves_per_b - 1) / waves_per_b);
   const int wgs = (int)(((t_max + per - 1) / per + 3) / 4);
   dim3 grid(wgs, D.B);
-  const bool vl = dims_varlen(D);
+  auto iq = static_cast<const unsigned char*>(index_q);
+  auto ik = static_cast<const unsigned char*>(index_k);
+  auto go = [&](auto didx, auto vl, auto eb) {
+    hipLaunchKernelGGL((k_index_small<decltype(didx)::value, decltype(vl)::value, decltype(eb)::value>), grid,
+                       dim3(256), 0, stream, iq, ik, pooled, D, per);
+  };
+  using I128 = std::integral_constant<int, 128>;
+  using I64 = std::integral_constant<int, 64>;
+  using T = std::true_type;
+  using F = std::false_type;
+  using E2 = std::integral_constant<int, 2>;
+  using E1 = std::integral_constant<int, 1>;
+  const bool vl = dims_varlen(D), f8 = D.idx_eb == 1;
   if (D.d_idx == 128) {
-    if (vl) hipLaunchKernelGGL((k_index_small<128, true>), grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
-    else hipLaunchKernelGGL((k_index_small<128, false>), grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+    if (f8) { if (vl) go(I128{}, T{}, E1{}); else go(I128{}, F{}, E1{}); }
+    else    { if (vl) go(I128{}, T{}, E2{}); else go(I128{}, F{}, E2{}); }
   } else {
-    if (vl) hipLaunchKernelGGL((k_index_small<64, true>), grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
-    else hipLaunchKernelGGL((k_index_small<64, false>), grid, dim3(256), 0, stream, index_q, index_k, pooled, D, per);
+    if (f8) { if (vl) go(I64{}, T{}, E1{}); else go(I64{}, F{}, E1{}); }
+    else    { if (vl) go(I64{}, T{}, E2{}); else go(I64{}, F{}, E2{}); }
   }
   return hipGetLastError();
 }

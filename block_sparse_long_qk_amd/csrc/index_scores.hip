@@ -15,6 +15,11 @@
 // (its own row).  Products of bf16 values are exact in fp32; accumulation is
 // fp32.  Causal masking (key j > p -> -inf) is applied only on blocks that
 // reach past the wave's first position.
+//
+// FP8 index inputs (EB = 1; page "MiniMax lança MSA…", section "Kernel open
+// source e MiniMax-M3": the released kernels take FP8 as well as BF16) run the
+// same loop on the 32x32x64 E4M3 MFMA: half the bytes per key row, a quarter
+// of the k-steps, the same accumulator layout and epilogue.
 #include <type_traits>
 
 #include "launch.h"
@@ -22,15 +27,24 @@
 namespace msa {
 namespace {
 
-template <int DIDX>
+// EB: bytes per index element, 2 (bf16) or 1 (FP8 E4M3).
+template <int DIDX, int EB>
 struct IdxCfg {
-  static constexpr int KS = DIDX / 16;              // MFMA k-steps per key row
-  static constexpr int CPR = DIDX / 8;              // 16-byte chunks per key row
-  static constexpr int RPI = 1024 / (2 * DIDX);     // key rows per 1 KB direct-to-LDS instruction
+  static constexpr bool F8 = EB == 1;
+  static constexpr int ROWB = DIDX * EB;            // bytes per key row
+  static constexpr int KB = F8 ? 64 : 16;           // index elements per MFMA k-step
+  static constexpr int KS = DIDX / KB;              // MFMA k-steps per key row
+  static constexpr int FB = F8 ? 32 : 16;           // operand bytes per lane per k-step
+  static constexpr int RPK = F8 ? 4 : 2;            // 16-byte LDS reads per k-step (two key rows)
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per key row
+  static constexpr int RPI = 1024 / ROWB;           // key rows per 1 KB direct-to-LDS instruction
   static constexpr int NI = kBk / RPI / 4;          // such instructions per wave per block
   // slot of chunk c of key row r is c ^ swz(r): the 16 lanes reading one chunk
   // of 16 consecutive rows then cover all 64 banks once
-  static __device__ __forceinline__ int swz(int r) { return DIDX == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int swz(int r) {
+    return ROWB == 256 ? (r & 15) : ROWB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+  }
+  using Frag = std::conditional_t<F8, i32x8, uint4>;
 };
 
 // Sort the KK selected block ids of a lane ascending (bitonic network over a
@@ -65,17 +79,17 @@ __device__ __forceinline__ void sort_ids(int (&ti)[KK]) {
 // every row (no key split); each lane keeps its row's best KK non-local blocks
 // by (score desc, index asc) in registers and writes the block_idx row (k = KK+1)
 // exactly as the standalone top-k does from the same fp32 scores.
-template <int DIDX, int KK, bool VL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_index_scores(const uint16_t* __restrict__ iq,
-                                                      const uint16_t* __restrict__ ik, float* __restrict__ pooled,
-                                                      int32_t* __restrict__ block_idx, Dims D,
-                                                      int32_t blocks_per_split) {
-  using C = IdxCfg<DIDX>;
+template <int DIDX, int KK, bool VL, int EB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_index_scores(
+    const unsigned char* __restrict__ iq, const unsigned char* __restrict__ ik, float* __restrict__ pooled,
+    int32_t* __restrict__ block_idx, Dims D, int32_t blocks_per_split) {
+  using C = IdxCfg<DIDX, EB>;
+  using Frag = typename C::Frag;
   // two key blocks (rows unpadded, chunks swizzled) as two separate arrays, each
   // named statically where it is used: the compiler can then tell a read of
   // one from the direct-to-LDS loads filling the other and does not wait for them
-  __shared__ __align__(16) uint16_t lds0[kBk * DIDX];
-  __shared__ __align__(16) uint16_t lds1[kBk * DIDX];
+  __shared__ __align__(16) unsigned char lds0[kBk * C::ROWB];
+  __shared__ __align__(16) unsigned char lds1[kBk * C::ROWB];
   __shared__ __align__(16) float pstage[KK == 0 ? 4 : 1][64][kPoolStage];  // per-lane pooled staging
   const float NEG_INF = -__builtin_huge_valf();
 
@@ -100,22 +114,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int64_t p_wave_min = off_b + (int64_t)(wave_active ? wrow0 : 0) / D.h_kv;
 
   // B operand: this lane's query columns (n-tile 0: row wrow0+col, n-tile 1: +32),
-  // 8 bf16 of the index dim per k-step.
+  // FB bytes of the index dim per k-step (8 bf16 or 32 E4M3 values).
   int64_t pc[2];
-  uint4 qb[2][C::KS];
+  Frag qb[2][C::KS];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int r = wrow0 + 32 * nt + col;
     if (r < rows_total) {
       pc[nt] = off_b + r / D.h_kv;
       const int64_t qr = VL ? qrow_of<VL>(D, b, r / D.h_kv) * D.h_kv + r % D.h_kv : (int64_t)b * rows_total + r;
-      const uint16_t* src = iq + qr * DIDX + 8 * half;
+      const unsigned char* src = iq + qr * C::ROWB + C::FB * half;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) qb[nt][ks] = *reinterpret_cast<const uint4*>(src + 16 * ks);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        if constexpr (C::F8)
+          qb[nt][ks] = join32(*reinterpret_cast<const u32x4*>(src + 64 * ks),
+                              *reinterpret_cast<const u32x4*>(src + 64 * ks + 16));
+        else
+          qb[nt][ks] = *reinterpret_cast<const uint4*>(src + 32 * ks);
+      }
     } else {
       pc[nt] = -1;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) qb[nt][ks] = make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < C::KS; ++ks) qb[nt][ks] = Frag{};
     }
   }
 
@@ -142,14 +162,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // l % CPR of row RPI * i + l / CPR.  Keys past the cache end repeat its last
   // key: finite values the causal mask drops (they follow every row's
   // position), so the loads need no per-key branch.
-  const uint16_t* ikb = ik + (int64_t)b * D.n_kv * DIDX;  // uniform case: sequence b's keys
-  auto fetch_block = [&](int t, uint16_t* dst) {
+  const unsigned char* ikb = ik + (int64_t)b * D.n_kv * C::ROWB;  // uniform case: sequence b's keys
+  auto fetch_block = [&](int t, unsigned char* dst) {
     // the block's keys are contiguous (a page when paged); past its last cached
     // key the last one repeats
-    const uint16_t* blk;
+    const unsigned char* blk;
     int last;
     if constexpr (VL) {
-      blk = ik + ikoff_of<VL>(D, b, t);
+      blk = ik + ikoff_of<VL>(D, b, t) * EB;
       last = nkv_b - 1 - t * kBk;
     } else {
       blk = ikb;
@@ -161,15 +181,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int i = wave * C::NI + u;
       const int row = C::RPI * i + lane / C::CPR, sl = lane % C::CPR;
       const int64_t jr = min(j0 + row, last);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(blk + jr * DIDX + 8 * (sl ^ C::swz(row))),
-                                       (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(blk + jr * C::ROWB + 16 * (sl ^ C::swz(row))),
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
     }
   };
 
   fetch_block(t_begin, lds0);
   auto process = [&](int t, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
-    const uint16_t* cur = buf == 0 ? lds0 : lds1;
+    const unsigned char* cur = buf == 0 ? lds0 : lds1;
     // this wave's part of block t has landed; after the barrier every part has,
     // and every wave is done with block t-1, whose buffer takes block t+1
     // (past the end: a repeat of the last block, never used, so that every
@@ -180,28 +200,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (wave_active) {
       const bool need_mask = (int64_t)t * kBk + kBk - 1 > p_wave_min;
       float run0 = NEG_INF, run1 = NEG_INF;
-      // two 32-key row tiles per iteration: four MFMA chains of 8 k-steps (32
+      // two 32-key row tiles per iteration: four MFMA chains (32 bf16 or 8 E4M3
       // MFMAs) between epilogues, each LDS fragment feeding two MFMAs
 #pragma unroll 1
       for (int mp = 0; mp < 2; ++mp) {
         f32x16 a00 = {}, a01 = {}, a10 = {}, a11 = {};
         const int r0 = 64 * mp + col, r1 = r0 + 32;
-        const uint16_t* arow0 = cur + r0 * DIDX;
-        const uint16_t* arow1 = cur + r1 * DIDX;
+        const unsigned char* arow0 = cur + r0 * C::ROWB;
+        const unsigned char* arow1 = cur + r1 * C::ROWB;
         const int sw0 = C::swz(r0), sw1 = C::swz(r1);
+        // this lane's FB bytes of k-step ks of a key row (chunks 2ks+half, or
+        // 4ks+2half and the next for E4M3)
+        auto frag = [&](const unsigned char* row, int sw, int ks) -> Frag {
+          if constexpr (C::F8) {
+            const int c0 = 4 * ks + 2 * half;
+            return join32(*reinterpret_cast<const u32x4*>(row + 16 * (c0 ^ sw)),
+                          *reinterpret_cast<const u32x4*>(row + 16 * ((c0 + 1) ^ sw)));
+          } else {
+            return *reinterpret_cast<const uint4*>(row + 16 * ((2 * ks + half) ^ sw));
+          }
+        };
+        auto mma = [&](Frag a, Frag bq, f32x16 c) {
+          if constexpr (C::F8) return mfma_f8_32x32x64(a, bq, c);
+          else return mfma_32x32x16(a, bq, c);
+        };
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          const uint4 f0 = *reinterpret_cast<const uint4*>(arow0 + 8 * ((2 * ks + half) ^ sw0));
-          const uint4 f1 = *reinterpret_cast<const uint4*>(arow1 + 8 * ((2 * ks + half) ^ sw1));
-          a00 = mfma_32x32x16(f0, qb[0][ks], a00);
-          a01 = mfma_32x32x16(f0, qb[1][ks], a01);
-          a10 = mfma_32x32x16(f1, qb[0][ks], a10);
-          a11 = mfma_32x32x16(f1, qb[1][ks], a11);
+          const Frag f0 = frag(arow0, sw0, ks);
+          const Frag f1 = frag(arow1, sw1, ks);
+          a00 = mma(f0, qb[0][ks], a00);
+          a01 = mma(f0, qb[1][ks], a01);
+          a10 = mma(f1, qb[0][ks], a10);
+          a11 = mma(f1, qb[1][ks], a11);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        // LDS reads two k-steps ahead of their MFMAs
+        constexpr int AHEAD = C::KS < 2 ? C::KS : 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, C::RPK * AHEAD, 0);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          if (ks + 2 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          if (ks + 2 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, C::RPK, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         auto pool = [&](f32x16& x0, f32x16& x1, int mt) {
@@ -308,20 +345,39 @@ static void index_grid(const Dims& D, dim3* grid, int* per) {
   *grid = dim3(row_tiles, (unsigned)nsplit, D.B);
 }
 
-hipError_t launch_index_scores(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
+// Launch k_index_scores<DIDX, KK, VL, EB> for the runtime d_idx, batch kind and
+// index element type.
+template <int KK>
+static void launch_index_kernel(const Dims& D, dim3 grid, int per, const void* index_q, const void* index_k,
+                                float* pooled, int32_t* block_idx, hipStream_t stream) {
+  auto iq = static_cast<const unsigned char*>(index_q);
+  auto ik = static_cast<const unsigned char*>(index_k);
+  auto go = [&](auto didx, auto vl, auto eb) {
+    hipLaunchKernelGGL((k_index_scores<decltype(didx)::value, KK, decltype(vl)::value, decltype(eb)::value>), grid,
+                       dim3(256), 0, stream, iq, ik, pooled, block_idx, D, per);
+  };
+  using I128 = std::integral_constant<int, 128>;
+  using I64 = std::integral_constant<int, 64>;
+  using T = std::true_type;
+  using F = std::false_type;
+  using E2 = std::integral_constant<int, 2>;
+  using E1 = std::integral_constant<int, 1>;
+  const bool vl = dims_varlen(D), f8 = D.idx_eb == 1;
+  if (D.d_idx == 128) {
+    if (f8) { if (vl) go(I128{}, T{}, E1{}); else go(I128{}, F{}, E1{}); }
+    else    { if (vl) go(I128{}, T{}, E2{}); else go(I128{}, F{}, E2{}); }
+  } else {
+    if (f8) { if (vl) go(I64{}, T{}, E1{}); else go(I64{}, F{}, E1{}); }
+    else    { if (vl) go(I64{}, T{}, E2{}); else go(I64{}, F{}, E2{}); }
+  }
+}
+
+hipError_t launch_index_scores(const void* index_q, const void* index_k, float* pooled, const Dims& D,
                                hipStream_t stream) {
   dim3 grid;
   int per;
   index_grid(D, &grid, &per);
-  const bool vl = dims_varlen(D);
-#define MSA_IDX(DI, VL) \
-  hipLaunchKernelGGL((k_index_scores<DI, 0, VL>), grid, dim3(256), 0, stream, index_q, index_k, pooled, nullptr, D, per)
-  if (D.d_idx == 128) {
-    if (vl) MSA_IDX(128, true); else MSA_IDX(128, false);
-  } else {
-    if (vl) MSA_IDX(64, true); else MSA_IDX(64, false);
-  }
-#undef MSA_IDX
+  launch_index_kernel<0>(D, grid, per, index_q, index_k, pooled, nullptr, stream);
   return hipGetLastError();
 }
 
@@ -333,26 +389,13 @@ bool index_topk_fusable(const Dims& D) {
   return grid.y == 1;
 }
 
-hipError_t launch_index_topk(const uint16_t* index_q, const uint16_t* index_k, int32_t* block_idx, const Dims& D,
+hipError_t launch_index_topk(const void* index_q, const void* index_k, int32_t* block_idx, const Dims& D,
                              hipStream_t stream) {
   dim3 grid;
   int per;
   index_grid(D, &grid, &per);
-#define MSA_IDX_TOPK(DI, KK)                                                                          \
-  do {                                                                                                \
-    if (dims_varlen(D))                                                                               \
-      hipLaunchKernelGGL((k_index_scores<DI, KK, true>), grid, dim3(256), 0, stream, index_q, index_k, \
-                         nullptr, block_idx, D, per);                                                 \
-    else                                                                                              \
-      hipLaunchKernelGGL((k_index_scores<DI, KK, false>), grid, dim3(256), 0, stream, index_q, index_k, \
-                         nullptr, block_idx, D, per);                                                 \
-  } while (0)
-  if (D.d_idx == 128) {
-    if (D.k == 16) MSA_IDX_TOPK(128, 15); else MSA_IDX_TOPK(128, 7);
-  } else {
-    if (D.k == 16) MSA_IDX_TOPK(64, 15); else MSA_IDX_TOPK(64, 7);
-  }
-#undef MSA_IDX_TOPK
+  if (D.k == 16) launch_index_kernel<15>(D, grid, per, index_q, index_k, nullptr, block_idx, stream);
+  else launch_index_kernel<7>(D, grid, per, index_q, index_k, nullptr, block_idx, stream);
   return hipGetLastError();
 }
 

@@ -8,13 +8,14 @@
 namespace msa {
 
 // Index scores + block max-pool: pooled[B][h_kv][n_q][n_blk] (fp32).
-hipError_t launch_index_scores(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
+// index_q / index_k elements are bf16 or E4M3 bytes (Dims::idx_eb).
+hipError_t launch_index_scores(const void* index_q, const void* index_k, float* pooled, const Dims& D,
                                hipStream_t stream);
 
 // Index scores with the block top-k fused into the epilogue (no pooled
 // round-trip); possible when one launch covers every block of every row.
 bool index_topk_fusable(const Dims& D);
-hipError_t launch_index_topk(const uint16_t* index_q, const uint16_t* index_k, int32_t* block_idx, const Dims& D,
+hipError_t launch_index_topk(const void* index_q, const void* index_k, int32_t* block_idx, const Dims& D,
                              hipStream_t stream);
 
 // Exp-free block top-k with the forced local block: block_idx[B][h_kv][n_q][k].
@@ -35,7 +36,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
 bool use_index_small(const Dims& D);   // at most 16 (query, group) rows per sequence
 bool use_attn_rows(const Dims& D);     // query-outer attention
 size_t attn_rows_partial_bytes(const Dims& D);
-hipError_t launch_index_small(const uint16_t* index_q, const uint16_t* index_k, float* pooled, const Dims& D,
+hipError_t launch_index_small(const void* index_q, const void* index_k, float* pooled, const Dims& D,
                               hipStream_t stream);
 hipError_t launch_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
                             uint16_t* out, float* lse, float* part, const Dims& D, hipStream_t stream);

@@ -209,6 +209,14 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* Vt, f32x16 (&s)[4], i
     }
     m2 = mref;
   }
+  // Masked (local) blocks: each probability enters P V as two bf16 parts,
+  // hi = bf16(P) and lo = bf16(P - hi), so the weights carry 16 significant
+  // bits instead of 8 (|P - hi - lo| <= 2^-16 P) at the price of a second MFMA
+  // per k-step.  A row whose weight sits on a few keys (an early position sees
+  // only its local block) needs it: bf16 weights alone could move its output
+  // by 2^-8 of its V values.  The local pass is bound by HBM reads, so the
+  // extra MFMAs are free there; non-local blocks (128 visible keys each) keep
+  // one bf16 pass.
   float sum = 0.f;
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
@@ -218,10 +226,11 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* Vt, f32x16 (&s)[4], i
   sum += wave_xor32(sum);
 #pragma unroll
   for (int D = 0; D < 4; ++D) o[D] = f32x16{};
-  // k-step j = 2T + u covers keys 32T + 16u .. +15; its V^T operands are read
-  // from LDS while the MFMAs of k-step j-1 run
+  // k-step j = 2T + u covers keys 32T + 16u .. +15.  One pass: its V^T
+  // operands are read from LDS while the MFMAs of k-step j-1 run; two passes:
+  // right before its eight MFMAs (the other wave of the SIMD covers the read
+  // latency, and the registers go to the lo parts)
   const uint16_t* vbase = Vt + col * VP + 4 * half;
-  uint4 vf[2][4];
   auto read_v = [&](int j, uint4 (&dst)[4]) {
 #pragma unroll
     for (int D = 0; D < 4; ++D) {
@@ -231,24 +240,52 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* Vt, f32x16 (&s)[4], i
       dst[D] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   };
-  read_v(0, vf[0]);
+  if constexpr (MASKED) {
+    uint4 vf[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int T = j >> 1, u = j & 1;
-    if (j + 1 < 8) read_v(j + 1, vf[(j + 1) & 1]);
-    const uint4 pb = make_uint4(pack_bf16x2(s[T][8 * u + 0], s[T][8 * u + 1]), pack_bf16x2(s[T][8 * u + 2], s[T][8 * u + 3]),
-                                pack_bf16x2(s[T][8 * u + 4], s[T][8 * u + 5]), pack_bf16x2(s[T][8 * u + 6], s[T][8 * u + 7]));
+    for (int j = 0; j < 8; ++j) {
+      const int T = j >> 1, u = j & 1;
+      read_v(j, vf);
+      uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int D = 0; D < 4; ++D) o[D] = mfma_32x32x16(vf[j & 1][D], pb, o[D]);
-  }
-  // issue order of the LDS reads and MFMAs (the VALU work interleaves freely)
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+      for (int w = 0; w < 4; ++w) {
+        const float a = s[T][8 * u + 2 * w], b = s[T][8 * u + 2 * w + 1];
+        hi[w] = pack_bf16x2(a, b);
+        lo[w] = pack_bf16x2(a - __uint_as_float(hi[w] << 16), b - __uint_as_float(hi[w] & 0xFFFF0000u));
+      }
+      const uint4 ph = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      const uint4 pl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 #pragma unroll
-  for (int j = 0; j < 7; ++j) {
+      for (int D = 0; D < 4; ++D) o[D] = mfma_32x32x16(vf[D], ph, o[D]);
+#pragma unroll
+      for (int D = 0; D < 4; ++D) o[D] = mfma_32x32x16(vf[D], pl, o[D]);
+    }
+    // issue order of the LDS reads and MFMAs (the VALU work interleaves freely)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+    }
+  } else {
+    uint4 vf[2][4];
+    read_v(0, vf[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int T = j >> 1, u = j & 1;
+      if (j + 1 < 8) read_v(j + 1, vf[(j + 1) & 1]);
+      const uint4 pb = make_uint4(pack_bf16x2(s[T][8 * u + 0], s[T][8 * u + 1]), pack_bf16x2(s[T][8 * u + 2], s[T][8 * u + 3]),
+                                  pack_bf16x2(s[T][8 * u + 4], s[T][8 * u + 5]), pack_bf16x2(s[T][8 * u + 6], s[T][8 * u + 7]));
+#pragma unroll
+      for (int D = 0; D < 4; ++D) o[D] = mfma_32x32x16(vf[j & 1][D], pb, o[D]);
+    }
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+    }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   l = sum;
 }
 

@@ -24,8 +24,8 @@
  *   q, out     [B][n_q][H_q][d]        bf16
  *   k, v       [B][H_kv][n_kv][d]      bf16  (each 128-token block of one head
  *                                             is one contiguous 32 KiB run)
- *   index_q    [B][n_q][H_kv][d_idx]   bf16  (one index-query head per group)
- *   index_k    [B][n_kv][d_idx]        bf16  (one shared index-key head)
+ *   index_q    [B][n_q][H_kv][d_idx]   bf16 or FP8 E4M3 (one index-query head per group)
+ *   index_k    [B][n_kv][d_idx]        bf16 or FP8 E4M3 (one shared index-key head)
  *   pooled     [B][H_kv][n_q][n_blk]   fp32
  *   block_idx  [B][H_kv][n_q][k]       int32
  *   lse        [B][H_q][n_q]           fp32, natural log (optional output)
@@ -40,7 +40,7 @@
  * Errors: argument checks run before any HIP call.  On failure nothing is
  * enqueued and the call returns MSA_ERR_INVALID_ARGUMENT (bad shapes, null or
  * misaligned pointers, q_offset + n_q > n_kv, k < 1, H_q % H_kv != 0, index
- * overflow) or MSA_ERR_UNSUPPORTED (shapes the kernels are not built for:
+ * overflow, an unknown index_dtype) or MSA_ERR_UNSUPPORTED (shapes the kernels are not built for:
  * d != 128, d_idx not in {64, 128}, Bk != 128, k > 64, G > 128).  A failed
  * kernel launch returns MSA_ERR_HIP.  No C++ exception crosses the ABI.
  * All device pointers must be 16-byte aligned; NaN inputs are not supported.
@@ -65,9 +65,23 @@ typedef enum {
   MSA_ERR_HIP = 4
 } msa_status;
 
+/* Element type of index_q and index_k.  The released kernels take FP8 as
+ * well as BF16 (page "MiniMax lança MSA…", section "Kernel open source e
+ * MiniMax-M3"); the 8-bit format is OCP E4M3 (bias 7, largest finite value
+ * 448, no infinities, NaN = all exponent and mantissa bits set).  Index scores
+ * are then the raw dot products of the E4M3 values, exact products accumulated
+ * in fp32; a per-tensor quantisation scale is a positive factor that leaves
+ * the selection unchanged and is the caller's to apply.  Every other tensor
+ * stays bf16. */
+typedef enum {
+  MSA_DTYPE_BF16 = 0,
+  MSA_DTYPE_FP8_E4M3 = 1
+} msa_dtype;
+
 /* One problem instance.  q_offset = -1 means bottom-right alignment,
  * q_offset = n_kv - n_q (prefill: n_q = n_kv gives 0; decode: n_q = 1 puts the
- * query on the last cached token, whose block is its local block). */
+ * query on the last cached token, whose block is its local block).
+ * index_dtype is a msa_dtype (0, bf16, when the struct is zero-initialised). */
 typedef struct {
   int32_t batch, n_q, n_kv;
   int32_t h_q, h_kv;
@@ -75,6 +89,7 @@ typedef struct {
   int32_t block_size, topk;
   int64_t q_offset;
   float softmax_scale; /* 1/sqrt(d) in the standard configuration */
+  int32_t index_dtype;
 } msa_problem;
 
 /* Which call a workspace is sized for. */
@@ -94,7 +109,8 @@ msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes);
  * visible keys with the group's index-query head against the shared index-key
  * head, then max-pool to blocks; reading R1: the score is the raw dot product).
  *   pooled[b][g][i][t] = max_{j in block t, j <= p_i} sum_c index_q[b][i][g][c] * index_k[b][j][c]
- * for t = 0 .. l_i, computed with fp32 accumulation of exact bf16 products.
+ * for t = 0 .. l_i, computed with fp32 accumulation of exact bf16 (or E4M3)
+ * products.
  * Entries with t > l_i are not written (their contents are unspecified).
  */
 msa_status msa_index_scores(const msa_problem* p, const void* index_q, const void* index_k, float* pooled,
@@ -123,7 +139,9 @@ msa_status msa_block_topk(const msa_problem* p, const float* pooled, int32_t* bl
  * Each block_idx row must be ascending with entries in [0, l_i] followed by -1
  * padding (as msa_block_topk writes it); the local block l_i is always
  * attended, listed or not.  out is bf16 (rounded to nearest even from fp32);
- * lse (nullable) gets ln sum_{j in T} exp(scale * q . k_j).
+ * lse (nullable) gets ln sum_{j in T} exp(scale * q . k_j).  Scores and
+ * sums are fp32; the probabilities enter P V with 16 significant bits (two
+ * bf16 parts), so a row whose weight sits on a few keys keeps its accuracy.
  * Needs workspace of msa_workspace_size(p, MSA_OP_SPARSE_ATTN).
  */
 msa_status msa_sparse_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v,

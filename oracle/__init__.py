@@ -152,7 +152,8 @@ def merge(o_parts, lse_parts):
 def inputs_for_rows(w, b: int, g: int, rows, plant=None):
     """Host inputs of one (sequence, group) for the given query rows.
 
-    Returns dict(pos, iq [n, d_idx], q [n, G, d], ik [pmax+1, d_idx]).
+    Returns dict(pos, iq [n, d_idx], q [n, G, d], ik [pmax+1, d_idx]); iq and ik
+    are bf16 bits, or E4M3 codes for an "fp8" workload.
     """
     import synth
     rows = np.asarray(rows, dtype=np.int64)
@@ -160,9 +161,16 @@ def inputs_for_rows(w, b: int, g: int, rows, plant=None):
     pos = w.offset + rows
     G = w.group
     iq = synth.host_iq_rows(w, b, rows, plant)[:, g, :]
+    if w.index_dtype == "fp8":
+        iq = synth.to_e4m3(iq)
     q = synth.host_q_rows(w, b, rows)[:, g * G:(g + 1) * G, :]
     ik = _index_keys(w, b, plant)[:int(pos.max()) + 1]
     return {"pos": pos, "iq": np.ascontiguousarray(iq), "q": np.ascontiguousarray(q), "ik": ik}
+
+
+def pool_for(w, iq_rows, pos, ik) -> np.ndarray:
+    """pool() or pool_f8(), as the workload's index element type requires."""
+    return (pool_f8 if w.index_dtype == "fp8" else pool)(iq_rows, pos, ik, w.block_size)
 
 
 _ik_cache = {}
@@ -175,7 +183,8 @@ def _index_keys(w, b: int, plant):
     key = (w, b)
     if key not in _ik_cache:
         _ik_cache.clear()
-        _ik_cache[key] = synth.host_ik(w, b, 0, w.n_kv, plant)
+        ik = synth.host_ik(w, b, 0, w.n_kv, plant)
+        _ik_cache[key] = synth.to_e4m3(ik) if w.index_dtype == "fp8" else ik
     return _ik_cache[key]
 
 
@@ -203,7 +212,7 @@ def forward_rows(w, b: int, g: int, rows, sel_given=None, plant=None):
     is passed, attention runs on that block set instead of the oracle's own.
     """
     x = inputs_for_rows(w, b, g, rows, plant)
-    pooled = pool(x["iq"], x["pos"], x["ik"], w.block_size)
+    pooled = pool_for(w, x["iq"], x["pos"], x["ik"])
     sel = select(pooled, x["pos"], w.block_size, w.topk)
     use = sel if sel_given is None else np.asarray(sel_given, dtype=np.int32)
     K, V = kv_for_blocks(w, b, g, use)

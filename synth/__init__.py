@@ -132,6 +132,7 @@ class Workload:
     plant_m: int = 0            # planted blocks per group (0: none)
     plant_alpha: float = 0.0    # amplitude added to planted index keys
     plant_beta: float = 0.0     # amplitude added to that group's index queries
+    index_dtype: str = "bf16"   # "fp8": index_q / index_k are the bf16 values rounded to OCP E4M3
 
     @property
     def offset(self) -> int:
@@ -269,6 +270,15 @@ def host_ik(w: Workload, b: int, j0: int, j1: int, plant: Plant | None = None) -
     return x
 
 
+def to_e4m3(bits: np.ndarray) -> np.ndarray:
+    """OCP E4M3 codes (uint8) of bf16 bit patterns, rounded to nearest even by
+    torch's float8_e4m3fn conversion (the same conversion the device inputs use)."""
+    import torch
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    t = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(b.shape)
+
+
 def host_q_rows(w: Workload, b: int, rows) -> np.ndarray:
     """Q[b, rows] for arbitrary query rows, shape [len(rows), h_q, d]."""
     rows = np.asarray(rows, dtype=np.int64)
@@ -379,13 +389,16 @@ def device_fill(w: Workload, name: str, tensor, stream=None, nt_dev=None):
 
 
 def device_inputs(w: Workload, device="cuda:0") -> dict:
-    """All five input tensors of a workload, generated on the device."""
+    """All five input tensors of a workload, generated on the device.  With
+    index_dtype "fp8", index_q and index_k are uint8 tensors of E4M3 codes."""
     import torch
     nt = torch.from_numpy(normal_table().view(np.int16).copy()).to(device)
     out = {}
     for name, shp in w.shapes().items():
         t = torch.empty(shp, dtype=torch.bfloat16, device=device)
         device_fill(w, name, t, nt_dev=nt)
+        if w.index_dtype == "fp8" and name in ("iq", "ik"):
+            t = t.to(torch.float8_e4m3fn).view(torch.uint8)
         out[name] = t
     torch.cuda.synchronize(device)
     return out

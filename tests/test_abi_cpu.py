@@ -53,6 +53,8 @@ def prob(**kw):
     (dict(topk=65), msa.ERR_UNSUPPORTED),
     (dict(h_q=256, h_kv=1), msa.ERR_UNSUPPORTED),             # G > 128
     (dict(batch=64, n_q=262144, n_kv=262144, h_kv=8, h_q=64, topk=64), msa.ERR_INVALID_ARGUMENT),  # int32 overflow
+    (dict(index_dtype=2), msa.ERR_INVALID_ARGUMENT),         # unknown index element type
+    (dict(index_dtype=-1), msa.ERR_INVALID_ARGUMENT),
 ])
 def test_invalid_problems_rejected(kw, status):
     p = prob(**kw)
@@ -139,3 +141,19 @@ def test_null_varlen_is_the_plain_call():
     lib = msa.library()
     fake = 1 << 20
     assert lib.msa_block_topk_v(ctypes.byref(p), None, fake, fake, None) == msa.ERR_INVALID_ARGUMENT
+
+
+def test_problem_struct_layout():
+    """The ctypes mirror of msa_problem has the C layout: nine int32, the
+    int64 offset on an 8-byte boundary, the float scale, the int32 dtype."""
+    P = msa.Problem
+    assert P.q_offset.offset == 40 and P.softmax_scale.offset == 48 and P.index_dtype.offset == 52
+    assert ctypes.sizeof(P) == 56
+
+
+def test_fp8_index_problems_accepted():
+    for d_idx in (64, 128):
+        p = prob(index_dim=d_idx, index_dtype=msa.DTYPE_FP8_E4M3)
+        n = ctypes.c_size_t(0)
+        assert msa.library().msa_workspace_size(ctypes.byref(p), msa.OP_FORWARD, ctypes.byref(n)) == msa.OK
+        assert n.value == msa.workspace_size(prob(index_dim=d_idx), msa.OP_FORWARD)

@@ -25,6 +25,8 @@ CASES = [
     ("mix_decode", 16, 2, 128, 16, [(1, 5000), (3, 700), (1, 9000), (2, 128), (1, 1)]),
     # index dim 64, one KV head, small k, ragged caches
     ("mix_dimx64", 4, 1, 64, 8, [(500, 900), (1200, 1200), (77, 77)]),
+    # FP8 (E4M3) index inputs, prefill and decode rows in one batch
+    ("mix_fp8", 16, 2, 128, 16, [(2000, 2500), (1, 6000), (0, 10), (130, 130)], "fp8"),
 ]
 SENTINEL_IDX = -77
 SENTINEL_LSE = 12345.0
@@ -32,9 +34,11 @@ SENTINEL_LSE = 12345.0
 
 def _build(case, paged: bool, seed0: int):
     import torch
-    name, h_q, h_kv, d_idx, k, seqs = case
+    name, h_q, h_kv, d_idx, k, seqs = case[:6]
+    dtype = case[6] if len(case) > 6 else "bf16"
     B = len(seqs)
-    ws = [synth.Workload(f"{name}_{b}", 1, max(qo, 1), kv, h_q, h_kv, index_dim=d_idx, topk=k, seed=seed0 + b)
+    ws = [synth.Workload(f"{name}_{b}", 1, max(qo, 1), kv, h_q, h_kv, index_dim=d_idx, topk=k, seed=seed0 + b,
+                         index_dtype=dtype)
           for b, (qo, kv) in enumerate(seqs)]
     xs = [synth.device_inputs(w) for w in ws]
     qo_l = [qo for qo, _ in seqs]
@@ -44,6 +48,13 @@ def _build(case, paged: bool, seed0: int):
     total_q = int(sum(qo_l))
     dev = xs[0]["q"].device
     big = 1.0e4
+    ik_dtype = xs[0]["ik"].dtype
+
+    def filled_index(shape):
+        # memory the index kernels must not read: large values (E4M3: 448, code 0x7E)
+        if ik_dtype == torch.uint8:
+            return torch.full(shape, 0x7E, dtype=torch.uint8, device=dev)
+        return torch.full(shape, big, dtype=torch.bfloat16, device=dev)
 
     def pack(key):
         parts = [x[key][0, :qo] for x, qo in zip(xs, qo_l) if qo > 0]
@@ -64,7 +75,7 @@ def _build(case, paged: bool, seed0: int):
             at += n_blk[b]
         kp = torch.full((num_pages, h_kv, bk, d), big, dtype=torch.bfloat16, device=dev)
         vp = torch.full_like(kp, big)
-        ikp = torch.full((num_pages, bk, d_idx), big, dtype=torch.bfloat16, device=dev)
+        ikp = filled_index((num_pages, bk, d_idx))
         for b, x in enumerate(xs):
             for t in range(n_blk[b]):
                 j0, j1 = t * bk, min((t + 1) * bk, kv_l[b])
@@ -78,7 +89,7 @@ def _build(case, paged: bool, seed0: int):
         num_pages, table_t = 0, None
         k_in = torch.full((B, h_kv, max_kv, d), big, dtype=torch.bfloat16, device=dev)
         v_in = torch.full_like(k_in, big)
-        ik_in = torch.full((B, max_kv, d_idx), big, dtype=torch.bfloat16, device=dev)
+        ik_in = filled_index((B, max_kv, d_idx))
         for b, x in enumerate(xs):
             k_in[b, :, :kv_l[b]] = x["k"][0]
             v_in[b, :, :kv_l[b]] = x["v"][0]
@@ -86,7 +97,8 @@ def _build(case, paged: bool, seed0: int):
     i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
     vl = msa.Varlen.make(qo_lens=i32(qo_l), kv_lens=i32(kv_l), q_starts=i32(starts.tolist()), total_q=total_q,
                          page_table=table_t, num_pages=num_pages)
-    p = msa.Problem.make(B, max_q, max_kv, h_q, h_kv, 128, d_idx, bk, k)
+    p = msa.Problem.make(B, max_q, max_kv, h_q, h_kv, 128, d_idx, bk, k,
+                         index_dtype=msa.DTYPE_FP8_E4M3 if dtype == "fp8" else msa.DTYPE_BF16)
     return ws, xs, vl, p, dict(q=q, iq=iq, k=k_in, v=v_in, ik=ik_in), qo_l, starts, total_q
 
 
