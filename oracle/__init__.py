@@ -51,8 +51,10 @@ def _L():
         lib.oracle_merge.argtypes = [_f64p, _f64p, _i64, _i32, _i32, _f64p, _f64p]
         lib.oracle_e4m3_decode.argtypes = [_u8p, _i64, _f64p]
         lib.oracle_pool_f8.argtypes = [_u8p, _i64, _i64p, _u8p, _i64, _i32, _i32, _f64p, _i64]
+        lib.oracle_kl.argtypes = [_u16p, _i64, _i64p, _i32p, _i32, _i32, _u16p, _i64, _i32, _u16p, _u16p, _i32, _i32,
+                                  _f64, _f64p]
         for f in (lib.oracle_pool, lib.oracle_select, lib.oracle_attend, lib.oracle_dense_gqa, lib.oracle_merge,
-                  lib.oracle_e4m3_decode, lib.oracle_pool_f8):
+                  lib.oracle_e4m3_decode, lib.oracle_pool_f8, lib.oracle_kl):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -124,6 +126,22 @@ def attend(q_rows, pos, sel, K, V, bk: int, scale: float):
     _check(_L().oracle_attend(q_rows, n, pos, sel, sel.shape[1], G, K, V, K.shape[0], d, bk, scale, out, lse),
            "oracle_attend")
     return out, lse
+
+
+def kl(q_rows, pos, sel, K, iq_rows, ik, bk: int, scale: float) -> np.ndarray:
+    """KL(teacher || student) per row over the selected blocks' visible tokens.
+
+    q_rows [n, G, d]; sel [n, k]; K [n_kv, d]; iq_rows [n, d_idx]; ik [n_kv, d_idx] (bf16 bits) -> [n].
+    """
+    q_rows, K = _u16(q_rows), _u16(K)
+    iq_rows, ik = _u16(iq_rows), _u16(ik)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    n, G, d = q_rows.shape
+    out = np.empty(n)
+    _check(_L().oracle_kl(q_rows, n, pos, sel, sel.shape[1], G, K, K.shape[0], d, iq_rows, ik, iq_rows.shape[1], bk,
+                          scale, out), "oracle_kl")
+    return out
 
 
 def dense_gqa(q_rows, pos, K, V, scale: float):

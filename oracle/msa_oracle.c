@@ -29,7 +29,9 @@
  *   R6 with at most k visible blocks, all are selected; unused slots are -1;
  *   R7 equal pooled scores: the lower block index wins (-0 equals +0);
  *   R8 the selected indices are emitted in ascending order;
- *   R13 FP8 index inputs are OCP E4M3 (see oracle_pool_f8).
+ *   R13 FP8 index inputs are OCP E4M3 (see oracle_pool_f8);
+ *   R14 the KL student is the softmax of the raw index scores over the
+ *       teacher's token set (see oracle_kl).
  *
  * Every function works on a batch of independent "rows" (one query position of
  * one sequence and one GQA group); the caller slices the tensors.  bf16 inputs
@@ -240,6 +242,80 @@ int oracle_attend(const uint16_t* q, int64_t nrows, const int64_t* pos, const in
       lse[r * G + h] = m + log(l);
     }
     free(z);
+    free(tok);
+    free(blocks);
+  }
+  return 0;
+}
+
+/*
+ * KL alignment of the Index Branch to the Main Branch, the training signal of
+ * the index projections (page "MiniMax 发布 MSA…", section MSA 如何训练: the
+ * loss matches the Index Branch's distribution to the Main Branch's attention,
+ * the teacher being the Main Branch's distribution over the selected tokens
+ * averaged over the group's heads; page "MiniMax lança MSA…", section
+ * "Treinamento com KL Divergence").  Per row, over T (the visible tokens of the
+ * selected blocks, as in oracle_attend):
+ *   teacher  p_j = (1/G) sum_h softmax_j(scale * q_h . k_j),
+ *   student  s_j = softmax_j(iq . ik_j)            (R14: raw index scores, R1),
+ *   kl = sum_j p_j ln(p_j / s_j),  terms with p_j = 0 contribute 0.
+ *   q [nrows][G][d], iq [nrows][d_idx], pos [nrows], sel [nrows][k];
+ *   K [n_kv][d], ik [n_kv][d_idx]  ->  kl [nrows]
+ */
+int oracle_kl(const uint16_t* q, int64_t nrows, const int64_t* pos, const int32_t* sel, int32_t k, int32_t G,
+              const uint16_t* K, int64_t n_kv, int32_t d, const uint16_t* iq, const uint16_t* ik, int32_t d_idx,
+              int32_t bk, double scale, double* kl) {
+  if (nrows < 0 || k < 1 || G < 1 || d <= 0 || d_idx <= 0 || bk <= 0) return -1;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (pos[r] < 0 || pos[r] >= n_kv) return -1;
+  const int64_t n_blk = (n_kv + bk - 1) / bk;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t p = pos[r];
+    int32_t* blocks = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    memcpy(blocks, sel + r * k, sizeof(int32_t) * (size_t)k);
+    qsort(blocks, (size_t)k, sizeof(int32_t), int_order);
+    int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)k * (size_t)bk);
+    int64_t nt = 0;
+    for (int32_t s = 0; s < k; ++s) {
+      const int32_t t = blocks[s];
+      if (t < 0 || t >= n_blk || (s > 0 && t == blocks[s - 1])) continue;
+      for (int64_t j = (int64_t)t * bk; j < ((int64_t)t + 1) * bk && j < n_kv && j <= p; ++j) tok[nt++] = j;
+    }
+    const size_t n = (size_t)(nt > 0 ? nt : 1);
+    double* teach = (double*)calloc(n, sizeof(double));
+    double* w = (double*)malloc(sizeof(double) * n);
+    /* teacher: each head's softmax over T, averaged over the group */
+    for (int32_t h = 0; h < G; ++h) {
+      const uint16_t* qh = q + (r * G + h) * d;
+      double m = -INFINITY;
+      for (int64_t a = 0; a < nt; ++a) {
+        double dot = 0.0;
+        for (int32_t c = 0; c < d; ++c) dot += bf(qh[c]) * bf(K[tok[a] * d + c]);
+        w[a] = scale * dot;
+        if (w[a] > m) m = w[a];
+      }
+      double l = 0.0;
+      for (int64_t a = 0; a < nt; ++a) l += exp(w[a] - m);
+      for (int64_t a = 0; a < nt; ++a) teach[a] += exp(w[a] - m) / l / G;
+    }
+    /* student: softmax of the raw index scores over the same tokens */
+    double m = -INFINITY;
+    for (int64_t a = 0; a < nt; ++a) {
+      double dot = 0.0;
+      for (int32_t c = 0; c < d_idx; ++c) dot += bf(iq[r * d_idx + c]) * bf(ik[tok[a] * d_idx + c]);
+      w[a] = dot;
+      if (w[a] > m) m = w[a];
+    }
+    double l = 0.0;
+    for (int64_t a = 0; a < nt; ++a) l += exp(w[a] - m);
+    const double log_norm = m + log(l);
+    double acc = 0.0;
+    for (int64_t a = 0; a < nt; ++a)
+      if (teach[a] > 0.0) acc += teach[a] * (log(teach[a]) - (w[a] - log_norm));
+    kl[r] = acc;
+    free(w);
+    free(teach);
     free(tok);
     free(blocks);
   }
