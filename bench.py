@@ -79,7 +79,7 @@ class Timer:
         return self.a.elapsed_time(self.b) / n
 
 
-def gpu_leg(w, steps, warmup, stream, paged=False):
+def gpu_leg(w, steps, warmup, stream, paged=False, kl=False):
     import torch
     import block_sparse_long_qk_amd as msa
     import synth
@@ -115,6 +115,17 @@ def gpu_leg(w, steps, warmup, stream, paged=False):
                                                 attn_ws, stream=sp), steps)
     res = {"ms_step": ms_step, "wall_ms_step": wall, "ms_index": ms_idx, "ms_topk": ms_topk, "ms_attn": ms_attn}
     del attn_ws
+    if kl and msa.workspace_size(p, msa.OP_INDEX_KL) > 0:
+        # the KL alignment pass on this step's selection and lse
+        kl_out = torch.empty((w.batch, w.h_kv, w.n_q), dtype=torch.float32, device="cuda")
+        kl_ws = torch.empty(max(msa.workspace_size(p, msa.OP_INDEX_KL), 256), dtype=torch.uint8, device="cuda")
+        run_kl = lambda: msa.index_kl(p, x["q"], x["k"], x["iq"], x["ik"], f["block_idx"], f["lse"], kl_out, kl_ws,
+                                      stream=sp)
+        for _ in range(warmup):
+            run_kl()
+        res["ms_kl"] = t.run(run_kl, steps)
+        res["kl_mean"] = float(kl_out.mean().item())
+        del kl_out, kl_ws
     if paged:
         # the same step through msa_forward_v, the caches re-laid as a shuffled page pool
         ref = {key: f[key].clone() for key in ("out", "block_idx", "lse")}
@@ -205,6 +216,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache (msa_forward_v) legs")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) index-input legs")
+    ap.add_argument("--no-kl", action="store_true", help="skip the KL alignment pass")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; the multi-GPU sharding is a design note, "
@@ -223,7 +235,7 @@ def main():
     torch.cuda.synchronize()
     del probe_src, probe_dst
     w = synth.WORKLOADS[args.workload]
-    g = gpu_leg(w, args.steps, args.warmup, stream, paged=not args.no_paged)
+    g = gpu_leg(w, args.steps, args.warmup, stream, paged=not args.no_paged, kl=not args.no_kl)
     f_idx, f_attn, topk_bytes, _ = algorithmic_work(w)
     tok_s = w.batch * w.n_q / (g["ms_step"] * 1e-3)
 
@@ -273,6 +285,14 @@ def main():
             "stages_ms": {"index_scores": round(gd["ms_index"], 4), "block_topk": round(gd["ms_topk"], 4),
                           "sparse_attn": round(gd["ms_attn"], 4)},
         }
+
+    if "ms_kl" in g:
+        # S = Q K^T for every head and Z = IQ IK^T for every group, over each row's tokens
+        _, _, _, t_size = algorithmic_work(w)
+        f_kl = 2.0 * (w.head_dim * w.h_q + w.index_dim * w.h_kv) * w.batch * float(t_size.sum())
+        line["kl"] = {"ms": round(g["ms_kl"], 4), "tflops": round(f_kl / (g["ms_kl"] * 1e-3) / 1e12, 1),
+                      "frac_mfma": round(f_kl / (g["ms_kl"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "mean_kl": round(g["kl_mean"], 5)}
 
     if not args.no_paged:
         # the same steps with the caches in a shuffled page pool (msa_forward_v, uniform lengths)

@@ -7,7 +7,7 @@ import of a compute entry point raises; nothing falls back to another path.
 
 Entry points (same names as the C ABI, without the ``msa_`` prefix):
 ``index_scores``, ``block_topk``, ``sparse_attn_fwd``, ``forward``,
-``workspace_size``; ``Problem`` mirrors ``msa_problem``.  Each compute call
+``index_kl``, ``workspace_size``; ``Problem`` mirrors ``msa_problem``.  Each compute call
 takes an optional ``varlen`` (a ``Varlen``, mirroring ``msa_varlen``: per
 sequence query and cache lengths, packed query rows, a page table); given,
 the ``*_v`` variant of the C call is used.
@@ -22,11 +22,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
-OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN, OP_FORWARD = range(4)
+OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN, OP_FORWARD, OP_INDEX_KL = range(5)
 DTYPE_BF16, DTYPE_FP8_E4M3 = range(2)  # msa_dtype: element type of index_q / index_k
 
 EXPORTS = ("msa_workspace_size", "msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
-           "msa_index_scores_v", "msa_block_topk_v", "msa_sparse_attn_fwd_v", "msa_forward_v", "msa_status_string")
+           "msa_index_scores_v", "msa_block_topk_v", "msa_sparse_attn_fwd_v", "msa_forward_v", "msa_index_kl",
+           "msa_status_string")
 
 
 class Problem(ctypes.Structure):
@@ -103,6 +104,7 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.msa_block_topk_v.argtypes = [P, V, vp, vp, vp]
         lib.msa_sparse_attn_fwd_v.argtypes = [P, V, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_forward_v.argtypes = [P, V, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.msa_index_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTS[:-1]:
             getattr(lib, name).restype = ctypes.c_int
         lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -198,6 +200,19 @@ def forward(p: Problem, q, k, v, index_q, index_k, out, block_idx, lse=None, wor
         rc = L.msa_forward_v(ctypes.byref(p), ctypes.byref(varlen), *args)
     _check(rc, "msa_forward")
     return out
+
+
+def index_kl(p: Problem, q, k, index_q, index_k, block_idx, lse, kl, workspace=None, workspace_bytes=None,
+             stream=None):
+    """KL(teacher || student) per (b, g, query): the group-averaged main-branch
+    distribution over the selected tokens against the softmax of the raw index
+    scores over the same tokens; lse is the forward pass's output."""
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    L, st = library(), _stream(stream, q)
+    rc = L.msa_index_kl(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(index_q), _ptr(index_k), _ptr(block_idx), _ptr(lse),
+                        _ptr(kl), _ptr(workspace), nb, st)
+    _check(rc, "msa_index_kl")
+    return kl
 
 
 # ---------------------------------------------------------------- allocation helpers (torch)

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
-SOURCES = ["index_scores.hip", "block_topk.hip", "gather_plan.hip", "sparse_attn.hip", "decode.hip", "abi.cpp"]
+SOURCES = ["index_scores.hip", "block_topk.hip", "gather_plan.hip", "sparse_attn.hip", "decode.hip", "kl.hip",
+           "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -89,7 +89,9 @@ msa_status derive_v(const msa_problem* p, const msa_varlen* vl, Dims* D) {
 }
 
 // Carve the sparse-attention workspace out of `base` (nullptr: sizing only).
-size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
+// with_o = false leaves out the partial outputs (the KL pass needs only the
+// plan, whose fill also marks the partial lse of unused slots).
+size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws, bool with_o = true) {
   const int64_t nbgt = msa::plan_bins(D);
   const int64_t slots = (int64_t)D.B * D.h_kv * D.n_q * D.k;
   const int64_t max_tiles = (slots + D.pt - 1) / D.pt + nbgt;
@@ -107,7 +109,7 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws) {
   char* list = take(sizeof(int2) * max_tiles * D.pt);
   const int64_t pslots = (int64_t)D.B * D.h_kv * D.n_q * (D.k + 1);  // + the local slot
   char* part_lse = take(sizeof(float) * pslots * D.G);
-  char* part_o = take(sizeof(uint16_t) * pslots * D.G * msa::kHeadDim);
+  char* part_o = with_o ? take(sizeof(uint16_t) * pslots * D.G * msa::kHeadDim) : nullptr;
   if (ws) {
     ws->hist = reinterpret_cast<int32_t*>(hist);
     ws->cnt = reinterpret_cast<int32_t*>(cnt);
@@ -152,6 +154,11 @@ hipError_t run_index(const Dims& D, const void* index_q, const void* index_k, fl
 
 size_t pooled_bytes(const Dims& D) { return round256(sizeof(float) * (size_t)D.B * D.h_kv * D.n_q * D.n_blk); }
 
+// The KL pass: the gather plan (without partial outputs), then one float4
+// partial per (row, slot).
+size_t kl_part_bytes(const Dims& D) { return round256(sizeof(float) * 4 * (size_t)D.B * D.h_kv * D.n_q * (D.k + 1)); }
+size_t kl_bytes(const Dims& D) { return attn_ws_layout(D, nullptr, nullptr, false) + kl_part_bytes(D); }
+
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
 }  // namespace
@@ -175,6 +182,10 @@ msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
     case MSA_OP_FORWARD:
       if (!attn_path_ok(D)) return MSA_ERR_UNSUPPORTED;
       *bytes = pooled_bytes(D) + attn_bytes(D);
+      return MSA_OK;
+    case MSA_OP_INDEX_KL:
+      if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
+      *bytes = kl_bytes(D);
       return MSA_OK;
     default:
       return MSA_ERR_INVALID_ARGUMENT;
@@ -239,6 +250,26 @@ msa_status msa_forward_v(const msa_problem* p, const msa_varlen* vl, const void*
   }
   if (e != hipSuccess) return MSA_ERR_HIP;
   return hip_status(run_attention(D, q, k, v, block_idx, out, lse, static_cast<char*>(workspace) + pb, stream));
+}
+
+msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q, const void* index_k,
+                        const int32_t* block_idx, const float* lse, float* kl, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !index_q || !index_k || !block_idx || !lse || !kl || !workspace) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(index_q) || !aligned16(index_k) || !aligned16(block_idx) ||
+      !aligned16(lse) || !aligned16(kl) || !aligned16(workspace))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
+  if (kl_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  AttnWs ws;
+  char* base = static_cast<char*>(workspace);
+  const size_t plan = attn_ws_layout(D, base, &ws, false);
+  return hip_status(msa::launch_index_kl(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                         static_cast<const uint16_t*>(index_q), static_cast<const uint16_t*>(index_k),
+                                         block_idx, lse, kl, ws, reinterpret_cast<float4*>(base + plan), D, stream));
 }
 
 msa_status msa_index_scores(const msa_problem* p, const void* index_q, const void* index_k, float* pooled,

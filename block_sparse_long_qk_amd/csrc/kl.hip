@@ -1,0 +1,376 @@
+// KL alignment of the Index Branch to the Main Branch (the forward value of the
+// loss that trains the index projections).
+//
+// Page "MiniMax 发布 MSA 稀疏注意力方法，开源推理内核并推出 MiniMax-M3 模型", section
+// MSA 如何训练: top-k selection has no gradient, so a KL loss matches the Index
+// Branch's distribution to the Main Branch's attention; the teacher is the Main
+// Branch's distribution over the selected tokens averaged over the group's
+// heads.  Per (sequence, group, query) over T (the visible tokens of the
+// selected blocks and the local block):
+//   teacher  p_j = (1/G) sum_h exp(scale q_h . k_j - lse_h),
+//   student  s_j = softmax_j(iq . ik_j)   (raw index scores),
+//   kl = sum_j p_j ln p_j - sum_j p_j z_j + ln sum_j exp(z_j),  z_j = iq . ik_j,
+// with lse_h the Main Branch's log-sum-exp from the forward pass, so that the
+// teacher needs no normalisation of its own and every sum splits over blocks.
+//
+// KV-outer over the same gather plan as the attention: persistent workgroups
+// walk the tiles with K and the index keys of one block in LDS; each wave owns
+// 32 rows (32 / G positions, all G heads).  S = Q K^T and Z = IQ IK^T run on
+// 32x32x16 bf16 MFMA with the query rows as the M operand, so that a lane holds
+// the scores of one key for 16 rows: the heads of a position sit in the lane's
+// registers (and, for G >= 8, its partner lane's), and the group average is an
+// in-lane sum plus one exchange.  Z is formed for every head row (the rows of a
+// position read the same index-query row), which keeps it in S's layout.  Each
+// (row, slot) gets a partial {sum p log2 p, sum p z, max z log2 e, sum 2^(z log2 e
+// - max)}; a merge adds a row's partials.
+#include "attn_tiles.h"
+
+namespace msa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// Rows of index queries one wave keeps: 32 / G positions, at most 8 (G >= 4).
+constexpr int kIqRows = 8;
+
+// Stage the K block (row-major, pitch KP) and the index-key block (row-major,
+// pitch DIDX + 8) of one 128-key block.  Keys at or past n_valid repeat key
+// n_valid - 1 (finite data the causal mask drops).  All loads are issued
+// before the first LDS write.
+template <int DIDX>
+__device__ __forceinline__ void stage_k_ik(uint16_t* Ks, uint16_t* IKs, const uint16_t* __restrict__ kb,
+                                           const uint16_t* __restrict__ ikb, int n_valid) {
+  constexpr int IKP = DIDX + 8;
+  constexpr int CPI = DIDX / 8;                    // 16-byte chunks per index-key row
+  constexpr int KPER = 2048 / kThreads, IPER = kBk * CPI / kThreads;
+  const int tid = threadIdx.x;
+  uint4 kr[KPER], ir[IPER];
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    const int c = tid + kThreads * u;
+    const int key = min(c >> 4, n_valid - 1), oc = c & 15;
+    kr[u] = *reinterpret_cast<const uint4*>(kb + key * kHeadDim + oc * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < IPER; ++u) {
+    const int c = tid + kThreads * u;
+    const int key = min(c / CPI, n_valid - 1), oc = c % CPI;
+    ir[u] = *reinterpret_cast<const uint4*>(ikb + key * DIDX + oc * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    const int c = tid + kThreads * u;
+    *reinterpret_cast<uint4*>(Ks + (c >> 4) * KP + (c & 15) * 8) = kr[u];
+  }
+#pragma unroll
+  for (int u = 0; u < IPER; ++u) {
+    const int c = tid + kThreads * u;
+    *reinterpret_cast<uint4*>(IKs + (c / CPI) * IKP + (c % CPI) * 8) = ir[u];
+  }
+}
+
+// The wave's index-query rows (one per position) by direct global-to-LDS loads:
+// row r at r * 2 * DIDX bytes, its 16-byte chunk c in slot c ^ (r % CPI), so the
+// rows of different positions read at one chunk index fall in different bank
+// groups.  `mine` points at the index-query row of this lane's position; the
+// row of position u is taken from lane u * G.  Rows past the wave's positions
+// fetch the last one again (allocated, never read).
+template <int DIDX, int G>
+__device__ __forceinline__ void fetch_iq_rows(unsigned char* iqw, const uint16_t* mine, int lane) {
+  constexpr int NP = 32 / G;                       // positions per wave
+  constexpr int CPI = DIDX / 8;                    // chunks per row (16 or 8)
+  constexpr int RPI = 64 / CPI;                    // rows per load instruction (4 or 8)
+  constexpr int NI = (NP + RPI - 1) / RPI;
+  const uint64_t me = reinterpret_cast<uint64_t>(mine);
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int r = RPI * u + lane / CPI;
+    const uint64_t src = shfl_u64(me, min(r, NP - 1) * G);
+    const int c = (lane % CPI) ^ (r % CPI);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + 16 * c),
+                                     (__attribute__((address_space(3))) void*)(iqw + 1024 * u), 16, 0, 0);
+  }
+}
+
+// S = Q K^T for one wave (query rows as M, keys as N): s[T] holds keys
+// 32T .. 32T+31, lane column = key, register e = query row 8(e/4) + 4 half + e%4.
+__device__ __forceinline__ void q_k_scores(const uint16_t* Ks, const unsigned char* qw, int lane, f32x16 (&s)[4]) {
+  const int col = lane & 31, half = lane >> 5;
+  const uint16_t* kbase = Ks + col * KP + 8 * half;
+  const unsigned char* qbase = qw + col * 256;
+  const int qsw = col & 15;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) s[T] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const uint4 qf = *reinterpret_cast<const uint4*>(qbase + 16 * ((2 * ks + half) ^ qsw));
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+      s[T] = mfma_32x32x16(qf, *reinterpret_cast<const uint4*>(kbase + 32 * T * KP + 16 * ks), s[T]);
+  }
+}
+
+// Z = IQ IK^T in the layout of q_k_scores: the M operand row of query row r is
+// the index-query row of its position r / G.
+template <int DIDX, int G>
+__device__ __forceinline__ void iq_ik_scores(const uint16_t* IKs, const unsigned char* iqw, int lane,
+                                             f32x16 (&z)[4]) {
+  constexpr int IKP = DIDX + 8;
+  constexpr int CPI = DIDX / 8;
+  const int col = lane & 31, half = lane >> 5;
+  const int pos = col / G;
+  const uint16_t* kbase = IKs + col * IKP + 8 * half;
+  const unsigned char* qbase = iqw + pos * (2 * DIDX);
+#pragma unroll
+  for (int T = 0; T < 4; ++T) z[T] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < DIDX / 16; ++ks) {
+    const uint4 qf = *reinterpret_cast<const uint4*>(qbase + 16 * ((2 * ks + half) ^ (pos % CPI)));
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+      z[T] = mfma_32x32x16(qf, *reinterpret_cast<const uint4*>(kbase + 32 * T * IKP + 16 * ks), z[T]);
+  }
+}
+
+// Lane-local positions.  A lane's 16 registers hold rows 8(e/4) + 4 half + e%4;
+// the RPP consecutive registers of lane-local position j belong to one query
+// position (all its heads for G = 4, half of them otherwise, the rest in the
+// partner lane l ^ 32).
+template <int G>
+struct PosMap {
+  static constexpr int RPP = G == 4 ? 4 : G / 2;   // registers per position in one lane
+  static constexpr int NPL = 16 / RPP;             // positions per lane
+  // wave-local position of lane-local position j
+  static __device__ __forceinline__ int wpos(int j, int half) { return G == 4 ? 2 * j + half : j; }
+};
+
+struct KlAcc {
+  float a, b, m, l;   // sum p log2 p, sum p z, max z log2 e, sum 2^(z log2 e - m)
+};
+
+__device__ __forceinline__ KlAcc kl_combine(KlAcc x, KlAcc y) {
+  const float m = fmaxf(x.m, y.m);
+  const float NEG_INF = -__builtin_huge_valf();
+  const float lx = x.m == NEG_INF ? 0.f : x.l * __builtin_amdgcn_exp2f(x.m - m);
+  const float ly = y.m == NEG_INF ? 0.f : y.l * __builtin_amdgcn_exp2f(y.m - m);
+  return KlAcc{x.a + y.a, x.b + y.b, m, lx + ly};
+}
+
+// Teacher probabilities of one tile for one wave: P[T][j] is the group's
+// average probability of key key0 + 32T + column for lane-local position j
+// (0 for keys after the position and for rows that do not exist).
+template <int G, bool MASKED>
+__device__ __forceinline__ void teacher_probs(const f32x16 (&s)[4], const float (&lse2)[16], const bool (&rowok)[16],
+                                              const int64_t (&ppos)[PosMap<G>::NPL], int64_t key0, int lane,
+                                              float c, float (&P)[4][PosMap<G>::NPL]) {
+  using PM = PosMap<G>;
+  const int col = lane & 31;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const int64_t key = key0 + 32 * T + col;
+#pragma unroll
+    for (int j = 0; j < PM::NPL; ++j) {
+      float psum = 0.f;
+#pragma unroll
+      for (int e = j * PM::RPP; e < (j + 1) * PM::RPP; ++e)
+        psum += rowok[e] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[T][e], c, -lse2[e])) : 0.f;
+      if constexpr (G >= 8) psum += wave_xor32(psum);
+      const bool vis = !MASKED || key <= ppos[j];
+      P[T][j] = vis ? psum * (1.f / G) : 0.f;
+    }
+  }
+}
+
+// Fold a tile's student scores into the partials of the lane-local positions
+// and sum them over the block's 128 keys (the 32 lanes of each half): every
+// lane of a half ends with its positions' sums.
+template <int G, bool MASKED>
+__device__ __forceinline__ void student_fold(const f32x16 (&z)[4], const float (&P)[4][PosMap<G>::NPL],
+                                             const int64_t (&ppos)[PosMap<G>::NPL], int64_t key0, int lane,
+                                             KlAcc (&acc)[PosMap<G>::NPL]) {
+  using PM = PosMap<G>;
+  const float NEG_INF = -__builtin_huge_valf();
+  const int col = lane & 31;
+#pragma unroll
+  for (int j = 0; j < PM::NPL; ++j) {
+    KlAcc x{0.f, 0.f, NEG_INF, 0.f};
+    // max of the visible scores, then the sums
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const bool vis = ppos[j] >= 0 && (!MASKED || key0 + 32 * T + col <= ppos[j]);
+      if (vis) x.m = fmaxf(x.m, z[T][j * PM::RPP] * kLog2e);
+    }
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const bool vis = ppos[j] >= 0 && (!MASKED || key0 + 32 * T + col <= ppos[j]);
+      const float zz = z[T][j * PM::RPP], p = P[T][j];
+      if (p > 0.f) x.a += p * __log2f(p);
+      x.b += p * zz;
+      if (vis) x.l += __builtin_amdgcn_exp2f(zz * kLog2e - x.m);
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      KlAcc y{__shfl_xor(x.a, o, 64), __shfl_xor(x.b, o, 64), __shfl_xor(x.m, o, 64), __shfl_xor(x.l, o, 64)};
+      x = kl_combine(x, y);
+    }
+    acc[j] = x;
+  }
+}
+
+// Persistent, XCD-aware walk as in the attention tiles (non-local tiles from the
+// gather plan, LOCAL: the masked local tiles, slot k).
+template <int DIDX, int G, bool LOCAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_kl_tiles(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ iq,
+    const uint16_t* __restrict__ ik, const float* __restrict__ lse, AttnWs ws, float4* __restrict__ kl_part,
+    Dims D) {
+  using PM = PosMap<G>;
+  constexpr int IKP = DIDX + 8;
+  __shared__ __align__(16) uint16_t Ks[kBk * KP];
+  __shared__ __align__(16) uint16_t IKs[kBk * IKP];
+  __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];
+  __shared__ __align__(16) unsigned char IQs[kWaves][kIqRows * 2 * DIDX];
+  int total;
+  if constexpr (LOCAL) {
+    total = D.B * D.h_kv * local_tiles<false>(D);
+  } else {
+    total = ws.tile_off[ws.n_bins];
+  }
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = gridDim.x / kXcds;
+  const int lo = (int)((int64_t)total * xcd / kXcds), hi = (int)((int64_t)total * (xcd + 1) / kXcds);
+  const int stride = per_xcd * kRun;
+  Walk w{lo + slot * kRun, lo + slot * kRun, min(lo + slot * kRun + kRun, hi)};
+  if (w.tile >= hi) return;  // uniform over the workgroup
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int r = wave * 32 + col;
+  const int ps = r / G, hh = r % G;
+  unsigned char* qw = Qs[wave];
+  unsigned char* iqw = IQs[wave];
+  const float c = D.scale_log2;
+
+  int staged_bg = -1, staged_t = -1;
+  while (w.tile < hi) {
+    TileRow cur = tile_row<LOCAL, false>(tile_raw<LOCAL>(ws, D, w.tile, ps), D, ws, w.tile, ps);
+    const int b = cur.bg / D.h_kv, g = cur.bg % D.h_kv;
+    const int i = cur.valid ? cur.i : 0;
+    // this lane's row: its query row, its position's index-query row, its lse
+    // (the wave is done with its regions: the previous tile ran to the end)
+    fetch_q_rows(qw, q + (((int64_t)b * D.n_q + i) * D.h_q + g * G + hh) * kHeadDim, lane);
+    fetch_iq_rows<DIDX, G>(iqw, iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX, lane);
+    const float lse_mine = lse[((int64_t)b * D.h_q + g * G + hh) * D.n_q + i] * kLog2e;
+    const bool row_ok = cur.valid;
+    if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform: a new block for the workgroup
+      __syncthreads();  // every wave is done with the staged block
+      const int64_t kv0 = (((int64_t)b * D.h_kv + g) * D.n_kv + (int64_t)cur.t * kBk) * kHeadDim;
+      const int64_t ik0 = ((int64_t)b * D.n_kv + (int64_t)cur.t * kBk) * DIDX;
+      stage_k_ik<DIDX>(Ks, IKs, k + kv0, ik + ik0, max(1, min(kBk, D.n_kv - cur.t * kBk)));
+      staged_bg = cur.bg;
+      staged_t = cur.t;
+      __syncthreads();
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's query and index-query rows have landed
+    // the lse and validity of the 16 rows this lane's registers hold
+    float lse2[16];
+    bool rowok[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int re = 8 * (e >> 2) + 4 * half + (e & 3);
+      lse2[e] = __shfl(lse_mine, re, 64);
+      rowok[e] = __shfl((int)row_ok, re, 64) != 0;
+    }
+    int64_t ppos[PM::NPL];  // position of each lane-local position (-1: no such row)
+    int pi[PM::NPL], pv[PM::NPL], pslot[PM::NPL];
+#pragma unroll
+    for (int j = 0; j < PM::NPL; ++j) {
+      const int src = PM::wpos(j, half) * G;
+      pi[j] = __shfl(cur.i, src, 64);
+      pv[j] = __shfl((int)cur.valid, src, 64);
+      pslot[j] = __shfl(cur.s, src, 64);
+      ppos[j] = pv[j] ? D.offset + pi[j] : -1;
+    }
+    float P[4][PM::NPL];
+    {
+      f32x16 sc[4];
+      q_k_scores(Ks, qw, lane, sc);
+      teacher_probs<G, LOCAL>(sc, lse2, rowok, ppos, (int64_t)cur.t * kBk, lane, c, P);
+    }
+    KlAcc acc[PM::NPL];
+    {
+      f32x16 zz[4];
+      iq_ik_scores<DIDX, G>(IKs, iqw, lane, zz);
+      student_fold<G, LOCAL>(zz, P, ppos, (int64_t)cur.t * kBk, lane, acc);
+    }
+    // the lane of each position's first head row writes its partial
+#pragma unroll
+    for (int j = 0; j < PM::NPL; ++j) {
+      const bool writer = col == PM::wpos(j, half) * G && (G == 4 || half == 0);
+      if (writer && pv[j]) {
+        const int64_t row = (int64_t)cur.bg * D.n_q + pi[j];
+        kl_part[row * (D.k + 1) + pslot[j]] = make_float4(acc[j].a, acc[j].b, acc[j].m, acc[j].l);
+      }
+    }
+    w = walk_next(w, stride, hi);
+  }
+}
+
+// One thread per (sequence, group, query): add the row's partials (the listed
+// non-local blocks and the local block, slot k) and form the KL value.
+__global__ __launch_bounds__(256) void k_kl_merge(const int32_t* __restrict__ block_idx,
+                                                  const float4* __restrict__ kl_part, float* __restrict__ kl,
+                                                  Dims D) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= (int64_t)D.B * D.h_kv * D.n_q) return;
+  const int i = (int)(row % D.n_q);
+  const int local = (int)((D.offset + i) / kBk);
+  const int32_t* sel = block_idx + row * D.k;
+  const float4* part = kl_part + row * (D.k + 1);
+  KlAcc acc = kl_combine(KlAcc{0.f, 0.f, -__builtin_huge_valf(), 0.f},
+                         KlAcc{part[D.k].x, part[D.k].y, part[D.k].z, part[D.k].w});
+  for (int s = 0; s < D.k; ++s) {
+    if (!nonlocal_slot(sel, s, local)) continue;
+    const float4 x = part[s];
+    acc = kl_combine(acc, KlAcc{x.x, x.y, x.z, x.w});
+  }
+  kl[row] = acc.a * kLn2 - acc.b + (acc.m + __log2f(acc.l)) * kLn2;
+}
+
+}  // namespace
+
+bool kl_supported(const Dims& D) {
+  return (D.G == 4 || D.G == 8 || D.G == 16 || D.G == 32) && D.idx_eb == 2 && !dims_varlen(D);
+}
+
+hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,
+                           const int32_t* block_idx, const float* lse, float* kl, const AttnWs& ws, float4* kl_part,
+                           const Dims& D, hipStream_t stream) {
+  hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid(persistent_grid()), block(kThreads);
+  auto go = [&](auto didx, auto g) {
+    constexpr int DI = decltype(didx)::value, GG = decltype(g)::value;
+    hipLaunchKernelGGL((k_kl_tiles<DI, GG, false>), grid, block, 0, stream, q, k, index_q, index_k, lse, ws,
+                       kl_part, D);
+    hipLaunchKernelGGL((k_kl_tiles<DI, GG, true>), grid, block, 0, stream, q, k, index_q, index_k, lse, ws, kl_part,
+                       D);
+  };
+  using I128 = std::integral_constant<int, 128>;
+  using I64 = std::integral_constant<int, 64>;
+  auto by_g = [&](auto didx) {
+    switch (D.G) {
+      case 4: go(didx, std::integral_constant<int, 4>{}); break;
+      case 8: go(didx, std::integral_constant<int, 8>{}); break;
+      case 16: go(didx, std::integral_constant<int, 16>{}); break;
+      default: go(didx, std::integral_constant<int, 32>{}); break;
+    }
+  };
+  if (D.d_idx == 128) by_g(I128{}); else by_g(I64{});
+  const int64_t rows = (int64_t)D.B * D.h_kv * D.n_q;
+  hipLaunchKernelGGL(k_kl_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, block_idx, kl_part, kl,
+                     D);
+  return hipGetLastError();
+}
+
+}  // namespace msa

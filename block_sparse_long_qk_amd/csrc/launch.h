@@ -32,6 +32,15 @@ int64_t plan_bins(const Dims& D);         // (b, g, query group, block) bins
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream);
 
+// KL alignment of the index branch to the main branch's group-averaged
+// attention over the selected tokens (needs the forward's lse); kl_part holds
+// one float4 per (row, slot).  Supported for G in {4, 8, 16, 32}, bf16 index
+// inputs and uniform batches.
+bool kl_supported(const Dims& D);
+hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,
+                           const int32_t* block_idx, const float* lse, float* kl, const AttnWs& ws, float4* kl_part,
+                           const Dims& D, hipStream_t stream);
+
 // Decode-shaped calls (few query rows per sequence).
 bool use_index_small(const Dims& D);   // at most 16 (query, group) rows per sequence
 bool use_attn_rows(const Dims& D);     // query-outer attention

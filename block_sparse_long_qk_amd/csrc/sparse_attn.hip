@@ -26,18 +26,12 @@
 // l % 32, so all softmax statistics of a row live in one lane pair (l, l ^ 32).
 #include <algorithm>
 
-#include "launch.h"
+#include "attn_tiles.h"
 
 namespace msa {
 namespace {
 
-constexpr int KP = kHeadDim + 8;   // LDS pitch of K rows (bf16): 16-byte pad
-constexpr int kXcds = 8;           // XCDs of an MI355X; workgroups are dealt round-robin over them
-constexpr int kRun = 8;            // consecutive tiles one workgroup takes before moving on
 constexpr int VP = kBk + 4;        // LDS pitch of V^T rows (bf16): 8-byte pad
-constexpr int kWaves = 8;          // waves per tile workgroup (kWaves * 32 = 256 rows per tile)
-constexpr int kThreads = 64 * kWaves;
-constexpr int kQRegion = 32 * 256; // LDS bytes of one wave's 32 query rows
 
 // Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS
 // with the workgroup's kThreads threads.  Keys at or past n_valid (n_valid >= 1)
@@ -80,35 +74,6 @@ __device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint1
       const uint32_t v2 = (w[2][e >> 1] >> sh) & 0xFFFFu, v3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
       *reinterpret_cast<uint2*>(Vt + (od * 8 + e) * VP + kq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
     }
-  }
-}
-
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
-  const uint32_t lo = __shfl((uint32_t)x, src, 64);
-  const uint32_t hi = __shfl((uint32_t)(x >> 32), src, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// A wave's query rows live in its 8 KB LDS region row-major: row r (0..31) at
-// r * 256 bytes, its 16-byte chunk c (dims 8c..8c+7) in slot c ^ (r % 16), so
-// that the 16 lanes reading one chunk of 16 rows hit 16 different bank groups.
-// The rows are fetched with direct global-to-LDS loads, which place lane l's
-// 16 bytes at l * 16 past the instruction's LDS address: instruction u fills
-// rows 4u..4u+3, the 16 lanes of a row fetching its 16 chunks (permuted), so
-// every load instruction reads whole 256-byte rows.  `mine` is the row this
-// lane's column owns (lanes l and l ^ 32 own the same one); rows that do not
-// exist point at a stand-in row whose results are never stored.
-__device__ __forceinline__ void fetch_q_rows(unsigned char* qw, const uint16_t* mine, int lane) {
-  const uint64_t me = reinterpret_cast<uint64_t>(mine);
-  uint64_t row[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) row[u] = shfl_u64(me, 4 * u + (lane >> 4));
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r = 4 * u + (lane >> 4);
-    const int c = (lane & 15) ^ (r & 15);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(row[u] + 16 * c),
-                                     (__attribute__((address_space(3))) void*)(qw + 1024 * u), 16, 0, 0);
   }
 }
 
@@ -287,92 +252,6 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* Vt, f32x16 (&s)[4], i
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   }
   l = sum;
-}
-
-// Local tiles per (sequence, group): runs of pt consecutive positions (aligned
-// to pt) covering the sequence's query positions; with variable lengths an upper
-// bound, the tiles past a sequence's rows having no valid row.
-template <bool VL>
-__device__ __forceinline__ int local_tiles(const Dims& D) {
-  if (VL && (D.qo_lens || D.kv_lens)) return (D.n_q + D.pt - 1) / D.pt + 1;
-  return (int)((D.offset + D.n_q - 1) / D.pt - D.offset / D.pt + 1);
-}
-
-// One lane's row of a tile.  Non-local tiles come from the tile-major gather
-// lists (row = query i, slot s of its block_idx row); local tiles are runs of
-// pt consecutive positions that share their local block (slot k).
-struct TileRow {   // five ints, no padding bytes (which would keep the struct in memory)
-  int bg, t;      // (b * h_kv + g), KV block
-  int valid;      // this lane's row exists
-  int i, s;       // query row (position offset + i), partial slot (k = the local block)
-};
-
-// What a lane loads to describe its row of a non-local tile: its list entry,
-// which also carries the tile's bin.  Each lane reads its own entry (lanes past
-// pt read entry pt - 1), so the bin arrives per lane and nothing waits for it
-// until the tile is decoded, a step later.
-struct TileRaw {
-  int e, bin;
-};
-
-template <bool LOCAL>
-__device__ __forceinline__ TileRaw tile_raw(const AttnWs& ws, const Dims& D, int tile, int ps) {
-  TileRaw r{-1, 0};
-  if constexpr (!LOCAL) {
-    const int2 x = ws.list[(int64_t)tile * D.pt + min(ps, D.pt - 1)];
-    r.e = x.x;
-    r.bin = x.y;
-  }
-  return r;
-}
-
-template <bool LOCAL, bool VL>
-__device__ __forceinline__ TileRow tile_row(const TileRaw& raw, const Dims& D, const AttnWs& ws, int tile, int ps) {
-  TileRow tr;
-  tr.i = 0;
-  tr.s = 0;
-  if constexpr (!LOCAL) {
-    const int bin = __builtin_amdgcn_readfirstlane(raw.bin);  // equal over the tile
-    tr.bg = bin / (ws.n_groups * D.n_blk);
-    tr.t = bin % D.n_blk;
-    tr.valid = ps < D.pt && raw.e >= 0;
-    if (tr.valid) {
-      tr.i = raw.e / D.k;
-      tr.s = raw.e % D.k;
-    }
-  } else {
-    const int n_loc = local_tiles<VL>(D);
-    tr.bg = tile / n_loc;
-    const int b = tr.bg / D.h_kv;
-    const int64_t off_b = off_of<VL>(D, b);
-    const int64_t p0 = (off_b / D.pt + tile % n_loc) * D.pt;
-    tr.t = (int)min(p0 / kBk, (int64_t)D.n_blk - 1);  // tiles past the sequence's rows stay in bounds
-    const int64_t p = p0 + ps;
-    tr.valid = ps < D.pt && p >= off_b && p < off_b + nq_of<VL>(D, b);
-    if (tr.valid) {
-      tr.i = (int)(p - off_b);
-      tr.s = D.k;
-    }
-  }
-  return tr;
-}
-
-// Walk of one workgroup over its tiles: runs of kRun consecutive tiles,
-// successive runs `stride` apart, inside [.., hi).
-struct Walk {
-  int tile, run_start, run_end;
-};
-
-__device__ __forceinline__ Walk walk_next(const Walk& w, int stride, int hi) {
-  Walk n = w;
-  if (w.tile + 1 < w.run_end) {
-    n.tile = w.tile + 1;
-  } else {
-    n.run_start = w.run_start + stride;  // stride >= kRun: strictly increasing
-    n.tile = n.run_start < hi ? n.run_start : hi;
-    n.run_end = min(n.run_start + kRun, hi);
-  }
-  return n;
 }
 
 // The wave's 32 normalised partials, bf16 in lane order: row q's 128 values
@@ -646,18 +525,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         lse_out[((int64_t)b * D.h_q + g * D.G + hh) * D.n_q + cur.i] = (M + __log2f(L)) * 0.69314718055994531f;
     }
   }
-}
-
-int persistent_grid() {  // a multiple of kXcds
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || n <= 0)
-      n = 256;
-    cus = n;
-  }
-  return (cus + kXcds - 1) / kXcds * kXcds;  // one 131 KB-LDS workgroup of 8 waves per CU
 }
 
 }  // namespace

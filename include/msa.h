@@ -97,7 +97,8 @@ typedef enum {
   MSA_OP_INDEX_SCORES = 0,
   MSA_OP_BLOCK_TOPK = 1,
   MSA_OP_SPARSE_ATTN = 2,
-  MSA_OP_FORWARD = 3
+  MSA_OP_FORWARD = 3,
+  MSA_OP_INDEX_KL = 4
 } msa_op;
 
 /* Bytes of device workspace the call `op` needs for problem `p` (0 for the
@@ -156,6 +157,28 @@ msa_status msa_sparse_attn_fwd(const msa_problem* p, const void* q, const void* 
 msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const void* v, const void* index_q,
                        const void* index_k, void* out, int32_t* block_idx, float* lse, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * KL alignment of the Index Branch to the Main Branch: the forward value of
+ * the loss that trains the index projections (section MSA 如何训练: top-k has no
+ * gradient, so the Index Branch's distribution is matched to the Main
+ * Branch's; the teacher is the Main Branch's distribution over the selected
+ * tokens averaged over the group's heads).  For every (b, g, i), over
+ * T = { j <= p_i : floor(j / Bk) in S } as in msa_sparse_attn_fwd:
+ *   teacher  t_j = (1/G) sum_{h in g} exp(scale * q[b][i][h] . k[b][g][j] - lse[b][h][i]),
+ *   student  s_j = softmax_{j in T}(index_q[b][i][g] . index_k[b][j])   (raw index scores),
+ *   kl[b][g][i] = sum_{j in T} t_j ln(t_j / s_j)   (fp32; terms with t_j = 0 add 0).
+ * lse is the natural-log output of msa_sparse_attn_fwd (or msa_forward) for
+ * the same block_idx; the teacher is normalised by it, so its weights sum to 1
+ * to within that lse's accuracy.  kl is [B][H_kv][n_q] fp32.  Supported for
+ * G in {4, 8, 16, 32}, bf16 index inputs and uniform batches (else
+ * MSA_ERR_UNSUPPORTED).  Needs workspace of msa_workspace_size(p,
+ * MSA_OP_INDEX_KL).  The training reduction (mean over rows, the loss weight)
+ * and the gradient are the caller's.
+ */
+msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q, const void* index_k,
+                        const int32_t* block_idx, const float* lse, float* kl, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 
 /*
  * Variable-length batches and paged caches (section 运行 Kernel: the kernels

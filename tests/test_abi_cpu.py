@@ -157,3 +157,17 @@ def test_fp8_index_problems_accepted():
         n = ctypes.c_size_t(0)
         assert msa.library().msa_workspace_size(ctypes.byref(p), msa.OP_FORWARD, ctypes.byref(n)) == msa.OK
         assert n.value == msa.workspace_size(prob(index_dim=d_idx), msa.OP_FORWARD)
+
+
+@pytest.mark.parametrize("kw", [dict(h_q=4, h_kv=2), dict(h_q=64, h_kv=1), dict(index_dtype=1),
+                                dict(h_q=12, h_kv=2)])
+def test_index_kl_unsupported_shapes(kw):
+    """The KL pass takes G in {4, 8, 16, 32} and bf16 index inputs."""
+    p = prob(**kw)
+    n = ctypes.c_size_t(0)
+    assert msa.library().msa_workspace_size(ctypes.byref(p), msa.OP_INDEX_KL, ctypes.byref(n)) == msa.ERR_UNSUPPORTED
+
+
+def test_index_kl_workspace_is_smaller_than_attention():
+    p = prob(h_q=8, h_kv=1)
+    assert 0 < msa.workspace_size(p, msa.OP_INDEX_KL) < msa.workspace_size(p, msa.OP_SPARSE_ATTN)
