@@ -125,7 +125,16 @@ def gpu_leg(w, steps, warmup, stream, paged=False, kl=False):
             run_kl()
         res["ms_kl"] = t.run(run_kl, steps)
         res["kl_mean"] = float(kl_out.mean().item())
-        del kl_out, kl_ws
+        # dense mode (the indexer warmup): dense attention, then the KL over every visible token
+        d_out = torch.empty_like(f["out"])
+        d_lse = torch.empty_like(f["lse"])
+        run_dense = lambda: msa.dense_attn_fwd(p, x["q"], x["k"], x["v"], d_out, d_lse, stream=sp)
+        run_dkl = lambda: msa.dense_index_kl(p, x["q"], x["k"], x["iq"], x["ik"], d_lse, kl_out, stream=sp)
+        run_dense()
+        run_dkl()
+        res["ms_dense_attn"] = t.run(run_dense, max(1, steps // 2))
+        res["ms_dense_kl"] = t.run(run_dkl, max(1, steps // 2))
+        del kl_out, kl_ws, d_out, d_lse
     if paged:
         # the same step through msa_forward_v, the caches re-laid as a shuffled page pool
         ref = {key: f[key].clone() for key in ("out", "block_idx", "lse")}
@@ -293,6 +302,19 @@ def main():
         line["kl"] = {"ms": round(g["ms_kl"], 4), "tflops": round(f_kl / (g["ms_kl"] * 1e-3) / 1e12, 1),
                       "frac_mfma": round(f_kl / (g["ms_kl"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                       "mean_kl": round(g["kl_mean"], 5)}
+        # dense mode: every visible token (sum over rows of p + 1)
+        import numpy as np
+        n_vis = float(np.sum(w.offset + np.arange(w.n_q, dtype=np.int64) + 1)) * w.batch
+        f_dense = 4.0 * w.head_dim * w.h_q * n_vis
+        f_dkl = 2.0 * (w.head_dim * w.h_q + w.index_dim * w.h_kv) * n_vis
+        line["dense"] = {
+            "attn_ms": round(g["ms_dense_attn"], 3),
+            "attn_tflops": round(f_dense / (g["ms_dense_attn"] * 1e-3) / 1e12, 1),
+            "attn_frac_mfma": round(f_dense / (g["ms_dense_attn"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kl_ms": round(g["ms_dense_kl"], 3),
+            "kl_tflops": round(f_dkl / (g["ms_dense_kl"] * 1e-3) / 1e12, 1),
+            "kl_frac_mfma": round(f_dkl / (g["ms_dense_kl"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "msa_speedup_over_dense": round(g["ms_dense_attn"] / g["ms_step"], 2)}
 
     if not args.no_paged:
         # the same steps with the caches in a shuffled page pool (msa_forward_v, uniform lengths)

@@ -7,7 +7,7 @@ import of a compute entry point raises; nothing falls back to another path.
 
 Entry points (same names as the C ABI, without the ``msa_`` prefix):
 ``index_scores``, ``block_topk``, ``sparse_attn_fwd``, ``forward``,
-``index_kl``, ``workspace_size``; ``Problem`` mirrors ``msa_problem``.  Each compute call
+``index_kl``, ``dense_attn_fwd``, ``dense_index_kl``, ``workspace_size``; ``Problem`` mirrors ``msa_problem``.  Each compute call
 takes an optional ``varlen`` (a ``Varlen``, mirroring ``msa_varlen``: per
 sequence query and cache lengths, packed query rows, a page table); given,
 the ``*_v`` variant of the C call is used.
@@ -27,7 +27,7 @@ DTYPE_BF16, DTYPE_FP8_E4M3 = range(2)  # msa_dtype: element type of index_q / in
 
 EXPORTS = ("msa_workspace_size", "msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
            "msa_index_scores_v", "msa_block_topk_v", "msa_sparse_attn_fwd_v", "msa_forward_v", "msa_index_kl",
-           "msa_status_string")
+           "msa_dense_attn_fwd", "msa_dense_index_kl", "msa_status_string")
 
 
 class Problem(ctypes.Structure):
@@ -105,6 +105,8 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.msa_sparse_attn_fwd_v.argtypes = [P, V, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_forward_v.argtypes = [P, V, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_index_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.msa_dense_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        lib.msa_dense_index_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         for name in EXPORTS[:-1]:
             getattr(lib, name).restype = ctypes.c_int
         lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -212,6 +214,22 @@ def index_kl(p: Problem, q, k, index_q, index_k, block_idx, lse, kl, workspace=N
     rc = L.msa_index_kl(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(index_q), _ptr(index_k), _ptr(block_idx), _ptr(lse),
                         _ptr(kl), _ptr(workspace), nb, st)
     _check(rc, "msa_index_kl")
+    return kl
+
+
+def dense_attn_fwd(p: Problem, q, k, v, out, lse=None, stream=None):
+    """Dense causal GQA attention (every visible key): the warmup's main branch."""
+    L, st = library(), _stream(stream, q)
+    _check(L.msa_dense_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), st),
+           "msa_dense_attn_fwd")
+    return out
+
+
+def dense_index_kl(p: Problem, q, k, index_q, index_k, lse, kl, stream=None):
+    """index_kl over every visible token, with the dense attention's lse."""
+    L, st = library(), _stream(stream, q)
+    _check(L.msa_dense_index_kl(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(index_q), _ptr(index_k), _ptr(lse), _ptr(kl),
+                                st), "msa_dense_index_kl")
     return kl
 
 

@@ -272,6 +272,34 @@ msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, cons
                                          block_idx, lse, kl, ws, reinterpret_cast<float4*>(base + plan), D, stream));
 }
 
+msa_status msa_dense_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v, void* out, float* lse,
+                              hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !out) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)))
+    return MSA_ERR_INVALID_ARGUMENT;
+  return hip_status(msa::launch_dense_attn(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, D,
+                                           stream));
+}
+
+msa_status msa_dense_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q,
+                              const void* index_k, const float* lse, float* kl, hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !index_q || !index_k || !lse || !kl) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(index_q) || !aligned16(index_k) || !aligned16(lse) ||
+      !aligned16(kl))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (!msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
+  return hip_status(msa::launch_dense_index_kl(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                               static_cast<const uint16_t*>(index_q),
+                                               static_cast<const uint16_t*>(index_k), lse, kl, D, stream));
+}
+
 msa_status msa_index_scores(const msa_problem* p, const void* index_q, const void* index_k, float* pooled,
                             hipStream_t stream) {
   return msa_index_scores_v(p, nullptr, index_q, index_k, pooled, stream);

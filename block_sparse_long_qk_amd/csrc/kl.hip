@@ -182,9 +182,9 @@ __device__ __forceinline__ void teacher_probs(const f32x16 (&s)[4], const float 
   }
 }
 
-// Fold a tile's student scores into the partials of the lane-local positions
-// and sum them over the block's 128 keys (the 32 lanes of each half): every
-// lane of a half ends with its positions' sums.
+// Fold a block's teacher probabilities and student scores into this lane's
+// sums for its lane-local positions (its keys only; lanes_reduce adds the
+// lanes).
 template <int G, bool MASKED>
 __device__ __forceinline__ void student_fold(const f32x16 (&z)[4], const float (&P)[4][PosMap<G>::NPL],
                                              const int64_t (&ppos)[PosMap<G>::NPL], int64_t key0, int lane,
@@ -209,12 +209,22 @@ __device__ __forceinline__ void student_fold(const f32x16 (&z)[4], const float (
       x.b += p * zz;
       if (vis) x.l += __builtin_amdgcn_exp2f(zz * kLog2e - x.m);
     }
+    acc[j] = kl_combine(acc[j], x);
+  }
+}
+
+// Sums over the 32 lanes of each half (the keys of a block): every lane of a
+// half ends with its positions' totals.
+template <int G>
+__device__ __forceinline__ void lanes_reduce(KlAcc (&acc)[PosMap<G>::NPL]) {
+#pragma unroll
+  for (int j = 0; j < PosMap<G>::NPL; ++j) {
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
-      KlAcc y{__shfl_xor(x.a, o, 64), __shfl_xor(x.b, o, 64), __shfl_xor(x.m, o, 64), __shfl_xor(x.l, o, 64)};
-      x = kl_combine(x, y);
+      KlAcc y{__shfl_xor(acc[j].a, o, 64), __shfl_xor(acc[j].b, o, 64), __shfl_xor(acc[j].m, o, 64),
+              __shfl_xor(acc[j].l, o, 64)};
+      acc[j] = kl_combine(acc[j], y);
     }
-    acc[j] = x;
   }
 }
 
@@ -298,11 +308,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       teacher_probs<G, LOCAL>(sc, lse2, rowok, ppos, (int64_t)cur.t * kBk, lane, c, P);
     }
     KlAcc acc[PM::NPL];
+#pragma unroll
+    for (int j = 0; j < PM::NPL; ++j) acc[j] = KlAcc{0.f, 0.f, -__builtin_huge_valf(), 0.f};
     {
       f32x16 zz[4];
       iq_ik_scores<DIDX, G>(IKs, iqw, lane, zz);
       student_fold<G, LOCAL>(zz, P, ppos, (int64_t)cur.t * kBk, lane, acc);
     }
+    lanes_reduce<G>(acc);
     // the lane of each position's first head row writes its partial
 #pragma unroll
     for (int j = 0; j < PM::NPL; ++j) {
@@ -335,6 +348,158 @@ __global__ __launch_bounds__(256) void k_kl_merge(const int32_t* __restrict__ bl
     acc = kl_combine(acc, KlAcc{x.x, x.y, x.z, x.w});
   }
   kl[row] = acc.a * kLn2 - acc.b + (acc.m + __log2f(acc.l)) * kLn2;
+}
+
+// ---------------------------------------------------------------- dense mode
+// The KL value over every visible token (the indexer warmup, where both
+// branches run full attention: page "MiniMax 发布 MSA…", section MSA 如何训练),
+// with lse from the dense attention.  Query-outer like the dense attention:
+// a workgroup owns pt aligned positions of one (sequence, group) and streams
+// blocks 0 .. its own; K and the index keys of block t+1 are loaded into
+// registers while block t is computed.  Each lane sums over its keys across
+// all blocks; one reduction over the lanes at the end gives the row's value,
+// so there are no partials.
+template <int DIDX>
+struct KIkRegs {  // native vectors: whole-register copies, so the struct stays in registers
+  u32x4 kr[2048 / kThreads];
+  u32x4 ir[kBk * (DIDX / 8) / kThreads];
+};
+
+template <int DIDX>
+__device__ __forceinline__ void k_ik_load(KIkRegs<DIDX>& x, const uint16_t* __restrict__ kb,
+                                          const uint16_t* __restrict__ ikb, int n_valid) {
+  constexpr int CPI = DIDX / 8;
+  constexpr int KPER = 2048 / kThreads, IPER = kBk * CPI / kThreads;
+  const int tid = threadIdx.x;
+  const char* kbase = reinterpret_cast<const char*>(kb);
+  const char* ibase = reinterpret_cast<const char*>(ikb);
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    const int c = tid + kThreads * u;
+    x.kr[u] = *reinterpret_cast<const u32x4*>(kbase + (uint32_t)min(c >> 4, n_valid - 1) * 256u + 16u * (c & 15));
+  }
+#pragma unroll
+  for (int u = 0; u < IPER; ++u) {
+    const int c = tid + kThreads * u;
+    x.ir[u] = *reinterpret_cast<const u32x4*>(ibase + (uint32_t)min(c / CPI, n_valid - 1) * (2u * DIDX) +
+                                              16u * (c % CPI));
+  }
+}
+
+template <int DIDX>
+__device__ __forceinline__ void k_ik_store(uint16_t* Ks, uint16_t* IKs, const KIkRegs<DIDX>& x) {
+  constexpr int IKP = DIDX + 8;
+  constexpr int CPI = DIDX / 8;
+  constexpr int KPER = 2048 / kThreads, IPER = kBk * CPI / kThreads;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    const int c = tid + kThreads * u;
+    *reinterpret_cast<u32x4*>(Ks + (c >> 4) * KP + (c & 15) * 8) = x.kr[u];
+  }
+#pragma unroll
+  for (int u = 0; u < IPER; ++u) {
+    const int c = tid + kThreads * u;
+    *reinterpret_cast<u32x4*>(IKs + (c / CPI) * IKP + (c % CPI) * 8) = x.ir[u];
+  }
+}
+
+template <int DIDX, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_kl_dense(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ iq,
+    const uint16_t* __restrict__ ik, const float* __restrict__ lse, float* __restrict__ kl, Dims D) {
+  using PM = PosMap<G>;
+  constexpr int IKP = DIDX + 8;
+  __shared__ __align__(16) uint16_t Ks[kBk * KP];
+  __shared__ __align__(16) uint16_t IKs[kBk * IKP];
+  __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];
+  __shared__ __align__(16) unsigned char IQs[kWaves][kIqRows * 2 * DIDX];
+
+  const int nbg = D.B * D.h_kv;
+  const int n_t = (int)((D.offset + D.n_q - 1) / D.pt - D.offset / D.pt + 1);
+  const int bg = blockIdx.x % nbg;
+  const int tile = n_t - 1 - (int)(blockIdx.x / nbg);   // heaviest first
+  const int b = bg / D.h_kv, g = bg % D.h_kv;
+  const int p0 = (int)((D.offset / D.pt + tile) * D.pt);
+  const int t_last = p0 / kBk;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int r = wave * 32 + col;
+  const int ps = r / G, hh = r % G;
+  const int pos = p0 + ps;
+  const bool valid = ps < D.pt && pos >= D.offset && pos < D.offset + D.n_q;
+  const int i = valid ? (int)(pos - D.offset) : 0;
+  unsigned char* qw = Qs[wave];
+  unsigned char* iqw = IQs[wave];
+  const float c = D.scale_log2;
+
+  fetch_q_rows(qw, q + (((int64_t)b * D.n_q + i) * D.h_q + g * G + hh) * kHeadDim, lane);
+  fetch_iq_rows<DIDX, G>(iqw, iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX, lane);
+  const float lse_mine = lse[((int64_t)b * D.h_q + g * G + hh) * D.n_q + i] * kLog2e;
+  float lse2[16];
+  bool rowok[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int re = 8 * (e >> 2) + 4 * half + (e & 3);
+    lse2[e] = __shfl(lse_mine, re, 64);
+    rowok[e] = __shfl((int)valid, re, 64) != 0;
+  }
+  int64_t ppos[PM::NPL];
+  int pi[PM::NPL], pv[PM::NPL];
+#pragma unroll
+  for (int j = 0; j < PM::NPL; ++j) {
+    const int src = PM::wpos(j, half) * G;
+    pi[j] = __shfl(i, src, 64);
+    pv[j] = __shfl((int)valid, src, 64);
+    ppos[j] = pv[j] ? D.offset + pi[j] : -1;
+  }
+
+  const uint16_t* kg = k + ((int64_t)b * D.h_kv + g) * D.n_kv * kHeadDim;
+  const uint16_t* ikg = ik + (int64_t)b * D.n_kv * DIDX;
+  auto n_valid = [&](int t) { return max(1, min(kBk, D.n_kv - t * kBk)); };
+  {
+    KIkRegs<DIDX> x;
+    k_ik_load<DIDX>(x, kg, ikg, n_valid(0));
+    k_ik_store<DIDX>(Ks, IKs, x);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's query and index-query rows have landed
+    __syncthreads();
+  }
+  KlAcc acc[PM::NPL];
+#pragma unroll
+  for (int j = 0; j < PM::NPL; ++j) acc[j] = KlAcc{0.f, 0.f, -__builtin_huge_valf(), 0.f};
+  for (int t = 0; t <= t_last; ++t) {
+    const bool more = t < t_last;
+    KIkRegs<DIDX> x;
+    if (more)
+      k_ik_load<DIDX>(x, kg + (int64_t)(t + 1) * kBk * kHeadDim, ikg + (int64_t)(t + 1) * kBk * DIDX, n_valid(t + 1));
+    const int64_t key0 = (int64_t)t * kBk;
+    float P[4][PM::NPL];
+    {
+      f32x16 sc[4];
+      q_k_scores(Ks, qw, lane, sc);
+      if (t == t_last) teacher_probs<G, true>(sc, lse2, rowok, ppos, key0, lane, c, P);
+      else teacher_probs<G, false>(sc, lse2, rowok, ppos, key0, lane, c, P);
+    }
+    {
+      f32x16 zz[4];
+      iq_ik_scores<DIDX, G>(IKs, iqw, lane, zz);
+      if (t == t_last) student_fold<G, true>(zz, P, ppos, key0, lane, acc);
+      else student_fold<G, false>(zz, P, ppos, key0, lane, acc);
+    }
+    __syncthreads();  // every wave is done with block t
+    if (more) {
+      k_ik_store<DIDX>(Ks, IKs, x);
+      __syncthreads();
+    }
+  }
+  lanes_reduce<G>(acc);
+#pragma unroll
+  for (int j = 0; j < PM::NPL; ++j) {
+    const bool writer = col == PM::wpos(j, half) * G && (G == 4 || half == 0);
+    if (writer && pv[j])
+      kl[(int64_t)bg * D.n_q + pi[j]] = acc[j].a * kLn2 - acc[j].b + (acc[j].m + __log2f(acc[j].l)) * kLn2;
+  }
 }
 
 }  // namespace
@@ -370,6 +535,27 @@ hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t*
   const int64_t rows = (int64_t)D.B * D.h_kv * D.n_q;
   hipLaunchKernelGGL(k_kl_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, block_idx, kl_part, kl,
                      D);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q,
+                                 const uint16_t* index_k, const float* lse, float* kl, const Dims& D,
+                                 hipStream_t stream) {
+  const int64_t n_t = (D.offset + D.n_q - 1) / D.pt - D.offset / D.pt + 1;
+  const dim3 grid((unsigned)((int64_t)D.B * D.h_kv * n_t)), block(kThreads);
+  auto go = [&](auto didx, auto g) {
+    constexpr int DI = decltype(didx)::value, GG = decltype(g)::value;
+    hipLaunchKernelGGL((k_kl_dense<DI, GG>), grid, block, 0, stream, q, k, index_q, index_k, lse, kl, D);
+  };
+  auto by_g = [&](auto didx) {
+    switch (D.G) {
+      case 4: go(didx, std::integral_constant<int, 4>{}); break;
+      case 8: go(didx, std::integral_constant<int, 8>{}); break;
+      case 16: go(didx, std::integral_constant<int, 16>{}); break;
+      default: go(didx, std::integral_constant<int, 32>{}); break;
+    }
+  };
+  if (D.d_idx == 128) by_g(std::integral_constant<int, 128>{}); else by_g(std::integral_constant<int, 64>{});
   return hipGetLastError();
 }
 

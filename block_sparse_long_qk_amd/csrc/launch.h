@@ -41,6 +41,14 @@ hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int32_t* block_idx, const float* lse, float* kl, const AttnWs& ws, float4* kl_part,
                            const Dims& D, hipStream_t stream);
 
+// Dense mode (the indexer warmup): causal GQA attention over every visible
+// token, and the KL value over every visible token (needs the dense lse).
+hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, float* lse,
+                             const Dims& D, hipStream_t stream);
+hipError_t launch_dense_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q,
+                                 const uint16_t* index_k, const float* lse, float* kl, const Dims& D,
+                                 hipStream_t stream);
+
 // Decode-shaped calls (few query rows per sequence).
 bool use_index_small(const Dims& D);   // at most 16 (query, group) rows per sequence
 bool use_attn_rows(const Dims& D);     // query-outer attention

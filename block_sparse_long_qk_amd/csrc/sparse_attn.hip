@@ -31,88 +31,6 @@
 namespace msa {
 namespace {
 
-constexpr int VP = kBk + 4;        // LDS pitch of V^T rows (bf16): 8-byte pad
-
-// Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS
-// with the workgroup's kThreads threads.  Keys at or past n_valid (n_valid >= 1)
-// repeat key n_valid - 1: finite data that the causal mask drops, so the block
-// needs no zero fill.  All loads are issued before the first LDS write.
-__device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint16_t* __restrict__ kb,
-                                         const uint16_t* __restrict__ vb, int n_valid) {
-  constexpr int KPER = 2048 / kThreads, VPER = 512 / kThreads;  // 16-byte K chunks, 4-key V units
-  const int tid = threadIdx.x;
-  uint4 kr[KPER], vr[4 * VPER];
-#pragma unroll
-  for (int u = 0; u < KPER; ++u) {
-    const int c = tid + kThreads * u;
-    const int key = min(c >> 4, n_valid - 1), oc = c & 15;
-    kr[u] = *reinterpret_cast<const uint4*>(kb + key * kHeadDim + oc * 8);
-  }
-#pragma unroll
-  for (int u = 0; u < VPER; ++u) {
-    const int c = tid + kThreads * u;
-    const int kq = c >> 4, od = c & 15;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      vr[4 * u + q] = *reinterpret_cast<const uint4*>(vb + min(kq * 4 + q, n_valid - 1) * kHeadDim + od * 8);
-  }
-#pragma unroll
-  for (int u = 0; u < KPER; ++u) {
-    const int c = tid + kThreads * u;
-    *reinterpret_cast<uint4*>(Ks + (c >> 4) * KP + (c & 15) * 8) = kr[u];
-  }
-#pragma unroll
-  for (int u = 0; u < VPER; ++u) {  // written transposed: Vt[d][key]
-    const int c = tid + kThreads * u;
-    const int kq = c >> 4, od = c & 15;
-    const uint32_t* w[4] = {reinterpret_cast<const uint32_t*>(&vr[4 * u + 0]), reinterpret_cast<const uint32_t*>(&vr[4 * u + 1]),
-                            reinterpret_cast<const uint32_t*>(&vr[4 * u + 2]), reinterpret_cast<const uint32_t*>(&vr[4 * u + 3])};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16;
-      const uint32_t v0 = (w[0][e >> 1] >> sh) & 0xFFFFu, v1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
-      const uint32_t v2 = (w[2][e >> 1] >> sh) & 0xFFFFu, v3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
-      *reinterpret_cast<uint2*>(Vt + (od * 8 + e) * VP + kq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
-    }
-  }
-}
-
-// S^T = K Q^T for one wave: the 128 keys of the staged block (4 row tiles of
-// 32) against the wave's 32 query rows (from its LDS region), raw dot
-// products.  k-steps outer, so the four accumulator chains interleave; the
-// operands of k-step ks+1 are read from LDS while the MFMAs of k-step ks run.
-__device__ __forceinline__ void qk_block(const uint16_t* Ks, const unsigned char* qw, int lane, f32x16 (&s)[4]) {
-  const int col = lane & 31, half = lane >> 5;
-  const uint16_t* kbase = Ks + col * KP + 8 * half;
-  const unsigned char* qbase = qw + col * 256;
-  const int qsw = col & 15;
-  uint4 kf[2][4], qf[2];
-#pragma unroll
-  for (int T = 0; T < 4; ++T) kf[0][T] = *reinterpret_cast<const uint4*>(kbase + 32 * T * KP);
-  qf[0] = *reinterpret_cast<const uint4*>(qbase + 16 * (half ^ qsw));
-#pragma unroll
-  for (int T = 0; T < 4; ++T) s[T] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const int cb = ks & 1, nb = cb ^ 1;
-    if (ks + 1 < 8) {
-#pragma unroll
-      for (int T = 0; T < 4; ++T) kf[nb][T] = *reinterpret_cast<const uint4*>(kbase + 32 * T * KP + 16 * (ks + 1));
-      qf[nb] = *reinterpret_cast<const uint4*>(qbase + 16 * ((2 * (ks + 1) + half) ^ qsw));
-    }
-#pragma unroll
-    for (int T = 0; T < 4; ++T) s[T] = mfma_32x32x16(kf[cb][T], qf[cb], s[T]);
-  }
-  // issue order: the first operands, then per k-step the next operands ahead
-  // of that step's four MFMAs
-  __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-#pragma unroll
-  for (int ks = 0; ks < 7; ++ks) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-}
 
 // Softmax of one wave's raw scores (in place) and the unnormalised
 // O^T = V^T P^T.  Returns the row max m2 and sum l in base-2 units

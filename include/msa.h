@@ -181,6 +181,26 @@ msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, cons
                         hipStream_t stream);
 
 /*
+ * Dense mode: both branches over every visible token, as during the indexer
+ * warmup (section MSA 如何训练: in the first iterations both branches run full
+ * attention, so that the indexer learns from the KL loss before it routes).
+ *
+ * msa_dense_attn_fwd: causal GQA attention, out[b][i][h] = sum_{j <= p_i}
+ * softmax_j(scale * q . k[b][g][j]) v[b][g][j], with lse (nullable) the natural
+ * log-sum-exp; layouts as for msa_sparse_attn_fwd.  No workspace.
+ *
+ * msa_dense_index_kl: the KL value of msa_index_kl with T = { j <= p_i }; lse
+ * is msa_dense_attn_fwd's.  Same support as msa_index_kl (G in {4, 8, 16,
+ * 32}, bf16 index inputs).  No workspace.
+ *
+ * Both take uniform batches (no msa_varlen form).
+ */
+msa_status msa_dense_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v, void* out, float* lse,
+                              hipStream_t stream);
+msa_status msa_dense_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q,
+                              const void* index_k, const float* lse, float* kl, hipStream_t stream);
+
+/*
  * Variable-length batches and paged caches (section 运行 Kernel: the kernels
  * take per-sequence query and cache lengths and K/V held in pages of
  * block_size tokens addressed through a page table).  All pointers are device
