@@ -53,8 +53,10 @@ def _L():
         lib.oracle_pool_f8.argtypes = [_u8p, _i64, _i64p, _u8p, _i64, _i32, _i32, _f64p, _i64]
         lib.oracle_kl.argtypes = [_u16p, _i64, _i64p, _i32p, _i32, _i32, _u16p, _i64, _i32, _u16p, _u16p, _i32, _i32,
                                   _f64, _f64p]
+        lib.oracle_attend_bwd.argtypes = [_u16p, _i64, _i64p, _i32p, _i32, _i32, _u16p, _u16p, _i64, _i32, _i32,
+                                          _f64, _u16p, _f64p, _f64p, _f64p]
         for f in (lib.oracle_pool, lib.oracle_select, lib.oracle_attend, lib.oracle_dense_gqa, lib.oracle_merge,
-                  lib.oracle_e4m3_decode, lib.oracle_pool_f8, lib.oracle_kl):
+                  lib.oracle_e4m3_decode, lib.oracle_pool_f8, lib.oracle_kl, lib.oracle_attend_bwd):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -126,6 +128,21 @@ def attend(q_rows, pos, sel, K, V, bk: int, scale: float):
     _check(_L().oracle_attend(q_rows, n, pos, sel, sel.shape[1], G, K, V, K.shape[0], d, bk, scale, out, lse),
            "oracle_attend")
     return out, lse
+
+
+def attend_bwd(q_rows, pos, sel, K, V, bk: int, scale: float, dO_rows):
+    """Gradient of attend(): returns (dQ [n, G, d], dK [n_kv, d], dV [n_kv, d]),
+    dK and dV summed over every row and head passed."""
+    q_rows, K, V, dO_rows = _u16(q_rows), _u16(K), _u16(V), _u16(dO_rows)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    n, G, d = q_rows.shape
+    dQ = np.zeros((n, G, d))
+    dK = np.zeros((K.shape[0], d))
+    dV = np.zeros((K.shape[0], d))
+    _check(_L().oracle_attend_bwd(q_rows, n, pos, sel, sel.shape[1], G, K, V, K.shape[0], d, bk, scale, dO_rows, dQ,
+                                  dK, dV), "oracle_attend_bwd")
+    return dQ, dK, dV
 
 
 def kl(q_rows, pos, sel, K, iq_rows, ik, bk: int, scale: float) -> np.ndarray:

@@ -323,6 +323,84 @@ int oracle_kl(const uint16_t* q, int64_t nrows, const int64_t* pos, const int32_
 }
 
 /*
+ * Gradient of the Main Branch (the backward pass of oracle_attend), from the
+ * definition of softmax attention over the row's token set T:
+ *   P_hj = softmax_j(scale q_h . k_j),  o_h = sum_j P_hj v_j,
+ *   given dO_h:  dv_j += P_hj dO_h,
+ *                dP_hj = dO_h . v_j,  dS_hj = P_hj (dP_hj - dO_h . o_h),
+ *                dq_h  = scale sum_j dS_hj k_j,   dk_j += scale dS_hj q_h.
+ *   q, dO [nrows][G][d]; pos, sel [nrows][k] as in oracle_attend;
+ *   K, V [n_kv][d] -> dQ [nrows][G][d]; dK, dV [n_kv][d] accumulated over every
+ *   row and head of the call (the caller zeroes them).  Rows run one after the
+ *   other (dK, dV are shared).
+ */
+int oracle_attend_bwd(const uint16_t* q, int64_t nrows, const int64_t* pos, const int32_t* sel, int32_t k,
+                      int32_t G, const uint16_t* K, const uint16_t* V, int64_t n_kv, int32_t d, int32_t bk,
+                      double scale, const uint16_t* dO, double* dQ, double* dK, double* dV) {
+  if (nrows < 0 || k < 1 || G < 1 || d <= 0 || bk <= 0) return -1;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (pos[r] < 0 || pos[r] >= n_kv) return -1;
+  const int64_t n_blk = (n_kv + bk - 1) / bk;
+  int32_t* blocks = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)k * (size_t)bk);
+  double* P = (double*)malloc(sizeof(double) * (size_t)k * (size_t)bk);
+  double* o = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t p = pos[r];
+    memcpy(blocks, sel + r * k, sizeof(int32_t) * (size_t)k);
+    qsort(blocks, (size_t)k, sizeof(int32_t), int_order);
+    int64_t nt = 0;
+    for (int32_t s = 0; s < k; ++s) {
+      const int32_t t = blocks[s];
+      if (t < 0 || t >= n_blk || (s > 0 && t == blocks[s - 1])) continue;
+      for (int64_t j = (int64_t)t * bk; j < ((int64_t)t + 1) * bk && j < n_kv && j <= p; ++j) tok[nt++] = j;
+    }
+    for (int32_t h = 0; h < G; ++h) {
+      const uint16_t* qh = q + (r * G + h) * d;
+      const uint16_t* gh = dO + (r * G + h) * d;
+      double* dqh = dQ + (r * G + h) * d;
+      /* probabilities and the output of this head */
+      double m = -INFINITY;
+      for (int64_t a = 0; a < nt; ++a) {
+        double dot = 0.0;
+        for (int32_t c = 0; c < d; ++c) dot += bf(qh[c]) * bf(K[tok[a] * d + c]);
+        P[a] = scale * dot;
+        if (P[a] > m) m = P[a];
+      }
+      double l = 0.0;
+      for (int64_t a = 0; a < nt; ++a) {
+        P[a] = exp(P[a] - m);
+        l += P[a];
+      }
+      for (int32_t c = 0; c < d; ++c) o[c] = 0.0;
+      for (int64_t a = 0; a < nt; ++a) {
+        P[a] /= l;
+        for (int32_t c = 0; c < d; ++c) o[c] += P[a] * bf(V[tok[a] * d + c]);
+      }
+      double delta = 0.0; /* dO_h . o_h */
+      for (int32_t c = 0; c < d; ++c) delta += bf(gh[c]) * o[c];
+      for (int32_t c = 0; c < d; ++c) dqh[c] = 0.0;
+      for (int64_t a = 0; a < nt; ++a) {
+        const int64_t j = tok[a];
+        double dp = 0.0;
+        for (int32_t c = 0; c < d; ++c) dp += bf(gh[c]) * bf(V[j * d + c]);
+        const double ds = P[a] * (dp - delta);
+        for (int32_t c = 0; c < d; ++c) {
+          dV[j * d + c] += P[a] * bf(gh[c]);
+          dqh[c] += scale * ds * bf(K[j * d + c]);
+          dK[j * d + c] += scale * ds * bf(qh[c]);
+        }
+      }
+    }
+  }
+  free(o);
+  free(P);
+  free(tok);
+  free(blocks);
+  return 0;
+}
+
+/*
  * Dense causal GQA softmax attention (every key j <= p), written separately
  * from oracle_attend; with k*Bk >= n_kv the sparse result must equal it.
  */
