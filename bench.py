@@ -135,6 +135,16 @@ def gpu_leg(w, steps, warmup, stream, paged=False, kl=False):
         res["ms_dense_attn"] = t.run(run_dense, max(1, steps // 2))
         res["ms_dense_kl"] = t.run(run_dkl, max(1, steps // 2))
         del kl_out, kl_ws, d_out, d_lse
+        # the main-branch backward on this step's selection, out and lse
+        dout = synth.device_dout(w)
+        dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+        b_ws = torch.empty(max(msa.workspace_size(p, msa.OP_SPARSE_ATTN_BWD), 256), dtype=torch.uint8, device="cuda")
+        run_bwd = lambda: msa.sparse_attn_bwd(p, x["q"], x["k"], x["v"], f["block_idx"], f["out"], f["lse"], dout, dq,
+                                              dk, dv, b_ws, stream=sp)
+        for _ in range(warmup):
+            run_bwd()
+        res["ms_bwd"] = t.run(run_bwd, steps)
+        del dout, dq, dk, dv, b_ws
     if paged:
         # the same step through msa_forward_v, the caches re-laid as a shuffled page pool
         ref = {key: f[key].clone() for key in ("out", "block_idx", "lse")}
@@ -307,6 +317,10 @@ def main():
         n_vis = float(np.sum(w.offset + np.arange(w.n_q, dtype=np.int64) + 1)) * w.batch
         f_dense = 4.0 * w.head_dim * w.h_q * n_vis
         f_dkl = 2.0 * (w.head_dim * w.h_q + w.index_dim * w.h_kv) * n_vis
+        # backward: S recomputed, dP, dV, dK, dQ over each row's tokens (five products)
+        f_bwd = 2.5 * f_attn
+        line["backward"] = {"ms": round(g["ms_bwd"], 4), "tflops": round(f_bwd / (g["ms_bwd"] * 1e-3) / 1e12, 1),
+                            "frac_mfma": round(f_bwd / (g["ms_bwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         line["dense"] = {
             "attn_ms": round(g["ms_dense_attn"], 3),
             "attn_tflops": round(f_dense / (g["ms_dense_attn"] * 1e-3) / 1e12, 1),

@@ -159,6 +159,16 @@ size_t pooled_bytes(const Dims& D) { return round256(sizeof(float) * (size_t)D.B
 size_t kl_part_bytes(const Dims& D) { return round256(sizeof(float) * 4 * (size_t)D.B * D.h_kv * D.n_q * (D.k + 1)); }
 size_t kl_bytes(const Dims& D) { return attn_ws_layout(D, nullptr, nullptr, false) + kl_part_bytes(D); }
 
+// The backward pass: the plan, one bf16 dQ partial per (row, slot, head), the
+// per-(row, head) dO . O.
+size_t bwd_part_bytes(const Dims& D) {
+  return round256(sizeof(uint16_t) * (size_t)D.B * D.h_kv * D.n_q * (D.k + 1) * D.G * msa::kHeadDim);
+}
+size_t bwd_delta_bytes(const Dims& D) { return round256(sizeof(float) * (size_t)D.B * D.h_q * D.n_q); }
+size_t bwd_bytes(const Dims& D) {
+  return attn_ws_layout(D, nullptr, nullptr, false) + bwd_part_bytes(D) + bwd_delta_bytes(D);
+}
+
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
 }  // namespace
@@ -182,6 +192,10 @@ msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
     case MSA_OP_FORWARD:
       if (!attn_path_ok(D)) return MSA_ERR_UNSUPPORTED;
       *bytes = pooled_bytes(D) + attn_bytes(D);
+      return MSA_OK;
+    case MSA_OP_SPARSE_ATTN_BWD:
+      if (D.n_blk > msa::kMaxPlanBlocks) return MSA_ERR_UNSUPPORTED;
+      *bytes = bwd_bytes(D);
       return MSA_OK;
     case MSA_OP_INDEX_KL:
       if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
@@ -270,6 +284,31 @@ msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, cons
   return hip_status(msa::launch_index_kl(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                          static_cast<const uint16_t*>(index_q), static_cast<const uint16_t*>(index_k),
                                          block_idx, lse, kl, ws, reinterpret_cast<float4*>(base + plan), D, stream));
+}
+
+msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, const void* out, const float* lse, const void* dout, void* dq,
+                               void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !block_idx || !out || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(out) ||
+      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(workspace))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (D.n_blk > msa::kMaxPlanBlocks) return MSA_ERR_UNSUPPORTED;
+  if (bwd_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  AttnWs ws;
+  char* base = static_cast<char*>(workspace);
+  const size_t plan = attn_ws_layout(D, base, &ws, false);
+  auto part = reinterpret_cast<uint16_t*>(base + plan);
+  auto delta = reinterpret_cast<float*>(base + plan + bwd_part_bytes(D));
+  return hip_status(msa::launch_sparse_attn_bwd(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), block_idx,
+      static_cast<const uint16_t*>(out), lse, static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dq),
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), ws, part, delta, D, stream));
 }
 
 msa_status msa_dense_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v, void* out, float* lse,

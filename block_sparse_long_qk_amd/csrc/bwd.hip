@@ -1,0 +1,390 @@
+// Main Branch backward: dQ, dK, dV of the sparse attention over the selected
+// blocks (the gradient that training needs; page "MiniMax 发布 MSA 稀疏注意力方法，
+// 开源推理内核并推出 MiniMax-M3 模型", section MSA 如何训练: the language-model loss
+// trains the Main Branch, which attends only over the selected blocks).
+//
+// Per row (query position i, head h) over its token set T:
+//   P_j = exp(scale q . k_j - lse),  D = dO . o,
+//   dS_j = P_j (dO . v_j - D),  dq = scale sum_j dS_j k_j,
+//   dk_j += scale dS_j q,  dv_j += P_j dO.
+//
+// KV-outer and owner-computes: one workgroup per (sequence, group, block) owns
+// that block's dK and dV and walks every row that attends it - the gathered
+// rows of the forward's plan (one bin per query group) and the block's own
+// positions (masked) - in chunks of 32 rows.  Wave w owns keys 16w .. 16w+15:
+// their K and V fragments stay in registers and their dK^T, dV^T accumulate in
+// registers over all chunks, so each block is written once, without atomics.
+// Per chunk, on 16x16x32 bf16 MFMA (lane l: column l % 16, k-group l / 16):
+//   S = Q K_w^T and dP = dO V_w^T with the rows as M: lane (key n, group c)
+//   holds rows {4c..4c+3} and {16+4c..16+4c+3}, which is exactly the k-group c
+//   that a 32-row contraction reads, so P and dS serve as B operands as they are;
+//   dV^T += dO^T P and dK^T += Q^T dS take dO^T and Q^T from transposed copies
+//   of the chunk in LDS;
+//   dQ^T = K^T dS^T needs every wave's dS: it goes through LDS once, and wave w
+//   forms head dims 16w .. 16w+15 of the chunk's dQ from the staged K^T.
+// dQ leaves as one bf16 partial per (row, slot); a merge adds a row's slots.
+#include "attn_tiles.h"
+
+namespace msa {
+namespace {
+
+typedef __bf16 bf16x8b __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8b, a), __builtin_bit_cast(bf16x8b, b), c,
+                                                 0, 0, 0);
+}
+
+constexpr int kBwdWaves = 8;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kTP = 32 + 4;        // pitch (bf16) of the transposed chunk copies [d][32 rows]
+constexpr int kKtP = kBk + 8;      // pitch (bf16) of K^T [d][128 keys]
+
+// D[b][h][i] = dO . O for every (row, head): one wave per 8 (row, head) pairs.
+__global__ __launch_bounds__(256) void k_bwd_delta(const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout,
+                                                   float* __restrict__ delta, Dims D) {
+  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 8;  // (b, i, h) in out's order
+  const int part = threadIdx.x & 7;                                   // 16 head dims each
+  if (pair >= (int64_t)D.B * D.n_q * D.h_q) return;
+  const uint16_t* o = out + pair * kHeadDim + part * 16;
+  const uint16_t* g = dout + pair * kHeadDim + part * 16;
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + 8 * u);
+    const uint4 b = *reinterpret_cast<const uint4*>(g + 8 * u);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc += __uint_as_float(aw[w] << 16) * __uint_as_float(bw[w] << 16);
+      acc += __uint_as_float(aw[w] & 0xFFFF0000u) * __uint_as_float(bw[w] & 0xFFFF0000u);
+    }
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 4, 64);
+  if (part == 0) {
+    const int h = (int)(pair % D.h_q);
+    const int64_t bi = pair / D.h_q;
+    const int i = (int)(bi % D.n_q), b = (int)(bi / D.n_q);
+    delta[((int64_t)b * D.h_q + h) * D.n_q + i] = acc;
+  }
+}
+
+// The rows of one source (a bin of the plan, or the block's own positions):
+// chunk row r (0..31) of chunk ch is flattened row 32 ch + r = entry * G + head.
+struct Src {
+  int kind;        // 0: plan bin, 1: the block's own positions
+  int tile0, n_entries;  // bin: first tile, entries (tiles * pt); own: -, positions
+  int pos0;        // own: first position
+};
+
+// Position, slot and validity of flattened entry e of a source.
+__device__ __forceinline__ void src_entry(const Src& sc, const AttnWs& ws, const Dims& D, int e, int& i, int& s,
+                                          bool& ok) {
+  if (sc.kind == 0) {
+    const int2 x = ws.list[(int64_t)sc.tile0 * D.pt + min(e, sc.n_entries - 1)];  // stays inside the bin's tiles
+    ok = e < sc.n_entries && x.x >= 0;
+    i = ok ? x.x / D.k : 0;
+    s = ok ? x.x % D.k : 0;
+  } else {
+    ok = e < sc.n_entries;
+    i = ok ? (int)(sc.pos0 + e - D.offset) : 0;
+    s = D.k;
+  }
+}
+
+// Fetch 32 rows (row r: 256 bytes at r * 256, chunk c in slot c ^ (r % 16)) by
+// direct global-to-LDS loads: wave w issues the 1-KB instruction for rows
+// 4w .. 4w+3; `rowp` is the row this lane's instruction row takes.
+__device__ __forceinline__ void fetch_rows32(unsigned char* dst, const uint16_t* rowp, int wave, int lane) {
+  const int r = 4 * wave + (lane >> 4);
+  const int c = (lane & 15) ^ (r & 15);
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(rowp + 8 * c),
+                                   (__attribute__((address_space(3))) void*)(dst + 1024 * wave), 16, 0, 0);
+}
+
+template <bool VL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_kv(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta, AttnWs ws,
+    uint16_t* __restrict__ dq_part, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, Dims D) {
+  __shared__ __align__(16) uint16_t Kt[kHeadDim * kKtP];          // K^T of the block
+  __shared__ __align__(16) unsigned char Qs[32 * 256], Os[32 * 256];  // chunk rows of Q and dO (swizzled)
+  __shared__ __align__(16) uint16_t Qt[kHeadDim * kTP], Ot[kHeadDim * kTP];  // their transposes [d][row]
+  __shared__ __align__(16) unsigned char Ss[32 * 256];            // the chunk's dS [row][key] (swizzled)
+
+  // heaviest first: early blocks are candidates for the most rows
+  const int nbg = D.B * D.h_kv;
+  const int t = (int)(blockIdx.x / nbg);
+  const int bg = (int)(blockIdx.x % nbg);
+  const int b = bg / D.h_kv, g = bg % D.h_kv;
+  const int G = D.G;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, cgrp = lane >> 4;
+  const int nkv = D.n_kv;
+  const int n_valid = max(1, min(kBk, nkv - t * kBk));
+  const uint16_t* kblk = k + (((int64_t)b * D.h_kv + g) * nkv + (int64_t)t * kBk) * kHeadDim;
+  const uint16_t* vblk = v + (((int64_t)b * D.h_kv + g) * nkv + (int64_t)t * kBk) * kHeadDim;
+
+  // K^T of the block into LDS (keys past the cache repeat the last one)
+  {
+    const int tid = threadIdx.x;
+    const int kq = tid >> 4, od = tid & 15;  // keys 4kq .. 4kq+3, dims 8od .. 8od+7
+    u32x4 x[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      x[qq] = *reinterpret_cast<const u32x4*>(kblk + min(4 * kq + qq, n_valid - 1) * kHeadDim + od * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) * 16;
+      const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
+      const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
+      *reinterpret_cast<uint2*>(Kt + (od * 8 + e) * kKtP + kq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+    }
+  }
+  // this wave's keys as B operands: key 16w + n, dims 32ks + 8c .. +7
+  u32x4 kf[4], vf[4];
+  {
+    const int key = min(16 * wave + n, n_valid - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kf[ks] = *reinterpret_cast<const u32x4*>(kblk + key * kHeadDim + 32 * ks + 8 * cgrp);
+      vf[ks] = *reinterpret_cast<const u32x4*>(vblk + key * kHeadDim + 32 * ks + 8 * cgrp);
+    }
+  }
+  f32x4 dkT[8], dvT[8];  // [d tile]: lane (key n, group c) holds dims 16dt + 4c + e of key 16w + n
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    dkT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dvT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float c2 = D.scale_log2;
+  const int key_abs = t * kBk + 16 * wave + n;  // this lane's key (B-operand column)
+
+  auto run_source = [&](const Src& sc) {
+    const int rows_total = sc.n_entries * G;
+    for (int r0 = 0; r0 < rows_total; r0 += 32) {
+      // rows of the chunk: the one this lane's fetch instruction takes, and the
+      // 8 whose statistics this lane's accumulators hold
+      {
+        const int rr = r0 + 4 * wave + (lane >> 4);
+        int i, s;
+        bool ok;
+        src_entry(sc, ws, D, rr / G, i, s, ok);
+        const int h = rr % G;
+        const int64_t qrow = (((int64_t)b * D.n_q + i) * D.h_q + g * G + h) * kHeadDim;
+        fetch_rows32(Qs, q + qrow, wave, lane);
+        fetch_rows32(Os, dout + qrow, wave, lane);
+      }
+      float lse2[8], dl[8];
+      int pos8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int rr = r0 + 16 * (u >> 2) + 4 * cgrp + (u & 3);
+        int i, s;
+        bool ok;
+        src_entry(sc, ws, D, rr / G, i, s, ok);
+        ok = ok && rr < rows_total;
+        const int h = rr % G;
+        const int64_t li = ((int64_t)b * D.h_q + g * G + h) * D.n_q + i;
+        lse2[u] = ok ? lse[li] * 1.4426950408889634f : __builtin_huge_valf();  // P = 0 for rows that do not exist
+        dl[u] = ok ? delta[li] : 0.f;
+        pos8[u] = ok ? (int)(D.offset + i) : -1;
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();  // the chunk's rows are in LDS
+      // transposed copies: thread (task) handles 4 rows x 8 dims of Q (tasks 0..127) or dO (128..255)
+      if (threadIdx.x < 256) {
+        const int task = threadIdx.x & 127;
+        const int rq = task >> 4, od = task & 15;  // rows 4rq .. 4rq+3, dims 8od .. 8od+7
+        const unsigned char* src = threadIdx.x < 128 ? Qs : Os;
+        uint16_t* dst = threadIdx.x < 128 ? Qt : Ot;
+        u32x4 x[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int r = 4 * rq + qq;
+          x[qq] = *reinterpret_cast<const u32x4*>(src + r * 256 + 16 * (od ^ (r & 15)));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sh = (e & 1) * 16;
+          const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
+          const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
+          *reinterpret_cast<uint2*>(dst + (od * 8 + e) * kTP + rq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+        }
+      }
+      // S = Q K_w^T and dP = dO V_w^T, rows as M (two 16-row tiles)
+      f32x4 sc4[2], dp4[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        sc4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * mt + n;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int slot = (4 * ks + cgrp) ^ (r & 15);
+          const u32x4 qa = *reinterpret_cast<const u32x4*>(Qs + r * 256 + 16 * slot);
+          const u32x4 oa = *reinterpret_cast<const u32x4*>(Os + r * 256 + 16 * slot);
+          sc4[mt] = mfma16(qa, kf[ks], sc4[mt]);
+          dp4[mt] = mfma16(oa, vf[ks], dp4[mt]);
+        }
+      }
+      // P and dS: accumulator u = 4 mt + e is row 16 mt + 4c + e, key 16w + n
+      float P[8], dS[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float sv = sc4[u >> 2][u & 3];
+        const bool vis = key_abs <= pos8[u] && key_abs < nkv;
+        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -lse2[u])) : 0.f;
+        P[u] = p;
+        dS[u] = p * (dp4[u >> 2][u & 3] - dl[u]);
+      }
+      const u32x4 pb = {pack_bf16x2(P[0], P[1]), pack_bf16x2(P[2], P[3]), pack_bf16x2(P[4], P[5]),
+                        pack_bf16x2(P[6], P[7])};
+      const u32x4 sb = {pack_bf16x2(dS[0], dS[1]), pack_bf16x2(dS[2], dS[3]), pack_bf16x2(dS[4], dS[5]),
+                        pack_bf16x2(dS[6], dS[7])};
+      // the chunk's dS for every wave: element (row, key 16w + n) at row * 256 + slot * 16 + 2 (key % 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = 16 * (u >> 2) + 4 * cgrp + (u & 3);
+        const int key = 16 * wave + n;
+        const int slot = (key >> 3) ^ (r & 15);
+        *reinterpret_cast<uint16_t*>(Ss + r * 256 + slot * 16 + 2 * (key & 7)) =
+            (uint16_t)((u & 1) ? (sb[u >> 1] >> 16) : (sb[u >> 1] & 0xFFFFu));
+      }
+      __syncthreads();  // transposes and dS are in LDS
+      // dV^T += dO^T P, dK^T += Q^T dS: M = head dims (8 tiles), K = the 32 rows
+      // (k-group c: rows 4c..4c+3 and 16+4c..16+4c+3), N = this wave's keys
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d = 16 * dt + n;
+        const uint2 o0 = *reinterpret_cast<const uint2*>(Ot + d * kTP + 4 * cgrp);
+        const uint2 o1 = *reinterpret_cast<const uint2*>(Ot + d * kTP + 16 + 4 * cgrp);
+        const uint2 q0 = *reinterpret_cast<const uint2*>(Qt + d * kTP + 4 * cgrp);
+        const uint2 q1 = *reinterpret_cast<const uint2*>(Qt + d * kTP + 16 + 4 * cgrp);
+        dvT[dt] = mfma16(u32x4{o0.x, o0.y, o1.x, o1.y}, pb, dvT[dt]);
+        dkT[dt] = mfma16(u32x4{q0.x, q0.y, q1.x, q1.y}, sb, dkT[dt]);
+      }
+      // dQ^T (dims 16w .. 16w+15 x 32 rows) = K^T dS^T over the block's 128 keys
+      f32x4 dq4[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        dq4[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * nt + n;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(Kt + (16 * wave + n) * kKtP + 32 * ks + 8 * cgrp);
+          const u32x4 sbv = *reinterpret_cast<const u32x4*>(Ss + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
+          dq4[nt] = mfma16(ka, sbv, dq4[nt]);
+        }
+      }
+      // lane (row 16nt + n, group c) holds dims 16w + 4c .. +3 of that row
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int rr = r0 + 16 * nt + n;
+        int i, s;
+        bool ok;
+        src_entry(sc, ws, D, rr / G, i, s, ok);
+        if (ok && rr < rows_total) {
+          const int h = rr % G;
+          const float sc = D.scale;
+          uint16_t* dst = dq_part + ((((int64_t)bg * D.n_q + i) * (D.k + 1) + s) * G + h) * kHeadDim + 16 * wave +
+                          4 * cgrp;
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(dq4[nt][0] * sc, dq4[nt][1] * sc),
+                                                      pack_bf16x2(dq4[nt][2] * sc, dq4[nt][3] * sc));
+        }
+      }
+      __syncthreads();  // the chunk's LDS is free for the next one
+    }
+  };
+
+  // the rows that gathered this block (one bin per query group), then its own positions
+  for (int qg = 0; qg < ws.n_groups; ++qg) {
+    const int bin = (bg * ws.n_groups + qg) * D.n_blk + t;
+    Src sc;
+    sc.kind = 0;
+    sc.tile0 = ws.tile_off[bin];
+    sc.n_entries = (ws.tile_off[bin + 1] - sc.tile0) * D.pt;
+    sc.pos0 = 0;
+    if (sc.n_entries > 0) run_source(sc);
+  }
+  {
+    const int lo = max(t * kBk, (int)D.offset), hi = min((t + 1) * kBk, (int)(D.offset + D.n_q));
+    if (hi > lo) {
+      Src sc;
+      sc.kind = 1;
+      sc.tile0 = 0;
+      sc.n_entries = hi - lo;
+      sc.pos0 = lo;
+      run_source(sc);
+    }
+  }
+  // write this wave's keys: lane (key n, group c) holds dims 16dt + 4c .. +3
+  if (key_abs < nkv) {
+    const int64_t row = (((int64_t)b * D.h_kv + g) * nkv + key_abs) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 16 * dt + 4 * cgrp;
+      const float sc = D.scale;
+      *reinterpret_cast<uint2*>(dk + row + d) = make_uint2(pack_bf16x2(dkT[dt][0] * sc, dkT[dt][1] * sc),
+                                                           pack_bf16x2(dkT[dt][2] * sc, dkT[dt][3] * sc));
+      *reinterpret_cast<uint2*>(dv + row + d) =
+          make_uint2(pack_bf16x2(dvT[dt][0], dvT[dt][1]), pack_bf16x2(dvT[dt][2], dvT[dt][3]));
+    }
+  }
+}
+
+// dq = the sum of a row's slot partials (its listed non-local blocks and the
+// local one): one thread per (row, head, 8 dims).
+__global__ __launch_bounds__(256) void k_bwd_dq_merge(const int32_t* __restrict__ block_idx,
+                                                      const uint16_t* __restrict__ dq_part, uint16_t* __restrict__ dq,
+                                                      Dims D) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = (int64_t)D.G * 16;
+  const int64_t row = id / per_row;  // (b, g, i)
+  if (row >= (int64_t)D.B * D.h_kv * D.n_q) return;
+  const int h = (int)((id % per_row) / 16), part = (int)(id % 16);
+  const int i = (int)(row % D.n_q);
+  const int64_t bg = row / D.n_q;
+  const int g = (int)(bg % D.h_kv), b = (int)(bg / D.h_kv);
+  const int local = (int)((D.offset + i) / kBk);
+  const int32_t* sel = block_idx + row * D.k;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](int s) {
+    const uint4 x = *reinterpret_cast<const uint4*>(dq_part + ((row * (D.k + 1) + s) * D.G + h) * kHeadDim + 8 * part);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[2 * u] += __uint_as_float(w[u] << 16);
+      acc[2 * u + 1] += __uint_as_float(w[u] & 0xFFFF0000u);
+    }
+  };
+  for (int s = 0; s < D.k; ++s)
+    if (nonlocal_slot(sel, s, local)) add(s);
+  add(D.k);
+  uint16_t* dst = dq + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + h) * kHeadDim + 8 * part;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+}
+
+}  // namespace
+
+hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
+                                  const uint16_t* out, const float* lse, const uint16_t* dout, uint16_t* dq,
+                                  uint16_t* dk, uint16_t* dv, const AttnWs& ws, uint16_t* dq_part, float* delta,
+                                  const Dims& D, hipStream_t stream) {
+  hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
+  if (e != hipSuccess) return e;
+  const int64_t pairs = (int64_t)D.B * D.n_q * D.h_q;
+  hipLaunchKernelGGL(k_bwd_delta, dim3((unsigned)((pairs * 8 + 255) / 256)), dim3(256), 0, stream, out, dout, delta,
+                     D);
+  hipLaunchKernelGGL(k_bwd_kv<false>, dim3((unsigned)((int64_t)D.B * D.h_kv * D.n_blk)), dim3(kBwdThreads), 0,
+                     stream, q, k, v, dout, lse, delta, ws, dq_part, dk, dv, D);
+  const int64_t threads = (int64_t)D.B * D.h_kv * D.n_q * D.G * 16;
+  hipLaunchKernelGGL(k_bwd_dq_merge, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, block_idx,
+                     dq_part, dq, D);
+  return hipGetLastError();
+}
+
+}  // namespace msa

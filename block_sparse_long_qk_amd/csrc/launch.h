@@ -41,6 +41,14 @@ hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int32_t* block_idx, const float* lse, float* kl, const AttnWs& ws, float4* kl_part,
                            const Dims& D, hipStream_t stream);
 
+// Main-branch backward over the forward's selection: dq, dk, dv (bf16) from
+// dout, out and lse; dq_part holds one bf16 partial per (row, slot, head),
+// delta the per-(row, head) dO . O.
+hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
+                                  const uint16_t* out, const float* lse, const uint16_t* dout, uint16_t* dq,
+                                  uint16_t* dk, uint16_t* dv, const AttnWs& ws, uint16_t* dq_part, float* delta,
+                                  const Dims& D, hipStream_t stream);
+
 // Dense mode (the indexer warmup): causal GQA attention over every visible
 // token, and the KL value over every visible token (needs the dense lse).
 hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, float* lse,

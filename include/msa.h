@@ -98,7 +98,8 @@ typedef enum {
   MSA_OP_BLOCK_TOPK = 1,
   MSA_OP_SPARSE_ATTN = 2,
   MSA_OP_FORWARD = 3,
-  MSA_OP_INDEX_KL = 4
+  MSA_OP_INDEX_KL = 4,
+  MSA_OP_SPARSE_ATTN_BWD = 5
 } msa_op;
 
 /* Bytes of device workspace the call `op` needs for problem `p` (0 for the
@@ -179,6 +180,26 @@ msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const
 msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q, const void* index_k,
                         const int32_t* block_idx, const float* lse, float* kl, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/*
+ * Backward of msa_sparse_attn_fwd: the gradients the language-model loss sends
+ * into the Main Branch (section MSA 如何训练), over the same token sets T as
+ * the forward (block_idx as the forward used it, the local block always in).
+ * With dout = dL/dout, for every (b, i, h) of group g and j in T:
+ *   P_j = exp(scale q . k_j - lse),  Delta = dout . out,
+ *   dS_j = P_j (dout . v_j - Delta),
+ *   dq[b][i][h] = scale sum_j dS_j k_j,
+ *   dk[b][g][j] = scale sum over rows and heads of dS_j q,
+ *   dv[b][g][j] = sum over rows and heads of P_j dout.
+ * out and lse are the forward's outputs for the same inputs; dq has q's layout,
+ * dk and dv k's (bf16, overwritten; keys no row attends get 0).  Needs
+ * workspace of msa_workspace_size(p, MSA_OP_SPARSE_ATTN_BWD); uniform batches.
+ * dk and dv are reduced in a fixed order (one workgroup per block), so the
+ * result is deterministic.
+ */
+msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, const void* out, const float* lse, const void* dout, void* dq,
+                               void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Dense mode: both branches over every visible token, as during the indexer

@@ -42,6 +42,7 @@ import numpy as np
 
 # Tensor ids of the element generator.
 T_Q, T_K, T_V, T_IQ, T_IK, T_PLANT_DIR, T_PLANT_POS = 1, 2, 3, 4, 5, 6, 7
+T_DO = 8  # the output gradient of the backward tests (q's layout)
 
 _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
@@ -287,6 +288,23 @@ def host_q_rows(w: Workload, b: int, rows) -> np.ndarray:
     return gen_at(w.seed, T_Q, idx).reshape(len(rows), w.h_q, w.head_dim)
 
 
+def host_do_rows(w: Workload, b: int, rows) -> np.ndarray:
+    """The output gradient dO[b, rows] (q's layout), shape [len(rows), h_q, d]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    row = w.h_q * w.head_dim
+    idx = ((b * w.n_q + rows)[:, None] * row + np.arange(row)[None, :]).reshape(-1)
+    return gen_at(w.seed, T_DO, idx).reshape(len(rows), w.h_q, w.head_dim)
+
+
+def device_dout(w: Workload, device="cuda:0"):
+    """The output gradient dO of a workload (q's shape), generated on the device."""
+    import torch
+    t = torch.empty(w.shapes()["q"], dtype=torch.bfloat16, device=device)
+    device_fill(w, "do", t)
+    torch.cuda.synchronize(device)
+    return t
+
+
 def host_iq_rows(w: Workload, b: int, rows, plant: Plant | None = None) -> np.ndarray:
     """index-q[b, rows] for arbitrary query rows, shape [len(rows), h_kv, d_idx], planted."""
     rows = np.asarray(rows, dtype=np.int64)
@@ -352,9 +370,9 @@ def _devlib():
 def device_fill(w: Workload, name: str, tensor, stream=None, nt_dev=None):
     """Fill a device tensor (torch, bf16, canonical layout) with generator values."""
     import torch
-    tid = {"q": T_Q, "k": T_K, "v": T_V, "iq": T_IQ, "ik": T_IK}[name]
+    tid = {"q": T_Q, "k": T_K, "v": T_V, "iq": T_IQ, "ik": T_IK, "do": T_DO}[name]
     assert tensor.is_contiguous() and tensor.element_size() == 2
-    assert tuple(tensor.shape) == w.shapes()[name], (tensor.shape, w.shapes()[name])
+    assert tuple(tensor.shape) == w.shapes()["q" if name == "do" else name], (tensor.shape, w.shapes()[name])
     if nt_dev is None:
         nt_dev = torch.from_numpy(normal_table().view(np.int16).copy()).to(tensor.device)
     s = (stream or torch.cuda.current_stream(tensor.device)).cuda_stream

@@ -1,0 +1,106 @@
+"""GPU parity of the Main-Branch backward (msa_sparse_attn_bwd) against the
+fp64 oracle (oracle_attend_bwd, pinned to torch autograd).
+
+The forward runs on the GPU (block_idx, out, lse); the output gradient is a
+seeded synthetic tensor.  Small cases compare dq, dk and dv element by
+element with the oracle run over every row and head of each group (the
+GPU's own selection); the 32K workload compares dq on sampled rows and checks
+the exact sum rules sum_j dv_j = sum dO and sum_j dk_j = 0 per group.
+
+Tolerance: the kernels feed P and dS to the MFMA as bf16 (relative error
+2^-9 each), accumulate in fp32 and round the results (and the dq partials)
+to bf16, so an element is off by about 2^-8 of the magnitude of the terms it
+sums; the bound is 2e-2 of the tensor's largest |value| for every element and
+2e-3 of it on average.
+"""
+import numpy as np
+import pytest
+
+import block_sparse_long_qk_amd as msa
+import oracle
+import synth
+from gpu_helpers import problem, run_gpu, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+GRAD_MAX_REL, GRAD_MEAN_REL = 2e-2, 2e-3
+
+FULL = [
+    synth.Workload("bwd_g4", 1, 600, 600, 8, 2, topk=4, seed=2601),
+    synth.Workload("bwd_g8_chunk", 2, 300, 1000, 16, 2, topk=5, q_offset=700, seed=2602),
+    synth.Workload("bwd_g1_ragged", 1, 777, 777, 4, 4, topk=3, seed=2603),
+    synth.Workload("bwd_g16", 1, 512, 512, 16, 1, topk=3, seed=2604),
+]
+
+
+def run_bwd(w, res):
+    import torch
+    p = problem(w)
+    x = res["inputs"]
+    dout = synth.device_dout(w)
+    dq = torch.empty_like(x["q"])
+    dk = torch.empty_like(x["k"])
+    dv = torch.empty_like(x["v"])
+    ws = torch.empty(msa.workspace_size(p, msa.OP_SPARSE_ATTN_BWD), dtype=torch.uint8, device="cuda")
+    msa.sparse_attn_bwd(p, x["q"], x["k"], x["v"], res["block_idx"], res["out"], res["lse"], dout, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    return dout, dq, dk, dv
+
+
+def close(name, got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = max(np.abs(ref).max(), 1e-30)
+    err = np.abs(got - ref)
+    say(f"    {name}: max |d| {err.max():.3e} (rel {err.max() / scale:.2e}), mean rel {err.mean() / scale:.2e}")
+    assert err.max() <= GRAD_MAX_REL * scale and err.mean() <= GRAD_MEAN_REL * scale, name
+
+
+@pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
+def test_backward_matches_oracle(w):
+    say(f"[gpu] backward {w.name}: B={w.batch} n_q={w.n_q} n_kv={w.n_kv} h={w.h_q}/{w.h_kv} k={w.topk}")
+    res = run_gpu(w, with_forward=False)
+    dout, dq, dk, dv = run_bwd(w, res)
+    rows = np.arange(w.n_q)
+    G = w.group
+    for b in range(w.batch):
+        for g in range(w.h_kv):
+            q_rows = synth.host_q_rows(w, b, rows)[:, g * G:(g + 1) * G, :]
+            dO = synth.host_do_rows(w, b, rows)[:, g * G:(g + 1) * G, :]
+            sel = res["block_idx"][b, g].cpu().numpy()
+            K = synth.host_kv(w, "k", b, g, 0, w.n_kv)
+            V = synth.host_kv(w, "v", b, g, 0, w.n_kv)
+            rdq, rdk, rdv = oracle.attend_bwd(q_rows, w.offset + rows, sel, K, V, w.block_size, w.scale, dO)
+            close(f"dq b{b} g{g}", dq[b][:, g * G:(g + 1) * G].float().cpu().numpy(), rdq)
+            close(f"dk b{b} g{g}", dk[b, g].float().cpu().numpy(), rdk)
+            close(f"dv b{b} g{g}", dv[b, g].float().cpu().numpy(), rdv)
+
+
+def test_backward_32k_sampled_and_sum_rules():
+    import torch
+    w = synth.WORKLOADS["prefill_32k"]
+    res = run_gpu(w, with_forward=False)
+    dout, dq, dk, dv = run_bwd(w, res)
+    G = w.group
+    rows = sample_rows(w, 32, seed=w.seed, whole_blocks=0)
+    # dq of sampled rows: the oracle over the rows' own blocks (dk, dv are not compared here)
+    worst = 0.0
+    for g in range(w.h_kv):
+        xr = oracle.inputs_for_rows(w, 0, g, rows)
+        sel = res["block_idx"][0, g].cpu().numpy()[rows]
+        K, V = oracle.kv_for_blocks(w, 0, g, sel)
+        dO = synth.host_do_rows(w, 0, rows)[:, g * G:(g + 1) * G, :]
+        rdq, _, _ = oracle.attend_bwd(xr["q"], xr["pos"], sel, K, V, w.block_size, w.scale, dO)
+        got = dq[0].index_select(0, torch.from_numpy(rows).cuda())[:, g * G:(g + 1) * G].float().cpu().numpy()
+        close(f"dq g{g}", got, rdq)
+    # sum rules per group: sum_j dv_j = sum over rows and heads of dO; sum_j dk_j = 0
+    do_sum = dout[0].float().view(w.n_q, w.h_kv, G, w.head_dim).sum(dim=(0, 2))
+    dv_sum = dv[0].float().sum(dim=1)
+    dk_sum = dk[0].float().sum(dim=1)
+    scale_v = dv[0].float().abs().sum(dim=1)
+    scale_k = dk[0].float().abs().sum(dim=1)
+    say(f"    sum rules: max |sum dv - sum dO| / sum|dv| = {((dv_sum - do_sum).abs() / scale_v).max().item():.2e}, "
+        f"max |sum dk| / sum|dk| = {(dk_sum.abs() / scale_k).max().item():.2e}")
+    assert bool(((dv_sum - do_sum).abs() <= 1e-2 * scale_v).all())
+    assert bool((dk_sum.abs() <= 1e-2 * scale_k).all())
+    assert bool(torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all())
