@@ -55,8 +55,10 @@ def _L():
                                   _f64, _f64p]
         lib.oracle_attend_bwd.argtypes = [_u16p, _i64, _i64p, _i32p, _i32, _i32, _u16p, _u16p, _i64, _i32, _i32,
                                           _f64, _u16p, _f64p, _f64p, _f64p]
+        lib.oracle_kl_bwd.argtypes = [_u16p, _i64, _i64p, _i32p, _i32, _i32, _u16p, _i64, _i32, _u16p, _u16p, _i32,
+                                      _i32, _f64, _f64p, _f64p, _f64p]
         for f in (lib.oracle_pool, lib.oracle_select, lib.oracle_attend, lib.oracle_dense_gqa, lib.oracle_merge,
-                  lib.oracle_e4m3_decode, lib.oracle_pool_f8, lib.oracle_kl, lib.oracle_attend_bwd):
+                  lib.oracle_e4m3_decode, lib.oracle_pool_f8, lib.oracle_kl, lib.oracle_attend_bwd, lib.oracle_kl_bwd):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -143,6 +145,22 @@ def attend_bwd(q_rows, pos, sel, K, V, bk: int, scale: float, dO_rows):
     _check(_L().oracle_attend_bwd(q_rows, n, pos, sel, sel.shape[1], G, K, V, K.shape[0], d, bk, scale, dO_rows, dQ,
                                   dK, dV), "oracle_attend_bwd")
     return dQ, dK, dV
+
+
+def kl_bwd(q_rows, pos, sel, K, iq_rows, ik, bk: int, scale: float, w=None):
+    """Gradient of sum_r w_r kl_r with respect to iq_rows and ik, the teacher
+    held fixed: returns (d_iq [n, d_idx], d_ik [n_kv, d_idx])."""
+    q_rows, K = _u16(q_rows), _u16(K)
+    iq_rows, ik = _u16(iq_rows), _u16(ik)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    n, G, d = q_rows.shape
+    w = np.ones(n) if w is None else np.ascontiguousarray(w, dtype=np.float64)
+    d_iq = np.zeros((n, iq_rows.shape[1]))
+    d_ik = np.zeros(ik.shape)
+    _check(_L().oracle_kl_bwd(q_rows, n, pos, sel, sel.shape[1], G, K, K.shape[0], d, iq_rows, ik, iq_rows.shape[1],
+                              bk, scale, w, d_iq, d_ik), "oracle_kl_bwd")
+    return d_iq, d_ik
 
 
 def kl(q_rows, pos, sel, K, iq_rows, ik, bk: int, scale: float) -> np.ndarray:

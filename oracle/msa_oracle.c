@@ -323,6 +323,81 @@ int oracle_kl(const uint16_t* q, int64_t nrows, const int64_t* pos, const int32_
 }
 
 /*
+ * Gradient of the KL alignment term with respect to the index projections'
+ * outputs, the teacher held fixed (page "MiniMax 发布 MSA…", section MSA 如何训练:
+ * gradient detach stops the KL gradient at the Index Branch's inputs, so it
+ * trains only the index projections; the teacher comes from the Main Branch).
+ * With z_j = iq . ik_j, student s_j = softmax_j(z_j) and teacher t_j over T
+ * as in oracle_kl, d kl / d z_j = s_j - t_j, so for a row weight w (the
+ * gradient of the loss with respect to the row's kl):
+ *   d_iq = w sum_j (s_j - t_j) ik_j,   d_ik_j += w (s_j - t_j) iq.
+ *   rows as in oracle_kl; w [nrows] -> d_iq [nrows][d_idx];
+ *   d_ik [n_kv][d_idx] accumulated over every row (the caller zeroes it).
+ */
+int oracle_kl_bwd(const uint16_t* q, int64_t nrows, const int64_t* pos, const int32_t* sel, int32_t k, int32_t G,
+                  const uint16_t* K, int64_t n_kv, int32_t d, const uint16_t* iq, const uint16_t* ik, int32_t d_idx,
+                  int32_t bk, double scale, const double* w, double* d_iq, double* d_ik) {
+  if (nrows < 0 || k < 1 || G < 1 || d <= 0 || d_idx <= 0 || bk <= 0) return -1;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (pos[r] < 0 || pos[r] >= n_kv) return -1;
+  const int64_t n_blk = (n_kv + bk - 1) / bk;
+  int32_t* blocks = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)k * (size_t)bk);
+  const size_t cap = (size_t)k * (size_t)bk;
+  double* teach = (double*)malloc(sizeof(double) * cap);
+  double* zz = (double*)malloc(sizeof(double) * cap);
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t p = pos[r];
+    memcpy(blocks, sel + r * k, sizeof(int32_t) * (size_t)k);
+    qsort(blocks, (size_t)k, sizeof(int32_t), int_order);
+    int64_t nt = 0;
+    for (int32_t s = 0; s < k; ++s) {
+      const int32_t t = blocks[s];
+      if (t < 0 || t >= n_blk || (s > 0 && t == blocks[s - 1])) continue;
+      for (int64_t j = (int64_t)t * bk; j < ((int64_t)t + 1) * bk && j < n_kv && j <= p; ++j) tok[nt++] = j;
+    }
+    /* teacher */
+    for (int64_t a = 0; a < nt; ++a) teach[a] = 0.0;
+    for (int32_t h = 0; h < G; ++h) {
+      const uint16_t* qh = q + (r * G + h) * d;
+      double m = -INFINITY;
+      for (int64_t a = 0; a < nt; ++a) {
+        double dot = 0.0;
+        for (int32_t c = 0; c < d; ++c) dot += bf(qh[c]) * bf(K[tok[a] * d + c]);
+        zz[a] = scale * dot;
+        if (zz[a] > m) m = zz[a];
+      }
+      double l = 0.0;
+      for (int64_t a = 0; a < nt; ++a) l += exp(zz[a] - m);
+      for (int64_t a = 0; a < nt; ++a) teach[a] += exp(zz[a] - m) / l / G;
+    }
+    /* student and the gradient */
+    double m = -INFINITY;
+    for (int64_t a = 0; a < nt; ++a) {
+      double dot = 0.0;
+      for (int32_t c = 0; c < d_idx; ++c) dot += bf(iq[r * d_idx + c]) * bf(ik[tok[a] * d_idx + c]);
+      zz[a] = dot;
+      if (dot > m) m = dot;
+    }
+    double l = 0.0;
+    for (int64_t a = 0; a < nt; ++a) l += exp(zz[a] - m);
+    for (int32_t c = 0; c < d_idx; ++c) d_iq[r * d_idx + c] = 0.0;
+    for (int64_t a = 0; a < nt; ++a) {
+      const double gz = w[r] * (exp(zz[a] - m) / l - teach[a]);
+      for (int32_t c = 0; c < d_idx; ++c) {
+        d_iq[r * d_idx + c] += gz * bf(ik[tok[a] * d_idx + c]);
+        d_ik[tok[a] * d_idx + c] += gz * bf(iq[r * d_idx + c]);
+      }
+    }
+  }
+  free(zz);
+  free(teach);
+  free(tok);
+  free(blocks);
+  return 0;
+}
+
+/*
  * Gradient of the Main Branch (the backward pass of oracle_attend), from the
  * definition of softmax attention over the row's token set T:
  *   P_hj = softmax_j(scale q_h . k_j),  o_h = sum_j P_hj v_j,

@@ -133,3 +133,62 @@ def test_matches_torch_softmax_and_kl_div(seed):
         log_student = torch.log_softmax(IQ[r] @ IK[idx].T, dim=-1)
         want = torch.nn.functional.kl_div(log_student, teacher, reduction="sum").item()
         assert abs(got[r] - want) < 1e-12 * max(1.0, abs(want))
+
+
+# ---------------------------------------------------------------- gradient (teacher detached)
+def _kl_case(seed):
+    rng = np.random.default_rng(seed)
+    n_kv, d, di, bk, G, k, n = 64, 16, 8, 8, 4, 3, 9
+    q, K = rand_bits(rng, (n, G, d)), rand_bits(rng, (n_kv, d))
+    iq, ik = rand_bits(rng, (n, di)), rand_bits(rng, (n_kv, di))
+    pos = rng.integers(0, n_kv, size=n)
+    sel = []
+    for p in pos:
+        loc = p // bk
+        others = sorted(rng.choice(loc, size=min(k - 1, loc), replace=False).tolist()) if loc else []
+        row = sorted(others + [loc])
+        sel.append(row + [-1] * (k - len(row)))
+    return q, K, iq, ik, pos, np.array(sel, np.int32), bk, 1.0 / math.sqrt(d), rng.standard_normal(n)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_kl_gradient_matches_torch_autograd_with_detached_teacher(seed):
+    q, K, iq, ik, pos, sel, bk, scale, w = _kl_case(300 + seed)
+    d_iq, d_ik = oracle.kl_bwd(q, pos, sel, K, iq, ik, bk, scale, w)
+    f = lambda b: torch.from_numpy(synth.bf16_to_f32(b).astype(np.float64))
+    Qt, Kt = f(q), f(K)
+    IQ = f(iq).requires_grad_(True)
+    IK = f(ik).requires_grad_(True)
+    loss = 0.0
+    for r in range(len(pos)):
+        toks = [j for t in sel[r] if t >= 0 for j in range(t * bk, min((t + 1) * bk, K.shape[0])) if j <= pos[r]]
+        idx = torch.tensor(toks)
+        teacher = torch.softmax(scale * Qt[r] @ Kt[idx].T, dim=-1).mean(dim=0).detach()
+        log_student = torch.log_softmax(IQ[r] @ IK[idx].T, dim=-1)
+        loss = loss + w[r] * torch.nn.functional.kl_div(log_student, teacher, reduction="sum")
+    loss.backward()
+    assert np.allclose(d_iq, IQ.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(d_ik, IK.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_kl_gradient_ignores_a_common_shift_of_the_index_keys():
+    # sum_j (s_j - t_j) = 0: shifting every index key by one vector leaves d_iq unchanged
+    q, K, iq, ik, pos, sel, bk, scale, w = _kl_case(310)
+    ikc = synth.f32_to_bf16(np.round(synth.bf16_to_f32(ik) * 4).astype(np.float32) / 4)
+    iks = synth.f32_to_bf16((synth.bf16_to_f32(ikc) + 0.25).astype(np.float32))
+    a, _ = oracle.kl_bwd(q, pos, sel, K, iq, ikc, bk, scale, w)
+    # the shift changes every logit of a row by the same amount (0.25 * sum(iq)), so s and t are unchanged
+    b, _ = oracle.kl_bwd(q, pos, sel, K, iq, iks, bk, scale, w)
+    assert np.allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_kl_gradient_vanishes_when_student_equals_teacher():
+    rng = np.random.default_rng(320)
+    n_kv, d, bk = 40, 8, 4
+    q = rand_bits(rng, (6, 1, d))
+    K = rand_bits(rng, (n_kv, d))
+    pos = rng.integers(0, n_kv, size=6)
+    sel = np.array([[t for t in range(p // bk + 1)][-3:] + [-1] * (3 - len([t for t in range(p // bk + 1)][-3:]))
+                    for p in pos], np.int32)
+    d_iq, d_ik = oracle.kl_bwd(q, pos, sel, K, q[:, 0, :], K, bk, 1.0)
+    assert np.abs(d_iq).max() < 1e-12 and np.abs(d_ik).max() < 1e-12
