@@ -104,9 +104,9 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.msa_block_topk_v.argtypes = [P, V, vp, vp, vp]
         lib.msa_sparse_attn_fwd_v.argtypes = [P, V, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_forward_v.argtypes = [P, V, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        lib.msa_index_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.msa_index_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_dense_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
-        lib.msa_dense_index_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        lib.msa_dense_index_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.msa_sparse_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTS[:-1]:
             getattr(lib, name).restype = ctypes.c_int
@@ -206,14 +206,14 @@ def forward(p: Problem, q, k, v, index_q, index_k, out, block_idx, lse=None, wor
 
 
 def index_kl(p: Problem, q, k, index_q, index_k, block_idx, lse, kl, workspace=None, workspace_bytes=None,
-             stream=None):
+             stream=None, lse_index=None):
     """KL(teacher || student) per (b, g, query): the group-averaged main-branch
     distribution over the selected tokens against the softmax of the raw index
     scores over the same tokens; lse is the forward pass's output."""
     nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     L, st = library(), _stream(stream, q)
     rc = L.msa_index_kl(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(index_q), _ptr(index_k), _ptr(block_idx), _ptr(lse),
-                        _ptr(kl), _ptr(workspace), nb, st)
+                        _ptr(kl), _ptr(lse_index), _ptr(workspace), nb, st)
     _check(rc, "msa_index_kl")
     return kl
 
@@ -237,11 +237,11 @@ def dense_attn_fwd(p: Problem, q, k, v, out, lse=None, stream=None):
     return out
 
 
-def dense_index_kl(p: Problem, q, k, index_q, index_k, lse, kl, stream=None):
+def dense_index_kl(p: Problem, q, k, index_q, index_k, lse, kl, stream=None, lse_index=None):
     """index_kl over every visible token, with the dense attention's lse."""
     L, st = library(), _stream(stream, q)
     _check(L.msa_dense_index_kl(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(index_q), _ptr(index_k), _ptr(lse), _ptr(kl),
-                                st), "msa_dense_index_kl")
+                                _ptr(lse_index), st), "msa_dense_index_kl")
     return kl
 
 

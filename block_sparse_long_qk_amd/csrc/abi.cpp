@@ -267,14 +267,14 @@ msa_status msa_forward_v(const msa_problem* p, const msa_varlen* vl, const void*
 }
 
 msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q, const void* index_k,
-                        const int32_t* block_idx, const float* lse, float* kl, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
+                        const int32_t* block_idx, const float* lse, float* kl, float* lse_index, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
   Dims D;
   const msa_status st = derive(p, &D);
   if (st != MSA_OK) return st;
   if (!q || !k || !index_q || !index_k || !block_idx || !lse || !kl || !workspace) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(index_q) || !aligned16(index_k) || !aligned16(block_idx) ||
-      !aligned16(lse) || !aligned16(kl) || !aligned16(workspace))
+      !aligned16(lse) || !aligned16(kl) || !aligned16(workspace) || (lse_index && !aligned16(lse_index)))
     return MSA_ERR_INVALID_ARGUMENT;
   if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
   if (kl_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
@@ -283,7 +283,8 @@ msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, cons
   const size_t plan = attn_ws_layout(D, base, &ws, false);
   return hip_status(msa::launch_index_kl(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                          static_cast<const uint16_t*>(index_q), static_cast<const uint16_t*>(index_k),
-                                         block_idx, lse, kl, ws, reinterpret_cast<float4*>(base + plan), D, stream));
+                                         block_idx, lse, kl, lse_index, ws, reinterpret_cast<float4*>(base + plan), D,
+                                         stream));
 }
 
 msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* k, const void* v,
@@ -325,18 +326,18 @@ msa_status msa_dense_attn_fwd(const msa_problem* p, const void* q, const void* k
 }
 
 msa_status msa_dense_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q,
-                              const void* index_k, const float* lse, float* kl, hipStream_t stream) {
+                              const void* index_k, const float* lse, float* kl, float* lse_index, hipStream_t stream) {
   Dims D;
   const msa_status st = derive(p, &D);
   if (st != MSA_OK) return st;
   if (!q || !k || !index_q || !index_k || !lse || !kl) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(index_q) || !aligned16(index_k) || !aligned16(lse) ||
-      !aligned16(kl))
+      !aligned16(kl) || (lse_index && !aligned16(lse_index)))
     return MSA_ERR_INVALID_ARGUMENT;
   if (!msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
   return hip_status(msa::launch_dense_index_kl(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                                static_cast<const uint16_t*>(index_q),
-                                               static_cast<const uint16_t*>(index_k), lse, kl, D, stream));
+                                               static_cast<const uint16_t*>(index_k), lse, kl, lse_index, D, stream));
 }
 
 msa_status msa_index_scores(const msa_problem* p, const void* index_q, const void* index_k, float* pooled,

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // non-local blocks and the local block, slot k) and form the KL value.
 __global__ __launch_bounds__(256) void k_kl_merge(const int32_t* __restrict__ block_idx,
                                                   const float4* __restrict__ kl_part, float* __restrict__ kl,
-                                                  Dims D) {
+                                                  float* __restrict__ lse_index, Dims D) {
   const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (row >= (int64_t)D.B * D.h_kv * D.n_q) return;
   const int i = (int)(row % D.n_q);
@@ -347,7 +347,9 @@ __global__ __launch_bounds__(256) void k_kl_merge(const int32_t* __restrict__ bl
     const float4 x = part[s];
     acc = kl_combine(acc, KlAcc{x.x, x.y, x.z, x.w});
   }
-  kl[row] = acc.a * kLn2 - acc.b + (acc.m + __log2f(acc.l)) * kLn2;
+  const float lz = (acc.m + __log2f(acc.l)) * kLn2;  // the student's log-normaliser
+  kl[row] = acc.a * kLn2 - acc.b + lz;
+  if (lse_index) lse_index[row] = lz;
 }
 
 // ---------------------------------------------------------------- dense mode
@@ -407,7 +409,8 @@ __device__ __forceinline__ void k_ik_store(uint16_t* Ks, uint16_t* IKs, const KI
 template <int DIDX, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_kl_dense(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ iq,
-    const uint16_t* __restrict__ ik, const float* __restrict__ lse, float* __restrict__ kl, Dims D) {
+    const uint16_t* __restrict__ ik, const float* __restrict__ lse, float* __restrict__ kl,
+    float* __restrict__ lse_index, Dims D) {
   using PM = PosMap<G>;
   constexpr int IKP = DIDX + 8;
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
@@ -497,8 +500,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int j = 0; j < PM::NPL; ++j) {
     const bool writer = col == PM::wpos(j, half) * G && (G == 4 || half == 0);
-    if (writer && pv[j])
-      kl[(int64_t)bg * D.n_q + pi[j]] = acc[j].a * kLn2 - acc[j].b + (acc[j].m + __log2f(acc[j].l)) * kLn2;
+    if (writer && pv[j]) {
+      const float lz = (acc[j].m + __log2f(acc[j].l)) * kLn2;
+      kl[(int64_t)bg * D.n_q + pi[j]] = acc[j].a * kLn2 - acc[j].b + lz;
+      if (lse_index) lse_index[(int64_t)bg * D.n_q + pi[j]] = lz;
+    }
   }
 }
 
@@ -509,8 +515,8 @@ bool kl_supported(const Dims& D) {
 }
 
 hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,
-                           const int32_t* block_idx, const float* lse, float* kl, const AttnWs& ws, float4* kl_part,
-                           const Dims& D, hipStream_t stream) {
+                           const int32_t* block_idx, const float* lse, float* kl, float* lse_index, const AttnWs& ws,
+                           float4* kl_part, const Dims& D, hipStream_t stream) {
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
   if (e != hipSuccess) return e;
   const dim3 grid(persistent_grid()), block(kThreads);
@@ -534,18 +540,18 @@ hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t*
   if (D.d_idx == 128) by_g(I128{}); else by_g(I64{});
   const int64_t rows = (int64_t)D.B * D.h_kv * D.n_q;
   hipLaunchKernelGGL(k_kl_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, block_idx, kl_part, kl,
-                     D);
+                     lse_index, D);
   return hipGetLastError();
 }
 
 hipError_t launch_dense_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q,
-                                 const uint16_t* index_k, const float* lse, float* kl, const Dims& D,
-                                 hipStream_t stream) {
+                                 const uint16_t* index_k, const float* lse, float* kl, float* lse_index,
+                                 const Dims& D, hipStream_t stream) {
   const int64_t n_t = (D.offset + D.n_q - 1) / D.pt - D.offset / D.pt + 1;
   const dim3 grid((unsigned)((int64_t)D.B * D.h_kv * n_t)), block(kThreads);
   auto go = [&](auto didx, auto g) {
     constexpr int DI = decltype(didx)::value, GG = decltype(g)::value;
-    hipLaunchKernelGGL((k_kl_dense<DI, GG>), grid, block, 0, stream, q, k, index_q, index_k, lse, kl, D);
+    hipLaunchKernelGGL((k_kl_dense<DI, GG>), grid, block, 0, stream, q, k, index_q, index_k, lse, kl, lse_index, D);
   };
   auto by_g = [&](auto didx) {
     switch (D.G) {

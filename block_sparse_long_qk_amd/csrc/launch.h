@@ -38,8 +38,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
 // inputs and uniform batches.
 bool kl_supported(const Dims& D);
 hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,
-                           const int32_t* block_idx, const float* lse, float* kl, const AttnWs& ws, float4* kl_part,
-                           const Dims& D, hipStream_t stream);
+                           const int32_t* block_idx, const float* lse, float* kl, float* lse_index, const AttnWs& ws,
+                           float4* kl_part, const Dims& D, hipStream_t stream);
 
 // Main-branch backward over the forward's selection: dq, dk, dv (bf16) from
 // dout, out and lse; dq_part holds one bf16 partial per (row, slot, head),
@@ -54,8 +54,8 @@ hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const ui
 hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, float* lse,
                              const Dims& D, hipStream_t stream);
 hipError_t launch_dense_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q,
-                                 const uint16_t* index_k, const float* lse, float* kl, const Dims& D,
-                                 hipStream_t stream);
+                                 const uint16_t* index_k, const float* lse, float* kl, float* lse_index,
+                                 const Dims& D, hipStream_t stream);
 
 // Decode-shaped calls (few query rows per sequence).
 bool use_index_small(const Dims& D);   // at most 16 (query, group) rows per sequence

@@ -168,7 +168,9 @@ msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const
  * T = { j <= p_i : floor(j / Bk) in S } as in msa_sparse_attn_fwd:
  *   teacher  t_j = (1/G) sum_{h in g} exp(scale * q[b][i][h] . k[b][g][j] - lse[b][h][i]),
  *   student  s_j = softmax_{j in T}(index_q[b][i][g] . index_k[b][j])   (raw index scores),
- *   kl[b][g][i] = sum_{j in T} t_j ln(t_j / s_j)   (fp32; terms with t_j = 0 add 0).
+ *   kl[b][g][i] = sum_{j in T} t_j ln(t_j / s_j)   (fp32; terms with t_j = 0 add 0);
+ *   lse_index[b][g][i] (nullable) = ln sum_{j in T} exp(index_q . index_k_j), the
+ *   student's log-normaliser, which msa_index_kl_bwd takes.
  * lse is the natural-log output of msa_sparse_attn_fwd (or msa_forward) for
  * the same block_idx; the teacher is normalised by it, so its weights sum to 1
  * to within that lse's accuracy.  kl is [B][H_kv][n_q] fp32.  Supported for
@@ -178,8 +180,8 @@ msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const
  * and the gradient are the caller's.
  */
 msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q, const void* index_k,
-                        const int32_t* block_idx, const float* lse, float* kl, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream);
+                        const int32_t* block_idx, const float* lse, float* kl, float* lse_index, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Backward of msa_sparse_attn_fwd: the gradients the language-model loss sends
@@ -210,8 +212,8 @@ msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* 
  * softmax_j(scale * q . k[b][g][j]) v[b][g][j], with lse (nullable) the natural
  * log-sum-exp; layouts as for msa_sparse_attn_fwd.  No workspace.
  *
- * msa_dense_index_kl: the KL value of msa_index_kl with T = { j <= p_i }; lse
- * is msa_dense_attn_fwd's.  Same support as msa_index_kl (G in {4, 8, 16,
+ * msa_dense_index_kl: the KL value (and lse_index) of msa_index_kl with
+ * T = { j <= p_i }; lse is msa_dense_attn_fwd's.  Same support as msa_index_kl (G in {4, 8, 16,
  * 32}, bf16 index inputs).  No workspace.
  *
  * Both take uniform batches (no msa_varlen form).
@@ -219,7 +221,7 @@ msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* 
 msa_status msa_dense_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v, void* out, float* lse,
                               hipStream_t stream);
 msa_status msa_dense_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q,
-                              const void* index_k, const float* lse, float* kl, hipStream_t stream);
+                              const void* index_k, const float* lse, float* kl, float* lse_index, hipStream_t stream);
 
 /*
  * Variable-length batches and paged caches (section 运行 Kernel: the kernels
