@@ -119,12 +119,22 @@ def gpu_leg(w, steps, warmup, stream, paged=False, kl=False):
         # the KL alignment pass on this step's selection and lse
         kl_out = torch.empty((w.batch, w.h_kv, w.n_q), dtype=torch.float32, device="cuda")
         kl_ws = torch.empty(max(msa.workspace_size(p, msa.OP_INDEX_KL), 256), dtype=torch.uint8, device="cuda")
+        lse_index = torch.empty_like(kl_out)
         run_kl = lambda: msa.index_kl(p, x["q"], x["k"], x["iq"], x["ik"], f["block_idx"], f["lse"], kl_out, kl_ws,
-                                      stream=sp)
+                                      stream=sp, lse_index=lse_index)
         for _ in range(warmup):
             run_kl()
         res["ms_kl"] = t.run(run_kl, steps)
         res["kl_mean"] = float(kl_out.mean().item())
+        # its gradient into the index projections (teacher detached)
+        d_iq, d_ik = torch.empty_like(x["iq"]), torch.empty_like(x["ik"])
+        kb_ws = torch.empty(msa.workspace_size(p, msa.OP_INDEX_KL_BWD), dtype=torch.uint8, device="cuda")
+        run_klb = lambda: msa.index_kl_bwd(p, x["q"], x["k"], x["iq"], x["ik"], f["block_idx"], f["lse"], lse_index,
+                                           d_iq, d_ik, workspace=kb_ws, stream=sp)
+        for _ in range(warmup):
+            run_klb()
+        res["ms_kl_bwd"] = t.run(run_klb, steps)
+        del d_iq, d_ik, kb_ws, lse_index
         # dense mode (the indexer warmup): dense attention, then the KL over every visible token
         d_out = torch.empty_like(f["out"])
         d_lse = torch.empty_like(f["lse"])
@@ -312,6 +322,11 @@ def main():
         line["kl"] = {"ms": round(g["ms_kl"], 4), "tflops": round(f_kl / (g["ms_kl"] * 1e-3) / 1e12, 1),
                       "frac_mfma": round(f_kl / (g["ms_kl"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                       "mean_kl": round(g["kl_mean"], 5)}
+        # its gradient: S for every head, then Z, d_index_k and d_index_q for every group
+        f_klb = 2.0 * (w.head_dim * w.h_q + 3 * w.index_dim * w.h_kv) * w.batch * float(t_size.sum())
+        line["kl_backward"] = {"ms": round(g["ms_kl_bwd"], 4),
+                               "tflops": round(f_klb / (g["ms_kl_bwd"] * 1e-3) / 1e12, 1),
+                               "frac_mfma": round(f_klb / (g["ms_kl_bwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         # dense mode: every visible token (sum over rows of p + 1)
         import numpy as np
         n_vis = float(np.sum(w.offset + np.arange(w.n_q, dtype=np.int64) + 1)) * w.batch

@@ -7,7 +7,8 @@ import of a compute entry point raises; nothing falls back to another path.
 
 Entry points (same names as the C ABI, without the ``msa_`` prefix):
 ``index_scores``, ``block_topk``, ``sparse_attn_fwd``, ``forward``,
-``index_kl``, ``dense_attn_fwd``, ``dense_index_kl``, ``sparse_attn_bwd``, ``workspace_size``; ``Problem`` mirrors ``msa_problem``.  Each compute call
+``index_kl``, ``dense_attn_fwd``, ``dense_index_kl``, ``sparse_attn_bwd``, ``index_kl_bwd``,
+``workspace_size``; ``Problem`` mirrors ``msa_problem``.  Each compute call
 takes an optional ``varlen`` (a ``Varlen``, mirroring ``msa_varlen``: per
 sequence query and cache lengths, packed query rows, a page table); given,
 the ``*_v`` variant of the C call is used.
@@ -22,12 +23,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
-OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN, OP_FORWARD, OP_INDEX_KL, OP_SPARSE_ATTN_BWD = range(6)
+OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN, OP_FORWARD, OP_INDEX_KL, OP_SPARSE_ATTN_BWD, OP_INDEX_KL_BWD = range(7)
 DTYPE_BF16, DTYPE_FP8_E4M3 = range(2)  # msa_dtype: element type of index_q / index_k
 
 EXPORTS = ("msa_workspace_size", "msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
            "msa_index_scores_v", "msa_block_topk_v", "msa_sparse_attn_fwd_v", "msa_forward_v", "msa_index_kl",
-           "msa_dense_attn_fwd", "msa_dense_index_kl", "msa_sparse_attn_bwd", "msa_status_string")
+           "msa_dense_attn_fwd", "msa_dense_index_kl", "msa_sparse_attn_bwd", "msa_index_kl_bwd",
+           "msa_status_string")
 
 
 class Problem(ctypes.Structure):
@@ -108,6 +110,7 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.msa_dense_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
         lib.msa_dense_index_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.msa_sparse_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.msa_index_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTS[:-1]:
             getattr(lib, name).restype = ctypes.c_int
         lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -227,6 +230,19 @@ def sparse_attn_bwd(p: Problem, q, k, v, block_idx, out, lse, dout, dq, dk, dv, 
                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nb, st)
     _check(rc, "msa_sparse_attn_bwd")
     return dq, dk, dv
+
+
+def index_kl_bwd(p: Problem, q, k, index_q, index_k, block_idx, lse, lse_index, d_index_q, d_index_k, dkl=None,
+                 workspace=None, workspace_bytes=None, stream=None):
+    """Gradients of sum(dkl * kl) into index_q and index_k, the teacher held
+    fixed; lse_index is index_kl's output for the same inputs (dkl None: ones)."""
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    L, st = library(), _stream(stream, q)
+    rc = L.msa_index_kl_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(index_q), _ptr(index_k), _ptr(block_idx),
+                            _ptr(lse), _ptr(lse_index), _ptr(dkl), _ptr(d_index_q), _ptr(d_index_k), _ptr(workspace),
+                            nb, st)
+    _check(rc, "msa_index_kl_bwd")
+    return d_index_q, d_index_k
 
 
 def dense_attn_fwd(p: Problem, q, k, v, out, lse=None, stream=None):

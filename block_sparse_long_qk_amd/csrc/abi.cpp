@@ -169,6 +169,16 @@ size_t bwd_bytes(const Dims& D) {
   return attn_ws_layout(D, nullptr, nullptr, false) + bwd_part_bytes(D) + bwd_delta_bytes(D);
 }
 
+// The KL backward: the plan, one bf16 d_index_q partial per (row, slot), and
+// each group's fp32 share of d_index_k.
+size_t klb_part_bytes(const Dims& D) {
+  return round256(sizeof(uint16_t) * (size_t)D.B * D.h_kv * D.n_q * (D.k + 1) * D.d_idx);
+}
+size_t klb_group_bytes(const Dims& D) { return round256(sizeof(float) * (size_t)D.B * D.h_kv * D.n_kv * D.d_idx); }
+size_t klb_bytes(const Dims& D) {
+  return attn_ws_layout(D, nullptr, nullptr, false) + klb_part_bytes(D) + klb_group_bytes(D);
+}
+
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
 }  // namespace
@@ -200,6 +210,10 @@ msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
     case MSA_OP_INDEX_KL:
       if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
       *bytes = kl_bytes(D);
+      return MSA_OK;
+    case MSA_OP_INDEX_KL_BWD:
+      if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
+      *bytes = klb_bytes(D);
       return MSA_OK;
     default:
       return MSA_ERR_INVALID_ARGUMENT;
@@ -285,6 +299,32 @@ msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, cons
                                          static_cast<const uint16_t*>(index_q), static_cast<const uint16_t*>(index_k),
                                          block_idx, lse, kl, lse_index, ws, reinterpret_cast<float4*>(base + plan), D,
                                          stream));
+}
+
+msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, const void* index_q,
+                            const void* index_k, const int32_t* block_idx, const float* lse, const float* lse_index,
+                            const float* dkl, void* d_index_q, void* d_index_k, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !index_q || !index_k || !block_idx || !lse || !lse_index || !d_index_q || !d_index_k || !workspace)
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(index_q) || !aligned16(index_k) || !aligned16(block_idx) ||
+      !aligned16(lse) || !aligned16(lse_index) || (dkl && !aligned16(dkl)) || !aligned16(d_index_q) ||
+      !aligned16(d_index_k) || !aligned16(workspace))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
+  if (klb_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  AttnWs ws;
+  char* base = static_cast<char*>(workspace);
+  const size_t plan = attn_ws_layout(D, base, &ws, false);
+  auto part = reinterpret_cast<uint16_t*>(base + plan);
+  auto group = reinterpret_cast<float*>(base + plan + klb_part_bytes(D));
+  return hip_status(msa::launch_index_kl_bwd(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(index_q),
+      static_cast<const uint16_t*>(index_k), block_idx, lse, lse_index, dkl, static_cast<uint16_t*>(d_index_q),
+      static_cast<uint16_t*>(d_index_k), ws, part, group, D, stream));
 }
 
 msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* k, const void* v,

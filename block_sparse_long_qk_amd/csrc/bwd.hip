@@ -368,7 +368,355 @@ __global__ __launch_bounds__(256) void k_bwd_dq_merge(const int32_t* __restrict_
                                               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
 }
 
+// ---------------------------------------------------------------- KL backward
+// Gradient of the KL alignment term into the index projections' outputs, the
+// teacher held fixed (page "MiniMax 发布 MSA…", section MSA 如何训练: gradient
+// detach keeps the KL loss off the backbone; only the index projections learn
+// from it).  With z_j = iq . ik_j, student s_j = exp(z_j - lse_index) and the
+// teacher t_j of the forward pass, a row of weight w (d loss / d kl) gives
+//   g_j = w (s_j - t_j),  d_iq = sum_j g_j ik_j,  d_ik_j += g_j iq.
+// Same owner-computes walk as k_bwd_kv, one workgroup per (sequence, group,
+// block): the teacher needs the group's K (S = Q K_w^T over the G head rows
+// of each position, summed over the heads), the student Z = IQ IK_w^T with
+// every head row reading its position's index-query row; g enters only
+// through the position's first head row (the others carry 0), so the same
+// 32-row contractions serve: d_ik^T += IQ^T g and d_iq^T = IK^T g^T.  d_ik
+// accumulates per group in fp32 (a reduction over groups follows: the index
+// keys are shared), d_iq leaves as one bf16 partial per (row, slot).
+
+// Fetch 32 index-query rows of DIDX bf16 (row r at r * 2 DIDX bytes, chunk c in
+// slot c ^ (r % CPI)) by direct loads; `rowp` is the row this lane's
+// instruction row takes.
+template <int DIDX>
+__device__ __forceinline__ void fetch_iq32(unsigned char* dst, const uint16_t* rowp, int wave, int lane) {
+  constexpr int CPI = DIDX / 8, RPI = 64 / CPI, NI = 32 / RPI;  // instructions: 8 (128) or 4 (64)
+  if (wave < NI) {
+    const int r = RPI * wave + lane / CPI;
+    const int c = (lane % CPI) ^ (r % CPI);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(rowp + 8 * c),
+                                     (__attribute__((address_space(3))) void*)(dst + 1024 * wave), 16, 0, 0);
+  }
+}
+
+template <int DIDX, int G>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_kl_bwd(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ iq,
+    const uint16_t* __restrict__ ik, const float* __restrict__ lse, const float* __restrict__ lse_index,
+    const float* __restrict__ wrow, AttnWs ws, uint16_t* __restrict__ diq_part, float* __restrict__ dik_group,
+    Dims D) {
+  constexpr int CPI = DIDX / 8;
+  constexpr int DT = DIDX / 16;       // 16-dim tiles of the index dim
+  constexpr int IKS = DIDX / 32;      // k-steps of Z
+  __shared__ __align__(16) uint16_t IKt[DIDX * kKtP];              // index keys of the block, transposed
+  __shared__ __align__(16) unsigned char Qs[32 * 256];             // the chunk's query rows (swizzled)
+  __shared__ __align__(16) unsigned char IQs[32 * 2 * DIDX];       // each row's index-query row (swizzled)
+  __shared__ __align__(16) uint16_t IQt[DIDX * kTP];               // its transpose [d][row]
+  __shared__ __align__(16) unsigned char Ss[32 * 256];             // the chunk's g [row][key] (swizzled)
+
+  const int nbg = D.B * D.h_kv;
+  const int t = (int)(blockIdx.x / nbg);
+  const int bg = (int)(blockIdx.x % nbg);
+  const int b = bg / D.h_kv, g = bg % D.h_kv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, cgrp = lane >> 4;
+  const int nkv = D.n_kv;
+  const int n_valid = max(1, min(kBk, nkv - t * kBk));
+  const uint16_t* kblk = k + (((int64_t)b * D.h_kv + g) * nkv + (int64_t)t * kBk) * kHeadDim;
+  const uint16_t* ikblk = ik + ((int64_t)b * nkv + (int64_t)t * kBk) * DIDX;
+
+  // the block's index keys transposed into LDS: task = 4 keys x 8 dims
+  for (int task = threadIdx.x; task < 32 * CPI; task += kBwdThreads) {
+    const int kq = task / CPI, od = task % CPI;
+    u32x4 x[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      x[qq] = *reinterpret_cast<const u32x4*>(ikblk + min(4 * kq + qq, n_valid - 1) * DIDX + od * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) * 16;
+      const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
+      const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
+      *reinterpret_cast<uint2*>(IKt + (od * 8 + e) * kKtP + kq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+    }
+  }
+  // this wave's 16 keys as B operands (K of the group, and the index keys)
+  u32x4 kf[4], ikf[IKS];
+  {
+    const int key = min(16 * wave + n, n_valid - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kf[ks] = *reinterpret_cast<const u32x4*>(kblk + key * kHeadDim + 32 * ks + 8 * cgrp);
+#pragma unroll
+    for (int ks = 0; ks < IKS; ++ks) ikf[ks] = *reinterpret_cast<const u32x4*>(ikblk + key * DIDX + 32 * ks + 8 * cgrp);
+  }
+  f32x4 dikT[DT];  // lane (key n, group c): dims 16dt + 4c + e of key 16w + n
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dikT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float c2 = D.scale_log2;
+  constexpr float kL2e = 1.4426950408889634f;
+  const int key_abs = t * kBk + 16 * wave + n;
+
+  auto run_source = [&](const Src& sc) {
+    const int rows_total = sc.n_entries * G;
+    for (int r0 = 0; r0 < rows_total; r0 += 32) {
+      {
+        // the rows this lane's fetch instructions take
+        const int rq = r0 + 4 * wave + (lane >> 4);
+        int i, s;
+        bool ok;
+        src_entry(sc, ws, D, rq / G, i, s, ok);
+        fetch_rows32(Qs, q + (((int64_t)b * D.n_q + i) * D.h_q + g * G + rq % G) * kHeadDim, wave, lane);
+        const int ri = r0 + (64 / CPI) * wave + lane / CPI;
+        src_entry(sc, ws, D, ri / G, i, s, ok);
+        fetch_iq32<DIDX>(IQs, iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX, wave, lane);
+      }
+      float lse2[8], lz2[8], wg[8];
+      int pos8[8];
+      bool first[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int rr = r0 + 16 * (u >> 2) + 4 * cgrp + (u & 3);
+        int i, s;
+        bool ok;
+        src_entry(sc, ws, D, rr / G, i, s, ok);
+        ok = ok && rr < rows_total;
+        const int h = rr % G;
+        lse2[u] = ok ? lse[((int64_t)b * D.h_q + g * G + h) * D.n_q + i] * kL2e : __builtin_huge_valf();
+        const int64_t prow = (int64_t)bg * D.n_q + i;
+        lz2[u] = ok ? lse_index[prow] * kL2e : __builtin_huge_valf();
+        wg[u] = ok ? (wrow ? wrow[prow] : 1.f) : 0.f;
+        pos8[u] = ok ? (int)(D.offset + i) : -1;
+        first[u] = ok && h == 0;
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();  // the chunk's rows are in LDS
+      // IQ^T for the d_ik contraction: task = 4 rows x 8 dims
+      for (int task = threadIdx.x; task < 8 * CPI; task += kBwdThreads) {
+        const int rq = task / CPI, od = task % CPI;
+        u32x4 x[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int r = 4 * rq + qq;
+          x[qq] = *reinterpret_cast<const u32x4*>(IQs + r * 2 * DIDX + 16 * (od ^ (r % CPI)));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sh = (e & 1) * 16;
+          const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
+          const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
+          *reinterpret_cast<uint2*>(IQt + (od * 8 + e) * kTP + rq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+        }
+      }
+      // S (teacher) and Z (student), rows as M
+      f32x4 sc4[2], z4[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        sc4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        z4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * mt + n;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 qa = *reinterpret_cast<const u32x4*>(Qs + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
+          sc4[mt] = mfma16(qa, kf[ks], sc4[mt]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < IKS; ++ks) {
+          const u32x4 ia =
+              *reinterpret_cast<const u32x4*>(IQs + r * 2 * DIDX + 16 * ((4 * ks + cgrp) ^ (r % CPI)));
+          z4[mt] = mfma16(ia, ikf[ks], z4[mt]);
+        }
+      }
+      // teacher: the head average of each position (rows 16mt + 4c + e; the heads of
+      // a position sit in this lane's e and, for G >= 8, the lanes l ^ 16 and l ^ 32)
+      float tsum[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        float sacc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int u = 4 * mt + e;
+          const bool vis = key_abs <= pos8[u] && key_abs < nkv;
+          sacc += vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc4[mt][e], c2, -lse2[u])) : 0.f;
+        }
+        tsum[mt] = sacc;
+      }
+      if constexpr (G >= 8) {
+        tsum[0] += __shfl_xor(tsum[0], 16, 64);
+        tsum[1] += __shfl_xor(tsum[1], 16, 64);
+      }
+      if constexpr (G >= 16) {
+        tsum[0] += __shfl_xor(tsum[0], 32, 64);
+        tsum[1] += __shfl_xor(tsum[1], 32, 64);
+      }
+      if constexpr (G == 32) tsum[0] = tsum[1] = tsum[0] + tsum[1];
+      // g = w (s - t) on each position's first head row, 0 elsewhere
+      float gv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool vis = key_abs <= pos8[u] && key_abs < nkv;
+        const float sv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(z4[u >> 2][u & 3], kL2e, -lz2[u])) : 0.f;
+        const float tv = vis ? tsum[u >> 2] * (1.f / G) : 0.f;
+        gv[u] = first[u] ? wg[u] * (sv - tv) : 0.f;
+      }
+      const u32x4 gb = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]), pack_bf16x2(gv[4], gv[5]),
+                        pack_bf16x2(gv[6], gv[7])};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = 16 * (u >> 2) + 4 * cgrp + (u & 3);
+        const int key = 16 * wave + n;
+        const int slot = (key >> 3) ^ (r & 15);
+        *reinterpret_cast<uint16_t*>(Ss + r * 256 + slot * 16 + 2 * (key & 7)) =
+            (uint16_t)((u & 1) ? (gb[u >> 1] >> 16) : (gb[u >> 1] & 0xFFFFu));
+      }
+      __syncthreads();  // IQ^T and g are in LDS
+      // d_ik^T += IQ^T g (M = index dims, K = the 32 rows, N = this wave's keys)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + n;
+        const uint2 a0 = *reinterpret_cast<const uint2*>(IQt + d * kTP + 4 * cgrp);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(IQt + d * kTP + 16 + 4 * cgrp);
+        dikT[dt] = mfma16(u32x4{a0.x, a0.y, a1.x, a1.y}, gb, dikT[dt]);
+      }
+      // d_iq^T (dims 16w .. 16w+15 x 32 rows) = IK^T g^T over the block's keys
+      if (wave < DT) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const int r = 16 * nt + n;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(IKt + (16 * wave + n) * kKtP + 32 * ks + 8 * cgrp);
+            const u32x4 gbv = *reinterpret_cast<const u32x4*>(Ss + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
+            acc = mfma16(ka, gbv, acc);
+          }
+          const int rr = r0 + r;
+          int i, s;
+          bool ok;
+          src_entry(sc, ws, D, rr / G, i, s, ok);
+          if (ok && rr < rows_total && rr % G == 0) {
+            uint16_t* dst = diq_part + (((int64_t)bg * D.n_q + i) * (D.k + 1) + s) * DIDX + 16 * wave + 4 * cgrp;
+            *reinterpret_cast<uint2*>(dst) =
+                make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+          }
+        }
+      }
+      __syncthreads();  // the chunk's LDS is free for the next one
+    }
+  };
+
+  for (int qg = 0; qg < ws.n_groups; ++qg) {
+    const int bin = (bg * ws.n_groups + qg) * D.n_blk + t;
+    Src sc;
+    sc.kind = 0;
+    sc.tile0 = ws.tile_off[bin];
+    sc.n_entries = (ws.tile_off[bin + 1] - sc.tile0) * D.pt;
+    sc.pos0 = 0;
+    if (sc.n_entries > 0) run_source(sc);
+  }
+  {
+    const int lo = max(t * kBk, (int)D.offset), hi = min((t + 1) * kBk, (int)(D.offset + D.n_q));
+    if (hi > lo) {
+      Src sc;
+      sc.kind = 1;
+      sc.tile0 = 0;
+      sc.n_entries = hi - lo;
+      sc.pos0 = lo;
+      run_source(sc);
+    }
+  }
+  // this group's share of d_ik for the wave's keys (fp32; the groups are added next)
+  if (key_abs < nkv) {
+    float* dst = dik_group + (((int64_t)b * D.h_kv + g) * nkv + key_abs) * DIDX;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(dst + 16 * dt + 4 * cgrp) =
+          make_float4(dikT[dt][0], dikT[dt][1], dikT[dt][2], dikT[dt][3]);
+  }
+}
+
+// d_ik[b][j] = sum over groups of their shares (bf16): one thread per 4 dims.
+__global__ __launch_bounds__(256) void k_kl_bwd_dik(const float* __restrict__ dik_group, uint16_t* __restrict__ dik,
+                                                    Dims D) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q4 = D.d_idx / 4;
+  const int64_t total = (int64_t)D.B * D.n_kv * q4;
+  if (id >= total) return;
+  const int64_t bj = id / q4;
+  const int part = (int)(id % q4);
+  const int64_t b = bj / D.n_kv, j = bj % D.n_kv;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int g = 0; g < D.h_kv; ++g) {
+    const float4 x = *reinterpret_cast<const float4*>(dik_group + ((b * D.h_kv + g) * D.n_kv + j) * D.d_idx + 4 * part);
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  *reinterpret_cast<uint2*>(dik + bj * D.d_idx + 4 * part) =
+      make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+}
+
+// d_iq[b][i][g] = the sum of the row's slot partials: one thread per (row, 8 dims).
+__global__ __launch_bounds__(256) void k_kl_bwd_diq(const int32_t* __restrict__ block_idx,
+                                                    const uint16_t* __restrict__ diq_part, uint16_t* __restrict__ diq,
+                                                    Dims D) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int c8 = D.d_idx / 8;
+  const int64_t row = id / c8;  // (b, g, i)
+  if (row >= (int64_t)D.B * D.h_kv * D.n_q) return;
+  const int part = (int)(id % c8);
+  const int i = (int)(row % D.n_q);
+  const int64_t bg = row / D.n_q;
+  const int g = (int)(bg % D.h_kv), b = (int)(bg / D.h_kv);
+  const int local = (int)((D.offset + i) / kBk);
+  const int32_t* sel = block_idx + row * D.k;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](int s) {
+    const uint4 x = *reinterpret_cast<const uint4*>(diq_part + (row * (D.k + 1) + s) * D.d_idx + 8 * part);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[2 * u] += __uint_as_float(w[u] << 16);
+      acc[2 * u + 1] += __uint_as_float(w[u] & 0xFFFF0000u);
+    }
+  };
+  for (int s = 0; s < D.k; ++s)
+    if (nonlocal_slot(sel, s, local)) add(s);
+  add(D.k);
+  uint16_t* dst = diq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * D.d_idx + 8 * part;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+}
+
 }  // namespace
+
+hipError_t launch_index_kl_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,
+                               const int32_t* block_idx, const float* lse, const float* lse_index, const float* wrow,
+                               uint16_t* d_index_q, uint16_t* d_index_k, const AttnWs& ws, uint16_t* diq_part,
+                               float* dik_group, const Dims& D, hipStream_t stream) {
+  hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((int64_t)D.B * D.h_kv * D.n_blk)), block(kBwdThreads);
+  auto go = [&](auto didx, auto gg) {
+    constexpr int DI = decltype(didx)::value, GG = decltype(gg)::value;
+    hipLaunchKernelGGL((k_kl_bwd<DI, GG>), grid, block, 0, stream, q, k, index_q, index_k, lse, lse_index, wrow, ws,
+                       diq_part, dik_group, D);
+  };
+  auto by_g = [&](auto didx) {
+    switch (D.G) {
+      case 4: go(didx, std::integral_constant<int, 4>{}); break;
+      case 8: go(didx, std::integral_constant<int, 8>{}); break;
+      case 16: go(didx, std::integral_constant<int, 16>{}); break;
+      default: go(didx, std::integral_constant<int, 32>{}); break;
+    }
+  };
+  if (D.d_idx == 128) by_g(std::integral_constant<int, 128>{}); else by_g(std::integral_constant<int, 64>{});
+  const int64_t n_ik = (int64_t)D.B * D.n_kv * (D.d_idx / 4);
+  hipLaunchKernelGGL(k_kl_bwd_dik, dim3((unsigned)((n_ik + 255) / 256)), dim3(256), 0, stream, dik_group, d_index_k, D);
+  const int64_t n_iq = (int64_t)D.B * D.h_kv * D.n_q * (D.d_idx / 8);
+  hipLaunchKernelGGL(k_kl_bwd_diq, dim3((unsigned)((n_iq + 255) / 256)), dim3(256), 0, stream, block_idx, diq_part,
+                     d_index_q, D);
+  return hipGetLastError();
+}
 
 hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
                                   const uint16_t* out, const float* lse, const uint16_t* dout, uint16_t* dq,

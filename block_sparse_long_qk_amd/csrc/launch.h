@@ -44,6 +44,10 @@ hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t*
 // Main-branch backward over the forward's selection: dq, dk, dv (bf16) from
 // dout, out and lse; dq_part holds one bf16 partial per (row, slot, head),
 // delta the per-(row, head) dO . O.
+hipError_t launch_index_kl_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,
+                               const int32_t* block_idx, const float* lse, const float* lse_index, const float* wrow,
+                               uint16_t* d_index_q, uint16_t* d_index_k, const AttnWs& ws, uint16_t* diq_part,
+                               float* dik_group, const Dims& D, hipStream_t stream);
 hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
                                   const uint16_t* out, const float* lse, const uint16_t* dout, uint16_t* dq,
                                   uint16_t* dk, uint16_t* dv, const AttnWs& ws, uint16_t* dq_part, float* delta,

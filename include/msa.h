@@ -99,7 +99,8 @@ typedef enum {
   MSA_OP_SPARSE_ATTN = 2,
   MSA_OP_FORWARD = 3,
   MSA_OP_INDEX_KL = 4,
-  MSA_OP_SPARSE_ATTN_BWD = 5
+  MSA_OP_SPARSE_ATTN_BWD = 5,
+  MSA_OP_INDEX_KL_BWD = 6
 } msa_op;
 
 /* Bytes of device workspace the call `op` needs for problem `p` (0 for the
@@ -182,6 +183,27 @@ msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const
 msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q, const void* index_k,
                         const int32_t* block_idx, const float* lse, float* kl, float* lse_index, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward of msa_index_kl into the Index Branch (section MSA 如何训练: the KL
+ * loss trains only the index projections; gradient detach keeps it off the
+ * backbone, so the teacher is a constant here and q, k get no gradient).
+ * With z_j = index_q[b][i][g] . index_k[b][j], s_j = exp(z_j - lse_index[b][g][i])
+ * and t_j the teacher of msa_index_kl, over the same T:
+ *   g_j = dkl[b][g][i] * (s_j - t_j)      (dkl = dL/dkl; NULL means all ones),
+ *   d_index_q[b][i][g] = sum_{j in T} g_j index_k[b][j],
+ *   d_index_k[b][j]    = sum over every (g, i) with j in its T of g_j index_q[b][i][g].
+ * lse and lse_index are msa_sparse_attn_fwd's and msa_index_kl's outputs for
+ * the same block_idx.  d_index_q and d_index_k have index_q's and index_k's
+ * layouts (bf16, overwritten; keys no row reaches get 0).  Same support as
+ * msa_index_kl; needs workspace of msa_workspace_size(p, MSA_OP_INDEX_KL_BWD).
+ * Reduced in a fixed order (one workgroup per (sequence, group, block), then
+ * the groups in order), so the result is deterministic.
+ */
+msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, const void* index_q,
+                            const void* index_k, const int32_t* block_idx, const float* lse, const float* lse_index,
+                            const float* dkl, void* d_index_q, void* d_index_k, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Backward of msa_sparse_attn_fwd: the gradients the language-model loss sends

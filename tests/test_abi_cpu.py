@@ -162,12 +162,32 @@ def test_fp8_index_problems_accepted():
 @pytest.mark.parametrize("kw", [dict(h_q=4, h_kv=2), dict(h_q=64, h_kv=1), dict(index_dtype=1),
                                 dict(h_q=12, h_kv=2)])
 def test_index_kl_unsupported_shapes(kw):
-    """The KL pass takes G in {4, 8, 16, 32} and bf16 index inputs."""
+    """The KL pass and its backward take G in {4, 8, 16, 32} and bf16 index inputs."""
     p = prob(**kw)
     n = ctypes.c_size_t(0)
-    assert msa.library().msa_workspace_size(ctypes.byref(p), msa.OP_INDEX_KL, ctypes.byref(n)) == msa.ERR_UNSUPPORTED
+    for op in (msa.OP_INDEX_KL, msa.OP_INDEX_KL_BWD):
+        assert msa.library().msa_workspace_size(ctypes.byref(p), op, ctypes.byref(n)) == msa.ERR_UNSUPPORTED
 
 
 def test_index_kl_workspace_is_smaller_than_attention():
     p = prob(h_q=8, h_kv=1)
     assert 0 < msa.workspace_size(p, msa.OP_INDEX_KL) < msa.workspace_size(p, msa.OP_SPARSE_ATTN)
+
+
+def test_index_kl_bwd_workspace():
+    """The plan, one bf16 d_index_q partial per (row, slot) and an fp32 d_index_k
+    share per (group, key): at least those two buffers' bytes."""
+    B, n_q, n_kv, h_kv, d_idx, k = 1, 4096, 4096, 2, 128, 8
+    p = prob(batch=B, n_q=n_q, n_kv=n_kv, h_q=16, h_kv=h_kv, index_dim=d_idx, topk=k)
+    need = 2 * B * h_kv * n_q * (k + 1) * d_idx + 4 * B * h_kv * n_kv * d_idx
+    assert msa.workspace_size(p, msa.OP_INDEX_KL_BWD) >= need
+
+
+def test_index_kl_bwd_rejects_null_lse_index():
+    """lse_index is required (the student's normaliser); nothing is launched."""
+    p = prob(h_q=16, h_kv=2)
+    fake = ctypes.c_void_p(4096)
+    L = msa.library()
+    rc = L.msa_index_kl_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None, fake, fake, fake,
+                            1 << 40, None)
+    assert rc == msa.ERR_INVALID_ARGUMENT

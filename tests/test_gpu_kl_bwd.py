@@ -1,0 +1,122 @@
+"""GPU parity of the KL backward into the Index Branch (msa_index_kl_bwd)
+against the fp64 oracle (oracle_kl_bwd, pinned to torch autograd with the
+teacher detached).
+
+The forward pass and the KL pass run on the GPU (block_idx, lse, lse_index);
+the KL backward then takes them through the C ABI.  Small cases compare
+d_index_q and d_index_k element by element with the oracle over every row of
+each group (the GPU's own selection; d_index_k is the sum of the groups'
+contributions, since the index keys are shared); one case takes random row
+weights dkl.  The 32K workload compares d_index_q on sampled rows and checks
+the sum rule: every row's g_j = w (s_j - t_j) sums to zero over T (student
+and teacher are both distributions over T), so sum_j d_index_k[j] = 0.
+
+Tolerance: g enters the MFMA as bf16 (relative error 2^-9), the index inputs
+are exact bf16, sums run in fp32 and the results (and the d_index_q partials)
+are rounded to bf16: an element is off by about 2^-8 of the magnitude of the
+terms it sums.  The bound is the one of the attention backward: 2e-2 of the
+tensor's largest |value| for every element, 2e-3 of it on average.
+"""
+import numpy as np
+import pytest
+
+import block_sparse_long_qk_amd as msa
+import oracle
+import synth
+from gpu_helpers import problem, run_gpu, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+GRAD_MAX_REL, GRAD_MEAN_REL = 2e-2, 2e-3
+
+CASES = [
+    synth.Workload("klb_g8", 1, 2048, 2048, 16, 2, topk=8, seed=2701),
+    synth.Workload("klb_g4_ragged_dimx64", 2, 1000, 1000, 8, 2, index_dim=64, topk=4, seed=2702),
+    synth.Workload("klb_g16_chunk", 1, 300, 1000, 32, 2, topk=4, q_offset=700, seed=2703),
+    synth.Workload("klb_g32", 1, 1536, 1536, 32, 1, topk=5, seed=2704),
+    synth.Workload("klb_decode", 3, 1, 5000, 16, 2, topk=8, seed=2705),
+]
+WEIGHTED = {"klb_g4_ragged_dimx64"}
+
+
+def run_kl_bwd(w, res, dkl=None):
+    import torch
+    p = problem(w)
+    x = res["inputs"]
+    kl = torch.empty((w.batch, w.h_kv, w.n_q), dtype=torch.float32, device="cuda")
+    lse_index = torch.full_like(kl, float("nan"))
+    ws = torch.empty(max(msa.workspace_size(p, msa.OP_INDEX_KL), 256), dtype=torch.uint8, device="cuda")
+    msa.index_kl(p, x["q"], x["k"], x["iq"], x["ik"], res["block_idx"], res["lse"], kl, ws, lse_index=lse_index)
+    del ws
+    d_iq = torch.full_like(x["iq"], float("nan"))  # every element must be written
+    d_ik = torch.full_like(x["ik"], float("nan"))
+    ws = torch.empty(msa.workspace_size(p, msa.OP_INDEX_KL_BWD), dtype=torch.uint8, device="cuda")
+    msa.index_kl_bwd(p, x["q"], x["k"], x["iq"], x["ik"], res["block_idx"], res["lse"], lse_index, d_iq, d_ik,
+                     dkl=dkl, workspace=ws)
+    torch.cuda.synchronize()
+    return lse_index, d_iq, d_ik
+
+
+def as_float(t):
+    import torch
+    return t.view(torch.bfloat16).float().cpu().numpy()
+
+
+def close(name, got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = max(np.abs(ref).max(), 1e-30)
+    err = np.abs(got - ref)
+    say(f"    {name}: max |d| {err.max():.3e} (rel {err.max() / scale:.2e}), mean rel {err.mean() / scale:.2e}")
+    assert np.all(np.isfinite(got)), name
+    assert err.max() <= GRAD_MAX_REL * scale and err.mean() <= GRAD_MEAN_REL * scale, name
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_kl_backward_matches_oracle(w):
+    import torch
+    say(f"[gpu] kl backward {w.name}: B={w.batch} n_q={w.n_q} n_kv={w.n_kv} h={w.h_q}/{w.h_kv} "
+        f"d_idx={w.index_dim} k={w.topk}")
+    res = run_gpu(w, with_forward=False)
+    dkl = None
+    if w.name in WEIGHTED:
+        gen = torch.Generator().manual_seed(w.seed)
+        dkl = (torch.rand((w.batch, w.h_kv, w.n_q), generator=gen) * 2 - 0.5).cuda()
+    _, d_iq, d_ik = run_kl_bwd(w, res, dkl)
+    rows = np.arange(w.n_q)
+    for b in range(w.batch):
+        ref_ik = None
+        for g in range(w.h_kv):
+            x = oracle.inputs_for_rows(w, b, g, rows)
+            sel = res["block_idx"][b, g].cpu().numpy()
+            K = synth.host_kv(w, "k", b, g, 0, w.n_kv)
+            wr = None if dkl is None else dkl[b, g].double().cpu().numpy()
+            r_iq, r_ik = oracle.kl_bwd(x["q"], x["pos"], sel, K, x["iq"], x["ik"], w.block_size, w.scale, wr)
+            close(f"d_iq b{b} g{g}", as_float(d_iq[b][:, g]), r_iq)
+            ref_ik = r_ik if ref_ik is None else ref_ik + r_ik
+        got_ik = as_float(d_ik[b])
+        n_seen = ref_ik.shape[0]
+        close(f"d_ik b{b}", got_ik[:n_seen], ref_ik)
+        assert np.all(got_ik[n_seen:] == 0.0), "keys past every row's position must get 0"
+
+
+def test_kl_backward_32k_sampled_and_sum_rule():
+    import torch
+    w = synth.WORKLOADS["prefill_32k"]
+    say(f"[gpu] kl backward {w.name}")
+    res = run_gpu(w, with_forward=False)
+    _, d_iq, d_ik = run_kl_bwd(w, res)
+    rows = sample_rows(w, 32, seed=w.seed, whole_blocks=0)
+    for g in range(w.h_kv):
+        x = oracle.inputs_for_rows(w, 0, g, rows)
+        sel = res["block_idx"][0, g].cpu().numpy()[rows]
+        K, _ = oracle.kv_for_blocks(w, 0, g, sel)
+        r_iq, _ = oracle.kl_bwd(x["q"], x["pos"], sel, K, x["iq"], x["ik"], w.block_size, w.scale)
+        got = as_float(d_iq[0].index_select(0, torch.from_numpy(rows).cuda())[:, g])
+        close(f"d_iq g{g}", got, r_iq)
+    dik = d_ik[0].view(torch.bfloat16).float()
+    total = dik.sum(dim=0)
+    mag = dik.abs().sum(dim=0)
+    say(f"    sum rule: max |sum_j d_ik_j| / sum_j |d_ik_j| = {(total.abs() / mag).max().item():.2e}")
+    assert bool(torch.isfinite(dik).all())
+    assert bool((total.abs() <= 1e-2 * mag).all())
