@@ -104,15 +104,148 @@ __device__ __forceinline__ void fetch_rows32(unsigned char* dst, const uint16_t*
                                    (__attribute__((address_space(3))) void*)(dst + 1024 * wave), 16, 0, 0);
 }
 
+// ---------------------------------------------------------------- the chunk walk
+// The rows one workgroup walks for its (sequence, group, block): the plan's bin
+// of the block for each query group (its entries are compact: list indices
+// base .. base + count - 1), then the block's own positions; 32 rows a chunk,
+// flattened row R of a source = entry * G + head.  The walk is pipelined: a
+// chunk's row table (query row, slot, head of each of its 32 rows) is written
+// to LDS two chunks ahead, from list entries loaded one iteration before, so
+// every lane can address the next chunk's rows right after a barrier.
+constexpr int kMaxSrc = 260;  // query groups per (b, g) + 1 (n_kv <= 2M: at most 256 groups)
+constexpr int kRing = 4;      // row tables in flight: the chunk computed, the one fetched, the one built
+
+struct WalkTab {
+  int nent[kMaxSrc];    // entries (positions) of each source
+  int base[kMaxSrc];    // bin: first list index; own positions: the first position
+  int2 row[kRing][32];  // per chunk row: (query row i, or -1 for none; slot * 256 + head)
+  int n_chunks;
+};
+
+__device__ __forceinline__ void walk_setup(WalkTab& W, const AttnWs& ws, const Dims& D, int bg, int t) {
+  const int n_src = ws.n_groups + 1;
+  if (threadIdx.x == 0) W.n_chunks = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int q = threadIdx.x; q < n_src; q += blockDim.x) {
+    int nent, base;
+    if (q < ws.n_groups) {
+      const int bin = (bg * ws.n_groups + q) * D.n_blk + t;
+      nent = ws.cnt[bin];
+      base = ws.tile_off[bin] * D.pt;
+    } else {
+      const int lo = max(t * kBk, (int)D.offset), hi = min((t + 1) * kBk, (int)(D.offset + D.n_q));
+      nent = max(0, hi - lo);
+      base = lo;
+    }
+    W.nent[q] = nent;
+    W.base[q] = base;
+    mine += (nent * D.G + 31) / 32;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) mine += __shfl_xor(mine, m, 64);
+  if ((threadIdx.x & 63) == 0 && mine) atomicAdd(&W.n_chunks, mine);
+  __syncthreads();
+}
+
+// Row-table builder, run by wave 0 (lane r < 32 owns chunk row r).  The
+// cursor (source, first row) is uniform over the wave.
+struct Builder {
+  int src, r0;
+  int x;      // pending: list entry (row * k + slot), loaded for every lane (entry 0 if none)
+  int kind;   // pending row: 0 none, 1 plan entry x, 2 own position pos
+  int pos;    // pending own position
+  int h;      // pending row's head
+};
+
+__device__ __forceinline__ void bld_skip(Builder& bd, const WalkTab& W, int G, int n_src) {
+  while (bd.src < n_src && bd.r0 >= W.nent[bd.src] * G) {
+    ++bd.src;
+    bd.r0 = 0;
+  }
+}
+
+// The list load is unconditional (entry 0 when the row is not a plan row), so
+// the pending value is defined on every path and needs no copy until its use.
+__device__ __forceinline__ void bld_load(Builder& bd, const WalkTab& W, const AttnWs& ws, int G, int n_src,
+                                         int lane) {
+  const int R = bd.r0 + (lane & 31);
+  const bool live = bd.src < n_src && lane < 32 && R < W.nent[min(bd.src, n_src - 1)] * G;
+  const bool plan = live && bd.src < n_src - 1;
+  const int base = W.base[min(bd.src, n_src - 1)];
+  bd.x = ws.list[plan ? base + R / G : 0].x;
+  bd.kind = plan ? 1 : (live ? 2 : 0);
+  bd.pos = base + R / G;
+  bd.h = R % G;
+}
+
+__device__ __forceinline__ void bld_write(const Builder& bd, WalkTab& W, int slot, const Dims& D, int lane) {
+  if (lane < 32) {
+    int2 e = make_int2(-1, 0);
+    if (bd.kind == 2) e = make_int2((int)(bd.pos - D.offset), D.k * 256 + bd.h);
+    if (bd.kind == 1 && bd.x >= 0) e = make_int2(bd.x / D.k, (bd.x % D.k) * 256 + bd.h);
+    W.row[slot][lane] = e;
+  }
+}
+
+__device__ __forceinline__ void bld_next(Builder& bd, const WalkTab& W, int G, int n_src) {
+  bd.r0 += 32;
+  bld_skip(bd, W, G, n_src);
+}
+
+// Tables of chunks 0 and 1 written, chunk 2's entries pending (wave 0 only).
+__device__ __forceinline__ void bld_prologue(Builder& bd, WalkTab& W, const AttnWs& ws, const Dims& D, int lane) {
+  const int n_src = ws.n_groups + 1;
+  bd.src = 0;
+  bd.r0 = 0;
+  bld_skip(bd, W, D.G, n_src);
+  bld_load(bd, W, ws, D.G, n_src, lane);
+  bld_write(bd, W, 0, D, lane);
+  bld_next(bd, W, D.G, n_src);
+  bld_load(bd, W, ws, D.G, n_src, lane);
+  bld_write(bd, W, 1, D, lane);
+  bld_next(bd, W, D.G, n_src);
+  bld_load(bd, W, ws, D.G, n_src, lane);
+}
+
+// One iteration of the builder: chunk c + 2's table from the pending entries,
+// then chunk c + 3's entries loaded.
+__device__ __forceinline__ void bld_step(Builder& bd, WalkTab& W, const AttnWs& ws, const Dims& D, int c, int lane) {
+  const int n_src = ws.n_groups + 1;
+  bld_write(bd, W, (c + 2) & (kRing - 1), D, lane);
+  bld_next(bd, W, D.G, n_src);
+  bld_load(bd, W, ws, D.G, n_src, lane);
+}
+
+// dst[d][row] (pitch kTP) = src rows (32 x 128 bf16, swizzled): task (0..127)
+// handles rows 4 (task / 16) .. +3, dims 8 (task % 16) .. +7.
+__device__ __forceinline__ void transpose_rows32(const unsigned char* src, uint16_t* dst, int task) {
+  const int rq = task >> 4, od = task & 15;
+  u32x4 x[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int r = 4 * rq + qq;
+    x[qq] = *reinterpret_cast<const u32x4*>(src + r * 256 + 16 * (od ^ (r & 15)));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int sh = (e & 1) * 16;
+    const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
+    const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
+    *reinterpret_cast<uint2*>(dst + (od * 8 + e) * kTP + rq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+  }
+}
+
 template <bool VL>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta, AttnWs ws,
     uint16_t* __restrict__ dq_part, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, Dims D) {
-  __shared__ __align__(16) uint16_t Kt[kHeadDim * kKtP];          // K^T of the block
+  __shared__ __align__(16) uint16_t Kt[kHeadDim * kKtP];             // K^T of the block
   __shared__ __align__(16) unsigned char Qs[32 * 256], Os[32 * 256];  // chunk rows of Q and dO (swizzled)
   __shared__ __align__(16) uint16_t Qt[kHeadDim * kTP], Ot[kHeadDim * kTP];  // their transposes [d][row]
-  __shared__ __align__(16) unsigned char Ss[32 * 256];            // the chunk's dS [row][key] (swizzled)
+  __shared__ __align__(16) unsigned char Ss[32 * 256];  // the chunk's dS [row][key] (swizzled)
+  __shared__ WalkTab W;
 
   // heaviest first: early blocks are candidates for the most rows
   const int nbg = D.B * D.h_kv;
@@ -126,6 +259,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int n_valid = max(1, min(kBk, nkv - t * kBk));
   const uint16_t* kblk = k + (((int64_t)b * D.h_kv + g) * nkv + (int64_t)t * kBk) * kHeadDim;
   const uint16_t* vblk = v + (((int64_t)b * D.h_kv + g) * nkv + (int64_t)t * kBk) * kHeadDim;
+
+  walk_setup(W, ws, D, bg, t);
+  const int nch = W.n_chunks;
+  Builder bd;
+  if (wave == 0) bld_prologue(bd, W, ws, D, lane);
 
   // K^T of the block into LDS (keys past the cache repeat the last one)
   {
@@ -161,164 +299,140 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
   const float c2 = D.scale_log2;
   const int key_abs = t * kBk + 16 * wave + n;  // this lane's key (B-operand column)
+  __syncthreads();  // row tables of chunks 0 and 1 are written
 
-  auto run_source = [&](const Src& sc) {
-    const int rows_total = sc.n_entries * G;
-    for (int r0 = 0; r0 < rows_total; r0 += 32) {
-      // rows of the chunk: the one this lane's fetch instruction takes, and the
-      // 8 whose statistics this lane's accumulators hold
-      {
-        const int rr = r0 + 4 * wave + (lane >> 4);
-        int i, s;
-        bool ok;
-        src_entry(sc, ws, D, rr / G, i, s, ok);
-        const int h = rr % G;
-        const int64_t qrow = (((int64_t)b * D.n_q + i) * D.h_q + g * G + h) * kHeadDim;
-        fetch_rows32(Qs, q + qrow, wave, lane);
-        fetch_rows32(Os, dout + qrow, wave, lane);
-      }
-      float lse2[8], dl[8];
-      int pos8[8];
+  // A chunk's rows travel through registers: lane l of wave w loads 16 bytes
+  // of row r = 4w + l / 16 (its 16-byte piece (l % 16) ^ (r % 16)) and stores
+  // them at byte 1024 w + 16 l of the row buffer, so row r's piece p sits in
+  // slot p ^ (r % 16).
+  u32x4 q_next, o_next;
+  auto load_rows = [&](int slot) {
+    const int2 e = W.row[slot][4 * wave + (lane >> 4)];
+    const int r = 4 * wave + (lane >> 4);
+    const int i = max(e.x, 0), h = e.y & 255;
+    const int64_t qrow = (((int64_t)b * D.n_q + i) * D.h_q + g * G + h) * kHeadDim + 8 * ((lane & 15) ^ (r & 15));
+    q_next = *reinterpret_cast<const u32x4*>(q + qrow);
+    o_next = *reinterpret_cast<const u32x4*>(dout + qrow);
+  };
+  auto store_rows = [&]() {
+    *reinterpret_cast<u32x4*>(Qs + 1024 * wave + 16 * lane) = q_next;
+    *reinterpret_cast<u32x4*>(Os + 1024 * wave + 16 * lane) = o_next;
+  };
+  // raw lse and delta of the next chunk's rows (row 0's for rows that do not
+  // exist), first used in the next iteration
+  float lse_raw[8], dl_raw[8];
+  auto stats = [&](int slot) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int rr = r0 + 16 * (u >> 2) + 4 * cgrp + (u & 3);
-        int i, s;
-        bool ok;
-        src_entry(sc, ws, D, rr / G, i, s, ok);
-        ok = ok && rr < rows_total;
-        const int h = rr % G;
-        const int64_t li = ((int64_t)b * D.h_q + g * G + h) * D.n_q + i;
-        lse2[u] = ok ? lse[li] * 1.4426950408889634f : __builtin_huge_valf();  // P = 0 for rows that do not exist
-        dl[u] = ok ? delta[li] : 0.f;
-        pos8[u] = ok ? (int)(D.offset + i) : -1;
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      __syncthreads();  // the chunk's rows are in LDS
-      // transposed copies: thread (task) handles 4 rows x 8 dims of Q (tasks 0..127) or dO (128..255)
-      if (threadIdx.x < 256) {
-        const int task = threadIdx.x & 127;
-        const int rq = task >> 4, od = task & 15;  // rows 4rq .. 4rq+3, dims 8od .. 8od+7
-        const unsigned char* src = threadIdx.x < 128 ? Qs : Os;
-        uint16_t* dst = threadIdx.x < 128 ? Qt : Ot;
-        u32x4 x[4];
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int r = 4 * rq + qq;
-          x[qq] = *reinterpret_cast<const u32x4*>(src + r * 256 + 16 * (od ^ (r & 15)));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int sh = (e & 1) * 16;
-          const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
-          const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
-          *reinterpret_cast<uint2*>(dst + (od * 8 + e) * kTP + rq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
-        }
-      }
-      // S = Q K_w^T and dP = dO V_w^T, rows as M (two 16-row tiles)
-      f32x4 sc4[2], dp4[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        sc4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r = 16 * mt + n;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int slot = (4 * ks + cgrp) ^ (r & 15);
-          const u32x4 qa = *reinterpret_cast<const u32x4*>(Qs + r * 256 + 16 * slot);
-          const u32x4 oa = *reinterpret_cast<const u32x4*>(Os + r * 256 + 16 * slot);
-          sc4[mt] = mfma16(qa, kf[ks], sc4[mt]);
-          dp4[mt] = mfma16(oa, vf[ks], dp4[mt]);
-        }
-      }
-      // P and dS: accumulator u = 4 mt + e is row 16 mt + 4c + e, key 16w + n
-      float P[8], dS[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float sv = sc4[u >> 2][u & 3];
-        const bool vis = key_abs <= pos8[u] && key_abs < nkv;
-        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -lse2[u])) : 0.f;
-        P[u] = p;
-        dS[u] = p * (dp4[u >> 2][u & 3] - dl[u]);
-      }
-      const u32x4 pb = {pack_bf16x2(P[0], P[1]), pack_bf16x2(P[2], P[3]), pack_bf16x2(P[4], P[5]),
-                        pack_bf16x2(P[6], P[7])};
-      const u32x4 sb = {pack_bf16x2(dS[0], dS[1]), pack_bf16x2(dS[2], dS[3]), pack_bf16x2(dS[4], dS[5]),
-                        pack_bf16x2(dS[6], dS[7])};
-      // the chunk's dS for every wave: element (row, key 16w + n) at row * 256 + slot * 16 + 2 (key % 8)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int r = 16 * (u >> 2) + 4 * cgrp + (u & 3);
-        const int key = 16 * wave + n;
-        const int slot = (key >> 3) ^ (r & 15);
-        *reinterpret_cast<uint16_t*>(Ss + r * 256 + slot * 16 + 2 * (key & 7)) =
-            (uint16_t)((u & 1) ? (sb[u >> 1] >> 16) : (sb[u >> 1] & 0xFFFFu));
-      }
-      __syncthreads();  // transposes and dS are in LDS
-      // dV^T += dO^T P, dK^T += Q^T dS: M = head dims (8 tiles), K = the 32 rows
-      // (k-group c: rows 4c..4c+3 and 16+4c..16+4c+3), N = this wave's keys
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int d = 16 * dt + n;
-        const uint2 o0 = *reinterpret_cast<const uint2*>(Ot + d * kTP + 4 * cgrp);
-        const uint2 o1 = *reinterpret_cast<const uint2*>(Ot + d * kTP + 16 + 4 * cgrp);
-        const uint2 q0 = *reinterpret_cast<const uint2*>(Qt + d * kTP + 4 * cgrp);
-        const uint2 q1 = *reinterpret_cast<const uint2*>(Qt + d * kTP + 16 + 4 * cgrp);
-        dvT[dt] = mfma16(u32x4{o0.x, o0.y, o1.x, o1.y}, pb, dvT[dt]);
-        dkT[dt] = mfma16(u32x4{q0.x, q0.y, q1.x, q1.y}, sb, dkT[dt]);
-      }
-      // dQ^T (dims 16w .. 16w+15 x 32 rows) = K^T dS^T over the block's 128 keys
-      f32x4 dq4[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        dq4[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r = 16 * nt + n;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(Kt + (16 * wave + n) * kKtP + 32 * ks + 8 * cgrp);
-          const u32x4 sbv = *reinterpret_cast<const u32x4*>(Ss + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
-          dq4[nt] = mfma16(ka, sbv, dq4[nt]);
-        }
-      }
-      // lane (row 16nt + n, group c) holds dims 16w + 4c .. +3 of that row
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int rr = r0 + 16 * nt + n;
-        int i, s;
-        bool ok;
-        src_entry(sc, ws, D, rr / G, i, s, ok);
-        if (ok && rr < rows_total) {
-          const int h = rr % G;
-          const float sc = D.scale;
-          uint16_t* dst = dq_part + ((((int64_t)bg * D.n_q + i) * (D.k + 1) + s) * G + h) * kHeadDim + 16 * wave +
-                          4 * cgrp;
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(dq4[nt][0] * sc, dq4[nt][1] * sc),
-                                                      pack_bf16x2(dq4[nt][2] * sc, dq4[nt][3] * sc));
-        }
-      }
-      __syncthreads();  // the chunk's LDS is free for the next one
+    for (int u = 0; u < 8; ++u) {
+      const int2 e = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)];
+      const int64_t li = ((int64_t)b * D.h_q + g * G + (e.y & 255)) * D.n_q + max(e.x, 0);
+      lse_raw[u] = lse[li];
+      dl_raw[u] = delta[li];
     }
   };
 
-  // the rows that gathered this block (one bin per query group), then its own positions
-  for (int qg = 0; qg < ws.n_groups; ++qg) {
-    const int bin = (bg * ws.n_groups + qg) * D.n_blk + t;
-    Src sc;
-    sc.kind = 0;
-    sc.tile0 = ws.tile_off[bin];
-    sc.n_entries = (ws.tile_off[bin + 1] - sc.tile0) * D.pt;
-    sc.pos0 = 0;
-    if (sc.n_entries > 0) run_source(sc);
+  if (nch > 0) {
+    load_rows(0);
+    stats(0);
+    store_rows();
   }
-  {
-    const int lo = max(t * kBk, (int)D.offset), hi = min((t + 1) * kBk, (int)(D.offset + D.n_q));
-    if (hi > lo) {
-      Src sc;
-      sc.kind = 1;
-      sc.tile0 = 0;
-      sc.n_entries = hi - lo;
-      sc.pos0 = lo;
-      run_source(sc);
+  for (int c = 0; c < nch; ++c) {
+    const int slot = c & (kRing - 1);
+    __syncthreads();  // chunk c's rows are in LDS; chunk c + 1's table is visible
+    float lse_c[8], dl_c[8];
+    int pos8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int2 e = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)];
+      const bool ok = e.x >= 0;
+      pos8[u] = ok ? (int)(D.offset + e.x) : -1;
+      lse_c[u] = ok ? lse_raw[u] * 1.4426950408889634f : __builtin_huge_valf();  // P = 0 for rows that do not exist
+      dl_c[u] = ok ? dl_raw[u] : 0.f;
     }
+    if (wave == 0) bld_step(bd, W, ws, D, c, lane);
+    // the next chunk's rows and statistics (past the last chunk the table holds
+    // empty rows, which read row 0: in bounds and unused)
+    load_rows((c + 1) & (kRing - 1));
+    stats((c + 1) & (kRing - 1));
+    // transposed copies: threads 0..127 take Q, 128..255 dO
+    if (threadIdx.x < 128)
+      transpose_rows32(Qs, Qt, threadIdx.x);
+    else if (threadIdx.x < 256)
+      transpose_rows32(Os, Ot, threadIdx.x - 128);
+    // S = Q K_w^T and dP = dO V_w^T, rows as M (two 16-row tiles)
+    f32x4 sc4[2], dp4[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sc4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * mt + n;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int sl = (4 * ks + cgrp) ^ (r & 15);
+        const u32x4 qa = *reinterpret_cast<const u32x4*>(Qs + r * 256 + 16 * sl);
+        const u32x4 oa = *reinterpret_cast<const u32x4*>(Os + r * 256 + 16 * sl);
+        sc4[mt] = mfma16(qa, kf[ks], sc4[mt]);
+        dp4[mt] = mfma16(oa, vf[ks], dp4[mt]);
+      }
+    }
+    // P and dS: accumulator u = 4 mt + e is row 16 mt + 4c + e, key 16w + n
+    float Pv[8], dS[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float sv = sc4[u >> 2][u & 3];
+      const bool vis = key_abs <= pos8[u] && key_abs < nkv;
+      const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -lse_c[u])) : 0.f;
+      Pv[u] = p;
+      dS[u] = p * (dp4[u >> 2][u & 3] - dl_c[u]);
+    }
+    const u32x4 pb = {pack_bf16x2(Pv[0], Pv[1]), pack_bf16x2(Pv[2], Pv[3]), pack_bf16x2(Pv[4], Pv[5]),
+                      pack_bf16x2(Pv[6], Pv[7])};
+    const u32x4 sb = {pack_bf16x2(dS[0], dS[1]), pack_bf16x2(dS[2], dS[3]), pack_bf16x2(dS[4], dS[5]),
+                      pack_bf16x2(dS[6], dS[7])};
+    // the chunk's dS for every wave: element (row, key 16w + n) at row * 256 + slot * 16 + 2 (key % 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = 16 * (u >> 2) + 4 * cgrp + (u & 3);
+      const int key = 16 * wave + n;
+      const int sl = (key >> 3) ^ (r & 15);
+      *reinterpret_cast<uint16_t*>(Ss + r * 256 + sl * 16 + 2 * (key & 7)) =
+          (uint16_t)((u & 1) ? (sb[u >> 1] >> 16) : (sb[u >> 1] & 0xFFFFu));
+    }
+    __syncthreads();  // transposes and dS are in LDS; the row buffers are free
+    // dV^T += dO^T P, dK^T += Q^T dS: M = head dims (8 tiles), K = the 32 rows
+    // (k-group c: rows 4c..4c+3 and 16+4c..16+4c+3), N = this wave's keys
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 16 * dt + n;
+      const uint2 o0 = *reinterpret_cast<const uint2*>(Ot + d * kTP + 4 * cgrp);
+      const uint2 o1 = *reinterpret_cast<const uint2*>(Ot + d * kTP + 16 + 4 * cgrp);
+      const uint2 q0 = *reinterpret_cast<const uint2*>(Qt + d * kTP + 4 * cgrp);
+      const uint2 q1 = *reinterpret_cast<const uint2*>(Qt + d * kTP + 16 + 4 * cgrp);
+      dvT[dt] = mfma16(u32x4{o0.x, o0.y, o1.x, o1.y}, pb, dvT[dt]);
+      dkT[dt] = mfma16(u32x4{q0.x, q0.y, q1.x, q1.y}, sb, dkT[dt]);
+    }
+    // dQ^T (dims 16w .. 16w+15 x 32 rows) = K^T dS^T over the block's 128 keys;
+    // lane (row 16nt + n, group c) holds dims 16w + 4c .. +3 of that row
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * nt + n;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(Kt + (16 * wave + n) * kKtP + 32 * ks + 8 * cgrp);
+        const u32x4 sbv = *reinterpret_cast<const u32x4*>(Ss + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
+        acc = mfma16(ka, sbv, acc);
+      }
+      const int2 e = W.row[slot][r];
+      if (e.x >= 0) {
+        const float sc = D.scale;
+        uint16_t* dst = dq_part + ((((int64_t)bg * D.n_q + e.x) * (D.k + 1) + (e.y >> 8)) * G + (e.y & 255)) * kHeadDim +
+                        16 * wave + 4 * cgrp;
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2(pack_bf16x2(acc[0] * sc, acc[1] * sc), pack_bf16x2(acc[2] * sc, acc[3] * sc));
+      }
+    }
+    store_rows();  // chunk c + 1's rows, read after the next barrier
   }
   // write this wave's keys: lane (key n, group c) holds dims 16dt + 4c .. +3
   if (key_abs < nkv) {
@@ -722,6 +836,7 @@ hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const ui
                                   const uint16_t* out, const float* lse, const uint16_t* dout, uint16_t* dq,
                                   uint16_t* dk, uint16_t* dv, const AttnWs& ws, uint16_t* dq_part, float* delta,
                                   const Dims& D, hipStream_t stream) {
+  if (ws.n_groups + 1 > kMaxSrc) return hipErrorInvalidValue;  // the walk's source table
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
   if (e != hipSuccess) return e;
   const int64_t pairs = (int64_t)D.B * D.n_q * D.h_q;
