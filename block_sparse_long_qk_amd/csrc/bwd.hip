@@ -71,39 +71,6 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const uint16_t* __restrict__ 
   }
 }
 
-// The rows of one source (a bin of the plan, or the block's own positions):
-// chunk row r (0..31) of chunk ch is flattened row 32 ch + r = entry * G + head.
-struct Src {
-  int kind;        // 0: plan bin, 1: the block's own positions
-  int tile0, n_entries;  // bin: first tile, entries (tiles * pt); own: -, positions
-  int pos0;        // own: first position
-};
-
-// Position, slot and validity of flattened entry e of a source.
-__device__ __forceinline__ void src_entry(const Src& sc, const AttnWs& ws, const Dims& D, int e, int& i, int& s,
-                                          bool& ok) {
-  if (sc.kind == 0) {
-    const int2 x = ws.list[(int64_t)sc.tile0 * D.pt + min(e, sc.n_entries - 1)];  // stays inside the bin's tiles
-    ok = e < sc.n_entries && x.x >= 0;
-    i = ok ? x.x / D.k : 0;
-    s = ok ? x.x % D.k : 0;
-  } else {
-    ok = e < sc.n_entries;
-    i = ok ? (int)(sc.pos0 + e - D.offset) : 0;
-    s = D.k;
-  }
-}
-
-// Fetch 32 rows (row r: 256 bytes at r * 256, chunk c in slot c ^ (r % 16)) by
-// direct global-to-LDS loads: wave w issues the 1-KB instruction for rows
-// 4w .. 4w+3; `rowp` is the row this lane's instruction row takes.
-__device__ __forceinline__ void fetch_rows32(unsigned char* dst, const uint16_t* rowp, int wave, int lane) {
-  const int r = 4 * wave + (lane >> 4);
-  const int c = (lane & 15) ^ (r & 15);
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(rowp + 8 * c),
-                                   (__attribute__((address_space(3))) void*)(dst + 1024 * wave), 16, 0, 0);
-}
-
 // ---------------------------------------------------------------- the chunk walk
 // The rows one workgroup walks for its (sequence, group, block): the plan's bin
 // of the block for each query group (its entries are compact: list indices
@@ -331,11 +298,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
   };
 
-  if (nch > 0) {
-    load_rows(0);
-    stats(0);
-    store_rows();
-  }
+  // (also without chunks: the table then holds empty rows, which read row 0,
+  // and every path reaches the loop with the fragment loads above complete)
+  load_rows(0);
+  stats(0);
+  store_rows();
   for (int c = 0; c < nch; ++c) {
     const int slot = c & (kRing - 1);
     __syncthreads();  // chunk c's rows are in LDS; chunk c + 1's table is visible
@@ -348,6 +315,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       pos8[u] = ok ? (int)(D.offset + e.x) : -1;
       lse_c[u] = ok ? lse_raw[u] * 1.4426950408889634f : __builtin_huge_valf();  // P = 0 for rows that do not exist
       dl_c[u] = ok ? dl_raw[u] : 0.f;
+      // formed here, before the next chunk's loads are issued (a later use
+      // would make its wait count those loads too)
+      asm volatile("" ::"v"(lse_c[u]), "v"(dl_c[u]) : "memory");
     }
     if (wave == 0) bld_step(bd, W, ws, D, c, lane);
     // the next chunk's rows and statistics (past the last chunk the table holds
@@ -498,34 +468,23 @@ __global__ __launch_bounds__(256) void k_bwd_dq_merge(const int32_t* __restrict_
 // accumulates per group in fp32 (a reduction over groups follows: the index
 // keys are shared), d_iq leaves as one bf16 partial per (row, slot).
 
-// Fetch 32 index-query rows of DIDX bf16 (row r at r * 2 DIDX bytes, chunk c in
-// slot c ^ (r % CPI)) by direct loads; `rowp` is the row this lane's
-// instruction row takes.
-template <int DIDX>
-__device__ __forceinline__ void fetch_iq32(unsigned char* dst, const uint16_t* rowp, int wave, int lane) {
-  constexpr int CPI = DIDX / 8, RPI = 64 / CPI, NI = 32 / RPI;  // instructions: 8 (128) or 4 (64)
-  if (wave < NI) {
-    const int r = RPI * wave + lane / CPI;
-    const int c = (lane % CPI) ^ (r % CPI);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(rowp + 8 * c),
-                                     (__attribute__((address_space(3))) void*)(dst + 1024 * wave), 16, 0, 0);
-  }
-}
-
 template <int DIDX, int G>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_kl_bwd(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ iq,
     const uint16_t* __restrict__ ik, const float* __restrict__ lse, const float* __restrict__ lse_index,
     const float* __restrict__ wrow, AttnWs ws, uint16_t* __restrict__ diq_part, float* __restrict__ dik_group,
     Dims D) {
-  constexpr int CPI = DIDX / 8;
+  constexpr int CPI = DIDX / 8;       // 16-byte pieces of an index row
+  constexpr int RPI = 64 / CPI;       // index rows per wave instruction
+  constexpr int NI = 32 / RPI;        // waves that carry the chunk's index rows
   constexpr int DT = DIDX / 16;       // 16-dim tiles of the index dim
   constexpr int IKS = DIDX / 32;      // k-steps of Z
-  __shared__ __align__(16) uint16_t IKt[DIDX * kKtP];              // index keys of the block, transposed
-  __shared__ __align__(16) unsigned char Qs[32 * 256];             // the chunk's query rows (swizzled)
-  __shared__ __align__(16) unsigned char IQs[32 * 2 * DIDX];       // each row's index-query row (swizzled)
-  __shared__ __align__(16) uint16_t IQt[DIDX * kTP];               // its transpose [d][row]
-  __shared__ __align__(16) unsigned char Ss[32 * 256];             // the chunk's g [row][key] (swizzled)
+  __shared__ __align__(16) uint16_t IKt[DIDX * kKtP];         // index keys of the block, transposed
+  __shared__ __align__(16) unsigned char Qs[32 * 256];        // the chunk's query rows (swizzled)
+  __shared__ __align__(16) unsigned char IQs[32 * 2 * DIDX];  // each row's index-query row (swizzled)
+  __shared__ __align__(16) uint16_t IQt[DIDX * kTP];          // its transpose [d][row]
+  __shared__ __align__(16) unsigned char Ss[32 * 256];        // the chunk's g [row][key] (swizzled)
+  __shared__ WalkTab W;
 
   const int nbg = D.B * D.h_kv;
   const int t = (int)(blockIdx.x / nbg);
@@ -537,6 +496,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int n_valid = max(1, min(kBk, nkv - t * kBk));
   const uint16_t* kblk = k + (((int64_t)b * D.h_kv + g) * nkv + (int64_t)t * kBk) * kHeadDim;
   const uint16_t* ikblk = ik + ((int64_t)b * nkv + (int64_t)t * kBk) * DIDX;
+
+  walk_setup(W, ws, D, bg, t);
+  const int nch = W.n_chunks;
+  Builder bd;
+  if (wave == 0) bld_prologue(bd, W, ws, D, lane);
 
   // the block's index keys transposed into LDS: task = 4 keys x 8 dims
   for (int task = threadIdx.x; task < 32 * CPI; task += kBwdThreads) {
@@ -568,174 +532,194 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const float c2 = D.scale_log2;
   constexpr float kL2e = 1.4426950408889634f;
   const int key_abs = t * kBk + 16 * wave + n;
+  const bool has_w = wrow != nullptr;
+  const float* wsrc = has_w ? wrow : lse_index;  // read either way; 1 is used without weights
+  __syncthreads();  // row tables of chunks 0 and 1 are written
 
-  auto run_source = [&](const Src& sc) {
-    const int rows_total = sc.n_entries * G;
-    for (int r0 = 0; r0 < rows_total; r0 += 32) {
-      {
-        // the rows this lane's fetch instructions take
-        const int rq = r0 + 4 * wave + (lane >> 4);
-        int i, s;
-        bool ok;
-        src_entry(sc, ws, D, rq / G, i, s, ok);
-        fetch_rows32(Qs, q + (((int64_t)b * D.n_q + i) * D.h_q + g * G + rq % G) * kHeadDim, wave, lane);
-        const int ri = r0 + (64 / CPI) * wave + lane / CPI;
-        src_entry(sc, ws, D, ri / G, i, s, ok);
-        fetch_iq32<DIDX>(IQs, iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX, wave, lane);
-      }
-      float lse2[8], lz2[8], wg[8];
-      int pos8[8];
-      bool first[8];
+  // A chunk's rows travel through registers, as in the main-branch backward:
+  // lane l of wave w carries 16 bytes of query row 4w + l / 16 and (waves
+  // below NI) of index row RPI w + l / CPI, stored at byte 1024 w + 16 l.
+  u32x4 q_next, iq_next;
+  auto load_rows = [&](int slot) {
+    {
+      const int r = 4 * wave + (lane >> 4);
+      const int2 e = W.row[slot][r];
+      const int i = max(e.x, 0), h = e.y & 255;
+      q_next = *reinterpret_cast<const u32x4*>(q + (((int64_t)b * D.n_q + i) * D.h_q + g * G + h) * kHeadDim +
+                                               8 * ((lane & 15) ^ (r & 15)));
+    }
+    if (wave < NI) {
+      const int r = RPI * wave + lane / CPI;
+      const int i = max(W.row[slot][r].x, 0);
+      iq_next = *reinterpret_cast<const u32x4*>(iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX +
+                                                8 * ((lane % CPI) ^ (r % CPI)));
+    }
+  };
+  auto store_rows = [&]() {
+    *reinterpret_cast<u32x4*>(Qs + 1024 * wave + 16 * lane) = q_next;
+    if (wave < NI) *reinterpret_cast<u32x4*>(IQs + 1024 * wave + 16 * lane) = iq_next;
+  };
+  // raw statistics of the next chunk (row 0's for rows that do not exist):
+  // the teacher's lse for each of the lane's 8 rows; the student's
+  // normaliser and the row weight for its rows 16 m + 4c (m = 0, 1), the only
+  // ones that can be a position's first head (G >= 4)
+  float lse_raw[8], lz_raw[2], w_raw[2];
+  auto stats = [&](int slot) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int rr = r0 + 16 * (u >> 2) + 4 * cgrp + (u & 3);
-        int i, s;
-        bool ok;
-        src_entry(sc, ws, D, rr / G, i, s, ok);
-        ok = ok && rr < rows_total;
-        const int h = rr % G;
-        lse2[u] = ok ? lse[((int64_t)b * D.h_q + g * G + h) * D.n_q + i] * kL2e : __builtin_huge_valf();
-        const int64_t prow = (int64_t)bg * D.n_q + i;
-        lz2[u] = ok ? lse_index[prow] * kL2e : __builtin_huge_valf();
-        wg[u] = ok ? (wrow ? wrow[prow] : 1.f) : 0.f;
-        pos8[u] = ok ? (int)(D.offset + i) : -1;
-        first[u] = ok && h == 0;
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      __syncthreads();  // the chunk's rows are in LDS
-      // IQ^T for the d_ik contraction: task = 4 rows x 8 dims
-      for (int task = threadIdx.x; task < 8 * CPI; task += kBwdThreads) {
-        const int rq = task / CPI, od = task % CPI;
-        u32x4 x[4];
+    for (int u = 0; u < 8; ++u) {
+      const int2 e = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)];
+      lse_raw[u] = lse[((int64_t)b * D.h_q + g * G + (e.y & 255)) * D.n_q + max(e.x, 0)];
+    }
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int r = 4 * rq + qq;
-          x[qq] = *reinterpret_cast<const u32x4*>(IQs + r * 2 * DIDX + 16 * (od ^ (r % CPI)));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int sh = (e & 1) * 16;
-          const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
-          const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
-          *reinterpret_cast<uint2*>(IQt + (od * 8 + e) * kTP + rq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
-        }
-      }
-      // S (teacher) and Z (student), rows as M
-      f32x4 sc4[2], z4[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        sc4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        z4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r = 16 * mt + n;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 qa = *reinterpret_cast<const u32x4*>(Qs + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
-          sc4[mt] = mfma16(qa, kf[ks], sc4[mt]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < IKS; ++ks) {
-          const u32x4 ia =
-              *reinterpret_cast<const u32x4*>(IQs + r * 2 * DIDX + 16 * ((4 * ks + cgrp) ^ (r % CPI)));
-          z4[mt] = mfma16(ia, ikf[ks], z4[mt]);
-        }
-      }
-      // teacher: the head average of each position (rows 16mt + 4c + e; the heads of
-      // a position sit in this lane's e and, for G >= 8, the lanes l ^ 16 and l ^ 32)
-      float tsum[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        float sacc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int u = 4 * mt + e;
-          const bool vis = key_abs <= pos8[u] && key_abs < nkv;
-          sacc += vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc4[mt][e], c2, -lse2[u])) : 0.f;
-        }
-        tsum[mt] = sacc;
-      }
-      if constexpr (G >= 8) {
-        tsum[0] += __shfl_xor(tsum[0], 16, 64);
-        tsum[1] += __shfl_xor(tsum[1], 16, 64);
-      }
-      if constexpr (G >= 16) {
-        tsum[0] += __shfl_xor(tsum[0], 32, 64);
-        tsum[1] += __shfl_xor(tsum[1], 32, 64);
-      }
-      if constexpr (G == 32) tsum[0] = tsum[1] = tsum[0] + tsum[1];
-      // g = w (s - t) on each position's first head row, 0 elsewhere
-      float gv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool vis = key_abs <= pos8[u] && key_abs < nkv;
-        const float sv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(z4[u >> 2][u & 3], kL2e, -lz2[u])) : 0.f;
-        const float tv = vis ? tsum[u >> 2] * (1.f / G) : 0.f;
-        gv[u] = first[u] ? wg[u] * (sv - tv) : 0.f;
-      }
-      const u32x4 gb = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]), pack_bf16x2(gv[4], gv[5]),
-                        pack_bf16x2(gv[6], gv[7])};
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int r = 16 * (u >> 2) + 4 * cgrp + (u & 3);
-        const int key = 16 * wave + n;
-        const int slot = (key >> 3) ^ (r & 15);
-        *reinterpret_cast<uint16_t*>(Ss + r * 256 + slot * 16 + 2 * (key & 7)) =
-            (uint16_t)((u & 1) ? (gb[u >> 1] >> 16) : (gb[u >> 1] & 0xFFFFu));
-      }
-      __syncthreads();  // IQ^T and g are in LDS
-      // d_ik^T += IQ^T g (M = index dims, K = the 32 rows, N = this wave's keys)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 16 * dt + n;
-        const uint2 a0 = *reinterpret_cast<const uint2*>(IQt + d * kTP + 4 * cgrp);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(IQt + d * kTP + 16 + 4 * cgrp);
-        dikT[dt] = mfma16(u32x4{a0.x, a0.y, a1.x, a1.y}, gb, dikT[dt]);
-      }
-      // d_iq^T (dims 16w .. 16w+15 x 32 rows) = IK^T g^T over the block's keys
-      if (wave < DT) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          const int r = 16 * nt + n;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const u32x4 ka = *reinterpret_cast<const u32x4*>(IKt + (16 * wave + n) * kKtP + 32 * ks + 8 * cgrp);
-            const u32x4 gbv = *reinterpret_cast<const u32x4*>(Ss + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
-            acc = mfma16(ka, gbv, acc);
-          }
-          const int rr = r0 + r;
-          int i, s;
-          bool ok;
-          src_entry(sc, ws, D, rr / G, i, s, ok);
-          if (ok && rr < rows_total && rr % G == 0) {
-            uint16_t* dst = diq_part + (((int64_t)bg * D.n_q + i) * (D.k + 1) + s) * DIDX + 16 * wave + 4 * cgrp;
-            *reinterpret_cast<uint2*>(dst) =
-                make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
-          }
-        }
-      }
-      __syncthreads();  // the chunk's LDS is free for the next one
+    for (int m = 0; m < 2; ++m) {
+      const int64_t prow = (int64_t)bg * D.n_q + max(W.row[slot][16 * m + 4 * cgrp].x, 0);
+      lz_raw[m] = lse_index[prow];
+      w_raw[m] = wsrc[prow];
     }
   };
 
-  for (int qg = 0; qg < ws.n_groups; ++qg) {
-    const int bin = (bg * ws.n_groups + qg) * D.n_blk + t;
-    Src sc;
-    sc.kind = 0;
-    sc.tile0 = ws.tile_off[bin];
-    sc.n_entries = (ws.tile_off[bin + 1] - sc.tile0) * D.pt;
-    sc.pos0 = 0;
-    if (sc.n_entries > 0) run_source(sc);
-  }
-  {
-    const int lo = max(t * kBk, (int)D.offset), hi = min((t + 1) * kBk, (int)(D.offset + D.n_q));
-    if (hi > lo) {
-      Src sc;
-      sc.kind = 1;
-      sc.tile0 = 0;
-      sc.n_entries = hi - lo;
-      sc.pos0 = lo;
-      run_source(sc);
+  // (also without chunks: the table then holds empty rows, which read row 0,
+  // and every path reaches the loop with the fragment loads above complete)
+  load_rows(0);
+  stats(0);
+  store_rows();
+  for (int c = 0; c < nch; ++c) {
+    const int slot = c & (kRing - 1);
+    __syncthreads();  // chunk c's rows are in LDS; chunk c + 1's table is visible
+    float lse2[8], lz2[2], wg[2];
+    int pos8[8];
+    bool first[2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int2 e = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)];
+      const bool ok = e.x >= 0;
+      pos8[u] = ok ? (int)(D.offset + e.x) : -1;
+      lse2[u] = ok ? lse_raw[u] * kL2e : __builtin_huge_valf();
     }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int2 e = W.row[slot][16 * m + 4 * cgrp];
+      first[m] = e.x >= 0 && (e.y & 255) == 0;
+      lz2[m] = lz_raw[m] * kL2e;
+      wg[m] = has_w ? w_raw[m] : 1.f;
+      asm volatile("" ::"v"(lz2[m]), "v"(wg[m]) : "memory");  // formed before the next chunk's loads
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) asm volatile("" ::"v"(lse2[u]) : "memory");
+    if (wave == 0) bld_step(bd, W, ws, D, c, lane);
+    load_rows((c + 1) & (kRing - 1));
+    stats((c + 1) & (kRing - 1));
+    // IQ^T for the d_ik contraction: task = 4 rows x 8 dims
+    for (int task = threadIdx.x; task < 8 * CPI; task += kBwdThreads) {
+      const int rq = task / CPI, od = task % CPI;
+      u32x4 x[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r = 4 * rq + qq;
+        x[qq] = *reinterpret_cast<const u32x4*>(IQs + r * 2 * DIDX + 16 * (od ^ (r % CPI)));
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
+        *reinterpret_cast<uint2*>(IQt + (od * 8 + e) * kTP + rq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+      }
+    }
+    // S (teacher) and Z (student), rows as M
+    f32x4 sc4[2], z4[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sc4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      z4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * mt + n;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 qa = *reinterpret_cast<const u32x4*>(Qs + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
+        sc4[mt] = mfma16(qa, kf[ks], sc4[mt]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < IKS; ++ks) {
+        const u32x4 ia =
+            *reinterpret_cast<const u32x4*>(IQs + r * 2 * DIDX + 16 * ((4 * ks + cgrp) ^ (r % CPI)));
+        z4[mt] = mfma16(ia, ikf[ks], z4[mt]);
+      }
+    }
+    // teacher: the head sum of each position (rows 16mt + 4c + e; the heads of
+    // a position sit in this lane's e and, for G >= 8, the lanes l ^ 16 and l ^ 32)
+    float tsum[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int u = 4 * mt + e;
+        const bool vis = key_abs <= pos8[u] && key_abs < nkv;
+        sacc += vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc4[mt][e], c2, -lse2[u])) : 0.f;
+      }
+      tsum[mt] = sacc;
+    }
+    if constexpr (G >= 8) {
+      tsum[0] += __shfl_xor(tsum[0], 16, 64);
+      tsum[1] += __shfl_xor(tsum[1], 16, 64);
+    }
+    if constexpr (G >= 16) {
+      tsum[0] += __shfl_xor(tsum[0], 32, 64);
+      tsum[1] += __shfl_xor(tsum[1], 32, 64);
+    }
+    if constexpr (G == 32) tsum[0] = tsum[1] = tsum[0] + tsum[1];
+    // g = w (s - t) on each position's first head row (e = 0 of tile m), 0 elsewhere
+    float gv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gv[u] = 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int u = 4 * m;
+      const bool vis = key_abs <= pos8[u] && key_abs < nkv;
+      const float sv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(z4[m][0], kL2e, -lz2[m])) : 0.f;
+      const float tv = vis ? tsum[m] * (1.f / G) : 0.f;
+      gv[u] = first[m] ? wg[m] * (sv - tv) : 0.f;
+    }
+    const u32x4 gb = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]), pack_bf16x2(gv[4], gv[5]),
+                      pack_bf16x2(gv[6], gv[7])};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = 16 * (u >> 2) + 4 * cgrp + (u & 3);
+      const int key = 16 * wave + n;
+      const int sl = (key >> 3) ^ (r & 15);
+      *reinterpret_cast<uint16_t*>(Ss + r * 256 + sl * 16 + 2 * (key & 7)) =
+          (uint16_t)((u & 1) ? (gb[u >> 1] >> 16) : (gb[u >> 1] & 0xFFFFu));
+    }
+    __syncthreads();  // IQ^T and g are in LDS; the row buffers are free
+    // d_ik^T += IQ^T g (M = index dims, K = the 32 rows, N = this wave's keys)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 16 * dt + n;
+      const uint2 a0 = *reinterpret_cast<const uint2*>(IQt + d * kTP + 4 * cgrp);
+      const uint2 a1 = *reinterpret_cast<const uint2*>(IQt + d * kTP + 16 + 4 * cgrp);
+      dikT[dt] = mfma16(u32x4{a0.x, a0.y, a1.x, a1.y}, gb, dikT[dt]);
+    }
+    // d_iq^T (dims 16w .. 16w+15 x 32 rows) = IK^T g^T over the block's keys
+    if (wave < DT) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * nt + n;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(IKt + (16 * wave + n) * kKtP + 32 * ks + 8 * cgrp);
+          const u32x4 gbv = *reinterpret_cast<const u32x4*>(Ss + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
+          acc = mfma16(ka, gbv, acc);
+        }
+        const int2 e = W.row[slot][r];
+        if (e.x >= 0 && (e.y & 255) == 0) {
+          uint16_t* dst = diq_part + (((int64_t)bg * D.n_q + e.x) * (D.k + 1) + (e.y >> 8)) * DIDX + 16 * wave +
+                          4 * cgrp;
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        }
+      }
+    }
+    store_rows();  // chunk c + 1's rows, read after the next barrier
   }
   // this group's share of d_ik for the wave's keys (fp32; the groups are added next)
   if (key_abs < nkv) {
@@ -807,6 +791,7 @@ hipError_t launch_index_kl_bwd(const uint16_t* q, const uint16_t* k, const uint1
                                const int32_t* block_idx, const float* lse, const float* lse_index, const float* wrow,
                                uint16_t* d_index_q, uint16_t* d_index_k, const AttnWs& ws, uint16_t* diq_part,
                                float* dik_group, const Dims& D, hipStream_t stream) {
+  if (ws.n_groups + 1 > kMaxSrc) return hipErrorInvalidValue;  // the walk's source table
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((int64_t)D.B * D.h_kv * D.n_blk)), block(kBwdThreads);
