@@ -78,14 +78,20 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const uint16_t* __restrict__ 
 // flattened row R of a source = entry * G + head.  The walk is pipelined: a
 // chunk's row table (query row, slot, head of each of its 32 rows) is written
 // to LDS two chunks ahead, from list entries loaded one iteration before, so
-// every lane can address the next chunk's rows right after a barrier.
+// every lane can address the next chunk's rows right after a barrier.  The
+// table holds ready offsets (one lane per row computes them once), so the
+// lanes that use a row do no index arithmetic of their own.
 constexpr int kMaxSrc = 260;  // query groups per (b, g) + 1 (n_kv <= 2M: at most 256 groups)
 constexpr int kRing = 4;      // row tables in flight: the chunk computed, the one fetched, the one built
 
 struct WalkTab {
   int nent[kMaxSrc];    // entries (positions) of each source
   int base[kMaxSrc];    // bin: first list index; own positions: the first position
-  int2 row[kRing][32];  // per chunk row: (query row i, or -1 for none; slot * 256 + head)
+  // per chunk row, for query row i of head h at slot s: {position (-1: no row),
+  // lse index within the sequence (g G + h) n_q + i, query row within the
+  // sequence i h_q + g G + h, h}; an empty row reads row 0 of head 0
+  int4 row[kRing][32];
+  int64_t part[kRing][32];  // partial offset ((b h_kv + g) n_q + i)(k + 1) + s) rs_mul + h h_mul
   int n_chunks;
 };
 
@@ -146,12 +152,33 @@ __device__ __forceinline__ void bld_load(Builder& bd, const WalkTab& W, const At
   bd.h = R % G;
 }
 
-__device__ __forceinline__ void bld_write(const Builder& bd, WalkTab& W, int slot, const Dims& D, int lane) {
+// What a kernel's partial offsets are made of: ((bg n_q + i)(k + 1) + s) rs_mul + h h_mul.
+struct PartMul {
+  int64_t rs;
+  int h;
+};
+
+__device__ __forceinline__ void bld_write(const Builder& bd, WalkTab& W, int slot, const Dims& D, int bg,
+                                          PartMul pm, int lane) {
   if (lane < 32) {
-    int2 e = make_int2(-1, 0);
-    if (bd.kind == 2) e = make_int2((int)(bd.pos - D.offset), D.k * 256 + bd.h);
-    if (bd.kind == 1 && bd.x >= 0) e = make_int2(bd.x / D.k, (bd.x % D.k) * 256 + bd.h);
+    const int g = bg % D.h_kv;
+    int i = -1, sl = 0;
+    if (bd.kind == 2) {
+      i = (int)(bd.pos - D.offset);
+      sl = D.k;
+    }
+    if (bd.kind == 1 && bd.x >= 0) {
+      i = bd.x / D.k;
+      sl = bd.x % D.k;
+    }
+    int4 e = make_int4(-1, 0, 0, 0);
+    int64_t off = 0;
+    if (i >= 0) {
+      e = make_int4((int)(D.offset + i), (g * D.G + bd.h) * D.n_q + i, i * D.h_q + g * D.G + bd.h, bd.h);
+      off = (((int64_t)bg * D.n_q + i) * (D.k + 1) + sl) * pm.rs + (int64_t)bd.h * pm.h;
+    }
     W.row[slot][lane] = e;
+    W.part[slot][lane] = off;
   }
 }
 
@@ -161,46 +188,52 @@ __device__ __forceinline__ void bld_next(Builder& bd, const WalkTab& W, int G, i
 }
 
 // Tables of chunks 0 and 1 written, chunk 2's entries pending (wave 0 only).
-__device__ __forceinline__ void bld_prologue(Builder& bd, WalkTab& W, const AttnWs& ws, const Dims& D, int lane) {
+__device__ __forceinline__ void bld_prologue(Builder& bd, WalkTab& W, const AttnWs& ws, const Dims& D, int bg,
+                                             PartMul pm, int lane) {
   const int n_src = ws.n_groups + 1;
   bd.src = 0;
   bd.r0 = 0;
   bld_skip(bd, W, D.G, n_src);
   bld_load(bd, W, ws, D.G, n_src, lane);
-  bld_write(bd, W, 0, D, lane);
+  bld_write(bd, W, 0, D, bg, pm, lane);
   bld_next(bd, W, D.G, n_src);
   bld_load(bd, W, ws, D.G, n_src, lane);
-  bld_write(bd, W, 1, D, lane);
+  bld_write(bd, W, 1, D, bg, pm, lane);
   bld_next(bd, W, D.G, n_src);
   bld_load(bd, W, ws, D.G, n_src, lane);
 }
 
 // One iteration of the builder: chunk c + 2's table from the pending entries,
 // then chunk c + 3's entries loaded.
-__device__ __forceinline__ void bld_step(Builder& bd, WalkTab& W, const AttnWs& ws, const Dims& D, int c, int lane) {
+__device__ __forceinline__ void bld_step(Builder& bd, WalkTab& W, const AttnWs& ws, const Dims& D, int bg,
+                                         PartMul pm, int c, int lane) {
   const int n_src = ws.n_groups + 1;
-  bld_write(bd, W, (c + 2) & (kRing - 1), D, lane);
+  bld_write(bd, W, (c + 2) & (kRing - 1), D, bg, pm, lane);
   bld_next(bd, W, D.G, n_src);
   bld_load(bd, W, ws, D.G, n_src, lane);
 }
 
-// dst[d][row] (pitch kTP) = src rows (32 x 128 bf16, swizzled): task (0..127)
-// handles rows 4 (task / 16) .. +3, dims 8 (task % 16) .. +7.
-__device__ __forceinline__ void transpose_rows32(const unsigned char* src, uint16_t* dst, int task) {
-  const int rq = task >> 4, od = task & 15;
-  u32x4 x[4];
+// Transposed chunk copies [d][row] (pitch kTP) with the 4-row quads of dim d
+// XOR-swizzled by (d / 8) % 8: element (d, r) at d kTP + 4 ((r / 4) ^ ((d / 8) % 8)) + r % 4.
+// Writing a lane's 8 dims of one row then spreads over the banks, and the
+// 8-byte reads of an MFMA operand (quads c and 4 + c of dim d) stay conflict free.
+__device__ __forceinline__ int tp_at(int d, int r) { return d * kTP + 4 * ((r >> 2) ^ ((d >> 3) & 7)) + (r & 3); }
+
+// dims 8p .. 8p+7 of row r (one 16-byte register piece) into a transposed copy
+__device__ __forceinline__ void tp_store8(uint16_t* dst, u32x4 v, int p, int r) {
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    const int r = 4 * rq + qq;
-    x[qq] = *reinterpret_cast<const u32x4*>(src + r * 256 + 16 * (od ^ (r & 15)));
+  for (int j = 0; j < 4; ++j) {
+    dst[tp_at(8 * p + 2 * j, r)] = (uint16_t)(v[j] & 0xFFFFu);
+    dst[tp_at(8 * p + 2 * j + 1, r)] = (uint16_t)(v[j] >> 16);
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int sh = (e & 1) * 16;
-    const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
-    const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
-    *reinterpret_cast<uint2*>(dst + (od * 8 + e) * kTP + rq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
-  }
+}
+
+// the MFMA operand of dim d: rows 4c .. 4c+3 and 16+4c .. 16+4c+3
+__device__ __forceinline__ u32x4 tp_operand(const uint16_t* src, int d, int c) {
+  const int sw = (d >> 3) & 7;
+  const uint2 a = *reinterpret_cast<const uint2*>(src + d * kTP + 4 * (c ^ sw));
+  const uint2 b = *reinterpret_cast<const uint2*>(src + d * kTP + 4 * ((4 + c) ^ sw));
+  return u32x4{a.x, a.y, b.x, b.y};
 }
 
 template <bool VL>
@@ -230,7 +263,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   walk_setup(W, ws, D, bg, t);
   const int nch = W.n_chunks;
   Builder bd;
-  if (wave == 0) bld_prologue(bd, W, ws, D, lane);
+  const PartMul pm{(int64_t)G * kHeadDim, kHeadDim};  // dq partial of (row, slot, head)
+  if (wave == 0) bld_prologue(bd, W, ws, D, bg, pm, lane);
 
   // K^T of the block into LDS (keys past the cache repeat the last one)
   {
@@ -268,22 +302,31 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int key_abs = t * kBk + 16 * wave + n;  // this lane's key (B-operand column)
   __syncthreads();  // row tables of chunks 0 and 1 are written
 
+  // this sequence's rows of Q, dO and their statistics
+  const uint16_t* qb = q + (int64_t)b * D.n_q * D.h_q * kHeadDim;
+  const uint16_t* ob = dout + (int64_t)b * D.n_q * D.h_q * kHeadDim;
+  const float* lseb = lse + (int64_t)b * D.h_q * D.n_q;
+  const float* dlb = delta + (int64_t)b * D.h_q * D.n_q;
+
   // A chunk's rows travel through registers: lane l of wave w loads 16 bytes
-  // of row r = 4w + l / 16 (its 16-byte piece (l % 16) ^ (r % 16)) and stores
-  // them at byte 1024 w + 16 l of the row buffer, so row r's piece p sits in
-  // slot p ^ (r % 16).
+  // of row r = 4w + l / 16, its piece p = (l % 16) ^ (r % 16) (dims 8p .. 8p+7),
+  // and stores them at byte 1024 w + 16 l of the row buffer (so row r's piece
+  // p sits in slot p ^ (r % 16)) and, element by element, into the transposes.
+  const int my_r = 4 * wave + (lane >> 4);
+  const int my_p = (lane & 15) ^ (my_r & 15);
   u32x4 q_next, o_next;
   auto load_rows = [&](int slot) {
-    const int2 e = W.row[slot][4 * wave + (lane >> 4)];
-    const int r = 4 * wave + (lane >> 4);
-    const int i = max(e.x, 0), h = e.y & 255;
-    const int64_t qrow = (((int64_t)b * D.n_q + i) * D.h_q + g * G + h) * kHeadDim + 8 * ((lane & 15) ^ (r & 15));
-    q_next = *reinterpret_cast<const u32x4*>(q + qrow);
-    o_next = *reinterpret_cast<const u32x4*>(dout + qrow);
+    const int64_t qrow = (int64_t)W.row[slot][my_r].z * kHeadDim + 8 * my_p;
+    q_next = *reinterpret_cast<const u32x4*>(qb + qrow);
+    o_next = *reinterpret_cast<const u32x4*>(ob + qrow);
   };
   auto store_rows = [&]() {
     *reinterpret_cast<u32x4*>(Qs + 1024 * wave + 16 * lane) = q_next;
     *reinterpret_cast<u32x4*>(Os + 1024 * wave + 16 * lane) = o_next;
+  };
+  auto store_transposes = [&]() {
+    tp_store8(Qt, q_next, my_p, my_r);
+    tp_store8(Ot, o_next, my_p, my_r);
   };
   // raw lse and delta of the next chunk's rows (row 0's for rows that do not
   // exist), first used in the next iteration
@@ -291,10 +334,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   auto stats = [&](int slot) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int2 e = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)];
-      const int64_t li = ((int64_t)b * D.h_q + g * G + (e.y & 255)) * D.n_q + max(e.x, 0);
-      lse_raw[u] = lse[li];
-      dl_raw[u] = delta[li];
+      const int so = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)].y;
+      lse_raw[u] = lseb[so];
+      dl_raw[u] = dlb[so];
     }
   };
 
@@ -306,29 +348,27 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   for (int c = 0; c < nch; ++c) {
     const int slot = c & (kRing - 1);
     __syncthreads();  // chunk c's rows are in LDS; chunk c + 1's table is visible
+    // chunk c's transposes, from the registers that still hold its rows (the
+    // previous chunk's were last read before the barrier above)
+    store_transposes();
     float lse_c[8], dl_c[8];
     int pos8[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int2 e = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)];
-      const bool ok = e.x >= 0;
-      pos8[u] = ok ? (int)(D.offset + e.x) : -1;
+      const int pos = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)].x;
+      const bool ok = pos >= 0;
+      pos8[u] = pos;
       lse_c[u] = ok ? lse_raw[u] * 1.4426950408889634f : __builtin_huge_valf();  // P = 0 for rows that do not exist
       dl_c[u] = ok ? dl_raw[u] : 0.f;
       // formed here, before the next chunk's loads are issued (a later use
       // would make its wait count those loads too)
       asm volatile("" ::"v"(lse_c[u]), "v"(dl_c[u]) : "memory");
     }
-    if (wave == 0) bld_step(bd, W, ws, D, c, lane);
+    if (wave == 0) bld_step(bd, W, ws, D, bg, pm, c, lane);
     // the next chunk's rows and statistics (past the last chunk the table holds
     // empty rows, which read row 0: in bounds and unused)
     load_rows((c + 1) & (kRing - 1));
     stats((c + 1) & (kRing - 1));
-    // transposed copies: threads 0..127 take Q, 128..255 dO
-    if (threadIdx.x < 128)
-      transpose_rows32(Qs, Qt, threadIdx.x);
-    else if (threadIdx.x < 256)
-      transpose_rows32(Os, Ot, threadIdx.x - 128);
     // S = Q K_w^T and dP = dO V_w^T, rows as M (two 16-row tiles)
     f32x4 sc4[2], dp4[2];
 #pragma unroll
@@ -374,12 +414,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const int d = 16 * dt + n;
-      const uint2 o0 = *reinterpret_cast<const uint2*>(Ot + d * kTP + 4 * cgrp);
-      const uint2 o1 = *reinterpret_cast<const uint2*>(Ot + d * kTP + 16 + 4 * cgrp);
-      const uint2 q0 = *reinterpret_cast<const uint2*>(Qt + d * kTP + 4 * cgrp);
-      const uint2 q1 = *reinterpret_cast<const uint2*>(Qt + d * kTP + 16 + 4 * cgrp);
-      dvT[dt] = mfma16(u32x4{o0.x, o0.y, o1.x, o1.y}, pb, dvT[dt]);
-      dkT[dt] = mfma16(u32x4{q0.x, q0.y, q1.x, q1.y}, sb, dkT[dt]);
+      dvT[dt] = mfma16(tp_operand(Ot, d, cgrp), pb, dvT[dt]);
+      dkT[dt] = mfma16(tp_operand(Qt, d, cgrp), sb, dkT[dt]);
     }
     // dQ^T (dims 16w .. 16w+15 x 32 rows) = K^T dS^T over the block's 128 keys;
     // lane (row 16nt + n, group c) holds dims 16w + 4c .. +3 of that row
@@ -393,11 +429,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
         const u32x4 sbv = *reinterpret_cast<const u32x4*>(Ss + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
         acc = mfma16(ka, sbv, acc);
       }
-      const int2 e = W.row[slot][r];
-      if (e.x >= 0) {
+      if (W.row[slot][r].x >= 0) {
         const float sc = D.scale;
-        uint16_t* dst = dq_part + ((((int64_t)bg * D.n_q + e.x) * (D.k + 1) + (e.y >> 8)) * G + (e.y & 255)) * kHeadDim +
-                        16 * wave + 4 * cgrp;
+        uint16_t* dst = dq_part + W.part[slot][r] + 16 * wave + 4 * cgrp;
         *reinterpret_cast<uint2*>(dst) =
             make_uint2(pack_bf16x2(acc[0] * sc, acc[1] * sc), pack_bf16x2(acc[2] * sc, acc[3] * sc));
       }
@@ -500,7 +534,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   walk_setup(W, ws, D, bg, t);
   const int nch = W.n_chunks;
   Builder bd;
-  if (wave == 0) bld_prologue(bd, W, ws, D, lane);
+  const PartMul pm{DIDX, 0};  // d_iq partial of (row, slot)
+  if (wave == 0) bld_prologue(bd, W, ws, D, bg, pm, lane);
 
   // the block's index keys transposed into LDS: task = 4 keys x 8 dims
   for (int task = threadIdx.x; task < 32 * CPI; task += kBwdThreads) {
@@ -536,23 +571,27 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const float* wsrc = has_w ? wrow : lse_index;  // read either way; 1 is used without weights
   __syncthreads();  // row tables of chunks 0 and 1 are written
 
+  // this sequence's rows and statistics
+  const uint16_t* qb = q + (int64_t)b * D.n_q * D.h_q * kHeadDim;
+  const uint16_t* iqb = iq + ((int64_t)b * D.n_q * D.h_kv + g) * DIDX;
+  const float* lseb = lse + (int64_t)b * D.h_q * D.n_q;
+  const float* lzb = lse_index + (int64_t)bg * D.n_q;
+  const float* wb = wsrc + (int64_t)bg * D.n_q;
+
   // A chunk's rows travel through registers, as in the main-branch backward:
   // lane l of wave w carries 16 bytes of query row 4w + l / 16 and (waves
-  // below NI) of index row RPI w + l / CPI, stored at byte 1024 w + 16 l.
+  // below NI) piece p of index row RPI w + l / CPI, stored at byte 1024 w + 16 l
+  // and, element by element, into the index rows' transpose.
+  const int my_r = 4 * wave + (lane >> 4);
+  const int my_ri = RPI * wave + lane / CPI;
+  const int my_pi = (lane % CPI) ^ (my_ri % CPI);
   u32x4 q_next, iq_next;
   auto load_rows = [&](int slot) {
-    {
-      const int r = 4 * wave + (lane >> 4);
-      const int2 e = W.row[slot][r];
-      const int i = max(e.x, 0), h = e.y & 255;
-      q_next = *reinterpret_cast<const u32x4*>(q + (((int64_t)b * D.n_q + i) * D.h_q + g * G + h) * kHeadDim +
-                                               8 * ((lane & 15) ^ (r & 15)));
-    }
+    q_next = *reinterpret_cast<const u32x4*>(qb + (int64_t)W.row[slot][my_r].z * kHeadDim +
+                                             8 * ((lane & 15) ^ (my_r & 15)));
     if (wave < NI) {
-      const int r = RPI * wave + lane / CPI;
-      const int i = max(W.row[slot][r].x, 0);
-      iq_next = *reinterpret_cast<const u32x4*>(iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX +
-                                                8 * ((lane % CPI) ^ (r % CPI)));
+      const int i = max(W.row[slot][my_ri].x - (int)D.offset, 0);
+      iq_next = *reinterpret_cast<const u32x4*>(iqb + (int64_t)i * D.h_kv * DIDX + 8 * my_pi);
     }
   };
   auto store_rows = [&]() {
@@ -566,15 +605,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   float lse_raw[8], lz_raw[2], w_raw[2];
   auto stats = [&](int slot) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int2 e = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)];
-      lse_raw[u] = lse[((int64_t)b * D.h_q + g * G + (e.y & 255)) * D.n_q + max(e.x, 0)];
-    }
+    for (int u = 0; u < 8; ++u) lse_raw[u] = lseb[W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)].y];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const int64_t prow = (int64_t)bg * D.n_q + max(W.row[slot][16 * m + 4 * cgrp].x, 0);
-      lz_raw[m] = lse_index[prow];
-      w_raw[m] = wsrc[prow];
+      const int i = max(W.row[slot][16 * m + 4 * cgrp].x - (int)D.offset, 0);
+      lz_raw[m] = lzb[i];
+      w_raw[m] = wb[i];
     }
   };
 
@@ -586,46 +622,30 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   for (int c = 0; c < nch; ++c) {
     const int slot = c & (kRing - 1);
     __syncthreads();  // chunk c's rows are in LDS; chunk c + 1's table is visible
+    // chunk c's index-row transpose, from the registers that still hold its rows
+    if (wave < NI) tp_store8(IQt, iq_next, my_pi, my_ri);
     float lse2[8], lz2[2], wg[2];
     int pos8[8];
     bool first[2];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int2 e = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)];
-      const bool ok = e.x >= 0;
-      pos8[u] = ok ? (int)(D.offset + e.x) : -1;
-      lse2[u] = ok ? lse_raw[u] * kL2e : __builtin_huge_valf();
+      const int pos = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)].x;
+      pos8[u] = pos;
+      lse2[u] = pos >= 0 ? lse_raw[u] * kL2e : __builtin_huge_valf();
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const int2 e = W.row[slot][16 * m + 4 * cgrp];
-      first[m] = e.x >= 0 && (e.y & 255) == 0;
+      const int4 e = W.row[slot][16 * m + 4 * cgrp];
+      first[m] = e.x >= 0 && e.w == 0;
       lz2[m] = lz_raw[m] * kL2e;
       wg[m] = has_w ? w_raw[m] : 1.f;
       asm volatile("" ::"v"(lz2[m]), "v"(wg[m]) : "memory");  // formed before the next chunk's loads
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) asm volatile("" ::"v"(lse2[u]) : "memory");
-    if (wave == 0) bld_step(bd, W, ws, D, c, lane);
+    if (wave == 0) bld_step(bd, W, ws, D, bg, pm, c, lane);
     load_rows((c + 1) & (kRing - 1));
     stats((c + 1) & (kRing - 1));
-    // IQ^T for the d_ik contraction: task = 4 rows x 8 dims
-    for (int task = threadIdx.x; task < 8 * CPI; task += kBwdThreads) {
-      const int rq = task / CPI, od = task % CPI;
-      u32x4 x[4];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int r = 4 * rq + qq;
-        x[qq] = *reinterpret_cast<const u32x4*>(IQs + r * 2 * DIDX + 16 * (od ^ (r % CPI)));
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
-        *reinterpret_cast<uint2*>(IQt + (od * 8 + e) * kTP + rq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
-      }
-    }
     // S (teacher) and Z (student), rows as M
     f32x4 sc4[2], z4[2];
 #pragma unroll
@@ -693,12 +713,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     __syncthreads();  // IQ^T and g are in LDS; the row buffers are free
     // d_ik^T += IQ^T g (M = index dims, K = the 32 rows, N = this wave's keys)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 16 * dt + n;
-      const uint2 a0 = *reinterpret_cast<const uint2*>(IQt + d * kTP + 4 * cgrp);
-      const uint2 a1 = *reinterpret_cast<const uint2*>(IQt + d * kTP + 16 + 4 * cgrp);
-      dikT[dt] = mfma16(u32x4{a0.x, a0.y, a1.x, a1.y}, gb, dikT[dt]);
-    }
+    for (int dt = 0; dt < DT; ++dt) dikT[dt] = mfma16(tp_operand(IQt, 16 * dt + n, cgrp), gb, dikT[dt]);
     // d_iq^T (dims 16w .. 16w+15 x 32 rows) = IK^T g^T over the block's keys
     if (wave < DT) {
 #pragma unroll
@@ -711,10 +726,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
           const u32x4 gbv = *reinterpret_cast<const u32x4*>(Ss + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
           acc = mfma16(ka, gbv, acc);
         }
-        const int2 e = W.row[slot][r];
-        if (e.x >= 0 && (e.y & 255) == 0) {
-          uint16_t* dst = diq_part + (((int64_t)bg * D.n_q + e.x) * (D.k + 1) + (e.y >> 8)) * DIDX + 16 * wave +
-                          4 * cgrp;
+        const int4 e = W.row[slot][r];
+        if (e.x >= 0 && e.w == 0) {
+          uint16_t* dst = diq_part + W.part[slot][r] + 16 * wave + 4 * cgrp;
           *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
         }
       }

@@ -197,8 +197,9 @@ msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, cons
  * the same block_idx.  d_index_q and d_index_k have index_q's and index_k's
  * layouts (bf16, overwritten; keys no row reaches get 0).  Same support as
  * msa_index_kl; needs workspace of msa_workspace_size(p, MSA_OP_INDEX_KL_BWD).
- * Reduced in a fixed order (one workgroup per (sequence, group, block), then
- * the groups in order), so the result is deterministic.
+ * Reduced without atomics (one workgroup per (sequence, group, block), then
+ * the groups in order), over rows in the gather plan's order, which may vary
+ * from run to run within a block: results can differ in the last bits.
  */
 msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, const void* index_q,
                             const void* index_k, const int32_t* block_idx, const float* lse, const float* lse_index,
@@ -218,8 +219,9 @@ msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, 
  * out and lse are the forward's outputs for the same inputs; dq has q's layout,
  * dk and dv k's (bf16, overwritten; keys no row attends get 0).  Needs
  * workspace of msa_workspace_size(p, MSA_OP_SPARSE_ATTN_BWD); uniform batches.
- * dk and dv are reduced in a fixed order (one workgroup per block), so the
- * result is deterministic.
+ * dk and dv are reduced without atomics (one workgroup owns each block), in
+ * the order of the gather plan, whose rows within one block's bin may come in
+ * a different order from run to run: results can differ in the last bits.
  */
 msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* k, const void* v,
                                const int32_t* block_idx, const void* out, const float* lse, const void* dout, void* dq,
