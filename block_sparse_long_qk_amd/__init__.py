@@ -42,15 +42,16 @@ class Problem(ctypes.Structure):
         ("q_offset", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float),
         ("index_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, batch, n_q, n_kv, h_q, h_kv, head_dim=128, index_dim=128, block_size=128, topk=16,
-             q_offset=-1, softmax_scale=None, index_dtype=DTYPE_BF16):
+             q_offset=-1, softmax_scale=None, index_dtype=DTYPE_BF16, kv_dtype=DTYPE_BF16):
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(head_dim)
         return cls(batch, n_q, n_kv, h_q, h_kv, head_dim, index_dim, block_size, topk, q_offset, softmax_scale,
-                   index_dtype)
+                   index_dtype, kv_dtype)
 
     @property
     def offset(self) -> int:

@@ -2,6 +2,7 @@
 // dispatch.  Every check runs on the host before any HIP call, so a rejected
 // call enqueues nothing.
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 
 #include "../../include/msa.h"
@@ -28,6 +29,7 @@ msa_status derive(const msa_problem* p, Dims* D) {
   if (offset < 0 || offset + p->n_q > p->n_kv) return MSA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(p->softmax_scale)) return MSA_ERR_INVALID_ARGUMENT;
   if (p->index_dtype != MSA_DTYPE_BF16 && p->index_dtype != MSA_DTYPE_FP8_E4M3) return MSA_ERR_INVALID_ARGUMENT;
+  if (p->kv_dtype != MSA_DTYPE_BF16 && p->kv_dtype != MSA_DTYPE_FP8_E4M3) return MSA_ERR_INVALID_ARGUMENT;
   const int64_t G = p->h_q / p->h_kv;
   const int64_t n_blk = ((int64_t)p->n_kv + p->block_size - 1) / p->block_size;
   // index ranges the kernels keep in 32 bits
@@ -58,6 +60,7 @@ msa_status derive(const msa_problem* p, Dims* D) {
   D->d = p->head_dim;
   D->d_idx = p->index_dim;
   D->idx_eb = p->index_dtype == MSA_DTYPE_FP8_E4M3 ? 1 : 2;
+  D->kv_eb = p->kv_dtype == MSA_DTYPE_FP8_E4M3 ? 1 : 2;
   D->k = p->topk;
   D->n_blk = (int32_t)n_blk;
   D->pt = pt;
@@ -137,14 +140,12 @@ size_t attn_bytes(const Dims& D) {
 hipError_t run_attention(const Dims& D, const void* q, const void* k, const void* v, const int32_t* block_idx,
                          void* out, float* lse, char* ws_base, hipStream_t stream) {
   auto q16 = static_cast<const uint16_t*>(q);
-  auto k16 = static_cast<const uint16_t*>(k);
-  auto v16 = static_cast<const uint16_t*>(v);
   auto o16 = static_cast<uint16_t*>(out);
   if (msa::use_attn_rows(D))
-    return msa::launch_attn_rows(q16, k16, v16, block_idx, o16, lse, reinterpret_cast<float*>(ws_base), D, stream);
+    return msa::launch_attn_rows(q16, k, v, block_idx, o16, lse, reinterpret_cast<float*>(ws_base), D, stream);
   AttnWs ws;
   attn_ws_layout(D, ws_base, &ws);
-  return msa::launch_sparse_attn(q16, k16, v16, block_idx, o16, lse, ws, D, stream);
+  return msa::launch_sparse_attn(q16, k, v, block_idx, o16, lse, ws, D, stream);
 }
 
 hipError_t run_index(const Dims& D, const void* index_q, const void* index_k, float* pooled, hipStream_t stream) {
@@ -183,6 +184,10 @@ msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_
 
 }  // namespace
 
+static_assert(sizeof(msa_problem) == 64 && offsetof(msa_problem, index_dtype) == 52 &&
+                  offsetof(msa_problem, kv_dtype) == 56,
+              "msa_problem layout is part of the ABI");
+
 extern "C" {
 
 msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
@@ -204,7 +209,7 @@ msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
       *bytes = pooled_bytes(D) + attn_bytes(D);
       return MSA_OK;
     case MSA_OP_SPARSE_ATTN_BWD:
-      if (D.n_blk > msa::kMaxPlanBlocks) return MSA_ERR_UNSUPPORTED;
+      if (D.n_blk > msa::kMaxPlanBlocks || D.kv_eb != 2) return MSA_ERR_UNSUPPORTED;
       *bytes = bwd_bytes(D);
       return MSA_OK;
     case MSA_OP_INDEX_KL:
@@ -339,7 +344,7 @@ msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* 
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       !aligned16(workspace))
     return MSA_ERR_INVALID_ARGUMENT;
-  if (D.n_blk > msa::kMaxPlanBlocks) return MSA_ERR_UNSUPPORTED;
+  if (D.n_blk > msa::kMaxPlanBlocks || D.kv_eb != 2) return MSA_ERR_UNSUPPORTED;
   if (bwd_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
   AttnWs ws;
   char* base = static_cast<char*>(workspace);
@@ -360,6 +365,7 @@ msa_status msa_dense_attn_fwd(const msa_problem* p, const void* q, const void* k
   if (!q || !k || !v || !out) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)))
     return MSA_ERR_INVALID_ARGUMENT;
+  if (D.kv_eb != 2) return MSA_ERR_UNSUPPORTED;
   return hip_status(msa::launch_dense_attn(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                            static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, D,
                                            stream));

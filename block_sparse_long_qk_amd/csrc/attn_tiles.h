@@ -88,6 +88,64 @@ __device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint1
   }
 }
 
+// stage_kv for FP8 E4M3 K and V (1 byte per element, same row layout): the
+// same LDS content, each element widened to bf16 between the load and the
+// store.  K: 16-byte pieces (16 dims), two per thread; V: 4 keys x 8 dims per
+// thread, written transposed as above.
+__device__ __forceinline__ void stage_kv8(uint16_t* Ks, uint16_t* Vt, const unsigned char* __restrict__ kb,
+                                          const unsigned char* __restrict__ vb, int n_valid) {
+  constexpr int KPER = 1024 / kThreads, VPER = 512 / kThreads;
+  const int tid = threadIdx.x;
+  uint4 kr[KPER];
+  uint2 vr[4 * VPER];
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    const int c = tid + kThreads * u;
+    const int key = min(c >> 3, n_valid - 1), oc = c & 7;
+    kr[u] = *reinterpret_cast<const uint4*>(kb + key * kHeadDim + oc * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < VPER; ++u) {
+    const int c = tid + kThreads * u;
+    const int kq = c >> 4, od = c & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      vr[4 * u + q] = *reinterpret_cast<const uint2*>(vb + min(kq * 4 + q, n_valid - 1) * kHeadDim + od * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < KPER; ++u) {
+    const int c = tid + kThreads * u;
+    uint16_t* dst = Ks + (c >> 3) * KP + (c & 7) * 16;
+    *reinterpret_cast<u32x4*>(dst) = e4m3x8_to_bf16(make_uint2(kr[u].x, kr[u].y));
+    *reinterpret_cast<u32x4*>(dst + 8) = e4m3x8_to_bf16(make_uint2(kr[u].z, kr[u].w));
+  }
+#pragma unroll
+  for (int u = 0; u < VPER; ++u) {  // written transposed: Vt[d][key]
+    const int c = tid + kThreads * u;
+    const int kq = c >> 4, od = c & 15;
+    const u32x4 w0 = e4m3x8_to_bf16(vr[4 * u + 0]), w1 = e4m3x8_to_bf16(vr[4 * u + 1]);
+    const u32x4 w2 = e4m3x8_to_bf16(vr[4 * u + 2]), w3 = e4m3x8_to_bf16(vr[4 * u + 3]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) * 16;
+      const uint32_t v0 = (w0[e >> 1] >> sh) & 0xFFFFu, v1 = (w1[e >> 1] >> sh) & 0xFFFFu;
+      const uint32_t v2 = (w2[e >> 1] >> sh) & 0xFFFFu, v3 = (w3[e >> 1] >> sh) & 0xFFFFu;
+      *reinterpret_cast<uint2*>(Vt + (od * 8 + e) * VP + kq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+    }
+  }
+}
+
+// K/V block (keys t Bk .. of kv element offset kv0) staged from bf16 or FP8 caches.
+template <bool KV8>
+__device__ __forceinline__ void stage_kv_any(uint16_t* Ks, uint16_t* Vt, const void* k, const void* v, int64_t kv0,
+                                             int n_valid) {
+  if constexpr (KV8)
+    stage_kv8(Ks, Vt, static_cast<const unsigned char*>(k) + kv0, static_cast<const unsigned char*>(v) + kv0,
+              n_valid);
+  else
+    stage_kv(Ks, Vt, static_cast<const uint16_t*>(k) + kv0, static_cast<const uint16_t*>(v) + kv0, n_valid);
+}
+
 // S^T = K Q^T for one wave: the 128 keys of the staged block (4 row tiles of
 // 32) against the wave's 32 query rows (from its LDS region), raw dot
 // products.  k-steps outer, so the four accumulator chains interleave; the

@@ -22,6 +22,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Eight FP8 E4M3 codes (bytes 0..7 of w) widened to eight bf16, in order.
+// Every E4M3 value is a bf16 value, so the conversion (scale 1) is exact.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint2 w) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true))};
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
@@ -34,6 +43,7 @@ struct Dims {
   float scale;         // softmax scale
   float scale_log2;    // softmax scale * log2(e)
   int32_t idx_eb;      // bytes per index_q / index_k element: 2 (bf16) or 1 (FP8 E4M3)
+  int32_t kv_eb;       // bytes per k / v element: 2 (bf16) or 1 (FP8 E4M3)
   // Variable-length batches and paged caches.  All null: every sequence has
   // n_q query rows at positions offset .. offset + n_q - 1 and n_kv cached
   // tokens, each tensor contiguous.  Otherwise n_q and n_kv are maxima, per-row

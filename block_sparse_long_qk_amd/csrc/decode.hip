@@ -195,9 +195,11 @@ __device__ __forceinline__ int slot_block(const int32_t* row, int s, int k, int 
 }
 
 // One wave per (row, slot); GMAX (8 or 16) >= G query heads of the row's group.
-template <int GMAX, bool VL>
-__global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                   const uint16_t* __restrict__ v,
+// KV8: K and V hold FP8 E4M3 codes (1 byte per element), widened to bf16 as
+// they are loaded; the arithmetic is then the bf16 path's.
+template <int GMAX, bool VL, bool KV8>
+__global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ q, const void* __restrict__ k,
+                                                   const void* __restrict__ v,
                                                    const int32_t* __restrict__ block_idx, float* __restrict__ part,
                                                    Dims D) {
   __shared__ float P[4][kBk][GMAX];  // per wave: probabilities [key][head]
@@ -222,8 +224,9 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
   }
   const int n = lane & 15, c = lane >> 4;
   const int64_t key0 = (int64_t)t * kBk;
-  const uint16_t* kb = k + kvoff_of<VL>(D, b, g, t);
-  const uint16_t* vb = v + kvoff_of<VL>(D, b, g, t);
+  constexpr int EBKV = KV8 ? 1 : 2;  // bytes per K/V element
+  const unsigned char* kbytes = static_cast<const unsigned char*>(k) + kvoff_of<VL>(D, b, g, t) * EBKV;
+  const unsigned char* vbytes = static_cast<const unsigned char*>(v) + kvoff_of<VL>(D, b, g, t) * EBKV;
 
   // scores S[h][key] with MFMA: A = Q (rows = heads), B = K^T (columns = keys);
   // lane group c and k-step ks hold head dims 32*c + 8*ks .. +8.
@@ -240,14 +243,20 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
   unsigned char* kbuf = Kst[wave];
   const int lk = lane >> 4, lo = (lane & 15) * 16;
   const int n_keys = (int)min((int64_t)kBk, (int64_t)nkv_b - key0);
-  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kb);
   uint4 kx[8];
   auto fetch_k = [&](int st) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = 32 * st + 4 * u + lk;
-      kx[u] = key < n_keys ? *reinterpret_cast<const uint4*>(kbytes + key * (kHeadDim * 2) + lo)
-                           : make_uint4(0, 0, 0, 0);
+      if constexpr (KV8) {
+        const uint2 c8 = key < n_keys ? *reinterpret_cast<const uint2*>(kbytes + key * kHeadDim + lo / 2)
+                                      : make_uint2(0, 0);
+        const u32x4 wv = e4m3x8_to_bf16(c8);
+        kx[u] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      } else {
+        kx[u] = key < n_keys ? *reinterpret_cast<const uint4*>(kbytes + key * (kHeadDim * 2) + lo)
+                             : make_uint4(0, 0, 0, 0);
+      }
     }
   };
   f32x4 sc[8];
@@ -320,14 +329,23 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
 #pragma unroll 1
   for (int kb8 = 0; kb8 < kBk; kb8 += 32) {
     uint4 w8[8];
+    uint2 c8[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int kk = kb8 + 4 * u + kr;
-      w8[u] = kk < n_keys ? *reinterpret_cast<const uint4*>(vb + kk * kHeadDim + 8 * dc) : make_uint4(0, 0, 0, 0);
+      if constexpr (KV8)
+        c8[u] = kk < n_keys ? *reinterpret_cast<const uint2*>(vbytes + kk * kHeadDim + 8 * dc) : make_uint2(0, 0);
+      else
+        w8[u] = kk < n_keys ? *reinterpret_cast<const uint4*>(vbytes + kk * (kHeadDim * 2) + 16 * dc)
+                            : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int kk = kb8 + 4 * u + kr;
+      if constexpr (KV8) {
+        const u32x4 wv = e4m3x8_to_bf16(c8[u]);
+        w8[u] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      }
       const uint32_t x[4] = {w8[u].x, w8[u].y, w8[u].z, w8[u].w};
       float vv[8];
 #pragma unroll
@@ -460,19 +478,22 @@ hipError_t launch_index_small(const void* index_q, const void* index_k, float* p
   return hipGetLastError();
 }
 
-hipError_t launch_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
+hipError_t launch_attn_rows(const uint16_t* q, const void* k, const void* v, const int32_t* block_idx,
                             uint16_t* out, float* lse, float* part, const Dims& D, hipStream_t stream) {
   const int64_t rows = (int64_t)D.B * D.h_kv * D.n_q;
   dim3 grid((unsigned)rows, (D.k + 1 + 3) / 4);
-#define MSA_ROWS(GM, VL)                                                                                  \
-  hipLaunchKernelGGL((k_attn_rows<GM, VL>), grid, dim3(256), 0, stream, q, k, v, block_idx, part, D)
+  auto go = [&](auto gm, auto vlc, auto kv8) {
+    hipLaunchKernelGGL((k_attn_rows<decltype(gm)::value, decltype(vlc)::value, decltype(kv8)::value>), grid,
+                       dim3(256), 0, stream, q, k, v, block_idx, part, D);
+  };
+  auto by_kv = [&](auto gm, auto vlc) {
+    if (D.kv_eb == 1) go(gm, vlc, std::true_type{}); else go(gm, vlc, std::false_type{});
+  };
+  auto by_vl = [&](auto gm) {
+    if (dims_varlen(D)) by_kv(gm, std::true_type{}); else by_kv(gm, std::false_type{});
+  };
+  if (D.G <= 8) by_vl(std::integral_constant<int, 8>{}); else by_vl(std::integral_constant<int, 16>{});
   const bool vl = dims_varlen(D);
-  if (D.G <= 8) {
-    if (vl) MSA_ROWS(8, true); else MSA_ROWS(8, false);
-  } else {
-    if (vl) MSA_ROWS(16, true); else MSA_ROWS(16, false);
-  }
-#undef MSA_ROWS
   if (vl)
     hipLaunchKernelGGL(k_merge_rows<true>, dim3((unsigned)rows), dim3(256), 0, stream, part, out, lse, D);
   else

@@ -511,7 +511,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }  // namespace
 
 bool kl_supported(const Dims& D) {
-  return (D.G == 4 || D.G == 8 || D.G == 16 || D.G == 32) && D.idx_eb == 2 && !dims_varlen(D);
+  return (D.G == 4 || D.G == 8 || D.G == 16 || D.G == 32) && D.idx_eb == 2 && D.kv_eb == 2 && !dims_varlen(D);
 }
 
 hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,

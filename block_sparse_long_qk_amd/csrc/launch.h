@@ -29,7 +29,7 @@ int64_t plan_groups(const Dims& D);       // query groups (kGroupChunks chunks) 
 int64_t plan_bins(const Dims& D);         // (b, g, query group, block) bins
 
 // Gather plan + gathered non-local tiles + local tiles with the merge.
-hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
+hipError_t launch_sparse_attn(const uint16_t* q, const void* k, const void* v, const int32_t* block_idx,
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream);
 
 // KL alignment of the index branch to the main branch's group-averaged
@@ -67,7 +67,7 @@ bool use_attn_rows(const Dims& D);     // query-outer attention
 size_t attn_rows_partial_bytes(const Dims& D);
 hipError_t launch_index_small(const void* index_q, const void* index_k, float* pooled, const Dims& D,
                               hipStream_t stream);
-hipError_t launch_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
+hipError_t launch_attn_rows(const uint16_t* q, const void* k, const void* v, const int32_t* block_idx,
                             uint16_t* out, float* lse, float* part, const Dims& D, hipStream_t stream);
 
 }  // namespace msa

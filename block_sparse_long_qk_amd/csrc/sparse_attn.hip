@@ -220,10 +220,9 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, fl
 // vector loads and stores alike, so a wait for loads waits for every store
 // issued before them: issued where they are, the stores and the next rows
 // have a whole softmax and P.V to land before the next tile waits for them.
-template <bool LOCAL, bool VL>
+template <bool LOCAL, bool VL, bool KV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_tiles(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, AttnWs ws,
-    Dims D) {
+    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, AttnWs ws, Dims D) {
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
   __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];  // per wave: its query rows
@@ -263,7 +262,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     {
       const int sb = cur.bg / D.h_kv;
       const int64_t kv0 = kvoff_of<VL>(D, sb, cur.bg % D.h_kv, cur.t);
-      stage_kv(Ks, Vt, k + kv0, v + kv0, max(1, min(kBk, nkv_of<VL>(D, sb) - cur.t * kBk)));
+      stage_kv_any<KV8>(Ks, Vt, k, v, kv0, max(1, min(kBk, nkv_of<VL>(D, sb) - cur.t * kBk)));
       __syncthreads();
     }
     const int staged_bg = cur.bg, staged_t = cur.t;
@@ -313,9 +312,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // in registers, and the row's non-local partials (lse -inf: no partial) are
 // folded in two slots at a time with a running max.  Normalised, the result is
 // written to `out` (bf16) and `lse` (natural log).
-template <bool VL>
+template <bool VL, bool KV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_local_merge(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, AttnWs ws,
+    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, AttnWs ws,
     uint16_t* __restrict__ out, float* __restrict__ lse_out, Dims D) {
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
@@ -366,7 +365,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (staged_bg >= 0) __syncthreads();
       const int sb = cur.bg / D.h_kv;
       const int64_t kv0 = kvoff_of<VL>(D, sb, cur.bg % D.h_kv, cur.t);
-      stage_kv(Ks, Vt, k + kv0, v + kv0, max(1, min(kBk, nkv_of<VL>(D, sb) - cur.t * kBk)));
+      stage_kv_any<KV8>(Ks, Vt, k, v, kv0, max(1, min(kBk, nkv_of<VL>(D, sb) - cur.t * kBk)));
       __syncthreads();
       staged_bg = cur.bg;
       staged_t = cur.t;
@@ -447,19 +446,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 }  // namespace
 
-hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
+hipError_t launch_sparse_attn(const uint16_t* q, const void* k, const void* v, const int32_t* block_idx,
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream) {
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
   if (e != hipSuccess) return e;
-  if (dims_varlen(D)) {
-    hipLaunchKernelGGL((k_attn_tiles<false, true>), dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws, D);
-    hipLaunchKernelGGL(k_attn_local_merge<true>, dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws, out,
-                       lse, D);
-  } else {
-    hipLaunchKernelGGL((k_attn_tiles<false, false>), dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws,
+  auto go = [&](auto vl, auto kv8) {
+    constexpr bool VL = decltype(vl)::value, K8 = decltype(kv8)::value;
+    hipLaunchKernelGGL((k_attn_tiles<false, VL, K8>), dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws,
                        D);
-    hipLaunchKernelGGL(k_attn_local_merge<false>, dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws, out,
-                       lse, D);
+    hipLaunchKernelGGL((k_attn_local_merge<VL, K8>), dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws,
+                       out, lse, D);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (dims_varlen(D)) {
+    if (D.kv_eb == 1) go(T{}, T{}); else go(T{}, F{});
+  } else {
+    if (D.kv_eb == 1) go(F{}, T{}); else go(F{}, F{});
   }
   return hipGetLastError();
 }

@@ -22,7 +22,7 @@
  *
  * Tensor layouts (all dense, row-major, contiguous):
  *   q, out     [B][n_q][H_q][d]        bf16
- *   k, v       [B][H_kv][n_kv][d]      bf16  (each 128-token block of one head
+ *   k, v       [B][H_kv][n_kv][d]      bf16 or FP8 E4M3  (each 128-token block of one head
  *                                             is one contiguous 32 KiB run)
  *   index_q    [B][n_q][H_kv][d_idx]   bf16 or FP8 E4M3 (one index-query head per group)
  *   index_k    [B][n_kv][d_idx]        bf16 or FP8 E4M3 (one shared index-key head)
@@ -71,8 +71,15 @@ typedef enum {
  * 448, no infinities, NaN = all exponent and mantissa bits set).  Index scores
  * are then the raw dot products of the E4M3 values, exact products accumulated
  * in fp32; a per-tensor quantisation scale is a positive factor that leaves
- * the selection unchanged and is the caller's to apply.  Every other tensor
- * stays bf16. */
+ * the selection unchanged and is the caller's to apply.
+ *
+ * K and V may be FP8 E4M3 as well (kv_dtype): the main branch then attends over
+ * the values the codes represent, each widened exactly to bf16 as it is staged,
+ * so the arithmetic after the load is the bf16 path's.  No scale is applied: a
+ * per-tensor K scale folds into softmax_scale, a V scale multiplies the output
+ * and is the caller's.  FP8 K/V is taken by msa_sparse_attn_fwd and
+ * msa_forward (and their _v forms); the KL, dense and backward calls return
+ * MSA_ERR_UNSUPPORTED for it.  q and out stay bf16. */
 typedef enum {
   MSA_DTYPE_BF16 = 0,
   MSA_DTYPE_FP8_E4M3 = 1
@@ -81,7 +88,8 @@ typedef enum {
 /* One problem instance.  q_offset = -1 means bottom-right alignment,
  * q_offset = n_kv - n_q (prefill: n_q = n_kv gives 0; decode: n_q = 1 puts the
  * query on the last cached token, whose block is its local block).
- * index_dtype is a msa_dtype (0, bf16, when the struct is zero-initialised). */
+ * index_dtype and kv_dtype are msa_dtypes (0, bf16, when the struct is
+ * zero-initialised). */
 typedef struct {
   int32_t batch, n_q, n_kv;
   int32_t h_q, h_kv;
@@ -89,7 +97,8 @@ typedef struct {
   int32_t block_size, topk;
   int64_t q_offset;
   float softmax_scale; /* 1/sqrt(d) in the standard configuration */
-  int32_t index_dtype;
+  int32_t index_dtype; /* element type of index_q and index_k */
+  int32_t kv_dtype;    /* element type of k and v (and of k_pages, v_pages) */
 } msa_problem;
 
 /* Which call a workspace is sized for. */

@@ -241,6 +241,17 @@ def _index_keys(w, b: int, plant):
     return _ik_cache[key]
 
 
+def kv_values_bf16(w, bits):
+    """K or V rows as the attention sees them: the bf16 bits themselves, or,
+    for a workload with FP8 K/V, the bf16 bits of the values their E4M3 codes
+    represent (exact: every E4M3 value is a bf16 value)."""
+    if getattr(w, "kv_dtype", "bf16") != "fp8":
+        return bits
+    import synth
+    vals = e4m3_decode(synth.to_e4m3(bits)).astype(np.float32)
+    return (vals.view(np.uint32) >> 16).astype(np.uint16)
+
+
 def kv_for_blocks(w, b: int, g: int, sel):
     """K and V of one (sequence, group) with only the selected blocks filled.
 
@@ -253,8 +264,8 @@ def kv_for_blocks(w, b: int, g: int, sel):
     blocks = np.unique(np.asarray(sel)[np.asarray(sel) >= 0])
     for t in blocks:
         j0, j1 = int(t) * w.block_size, min((int(t) + 1) * w.block_size, w.n_kv)
-        K[j0:j1] = synth.host_kv(w, "k", b, g, j0, j1)
-        V[j0:j1] = synth.host_kv(w, "v", b, g, j0, j1)
+        K[j0:j1] = kv_values_bf16(w, synth.host_kv(w, "k", b, g, j0, j1))
+        V[j0:j1] = kv_values_bf16(w, synth.host_kv(w, "v", b, g, j0, j1))
     return K, V
 
 

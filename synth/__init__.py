@@ -134,6 +134,7 @@ class Workload:
     plant_alpha: float = 0.0    # amplitude added to planted index keys
     plant_beta: float = 0.0     # amplitude added to that group's index queries
     index_dtype: str = "bf16"   # "fp8": index_q / index_k are the bf16 values rounded to OCP E4M3
+    kv_dtype: str = "bf16"      # "fp8": k / v are the bf16 values rounded to OCP E4M3
 
     @property
     def offset(self) -> int:
@@ -408,14 +409,15 @@ def device_fill(w: Workload, name: str, tensor, stream=None, nt_dev=None):
 
 def device_inputs(w: Workload, device="cuda:0") -> dict:
     """All five input tensors of a workload, generated on the device.  With
-    index_dtype "fp8", index_q and index_k are uint8 tensors of E4M3 codes."""
+    index_dtype "fp8", index_q and index_k are uint8 tensors of E4M3 codes;
+    with kv_dtype "fp8", k and v are."""
     import torch
     nt = torch.from_numpy(normal_table().view(np.int16).copy()).to(device)
     out = {}
     for name, shp in w.shapes().items():
         t = torch.empty(shp, dtype=torch.bfloat16, device=device)
         device_fill(w, name, t, nt_dev=nt)
-        if w.index_dtype == "fp8" and name in ("iq", "ik"):
+        if (w.index_dtype == "fp8" and name in ("iq", "ik")) or (w.kv_dtype == "fp8" and name in ("k", "v")):
             t = t.to(torch.float8_e4m3fn).view(torch.uint8)
         out[name] = t
     torch.cuda.synchronize(device)

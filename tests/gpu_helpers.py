@@ -32,8 +32,9 @@ def say(*a):
 
 def problem(w: synth.Workload) -> msa.Problem:
     dt = msa.DTYPE_FP8_E4M3 if w.index_dtype == "fp8" else msa.DTYPE_BF16
+    kt = msa.DTYPE_FP8_E4M3 if w.kv_dtype == "fp8" else msa.DTYPE_BF16
     return msa.Problem.make(w.batch, w.n_q, w.n_kv, w.h_q, w.h_kv, w.head_dim, w.index_dim, w.block_size, w.topk,
-                            w.q_offset, w.scale, index_dtype=dt)
+                            w.q_offset, w.scale, index_dtype=dt, kv_dtype=kt)
 
 
 def bf16_np(t) -> np.ndarray:

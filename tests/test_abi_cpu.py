@@ -55,6 +55,8 @@ def prob(**kw):
     (dict(batch=64, n_q=262144, n_kv=262144, h_kv=8, h_q=64, topk=64), msa.ERR_INVALID_ARGUMENT),  # int32 overflow
     (dict(index_dtype=2), msa.ERR_INVALID_ARGUMENT),         # unknown index element type
     (dict(index_dtype=-1), msa.ERR_INVALID_ARGUMENT),
+    (dict(kv_dtype=2), msa.ERR_INVALID_ARGUMENT),            # unknown K/V element type
+    (dict(kv_dtype=-1), msa.ERR_INVALID_ARGUMENT),
 ])
 def test_invalid_problems_rejected(kw, status):
     p = prob(**kw)
@@ -148,7 +150,8 @@ def test_problem_struct_layout():
     int64 offset on an 8-byte boundary, the float scale, the int32 dtype."""
     P = msa.Problem
     assert P.q_offset.offset == 40 and P.softmax_scale.offset == 48 and P.index_dtype.offset == 52
-    assert ctypes.sizeof(P) == 56
+    assert P.kv_dtype.offset == 56
+    assert ctypes.sizeof(P) == 64
 
 
 def test_fp8_index_problems_accepted():
@@ -191,3 +194,19 @@ def test_index_kl_bwd_rejects_null_lse_index():
     rc = L.msa_index_kl_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None, fake, fake, fake,
                             1 << 40, None)
     assert rc == msa.ERR_INVALID_ARGUMENT
+
+
+def test_fp8_kv_forward_accepted_with_the_same_workspace():
+    """FP8 K/V changes how the attention stages K and V, not its workspace."""
+    for op in (msa.OP_SPARSE_ATTN, msa.OP_FORWARD):
+        assert msa.workspace_size(prob(kv_dtype=msa.DTYPE_FP8_E4M3), op) == msa.workspace_size(prob(), op)
+
+
+@pytest.mark.parametrize("op", ["OP_INDEX_KL", "OP_SPARSE_ATTN_BWD", "OP_INDEX_KL_BWD"])
+def test_fp8_kv_training_calls_unsupported(op):
+    """The KL pass and both backward passes take bf16 K/V only."""
+    p = prob(h_q=16, h_kv=2, kv_dtype=msa.DTYPE_FP8_E4M3)
+    n = ctypes.c_size_t(0)
+    assert msa.library().msa_workspace_size(ctypes.byref(p), getattr(msa, op), ctypes.byref(n)) == \
+        msa.ERR_UNSUPPORTED
+    assert msa.workspace_size(prob(h_q=16, h_kv=2), getattr(msa, op)) > 0

@@ -27,6 +27,8 @@ CASES = [
     ("mix_dimx64", 4, 1, 64, 8, [(500, 900), (1200, 1200), (77, 77)]),
     # FP8 (E4M3) index inputs, prefill and decode rows in one batch
     ("mix_fp8", 16, 2, 128, 16, [(2000, 2500), (1, 6000), (0, 10), (130, 130)], "fp8"),
+    # FP8 (E4M3) K and V caches, bf16 index inputs
+    ("mix_kv8", 16, 2, 128, 16, [(2000, 2500), (1, 6000), (0, 10), (130, 130), (3, 700)], "bf16", "fp8"),
 ]
 SENTINEL_IDX = -77
 SENTINEL_LSE = 12345.0
@@ -36,9 +38,10 @@ def _build(case, paged: bool, seed0: int):
     import torch
     name, h_q, h_kv, d_idx, k, seqs = case[:6]
     dtype = case[6] if len(case) > 6 else "bf16"
+    kv_dtype = case[7] if len(case) > 7 else "bf16"
     B = len(seqs)
     ws = [synth.Workload(f"{name}_{b}", 1, max(qo, 1), kv, h_q, h_kv, index_dim=d_idx, topk=k, seed=seed0 + b,
-                         index_dtype=dtype)
+                         index_dtype=dtype, kv_dtype=kv_dtype)
           for b, (qo, kv) in enumerate(seqs)]
     xs = [synth.device_inputs(w) for w in ws]
     qo_l = [qo for qo, _ in seqs]
@@ -53,6 +56,12 @@ def _build(case, paged: bool, seed0: int):
     def filled_index(shape):
         # memory the index kernels must not read: large values (E4M3: 448, code 0x7E)
         if ik_dtype == torch.uint8:
+            return torch.full(shape, 0x7E, dtype=torch.uint8, device=dev)
+        return torch.full(shape, big, dtype=torch.bfloat16, device=dev)
+
+    def filled_kv(shape):
+        # cache memory outside the sequences: large values (E4M3: 448, code 0x7E)
+        if kv_dtype == "fp8":
             return torch.full(shape, 0x7E, dtype=torch.uint8, device=dev)
         return torch.full(shape, big, dtype=torch.bfloat16, device=dev)
 
@@ -73,8 +82,8 @@ def _build(case, paged: bool, seed0: int):
             table[b, :n_blk[b]] = perm[at:at + n_blk[b]]
             table[b, n_blk[b]:] = perm[-1]     # never read: past the sequence's blocks
             at += n_blk[b]
-        kp = torch.full((num_pages, h_kv, bk, d), big, dtype=torch.bfloat16, device=dev)
-        vp = torch.full_like(kp, big)
+        kp = filled_kv((num_pages, h_kv, bk, d))
+        vp = filled_kv((num_pages, h_kv, bk, d))
         ikp = filled_index((num_pages, bk, d_idx))
         for b, x in enumerate(xs):
             for t in range(n_blk[b]):
@@ -87,8 +96,8 @@ def _build(case, paged: bool, seed0: int):
         k_in, v_in, ik_in = kp, vp, ikp
     else:
         num_pages, table_t = 0, None
-        k_in = torch.full((B, h_kv, max_kv, d), big, dtype=torch.bfloat16, device=dev)
-        v_in = torch.full_like(k_in, big)
+        k_in = filled_kv((B, h_kv, max_kv, d))
+        v_in = filled_kv((B, h_kv, max_kv, d))
         ik_in = filled_index((B, max_kv, d_idx))
         for b, x in enumerate(xs):
             k_in[b, :, :kv_l[b]] = x["k"][0]
@@ -98,7 +107,8 @@ def _build(case, paged: bool, seed0: int):
     vl = msa.Varlen.make(qo_lens=i32(qo_l), kv_lens=i32(kv_l), q_starts=i32(starts.tolist()), total_q=total_q,
                          page_table=table_t, num_pages=num_pages)
     p = msa.Problem.make(B, max_q, max_kv, h_q, h_kv, 128, d_idx, bk, k,
-                         index_dtype=msa.DTYPE_FP8_E4M3 if dtype == "fp8" else msa.DTYPE_BF16)
+                         index_dtype=msa.DTYPE_FP8_E4M3 if dtype == "fp8" else msa.DTYPE_BF16,
+                         kv_dtype=msa.DTYPE_FP8_E4M3 if kv_dtype == "fp8" else msa.DTYPE_BF16)
     return ws, xs, vl, p, dict(q=q, iq=iq, k=k_in, v=v_in, ik=ik_in), qo_l, starts, total_q
 
 

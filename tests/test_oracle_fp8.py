@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 
 
 def test_e4m3_decoder_matches_torch_on_every_code():
@@ -72,3 +73,17 @@ def test_pool_f8_hand_worked():
     # block 0: max(2 - 0.5, 0.5 - 224) = 1.5; block 1: only key 2 is visible: -1 - 2^-7
     assert pooled[0, 0] == 1.5
     assert pooled[0, 1] == -1.0 - 2.0 ** -7
+
+
+def test_kv_values_bf16_are_the_e4m3_values():
+    """The oracle's view of FP8 K/V rows equals torch's own float8_e4m3fn round
+    trip of the same bf16 values, and is the identity for bf16 workloads."""
+    import torch
+    rng = np.random.default_rng(7)
+    bits = synth.f32_to_bf16((rng.standard_normal((64, 128)) * 3).astype(np.float32))
+    w8 = synth.Workload("kv8_pin", 1, 4, 4, 4, 1, kv_dtype="fp8")
+    got = oracle.kv_values_bf16(w8, bits)
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    ref = t.to(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal((got.astype(np.uint32) << 16).view(np.float32), ref)
+    assert oracle.kv_values_bf16(synth.Workload("kv_pin", 1, 4, 4, 4, 1), bits) is bits
