@@ -7,8 +7,9 @@ k 16), inputs seeded and synthetic, resident in HBM before timing starts.
 Prints one JSON line: prefill tokens/s (the value), the decode rate at a
 256K-token cache (64 sequences), per-stage times, the roofline of the dominant
 kernel, the same two steps with the caches in a shuffled page pool
-(msa_forward_v), the same two steps with FP8 (E4M3) index inputs, and the
-oracle's CPU rate on a bounded sample of the same workload.
+(msa_forward_v), the same two steps with FP8 (E4M3) index inputs and with
+FP8 K/V caches, the KL pass and both backward passes and dense mode at 128K,
+and the oracle's CPU rate on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -52,8 +53,9 @@ def decode_bytes(w):
     selected tokens, Q, index-q, the output and the block indices."""
     _, _, _, t_size = algorithmic_work(w)
     eb = 1.0 if w.index_dtype == "fp8" else 2.0   # bytes per index element
+    ekv = 1.0 if w.kv_dtype == "fp8" else 2.0     # bytes per K/V element
     ik = eb * w.batch * w.n_kv * w.index_dim
-    kv = 2.0 * 2 * w.head_dim * w.h_kv * w.batch * float(t_size.sum())
+    kv = ekv * 2 * w.head_dim * w.h_kv * w.batch * float(t_size.sum())
     small = (2.0 * w.batch * w.n_q * 2 * w.h_q * w.head_dim + eb * w.batch * w.n_q * w.h_kv * w.index_dim
              + 4.0 * w.batch * w.h_kv * w.topk)
     return ik + kv + small
@@ -87,7 +89,8 @@ def gpu_leg(w, steps, warmup, stream, paged=False, kl=False):
     x = synth.device_inputs(w)
     p = msa.Problem.make(w.batch, w.n_q, w.n_kv, w.h_q, w.h_kv, w.head_dim, w.index_dim, w.block_size, w.topk,
                          w.q_offset, w.scale,
-                         index_dtype=msa.DTYPE_FP8_E4M3 if w.index_dtype == "fp8" else msa.DTYPE_BF16)
+                         index_dtype=msa.DTYPE_FP8_E4M3 if w.index_dtype == "fp8" else msa.DTYPE_BF16,
+                         kv_dtype=msa.DTYPE_FP8_E4M3 if w.kv_dtype == "fp8" else msa.DTYPE_BF16)
     f = msa.alloc_outputs(p)
     sp = stream.cuda_stream
 
@@ -241,10 +244,10 @@ def main():
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--decode-workload", default="decode_256k")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-positions", type=int, default=1024)
+    ap.add_argument("--cpu-positions", type=int, default=3072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache (msa_forward_v) legs")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) index-input legs")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) index-input and K/V legs")
     ap.add_argument("--no-kl", action="store_true", help="skip the KL alignment pass")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -378,6 +381,24 @@ def main():
                 "decode_bytes_per_step": dbf,
                 "decode_frac_hbm": round(dbf / (gdf["ms_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 "decode_index_ms": round(gdf["ms_index"], 4)})
+        # E4M3 K/V caches (the index branch bf16), then both branches E4M3 for decode
+        wk = w.replace(name=w.name + "_fp8_kv", kv_dtype="fp8")
+        gk = gpu_leg(wk, args.steps, args.warmup, stream)
+        line["fp8_kv"] = {"prefill_ms_per_step": round(gk["ms_step"], 4),
+                          "prefill_tokens_per_s": round(w.batch * w.n_q / (gk["ms_step"] * 1e-3), 1),
+                          "sparse_attn_ms": round(gk["ms_attn"], 4)}
+        if not args.no_decode:
+            for key, wdk in (("decode", wd.replace(name=wd.name + "_fp8_kv", kv_dtype="fp8")),
+                             ("decode_fp8_both", wd.replace(name=wd.name + "_fp8_both", kv_dtype="fp8",
+                                                            index_dtype="fp8"))):
+                gdk = gpu_leg(wdk, args.steps, args.warmup, stream)
+                dbk = decode_bytes(wdk)
+                line["fp8_kv"].update({
+                    key + "_ms_per_step": round(gdk["ms_step"], 4),
+                    key + "_tokens_per_s": round(wdk.batch / (gdk["ms_step"] * 1e-3), 1),
+                    key + "_bytes_per_step": dbk,
+                    key + "_frac_hbm": round(dbk / (gdk["ms_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    key + "_attn_ms": round(gdk["ms_attn"], 4)})
 
     if not args.no_cpu_baseline:
         print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
