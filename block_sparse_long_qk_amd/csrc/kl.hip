@@ -261,17 +261,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   unsigned char* iqw = IQs[wave];
   const float c = D.scale_log2;
 
+  // A tile's query and index-query rows are fetched into the wave's LDS
+  // regions one tile ahead: each region is refilled as soon as the scores that
+  // read it are formed, so the fetch overlaps the teacher / student folds.
+  auto q_src = [&](const TileRow& tr) {  // rows that do not exist read row 0 of the group
+    const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv, i = tr.valid ? tr.i : 0;
+    return q + (((int64_t)b * D.n_q + i) * D.h_q + g * G + hh) * kHeadDim;
+  };
+  auto iq_src = [&](const TileRow& tr) {
+    const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv, i = tr.valid ? tr.i : 0;
+    return iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX;
+  };
+  auto lse_of = [&](const TileRow& tr) {
+    const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv, i = tr.valid ? tr.i : 0;
+    return lse[((int64_t)b * D.h_q + g * G + hh) * D.n_q + i];
+  };
+  TileRow cur = tile_row<LOCAL, false>(tile_raw<LOCAL>(ws, D, w.tile, ps), D, ws, w.tile, ps);
+  fetch_q_rows(qw, q_src(cur), lane);
+  fetch_iq_rows<DIDX, G>(iqw, iq_src(cur), lane);
+  float lse_raw = lse_of(cur);
+  // the list entry of the tile after next is loaded one tile ahead of its decode
+  Walk w1 = walk_next(w, stride, hi);
+  TileRaw raw1 = tile_raw<LOCAL>(ws, D, min(w1.tile, hi - 1), ps);
   int staged_bg = -1, staged_t = -1;
   while (w.tile < hi) {
-    TileRow cur = tile_row<LOCAL, false>(tile_raw<LOCAL>(ws, D, w.tile, ps), D, ws, w.tile, ps);
     const int b = cur.bg / D.h_kv, g = cur.bg % D.h_kv;
-    const int i = cur.valid ? cur.i : 0;
-    // this lane's row: its query row, its position's index-query row, its lse
-    // (the wave is done with its regions: the previous tile ran to the end)
-    fetch_q_rows(qw, q + (((int64_t)b * D.n_q + i) * D.h_q + g * G + hh) * kHeadDim, lane);
-    fetch_iq_rows<DIDX, G>(iqw, iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX, lane);
-    const float lse_mine = lse[((int64_t)b * D.h_q + g * G + hh) * D.n_q + i] * kLog2e;
-    const bool row_ok = cur.valid;
     if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform: a new block for the workgroup
       __syncthreads();  // every wave is done with the staged block
       const int64_t kv0 = (((int64_t)b * D.h_kv + g) * D.n_kv + (int64_t)cur.t * kBk) * kHeadDim;
@@ -282,6 +296,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       __syncthreads();
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's query and index-query rows have landed
+    const float lse_mine = lse_raw * kLog2e;
+    const bool row_ok = cur.valid;
     // the lse and validity of the 16 rows this lane's registers hold
     float lse2[16];
     bool rowok[16];
@@ -301,10 +317,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       pslot[j] = __shfl(cur.s, src, 64);
       ppos[j] = pv[j] ? D.offset + pi[j] : -1;
     }
+    // the next tile (past the last: a stand-in decode of the last one, whose
+    // fetches stay in bounds and are never used), and the list entry after it
+    const TileRow nxt = tile_row<LOCAL, false>(raw1, D, ws, min(w1.tile, hi - 1), ps);
+    const Walk w2 = w1.tile < hi ? walk_next(w1, stride, hi) : w1;
+    const TileRaw raw2 = tile_raw<LOCAL>(ws, D, min(w2.tile, hi - 1), ps);
     float P[4][PM::NPL];
     {
       f32x16 sc[4];
       q_k_scores(Ks, qw, lane, sc);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the query region has been read
+      fetch_q_rows(qw, q_src(nxt), lane);
+      lse_raw = lse_of(nxt);
       teacher_probs<G, LOCAL>(sc, lse2, rowok, ppos, (int64_t)cur.t * kBk, lane, c, P);
     }
     KlAcc acc[PM::NPL];
@@ -313,6 +337,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     {
       f32x16 zz[4];
       iq_ik_scores<DIDX, G>(IKs, iqw, lane, zz);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the index-query region has been read
+      fetch_iq_rows<DIDX, G>(iqw, iq_src(nxt), lane);
       student_fold<G, LOCAL>(zz, P, ppos, (int64_t)cur.t * kBk, lane, acc);
     }
     lanes_reduce<G>(acc);
@@ -325,8 +351,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         kl_part[row * (D.k + 1) + pslot[j]] = make_float4(acc[j].a, acc[j].b, acc[j].m, acc[j].l);
       }
     }
-    w = walk_next(w, stride, hi);
+    w = w1;
+    w1 = w2;
+    raw1 = raw2;
+    cur = nxt;
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the last (unused) row fetch has landed before the workgroup ends
 }
 
 // One thread per (sequence, group, query): add the row's partials (the listed
