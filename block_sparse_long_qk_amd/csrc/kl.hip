@@ -213,6 +213,45 @@ __device__ __forceinline__ void student_fold(const f32x16 (&z)[4], const float (
   }
 }
 
+// One tile's KL partials for this lane's positions over the block's 128 keys
+// (the 32 lanes of a half hold 4 keys each): the max of the visible student
+// scores first (a max over the lanes), then the three sums with that common
+// max, added over the lanes.  Every lane of a half ends with the totals; a
+// position without visible keys gets m = -inf and l = 0.
+template <int G, bool MASKED>
+__device__ __forceinline__ void student_tile(const f32x16 (&z)[4], const float (&P)[4][PosMap<G>::NPL],
+                                             const int64_t (&ppos)[PosMap<G>::NPL], int64_t key0, int lane,
+                                             KlAcc (&out)[PosMap<G>::NPL]) {
+  using PM = PosMap<G>;
+  const float NEG_INF = -__builtin_huge_valf();
+  const int col = lane & 31;
+#pragma unroll
+  for (int j = 0; j < PM::NPL; ++j) {
+    auto visible = [&](int T) { return ppos[j] >= 0 && (!MASKED || key0 + 32 * T + col <= ppos[j]); };
+    float m = NEG_INF;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+      if (visible(T)) m = fmaxf(m, z[T][j * PM::RPP] * kLog2e);
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float a = 0.f, b = 0.f, l = 0.f;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const float zz = z[T][j * PM::RPP], p = P[T][j];
+      if (p > 0.f) a += p * __log2f(p);
+      b += p * zz;
+      if (visible(T)) l += __builtin_amdgcn_exp2f(zz * kLog2e - m);
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      a += __shfl_xor(a, o, 64);
+      b += __shfl_xor(b, o, 64);
+      l += __shfl_xor(l, o, 64);
+    }
+    out[j] = KlAcc{a, b, m, l};
+  }
+}
+
 // Sums over the 32 lanes of each half (the keys of a block): every lane of a
 // half ends with its positions' totals.
 template <int G>
@@ -332,16 +371,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       teacher_probs<G, LOCAL>(sc, lse2, rowok, ppos, (int64_t)cur.t * kBk, lane, c, P);
     }
     KlAcc acc[PM::NPL];
-#pragma unroll
-    for (int j = 0; j < PM::NPL; ++j) acc[j] = KlAcc{0.f, 0.f, -__builtin_huge_valf(), 0.f};
     {
       f32x16 zz[4];
       iq_ik_scores<DIDX, G>(IKs, iqw, lane, zz);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the index-query region has been read
       fetch_iq_rows<DIDX, G>(iqw, iq_src(nxt), lane);
-      student_fold<G, LOCAL>(zz, P, ppos, (int64_t)cur.t * kBk, lane, acc);
+      student_tile<G, LOCAL>(zz, P, ppos, (int64_t)cur.t * kBk, lane, acc);
     }
-    lanes_reduce<G>(acc);
     // the lane of each position's first head row writes its partial
 #pragma unroll
     for (int j = 0; j < PM::NPL; ++j) {
