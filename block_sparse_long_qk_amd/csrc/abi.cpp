@@ -2,6 +2,7 @@
 // dispatch.  Every check runs on the host before any HIP call, so a rejected
 // call enqueues nothing.
 #include <cmath>
+#include <climits>
 #include <cstddef>
 #include <cstring>
 
@@ -166,6 +167,12 @@ size_t bwd_part_bytes(const Dims& D) {
   return round256(sizeof(uint16_t) * (size_t)D.B * D.h_kv * D.n_q * (D.k + 1) * D.G * msa::kHeadDim);
 }
 size_t bwd_delta_bytes(const Dims& D) { return round256(sizeof(float) * (size_t)D.B * D.h_q * D.n_q); }
+// The backward walks keep per-row offsets within a sequence ((g G + h) n_q + i
+// and i h_q + g G + h) in 32 bits.  derive()'s tile bound (rows k G 2 < 2^32)
+// already implies h_q n_q < 2^31; the check keeps the walks safe should that
+// bound change.
+bool bwd_walk_ok(const Dims& D) { return (int64_t)D.h_q * D.n_q < INT32_MAX; }
+
 size_t bwd_bytes(const Dims& D) {
   return attn_ws_layout(D, nullptr, nullptr, false) + bwd_part_bytes(D) + bwd_delta_bytes(D);
 }
@@ -209,7 +216,7 @@ msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
       *bytes = pooled_bytes(D) + attn_bytes(D);
       return MSA_OK;
     case MSA_OP_SPARSE_ATTN_BWD:
-      if (D.n_blk > msa::kMaxPlanBlocks || D.kv_eb != 2) return MSA_ERR_UNSUPPORTED;
+      if (D.n_blk > msa::kMaxPlanBlocks || D.kv_eb != 2 || !bwd_walk_ok(D)) return MSA_ERR_UNSUPPORTED;
       *bytes = bwd_bytes(D);
       return MSA_OK;
     case MSA_OP_INDEX_KL:
@@ -217,7 +224,7 @@ msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
       *bytes = kl_bytes(D);
       return MSA_OK;
     case MSA_OP_INDEX_KL_BWD:
-      if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
+      if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D) || !bwd_walk_ok(D)) return MSA_ERR_UNSUPPORTED;
       *bytes = klb_bytes(D);
       return MSA_OK;
     default:
@@ -319,7 +326,7 @@ msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, 
       !aligned16(lse) || !aligned16(lse_index) || (dkl && !aligned16(dkl)) || !aligned16(d_index_q) ||
       !aligned16(d_index_k) || !aligned16(workspace))
     return MSA_ERR_INVALID_ARGUMENT;
-  if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
+  if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D) || !bwd_walk_ok(D)) return MSA_ERR_UNSUPPORTED;
   if (klb_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
   AttnWs ws;
   char* base = static_cast<char*>(workspace);
@@ -344,7 +351,7 @@ msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* 
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       !aligned16(workspace))
     return MSA_ERR_INVALID_ARGUMENT;
-  if (D.n_blk > msa::kMaxPlanBlocks || D.kv_eb != 2) return MSA_ERR_UNSUPPORTED;
+  if (D.n_blk > msa::kMaxPlanBlocks || D.kv_eb != 2 || !bwd_walk_ok(D)) return MSA_ERR_UNSUPPORTED;
   if (bwd_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
   AttnWs ws;
   char* base = static_cast<char*>(workspace);

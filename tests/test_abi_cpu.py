@@ -210,3 +210,4 @@ def test_fp8_kv_training_calls_unsupported(op):
     assert msa.library().msa_workspace_size(ctypes.byref(p), getattr(msa, op), ctypes.byref(n)) == \
         msa.ERR_UNSUPPORTED
     assert msa.workspace_size(prob(h_q=16, h_kv=2), getattr(msa, op)) > 0
+
