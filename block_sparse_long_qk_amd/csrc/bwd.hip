@@ -214,10 +214,12 @@ __device__ __forceinline__ void bld_step(Builder& bd, WalkTab& W, const AttnWs& 
 }
 
 // Transposed chunk copies [d][row] (pitch kTP) with the 4-row quads of dim d
-// XOR-swizzled by (d / 8) % 8: element (d, r) at d kTP + 4 ((r / 4) ^ ((d / 8) % 8)) + r % 4.
-// Writing a lane's 8 dims of one row then spreads over the banks, and the
-// 8-byte reads of an MFMA operand (quads c and 4 + c of dim d) stay conflict free.
-__device__ __forceinline__ int tp_at(int d, int r) { return d * kTP + 4 * ((r >> 2) ^ ((d >> 3) & 7)) + (r & 3); }
+// XOR-swizzled by (d / 16) % 8: element (d, r) at d kTP + 4 ((r / 4) ^ ((d / 16) % 8)) + r % 4.
+// With this swizzle (chosen by a bank model of both access patterns) the
+// 2-byte writes of a lane's 8 dims of one row and the 8-byte reads of an MFMA
+// operand (quads c and 4 + c of dims 16dt .. 16dt+15) each take the minimum
+// number of LDS passes; with (d / 8) % 8 both took twice that.
+__device__ __forceinline__ int tp_at(int d, int r) { return d * kTP + 4 * ((r >> 2) ^ ((d >> 4) & 7)) + (r & 3); }
 
 // dims 8p .. 8p+7 of row r (one 16-byte register piece) into a transposed copy
 __device__ __forceinline__ void tp_store8(uint16_t* dst, u32x4 v, int p, int r) {
@@ -230,7 +232,7 @@ __device__ __forceinline__ void tp_store8(uint16_t* dst, u32x4 v, int p, int r) 
 
 // the MFMA operand of dim d: rows 4c .. 4c+3 and 16+4c .. 16+4c+3
 __device__ __forceinline__ u32x4 tp_operand(const uint16_t* src, int d, int c) {
-  const int sw = (d >> 3) & 7;
+  const int sw = (d >> 4) & 7;
   const uint2 a = *reinterpret_cast<const uint2*>(src + d * kTP + 4 * (c ^ sw));
   const uint2 b = *reinterpret_cast<const uint2*>(src + d * kTP + 4 * ((4 + c) ^ sw));
   return u32x4{a.x, a.y, b.x, b.y};
