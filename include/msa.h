@@ -1,6 +1,9 @@
 /*
- * msa.h -- C ABI of the MiniMax Sparse Attention (MSA) forward pass for
- * AMD Instinct MI355X (gfx950).
+ * msa.h -- C ABI of MiniMax Sparse Attention (MSA) for AMD Instinct MI355X
+ * (gfx950): the forward pass (index scores, block top-k, sparse attention),
+ * variable-length and paged batches, FP8 index inputs and K/V caches, and the
+ * training-side calls (the KL alignment value and its gradient, the sparse
+ * attention backward, dense mode for the indexer warmup).
  *
  * The method (page "MiniMax 发布 MSA 稀疏注意力方法，开源推理内核并推出 MiniMax-M3
  * 模型", sections 什么是 MSA and 两个分支如何工作): an Index Branch scores every
@@ -40,8 +43,9 @@
  * Errors: argument checks run before any HIP call.  On failure nothing is
  * enqueued and the call returns MSA_ERR_INVALID_ARGUMENT (bad shapes, null or
  * misaligned pointers, q_offset + n_q > n_kv, k < 1, H_q % H_kv != 0, index
- * overflow, an unknown index_dtype) or MSA_ERR_UNSUPPORTED (shapes the kernels are not built for:
- * d != 128, d_idx not in {64, 128}, Bk != 128, k > 64, G > 128).  A failed
+ * overflow, an unknown index_dtype or kv_dtype) or MSA_ERR_UNSUPPORTED (shapes
+ * the kernels are not built for: d != 128, d_idx not in {64, 128}, Bk != 128,
+ * k > 64, G > 128; the further limits of each call are stated with it).  A failed
  * kernel launch returns MSA_ERR_HIP.  No C++ exception crosses the ABI.
  * All device pointers must be 16-byte aligned; NaN inputs are not supported.
  */
@@ -152,8 +156,10 @@ msa_status msa_block_topk(const msa_problem* p, const float* pooled, int32_t* bl
  * padding (as msa_block_topk writes it); the local block l_i is always
  * attended, listed or not.  out is bf16 (rounded to nearest even from fp32);
  * lse (nullable) gets ln sum_{j in T} exp(scale * q . k_j).  Scores and
- * sums are fp32; the probabilities enter P V with 16 significant bits (two
- * bf16 parts), so a row whose weight sits on a few keys keeps its accuracy.
+ * sums are fp32; the probabilities enter P V as bf16, and on the local block
+ * as two bf16 parts (16 significant bits), so a row whose weight sits on its
+ * few visible local keys keeps its accuracy.  With kv_dtype FP8 E4M3 the K and
+ * V codes are widened exactly to bf16 as they are loaded.
  * Needs workspace of msa_workspace_size(p, MSA_OP_SPARSE_ATTN).
  */
 msa_status msa_sparse_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v,
@@ -184,7 +190,7 @@ msa_status msa_forward(const msa_problem* p, const void* q, const void* k, const
  * lse is the natural-log output of msa_sparse_attn_fwd (or msa_forward) for
  * the same block_idx; the teacher is normalised by it, so its weights sum to 1
  * to within that lse's accuracy.  kl is [B][H_kv][n_q] fp32.  Supported for
- * G in {4, 8, 16, 32}, bf16 index inputs and uniform batches (else
+ * G in {4, 8, 16, 32}, bf16 index inputs, bf16 K/V and uniform batches (else
  * MSA_ERR_UNSUPPORTED).  Needs workspace of msa_workspace_size(p,
  * MSA_OP_INDEX_KL).  The training reduction (mean over rows, the loss weight)
  * and the gradient are the caller's.
@@ -227,7 +233,8 @@ msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, 
  *   dv[b][g][j] = sum over rows and heads of P_j dout.
  * out and lse are the forward's outputs for the same inputs; dq has q's layout,
  * dk and dv k's (bf16, overwritten; keys no row attends get 0).  Needs
- * workspace of msa_workspace_size(p, MSA_OP_SPARSE_ATTN_BWD); uniform batches.
+ * workspace of msa_workspace_size(p, MSA_OP_SPARSE_ATTN_BWD); uniform batches and bf16
+ * K/V (else MSA_ERR_UNSUPPORTED).
  * dk and dv are reduced without atomics (one workgroup owns each block), in
  * the order of the gather plan, whose rows within one block's bin may come in
  * a different order from run to run: results can differ in the last bits.
@@ -249,7 +256,8 @@ msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* 
  * T = { j <= p_i }; lse is msa_dense_attn_fwd's.  Same support as msa_index_kl (G in {4, 8, 16,
  * 32}, bf16 index inputs).  No workspace.
  *
- * Both take uniform batches (no msa_varlen form).
+ * Both take uniform batches (no msa_varlen form) and bf16 K/V (FP8 K/V:
+ * MSA_ERR_UNSUPPORTED).
  */
 msa_status msa_dense_attn_fwd(const msa_problem* p, const void* q, const void* k, const void* v, void* out, float* lse,
                               hipStream_t stream);
