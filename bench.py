@@ -108,6 +108,29 @@ def gpu_leg(w, steps, warmup, stream, paged=False, kl=False):
     ms_step = t.run(step, steps)
     wall = (time.perf_counter() - w0) * 1e3 / steps
 
+    if w.n_q == 1:
+        # decode: the same step captured once as a HIP graph and replayed (the
+        # calls enqueue kernels only, so the step captures as it is)
+        def step_cur():  # on the current stream, which is the capture stream while capturing
+            msa.forward(p, x["q"], x["k"], x["v"], x["iq"], x["ik"], f["out"], f["block_idx"], f["lse"],
+                        f["workspace"])
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_cur()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step_cur()
+        for _ in range(warmup):
+            graph.replay()
+        ms_graph = t.run(graph.replay, steps)
+        del graph
+    else:
+        ms_graph = None
+
     # stages alone, same stream, same buffers
     pooled = f["workspace"][:4 * w.batch * w.h_kv * w.n_q * w.n_blk].view(torch.float32)
     pooled = pooled.view(w.batch, w.h_kv, w.n_q, w.n_blk)
@@ -116,7 +139,8 @@ def gpu_leg(w, steps, warmup, stream, paged=False, kl=False):
     ms_topk = t.run(lambda: msa.block_topk(p, pooled, f["block_idx"], sp), steps)
     ms_attn = t.run(lambda: msa.sparse_attn_fwd(p, x["q"], x["k"], x["v"], f["block_idx"], f["out"], f["lse"],
                                                 attn_ws, stream=sp), steps)
-    res = {"ms_step": ms_step, "wall_ms_step": wall, "ms_index": ms_idx, "ms_topk": ms_topk, "ms_attn": ms_attn}
+    res = {"ms_step": ms_step, "wall_ms_step": wall, "ms_index": ms_idx, "ms_topk": ms_topk, "ms_attn": ms_attn,
+           "ms_step_graph": ms_graph}
     del attn_ws
     if kl and msa.workspace_size(p, msa.OP_INDEX_KL) > 0:
         # the KL alignment pass on this step's selection and lse
@@ -323,6 +347,8 @@ def main():
             "frac_of_copy": round(db / (gd["ms_step"] * 1e-3) / 1e9 / copy_gbs, 4),
             "stages_ms": {"index_scores": round(gd["ms_index"], 4), "block_topk": round(gd["ms_topk"], 4),
                           "sparse_attn": round(gd["ms_attn"], 4)},
+            "graph_ms_per_step": round(gd["ms_step_graph"], 4),
+            "graph_tokens_per_s": round(wd.batch / (gd["ms_step_graph"] * 1e-3), 1),
         }
 
     if "ms_kl" in g:
