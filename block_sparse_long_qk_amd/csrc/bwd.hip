@@ -809,6 +809,7 @@ hipError_t launch_index_kl_bwd(const uint16_t* q, const uint16_t* k, const uint1
                                float* dik_group, const Dims& D, hipStream_t stream) {
   if (ws.n_groups + 1 > kMaxSrc) return hipErrorInvalidValue;  // the walk's source table
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
+  if (e == hipSuccess) e = launch_plan_sort(ws, D, stream);  // a fixed summation order
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((int64_t)D.B * D.h_kv * D.n_blk)), block(kBwdThreads);
   auto go = [&](auto didx, auto gg) {
@@ -839,6 +840,7 @@ hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const ui
                                   const Dims& D, hipStream_t stream) {
   if (ws.n_groups + 1 > kMaxSrc) return hipErrorInvalidValue;  // the walk's source table
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
+  if (e == hipSuccess) e = launch_plan_sort(ws, D, stream);  // a fixed summation order
   if (e != hipSuccess) return e;
   const int64_t pairs = (int64_t)D.B * D.n_q * D.h_q;
   hipLaunchKernelGGL(k_bwd_delta, dim3((unsigned)((pairs * 8 + 255) / 256)), dim3(256), 0, stream, out, dout, delta,

@@ -214,6 +214,45 @@ __global__ void k_plan_tiles(const int32_t* __restrict__ cnt, const int32_t* __r
   }
 }
 
+// Canonical order of every bin's entries: ascending row-slot id.  The fill
+// places a bin's entries in the order the waves of a workgroup reach their
+// atomics, which can change from run to run; the attention forward does not
+// care (each entry is computed on its own), but sums over a bin's rows (the
+// backward passes) are reproducible only in a fixed order.  One workgroup
+// sorts one bin at a time in LDS (bitonic, padded to a power of two); a bin
+// holds at most one entry per row of its query group.
+constexpr int kSortCap = kChunkRows * kGroupChunks;
+__global__ __launch_bounds__(256) void k_plan_sort(const int32_t* __restrict__ cnt, const int32_t* __restrict__ tile_off,
+                                                   int2* __restrict__ list, int64_t n_bins, int32_t pt) {
+  __shared__ int32_t key[kSortCap];
+  for (int64_t bin = blockIdx.x; bin < n_bins; bin += gridDim.x) {
+    const int c = min(cnt[bin], kSortCap);  // uniform over the workgroup
+    if (c <= 1) continue;
+    int2* l = list + (int64_t)tile_off[bin] * pt;
+    int n = 2;
+    while (n < c) n <<= 1;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) key[i] = i < c ? l[i].x : 0x7FFFFFFF;
+    __syncthreads();
+    for (int k = 2; k <= n; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+          const int o = i ^ j;
+          if (o > i) {
+            const int a = key[i], b = key[o];
+            if ((a > b) == ((i & k) == 0)) {
+              key[i] = b;
+              key[o] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = threadIdx.x; i < c; i += blockDim.x) l[i].x = key[i];
+    __syncthreads();  // key[] is free for the next bin
+  }
+}
+
 unsigned grid_for(int64_t n, int threads) {
   int64_t g = (n + threads - 1) / threads;
   if (g < 1) g = 1;
@@ -246,6 +285,13 @@ hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const 
                      ws.part_lse, D, n_ch);
   hipLaunchKernelGGL(k_plan_tiles, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.cnt, ws.tile_off, ws.list,
                      nbgt, D.pt);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_sort(const AttnWs& ws, const Dims& D, hipStream_t stream) {
+  const int64_t nbgt = plan_bins(D);
+  hipLaunchKernelGGL(k_plan_sort, dim3(grid_for(nbgt, 1)), dim3(256), 0, stream, ws.cnt, ws.tile_off, ws.list, nbgt,
+                     D.pt);
   return hipGetLastError();
 }
 

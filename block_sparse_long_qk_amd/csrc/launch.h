@@ -23,6 +23,9 @@ hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims
 
 // Gather plan: per (b, g, block) lists of row-slot ids and the tile list.
 hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const Dims& D, hipStream_t stream);
+// Sorts every bin's entries of a built plan (ascending row-slot id), so that
+// sums over a bin's rows run in a fixed order.
+hipError_t launch_plan_sort(const AttnWs& ws, const Dims& D, hipStream_t stream);
 int64_t plan_chunks(const Dims& D);       // chunk workgroups per (b, g)
 int64_t plan_scan_blocks(const Dims& D);  // workgroups of the two-level scan
 int64_t plan_groups(const Dims& D);       // query groups (kGroupChunks chunks) per (b, g)

@@ -213,8 +213,8 @@ msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, cons
  * layouts (bf16, overwritten; keys no row reaches get 0).  Same support as
  * msa_index_kl; needs workspace of msa_workspace_size(p, MSA_OP_INDEX_KL_BWD).
  * Reduced without atomics (one workgroup per (sequence, group, block), then
- * the groups in order), over rows in the gather plan's order, which may vary
- * from run to run within a block: results can differ in the last bits.
+ * the groups in order) over rows in a fixed order (sorted plan bins), so the
+ * result is bitwise reproducible.
  */
 msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, const void* index_q,
                             const void* index_k, const int32_t* block_idx, const float* lse, const float* lse_index,
@@ -235,9 +235,9 @@ msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, 
  * dk and dv k's (bf16, overwritten; keys no row attends get 0).  Needs
  * workspace of msa_workspace_size(p, MSA_OP_SPARSE_ATTN_BWD); uniform batches and bf16
  * K/V (else MSA_ERR_UNSUPPORTED).
- * dk and dv are reduced without atomics (one workgroup owns each block), in
- * the order of the gather plan, whose rows within one block's bin may come in
- * a different order from run to run: results can differ in the last bits.
+ * dk and dv are reduced without atomics (one workgroup owns each block) over
+ * rows in a fixed order (the gather plan's bins are sorted by row and slot
+ * first), so the result is bitwise reproducible.
  */
 msa_status msa_sparse_attn_bwd(const msa_problem* p, const void* q, const void* k, const void* v,
                                const int32_t* block_idx, const void* out, const float* lse, const void* dout, void* dq,

@@ -110,3 +110,15 @@ def test_backward_32k_sampled_and_sum_rules():
     assert bool(((dv_sum - do_sum).abs() <= 1e-2 * scale_v).all())
     assert bool((dk_sum.abs() <= 1e-2 * scale_k).all())
     assert bool(torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all())
+
+
+def test_backward_is_deterministic():
+    """Two calls on the same inputs (fresh workspaces) give the same bits: the
+    plan's bins are sorted before the walk, so every sum runs in a fixed order."""
+    import torch
+    w = synth.WORKLOADS["prefill_32k"]
+    res = run_gpu(w, with_forward=False)
+    _, dq1, dk1, dv1 = run_bwd(w, res)
+    _, dq2, dk2, dv2 = run_bwd(w, res)
+    for name, a, b in (("dq", dq1, dq2), ("dk", dk1, dk2), ("dv", dv1, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name

@@ -124,3 +124,15 @@ def test_kl_backward_32k_sampled_and_sum_rule():
     say(f"    sum rule: max |sum_j d_ik_j| / sum_j |d_ik_j| = {(total.abs() / mag).max().item():.2e}")
     assert bool(torch.isfinite(dik).all())
     assert bool((total.abs() <= 1e-2 * mag).all())
+
+
+def test_kl_backward_is_deterministic():
+    """Two calls on the same inputs give the same bits (sorted plan bins, the
+    groups' d_index_k shares added in group order)."""
+    import torch
+    w = synth.WORKLOADS["prefill_32k"]
+    res = run_gpu(w, with_forward=False)
+    _, a_iq, a_ik = run_kl_bwd(w, res)
+    _, b_iq, b_ik = run_kl_bwd(w, res)
+    assert torch.equal(a_iq.view(torch.int16), b_iq.view(torch.int16))
+    assert torch.equal(a_ik.view(torch.int16), b_ik.view(torch.int16))
