@@ -35,6 +35,10 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint2 w) {
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
+// Word 3 of a gfx9 raw buffer descriptor (stride 0, byte-addressed records):
+// a 32-bit data format, so the range check is on bytes, offset < record count.
+constexpr int kRawBufferFlags = 0x00020000;
+
 // Problem dimensions as the kernels see them (all derived on the host).
 struct Dims {
   int32_t B, n_q, n_kv, h_q, h_kv, G, d, d_idx, k, n_blk;

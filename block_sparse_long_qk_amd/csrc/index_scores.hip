@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int tile = gridDim.x - 1 - blockIdx.x;     // heaviest (latest) rows first
   const int row0 = tile * 256;
   if (VL && row0 >= rows_total) return;            // uniform over the workgroup
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
 
   const int last_row = min(row0 + 255, rows_total - 1);
@@ -156,33 +156,83 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     ti[s] = -1;
   }
 
-  // Key blocks arrive by direct global-to-LDS loads one block ahead: the
+  // KK > 0: a block whose score beats the lane's current KK-th waits in a
+  // per-lane LDS list; the lists are merged into the registers, in block order,
+  // once some lane's list is nearly full and at the end.  The wave then runs the
+  // insertion once per few candidates of its busiest lane instead of in every
+  // block where any of its 64 rows has one.  The merge tests each candidate
+  // against the KK-th score of that moment, and the listing test admits a
+  // superset of those, so the kept set is the one that inserting at every block
+  // would keep.
+  constexpr int kCand = 7;  // entries per lane: 4 waves x 7 x 64 x 8 bytes = 14 KB
+  __shared__ float2 cand[KK > 0 ? 4 : 1][KK > 0 ? kCand : 1][64];
+  int n_cand = 0;
+  // insert (v, bt) into the lane's list sorted by (score desc, block asc); an
+  // equal score never displaces an earlier block
+  auto insert = [&](float v, int bt) {
+    bool ge[KK > 0 ? KK : 1];
+#pragma unroll
+    for (int s = 0; s < KK; ++s) ge[s] = tv[s] >= v;
+#pragma unroll
+    for (int s = KK - 1; s >= 0; --s) {
+      const bool here = s == 0 || ge[s - 1];
+      const float sv = here ? v : tv[s > 0 ? s - 1 : 0];
+      const int si = here ? bt : ti[s > 0 ? s - 1 : 0];
+      tv[s] = ge[s] ? tv[s] : sv;
+      ti[s] = ge[s] ? ti[s] : si;
+    }
+  };
+  auto merge = [&]() {
+#pragma unroll 1
+    for (int j = 0; j < kCand; ++j) {
+      if (j < n_cand) {
+        const float2 e = cand[wave][j][lane];
+        if (e.x > tv[KK > 0 ? KK - 1 : 0]) insert(e.x, __float_as_int(e.y));
+      }
+    }
+    n_cand = 0;
+  };
+
+  // Key blocks arrive by direct buffer-to-LDS loads one block ahead: the
   // hardware writes lane l's 16 bytes at l * 16 past the instruction's LDS
   // address, so lane l of instruction i fetches the chunk that belongs in slot
-  // l % CPR of row RPI * i + l / CPR.  Keys past the cache end repeat its last
-  // key: finite values the causal mask drops (they follow every row's
-  // position), so the loads need no per-key branch.
+  // l % CPR of row RPI * i + l / CPR.  Each instruction gets a descriptor of its
+  // own 1024 bytes whose record count stops at the cache end: the range check
+  // drops the loads of keys past it, whose LDS rows keep stale bytes that the
+  // causal mask replaces by -inf (a select, so any bit pattern goes) before
+  // they are pooled, as those keys follow every row's position.
+  //
+  // A lane's offset within an instruction's 1024 bytes is the chunk swizzle of
+  // its row, periodic in i with period SP: pattern v is pattern 0 with bits 6-7
+  // xor-ed by v (the swizzle's periodic part and the lane's own chunk bits do
+  // not overlap), so one register holds them all.
   const unsigned char* ikb = ik + (int64_t)b * D.n_kv * C::ROWB;  // uniform case: sequence b's keys
+  constexpr int SP = C::ROWB == 256 ? 4 : C::ROWB == 128 ? 2 : 1;
+  static_assert(C::NI % SP == 0, "the load index of a lane's u-th load is u modulo SP");
+  const uint32_t lane_pat0 = (lane / C::CPR) * C::ROWB + 16 * ((lane % C::CPR) ^ C::swz(lane / C::CPR));
   auto fetch_block = [&](int t, unsigned char* dst) {
-    // the block's keys are contiguous (a page when paged); past its last cached
-    // key the last one repeats
+    // the block's keys are contiguous (a page when paged); `n_cached` of them
+    // (at least one) precede the cache end
     const unsigned char* blk;
-    int last;
+    int n_cached;
     if constexpr (VL) {
       blk = ik + ikoff_of<VL>(D, b, t) * EB;
-      last = nkv_b - 1 - t * kBk;
+      n_cached = nkv_b - t * kBk;
     } else {
-      blk = ikb;
-      last = D.n_kv - 1;
+      blk = ikb + (int64_t)t * kBk * C::ROWB;
+      n_cached = D.n_kv - t * kBk;
     }
-    const int j0 = VL ? 0 : t * kBk;
+    const int bytes = min(n_cached, kBk) * C::ROWB;
+    // recomputed per block: kept out of the loop, the SP patterns would pin SP registers
+    uint32_t pat = lane_pat0;
+    asm volatile("" : "+v"(pat));
 #pragma unroll
     for (int u = 0; u < C::NI; ++u) {
       const int i = wave * C::NI + u;
-      const int row = C::RPI * i + lane / C::CPR, sl = lane % C::CPR;
-      const int64_t jr = min(j0 + row, last);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(blk + jr * C::ROWB + 16 * (sl ^ C::swz(row))),
-                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned char*>(blk) + 1024 * i, (short)0, max(bytes - 1024 * i, 0), kRawBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16,
+                                               pat ^ (64u * (u % SP)), 0, 0, 0);
     }
   };
 
@@ -255,9 +305,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             }
           }
 #pragma unroll
-          for (int e = 0; e < 16; e += 2) {
-            run0 = fmaxf(run0, fmaxf(x0[e], x0[e + 1]));
-            run1 = fmaxf(run1, fmaxf(x1[e], x1[e + 1]));
+          for (int e = 0; e < 16; e += 2) {  // max(max(r, a), b): one v_max3 per two scores
+            run0 = fmaxf(fmaxf(run0, x0[e]), x0[e + 1]);
+            run1 = fmaxf(fmaxf(run1, x1[e]), x1[e + 1]);
           }
         };
         pool(a00, a01, 2 * mp);
@@ -283,20 +333,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           }
         }
       } else {
-        // running top-KK of the non-local blocks (t < l_out); an equal score
-        // never displaces an earlier block
+        // a candidate for the running top-KK of the non-local blocks (t < l_out)
         if (t < l_out && v > tv[KK - 1]) {
-          bool ge[KK];
-#pragma unroll
-          for (int s = 0; s < KK; ++s) ge[s] = tv[s] >= v;
-#pragma unroll
-          for (int s = KK - 1; s >= 0; --s) {
-            const bool here = s == 0 || ge[s - 1];
-            const float sv = here ? v : tv[s > 0 ? s - 1 : 0];
-            const int si = here ? t : ti[s > 0 ? s - 1 : 0];
-            tv[s] = ge[s] ? tv[s] : sv;
-            ti[s] = ge[s] ? ti[s] : si;
-          }
+          cand[wave][n_cand][lane] = make_float2(v, __int_as_float(t));
+          ++n_cand;
         }
       }
     }
@@ -304,7 +344,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int t = t_begin; t < t_end; t += 2) {
     process(t, std::integral_constant<int, 0>{});
     if (t + 1 < t_end) process(t + 1, std::integral_constant<int, 1>{});
+    // a pair of blocks lists at most two: merge while every list has room for them
+    if constexpr (KK > 0)
+      if (wave_active && __builtin_amdgcn_ballot_w64(n_cand > kCand - 2) != 0) merge();
   }
+  if constexpr (KK > 0)
+    if (wave_active) merge();
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the last (unused) block fetch has landed before the workgroup ends
 
   if constexpr (KK > 0) {
