@@ -38,11 +38,33 @@ struct IdxCfg {
   static constexpr int RPK = F8 ? 4 : 2;            // 16-byte LDS reads per k-step (two key rows)
   static constexpr int CPR = ROWB / 16;             // 16-byte chunks per key row
   static constexpr int RPI = 1024 / ROWB;           // key rows per 1 KB direct-to-LDS instruction
-  static constexpr int NI = kBk / RPI / 4;          // such instructions per wave per block
-  // slot of chunk c of key row r is c ^ swz(r): the 16 lanes reading one chunk
-  // of 16 consecutive rows then cover all 64 banks once
-  static __device__ __forceinline__ int swz(int r) {
-    return ROWB == 256 ? (r & 15) : ROWB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+  static constexpr int NG = kBk / RPI;              // such instructions per block
+  static constexpr int NI = NG / 4;                 // per wave
+  // LDS layout of a block.  Instruction g writes its 1 KB (RPI rows, row slot j
+  // at j * ROWB, chunks in order) at g * PITCH; the 16-byte pad shifts each
+  // instruction's rows by one bank group.  The rows an instruction holds are
+  // chosen so that (a) a 32-key tile k (key rows 32k..32k+31) sits 256 k bytes
+  // past tile 0 in every slot, so a lane's fragment address is one base plus an
+  // immediate offset, and (b) the 16 lanes reading one chunk of rows
+  // 32k+16h..32k+16h+15 land on 16 different bank groups:
+  //   ROWB 256: row r in instruction r % 32, slot r / 32;
+  //   ROWB 128: instruction r % 16, slot r / 16;
+  //   ROWB  64: instruction r % 4 + 4 ((r / 16) % 2), slot (r / 4) % 4 + 4 (r / 32).
+  static constexpr int PITCH = 1024 + 16;
+  // byte offset, within the block's keys in HBM, of the chunk lane l of
+  // instruction g fetches: dma_group(g) (uniform) + dma_lane(l)
+  static __device__ __forceinline__ int dma_group(int g) {
+    return ROWB == 256 ? 256 * g : ROWB == 128 ? 128 * g : 64 * (16 * (g / 4) + g % 4);
+  }
+  static __device__ __forceinline__ int dma_lane(int l) {
+    const int j = l / CPR, c = l % CPR;
+    return (ROWB == 256 ? 32 * 256 * j : ROWB == 128 ? 16 * 128 * j : 64 * (32 * (j / 4) + 4 * (j % 4))) + 16 * c;
+  }
+  // LDS byte offset of chunk 0 of key row r
+  static __device__ __forceinline__ int lds_row(int r) {
+    const int g = ROWB == 256 ? r % 32 : ROWB == 128 ? r % 16 : r % 4 + 4 * ((r / 16) % 2);
+    const int j = ROWB == 256 ? r / 32 : ROWB == 128 ? r / 16 : (r / 4) % 4 + 4 * (r / 32);
+    return g * PITCH + j * ROWB;
   }
   using Frag = std::conditional_t<F8, i32x8, uint4>;
 };
@@ -88,8 +110,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // two key blocks (rows unpadded, chunks swizzled) as two separate arrays, each
   // named statically where it is used: the compiler can then tell a read of
   // one from the direct-to-LDS loads filling the other and does not wait for them
-  __shared__ __align__(16) unsigned char lds0[kBk * C::ROWB];
-  __shared__ __align__(16) unsigned char lds1[kBk * C::ROWB];
+  __shared__ __align__(16) unsigned char lds0[C::NG * C::PITCH];
+  __shared__ __align__(16) unsigned char lds1[C::NG * C::PITCH];
   __shared__ __align__(16) float pstage[KK == 0 ? 4 : 1][64][kPoolStage];  // per-lane pooled staging
   const float NEG_INF = -__builtin_huge_valf();
 
@@ -193,23 +215,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     n_cand = 0;
   };
 
-  // Key blocks arrive by direct buffer-to-LDS loads one block ahead: the
-  // hardware writes lane l's 16 bytes at l * 16 past the instruction's LDS
-  // address, so lane l of instruction i fetches the chunk that belongs in slot
-  // l % CPR of row RPI * i + l / CPR.  Each instruction gets a descriptor of its
-  // own 1024 bytes whose record count stops at the cache end: the range check
-  // drops the loads of keys past it, whose LDS rows keep stale bytes that the
-  // causal mask replaces by -inf (a select, so any bit pattern goes) before
-  // they are pooled, as those keys follow every row's position.
-  //
-  // A lane's offset within an instruction's 1024 bytes is the chunk swizzle of
-  // its row, periodic in i with period SP: pattern v is pattern 0 with bits 6-7
-  // xor-ed by v (the swizzle's periodic part and the lane's own chunk bits do
-  // not overlap), so one register holds them all.
+  // Key blocks arrive by direct buffer-to-LDS loads one block ahead, in the
+  // layout above: the hardware writes lane l's 16 bytes at l * 16 past the
+  // instruction's LDS address.  Each instruction gets a scalar descriptor whose
+  // base is its uniform part of the block and whose record count stops at the
+  // cache end: the range check drops the loads of keys past it, whose LDS rows
+  // keep stale bytes that the causal mask replaces by -inf (a select, so any
+  // bit pattern goes) before they are pooled, as those keys follow every row's
+  // position.  The lane part of every load is one loop-invariant register.
   const unsigned char* ikb = ik + (int64_t)b * D.n_kv * C::ROWB;  // uniform case: sequence b's keys
-  constexpr int SP = C::ROWB == 256 ? 4 : C::ROWB == 128 ? 2 : 1;
-  static_assert(C::NI % SP == 0, "the load index of a lane's u-th load is u modulo SP");
-  const uint32_t lane_pat0 = (lane / C::CPR) * C::ROWB + 16 * ((lane % C::CPR) ^ C::swz(lane / C::CPR));
+  const uint32_t dma_off = C::dma_lane(lane);
   auto fetch_block = [&](int t, unsigned char* dst) {
     // the block's keys are contiguous (a page when paged); `n_cached` of them
     // (at least one) precede the cache end
@@ -223,18 +238,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       n_cached = D.n_kv - t * kBk;
     }
     const int bytes = min(n_cached, kBk) * C::ROWB;
-    // recomputed per block: kept out of the loop, the SP patterns would pin SP registers
-    uint32_t pat = lane_pat0;
-    asm volatile("" : "+v"(pat));
 #pragma unroll
     for (int u = 0; u < C::NI; ++u) {
-      const int i = wave * C::NI + u;
+      const int g = wave * C::NI + u;
+      const int go = C::dma_group(g);
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<unsigned char*>(blk) + 1024 * i, (short)0, max(bytes - 1024 * i, 0), kRawBufferFlags);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16,
-                                               pat ^ (64u * (u % SP)), 0, 0, 0);
+          const_cast<unsigned char*>(blk) + go, (short)0, max(bytes - go, 0), kRawBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + g * C::PITCH), 16,
+                                               dma_off, 0, 0, 0);
     }
   };
+  // this lane's fragment base: key row `col` (tile 0), its half's chunk
+  const int rd_base = C::lds_row(col) + (C::F8 ? 32 : 16) * half;
 
   fetch_block(t_begin, lds0);
   auto process = [&](int t, auto buf_c) {
@@ -250,50 +265,89 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (wave_active) {
       const bool need_mask = (int64_t)t * kBk + kBk - 1 > p_wave_min;
       float run0 = NEG_INF, run1 = NEG_INF;
-      // two 32-key row tiles per iteration: four MFMA chains (32 bf16 or 8 E4M3
-      // MFMAs) between epilogues, each LDS fragment feeding two MFMAs
-#pragma unroll 1
-      for (int mp = 0; mp < 2; ++mp) {
-        f32x16 a00 = {}, a01 = {}, a10 = {}, a11 = {};
-        const int r0 = 64 * mp + col, r1 = r0 + 32;
-        const unsigned char* arow0 = cur + r0 * C::ROWB;
-        const unsigned char* arow1 = cur + r1 * C::ROWB;
-        const int sw0 = C::swz(r0), sw1 = C::swz(r1);
-        // this lane's FB bytes of k-step ks of a key row (chunks 2ks+half, or
-        // 4ks+2half and the next for E4M3)
-        auto frag = [&](const unsigned char* row, int sw, int ks) -> Frag {
-          if constexpr (C::F8) {
-            const int c0 = 4 * ks + 2 * half;
-            return join32(*reinterpret_cast<const u32x4*>(row + 16 * (c0 ^ sw)),
-                          *reinterpret_cast<const u32x4*>(row + 16 * ((c0 + 1) ^ sw)));
-          } else {
-            return *reinterpret_cast<const uint4*>(row + 16 * ((2 * ks + half) ^ sw));
+      // this lane's FB bytes of k-step ks of its key row in tile k (chunk
+      // 2ks+half, or chunks 4ks+2half and the next for E4M3): immediate offsets
+      const unsigned char* rd = cur + rd_base;
+      auto frag = [&](int k, int ks) -> Frag {
+        const unsigned char* p = rd + 256 * k + C::FB * 2 * ks;
+        if constexpr (C::F8)
+          return join32(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 16));
+        else
+          return *reinterpret_cast<const uint4*>(p);
+      };
+      auto mma = [&](Frag a, Frag bq, f32x16 c) {
+        if constexpr (C::F8) return mfma_f8_32x32x64(a, bq, c);
+        else return mfma_32x32x16(a, bq, c);
+      };
+      // max-pool of one 32-key tile's two query tiles: max(max(r, a), b) is one v_max3 per two scores
+      auto pool_tile = [&](const f32x16& x0, const f32x16& x1) {
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          run0 = fmaxf(fmaxf(run0, x0[e]), x0[e + 1]);
+          run1 = fmaxf(fmaxf(run1, x1[e]), x1[e + 1]);
+        }
+      };
+      if (!need_mask) {
+        // Every key of the block is visible to every row of the wave.  The four
+        // 32-key tiles form one straight-line region in which tile k's MFMAs
+        // (two chains, each LDS fragment feeding both) are interleaved with the
+        // max-pool of tile k-1, so the pool's VALU work issues while the MFMA
+        // pipe is busy; only the last tile's pool is left after the MFMAs.
+        // Software-pipelined over the 4 KS steps (tile k = st / KS, k-step
+        // st % KS): step st's fragment is read two steps ahead into a ring of
+        // three, and tile k-1's pool is spread over tile k's steps.  A
+        // scheduling barrier closes each step, so the compiler cannot sink the
+        // reads back next to their MFMAs to save registers.
+        constexpr int STEPS = 4 * C::KS, EPS = 16 / C::KS;  // pooled elements per accumulator per step
+        Frag fr[3];
+        f32x16 acc[2][2];  // [tile parity][query tile]
+        fr[0] = frag(0, 0);
+        if (STEPS > 1) fr[1] = frag(1 / C::KS, 1 % C::KS);
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+          const int k = st / C::KS, ks = st % C::KS;
+          if (st + 2 < STEPS) fr[(st + 2) % 3] = frag((st + 2) / C::KS, (st + 2) % C::KS);
+          f32x16& x0 = acc[k & 1][0];
+          f32x16& x1 = acc[k & 1][1];
+          x0 = mma(fr[st % 3], qb[0][ks], ks == 0 ? f32x16{} : x0);
+          x1 = mma(fr[st % 3], qb[1][ks], ks == 0 ? f32x16{} : x1);
+          if (k > 0) {
+            const f32x16& p0 = acc[(k - 1) & 1][0];
+            const f32x16& p1 = acc[(k - 1) & 1][1];
+#pragma unroll
+            for (int e = EPS * ks; e < EPS * (ks + 1); e += 2) {  // max(max(r, a), b): one v_max3
+              run0 = fmaxf(fmaxf(run0, p0[e]), p0[e + 1]);
+              run1 = fmaxf(fmaxf(run1, p1[e]), p1[e + 1]);
+            }
           }
-        };
-        auto mma = [&](Frag a, Frag bq, f32x16 c) {
-          if constexpr (C::F8) return mfma_f8_32x32x64(a, bq, c);
-          else return mfma_32x32x16(a, bq, c);
-        };
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const Frag f0 = frag(arow0, sw0, ks);
-          const Frag f1 = frag(arow1, sw1, ks);
-          a00 = mma(f0, qb[0][ks], a00);
-          a01 = mma(f0, qb[1][ks], a01);
-          a10 = mma(f1, qb[0][ks], a10);
-          a11 = mma(f1, qb[1][ks], a11);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // LDS reads two k-steps ahead of their MFMAs
-        constexpr int AHEAD = C::KS < 2 ? C::KS : 2;
-        __builtin_amdgcn_sched_group_barrier(0x100, C::RPK * AHEAD, 0);
+        pool_tile(acc[1][0], acc[1][1]);
+      } else {
+        // two 32-key row tiles per iteration: four MFMA chains (32 bf16 or 8 E4M3
+        // MFMAs) between epilogues, each LDS fragment feeding two MFMAs
+#pragma unroll 1
+        for (int mp = 0; mp < 2; ++mp) {
+          f32x16 a00 = {}, a01 = {}, a10 = {}, a11 = {};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          if (ks + 2 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, C::RPK, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        }
-        auto pool = [&](f32x16& x0, f32x16& x1, int mt) {
-          if (need_mask) {
-            // key (t*Bk + 32*mt + row) is visible to column position p iff row <= p - (t*Bk + 32*mt)
+          for (int ks = 0; ks < C::KS; ++ks) {
+            const Frag f0 = frag(2 * mp, ks);
+            const Frag f1 = frag(2 * mp + 1, ks);
+            a00 = mma(f0, qb[0][ks], a00);
+            a01 = mma(f0, qb[1][ks], a01);
+            a10 = mma(f1, qb[0][ks], a10);
+            a11 = mma(f1, qb[1][ks], a11);
+          }
+          // LDS reads two k-steps ahead of their MFMAs
+          constexpr int AHEAD = C::KS < 2 ? C::KS : 2;
+          __builtin_amdgcn_sched_group_barrier(0x100, C::RPK * AHEAD, 0);
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            if (ks + 2 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, C::RPK, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          }
+          // key (t*Bk + 32*mt + row) is visible to column position p iff row <= p - (t*Bk + 32*mt)
+          auto mask = [&](f32x16& x0, f32x16& x1, int mt) {
             const int64_t base = (int64_t)t * kBk + 32 * mt;
             const int rel0 = (int)max<int64_t>(-1, min<int64_t>(64, pc[0] - base)) - 4 * half;
             const int rel1 = (int)max<int64_t>(-1, min<int64_t>(64, pc[1] - base)) - 4 * half;
@@ -303,15 +357,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
               if (row > rel0) x0[e] = NEG_INF;
               if (row > rel1) x1[e] = NEG_INF;
             }
-          }
-#pragma unroll
-          for (int e = 0; e < 16; e += 2) {  // max(max(r, a), b): one v_max3 per two scores
-            run0 = fmaxf(fmaxf(run0, x0[e]), x0[e + 1]);
-            run1 = fmaxf(fmaxf(run1, x1[e]), x1[e + 1]);
-          }
-        };
-        pool(a00, a01, 2 * mp);
-        pool(a10, a11, 2 * mp + 1);
+          };
+          mask(a00, a01, 2 * mp);
+          mask(a10, a11, 2 * mp + 1);
+          pool_tile(a00, a01);
+          pool_tile(a10, a11);
+        }
       }
       run0 = fmaxf(run0, wave_xor32(run0));
       run1 = fmaxf(run1, wave_xor32(run1));
