@@ -28,7 +28,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x2, calibrated on a 1 GiB copy) + WRITE_SIZE (x1); see
 # profiles/prefill_128k_attention_index_counters.md.  Valid for this kernel
 # version only: re-measure (or set None) when the kernel changes.
-INDEX_TRAFFIC_BYTES = (2.9515e6 * 2 + 2.1472e6) * 1024
+INDEX_TRAFFIC_BYTES = (2.5965e6 * 2 + 2.335e6) * 1024
 # The same for one msa_sparse_attn_fwd at 128K: k_attn_tiles<false> plus
 # k_attn_local_merge (the plan kernels add under 1%).
 ATTN_TRAFFIC_BYTES = ((1.7700e7 + 1.8653e7) * 2 + 3.1715e7 + 2.2894e6) * 1024
