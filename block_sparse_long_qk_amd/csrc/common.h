@@ -181,6 +181,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Reduction over the 32 lanes of each half-wave with DPP moves inside rows of
+// 16 lanes (xor 1 and xor 2 by quad permutes, then the half-row and row
+// mirrors), after which every lane of a row holds its row's total, and four
+// lane reads that combine the two rows of each half.  No LDS round trip; every
+// lane of a half gets the same value (from lanes 0 and 16, or 32 and 48).
+// Needs all 64 lanes active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <typename Op>
+__device__ __forceinline__ float half_reduce(float x, Op op) {
+  x = op(x, dpp_move<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = op(x, dpp_move<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  x = op(x, dpp_move<0x141>(x));  // row_half_mirror
+  x = op(x, dpp_move<0x140>(x));  // row_mirror
+  const int xi = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  return (threadIdx.x & 32) ? op(r2, r3) : op(r0, r1);
+}
+__device__ __forceinline__ float half_max(float x) {
+  return half_reduce(x, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float half_sum(float x) {
+  return half_reduce(x, [](float a, float b) { return a + b; });
+}
+
 // A 32x32 MFMA accumulator register e of lane l holds row 8*(e/4) + 4*(l/32) + e%4,
 // column l%32.
 __device__ __forceinline__ int acc_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }

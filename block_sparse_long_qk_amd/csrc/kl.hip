@@ -157,26 +157,64 @@ __device__ __forceinline__ KlAcc kl_combine(KlAcc x, KlAcc y) {
   return KlAcc{x.a + y.a, x.b + y.b, m, lx + ly};
 }
 
+// Visibility limit of a lane-local position for this lane's key column: key
+// key0 + 32T + col is visible iff 32T <= limit.  -1 for a position without a
+// row; 127 (every key) when the tile needs no mask; else the position's
+// offset past the column's first key, clamped to [-1, 127].
+template <bool MASKED>
+__device__ __forceinline__ int key_limit(int valid, int64_t pos, int64_t key0, int col) {
+  if (!valid) return -1;
+  if (!MASKED) return 127;
+  return (int)max<int64_t>(-1, min<int64_t>(127, pos - key0 - col));
+}
+
+// The lse (log2 units) of the 16 query rows a lane's accumulator registers
+// hold (rows 8(e/4) + 4 half + e%4 of the wave's 32), through the wave's
+// 32-float LDS slot: both lanes of a row (l and l ^ 32 hold the same row)
+// write its value, and every lane reads its rows as four float4s (no
+// shuffles).  A row that does not exist must carry +inf, so that all its
+// probabilities come out exactly 0.
+__device__ __forceinline__ void rows_lse(float* slot, float lse_mine, int lane, float (&lse2)[16]) {
+  slot[lane & 31] = lse_mine;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float4 v = *reinterpret_cast<const float4*>(slot + 8 * m + 4 * half);
+    lse2[4 * m] = v.x;
+    lse2[4 * m + 1] = v.y;
+    lse2[4 * m + 2] = v.z;
+    lse2[4 * m + 3] = v.w;
+  }
+}
+
+// Value x of the first head row of lane-local position j (lane wpos(j, half) * G):
+// two lane reads with constant lanes, no shuffle.
+template <int G>
+__device__ __forceinline__ int pos_value(int x, int j, int half) {
+  const int v0 = __builtin_amdgcn_readlane(x, PosMap<G>::wpos(j, 0) * G);
+  const int v1 = __builtin_amdgcn_readlane(x, PosMap<G>::wpos(j, 1) * G);
+  return half ? v1 : v0;
+}
+
 // Teacher probabilities of one tile for one wave: P[T][j] is the group's
 // average probability of key key0 + 32T + column for lane-local position j
-// (0 for keys after the position and for rows that do not exist).
+// (0 for keys after the position and for rows that do not exist, whose lse2
+// is +inf).
 template <int G, bool MASKED>
-__device__ __forceinline__ void teacher_probs(const f32x16 (&s)[4], const float (&lse2)[16], const bool (&rowok)[16],
-                                              const int64_t (&ppos)[PosMap<G>::NPL], int64_t key0, int lane,
-                                              float c, float (&P)[4][PosMap<G>::NPL]) {
+__device__ __forceinline__ void teacher_probs(const f32x16 (&s)[4], const float (&lse2)[16],
+                                              const int (&lim)[PosMap<G>::NPL], float c,
+                                              float (&P)[4][PosMap<G>::NPL]) {
   using PM = PosMap<G>;
-  const int col = lane & 31;
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
-    const int64_t key = key0 + 32 * T + col;
 #pragma unroll
     for (int j = 0; j < PM::NPL; ++j) {
       float psum = 0.f;
 #pragma unroll
       for (int e = j * PM::RPP; e < (j + 1) * PM::RPP; ++e)
-        psum += rowok[e] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[T][e], c, -lse2[e])) : 0.f;
+        psum += __builtin_amdgcn_exp2f(__builtin_fmaf(s[T][e], c, -lse2[e]));  // 0 for an absent row
       if constexpr (G >= 8) psum += wave_xor32(psum);
-      const bool vis = !MASKED || key <= ppos[j];
+      const bool vis = !MASKED || 32 * T <= lim[j];
       P[T][j] = vis ? psum * (1.f / G) : 0.f;
     }
   }
@@ -187,23 +225,21 @@ __device__ __forceinline__ void teacher_probs(const f32x16 (&s)[4], const float 
 // lanes).
 template <int G, bool MASKED>
 __device__ __forceinline__ void student_fold(const f32x16 (&z)[4], const float (&P)[4][PosMap<G>::NPL],
-                                             const int64_t (&ppos)[PosMap<G>::NPL], int64_t key0, int lane,
-                                             KlAcc (&acc)[PosMap<G>::NPL]) {
+                                             const int (&lim)[PosMap<G>::NPL], KlAcc (&acc)[PosMap<G>::NPL]) {
   using PM = PosMap<G>;
   const float NEG_INF = -__builtin_huge_valf();
-  const int col = lane & 31;
 #pragma unroll
   for (int j = 0; j < PM::NPL; ++j) {
     KlAcc x{0.f, 0.f, NEG_INF, 0.f};
     // max of the visible scores, then the sums
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      const bool vis = ppos[j] >= 0 && (!MASKED || key0 + 32 * T + col <= ppos[j]);
+      const bool vis = 32 * T <= lim[j];
       if (vis) x.m = fmaxf(x.m, z[T][j * PM::RPP] * kLog2e);
     }
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      const bool vis = ppos[j] >= 0 && (!MASKED || key0 + 32 * T + col <= ppos[j]);
+      const bool vis = 32 * T <= lim[j];
       const float zz = z[T][j * PM::RPP], p = P[T][j];
       if (p > 0.f) x.a += p * __log2f(p);
       x.b += p * zz;
@@ -216,24 +252,21 @@ __device__ __forceinline__ void student_fold(const f32x16 (&z)[4], const float (
 // One tile's KL partials for this lane's positions over the block's 128 keys
 // (the 32 lanes of a half hold 4 keys each): the max of the visible student
 // scores first (a max over the lanes), then the three sums with that common
-// max, added over the lanes.  Every lane of a half ends with the totals; a
-// position without visible keys gets m = -inf and l = 0.
+// max, added over the lanes (DPP reductions, no LDS).  Every lane of a half
+// ends with the totals; a position without visible keys gets m = -inf and l = 0.
 template <int G, bool MASKED>
 __device__ __forceinline__ void student_tile(const f32x16 (&z)[4], const float (&P)[4][PosMap<G>::NPL],
-                                             const int64_t (&ppos)[PosMap<G>::NPL], int64_t key0, int lane,
-                                             KlAcc (&out)[PosMap<G>::NPL]) {
+                                             const int (&lim)[PosMap<G>::NPL], KlAcc (&out)[PosMap<G>::NPL]) {
   using PM = PosMap<G>;
   const float NEG_INF = -__builtin_huge_valf();
-  const int col = lane & 31;
 #pragma unroll
   for (int j = 0; j < PM::NPL; ++j) {
-    auto visible = [&](int T) { return ppos[j] >= 0 && (!MASKED || key0 + 32 * T + col <= ppos[j]); };
+    auto visible = [&](int T) { return 32 * T <= lim[j]; };
     float m = NEG_INF;
 #pragma unroll
     for (int T = 0; T < 4; ++T)
       if (visible(T)) m = fmaxf(m, z[T][j * PM::RPP] * kLog2e);
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = half_max(m);
     float a = 0.f, b = 0.f, l = 0.f;
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
@@ -242,13 +275,7 @@ __device__ __forceinline__ void student_tile(const f32x16 (&z)[4], const float (
       b += p * zz;
       if (visible(T)) l += __builtin_amdgcn_exp2f(zz * kLog2e - m);
     }
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      a += __shfl_xor(a, o, 64);
-      b += __shfl_xor(b, o, 64);
-      l += __shfl_xor(l, o, 64);
-    }
-    out[j] = KlAcc{a, b, m, l};
+    out[j] = KlAcc{half_sum(a), half_sum(b), m, half_sum(l)};
   }
 }
 
@@ -280,6 +307,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __align__(16) uint16_t IKs[kBk * IKP];
   __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];
   __shared__ __align__(16) unsigned char IQs[kWaves][kIqRows * 2 * DIDX];
+  __shared__ __align__(16) float LSs[kWaves][32];
   int total;
   if constexpr (LOCAL) {
     total = D.B * D.h_kv * local_tiles<false>(D);
@@ -335,26 +363,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       __syncthreads();
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's query and index-query rows have landed
-    const float lse_mine = lse_raw * kLog2e;
-    const bool row_ok = cur.valid;
-    // the lse and validity of the 16 rows this lane's registers hold
+    // the lse of the 16 rows this lane's registers hold (+inf: no such row)
     float lse2[16];
-    bool rowok[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int re = 8 * (e >> 2) + 4 * half + (e & 3);
-      lse2[e] = __shfl(lse_mine, re, 64);
-      rowok[e] = __shfl((int)row_ok, re, 64) != 0;
-    }
-    int64_t ppos[PM::NPL];  // position of each lane-local position (-1: no such row)
+    rows_lse(LSs[wave], cur.valid ? lse_raw * kLog2e : __builtin_huge_valf(), lane, lse2);
+    int lim[PM::NPL];  // visibility limit of each lane-local position (see key_limit)
     int pi[PM::NPL], pv[PM::NPL], pslot[PM::NPL];
 #pragma unroll
     for (int j = 0; j < PM::NPL; ++j) {
-      const int src = PM::wpos(j, half) * G;
-      pi[j] = __shfl(cur.i, src, 64);
-      pv[j] = __shfl((int)cur.valid, src, 64);
-      pslot[j] = __shfl(cur.s, src, 64);
-      ppos[j] = pv[j] ? D.offset + pi[j] : -1;
+      pi[j] = pos_value<G>(cur.i, j, half);
+      pv[j] = pos_value<G>((int)cur.valid, j, half);
+      pslot[j] = pos_value<G>(cur.s, j, half);
+      lim[j] = key_limit<LOCAL>(pv[j], D.offset + pi[j], (int64_t)cur.t * kBk, col);
     }
     // the next tile (past the last: a stand-in decode of the last one, whose
     // fetches stay in bounds and are never used), and the list entry after it
@@ -368,7 +387,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the query region has been read
       fetch_q_rows(qw, q_src(nxt), lane);
       lse_raw = lse_of(nxt);
-      teacher_probs<G, LOCAL>(sc, lse2, rowok, ppos, (int64_t)cur.t * kBk, lane, c, P);
+      teacher_probs<G, LOCAL>(sc, lse2, lim, c, P);
     }
     KlAcc acc[PM::NPL];
     {
@@ -376,7 +395,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       iq_ik_scores<DIDX, G>(IKs, iqw, lane, zz);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the index-query region has been read
       fetch_iq_rows<DIDX, G>(iqw, iq_src(nxt), lane);
-      student_tile<G, LOCAL>(zz, P, ppos, (int64_t)cur.t * kBk, lane, acc);
+      student_tile<G, LOCAL>(zz, P, lim, acc);
     }
     // the lane of each position's first head row writes its partial
 #pragma unroll
@@ -483,6 +502,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __align__(16) uint16_t IKs[kBk * IKP];
   __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];
   __shared__ __align__(16) unsigned char IQs[kWaves][kIqRows * 2 * DIDX];
+  __shared__ __align__(16) float LSs[kWaves][32];
 
   const int nbg = D.B * D.h_kv;
   const int n_t = (int)((D.offset + D.n_q - 1) / D.pt - D.offset / D.pt + 1);
@@ -507,21 +527,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   fetch_iq_rows<DIDX, G>(iqw, iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX, lane);
   const float lse_mine = lse[((int64_t)b * D.h_q + g * G + hh) * D.n_q + i] * kLog2e;
   float lse2[16];
-  bool rowok[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int re = 8 * (e >> 2) + 4 * half + (e & 3);
-    lse2[e] = __shfl(lse_mine, re, 64);
-    rowok[e] = __shfl((int)valid, re, 64) != 0;
-  }
-  int64_t ppos[PM::NPL];
+  rows_lse(LSs[wave], valid ? lse_mine : __builtin_huge_valf(), lane, lse2);
+  int64_t ppos[PM::NPL];  // position of each lane-local position
   int pi[PM::NPL], pv[PM::NPL];
 #pragma unroll
   for (int j = 0; j < PM::NPL; ++j) {
-    const int src = PM::wpos(j, half) * G;
-    pi[j] = __shfl(i, src, 64);
-    pv[j] = __shfl((int)valid, src, 64);
-    ppos[j] = pv[j] ? D.offset + pi[j] : -1;
+    pi[j] = pos_value<G>(i, j, half);
+    pv[j] = pos_value<G>((int)valid, j, half);
+    ppos[j] = D.offset + pi[j];
   }
 
   const uint16_t* kg = k + ((int64_t)b * D.h_kv + g) * D.n_kv * kHeadDim;
@@ -543,18 +556,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (more)
       k_ik_load<DIDX>(x, kg + (int64_t)(t + 1) * kBk * kHeadDim, ikg + (int64_t)(t + 1) * kBk * DIDX, n_valid(t + 1));
     const int64_t key0 = (int64_t)t * kBk;
+    int lim[PM::NPL];
+#pragma unroll
+    for (int j = 0; j < PM::NPL; ++j) lim[j] = key_limit<true>(pv[j], ppos[j], key0, col);
     float P[4][PM::NPL];
     {
       f32x16 sc[4];
       q_k_scores(Ks, qw, lane, sc);
-      if (t == t_last) teacher_probs<G, true>(sc, lse2, rowok, ppos, key0, lane, c, P);
-      else teacher_probs<G, false>(sc, lse2, rowok, ppos, key0, lane, c, P);
+      if (t == t_last) teacher_probs<G, true>(sc, lse2, lim, c, P);
+      else teacher_probs<G, false>(sc, lse2, lim, c, P);
     }
     {
       f32x16 zz[4];
       iq_ik_scores<DIDX, G>(IKs, iqw, lane, zz);
-      if (t == t_last) student_fold<G, true>(zz, P, ppos, key0, lane, acc);
-      else student_fold<G, false>(zz, P, ppos, key0, lane, acc);
+      if (t == t_last) student_fold<G, true>(zz, P, lim, acc);
+      else student_fold<G, false>(zz, P, lim, acc);
     }
     __syncthreads();  // every wave is done with block t
     if (more) {
