@@ -12,9 +12,9 @@
 // a row are distinct.  Selection:
 //   0. rows of up to 2048 blocks are loaded into registers once;
 //   1. each lane takes the max key of its strided share of the row;
-//   2. a bitonic sort of the 64 lane maxima gives tau, the (k-1)-th largest of
-//      them; at least k-1 keys of the row are >= tau, and for score rows of any
-//      shape only a handful more;
+//   2. a sort of the 64 lane maxima (a bitonic network, mostly DPP moves)
+//      gives tau, the (k-1)-th largest of them; at least k-1 keys of the row are
+//      >= tau, and for score rows of any shape only a handful more;
 //   3. the keys >= tau are compacted into LDS (one per lane) and sorted: the
 //      (k-1)-th largest of them is the exact threshold; should more than 64 pass
 //      tau, an exact bitwise threshold search over the whole row takes over;
@@ -32,31 +32,84 @@ __device__ __forceinline__ uint64_t sel_key(float f, int t) {
   return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)t);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)x, m, 64);
-  const uint32_t hi = __shfl_xor((uint32_t)(x >> 32), m, 64);
+// Value of lane `src` (uniform) as a uniform.
+__device__ __forceinline__ uint64_t lane_u64(uint64_t x, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), src);
   return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
-  const uint32_t lo = __shfl((uint32_t)x, src, 64);
-  const uint32_t hi = __shfl((uint32_t)(x >> 32), src, 64);
-  return ((uint64_t)hi << 32) | lo;
+// Partner values for the sorting network, each lane getting lane ^ M's value.
+// Within a row of 16 lanes they are DPP moves (no LDS): ^1, ^2 and ^3 are
+// quad permutes, ^7 and ^15 the half-row and row mirrors, ^8 a rotate of the
+// row by 8, ^4 the half-row mirror followed by the quad flip.  Across rows:
+// ^16 and ^31 by ds_swizzle (xor within 32 lanes), ^63 by ds_bpermute.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (M == 1) return dpp_u32<0xB1>(v);                  // quad_perm [1, 0, 3, 2]
+  else if constexpr (M == 2) return dpp_u32<0x4E>(v);             // quad_perm [2, 3, 0, 1]
+  else if constexpr (M == 3) return dpp_u32<0x1B>(v);             // quad_perm [3, 2, 1, 0]
+  else if constexpr (M == 4) return dpp_u32<0x1B>(dpp_u32<0x141>(v));
+  else if constexpr (M == 7) return dpp_u32<0x141>(v);            // row_half_mirror
+  else if constexpr (M == 8) return dpp_u32<0x128>(v);            // row_ror:8
+  else if constexpr (M == 15) return dpp_u32<0x140>(v);           // row_mirror
+  else if constexpr (M == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+  else if constexpr (M == 31) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x7C1F);
+  else return (uint32_t)__shfl_xor((int)v, M, 64);
+}
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x) {
+  return ((uint64_t)xor_lane<M>((uint32_t)(x >> 32)) << 32) | xor_lane<M>((uint32_t)x);
 }
 
-// Bitonic sort of one value per lane, ascending over lanes 0..63.
-__device__ __forceinline__ uint64_t wave_sort_asc(uint64_t x, int lane) {
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint64_t y = shfl_xor_u64(x, stride);
-      const bool asc = (lane & size) == 0;
-      const bool lower = (lane & stride) == 0;
-      const uint64_t mn = x < y ? x : y, mx = x < y ? y : x;
-      x = (lower == asc) ? mn : mx;
-    }
+// Compare-exchange with lane ^ M: the lane whose `LOWBIT` is clear keeps the smaller.
+template <int M, int LOWBIT>
+__device__ __forceinline__ uint64_t cmpx(uint64_t x, int lane) {
+  const uint64_t y = xor_lane_u64<M>(x);
+  const uint64_t mn = x < y ? x : y, mx = x < y ? y : x;
+  return (lane & LOWBIT) == 0 ? mn : mx;
+}
+template <int S>
+__device__ __forceinline__ uint64_t half_clean(uint64_t x, int lane) {  // xor partners S, S/2, ..., 1
+  if constexpr (S == 0) {
+    return x;
+  } else {
+    x = cmpx<S, S>(x, lane);
+    return half_clean<S / 2>(x, lane);
   }
+}
+template <int SIZE>
+__device__ __forceinline__ uint64_t merge_level(uint64_t x, int lane) {
+  x = cmpx<SIZE - 1, SIZE / 2>(x, lane);  // flip: lane i against SIZE-1-i of its block
+  return half_clean<SIZE / 4>(x, lane);
+}
+
+// Sort of one value per lane, ascending over lanes 0..63: a bitonic network
+// in its flip form (each merge level starts by comparing lane i with the
+// mirrored lane of its block, then halves with xor partners), so that 18 of
+// its 21 exchange steps are DPP moves.
+__device__ __forceinline__ uint64_t wave_sort_asc(uint64_t x, int lane) {
+  x = merge_level<2>(x, lane);
+  x = merge_level<4>(x, lane);
+  x = merge_level<8>(x, lane);
+  x = merge_level<16>(x, lane);
+  x = merge_level<32>(x, lane);
+  return merge_level<64>(x, lane);
+}
+
+// Inclusive prefix sum over the 64 lanes: DPP shifts within rows of 16, then
+// the row broadcasts of lanes 15 and 31 (no LDS).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
   return x;
 }
 
@@ -121,18 +174,13 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
     mx = c > mx ? c : mx;
   }
   // 2. tau = kk-th largest lane maximum (lanes without candidates hold 0)
-  const uint64_t tau = shfl_u64(wave_sort_asc(mx, lane), 64 - kk);
+  const uint64_t tau = lane_u64(wave_sort_asc(mx, lane), 64 - kk);
 
   // 3. compact the keys >= tau and find the exact kk-th largest key
   int mine = 0;
   for (int j = 0; j < nj; ++j) mine += key_at(j, lane + 64 * j) >= tau;
-  int incl = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  const int total = __shfl(incl, 63, 64);
+  const int incl = wave_incl_scan(mine);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
   uint64_t thr;
   if (total <= 64) {
     int at = incl - mine;
@@ -142,7 +190,7 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
     }
     wave_lds_sync();
     const uint64_t mine_c = lane < total ? cand[wave][lane] : 0;
-    thr = shfl_u64(wave_sort_asc(mine_c, lane), 64 - kk);
+    thr = lane_u64(wave_sort_asc(mine_c, lane), 64 - kk);
   } else {
     // exact threshold: the largest key x with #{keys >= x} >= kk, bit by bit
     uint64_t prefix = 0;
