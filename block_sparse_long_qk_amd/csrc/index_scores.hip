@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     int32_t* __restrict__ block_idx, Dims D, int32_t blocks_per_split) {
   using C = IdxCfg<DIDX, EB>;
   using Frag = typename C::Frag;
-  // two key blocks (rows unpadded, chunks swizzled) as two separate arrays, each
+  // two key blocks (in the tile-interleaved layout of IdxCfg) as two separate arrays, each
   // named statically where it is used: the compiler can then tell a read of
   // one from the direct-to-LDS loads filling the other and does not wait for them
   __shared__ __align__(16) unsigned char lds0[C::NG * C::PITCH];
