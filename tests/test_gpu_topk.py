@@ -84,3 +84,23 @@ def test_chunk_with_offset():
     n_kv, n_q, off = 50000, 777, 30001
     pooled = rng.standard_normal((1, 1, n_q, -(-n_kv // 128))).astype(np.float32)
     check(pooled, n_q, n_kv, 1, 16, q_offset=off, name="chunk")
+
+
+# Rows of 1000 blocks (up to 16 keys per lane), an odd number of rows and
+# three values of k around 32 selected blocks, with ties in one group.
+@pytest.mark.parametrize("k", [16, 33, 34])
+def test_rows_up_to_1024_blocks(k):
+    rng = np.random.default_rng(3500 + k)
+    n_kv, n_q = 128 * 1000, 333
+    pooled = rng.standard_normal((1, 2, n_q, n_kv // 128)).astype(np.float32)
+    pooled[0, 1] = np.round(pooled[0, 1] * 2)  # ties in the second group
+    check(pooled, n_q, n_kv, 2, k, name=f"1000 blocks, k={k}")
+
+
+def test_periodic_long_rows_take_the_exact_path():
+    """As test_periodic_rows_take_the_exact_path, with 1000-block rows."""
+    n_kv, n_q = 128 * 1000, 201
+    t = np.arange(n_kv // 128)
+    row = -(t % 64).astype(np.float32)
+    pooled = np.broadcast_to(row, (1, 1, n_q, n_kv // 128)).copy()
+    check(pooled, n_q, n_kv, 1, 16, name="periodic, 1000 blocks")
