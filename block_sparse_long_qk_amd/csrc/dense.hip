@@ -144,17 +144,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_sched_barrier(0);
     // online softmax in base 2; the last block (the diagonal) masks keys after the row's position
     const bool masked = t == t_last;
-    const int rel = max(-1, min(kBk, p - t * kBk)) - 4 * half;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[T][e] *= c;
+    }
+    if (masked) {  // uniform, and a branch of its own: the blocks before the diagonal skip it
+      const int rel = max(-1, min(kBk, p - t * kBk)) - 4 * half;
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * T + 8 * (e >> 2) + (e & 3) > rel) s[T][e] = NEG_INF;
+      }
+    }
     float mx = NEG_INF;
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float xv = s[T][e] * c;
-        if (masked && 32 * T + 8 * (e >> 2) + (e & 3) > rel) xv = NEG_INF;
-        s[T][e] = xv;
-        mx = fmaxf(mx, xv);
-      }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[T][e]);
     }
     mx = fmaxf(mx, wave_xor32(mx));
     const float m_new = fmaxf(m_run, mx);
