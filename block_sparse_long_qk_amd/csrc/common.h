@@ -191,6 +191,16 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+// Reduction over each row of 16 lanes (DPP only): every lane of a row gets
+// the same value, since each step combines a lane with its partner in both
+// orders of a commutative op.
+template <typename Op>
+__device__ __forceinline__ float row16_reduce(float x, Op op) {
+  x = op(x, dpp_move<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = op(x, dpp_move<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  x = op(x, dpp_move<0x141>(x));  // row_half_mirror
+  return op(x, dpp_move<0x140>(x));  // row_mirror
+}
 template <typename Op>
 __device__ __forceinline__ float half_reduce(float x, Op op) {
   x = op(x, dpp_move<0xB1>(x));   // quad_perm [1, 0, 3, 2]

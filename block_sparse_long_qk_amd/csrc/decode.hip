@@ -292,8 +292,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
       sc[T][j] = x;
       m = fmaxf(m, x);
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = row16_reduce(m, [](float a, float b) { return fmaxf(a, b); });
     const float mref = m == NEG_INF ? 0.f : m;
     float sum = 0.f;
 #pragma unroll
@@ -302,8 +301,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
       sum += e;
       if (4 * c + j < GMAX) P[wave][16 * T + n][4 * c + j] = e;
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+    sum = row16_reduce(sum, [](float a, float b) { return a + b; });
     mx[j] = m;
     sm[j] = sum;
   }
@@ -311,8 +309,8 @@ __global__ __launch_bounds__(256) void k_attn_rows(const uint16_t* __restrict__ 
   float lh[GMAX], mh[GMAX];
 #pragma unroll
   for (int h = 0; h < GMAX; ++h) {
-    lh[h] = __shfl(sm[h & 3], 16 * (h >> 2), 64);
-    mh[h] = __shfl(mx[h & 3], 16 * (h >> 2), 64);
+    lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sm[h & 3]), 16 * (h >> 2)));
+    mh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx[h & 3]), 16 * (h >> 2)));
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
