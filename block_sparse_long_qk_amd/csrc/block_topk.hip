@@ -15,9 +15,10 @@
 //   2. a sort of the 64 lane maxima (a bitonic network, mostly DPP moves)
 //      gives tau, the (k-1)-th largest of them; at least k-1 keys of the row are
 //      >= tau, and for score rows of any shape only a handful more;
-//   3. the keys >= tau are compacted into LDS (one per lane) and sorted: the
-//      (k-1)-th largest of them is the exact threshold; should more than 64 pass
-//      tau, an exact bitwise threshold search over the whole row takes over;
+//   3. the keys >= tau are compacted into LDS (one per lane) and sorted (over
+//      16, 32 or 64 lanes, as many as they need): the (k-1)-th largest of them
+//      is the exact threshold; should more than 64 pass tau, an exact bitwise
+//      threshold search over the whole row takes over;
 //   4. the selected blocks are emitted in ascending order with ballots (rank =
 //      number of selected blocks with a smaller index), then the local block.
 #include "launch.h"
@@ -190,7 +191,17 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
     }
     wave_lds_sync();
     const uint64_t mine_c = lane < total ? cand[wave][lane] : 0;
-    thr = lane_u64(wave_sort_asc(mine_c, lane), 64 - kk);
+    // the candidates sit in lanes 0 .. total-1: a network over the first 16 or
+    // 32 lanes orders them when they fit there (uniform branch on total)
+    if (total <= 16 && kk <= 16) {
+      const uint64_t x = merge_level<16>(merge_level<8>(merge_level<4>(merge_level<2>(mine_c, lane), lane), lane), lane);
+      thr = lane_u64(x, 16 - kk);
+    } else if (total <= 32 && kk <= 32) {
+      uint64_t x = merge_level<16>(merge_level<8>(merge_level<4>(merge_level<2>(mine_c, lane), lane), lane), lane);
+      thr = lane_u64(merge_level<32>(x, lane), 32 - kk);
+    } else {
+      thr = lane_u64(wave_sort_asc(mine_c, lane), 64 - kk);
+    }
   } else {
     // exact threshold: the largest key x with #{keys >= x} >= kk, bit by bit
     uint64_t prefix = 0;
