@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 OP_INDEX_SCORES, OP_BLOCK_TOPK, OP_SPARSE_ATTN, OP_FORWARD, OP_INDEX_KL, OP_SPARSE_ATTN_BWD, OP_INDEX_KL_BWD = range(7)
 DTYPE_BF16, DTYPE_FP8_E4M3 = range(2)  # msa_dtype: element type of index_q / index_k
+DEFAULT_CHUNK_ROWS, CHUNK_ALIGN = 131072, 8192  # MSA_DEFAULT_CHUNK_ROWS, MSA_CHUNK_ALIGN
 
 EXPORTS = ("msa_workspace_size", "msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
            "msa_index_scores_v", "msa_block_topk_v", "msa_sparse_attn_fwd_v", "msa_forward_v", "msa_index_kl",
@@ -43,15 +44,16 @@ class Problem(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("index_dtype", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
+        ("chunk_rows", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, batch, n_q, n_kv, h_q, h_kv, head_dim=128, index_dim=128, block_size=128, topk=16,
-             q_offset=-1, softmax_scale=None, index_dtype=DTYPE_BF16, kv_dtype=DTYPE_BF16):
+             q_offset=-1, softmax_scale=None, index_dtype=DTYPE_BF16, kv_dtype=DTYPE_BF16, chunk_rows=0):
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(head_dim)
         return cls(batch, n_q, n_kv, h_q, h_kv, head_dim, index_dim, block_size, topk, q_offset, softmax_scale,
-                   index_dtype, kv_dtype)
+                   index_dtype, kv_dtype, chunk_rows)
 
     @property
     def offset(self) -> int:
@@ -151,6 +153,128 @@ def _check(rc: int, what: str):
         raise MsaError(rc, what)
 
 
+# ---------------------------------------------------------------- argument checks
+# The C ABI sees plain pointers and cannot tell a buffer's size, element type or
+# device, so the binding checks every tensor against the sizes the problem
+# implies (include/msa.h states the layouts) before the call: a wrong shape,
+# dtype, a non-contiguous view or a host tensor raises ValueError and nothing
+# reaches the library.
+_BF16 = ("bfloat16",)
+_F32 = ("float32",)
+_I32 = ("int32",)
+_FP8 = ("uint8", "float8_e4m3fn")
+
+
+def _dtype_name(x) -> str:
+    return str(x.dtype).replace("torch.", "")
+
+
+def _elem(p_dtype: int):
+    return _FP8 if p_dtype == DTYPE_FP8_E4M3 else _BF16
+
+
+class _Args:
+    """Collects the tensors of one call, each checked for element type,
+    contiguity and size as it is added; device() then checks that all of
+    them live on one GPU."""
+
+    def __init__(self, what: str):
+        self.what = what
+        self.seen = []
+
+    def add(self, x, name: str, dtypes, numel: int, optional: bool = False):
+        if x is None:
+            if optional:
+                return None
+            raise ValueError(f"{self.what}: {name} is required")
+        if not (hasattr(x, "data_ptr") and hasattr(x, "is_contiguous")):
+            raise ValueError(f"{self.what}: {name} must be a torch tensor, got {type(x).__name__}")
+        if dtypes is not None and _dtype_name(x) not in dtypes:
+            raise ValueError(f"{self.what}: {name} has dtype {_dtype_name(x)}, expected {' or '.join(dtypes)}")
+        if not x.is_contiguous():
+            raise ValueError(f"{self.what}: {name} must be contiguous")
+        if x.numel() < numel:
+            raise ValueError(f"{self.what}: {name} holds {x.numel()} elements, the problem needs {numel}")
+        self.seen.append((name, x))
+        return x
+
+    def workspace(self, ws, nbytes: int):
+        """The workspace tensor (any dtype) must hold the bytes passed to the call."""
+        if ws is None:
+            raise ValueError(f"{self.what}: workspace is required")
+        self.add(ws, "workspace", None, 0)
+        have = ws.numel() * ws.element_size()
+        if nbytes > have:
+            raise ValueError(f"{self.what}: workspace_bytes={nbytes} exceeds the workspace tensor ({have} bytes)")
+
+    def device(self):
+        dev = None
+        for name, x in self.seen:
+            if not getattr(x, "is_cuda", False):
+                raise ValueError(f"{self.what}: {name} must be a GPU tensor (it is on {x.device})")
+            if dev is None:
+                dev = x.device
+            elif x.device != dev:
+                raise ValueError(f"{self.what}: {name} is on {x.device}, other arguments on {dev}")
+
+
+def _rows(p: Problem, varlen) -> int:
+    """Query rows of q, index_q and out: packed (total_q) or B * n_q."""
+    if varlen is not None and varlen.q_starts:
+        return int(varlen.total_q)
+    return p.batch * p.n_q
+
+
+def _kv_elems(p: Problem, varlen) -> int:
+    if varlen is not None and varlen.page_table:
+        return int(varlen.num_pages) * p.h_kv * p.block_size * p.head_dim
+    return p.batch * p.h_kv * p.n_kv * p.head_dim
+
+
+def _ik_elems(p: Problem, varlen) -> int:
+    if varlen is not None and varlen.page_table:
+        return int(varlen.num_pages) * p.block_size * p.index_dim
+    return p.batch * p.n_kv * p.index_dim
+
+
+def _varlen_args(a: _Args, p: Problem, varlen):
+    """The descriptor's own device arrays (kept alive by Varlen.make)."""
+    if varlen is None:
+        return
+    keep = getattr(varlen, "_keep", None)
+    if keep is None:
+        raise ValueError(f"{a.what}: build the Varlen with Varlen.make (its arrays are checked)")
+    qo, kv, qs, pt = keep
+    a.add(qo, "varlen.qo_lens", _I32, p.batch, optional=True)
+    a.add(kv, "varlen.kv_lens", _I32, p.batch, optional=True)
+    a.add(qs, "varlen.q_starts", _I32, p.batch, optional=True)
+    if pt is not None:
+        a.add(pt, "varlen.page_table", _I32, p.batch * int(varlen.pages_per_seq))
+        if pt.dim() != 2 or pt.shape[0] != p.batch:
+            raise ValueError(f"{a.what}: varlen.page_table must be [batch, pages_per_seq]")
+
+
+def _index_args(a: _Args, p: Problem, index_q, index_k, varlen):
+    a.add(index_q, "index_q", _elem(p.index_dtype), _rows(p, varlen) * p.h_kv * p.index_dim)
+    a.add(index_k, "index_k", _elem(p.index_dtype), _ik_elems(p, varlen))
+
+
+def _qkv_args(a: _Args, p: Problem, q, k, v, varlen, kv_dtypes=None, with_v=True):
+    a.add(q, "q", _BF16, _rows(p, varlen) * p.h_q * p.head_dim)
+    kvd = _elem(p.kv_dtype) if kv_dtypes is None else kv_dtypes
+    a.add(k, "k", kvd, _kv_elems(p, varlen))
+    if with_v:
+        a.add(v, "v", kvd, _kv_elems(p, varlen))
+
+
+def _bidx_numel(p: Problem) -> int:
+    return p.batch * p.h_kv * p.n_q * p.topk
+
+
+def _row_numel(p: Problem, heads: int) -> int:
+    return p.batch * heads * p.n_q
+
+
 def workspace_size(p: Problem, op: int) -> int:
     n = ctypes.c_size_t(0)
     _check(library().msa_workspace_size(ctypes.byref(p), op, ctypes.byref(n)), "msa_workspace_size")
@@ -159,6 +283,11 @@ def workspace_size(p: Problem, op: int) -> int:
 
 def index_scores(p: Problem, index_q, index_k, pooled, stream=None, varlen: Varlen | None = None):
     """pooled[b, g, i, t] = max over visible j in block t of index_q[b, i, g] . index_k[b, j]."""
+    a = _Args("index_scores")
+    _index_args(a, p, index_q, index_k, varlen)
+    a.add(pooled, "pooled", _F32, p.batch * p.h_kv * p.n_q * p.n_blk)
+    _varlen_args(a, p, varlen)
+    a.device()
     L, st = library(), _stream(stream, pooled)
     if varlen is None:
         rc = L.msa_index_scores(ctypes.byref(p), _ptr(index_q), _ptr(index_k), _ptr(pooled), st)
@@ -171,6 +300,11 @@ def index_scores(p: Problem, index_q, index_k, pooled, stream=None, varlen: Varl
 
 def block_topk(p: Problem, pooled, block_idx, stream=None, varlen: Varlen | None = None):
     """block_idx[b, g, i] = local block + top-(k-1) other visible blocks, ascending, -1 padded."""
+    a = _Args("block_topk")
+    a.add(pooled, "pooled", _F32, p.batch * p.h_kv * p.n_q * p.n_blk)
+    a.add(block_idx, "block_idx", _I32, _bidx_numel(p))
+    _varlen_args(a, p, varlen)
+    a.device()
     L, st = library(), _stream(stream, pooled)
     if varlen is None:
         rc = L.msa_block_topk(ctypes.byref(p), _ptr(pooled), _ptr(block_idx), st)
@@ -184,6 +318,14 @@ def sparse_attn_fwd(p: Problem, q, k, v, block_idx, out, lse=None, workspace=Non
                     stream=None, varlen: Varlen | None = None):
     """Softmax attention of every query head over its group's selected blocks."""
     nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    a = _Args("sparse_attn_fwd")
+    _qkv_args(a, p, q, k, v, varlen)
+    a.add(block_idx, "block_idx", _I32, _bidx_numel(p))
+    a.add(out, "out", _BF16, _rows(p, varlen) * p.h_q * p.head_dim)
+    a.add(lse, "lse", _F32, _row_numel(p, p.h_q), optional=True)
+    a.workspace(workspace, nb)
+    _varlen_args(a, p, varlen)
+    a.device()
     L, st = library(), _stream(stream, q)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(workspace), nb, st)
     if varlen is None:
@@ -198,6 +340,15 @@ def forward(p: Problem, q, k, v, index_q, index_k, out, block_idx, lse=None, wor
             stream=None, varlen: Varlen | None = None):
     """The whole MSA forward pass: index scores, block top-k, sparse attention."""
     nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    a = _Args("forward")
+    _qkv_args(a, p, q, k, v, varlen)
+    _index_args(a, p, index_q, index_k, varlen)
+    a.add(out, "out", _BF16, _rows(p, varlen) * p.h_q * p.head_dim)
+    a.add(block_idx, "block_idx", _I32, _bidx_numel(p))
+    a.add(lse, "lse", _F32, _row_numel(p, p.h_q), optional=True)
+    a.workspace(workspace, nb)
+    _varlen_args(a, p, varlen)
+    a.device()
     L, st = library(), _stream(stream, q)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(index_q), _ptr(index_k), _ptr(out), _ptr(block_idx), _ptr(lse),
             _ptr(workspace), nb, st)
@@ -215,6 +366,15 @@ def index_kl(p: Problem, q, k, index_q, index_k, block_idx, lse, kl, workspace=N
     distribution over the selected tokens against the softmax of the raw index
     scores over the same tokens; lse is the forward pass's output."""
     nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    a = _Args("index_kl")
+    _qkv_args(a, p, q, k, None, None, kv_dtypes=_BF16, with_v=False)
+    _index_args(a, p, index_q, index_k, None)
+    a.add(block_idx, "block_idx", _I32, _bidx_numel(p))
+    a.add(lse, "lse", _F32, _row_numel(p, p.h_q))
+    a.add(kl, "kl", _F32, _row_numel(p, p.h_kv))
+    a.add(lse_index, "lse_index", _F32, _row_numel(p, p.h_kv), optional=True)
+    a.workspace(workspace, nb)
+    a.device()
     L, st = library(), _stream(stream, q)
     rc = L.msa_index_kl(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(index_q), _ptr(index_k), _ptr(block_idx), _ptr(lse),
                         _ptr(kl), _ptr(lse_index), _ptr(workspace), nb, st)
@@ -226,6 +386,17 @@ def sparse_attn_bwd(p: Problem, q, k, v, block_idx, out, lse, dout, dq, dk, dv, 
                     workspace_bytes=None, stream=None):
     """Gradients dq, dk, dv of sparse_attn_fwd for the output gradient dout."""
     nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    a = _Args("sparse_attn_bwd")
+    _qkv_args(a, p, q, k, v, None, kv_dtypes=_BF16)
+    a.add(block_idx, "block_idx", _I32, _bidx_numel(p))
+    a.add(out, "out", _BF16, p.batch * p.n_q * p.h_q * p.head_dim)
+    a.add(lse, "lse", _F32, _row_numel(p, p.h_q))
+    a.add(dout, "dout", _BF16, p.batch * p.n_q * p.h_q * p.head_dim)
+    a.add(dq, "dq", _BF16, p.batch * p.n_q * p.h_q * p.head_dim)
+    a.add(dk, "dk", _BF16, _kv_elems(p, None))
+    a.add(dv, "dv", _BF16, _kv_elems(p, None))
+    a.workspace(workspace, nb)
+    a.device()
     L, st = library(), _stream(stream, q)
     rc = L.msa_sparse_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(lse),
                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nb, st)
@@ -238,6 +409,17 @@ def index_kl_bwd(p: Problem, q, k, index_q, index_k, block_idx, lse, lse_index, 
     """Gradients of sum(dkl * kl) into index_q and index_k, the teacher held
     fixed; lse_index is index_kl's output for the same inputs (dkl None: ones)."""
     nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    a = _Args("index_kl_bwd")
+    _qkv_args(a, p, q, k, None, None, kv_dtypes=_BF16, with_v=False)
+    _index_args(a, p, index_q, index_k, None)
+    a.add(block_idx, "block_idx", _I32, _bidx_numel(p))
+    a.add(lse, "lse", _F32, _row_numel(p, p.h_q))
+    a.add(lse_index, "lse_index", _F32, _row_numel(p, p.h_kv))
+    a.add(d_index_q, "d_index_q", _elem(p.index_dtype), p.batch * p.n_q * p.h_kv * p.index_dim)
+    a.add(d_index_k, "d_index_k", _elem(p.index_dtype), p.batch * p.n_kv * p.index_dim)
+    a.add(dkl, "dkl", _F32, _row_numel(p, p.h_kv), optional=True)
+    a.workspace(workspace, nb)
+    a.device()
     L, st = library(), _stream(stream, q)
     rc = L.msa_index_kl_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(index_q), _ptr(index_k), _ptr(block_idx),
                             _ptr(lse), _ptr(lse_index), _ptr(dkl), _ptr(d_index_q), _ptr(d_index_k), _ptr(workspace),
@@ -248,6 +430,11 @@ def index_kl_bwd(p: Problem, q, k, index_q, index_k, block_idx, lse, lse_index, 
 
 def dense_attn_fwd(p: Problem, q, k, v, out, lse=None, stream=None):
     """Dense causal GQA attention (every visible key): the warmup's main branch."""
+    a = _Args("dense_attn_fwd")
+    _qkv_args(a, p, q, k, v, None, kv_dtypes=_BF16)
+    a.add(out, "out", _BF16, p.batch * p.n_q * p.h_q * p.head_dim)
+    a.add(lse, "lse", _F32, _row_numel(p, p.h_q), optional=True)
+    a.device()
     L, st = library(), _stream(stream, q)
     _check(L.msa_dense_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), st),
            "msa_dense_attn_fwd")
@@ -256,6 +443,13 @@ def dense_attn_fwd(p: Problem, q, k, v, out, lse=None, stream=None):
 
 def dense_index_kl(p: Problem, q, k, index_q, index_k, lse, kl, stream=None, lse_index=None):
     """index_kl over every visible token, with the dense attention's lse."""
+    a = _Args("dense_index_kl")
+    _qkv_args(a, p, q, k, None, None, kv_dtypes=_BF16, with_v=False)
+    _index_args(a, p, index_q, index_k, None)
+    a.add(lse, "lse", _F32, _row_numel(p, p.h_q))
+    a.add(kl, "kl", _F32, _row_numel(p, p.h_kv))
+    a.add(lse_index, "lse_index", _F32, _row_numel(p, p.h_kv), optional=True)
+    a.device()
     L, st = library(), _stream(stream, q)
     _check(L.msa_dense_index_kl(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(index_q), _ptr(index_k), _ptr(lse), _ptr(kl),
                                 _ptr(lse_index), st), "msa_dense_index_kl")
