@@ -87,6 +87,63 @@ def pool(iq_rows, pos, ik, bk: int) -> np.ndarray:
     return out
 
 
+def index_values(x) -> np.ndarray:
+    """Index inputs as fp64 values: bf16 bits (uint16) widened exactly, or
+    E4M3 codes (uint8) through e4m3_decode."""
+    x = np.asarray(x)
+    if x.dtype == np.uint8:
+        return e4m3_decode(x)
+    return (np.ascontiguousarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(
+        np.float64)
+
+
+def pool_mm(iq_rows, pos, ik, bk: int, keys_per_step: int = 16384, ik_values=None) -> np.ndarray:
+    """pool() (or pool_f8()) written with a library matrix product.
+
+    The same definition as oracle_pool (page "MiniMax 发布 MSA…", section
+    两个分支如何工作: score every visible key, max-pool to blocks): the scores of
+    the rows against the keys are one fp64 product of the exact input values
+    and each block keeps the max of its scores; a row's own (local) block is
+    then pooled again over the keys up to the row's position only, and the
+    blocks after it are not candidates (NaN).  Only the summation order inside
+    each dot product differs from the plain loops (fp64, so by a few units in
+    the last place).  The parity tests use it where the loops would take
+    minutes (thousands of rows against a 1M-token cache).  Returns
+    [nrows, n_blk], NaN after each row's local block, like pool().
+    ik_values: index_values(ik), when the caller already holds it.
+    """
+    a = index_values(iq_rows)
+    kv = index_values(ik) if ik_values is None else ik_values
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    n_kv = ik.shape[0]
+    n_blk = -(-n_kv // bk)
+    n = len(pos)
+    out = np.full((n, n_blk), np.nan)
+    if n == 0:
+        return out
+    if np.any(pos < 0) or np.any(pos >= n_kv) or a.shape[1] != ik.shape[1]:
+        raise ValueError("pool_mm: invalid argument")
+    local = pos // bk
+    step = max(bk, keys_per_step // bk * bk)
+    # every block up to the last one a row sees, all of its keys
+    for j0 in range(0, int(pos.max()) + 1, step):
+        j1 = min(j0 + step, n_kv)
+        s = a @ kv[j0:j1].T
+        nb = -(-(j1 - j0) // bk)
+        if s.shape[1] < nb * bk:
+            s = np.concatenate([s, np.full((n, nb * bk - s.shape[1]), -np.inf)], axis=1)
+        out[:, j0 // bk:j0 // bk + nb] = s.reshape(n, nb, bk).max(axis=2)
+    # the local block: only the keys j <= p count
+    for r0 in range(0, n, 256):
+        r1 = min(r0 + 256, n)
+        keys = local[r0:r1, None] * bk + np.arange(bk)[None, :]
+        sl = np.matmul(kv[np.minimum(keys, n_kv - 1)], a[r0:r1, :, None])[:, :, 0]
+        sl[keys > pos[r0:r1, None]] = -np.inf
+        out[np.arange(r0, r1), local[r0:r1]] = sl.max(axis=1)
+    out[np.arange(n_blk)[None, :] > local[:, None]] = np.nan
+    return out
+
+
 def e4m3_decode(codes) -> np.ndarray:
     """OCP E4M3 codes (uint8) -> their values in fp64 (NaN for 0x7F / 0xFF)."""
     c = np.ascontiguousarray(codes, dtype=np.uint8)
@@ -208,17 +265,25 @@ def inputs_for_rows(w, b: int, g: int, rows, plant=None):
     Returns dict(pos, iq [n, d_idx], q [n, G, d], ik [pmax+1, d_idx]); iq and ik
     are bf16 bits, or E4M3 codes for an "fp8" workload.
     """
+    x = inputs_for_rows_all(w, b, rows, plant)
+    G = w.group
+    return {"pos": x["pos"], "iq": np.ascontiguousarray(x["iq"][:, g, :]),
+            "q": np.ascontiguousarray(x["q"][:, g * G:(g + 1) * G, :]), "ik": x["ik"]}
+
+
+def inputs_for_rows_all(w, b: int, rows, plant=None, with_q: bool = True):
+    """inputs_for_rows for every group at once: iq [n, h_kv, d_idx], q [n, h_q, d]
+    (q None when with_q is false)."""
     import synth
     rows = np.asarray(rows, dtype=np.int64)
     plant = synth.plant_spec(w) if plant is None else plant
     pos = w.offset + rows
-    G = w.group
-    iq = synth.host_iq_rows(w, b, rows, plant)[:, g, :]
+    iq = synth.host_iq_rows(w, b, rows, plant)
     if w.index_dtype == "fp8":
         iq = synth.to_e4m3(iq)
-    q = synth.host_q_rows(w, b, rows)[:, g * G:(g + 1) * G, :]
+    q = synth.host_q_rows(w, b, rows) if with_q else None
     ik = _index_keys(w, b, plant)[:int(pos.max()) + 1]
-    return {"pos": pos, "iq": np.ascontiguousarray(iq), "q": np.ascontiguousarray(q), "ik": ik}
+    return {"pos": pos, "iq": iq, "q": q, "ik": ik}
 
 
 def pool_for(w, iq_rows, pos, ik) -> np.ndarray:
@@ -262,6 +327,10 @@ def kv_for_blocks(w, b: int, g: int, sel):
     K = np.zeros((w.n_kv, w.head_dim), np.uint16)
     V = np.zeros((w.n_kv, w.head_dim), np.uint16)
     blocks = np.unique(np.asarray(sel)[np.asarray(sel) >= 0])
+    if 2 * len(blocks) > w.n_blk:   # most blocks: one generator pass over the whole head
+        K[:] = kv_values_bf16(w, synth.host_kv(w, "k", b, g, 0, w.n_kv))
+        V[:] = kv_values_bf16(w, synth.host_kv(w, "v", b, g, 0, w.n_kv))
+        return K, V
     for t in blocks:
         j0, j1 = int(t) * w.block_size, min((int(t) + 1) * w.block_size, w.n_kv)
         K[j0:j1] = kv_values_bf16(w, synth.host_kv(w, "k", b, g, j0, j1))

@@ -96,13 +96,35 @@ def normal_table() -> np.ndarray:
     return _NT
 
 
-def gen_range(seed: int, tensor_id: int, start: int, count: int) -> np.ndarray:
-    """bf16 bits of elements start .. start+count-1 of one generated tensor."""
-    key = np.uint64(stream_key(seed, tensor_id))
-    e = np.arange(count, dtype=np.uint64) + np.uint64(start)
+_GEN_CHUNK = 1 << 22   # elements per worker task of a large gen_range
+
+
+def _gen_into(out: np.ndarray, key: np.uint64, start: int, nt: np.ndarray):
+    e = np.arange(out.size, dtype=np.uint64) + np.uint64(start)
     with np.errstate(over="ignore"):
         h = _sm64_np(key + e)
-    return normal_table()[(h >> np.uint64(48)).astype(np.int64)]
+    out[:] = nt[(h >> np.uint64(48)).astype(np.int64)]
+
+
+def gen_range(seed: int, tensor_id: int, start: int, count: int) -> np.ndarray:
+    """bf16 bits of elements start .. start+count-1 of one generated tensor.
+
+    Large ranges are cut into pieces filled by a thread pool (numpy releases
+    the interpreter lock inside its array operations); every element is still
+    the same function of its index."""
+    key = np.uint64(stream_key(seed, tensor_id))
+    nt = normal_table()
+    out = np.empty(count, dtype=np.uint16)
+    if count <= _GEN_CHUNK:
+        _gen_into(out, key, start, nt)
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    workers = min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = [ex.submit(_gen_into, out[a:a + _GEN_CHUNK], key, start + a, nt) for a in range(0, count, _GEN_CHUNK)]
+        for f in futs:
+            f.result()
+    return out
 
 
 def gen_at(seed: int, tensor_id: int, idx) -> np.ndarray:
@@ -281,9 +303,15 @@ def to_e4m3(bits: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(b.shape)
 
 
+def _contiguous(rows: np.ndarray) -> bool:
+    return len(rows) > 1 and bool(np.all(np.diff(rows) == 1))
+
+
 def host_q_rows(w: Workload, b: int, rows) -> np.ndarray:
     """Q[b, rows] for arbitrary query rows, shape [len(rows), h_q, d]."""
     rows = np.asarray(rows, dtype=np.int64)
+    if _contiguous(rows):
+        return host_q(w, b, int(rows[0]), int(rows[-1]) + 1)
     row = w.h_q * w.head_dim
     idx = ((b * w.n_q + rows)[:, None] * row + np.arange(row)[None, :]).reshape(-1)
     return gen_at(w.seed, T_Q, idx).reshape(len(rows), w.h_q, w.head_dim)
@@ -309,6 +337,8 @@ def device_dout(w: Workload, device="cuda:0"):
 def host_iq_rows(w: Workload, b: int, rows, plant: Plant | None = None) -> np.ndarray:
     """index-q[b, rows] for arbitrary query rows, shape [len(rows), h_kv, d_idx], planted."""
     rows = np.asarray(rows, dtype=np.int64)
+    if _contiguous(rows):
+        return host_iq(w, b, int(rows[0]), int(rows[-1]) + 1, plant)
     row = w.h_kv * w.index_dim
     idx = ((b * w.n_q + rows)[:, None] * row + np.arange(row)[None, :]).reshape(-1)
     x = gen_at(w.seed, T_IQ, idx).reshape(len(rows), w.h_kv, w.index_dim)

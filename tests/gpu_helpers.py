@@ -72,8 +72,7 @@ def run_gpu(w: synth.Workload, inputs=None, with_forward=True, stream=None) -> d
 
 def index_values(x) -> np.ndarray:
     """Index inputs as fp64 values: bf16 bits (uint16) or E4M3 codes (uint8)."""
-    x = np.asarray(x)
-    return oracle.e4m3_decode(x) if x.dtype == np.uint8 else synth.bf16_to_f32(x).astype(np.float64)
+    return oracle.index_values(x)
 
 
 # The gfx950 E4M3 MFMA sums each run of 8 consecutive k-elements of a lane's
@@ -87,24 +86,63 @@ def index_values(x) -> np.ndarray:
 E4M3_RUN = 8
 E4M3_RUN_ERR = 7 * 2.0 ** -12
 
+# Work limits of the host-side checks, in (row, key) pairs of one call.
+PLAIN_POOL_MAX = 1 << 24    # the plain-loop oracle pool up to here (a fraction of a second); the product form beyond
+EXACT_TAU_MAX = 1 << 29     # the per-key summation bound up to here; its block-max upper bound beyond
+ROW_CHUNK_KEYS = 1 << 27    # (row, key) pairs per chunk on the exact-bound path, which bounds host memory
+ROW_CHUNK = 2048            # rows per chunk otherwise (every array is then [rows, n_blk] or [rows, 16384])
 
-def tau_pool(iq_rows, ik, pos, bk):
+
+def pooled_ref_for(w, iq_rows, pos, ik, ik_values=None) -> np.ndarray:
+    """The oracle's fp64 pooled scores: the plain loops, or their matrix-product
+    form (oracle.pool_mm, pinned to the loops) for large row sets."""
+    pos = np.asarray(pos)
+    if len(pos) * (int(pos.max()) + 1) <= PLAIN_POOL_MAX:
+        return oracle.pool_for(w, iq_rows, pos, ik)
+    return oracle.pool_mm(iq_rows, pos, ik, w.block_size, ik_values=ik_values)
+
+
+def tau_pool(iq_rows, ik, pos, bk, keys_per_step=16384, ik_abs=None, exact=None):
     """Per (row, block) bound on |pooled_gpu - pooled_exact|: the fp32
-    summation bound 2 * d_idx * 2^-24 * sum|p| (bf16 and E4M3 products are exact
-    in fp32), plus the run truncation of the E4M3 MFMA for E4M3 inputs."""
+    summation bound 2 * d_idx * 2^-24 * sum_c |iq_c ik_jc| (bf16 and E4M3
+    products are exact in fp32) maximised over the block's visible keys j, plus
+    the run truncation of the E4M3 MFMA for E4M3 inputs.  Beyond EXACT_TAU_MAX
+    (row, key) pairs each |ik_jc| is replaced by its maximum over the block,
+    which can only raise the bound (exact=False asks for that form at any
+    size).  ik_abs: |index_values(ik)|, when the caller already holds it."""
+    fp8 = np.asarray(iq_rows).dtype == np.uint8
+    pos = np.asarray(pos, dtype=np.int64)
     a = np.abs(index_values(iq_rows))
-    b = np.abs(index_values(ik))
-    s = 2.0 * iq_rows.shape[1] * 2.0 ** -24 * (a @ b.T)    # [n, n_kv]
-    if np.asarray(iq_rows).dtype == np.uint8:
-        ra = a.reshape(a.shape[0], -1, E4M3_RUN).max(axis=2)
-        rb = b.reshape(b.shape[0], -1, E4M3_RUN).max(axis=2)
-        s = s + E4M3_RUN_ERR * (ra @ rb.T)
+    n, d_idx = a.shape
+    ra = a.reshape(n, -1, E4M3_RUN).max(axis=2) if fp8 else None
     n_kv = ik.shape[0]
     n_blk = -(-n_kv // bk)
-    pad = np.full((len(pos), n_blk * bk), -np.inf)
-    pad[:, :n_kv] = s
-    pad[np.arange(n_blk * bk)[None, :] > np.asarray(pos)[:, None]] = -np.inf
-    return pad.reshape(len(pos), n_blk, bk).max(axis=2)
+    pmax = int(pos.max())
+    out = np.full((n, n_blk), -np.inf)
+
+    def bound(bk_abs):   # [keys, d_idx] -> [n, keys]
+        s = 2.0 * d_idx * 2.0 ** -24 * (a @ bk_abs.T)
+        if fp8:
+            s = s + E4M3_RUN_ERR * (ra @ bk_abs.reshape(bk_abs.shape[0], -1, E4M3_RUN).max(axis=2).T)
+        return s
+
+    exact = n * (pmax + 1) <= EXACT_TAU_MAX if exact is None else exact
+    step = max(bk, keys_per_step // bk * bk)
+    for j0 in range(0, pmax + 1, step):
+        j1 = min(j0 + step, n_kv)
+        nb = -(-(j1 - j0) // bk)
+        b = np.abs(index_values(ik[j0:j1])) if ik_abs is None else ik_abs[j0:j1]
+        if exact:
+            s = bound(b)
+            s[np.arange(j0, j1)[None, :] > pos[:, None]] = -np.inf
+            if s.shape[1] < nb * bk:
+                s = np.concatenate([s, np.full((n, nb * bk - s.shape[1]), -np.inf)], axis=1)
+            out[:, j0 // bk:j0 // bk + nb] = s.reshape(n, nb, bk).max(axis=2)
+        else:
+            if b.shape[0] < nb * bk:
+                b = np.concatenate([b, np.zeros((nb * bk - b.shape[0], d_idx))], axis=0)
+            out[:, j0 // bk:j0 // bk + nb] = bound(b.reshape(nb, bk, d_idx).max(axis=1))
+    return out
 
 
 class Stats:
@@ -138,37 +176,103 @@ class Stats:
         assert self.lse_max <= LSE_ABS
 
 
-def check_rows(w: synth.Workload, res: dict, b: int, g: int, rows, stats: Stats, plant=None):
-    """Compare the GPU result of some query rows of one (sequence, group)."""
+def check_rows(w: synth.Workload, res: dict, b: int, g: int, rows, stats: Stats, plant=None, host=None,
+               attend=True):
+    """Compare the GPU result of some query rows of one (sequence, group):
+    pooled scores within the summation bound, the GPU top-k equal to the
+    oracle's selection on the same fp32 values, the indices against the
+    oracle's fp64 selection (gap rule), and, with attend, the outputs and lse
+    against the oracle's attention on the GPU's block set.  host: the rows'
+    inputs for every group (oracle.inputs_for_rows_all), generated when None."""
     rows = np.asarray(rows, dtype=np.int64)
+    if len(rows) == 0:
+        return
+    if host is None:
+        host = oracle.inputs_for_rows_all(w, b, rows, plant)
     G, bk, k = w.group, w.block_size, w.topk
-    x = oracle.inputs_for_rows(w, b, g, rows, plant)
-    pos = x["pos"]
-    local = pos // bk
-    # pooled scores within the summation bound (visible part only)
-    pooled_ref = oracle.pool_for(w, x["iq"], pos, x["ik"])
-    nb = pooled_ref.shape[1]
-    idx = torch_index(rows)
-    pooled_gpu = res["pooled"][b, g].index_select(0, idx).cpu().numpy()[:, :nb].astype(np.float64)
-    tau = tau_pool(x["iq"], x["ik"], pos, bk)
-    vis = np.arange(nb)[None, :] <= local[:, None]
-    err = np.where(vis, np.abs(pooled_gpu - np.nan_to_num(pooled_ref)), 0.0)
-    assert np.all(err <= np.where(vis, tau, 0.0) + 1e-30), f"pooled beyond bound: {np.max(err / (tau + 1e-30))}"
-    # the GPU top-k on its own fp32 scores is the oracle's selection on those values, bit for bit
-    sel_gpu = res["block_idx"][b, g].index_select(0, idx).cpu().numpy()
-    pg = np.where(vis, pooled_gpu, np.nan)
-    assert np.array_equal(oracle.select(pg, pos, bk, k), sel_gpu), "top-k differs on identical fp32 input"
-    # indices against the oracle's own fp64 selection (gap rule)
-    sel_ref = oracle.select(pooled_ref, pos, bk, k)
-    for v in accept.check_indices(sel_gpu, sel_ref, pooled_ref, local, k):
-        stats.verdicts[v] += 1
-    # attention on the GPU's block set
-    K, V = oracle.kv_for_blocks(w, b, g, sel_gpu)
-    out_ref, lse_ref = oracle.attend(x["q"], pos, sel_gpu, K, V, bk, w.scale)
-    out_gpu = res["out"][b].index_select(0, idx)[:, g * G:(g + 1) * G, :].float().cpu().numpy()
-    stats.add_out(out_gpu, out_ref)
-    lse_gpu = res["lse"][b, g * G:(g + 1) * G].index_select(1, idx).cpu().numpy().T
-    stats.add_lse(lse_gpu, lse_ref)
+    pos_all = host["pos"]
+    ik = host["ik"]
+    if len(rows) * (int(pos_all.max()) + 1) > PLAIN_POOL_MAX and "ik_values" not in host:
+        host["ik_values"] = index_values(ik)        # shared by every group and chunk of the call
+        host["ik_abs"] = np.abs(host["ik_values"])
+    sel_all = res["block_idx"][b, g].index_select(0, torch_index(rows)).cpu().numpy()
+    if attend:
+        K, V = oracle.kv_for_blocks(w, b, g, sel_all)
+    per = ROW_CHUNK
+    if len(rows) * (int(pos_all.max()) + 1) <= EXACT_TAU_MAX:
+        per = max(16, min(ROW_CHUNK, ROW_CHUNK_KEYS // (int(pos_all.max()) + 1)))
+    for r0 in range(0, len(rows), per):
+        r1 = min(r0 + per, len(rows))
+        pos = pos_all[r0:r1]
+        iq = np.ascontiguousarray(host["iq"][r0:r1, g, :])
+        local = pos // bk
+        idx = torch_index(rows[r0:r1])
+        # pooled scores within the summation bound (visible part only)
+        if "pooled_ref" in host and len(rows) <= per:   # computed for every group at once by check_groups
+            pooled_ref, tau = host["pooled_ref"][g], host["tau"][g]
+        else:
+            pooled_ref = pooled_ref_for(w, iq, pos, ik, host.get("ik_values"))
+            tau = tau_pool(iq, ik, pos, bk, ik_abs=host.get("ik_abs"), exact=None if attend else False)
+        nb = pooled_ref.shape[1]
+        pooled_gpu = res["pooled"][b, g].index_select(0, idx).cpu().numpy()[:, :nb].astype(np.float64)
+        vis = np.arange(nb)[None, :] <= local[:, None]
+        err = np.where(vis, np.abs(pooled_gpu - np.nan_to_num(pooled_ref)), 0.0)
+        assert np.all(err <= np.where(vis, tau, 0.0) + 1e-30), f"pooled beyond bound: {np.max(err / (tau + 1e-30))}"
+        # the GPU top-k on its own fp32 scores is the oracle's selection on those values, bit for bit
+        sel_gpu = sel_all[r0:r1]
+        pg = np.where(vis, pooled_gpu, np.nan)
+        assert np.array_equal(oracle.select(pg, pos, bk, k), sel_gpu), "top-k differs on identical fp32 input"
+        # indices against the oracle's own fp64 selection (gap rule)
+        sel_ref = oracle.select(pooled_ref, pos, bk, k)
+        for v in accept.check_indices(sel_gpu, sel_ref, pooled_ref, local, k):
+            stats.verdicts[v] += 1
+        if not attend:
+            continue
+        # attention on the GPU's block set
+        q = np.ascontiguousarray(host["q"][r0:r1, g * G:(g + 1) * G, :])
+        out_ref, lse_ref = oracle.attend(q, pos, sel_gpu, K, V, bk, w.scale)
+        out_gpu = res["out"][b].index_select(0, idx)[:, g * G:(g + 1) * G, :].float().cpu().numpy()
+        stats.add_out(out_gpu, out_ref)
+        lse_gpu = res["lse"][b, g * G:(g + 1) * G].index_select(1, idx).cpu().numpy().T
+        stats.add_lse(lse_gpu, lse_ref)
+
+
+def check_groups(w: synth.Workload, res: dict, b: int, rows, stats: Stats, plant=None, attend=True):
+    """check_rows over every group of sequence b, the host inputs generated once."""
+    rows = np.asarray(rows, dtype=np.int64)
+    host = oracle.inputs_for_rows_all(w, b, rows, plant, with_q=attend)
+    if len(rows) * w.h_kv <= 256:
+        # few rows (decode): the oracle pool and the bound for every group in one
+        # call each, so that the rows run in parallel
+        n = len(rows)
+        iq_all = np.ascontiguousarray(host["iq"].transpose(1, 0, 2).reshape(w.h_kv * n, -1))
+        pos_all = np.tile(host["pos"], w.h_kv)
+        pr = pooled_ref_for(w, iq_all, pos_all, host["ik"])
+        host["pooled_ref"] = pr.reshape(w.h_kv, n, -1)
+        host["tau"] = tau_pool(iq_all, host["ik"], pos_all, w.block_size).reshape(w.h_kv, n, -1)
+    for g in range(w.h_kv):
+        check_rows(w, res, b, g, rows, stats, plant, host=host, attend=attend)
+
+
+def check_topk_all_rows(w: synth.Workload, res: dict, rows_per_step: int = 16384) -> int:
+    """Every row of the GPU's block_idx equals the oracle's selection run on
+    the GPU's own fp32 pooled scores, bit for bit (no gap exemption).  Returns
+    the number of rows compared."""
+    bk, k = w.block_size, w.topk
+    n = 0
+    for b in range(w.batch):
+        for g in range(w.h_kv):
+            for r0 in range(0, w.n_q, rows_per_step):
+                r1 = min(r0 + rows_per_step, w.n_q)
+                pos = w.offset + np.arange(r0, r1, dtype=np.int64)
+                pg = res["pooled"][b, g, r0:r1].cpu().numpy().astype(np.float64)
+                pg[np.arange(pg.shape[1])[None, :] > (pos // bk)[:, None]] = np.nan
+                got = res["block_idx"][b, g, r0:r1].cpu().numpy()
+                want = oracle.select(pg, pos, bk, k)
+                bad = np.nonzero(np.any(want != got, axis=1))[0]
+                assert bad.size == 0, f"(b={b}, g={g}) row {r0 + bad[0]}: got {got[bad[0]]} want {want[bad[0]]}"
+                n += r1 - r0
+    return n
 
 
 def torch_index(rows):
@@ -198,3 +302,14 @@ def sample_rows(w: synth.Workload, n_random: int, seed: int, whole_blocks: int =
         s = int(rng.integers(0, max(1, nq // bk))) * bk
         cand.update(range(s, min(s + bk, nq)))
     return np.array(sorted(cand), dtype=np.int64)
+
+
+def stratified_rows(w: synth.Workload, n_strata: int, seed: int, whole_blocks: int = 0):
+    """The edge rows of sample_rows, one seeded random row in each of n_strata
+    equal slices of the query rows, and every row of a few seeded random
+    query blocks."""
+    rng = np.random.default_rng(seed)
+    edges = np.linspace(0, w.n_q, n_strata + 1).astype(np.int64)
+    strata = [int(rng.integers(a, max(a + 1, z))) for a, z in zip(edges[:-1], edges[1:]) if a < w.n_q]
+    base = sample_rows(w, 0, seed, whole_blocks=whole_blocks)
+    return np.unique(np.concatenate([base, np.asarray(strata, dtype=np.int64)]))

@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import Stats, check_forward_matches_stages, check_rows, run_gpu, sample_rows, say
+from gpu_helpers import (Stats, check_forward_matches_stages, check_groups, check_rows, check_topk_all_rows,
+                         run_gpu, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,23 +58,27 @@ def test_fp8_small(w):
     _release()
 
 
-@pytest.mark.parametrize("name,n_rand,seqs", [("prefill_32k", 48, None), ("prefill_128k", 24, None),
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,n_rand,seqs", [("prefill_32k", 48, None), ("prefill_128k", 256, None),
                                                ("decode_256k", 0, (0, 37, 63)), ("chunked_1m", 6, None)])
 def test_fp8_full_size_sampled(name, n_rand, seqs):
+    """The full-size workloads with E4M3 index inputs: msa_forward (the fused
+    scoring + top-k launch at 32K and 128K) equals the three calls bit for bit,
+    every 128K row's top-k equals the oracle's on the GPU's fp32 scores, and
+    sampled rows match the oracle."""
     w = fp8(synth.WORKLOADS[name])
-    res = run_gpu(w, with_forward=name != "prefill_128k")
-    if "fwd" in res:
-        check_forward_matches_stages(res)
+    res = run_gpu(w, with_forward=True)
+    check_forward_matches_stages(res)
+    if name == "prefill_128k":
+        say(f"    top-k: {check_topk_all_rows(w, res)} rows bit-exact on the GPU's fp32 scores")
     st = Stats()
     plant = synth.plant_spec(w)
     if seqs is None:
-        rows = sample_rows(w, n_rand, seed=w.seed, whole_blocks=0)
-        for g in range(w.h_kv):
-            check_rows(w, res, 0, g, rows, st, plant)
+        rows = sample_rows(w, n_rand, seed=w.seed, whole_blocks=2 if name == "prefill_128k" else 0)
+        check_groups(w, res, 0, rows, st, plant)
     else:
         for b in seqs:
-            for g in range(w.h_kv):
-                check_rows(w, res, b, g, [0], st, plant)
+            check_groups(w, res, b, [0], st, plant)
     st.check()
     del res
     _release()

@@ -401,3 +401,61 @@ def test_oracle_rejects_bad_arguments():
         oracle.pool(np.zeros((1, 4), np.uint16), [10], np.zeros((8, 4), np.uint16), 4)   # p >= n_kv
     with pytest.raises(ValueError):
         oracle.select(np.zeros((1, 4)), [3], 1, 0)                                      # k < 1
+
+
+# ---------------------------------------------------------------- the matrix-product form of the pool
+def test_pool_mm_golden_and_closed_forms():
+    """pool_mm (fp64 library product + block max) reproduces the hand-worked
+    pooled values and the one-hot closed form exactly (small integers: every
+    summation order is exact)."""
+    g = json.load(open(GOLDEN))["index_example"]
+    ik = bf16_bits(g["ik"])
+    for row in g["rows"]:
+        pooled = oracle.pool_mm(bf16_bits([row["iq"]]), [row["p"]], ik, g["block_size"])
+        n = len(row["pooled"])
+        assert np.array_equal(pooled[0, :n], np.array(row["pooled"], float)), row["why"]
+        assert np.all(np.isnan(pooled[0, n:]))
+    rng = np.random.default_rng(1900)
+    bk, d_idx, n = 8, 16, 200
+    for trial in range(10):
+        a = int(rng.integers(d_idx))
+        c = rng.integers(-50, 50, size=n).astype(np.float32)
+        p = int(rng.integers(0, n - 1))
+        c[p + 1] = 1000.0   # the first invisible key must not leak into the local block
+        ik1 = np.zeros((n, d_idx), np.float32)
+        ik1[:, a] = c
+        iq = np.zeros((1, d_idx), np.float32)
+        iq[0, a] = 1.0
+        pooled = oracle.pool_mm(bf16_bits(iq), [p], bf16_bits(ik1), bk, keys_per_step=24)   # several key steps
+        for t in range(p // bk + 1):
+            assert pooled[0, t] == c[t * bk:min((t + 1) * bk, p + 1)].max()
+        assert np.all(np.isnan(pooled[0, p // bk + 1:]))
+
+
+@pytest.mark.parametrize("n_kv,bk,step", [(1000, 128, 256), (4096, 128, 16384), (333, 16, 48)])
+def test_pool_mm_equals_plain_loops(n_kv, bk, step):
+    """On random bf16 rows (ragged tail, every position class) the product
+    form equals the plain loops of oracle_pool to fp64 rounding."""
+    rng = np.random.default_rng(1901 + n_kv)
+    d_idx = 64
+    ik = rand_bits(rng, (n_kv, d_idx))
+    pos = np.unique(np.concatenate([[0, bk - 1, bk, n_kv - 1], rng.integers(0, n_kv, 60)]))
+    iq = rand_bits(rng, (len(pos), d_idx))
+    a = oracle.pool(iq, pos, ik, bk)
+    b = oracle.pool_mm(iq, pos, ik, bk, keys_per_step=step)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    fin = ~np.isnan(a)
+    assert np.max(np.abs(a[fin] - b[fin]) / np.maximum(np.abs(a[fin]), 1.0)) < 1e-13
+
+
+def test_pool_mm_fp8_equals_plain_loops():
+    rng = np.random.default_rng(1902)
+    n_kv, bk, d_idx = 700, 128, 128
+    ik = synth.to_e4m3(rand_bits(rng, (n_kv, d_idx)))
+    pos = np.array([0, 127, 128, 300, 699])
+    iq = synth.to_e4m3(rand_bits(rng, (len(pos), d_idx)))
+    a = oracle.pool_f8(iq, pos, ik, bk)
+    b = oracle.pool_mm(iq, pos, ik, bk, keys_per_step=256)
+    fin = ~np.isnan(a)
+    assert np.array_equal(fin, ~np.isnan(b))
+    assert np.max(np.abs(a[fin] - b[fin]) / np.maximum(np.abs(a[fin]), 1.0)) < 1e-13
