@@ -1,6 +1,7 @@
 // The C ABI of include/msa.h: argument validation, workspace layout and
 // dispatch.  Every check runs on the host before any HIP call, so a rejected
 // call enqueues nothing.
+#include <algorithm>
 #include <cmath>
 #include <climits>
 #include <cstddef>
@@ -11,6 +12,8 @@
 
 namespace {
 
+constexpr int kRowsMaxQForPasses = msa::kRowsMaxQ;  // decode-shaped calls (n_q <= 4) never run in passes
+
 using msa::AttnWs;
 using msa::Dims;
 
@@ -18,8 +21,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Validate a problem and derive the kernels' view of it.
-msa_status derive(const msa_problem* p, Dims* D) {
+// Validate a problem and derive the kernels' view of it.  limits = false skips
+// the bounds of one launch (32-bit row and tile indices, grid sizes): a call
+// that runs in passes checks them for each pass instead.
+msa_status derive(const msa_problem* p, Dims* D, bool limits = true) {
   if (!p) return MSA_ERR_INVALID_ARGUMENT;
   if (p->batch < 1 || p->n_q < 1 || p->n_kv < 1 || p->h_q < 1 || p->h_kv < 1 || p->head_dim < 1 ||
       p->index_dim < 1 || p->block_size < 1 || p->topk < 1)
@@ -35,9 +40,10 @@ msa_status derive(const msa_problem* p, Dims* D) {
   const int64_t n_blk = ((int64_t)p->n_kv + p->block_size - 1) / p->block_size;
   // index ranges the kernels keep in 32 bits
   const int64_t rows = (int64_t)p->batch * p->h_kv * p->n_q;
-  if (rows * p->topk > INT32_MAX || (int64_t)p->batch * p->h_kv * n_blk > INT32_MAX ||
-      (int64_t)p->n_q * p->topk > INT32_MAX || (int64_t)p->n_q * p->h_kv > INT32_MAX)
+  if (limits && (rows * p->topk > INT32_MAX || (int64_t)p->n_q * p->topk > INT32_MAX ||
+                 (int64_t)p->n_q * p->h_kv > INT32_MAX))
     return MSA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)p->batch * p->h_kv * n_blk > INT32_MAX) return MSA_ERR_INVALID_ARGUMENT;
   if (p->head_dim != msa::kHeadDim || (p->index_dim != 64 && p->index_dim != 128) || p->block_size != msa::kBk ||
       p->topk > msa::kMaxTopk || G > msa::kMaxGroup)
     return MSA_ERR_UNSUPPORTED;
@@ -49,8 +55,9 @@ msa_status derive(const msa_problem* p, Dims* D) {
   const int64_t n_groups = ((int64_t)p->n_q + msa::kChunkRows * msa::kGroupChunks - 1) /
                            (msa::kChunkRows * msa::kGroupChunks);
   const int64_t max_tiles = (rows * p->topk + pt - 1) / pt + (int64_t)p->batch * p->h_kv * n_groups * n_blk;
-  if ((int64_t)p->batch * p->h_kv > 65535 || max_tiles * 256 >= (int64_t(1) << 32) || max_tiles * pt > INT32_MAX ||
-      rows * 64 >= (int64_t(1) << 32) || rows > 65535LL * 65535LL)
+  if ((int64_t)p->batch * p->h_kv > 65535) return MSA_ERR_UNSUPPORTED;
+  if (limits && (max_tiles * 256 >= (int64_t(1) << 32) || max_tiles * pt > INT32_MAX ||
+                 rows * 64 >= (int64_t(1) << 32) || rows > 65535LL * 65535LL))
     return MSA_ERR_UNSUPPORTED;
   D->B = p->batch;
   D->n_q = p->n_q;
@@ -189,10 +196,139 @@ size_t klb_bytes(const Dims& D) {
 
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
+// ---- passes over query chunks of a long uniform prefill (msa_problem.chunk_rows)
+
+int64_t chunk_rows_of(const msa_problem* p) {
+  const int64_t c = p->chunk_rows > 0 ? p->chunk_rows : MSA_DEFAULT_CHUNK_ROWS;
+  return std::max<int64_t>(MSA_CHUNK_ALIGN, c / MSA_CHUNK_ALIGN * MSA_CHUNK_ALIGN);
+}
+
+// Does a forward or attention call on this (limit-free) view run in passes?
+// Uniform batches only; decode-shaped calls never do.
+bool runs_in_passes(const msa_problem* p, const Dims& D, const msa_varlen* vl) {
+  const bool varlen = vl && (vl->qo_lens || vl->kv_lens || vl->q_starts || vl->page_table);
+  return !varlen && D.n_q > kRowsMaxQForPasses && D.n_q > chunk_rows_of(p);
+}
+
+// One pass: rows c0 .. c0 + rows - 1 of one sequence, as a batch of one.  A
+// pass starts on a multiple of MSA_CHUNK_ALIGN, which is a whole number of the
+// gather plan's query groups and local tiles, so each row's tiles, partials and
+// merge are those of the single launch.
+msa_status pass_dims(const msa_problem* p, const Dims& D, int64_t c0, int64_t rows, Dims* Dp) {
+  msa_problem s = *p;
+  s.batch = 1;
+  s.n_q = (int32_t)rows;
+  s.q_offset = D.offset + c0;
+  s.chunk_rows = 0;
+  return derive(&s, Dp, true);
+}
+
+// Visits every pass (b, c0, rows) of a chunked call in order; stops at the
+// first non-OK status the visitor returns.
+template <typename F>
+msa_status for_each_pass(const msa_problem* p, const Dims& D, bool all_batches, F&& f) {
+  const int64_t C = chunk_rows_of(p);
+  for (int b = 0; b < (all_batches ? D.B : 1); ++b)
+    for (int64_t c0 = 0; c0 < D.n_q; c0 += C) {
+      const msa_status st = f(b, c0, std::min<int64_t>(C, D.n_q - c0));
+      if (st != MSA_OK) return st;
+    }
+  return MSA_OK;
+}
+
+// The forward pass's own workspace: pooled scores only when scoring and top-k
+// cannot run as one launch, then the attention's.
+bool forward_fused(const Dims& D) { return !msa::use_index_small(D) && msa::index_topk_fusable(D); }
+size_t forward_pass_bytes(const Dims& D) { return (forward_fused(D) ? 0 : pooled_bytes(D)) + attn_bytes(D); }
+
+// Workspace of a chunked call: the largest pass, then one pass's block_idx and
+// lse rows in the pass layout.
+msa_status chunked_bytes(const msa_problem* p, const Dims& D, bool forward, size_t* bytes) {
+  size_t most = 0;
+  const msa_status st = for_each_pass(p, D, false, [&](int, int64_t c0, int64_t rows) {
+    Dims Dp;
+    const msa_status s = pass_dims(p, D, c0, rows, &Dp);
+    if (s != MSA_OK) return s;
+    if (!attn_path_ok(Dp)) return MSA_ERR_UNSUPPORTED;
+    most = std::max(most, forward ? forward_pass_bytes(Dp) : attn_bytes(Dp));
+    return MSA_OK;
+  });
+  if (st != MSA_OK) return st;
+  const int64_t C = std::min<int64_t>(chunk_rows_of(p), D.n_q);
+  *bytes = most + round256(sizeof(int32_t) * C * D.h_kv * D.k) + round256(sizeof(float) * C * D.h_q);
+  return MSA_OK;
+}
+
+// One unchunked forward pass on view D (pointers at the view's row 0).
+hipError_t forward_pass(const Dims& D, const void* q, const void* k, const void* v, const void* index_q,
+                        const void* index_k, void* out, int32_t* block_idx, float* lse, char* ws, hipStream_t stream) {
+  hipError_t e;
+  size_t at = 0;
+  if (forward_fused(D)) {
+    e = msa::launch_index_topk(index_q, index_k, block_idx, D, stream);
+  } else {
+    float* pooled = reinterpret_cast<float*>(ws);
+    at = pooled_bytes(D);
+    e = run_index(D, index_q, index_k, pooled, stream);
+    if (e == hipSuccess) e = msa::launch_block_topk(pooled, block_idx, D, stream);
+  }
+  if (e != hipSuccess) return e;
+  return run_attention(D, q, k, v, block_idx, out, lse, ws + at, stream);
+}
+
+// A forward or attention call in passes.  Per pass: the inputs are the
+// caller's rows c0.. of sequence b (contiguous: q, index_q, out are token
+// major); block_idx and lse rows live in the pass layout at the workspace's
+// tail and are copied from (attention) or to (both) the caller's
+// [B][H_kv][n_q][k] and [B][H_q][n_q] tensors.
+msa_status run_in_passes(const msa_problem* p, const Dims& D, bool forward, const void* q, const void* k,
+                         const void* v, const void* index_q, const void* index_k, void* out, int32_t* block_idx,
+                         float* lse, char* ws, hipStream_t stream) {
+  size_t total = 0;
+  msa_status st = chunked_bytes(p, D, forward, &total);
+  if (st != MSA_OK) return st;
+  const int64_t C = std::min<int64_t>(chunk_rows_of(p), D.n_q);
+  char* tail = ws + total - round256(sizeof(int32_t) * C * D.h_kv * D.k) - round256(sizeof(float) * C * D.h_q);
+  int32_t* bidx_p = reinterpret_cast<int32_t*>(tail);
+  float* lse_p = reinterpret_cast<float*>(tail + round256(sizeof(int32_t) * C * D.h_kv * D.k));
+  const char* qb = static_cast<const char*>(q);
+  const char* kb = static_cast<const char*>(k);
+  const char* vb = static_cast<const char*>(v);
+  const char* iqb = static_cast<const char*>(index_q);
+  const char* ikb = static_cast<const char*>(index_k);
+  char* ob = static_cast<char*>(out);
+  return for_each_pass(p, D, true, [&](int b, int64_t c0, int64_t rows) {
+    Dims Dp;
+    msa_status s = pass_dims(p, D, c0, rows, &Dp);
+    if (s != MSA_OK) return s;
+    const int64_t row0 = (int64_t)b * D.n_q + c0;                        // caller's token-major row
+    const int64_t q_off = row0 * D.h_q * msa::kHeadDim * 2;              // bytes, bf16
+    const int64_t kv_off = (int64_t)b * D.h_kv * D.n_kv * msa::kHeadDim * D.kv_eb;
+    int32_t* bidx_dst = block_idx + ((int64_t)b * D.h_kv * D.n_q + c0) * D.k;
+    float* lse_dst = lse ? lse + (int64_t)b * D.h_q * D.n_q + c0 : nullptr;
+    hipError_t e;
+    if (forward) {
+      const int64_t iq_off = row0 * D.h_kv * D.d_idx * D.idx_eb;
+      const int64_t ik_off = (int64_t)b * D.n_kv * D.d_idx * D.idx_eb;
+      e = forward_pass(Dp, qb + q_off, kb + kv_off, vb + kv_off, iqb + iq_off, ikb + ik_off, ob + q_off, bidx_p,
+                       lse ? lse_p : nullptr, ws, stream);
+    } else {
+      e = msa::launch_copy_runs(bidx_dst, (int64_t)D.n_q * D.k, bidx_p, rows * D.k, rows * D.k, D.h_kv, stream);
+      if (e == hipSuccess)
+        e = run_attention(Dp, qb + q_off, kb + kv_off, vb + kv_off, bidx_p, ob + q_off, lse ? lse_p : nullptr, ws,
+                          stream);
+    }
+    if (e == hipSuccess && forward)
+      e = msa::launch_copy_runs(bidx_p, rows * D.k, bidx_dst, (int64_t)D.n_q * D.k, rows * D.k, D.h_kv, stream);
+    if (e == hipSuccess && lse) e = msa::launch_copy_runs(lse_p, rows, lse_dst, D.n_q, rows, D.h_q, stream);
+    return hip_status(e);
+  });
+}
+
 }  // namespace
 
 static_assert(sizeof(msa_problem) == 64 && offsetof(msa_problem, index_dtype) == 52 &&
-                  offsetof(msa_problem, kv_dtype) == 56,
+                  offsetof(msa_problem, kv_dtype) == 56 && offsetof(msa_problem, chunk_rows) == 60,
               "msa_problem layout is part of the ABI");
 
 extern "C" {
@@ -200,6 +336,11 @@ extern "C" {
 msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
   if (!bytes) return MSA_ERR_INVALID_ARGUMENT;
   Dims D;
+  if (op == MSA_OP_SPARSE_ATTN || op == MSA_OP_FORWARD) {
+    const msa_status st0 = derive(p, &D, false);
+    if (st0 != MSA_OK) return st0;
+    if (runs_in_passes(p, D, nullptr)) return chunked_bytes(p, D, op == MSA_OP_FORWARD, bytes);
+  }
   const msa_status st = derive(p, &D);
   if (st != MSA_OK) return st;
   switch (op) {
@@ -213,7 +354,7 @@ msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes) {
       return MSA_OK;
     case MSA_OP_FORWARD:
       if (!attn_path_ok(D)) return MSA_ERR_UNSUPPORTED;
-      *bytes = pooled_bytes(D) + attn_bytes(D);
+      *bytes = forward_pass_bytes(D);
       return MSA_OK;
     case MSA_OP_SPARSE_ATTN_BWD:
       if (D.n_blk > msa::kMaxPlanBlocks || D.kv_eb != 2 || !bwd_walk_ok(D)) return MSA_ERR_UNSUPPORTED;
@@ -256,12 +397,23 @@ msa_status msa_sparse_attn_fwd_v(const msa_problem* p, const msa_varlen* vl, con
                                  const void* v, const int32_t* block_idx, void* out, float* lse, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
   Dims D;
-  const msa_status st = derive_v(p, vl, &D);
+  msa_status st = derive(p, &D, false);
+  if (st != MSA_OK) return st;
+  const bool passes = runs_in_passes(p, D, vl);
+  if (!passes) st = derive_v(p, vl, &D);
   if (st != MSA_OK) return st;
   if (!q || !k || !v || !block_idx || !out || !workspace) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(out) ||
       !aligned16(workspace) || (lse && !aligned16(lse)))
     return MSA_ERR_INVALID_ARGUMENT;
+  if (passes) {
+    size_t need = 0;
+    st = chunked_bytes(p, D, false, &need);
+    if (st != MSA_OK) return st;
+    if (need > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    return run_in_passes(p, D, false, q, k, v, nullptr, nullptr, out, const_cast<int32_t*>(block_idx), lse,
+                         static_cast<char*>(workspace), stream);
+  }
   if (!attn_path_ok(D)) return MSA_ERR_UNSUPPORTED;
   if (attn_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
   return hip_status(run_attention(D, q, k, v, block_idx, out, lse, static_cast<char*>(workspace), stream));
@@ -271,25 +423,27 @@ msa_status msa_forward_v(const msa_problem* p, const msa_varlen* vl, const void*
                          const void* index_q, const void* index_k, void* out, int32_t* block_idx, float* lse,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Dims D;
-  const msa_status st = derive_v(p, vl, &D);
+  msa_status st = derive(p, &D, false);
+  if (st != MSA_OK) return st;
+  const bool passes = runs_in_passes(p, D, vl);
+  if (!passes) st = derive_v(p, vl, &D);
   if (st != MSA_OK) return st;
   if (!q || !k || !v || !index_q || !index_k || !out || !block_idx || !workspace) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(index_q) || !aligned16(index_k) ||
       !aligned16(out) || !aligned16(block_idx) || !aligned16(workspace) || (lse && !aligned16(lse)))
     return MSA_ERR_INVALID_ARGUMENT;
-  if (!attn_path_ok(D)) return MSA_ERR_UNSUPPORTED;
-  const size_t pb = pooled_bytes(D);
-  if (pb + attn_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
-  float* pooled = static_cast<float*>(workspace);
-  hipError_t e;
-  if (!msa::use_index_small(D) && msa::index_topk_fusable(D)) {
-    e = msa::launch_index_topk(index_q, index_k, block_idx, D, stream);
-  } else {
-    e = run_index(D, index_q, index_k, pooled, stream);
-    if (e == hipSuccess) e = msa::launch_block_topk(pooled, block_idx, D, stream);
+  if (passes) {
+    size_t need = 0;
+    st = chunked_bytes(p, D, true, &need);
+    if (st != MSA_OK) return st;
+    if (need > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    return run_in_passes(p, D, true, q, k, v, index_q, index_k, out, block_idx, lse, static_cast<char*>(workspace),
+                         stream);
   }
-  if (e != hipSuccess) return MSA_ERR_HIP;
-  return hip_status(run_attention(D, q, k, v, block_idx, out, lse, static_cast<char*>(workspace) + pb, stream));
+  if (!attn_path_ok(D)) return MSA_ERR_UNSUPPORTED;
+  if (forward_pass_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(forward_pass(D, q, k, v, index_q, index_k, out, block_idx, lse, static_cast<char*>(workspace),
+                                 stream));
 }
 
 msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q, const void* index_k,

@@ -28,6 +28,8 @@
 // that the merge needs no block_idx.
 // Entries inside one list appear in no fixed order; every row's attention is
 // independent of the other rows of its tile, so results do not depend on it.
+#include <algorithm>
+
 #include "launch.h"
 
 namespace msa {
@@ -285,6 +287,33 @@ hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const 
                      ws.part_lse, D, n_ch);
   hipLaunchKernelGGL(k_plan_tiles, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.cnt, ws.tile_off, ws.list,
                      nbgt, D.pt);
+  return hipGetLastError();
+}
+
+namespace {
+
+// n_seg runs of `words` 32-bit words, run s read at src + s * src_pitch and
+// written at dst + s * dst_pitch; `parts` workgroups share each run.
+__global__ __launch_bounds__(256) void k_copy_runs(const uint32_t* __restrict__ src, int64_t src_pitch,
+                                                   uint32_t* __restrict__ dst, int64_t dst_pitch, int64_t words,
+                                                   int parts) {
+  const int64_t seg = blockIdx.x / parts, part = blockIdx.x % parts;
+  const int64_t per = (words + parts - 1) / parts;
+  const int64_t i0 = part * per, i1 = min(words, i0 + per);
+  const uint32_t* s = src + seg * src_pitch;
+  uint32_t* d = dst + seg * dst_pitch;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) d[i] = s[i];
+}
+
+}  // namespace
+
+hipError_t launch_copy_runs(const void* src, int64_t src_pitch, void* dst, int64_t dst_pitch, int64_t words,
+                            int64_t n_seg, hipStream_t stream) {
+  if (words <= 0 || n_seg <= 0) return hipSuccess;
+  const int parts = (int)std::min<int64_t>(std::max<int64_t>(1, words / 8192), 256);
+  hipLaunchKernelGGL(k_copy_runs, dim3((unsigned)(n_seg * parts)), dim3(256), 0, stream,
+                     static_cast<const uint32_t*>(src), src_pitch, static_cast<uint32_t*>(dst), dst_pitch, words,
+                     parts);
   return hipGetLastError();
 }
 

@@ -23,6 +23,11 @@ hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims
 
 // Gather plan: per (b, g, block) lists of row-slot ids and the tile list.
 hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const Dims& D, hipStream_t stream);
+// Strided copy of n_seg runs of `words` 32-bit words (src + s * src_pitch ->
+// dst + s * dst_pitch, pitches in words): moves the per-row outputs of one pass
+// of a chunked call between the caller's layout and the pass's own.
+hipError_t launch_copy_runs(const void* src, int64_t src_pitch, void* dst, int64_t dst_pitch, int64_t words,
+                            int64_t n_seg, hipStream_t stream);
 // Sorts every bin's entries of a built plan (ascending row-slot id), so that
 // sums over a bin's rows run in a fixed order.
 hipError_t launch_plan_sort(const AttnWs& ws, const Dims& D, hipStream_t stream);

@@ -93,7 +93,16 @@ typedef enum {
  * q_offset = n_kv - n_q (prefill: n_q = n_kv gives 0; decode: n_q = 1 puts the
  * query on the last cached token, whose block is its local block).
  * index_dtype and kv_dtype are msa_dtypes (0, bf16, when the struct is
- * zero-initialised). */
+ * zero-initialised).
+ *
+ * chunk_rows bounds the workspace of a long prefill: msa_forward and
+ * msa_sparse_attn_fwd on a uniform batch (no msa_varlen) whose n_q exceeds it
+ * run as successive passes over chunk_rows query rows of one sequence, and
+ * their workspace holds one pass (the per-(row, slot) partial outputs grow
+ * with the rows of a pass, not with n_q).  0 means the library's default,
+ * MSA_DEFAULT_CHUNK_ROWS; other values are rounded down to a multiple of
+ * MSA_CHUNK_ALIGN (at least one).  Each row's results do not depend on the
+ * chunking: a chunked call writes the same bits as one pass. */
 typedef struct {
   int32_t batch, n_q, n_kv;
   int32_t h_q, h_kv;
@@ -103,7 +112,11 @@ typedef struct {
   float softmax_scale; /* 1/sqrt(d) in the standard configuration */
   int32_t index_dtype; /* element type of index_q and index_k */
   int32_t kv_dtype;    /* element type of k and v (and of k_pages, v_pages) */
+  int32_t chunk_rows;  /* query rows per pass of a long prefill (0: MSA_DEFAULT_CHUNK_ROWS) */
 } msa_problem;
+
+#define MSA_DEFAULT_CHUNK_ROWS 131072
+#define MSA_CHUNK_ALIGN 8192
 
 /* Which call a workspace is sized for. */
 typedef enum {
@@ -117,7 +130,17 @@ typedef enum {
 } msa_op;
 
 /* Bytes of device workspace the call `op` needs for problem `p` (0 for the
- * calls that take none).  Host only; enqueues nothing. */
+ * calls that take none).  Host only; enqueues nothing.
+ *
+ * How the forward workspace grows (uniform batch, G = 8, k = 16, d = 128):
+ * the attention's partial outputs take (k + 1) * G * d * 2 bytes plus a few
+ * plan and lse bytes per (sequence, group, query row) of one pass, about
+ * 278 KiB per query position at H_kv = 8, so at most ~36 GB for a pass of
+ * MSA_DEFAULT_CHUNK_ROWS rows whatever n_q is (a 1M-token prefill fits one
+ * MI355X); the fp32 pooled scores [B][H_kv][rows][n_blk] are added only when
+ * scoring and top-k cannot run as one launch (few rows against a long cache,
+ * e.g. a chunk of 8192 rows at a 1M-token cache).  Decode-shaped calls (n_q
+ * <= 4) need a few MiB.  A smaller chunk_rows trades passes for workspace. */
 msa_status msa_workspace_size(const msa_problem* p, int op, size_t* bytes);
 
 /*

@@ -61,7 +61,7 @@ def prob(**kw):
 def test_invalid_problems_rejected(kw, status):
     p = prob(**kw)
     n = ctypes.c_size_t(0)
-    assert msa.library().msa_workspace_size(ctypes.byref(p), msa.OP_FORWARD, ctypes.byref(n)) == status
+    assert msa.library().msa_workspace_size(ctypes.byref(p), msa.OP_INDEX_SCORES, ctypes.byref(n)) == status
     # the compute entry points reject it before touching the device
     fake = 1 << 20
     assert msa.library().msa_index_scores(ctypes.byref(p), fake, fake, fake, None) == status
@@ -108,7 +108,42 @@ def test_workspace_sizes():
     # partial outputs dominate: one bf16 [G, d] slab per (row, slot)
     assert a >= 2 * p.batch * p.h_kv * p.n_q * p.topk * (p.h_q // p.h_kv) * 128
     big = msa.Problem.make(1, 131072, 131072, 64, 8)
-    assert msa.workspace_size(big, msa.OP_FORWARD) < 64 << 30   # fits one MI355X comfortably
+    # scoring and top-k run as one launch here: no pooled scores in the workspace
+    assert msa.workspace_size(big, msa.OP_FORWARD) == msa.workspace_size(big, msa.OP_SPARSE_ATTN)
+    assert msa.workspace_size(big, msa.OP_FORWARD) < 40 << 30   # fits one MI355X comfortably
+
+
+def test_forward_workspace_bounded_at_1m():
+    """A 1M-token prefill runs in passes of MSA_DEFAULT_CHUNK_ROWS query rows:
+    its workspace is one pass's, under 64 GiB, where one pass over all rows
+    would need several hundred GiB."""
+    one_m = 1 << 20
+    p = msa.Problem.make(1, one_m, one_m, 64, 8)
+    f = msa.workspace_size(p, msa.OP_FORWARD)
+    a = msa.workspace_size(p, msa.OP_SPARSE_ATTN)
+    assert f <= 64 << 30 and a <= 64 << 30
+    per_pass_partials = 2 * 8 * msa.DEFAULT_CHUNK_ROWS * 17 * 8 * 128
+    assert f >= per_pass_partials
+    # smaller passes, smaller workspace; a value not on the alignment rounds down
+    small = msa.workspace_size(msa.Problem.make(1, one_m, one_m, 64, 8, chunk_rows=16384), msa.OP_FORWARD)
+    assert small < f / 4
+    assert msa.workspace_size(msa.Problem.make(1, one_m, one_m, 64, 8, chunk_rows=16384 + 5000),
+                              msa.OP_FORWARD) == small
+    # several sequences: still one pass's workspace
+    two = msa.Problem.make(2, 262144, 262144, 64, 8)
+    assert msa.workspace_size(two, msa.OP_FORWARD) <= 64 << 30
+
+
+def test_chunk_rows_at_or_above_n_q_is_one_pass():
+    """n_q at or below the pass size: the workspace of a single pass, whatever chunk_rows says."""
+    base = msa.workspace_size(msa.Problem.make(1, 32768, 32768, 64, 8), msa.OP_FORWARD)
+    for c in (32768, 40000, 1 << 20):
+        assert msa.workspace_size(msa.Problem.make(1, 32768, 32768, 64, 8, chunk_rows=c), msa.OP_FORWARD) == base
+    # passes of 8192 rows (the minimum): a quarter of the partials, plus pooled scores when
+    # 8192 rows cannot run scoring and top-k as one launch
+    c8 = msa.workspace_size(msa.Problem.make(1, 32768, 32768, 64, 8, chunk_rows=8192), msa.OP_FORWARD)
+    a8 = msa.workspace_size(msa.Problem.make(1, 32768, 32768, 64, 8, chunk_rows=8192), msa.OP_SPARSE_ATTN)
+    assert a8 < base / 3 and c8 >= a8
 
 
 def test_decode_and_chunked_offsets_accepted():
@@ -150,7 +185,7 @@ def test_problem_struct_layout():
     int64 offset on an 8-byte boundary, the float scale, the int32 dtype."""
     P = msa.Problem
     assert P.q_offset.offset == 40 and P.softmax_scale.offset == 48 and P.index_dtype.offset == 52
-    assert P.kv_dtype.offset == 56
+    assert P.kv_dtype.offset == 56 and P.chunk_rows.offset == 60
     assert ctypes.sizeof(P) == 64
 
 
@@ -210,4 +245,5 @@ def test_fp8_kv_training_calls_unsupported(op):
     assert msa.library().msa_workspace_size(ctypes.byref(p), getattr(msa, op), ctypes.byref(n)) == \
         msa.ERR_UNSUPPORTED
     assert msa.workspace_size(prob(h_q=16, h_kv=2), getattr(msa, op)) > 0
+
 
