@@ -8,7 +8,7 @@ import of a compute entry point raises; nothing falls back to another path.
 Entry points (same names as the C ABI, without the ``msa_`` prefix):
 ``index_scores``, ``block_topk``, ``sparse_attn_fwd``, ``forward``,
 ``index_kl``, ``dense_attn_fwd``, ``dense_index_kl``, ``sparse_attn_bwd``, ``index_kl_bwd``,
-``workspace_size``; ``Problem`` mirrors ``msa_problem``.  Each compute call
+``forward_noalloc``, ``workspace_size``; ``Problem`` mirrors ``msa_problem``.  Each compute call
 takes an optional ``varlen`` (a ``Varlen``, mirroring ``msa_varlen``: per
 sequence query and cache lengths, packed query rows, a page table); given,
 the ``*_v`` variant of the C call is used.
@@ -30,7 +30,8 @@ DEFAULT_CHUNK_ROWS, CHUNK_ALIGN = 131072, 8192  # MSA_DEFAULT_CHUNK_ROWS, MSA_CH
 EXPORTS = ("msa_workspace_size", "msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
            "msa_index_scores_v", "msa_block_topk_v", "msa_sparse_attn_fwd_v", "msa_forward_v", "msa_index_kl",
            "msa_dense_attn_fwd", "msa_dense_index_kl", "msa_sparse_attn_bwd", "msa_index_kl_bwd",
-           "msa_status_string")
+           "msa_forward_noalloc", "msa_status_string")
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MSA_NOALLOC_SCRATCH_BYTES
 
 
 class Problem(ctypes.Structure):
@@ -114,6 +115,7 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.msa_dense_index_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.msa_sparse_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_index_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.msa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         for name in EXPORTS[:-1]:
             getattr(lib, name).restype = ctypes.c_int
         lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -357,6 +359,25 @@ def forward(p: Problem, q, k, v, index_q, index_k, out, block_idx, lse=None, wor
     else:
         rc = L.msa_forward_v(ctypes.byref(p), ctypes.byref(varlen), *args)
     _check(rc, "msa_forward")
+    return out
+
+
+def forward_noalloc(p: Problem, q, k, v, index_q, index_k, out, block_idx, lse=None, stream=None):
+    """forward() with the library's fixed device scratch as its workspace (no
+    allocation anywhere; problems needing more than NOALLOC_SCRATCH_BYTES raise
+    MsaError with ERR_WORKSPACE_TOO_SMALL).  Calls that overlap in time on one
+    GPU share the scratch and race."""
+    a = _Args("forward_noalloc")
+    _qkv_args(a, p, q, k, v, None)
+    _index_args(a, p, index_q, index_k, None)
+    a.add(out, "out", _BF16, _rows(p, None) * p.h_q * p.head_dim)
+    a.add(block_idx, "block_idx", _I32, _bidx_numel(p))
+    a.add(lse, "lse", _F32, _row_numel(p, p.h_q), optional=True)
+    a.device()
+    L, st = library(), _stream(stream, q)
+    rc = L.msa_forward_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(index_q), _ptr(index_k), _ptr(out),
+                               _ptr(block_idx), _ptr(lse), st)
+    _check(rc, "msa_forward_noalloc")
     return out
 
 

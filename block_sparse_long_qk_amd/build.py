@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
 SOURCES = ["index_scores.hip", "block_topk.hip", "gather_plan.hip", "sparse_attn.hip", "decode.hip", "kl.hip",
-           "dense.hip", "bwd.hip", "abi.cpp"]
+           "dense.hip", "bwd.hip", "noalloc.hip", "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

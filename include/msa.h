@@ -331,6 +331,26 @@ msa_status msa_forward_v(const msa_problem* p, const msa_varlen* vl, const void*
                          const void* index_q, const void* index_k, void* out, int32_t* block_idx, float* lse,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * msa_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a fixed array of
+ * MSA_NOALLOC_SCRATCH_BYTES in the library's own device memory, one per GPU,
+ * held until the process ends; the call allocates nothing.  Problems whose
+ * msa_workspace_size(p, MSA_OP_FORWARD) exceeds it return
+ * MSA_ERR_WORKSPACE_TOO_SMALL with nothing enqueued (it covers decode steps
+ * such as 64 sequences against 256K-token caches, and prefills of a few
+ * thousand rows; use msa_forward with a caller's workspace beyond that).
+ * Results equal msa_forward's bit for bit.  All calls on one GPU share its
+ * array: calls that overlap in time on one GPU race and must be serialised
+ * by the caller (one stream, or events).  Other arguments and errors as
+ * msa_forward.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+msa_status msa_forward_noalloc(const msa_problem* p, const void* q, const void* k, const void* v,
+                               const void* index_q, const void* index_k, void* out, int32_t* block_idx, float* lse,
+                               hipStream_t stream);
+
 /* Static description of a status code. */
 const char* msa_status_string(msa_status s);
 

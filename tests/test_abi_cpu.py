@@ -247,3 +247,19 @@ def test_fp8_kv_training_calls_unsupported(op):
     assert msa.workspace_size(prob(h_q=16, h_kv=2), getattr(msa, op)) > 0
 
 
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """msa_forward_noalloc checks the workspace a problem needs against its
+    fixed scratch on the host, before any HIP call."""
+    lib = msa.library()
+    ok = 1 << 20
+    big = msa.Problem.make(1, 32768, 32768, 64, 8)
+    assert msa.workspace_size(big, msa.OP_FORWARD) > msa.NOALLOC_SCRATCH_BYTES
+    assert lib.msa_forward_noalloc(ctypes.byref(big), ok, ok, ok, ok, ok, ok, ok, None,
+                                   None) == msa.ERR_WORKSPACE_TOO_SMALL
+    bad = prob(h_q=6, h_kv=4)
+    assert lib.msa_forward_noalloc(ctypes.byref(bad), ok, ok, ok, ok, ok, ok, ok, None,
+                                   None) == msa.ERR_INVALID_ARGUMENT
+    # the 256K decode step and the 4K prefill fit
+    assert msa.workspace_size(msa.Problem.make(64, 1, 262144, 64, 8), msa.OP_FORWARD) <= msa.NOALLOC_SCRATCH_BYTES
+    assert msa.workspace_size(prob(), msa.OP_FORWARD) <= msa.NOALLOC_SCRATCH_BYTES
