@@ -5,39 +5,39 @@
 // the query is always included) and section 内核协同设计 (softmax preserves the
 // order, so the selection runs on the raw scores with no max, exp or sum).
 //
-// One wavefront per (sequence, group, query) row.  Every candidate block t < l
-// (l = the local block) is turned into a 64-bit key
-//     (order-preserving bits of the fp32 score, -0 folded onto +0) << 32 | ~t
-// so a single unsigned compare ranks by (score desc, index asc) and all keys of
-// a row are distinct.  Selection:
-//   0. rows of up to 2048 blocks are loaded into registers once;
-//   1. each lane takes the max key of its strided share of the row;
-//   2. a sort of the 64 lane maxima (a bitonic network, mostly DPP moves)
-//      gives tau, the (k-1)-th largest of them; at least k-1 keys of the row are
-//      >= tau, and for score rows of any shape only a handful more;
-//   3. the keys >= tau are compacted into LDS (one per lane) and sorted (over
-//      16, 32 or 64 lanes, as many as they need): the (k-1)-th largest of them
-//      is the exact threshold; should more than 64 pass tau, an exact bitwise
-//      threshold search over the whole row takes over;
-//   4. the selected blocks are emitted in ascending order with ballots (rank =
-//      number of selected blocks with a smaller index), then the local block.
+// One wavefront per (sequence, group, query) row; the waves stay resident and
+// walk the rows, the next row's scores loading while the current one is
+// selected.  Scores are compared as fp32 values (-0 equals +0; lanes and slots
+// without a candidate hold -inf, and pooled scores are finite).  Selection:
+//   0. the row's candidate scores (blocks t < l, l = the local block; block t
+//      = lane + 64 j) are loaded into registers through a buffer descriptor
+//      whose range is the row;
+//   1. each lane takes the max of its share of the row, and tau is the (k-1)-th
+//      largest of the 64 lane maxima (a sorting network, mostly DPP moves): at
+//      least k-1 scores of the row are >= tau, and for score rows of any shape
+//      only a handful more;
+//   2. the scores >= tau are compacted into LDS in ascending block order with
+//      their block ids, one per lane, and T, the (k-1)-th largest of them, is
+//      read off a sorted copy (16, 32 or 64 lanes, as many as they need);
+//      should more than 64 pass tau (many equal scores), T comes from a bitwise
+//      search over the whole row instead;
+//   3. the blocks scoring > T, and the lowest-indexed blocks scoring == T until
+//      k-1 are taken (equal scores go to the lower index), are written in
+//      ascending order (ballot ranks), then the local block.
+#include <algorithm>
+#include <type_traits>
+
 #include "launch.h"
 
 namespace msa {
 namespace {
 
-__device__ __forceinline__ uint64_t sel_key(float f, int t) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;                       // -0 ranks as +0
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);     // order-preserving
-  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)t);
-}
-
-// Value of lane `src` (uniform) as a uniform.
-__device__ __forceinline__ uint64_t lane_u64(uint64_t x, int src) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, src);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), src);
-  return ((uint64_t)hi << 32) | lo;
+// Order-preserving unsigned key of a score (the bitwise search of rows with
+// many equal scores): -0 + 0 = +0 folds the signed zeros, then negative scores
+// have all bits flipped and positive ones the sign bit set.
+__device__ __forceinline__ uint32_t sel_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // Partner values for the sorting network, each lane getting lane ^ M's value.
@@ -46,36 +46,33 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t x, int src) {
 // row by 8, ^4 the half-row mirror followed by the quad flip.  Across rows:
 // ^16 and ^31 by ds_swizzle (xor within 32 lanes), ^63 by ds_bpermute.
 template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 template <int M>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
-  if constexpr (M == 1) return dpp_u32<0xB1>(v);                  // quad_perm [1, 0, 3, 2]
-  else if constexpr (M == 2) return dpp_u32<0x4E>(v);             // quad_perm [2, 3, 0, 1]
-  else if constexpr (M == 3) return dpp_u32<0x1B>(v);             // quad_perm [3, 2, 1, 0]
-  else if constexpr (M == 4) return dpp_u32<0x1B>(dpp_u32<0x141>(v));
-  else if constexpr (M == 7) return dpp_u32<0x141>(v);            // row_half_mirror
-  else if constexpr (M == 8) return dpp_u32<0x128>(v);            // row_ror:8
-  else if constexpr (M == 15) return dpp_u32<0x140>(v);           // row_mirror
-  else if constexpr (M == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
-  else if constexpr (M == 31) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x7C1F);
-  else return (uint32_t)__shfl_xor((int)v, M, 64);
-}
-template <int M>
-__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x) {
-  return ((uint64_t)xor_lane<M>((uint32_t)(x >> 32)) << 32) | xor_lane<M>((uint32_t)x);
+__device__ __forceinline__ float xor_lane(float v) {
+  if constexpr (M == 1) return dpp_f32<0xB1>(v);                  // quad_perm [1, 0, 3, 2]
+  else if constexpr (M == 2) return dpp_f32<0x4E>(v);             // quad_perm [2, 3, 0, 1]
+  else if constexpr (M == 3) return dpp_f32<0x1B>(v);             // quad_perm [3, 2, 1, 0]
+  else if constexpr (M == 4) return dpp_f32<0x1B>(dpp_f32<0x141>(v));
+  else if constexpr (M == 7) return dpp_f32<0x141>(v);            // row_half_mirror
+  else if constexpr (M == 8) return dpp_f32<0x128>(v);            // row_ror:8
+  else if constexpr (M == 15) return dpp_f32<0x140>(v);           // row_mirror
+  else if constexpr (M == 16)
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  else if constexpr (M == 31)
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x7C1F));
+  else return __shfl_xor(v, M, 64);
 }
 
 // Compare-exchange with lane ^ M: the lane whose `LOWBIT` is clear keeps the smaller.
 template <int M, int LOWBIT>
-__device__ __forceinline__ uint64_t cmpx(uint64_t x, int lane) {
-  const uint64_t y = xor_lane_u64<M>(x);
-  const uint64_t mn = x < y ? x : y, mx = x < y ? y : x;
-  return (lane & LOWBIT) == 0 ? mn : mx;
+__device__ __forceinline__ float cmpx(float x, int lane) {
+  const float y = xor_lane<M>(x);
+  return (lane & LOWBIT) == 0 ? fminf(x, y) : fmaxf(x, y);
 }
 template <int S>
-__device__ __forceinline__ uint64_t half_clean(uint64_t x, int lane) {  // xor partners S, S/2, ..., 1
+__device__ __forceinline__ float half_clean(float x, int lane) {  // xor partners S, S/2, ..., 1
   if constexpr (S == 0) {
     return x;
   } else {
@@ -84,40 +81,26 @@ __device__ __forceinline__ uint64_t half_clean(uint64_t x, int lane) {  // xor p
   }
 }
 template <int SIZE>
-__device__ __forceinline__ uint64_t merge_level(uint64_t x, int lane) {
+__device__ __forceinline__ float merge_level(float x, int lane) {
   x = cmpx<SIZE - 1, SIZE / 2>(x, lane);  // flip: lane i against SIZE-1-i of its block
   return half_clean<SIZE / 4>(x, lane);
 }
 
-// Sort of one value per lane, ascending over lanes 0..63: a bitonic network
-// in its flip form (each merge level starts by comparing lane i with the
-// mirrored lane of its block, then halves with xor partners), so that 18 of
-// its 21 exchange steps are DPP moves.
-__device__ __forceinline__ uint64_t wave_sort_asc(uint64_t x, int lane) {
-  x = merge_level<2>(x, lane);
-  x = merge_level<4>(x, lane);
-  x = merge_level<8>(x, lane);
-  x = merge_level<16>(x, lane);
-  x = merge_level<32>(x, lane);
-  return merge_level<64>(x, lane);
-}
-
-// Inclusive prefix sum over the 64 lanes: DPP shifts within rows of 16, then
-// the row broadcasts of lanes 15 and 31 (no LDS).
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+// Ascending sort of one value per lane over blocks of N lanes (16, 32 or 64):
+// a bitonic network in its flip form (each merge level starts by comparing
+// lane i with the mirrored lane of its block, then halves with xor partners),
+// so that all but three of the 64-lane network's 21 exchange steps, and all of
+// the 16-lane one's, are DPP moves.
+template <int N>
+__device__ __forceinline__ float sort_lanes(float x, int lane) {
+  x = merge_level<16>(merge_level<8>(merge_level<4>(merge_level<2>(x, lane), lane), lane), lane);
+  if constexpr (N >= 32) x = merge_level<32>(x, lane);
+  if constexpr (N >= 64) x = merge_level<64>(x, lane);
   return x;
 }
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
+__device__ __forceinline__ float lane_f32(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -126,117 +109,198 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// PER > 0: the row's candidates (at most 64*PER) are loaded once into
-// registers and every pass runs on them; PER == 0: passes re-read the row.
-template <int PER>
+// Number of the wave's lanes where pred holds (a scalar).
+__device__ __forceinline__ int count(bool pred) { return __popcll(__ballot(pred)); }
+
+// PER > 0: a row's candidates (at most 64 * PER) are loaded once into
+// registers, the next row's while the current one is selected; PER == 0 (rows
+// beyond 2048 blocks): each of the two passes over the row streams it, eight
+// loads in flight (the second pass mostly from L2).
+template <int PER, bool VL>
 __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ pooled, int32_t* __restrict__ out,
-                                                    Dims D, int64_t nrows) {
-  __shared__ uint64_t cand[4][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= nrows) return;  // whole wave; no workgroup barrier below
-  const int i = (int)(row % D.n_q);
-  const int b = (int)(row / ((int64_t)D.h_kv * D.n_q));
-  if (i >= seq_nq(D, b)) return;  // a row past this sequence's queries (variable lengths)
-  const int local = (int)((seq_offset(D, b) + i) / kBk);
-  const float* src = pooled + row * D.n_blk;
-  int32_t* dst = out + row * D.k;
-  const int k = D.k;
-
-  if (local + 1 <= k) {  // every visible block is kept
-    for (int s = lane; s < k; s += 64) dst[s] = s <= local ? s : -1;
-    return;
-  }
-  const int kk = k - 1;  // blocks to pick among the `local` candidates
-  if (kk == 0) {
-    if (lane == 0) dst[0] = local;
-    return;
-  }
-
+                                                    Dims D, int nrows) {
+  __shared__ uint2 cand[4][64];  // (score bits, block) of the row's scores >= tau
+  // the wave index as a uniform value, so that the rows' buffer descriptors
+  // live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int stride = gridDim.x * 4;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const float NEG_INF = -__builtin_huge_valf();
+  const int k = D.k, kk = k - 1;  // kk blocks to pick among a row's `local` candidates
   constexpr int NREG = PER > 0 ? PER : 1;
-  uint64_t reg[NREG];  // keys of t = lane + 64*j (0 = no candidate)
-  if constexpr (PER > 0) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int t = lane + 64 * j;
-      reg[j] = t < local ? sel_key(src[t], t) : 0;
-    }
-  }
-  auto key_at = [&](int j, int t) -> uint64_t {
-    if constexpr (PER > 0) return reg[j];
-    else return t < local ? sel_key(src[t], t) : 0;
+
+  // A row (r < nrows: the launch's rows number below 2^31): its local block
+  // (-1: nothing to do) and the descriptor of its candidate scores (offsets
+  // past the candidates read 0 and never leave them).
+  struct Row {
+    int r, local;
+    __amdgpu_buffer_rsrc_t rs;
   };
-  const int nj = PER > 0 ? PER : (local + 63) / 64;
-
-  // 1. lane maxima
-  uint64_t mx = 0;
-  for (int j = 0; j < nj; ++j) {
-    const uint64_t c = key_at(j, lane + 64 * j);
-    mx = c > mx ? c : mx;
-  }
-  // 2. tau = kk-th largest lane maximum (lanes without candidates hold 0)
-  const uint64_t tau = lane_u64(wave_sort_asc(mx, lane), 64 - kk);
-
-  // 3. compact the keys >= tau and find the exact kk-th largest key
-  int mine = 0;
-  for (int j = 0; j < nj; ++j) mine += key_at(j, lane + 64 * j) >= tau;
-  const int incl = wave_incl_scan(mine);
-  const int total = __builtin_amdgcn_readlane(incl, 63);
-  uint64_t thr;
-  if (total <= 64) {
-    int at = incl - mine;
-    for (int j = 0; j < nj; ++j) {
-      const uint64_t c = key_at(j, lane + 64 * j);
-      if (c >= tau) cand[wave][at++] = c;
+  auto row_at = [&](int r) {
+    Row x;
+    x.r = r;
+    x.local = -1;
+    if (r < nrows) {
+      const int i = r % D.n_q;
+      if constexpr (VL) {
+        const int b = r / (D.h_kv * D.n_q);
+        if (i < seq_nq(D, b)) x.local = (int)((seq_offset(D, b) + i) / kBk);  // rows past a sequence's queries: none
+      } else {
+        x.local = (int)((D.offset + i) / kBk);
+      }
     }
-    wave_lds_sync();
-    const uint64_t mine_c = lane < total ? cand[wave][lane] : 0;
-    // the candidates sit in lanes 0 .. total-1: a network over the first 16 or
-    // 32 lanes orders them when they fit there (uniform branch on total)
-    if (total <= 16 && kk <= 16) {
-      const uint64_t x = merge_level<16>(merge_level<8>(merge_level<4>(merge_level<2>(mine_c, lane), lane), lane), lane);
-      thr = lane_u64(x, 16 - kk);
-    } else if (total <= 32 && kk <= 32) {
-      uint64_t x = merge_level<16>(merge_level<8>(merge_level<4>(merge_level<2>(mine_c, lane), lane), lane), lane);
-      thr = lane_u64(merge_level<32>(x, lane), 32 - kk);
+    x.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(pooled + (int64_t)r * D.n_blk), (short)0,
+                                             max(x.local, 0) * 4, kRawBufferFlags);
+    return x;
+  };
+  auto load = [&](const Row& x, int j) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(x.rs, 4 * lane + 256 * j, 0, 0));
+  };
+  // registers of a row's scores: issued now, used later
+  auto fetch = [&](const Row& x, float (&v)[NREG]) {
+    if constexpr (PER > 0) {
+      const int nj = (x.local + 63) >> 6;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (j < nj) v[j] = load(x, j);
+    }
+  };
+
+  Row cur = row_at(blockIdx.x * 4 + wave);
+  float vc[NREG];
+  fetch(cur, vc);
+  while (cur.r < nrows) {
+    const Row nxt = row_at(cur.r + stride);
+    float vn[NREG];
+    fetch(nxt, vn);
+    const int local = cur.local;
+    int32_t* dst = out + (int64_t)cur.r * k;
+    if (local < 0) {
+      // not a row of this batch
+    } else if (local + 1 <= k) {  // every visible block is kept
+      for (int s = lane; s < k; s += 64) dst[s] = s <= local ? s : -1;
+    } else if (kk == 0) {
+      if (lane == 0) dst[0] = local;
     } else {
-      thr = lane_u64(wave_sort_asc(mine_c, lane), 64 - kk);
-    }
-  } else {
-    // exact threshold: the largest key x with #{keys >= x} >= kk, bit by bit
-    uint64_t prefix = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-      const uint64_t trial = prefix | (1ull << bit);
-      int c = 0;
-      for (int j = 0; j < nj; ++j) c += key_at(j, lane + 64 * j) >= trial;
-      if (wave_sum(c) >= kk) prefix = trial;
-    }
-    thr = prefix;
-  }
+      const int nj = (local + 63) >> 6;  // score slots in use (uniform)
+      // f(j, score of block lane + 64 j) for j = 0 .. nj-1, in order; only the
+      // last slot can reach past the candidates
+      auto each_score = [&](auto&& f) {
+        if constexpr (PER > 0) {
+#pragma unroll
+          for (int j = 0; j < PER; ++j)
+            if (j < nj) f(j, j < nj - 1 || lane + 64 * j < local ? vc[j] : NEG_INF);
+        } else {
+          for (int j0 = 0; j0 < nj; j0 += 8) {  // eight loads in flight per step
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = load(cur, j0 + u);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (j0 + u < nj) f(j0 + u, lane + 64 * (j0 + u) < local ? v[u] : NEG_INF);
+          }
+        }
+      };
 
-  // 4. ascending output: rank by ballot over the strided slots
-  int base = 0;
-  for (int j = 0; j < nj; ++j) {
-    const int t = lane + 64 * j;
-    const bool take = t < local && key_at(j, t) >= thr;
-    const uint64_t m = __ballot(take);
-    if (take) dst[base + __popcll(m & ((1ull << lane) - 1ull))] = t;
-    base += __popcll(m);
+      // 1. tau = kk-th largest lane maximum
+      float mx = NEG_INF;
+      each_score([&](int, float c) { mx = fmaxf(mx, c); });
+      const float tau = lane_f32(sort_lanes<64>(mx, lane), 64 - kk);
+
+      // 2. scores >= tau, compacted in ascending block order (slot 63 takes
+      // the overflow of a row with more than 64, whose list is not used)
+      int total = 0;
+      each_score([&](int j, float c) {
+        const bool take = c >= tau;
+        const uint64_t m = __ballot(take);
+        if (m) {
+          const int slot = total + (int)__popcll(m & below);
+          if (take) cand[wave][slot < 63 ? slot : 63] = make_uint2(__float_as_uint(c), (uint32_t)(lane + 64 * j));
+          total += __popcll(m);
+        }
+      });
+      if (total <= 64) {
+        wave_lds_sync();
+        const bool have = lane < total;
+        const uint2 e = cand[wave][lane];
+        const float c = have ? __uint_as_float(e.x) : NEG_INF;
+        // T from a sorted copy of the candidates: a network over the first 16
+        // or 32 lanes when they hold them all (uniform branch on total)
+        float thr;
+        if (total <= 16 && kk <= 16)
+          thr = lane_f32(sort_lanes<16>(c, lane), 16 - kk);
+        else if (total <= 32 && kk <= 32)
+          thr = lane_f32(sort_lanes<32>(c, lane), 32 - kk);
+        else
+          thr = lane_f32(sort_lanes<64>(c, lane), 64 - kk);
+        // 3. emit: scores > T, then scores == T in block order until kk
+        const uint64_t meq = __ballot(have && c == thr);
+        const int need_eq = kk - count(have && c > thr);
+        const bool take = have && (c > thr || (c == thr && __popcll(meq & below) < need_eq));
+        const uint64_t m = __ballot(take);
+        if (take) dst[__popcll(m & below)] = (int)e.y;
+      } else {
+        // many equal scores: T = the largest key x with #{keys >= x} >= kk, bit by bit
+        uint32_t thr = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t trial = thr | (1u << bit);
+          int n = 0;
+          each_score([&](int, float c) { n += count(sel_key(c) >= trial); });
+          if (n >= kk) thr = trial;
+        }
+        int n_gt = 0;
+        each_score([&](int, float c) { n_gt += count(sel_key(c) > thr); });
+        const int need_eq = kk - n_gt;  // >= 1 keys equal to T are taken
+        int base = 0, eq_seen = 0;
+        each_score([&](int j, float c) {
+          const uint32_t u = sel_key(c);
+          const bool eq = u == thr;
+          const uint64_t meq = __ballot(eq);
+          const bool take = u > thr || (eq && eq_seen + __popcll(meq & below) < need_eq);
+          const uint64_t m = __ballot(take);
+          if (take) dst[base + __popcll(m & below)] = lane + 64 * j;
+          base += __popcll(m);
+          eq_seen += __popcll(meq);
+        });
+      }
+      if (lane == 0) dst[kk] = local;
+      wave_lds_sync();  // the list is read before the next row overwrites it
+    }
+    cur = nxt;
+#pragma unroll
+    for (int j = 0; j < NREG; ++j) vc[j] = vn[j];
   }
-  if (lane == 0) dst[kk] = local;
 }
 
 }  // namespace
 
 hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims& D, hipStream_t stream) {
   const int64_t nrows = (int64_t)D.B * D.h_kv * D.n_q;
-  const int64_t blocks = (nrows + 3) / 4;
-  if (D.n_blk <= 64 * 16)
-    hipLaunchKernelGGL(k_block_topk<16>, dim3((unsigned)blocks), dim3(256), 0, stream, pooled, block_idx, D, nrows);
-  else if (D.n_blk <= 64 * 32)
-    hipLaunchKernelGGL(k_block_topk<32>, dim3((unsigned)blocks), dim3(256), 0, stream, pooled, block_idx, D, nrows);
-  else
-    hipLaunchKernelGGL(k_block_topk<0>, dim3((unsigned)blocks), dim3(256), 0, stream, pooled, block_idx, D, nrows);
+  // resident waves that walk the rows: up to 8 workgroups of 4 waves per CU
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
+  }
+  const dim3 grid((unsigned)std::min<int64_t>((nrows + 3) / 4, (int64_t)cus * 8)), block(256);
+  const int n = (int)nrows;  // below 2^31 (the problem's row count is checked on the host)
+  // scores per lane for the longest row (rows are at most n_blk - 1 candidates)
+  const int per = (D.n_blk + 63) / 64;
+  auto go = [&](auto per_c, auto vl) {
+    hipLaunchKernelGGL((k_block_topk<decltype(per_c)::value, decltype(vl)::value>), grid, block, 0, stream, pooled,
+                       block_idx, D, n);
+  };
+  auto pick = [&](auto vl) {
+    if (per <= 4) go(std::integral_constant<int, 4>{}, vl);
+    else if (per <= 8) go(std::integral_constant<int, 8>{}, vl);
+    else if (per <= 16) go(std::integral_constant<int, 16>{}, vl);
+    else if (per <= 32) go(std::integral_constant<int, 32>{}, vl);
+    else go(std::integral_constant<int, 0>{}, vl);
+  };
+  if (dims_varlen(D)) pick(std::true_type{}); else pick(std::false_type{});
   return hipGetLastError();
 }
 

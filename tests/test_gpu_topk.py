@@ -104,3 +104,28 @@ def test_periodic_long_rows_take_the_exact_path():
     row = -(t % 64).astype(np.float32)
     pooled = np.broadcast_to(row, (1, 1, n_q, n_kv // 128)).copy()
     check(pooled, n_q, n_kv, 1, 16, name="periodic, 1000 blocks")
+
+
+# Row lengths for every register width of the kernel (4, 32 and 64 keys per
+# lane) and past 8192 blocks, where each pass re-reads the row.
+@pytest.mark.parametrize("n_blk,n_q", [(200, 700), (1500, 301), (3000, 257), (9000, 64)])
+def test_every_row_width(n_blk, n_q):
+    rng = np.random.default_rng(3600 + n_blk)
+    n_kv = 128 * n_blk - 77
+    pooled = rng.standard_normal((1, 2, n_q, n_blk)).astype(np.float32) * 10
+    pooled[0, 1] = np.round(pooled[0, 1])   # ties in the second group
+    check(pooled, n_q, n_kv, 2, 16, name=f"{n_blk} blocks")
+
+
+def test_ties_at_the_threshold():
+    """The ten best scores are distinct and twenty blocks tie for the next
+    place: the five lowest-indexed of the tied blocks are taken."""
+    rng = np.random.default_rng(3700)
+    n_q, n_blk = 256, 700
+    n_kv = 128 * n_blk - 50          # positions from 128 * (n_blk - 3) + 78: at least n_blk - 3 candidates
+    pooled = -rng.random((1, 1, n_q, n_blk)).astype(np.float32)
+    for r in range(n_q):
+        perm = rng.permutation(n_blk - 3)
+        pooled[0, 0, r, perm[:10]] = 100.0 + np.arange(10)
+        pooled[0, 0, r, perm[10:30]] = 50.0
+    check(pooled, n_q, n_kv, 1, 16, name="threshold ties")
