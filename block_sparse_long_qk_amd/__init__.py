@@ -30,7 +30,7 @@ DEFAULT_CHUNK_ROWS, CHUNK_ALIGN = 131072, 8192  # MSA_DEFAULT_CHUNK_ROWS, MSA_CH
 EXPORTS = ("msa_workspace_size", "msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
            "msa_index_scores_v", "msa_block_topk_v", "msa_sparse_attn_fwd_v", "msa_forward_v", "msa_index_kl",
            "msa_dense_attn_fwd", "msa_dense_index_kl", "msa_sparse_attn_bwd", "msa_index_kl_bwd",
-           "msa_forward_noalloc", "msa_status_string")
+           "msa_forward_noalloc", "msa_forward_marked", "msa_status_string")
 NOALLOC_SCRATCH_BYTES = 128 << 20  # MSA_NOALLOC_SCRATCH_BYTES
 
 
@@ -116,6 +116,8 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.msa_sparse_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_index_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.msa_forward_marked.argtypes = [P, V, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(vp),
+                                           ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int)]
         for name in EXPORTS[:-1]:
             getattr(lib, name).restype = ctypes.c_int
         lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -360,6 +362,34 @@ def forward(p: Problem, q, k, v, index_q, index_k, out, block_idx, lse=None, wor
         rc = L.msa_forward_v(ctypes.byref(p), ctypes.byref(varlen), *args)
     _check(rc, "msa_forward")
     return out
+
+
+def forward_marked(p: Problem, q, k, v, index_q, index_k, out, block_idx, lse, workspace, events, stream=None,
+                   varlen: Varlen | None = None, workspace_bytes=None):
+    """forward() with a HIP event recorded after each kernel it launches (for
+    benchmarks).  events: torch.cuda.Event objects with timing enabled, each
+    recorded once beforehand (so that the underlying event exists).  Returns
+    the list of (kernel name, event before, event after) of the call."""
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    a = _Args("forward_marked")
+    _qkv_args(a, p, q, k, v, varlen)
+    _index_args(a, p, index_q, index_k, varlen)
+    a.add(out, "out", _BF16, _rows(p, varlen) * p.h_q * p.head_dim)
+    a.add(block_idx, "block_idx", _I32, _bidx_numel(p))
+    a.add(lse, "lse", _F32, _row_numel(p, p.h_q), optional=True)
+    a.workspace(workspace, nb)
+    _varlen_args(a, p, varlen)
+    a.device()
+    L, st = library(), _stream(stream, q)
+    n = len(events)
+    evs = (ctypes.c_void_p * n)(*[e.cuda_event for e in events])
+    names = (ctypes.c_char_p * n)()
+    used = ctypes.c_int(0)
+    rc = L.msa_forward_marked(ctypes.byref(p), ctypes.byref(varlen) if varlen is not None else None, _ptr(q), _ptr(k),
+                              _ptr(v), _ptr(index_q), _ptr(index_k), _ptr(out), _ptr(block_idx), _ptr(lse),
+                              _ptr(workspace), nb, st, evs, n, names, ctypes.byref(used))
+    _check(rc, "msa_forward_marked")
+    return [(names[i].decode(), events[i], events[i + 1]) for i in range(used.value - 1)]
 
 
 def forward_noalloc(p: Problem, q, k, v, index_q, index_k, out, block_idx, lse=None, stream=None):

@@ -327,6 +327,25 @@ msa_status run_in_passes(const msa_problem* p, const Dims& D, bool forward, cons
 
 }  // namespace
 
+// ---- timing marks (msa_forward_marked)
+namespace {
+struct MarkLog {
+  hipEvent_t* events;
+  const char** names;
+  int cap, n;  // events available, events recorded
+};
+thread_local MarkLog* g_marks = nullptr;
+}  // namespace
+
+namespace msa {
+void mark(const char* name, hipStream_t stream) {
+  MarkLog* m = g_marks;
+  if (!m || m->n >= m->cap) return;
+  if (m->names) m->names[m->n - 1] = name;
+  if (hipEventRecord(m->events[m->n], stream) == hipSuccess) ++m->n;
+}
+}  // namespace msa
+
 static_assert(sizeof(msa_problem) == 64 && offsetof(msa_problem, index_dtype) == 52 &&
                   offsetof(msa_problem, kv_dtype) == 56 && offsetof(msa_problem, chunk_rows) == 60,
               "msa_problem layout is part of the ABI");
@@ -444,6 +463,28 @@ msa_status msa_forward_v(const msa_problem* p, const msa_varlen* vl, const void*
   if (forward_pass_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
   return hip_status(forward_pass(D, q, k, v, index_q, index_k, out, block_idx, lse, static_cast<char*>(workspace),
                                  stream));
+}
+
+msa_status msa_forward_marked(const msa_problem* p, const msa_varlen* vl, const void* q, const void* k, const void* v,
+                              const void* index_q, const void* index_k, void* out, int32_t* block_idx, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                              int max_events, const char** names, int* n_events) {
+  if (!events || max_events < 1 || !n_events) return MSA_ERR_INVALID_ARGUMENT;
+  *n_events = 0;
+  {
+    // validate first, so that a rejected call records nothing
+    Dims D;
+    const msa_status st = derive(p, &D, false);
+    if (st != MSA_OK) return st;
+  }
+  if (hipEventRecord(events[0], stream) != hipSuccess) return MSA_ERR_HIP;
+  MarkLog log{events, names, max_events, 1};
+  g_marks = &log;
+  const msa_status st = msa_forward_v(p, vl, q, k, v, index_q, index_k, out, block_idx, lse, workspace,
+                                      workspace_bytes, stream);
+  g_marks = nullptr;
+  *n_events = log.n;
+  return st;
 }
 
 msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, const void* index_q, const void* index_k,

@@ -292,6 +292,7 @@ hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims
   auto go = [&](auto per_c, auto vl) {
     hipLaunchKernelGGL((k_block_topk<decltype(per_c)::value, decltype(vl)::value>), grid, block, 0, stream, pooled,
                        block_idx, D, n);
+    mark("k_block_topk", stream);
   };
   auto pick = [&](auto vl) {
     if (per <= 4) go(std::integral_constant<int, 4>{}, vl);

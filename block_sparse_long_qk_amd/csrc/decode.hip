@@ -458,6 +458,7 @@ hipError_t launch_index_small(const void* index_q, const void* index_k, float* p
   auto go = [&](auto didx, auto vl, auto eb) {
     hipLaunchKernelGGL((k_index_small<decltype(didx)::value, decltype(vl)::value, decltype(eb)::value>), grid,
                        dim3(256), 0, stream, iq, ik, pooled, D, per);
+    mark("k_index_small", stream);
   };
   using I128 = std::integral_constant<int, 128>;
   using I64 = std::integral_constant<int, 64>;
@@ -483,6 +484,7 @@ hipError_t launch_attn_rows(const uint16_t* q, const void* k, const void* v, con
   auto go = [&](auto gm, auto vlc, auto kv8) {
     hipLaunchKernelGGL((k_attn_rows<decltype(gm)::value, decltype(vlc)::value, decltype(kv8)::value>), grid,
                        dim3(256), 0, stream, q, k, v, block_idx, part, D);
+    mark("k_attn_rows", stream);
   };
   auto by_kv = [&](auto gm, auto vlc) {
     if (D.kv_eb == 1) go(gm, vlc, std::true_type{}); else go(gm, vlc, std::false_type{});
@@ -496,6 +498,7 @@ hipError_t launch_attn_rows(const uint16_t* q, const void* k, const void* v, con
     hipLaunchKernelGGL(k_merge_rows<true>, dim3((unsigned)rows), dim3(256), 0, stream, part, out, lse, D);
   else
     hipLaunchKernelGGL(k_merge_rows<false>, dim3((unsigned)rows), dim3(256), 0, stream, part, out, lse, D);
+  mark("k_merge_rows", stream);
   return hipGetLastError();
 }
 

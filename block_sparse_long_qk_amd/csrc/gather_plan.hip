@@ -279,14 +279,21 @@ hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const 
   const size_t lds = sizeof(int32_t) * D.n_blk;
   dim3 cgrid(n_ch, D.B * D.h_kv);
   hipLaunchKernelGGL(k_plan_hist, cgrid, dim3(256), lds, stream, block_idx, ws.hist, D, n_ch);
+  mark("k_plan_hist", stream);
   hipLaunchKernelGGL(k_plan_colscan, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.hist, ws.cnt, D, n_ch);
+  mark("k_plan_colscan", stream);
   hipLaunchKernelGGL(k_scan_reduce, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, nbgt, D.pt);
+  mark("k_scan_reduce", stream);
   hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(256), 0, stream, ws.bsum, nb, ws.off, ws.tile_off, nbgt);
+  mark("k_scan_blocks", stream);
   hipLaunchKernelGGL(k_scan_apply, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, ws.off, ws.tile_off, nbgt, D.pt);
+  mark("k_scan_apply", stream);
   hipLaunchKernelGGL(k_plan_fill, cgrid, dim3(256), lds, stream, block_idx, ws.hist, ws.tile_off, ws.list,
                      ws.part_lse, D, n_ch);
+  mark("k_plan_fill", stream);
   hipLaunchKernelGGL(k_plan_tiles, dim3(grid_for(nbgt, 256)), dim3(256), 0, stream, ws.cnt, ws.tile_off, ws.list,
                      nbgt, D.pt);
+  mark("k_plan_tiles", stream);
   return hipGetLastError();
 }
 
@@ -314,6 +321,7 @@ hipError_t launch_copy_runs(const void* src, int64_t src_pitch, void* dst, int64
   hipLaunchKernelGGL(k_copy_runs, dim3((unsigned)(n_seg * parts)), dim3(256), 0, stream,
                      static_cast<const uint32_t*>(src), src_pitch, static_cast<uint32_t*>(dst), dst_pitch, words,
                      parts);
+  mark("k_copy_runs", stream);
   return hipGetLastError();
 }
 
@@ -321,6 +329,7 @@ hipError_t launch_plan_sort(const AttnWs& ws, const Dims& D, hipStream_t stream)
   const int64_t nbgt = plan_bins(D);
   hipLaunchKernelGGL(k_plan_sort, dim3(grid_for(nbgt, 1)), dim3(256), 0, stream, ws.cnt, ws.tile_off, ws.list, nbgt,
                      D.pt);
+  mark("k_plan_sort", stream);
   return hipGetLastError();
 }
 

@@ -451,6 +451,7 @@ static void launch_index_kernel(const Dims& D, dim3 grid, int per, const void* i
   auto go = [&](auto didx, auto vl, auto eb) {
     hipLaunchKernelGGL((k_index_scores<decltype(didx)::value, KK, decltype(vl)::value, decltype(eb)::value>), grid,
                        dim3(256), 0, stream, iq, ik, pooled, block_idx, D, per);
+    mark(KK > 0 ? "k_index_scores(top-k fused)" : "k_index_scores", stream);
   };
   using I128 = std::integral_constant<int, 128>;
   using I64 = std::integral_constant<int, 64>;

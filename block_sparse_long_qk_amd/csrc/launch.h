@@ -7,6 +7,11 @@
 
 namespace msa {
 
+// Timing marks (msa_forward_marked): records an event on `stream` after a
+// kernel launch, named `name`, when the calling thread is inside a marked
+// call; otherwise does nothing.
+void mark(const char* name, hipStream_t stream);
+
 // Index scores + block max-pool: pooled[B][h_kv][n_q][n_blk] (fp32).
 // index_q / index_k elements are bf16 or E4M3 bytes (Dims::idx_eb).
 hipError_t launch_index_scores(const void* index_q, const void* index_k, float* pooled, const Dims& D,

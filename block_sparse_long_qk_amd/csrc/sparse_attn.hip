@@ -454,8 +454,10 @@ hipError_t launch_sparse_attn(const uint16_t* q, const void* k, const void* v, c
     constexpr bool VL = decltype(vl)::value, K8 = decltype(kv8)::value;
     hipLaunchKernelGGL((k_attn_tiles<false, VL, K8>), dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws,
                        D);
+    mark("k_attn_tiles", stream);
     hipLaunchKernelGGL((k_attn_local_merge<VL, K8>), dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws,
                        out, lse, D);
+    mark("k_attn_local_merge", stream);
   };
   using T = std::true_type;
   using F = std::false_type;

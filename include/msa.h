@@ -351,6 +351,22 @@ msa_status msa_forward_noalloc(const msa_problem* p, const void* q, const void* 
                                const void* index_q, const void* index_k, void* out, int32_t* block_idx, float* lse,
                                hipStream_t stream);
 
+/*
+ * msa_forward_v with timing marks, for benchmarks: the per-kernel times of one
+ * forward pass, taken on the launch stream.  events[0] is recorded on `stream`
+ * before the call's first kernel, events[i] right after its i-th kernel
+ * launch, and (when names is non-null) names[i-1] is that kernel's name, a
+ * static string.  events holds max_events events the caller created
+ * (hipEventCreate, timing enabled); launches past max_events - 1 are not
+ * marked.  *n_events receives the number of events recorded (0 when the
+ * problem is rejected).  Results and errors otherwise as msa_forward_v.  The
+ * marks add one event record per launch and change nothing else.
+ */
+msa_status msa_forward_marked(const msa_problem* p, const msa_varlen* vl, const void* q, const void* k, const void* v,
+                              const void* index_q, const void* index_k, void* out, int32_t* block_idx, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                              int max_events, const char** names, int* n_events);
+
 /* Static description of a status code. */
 const char* msa_status_string(msa_status s);
 
