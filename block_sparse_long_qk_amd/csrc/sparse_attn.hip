@@ -199,7 +199,9 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, fl
     if (half == 0) part_lse[pblk * G + hh] = lse;
     uint16_t* dst = part_o + pblk * G * kHeadDim + hh * 8;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(dst + (8 * half + u) * G * 8) = w[u];
+    for (int u = 0; u < 8; ++u)  // read once, by the merge: streamed past the caches
+      __builtin_nontemporal_store(u32x4{w[u].x, w[u].y, w[u].z, w[u].w},
+                                  reinterpret_cast<u32x4*>(dst + (8 * half + u) * G * 8));
   }
 }
 
@@ -352,7 +354,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       ls = s0 < D.k ? lse_p[(int64_t)sl * D.G] : NEG_INF;
       const uint16_t* src = o_p + (int64_t)sl * D.G * kHeadDim;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const uint4*>(src + u * D.G * 8);
+      for (int u = 0; u < 8; ++u) {  // read once: streamed past the caches
+        const u32x4 y = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + u * D.G * 8));
+        x[u] = make_uint4(y.x, y.y, y.z, y.w);
+      }
     };
     float lv[16];
 #pragma unroll
