@@ -37,15 +37,15 @@ MAX_MARKS = 64                 # events per marked step
 # sha256 (first 16 hex digits) of the sources the kernel was built from when
 # they were taken.  A kernel whose sources have changed since reports null.
 COUNTER_TRAFFIC = {
-    # kernel name: (bytes per launch, {source file: sha16})
+    # kernel name: (bytes per launch, {source file: sha16}); profiles/prefill_128k_decode_256k_counters.md
+    "k_index_scores(top-k fused)": (2771779008, {"index_scores.hip": "d6c53c22822df47d"}),
+    "k_attn_tiles": (66243421336, {"sparse_attn.hip": "d1e3aac4d416fd6f", "attn_tiles.h": "a115cc27501125f5"}),
+    "k_attn_local_merge": (40917432688, {"sparse_attn.hip": "d1e3aac4d416fd6f", "attn_tiles.h": "a115cc27501125f5"}),
+    "k_block_topk": (2280000000, {"block_topk.hip": "aa3bc1eca70e83e0"}),
+    "k_index_small": (4354492196, {"decode.hip": "6cb61b92818c32a7"}),
+    "k_attn_rows": (575072296, {"decode.hip": "6cb61b92818c32a7"}),
 }
-KERNEL_SOURCES = {
-    "k_index_scores(top-k fused)": ["index_scores.hip"],
-    "k_index_scores": ["index_scores.hip"],
-    "k_block_topk": ["block_topk.hip"],
-    "k_attn_tiles": ["sparse_attn.hip", "attn_tiles.h"],
-    "k_attn_local_merge": ["sparse_attn.hip", "attn_tiles.h"],
-}
+COUNTER_WORKLOAD = {"k_index_small": "decode_256k", "k_attn_rows": "decode_256k"}  # the others: prefill_128k
 
 
 def source_sha16(name):
@@ -53,10 +53,11 @@ def source_sha16(name):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def counter_traffic(kernel):
-    """Counter bytes per launch recorded for this kernel's current sources, else None."""
+def counter_traffic(kernel, workload):
+    """Counter bytes per launch recorded for this kernel on this workload with
+    its current sources, else None."""
     rec = COUNTER_TRAFFIC.get(kernel)
-    if rec is None:
+    if rec is None or COUNTER_WORKLOAD.get(kernel, "prefill_128k") != workload:
         return None
     nbytes, shas = rec
     if any(source_sha16(f) != s for f, s in shas.items()):
@@ -108,6 +109,11 @@ def kernel_work(name, w, wk):
     edge_part = 2.0 * G * w.head_dim + 4.0 * G
     if name.startswith("k_index_scores"):
         return "mfma", wk["f_idx"], "flop", None
+    if name == "k_index_small":   # decode: a stream over every index key
+        return "hbm", (1.0 if w.index_dtype == "fp8" else 2.0) * w.batch * w.n_kv * w.index_dim, "byte", None
+    if name == "k_attn_rows":     # decode: the selected tokens' K and V
+        ekv = 1.0 if w.kv_dtype == "fp8" else 2.0
+        return "hbm", ekv * 2 * w.head_dim * w.h_kv * w.batch * float(wk["t_size"].sum()), "byte", None
     if name == "k_block_topk":
         return "hbm", wk["topk_bytes"], "byte", None
     if name == "k_attn_tiles":
@@ -201,6 +207,10 @@ def kernel_table(w, kernels, ms_step):
         if design_bytes is not None and d["launches_per_step"] == 1:
             e["design_gbs"] = round(design_bytes / (ms * 1e-3) / 1e9, 1)
             e["design_frac_hbm"] = round(design_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        traffic = counter_traffic(name, w.name)
+        if traffic is not None and d["launches_per_step"] == 1:
+            e["counter_bytes"] = traffic
+            e["counter_frac_hbm"] = round(traffic / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         out[name] = e
     return out
 
@@ -217,7 +227,7 @@ def roofline_of(w, kernels):
     else:
         ach, peak, u = work / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     return {"bound": bound, "kernel": name, "achieved": round(ach, 2), "peak": peak, "unit": u,
-            "frac": round(ach / peak, 4), "traffic": counter_traffic(name), "avg_ms": round(ms, 4)}
+            "frac": round(ach / peak, 4), "traffic": counter_traffic(name, w.name), "avg_ms": round(ms, 4)}
 
 
 def gpu_leg(w, steps, warmup, stream, paged=False, kl=False, stages=True, check=False):
@@ -491,15 +501,18 @@ def line_for(w, g):
     kern = g["kernels"]
     t_attn = sum(d["avg_ms"] * d["launches_per_step"] for n, d in kern.items()
                  if n.startswith("k_attn") or n.startswith("k_plan") or n.startswith("k_scan"))
-    t_idx = sum(d["avg_ms"] * d["launches_per_step"] for n, d in kern.items() if n.startswith("k_index_scores"))
+    t_idx = sum(d["avg_ms"] * d["launches_per_step"] for n, d in kern.items() if n.startswith("k_index_"))
+    t_attn = max(t_attn, sum(d["avg_ms"] * d["launches_per_step"] for n, d in kern.items()
+                             if n in ("k_attn_rows", "k_merge_rows")))
+    frac = lambda f, t: round(f / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) if t > 0 else None
     t_topk = sum(d["avg_ms"] * d["launches_per_step"] for n, d in kern.items() if n == "k_block_topk")
     out = {"workload": w.name, "tokens_per_s": round(w.batch * w.n_q / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
            "step_ms": stats(g["per_step"]),
            "combined_mfma_frac": round((wk["f_idx"] + wk["f_attn"]) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
            "scoring_ms": round(t_idx, 4),
-           "scoring_frac_mfma": round(wk["f_idx"] / (t_idx * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "scoring_frac_mfma": frac(wk["f_idx"], t_idx),
            "attention_ms": round(t_attn, 4),
-           "attention_frac_mfma": round(wk["f_attn"] / (t_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "attention_frac_mfma": frac(wk["f_attn"], t_attn),
            "kernels": kernel_table(w, kern, ms)}
     if t_topk > 0:
         out["topk_ms"] = round(t_topk, 4)
