@@ -121,6 +121,7 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws, bool with_o = true)
   const int64_t pslots = (int64_t)D.B * D.h_kv * D.n_q * (D.k + 1);  // + the local slot
   char* part_lse = take(sizeof(float) * pslots * D.G);
   char* part_o = with_o ? take(sizeof(uint16_t) * pslots * D.G * msa::kHeadDim) : nullptr;
+  char* ctr = take(sizeof(int32_t) * msa::kWorkCounters);
   if (ws) {
     ws->hist = reinterpret_cast<int32_t*>(hist);
     ws->cnt = reinterpret_cast<int32_t*>(cnt);
@@ -130,6 +131,7 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws, bool with_o = true)
     ws->list = reinterpret_cast<int2*>(list);
     ws->part_lse = reinterpret_cast<float*>(part_lse);
     ws->part_o = reinterpret_cast<uint16_t*>(part_o);
+    ws->ctr = reinterpret_cast<int32_t*>(ctr);
     ws->max_tiles = max_tiles;
     ws->n_bins = nbgt;
     ws->n_groups = (int32_t)msa::plan_groups(D);

@@ -45,23 +45,24 @@ __device__ __forceinline__ void fetch_q_rows(unsigned char* qw, const uint16_t* 
 }
 
 // Stage one 128-key block of K (row-major, padded) and V (transposed) into LDS
-// with the workgroup's kThreads threads.  Keys at or past n_valid (n_valid >= 1)
+// with the workgroup's NT threads.  Keys at or past n_valid (n_valid >= 1)
 // repeat key n_valid - 1: finite data that the causal mask drops, so the block
 // needs no zero fill.  All loads are issued before the first LDS write.
+template <int NT = kThreads>
 __device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint16_t* __restrict__ kb,
                                          const uint16_t* __restrict__ vb, int n_valid) {
-  constexpr int KPER = 2048 / kThreads, VPER = 512 / kThreads;  // 16-byte K chunks, 4-key V units
+  constexpr int KPER = 2048 / NT, VPER = 512 / NT;  // 16-byte K chunks, 4-key V units
   const int tid = threadIdx.x;
   uint4 kr[KPER], vr[4 * VPER];
 #pragma unroll
   for (int u = 0; u < KPER; ++u) {
-    const int c = tid + kThreads * u;
+    const int c = tid + NT * u;
     const int key = min(c >> 4, n_valid - 1), oc = c & 15;
     kr[u] = *reinterpret_cast<const uint4*>(kb + key * kHeadDim + oc * 8);
   }
 #pragma unroll
   for (int u = 0; u < VPER; ++u) {
-    const int c = tid + kThreads * u;
+    const int c = tid + NT * u;
     const int kq = c >> 4, od = c & 15;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -69,12 +70,12 @@ __device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint1
   }
 #pragma unroll
   for (int u = 0; u < KPER; ++u) {
-    const int c = tid + kThreads * u;
+    const int c = tid + NT * u;
     *reinterpret_cast<uint4*>(Ks + (c >> 4) * KP + (c & 15) * 8) = kr[u];
   }
 #pragma unroll
   for (int u = 0; u < VPER; ++u) {  // written transposed: Vt[d][key]
-    const int c = tid + kThreads * u;
+    const int c = tid + NT * u;
     const int kq = c >> 4, od = c & 15;
     const uint32_t* w[4] = {reinterpret_cast<const uint32_t*>(&vr[4 * u + 0]), reinterpret_cast<const uint32_t*>(&vr[4 * u + 1]),
                             reinterpret_cast<const uint32_t*>(&vr[4 * u + 2]), reinterpret_cast<const uint32_t*>(&vr[4 * u + 3])};
@@ -92,21 +93,22 @@ __device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, const uint1
 // same LDS content, each element widened to bf16 between the load and the
 // store.  K: 16-byte pieces (16 dims), two per thread; V: 4 keys x 8 dims per
 // thread, written transposed as above.
+template <int NT = kThreads>
 __device__ __forceinline__ void stage_kv8(uint16_t* Ks, uint16_t* Vt, const unsigned char* __restrict__ kb,
                                           const unsigned char* __restrict__ vb, int n_valid) {
-  constexpr int KPER = 1024 / kThreads, VPER = 512 / kThreads;
+  constexpr int KPER = 1024 / NT, VPER = 512 / NT;
   const int tid = threadIdx.x;
   uint4 kr[KPER];
   uint2 vr[4 * VPER];
 #pragma unroll
   for (int u = 0; u < KPER; ++u) {
-    const int c = tid + kThreads * u;
+    const int c = tid + NT * u;
     const int key = min(c >> 3, n_valid - 1), oc = c & 7;
     kr[u] = *reinterpret_cast<const uint4*>(kb + key * kHeadDim + oc * 16);
   }
 #pragma unroll
   for (int u = 0; u < VPER; ++u) {
-    const int c = tid + kThreads * u;
+    const int c = tid + NT * u;
     const int kq = c >> 4, od = c & 15;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -114,14 +116,14 @@ __device__ __forceinline__ void stage_kv8(uint16_t* Ks, uint16_t* Vt, const unsi
   }
 #pragma unroll
   for (int u = 0; u < KPER; ++u) {
-    const int c = tid + kThreads * u;
+    const int c = tid + NT * u;
     uint16_t* dst = Ks + (c >> 3) * KP + (c & 7) * 16;
     *reinterpret_cast<u32x4*>(dst) = e4m3x8_to_bf16(make_uint2(kr[u].x, kr[u].y));
     *reinterpret_cast<u32x4*>(dst + 8) = e4m3x8_to_bf16(make_uint2(kr[u].z, kr[u].w));
   }
 #pragma unroll
   for (int u = 0; u < VPER; ++u) {  // written transposed: Vt[d][key]
-    const int c = tid + kThreads * u;
+    const int c = tid + NT * u;
     const int kq = c >> 4, od = c & 15;
     const u32x4 w0 = e4m3x8_to_bf16(vr[4 * u + 0]), w1 = e4m3x8_to_bf16(vr[4 * u + 1]);
     const u32x4 w2 = e4m3x8_to_bf16(vr[4 * u + 2]), w3 = e4m3x8_to_bf16(vr[4 * u + 3]);
@@ -136,14 +138,14 @@ __device__ __forceinline__ void stage_kv8(uint16_t* Ks, uint16_t* Vt, const unsi
 }
 
 // K/V block (keys t Bk .. of kv element offset kv0) staged from bf16 or FP8 caches.
-template <bool KV8>
+template <bool KV8, int NT = kThreads>
 __device__ __forceinline__ void stage_kv_any(uint16_t* Ks, uint16_t* Vt, const void* k, const void* v, int64_t kv0,
                                              int n_valid) {
   if constexpr (KV8)
-    stage_kv8(Ks, Vt, static_cast<const unsigned char*>(k) + kv0, static_cast<const unsigned char*>(v) + kv0,
-              n_valid);
+    stage_kv8<NT>(Ks, Vt, static_cast<const unsigned char*>(k) + kv0, static_cast<const unsigned char*>(v) + kv0,
+                  n_valid);
   else
-    stage_kv(Ks, Vt, static_cast<const uint16_t*>(k) + kv0, static_cast<const uint16_t*>(v) + kv0, n_valid);
+    stage_kv<NT>(Ks, Vt, static_cast<const uint16_t*>(k) + kv0, static_cast<const uint16_t*>(v) + kv0, n_valid);
 }
 
 // S^T = K Q^T for one wave: the 128 keys of the staged block (4 row tiles of

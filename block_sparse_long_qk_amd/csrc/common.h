@@ -17,6 +17,7 @@ constexpr int kMaxPlanBlocks = 16384;  // LDS histogram bins of the gather plan 
 constexpr int kPoolStage = 8;          // pooled scores a lane stages before one 32-byte store
 constexpr int kRowsMaxQ = 4;           // query rows per sequence up to which attention runs query-outer
 constexpr int kRowsPart = 16 * kHeadDim + 16;  // floats per query-outer partial: o[16][d], lse[16]
+constexpr int kWorkCounters = 16;      // per-XCD run counters: 8 for the tiles, 8 for the local/merge pass
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -130,6 +131,7 @@ struct AttnWs {
   int2* list;          // [max_tiles * pt] {row-slot id i * k + s (-1 = empty), bin of the tile}, tile-major
   float* part_lse;     // [B*h_kv*n_q*(k+1)][G]     base-2 log-sum-exp of each non-local partial (-inf: none)
   uint16_t* part_o;    // [B*h_kv*n_q*(k+1)][16][G][8] normalised partials, bf16, chunk-major per block
+  int32_t* ctr;        // [kWorkCounters] work counters of the forward attention kernels (zeroed by the plan)
   int64_t max_tiles;
   int64_t n_bins;      // B * h_kv * query groups * n_blk
   int32_t n_groups;    // query groups per (b, g)

@@ -114,10 +114,13 @@ __global__ __launch_bounds__(256) void k_scan_reduce(const int32_t* __restrict__
 }
 
 // One workgroup: exclusive scan of the (edges, tiles) block sums in place;
-// writes the grand totals to off[n] and tile_off[n].
+// writes the grand totals to off[n] and tile_off[n], and clears the work
+// counters of the attention kernels that follow the plan.
 __global__ __launch_bounds__(256) void k_scan_blocks(int32_t* __restrict__ bsum, int32_t nb, int32_t* __restrict__ off,
-                                                     int32_t* __restrict__ tile_off, int64_t n) {
+                                                     int32_t* __restrict__ tile_off, int64_t n,
+                                                     int32_t* __restrict__ ctr) {
   __shared__ int32_t sa[256], sb[256];
+  if (threadIdx.x < kWorkCounters) ctr[threadIdx.x] = 0;
   const int per = (nb + 255) / 256;
   const int a0 = threadIdx.x * per, a1 = min(nb, a0 + per);
   int32_t e = 0, t = 0;
@@ -284,7 +287,8 @@ hipError_t launch_gather_plan(const int32_t* block_idx, const AttnWs& ws, const 
   mark("k_plan_colscan", stream);
   hipLaunchKernelGGL(k_scan_reduce, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, nbgt, D.pt);
   mark("k_scan_reduce", stream);
-  hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(256), 0, stream, ws.bsum, nb, ws.off, ws.tile_off, nbgt);
+  hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(256), 0, stream, ws.bsum, nb, ws.off, ws.tile_off, nbgt,
+                     ws.ctr);
   mark("k_scan_blocks", stream);
   hipLaunchKernelGGL(k_scan_apply, dim3(nb), dim3(256), 0, stream, ws.cnt, ws.bsum, ws.off, ws.tile_off, nbgt, D.pt);
   mark("k_scan_apply", stream);

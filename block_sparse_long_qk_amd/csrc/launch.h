@@ -44,6 +44,13 @@ int64_t plan_bins(const Dims& D);         // (b, g, query group, block) bins
 // Gather plan + gathered non-local tiles + local tiles with the merge.
 hipError_t launch_sparse_attn(const uint16_t* q, const void* k, const void* v, const int32_t* block_idx,
                               uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream);
+// The same in two parts, for callers that put the plan on another stream: the
+// forward's view of D (its tiles hold 128 rows, so pt is that of 128 rows; a
+// workspace sized for D fits it), and the two attention kernels over a built
+// plan of that view.
+Dims fwd_attn_dims(const Dims& D);
+hipError_t launch_attn_kernels(const uint16_t* q, const void* k, const void* v, uint16_t* out, float* lse,
+                               const AttnWs& ws, const Dims& F, hipStream_t stream);
 
 // KL alignment of the index branch to the main branch's group-averaged
 // attention over the selected tokens (needs the forward's lse); kl_part holds

@@ -9,16 +9,16 @@
 //
 // Stage A, gather plan (gather_plan.hip): for every (sequence, group, block)
 //   the list of query rows that selected it as a non-local block, cut into
-//   tiles of `pt` positions (pt * G <= 256 rows, pt <= 128).
-// Stage B, tiles (KV-outer): persistent workgroups of 8 waves walk runs of
-//   tiles; the 128-key K block and V block sit in LDS while the run stays on
-//   one (b, g, block); each wave owns 32 of the tile's 256 rows.  A wave's
-//   query rows arrive in its own LDS region by direct global-to-LDS loads
-//   issued one tile ahead, and S^T = K Q^T and O^T = V^T P^T run on 32x32x16
-//   bf16 MFMA.  Non-local tiles need no mask (the block lies wholly before the
-//   query); local tiles (pt consecutive positions sharing their local block)
-//   apply the causal mask.  Each (row, slot) writes a normalised bf16 partial
-//   and its base-2 log-sum-exp.
+//   tiles of `pt` positions (pt * G <= 128 rows for the forward, pt <= 128).
+// Stage B, tiles (KV-outer): persistent workgroups of 4 waves claim runs of
+//   tiles dynamically (per-XCD counters); the 128-key K block and V block sit
+//   in LDS while consecutive tiles stay on one (b, g, block); each wave owns
+//   32 of the tile's 128 rows and holds their query vectors in VGPRs, loaded
+//   one tile ahead.  S^T = K Q^T and O^T = V^T P^T run on 32x32x16 bf16 MFMA.
+//   Non-local tiles need no mask (the block lies wholly before the query);
+//   local tiles (pt consecutive positions sharing their local block) apply
+//   the causal mask.  Each (row, slot) writes a normalised bf16 partial and
+//   its base-2 log-sum-exp.
 // Stage C, merge: LSE weighting of each row's partials into the bf16 output
 //   and the natural-log lse.
 //
@@ -197,149 +197,492 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, fl
                                                int G, int half) {
   if (valid) {
     if (half == 0) part_lse[pblk * G + hh] = lse;
-    uint16_t* dst = part_o + pblk * G * kHeadDim + hh * 8;
+    uint64_t a = reinterpret_cast<uint64_t>(part_o + pblk * G * kHeadDim + (8 * half * G + hh) * 8);
+    // the eight addresses are formed here, one add each, rather than kept live
+    // in registers since the partial was packed
+    asm volatile("" : "+v"(a));
+    const int64_t step = (int64_t)G * 16;  // bytes between consecutive chunks of one head
+    typedef __attribute__((address_space(1))) u32x4* gvec;
 #pragma unroll
     for (int u = 0; u < 8; ++u)  // read once, by the merge: streamed past the caches
-      __builtin_nontemporal_store(u32x4{w[u].x, w[u].y, w[u].z, w[u].w},
-                                  reinterpret_cast<u32x4*>(dst + (8 * half + u) * G * 8));
+      __builtin_nontemporal_store(u32x4{w[u].x, w[u].y, w[u].z, w[u].w}, (gvec)(a + u * step));
   }
 }
 
-// Persistent and XCD-aware tile kernel, launched once over the gathered
-// non-local tiles and once (LOCAL) over the masked local tiles.  One
-// workgroup of kWaves waves per CU (2 waves per SIMD); workgroup w runs on XCD
-// w % kXcds (the hardware deals workgroups round-robin over the XCDs); XCD x
-// owns the contiguous x-th slice of the tile list, and its workgroups walk
-// that slice in runs of kRun consecutive tiles (same (b, g, block) as a rule),
-// run r going to workgroup r % (grid / kXcds).  So the K/V block in LDS is
-// reused across a run, and the query rows gathered at any time come from at
-// most kXcds query groups.
-//
-// Per tile and wave: scores from the query rows in LDS; decode of the next
-// tile's list entries; stores of the previous tile's partials; the next
-// tile's query rows fetched into the (now free) LDS region; softmax and P.V;
-// the partial packed for storing one tile later.  One counter (vmcnt) tracks
-// vector loads and stores alike, so a wait for loads waits for every store
-// issued before them: issued where they are, the stores and the next rows
-// have a whole softmax and P.V to land before the next tile waits for them.
-template <bool LOCAL, bool VL, bool KV8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_tiles(
-    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, AttnWs ws, Dims D) {
-  __shared__ __align__(16) uint16_t Ks[kBk * KP];
-  __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
-  __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];  // per wave: its query rows
-  int total;
-  if constexpr (LOCAL) {
-    total = D.B * D.h_kv * local_tiles<VL>(D);
+// The forward's tile workgroups are four waves (128 query rows per tile) and
+// hold only the K/V block in LDS (65 KB); each wave keeps its 32 query rows
+// in VGPRs.  Two such workgroups fill a CU, and one fits beside a scoring
+// workgroup, so the attention of one query pass can share CUs with the
+// scoring of the next.
+constexpr int kFWaves = 4;
+constexpr int kFThreads = 64 * kFWaves;
+constexpr int kFRows = 32 * kFWaves;
+constexpr int kFRun = 16;  // tiles per claimed run
+
+// Lane (column, half) of a wave's MFMA operand for query row `row`: dims
+// 16 ks + 8 half .. + 7 of k-step ks, the order qk_block reads from LDS.
+__device__ __forceinline__ void load_q(const uint16_t* row, int half, uint4 (&qf)[8]) {
+  const uint16_t* p = row + 8 * half;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(p + 16 * ks);
+}
+
+// K/V staging of the forward kernels (kFThreads threads).  K rows are stored
+// unpadded and swizzled: row r at r * 256 bytes, its 16-byte chunk c in slot
+// c ^ (r % 16), so the 16 lanes that read one chunk of 16 rows hit 16
+// different bank groups.  bf16 K arrives by direct global-to-LDS loads (no
+// registers): each wave issues 8 of the block's 32 one-KB instructions, one
+// per 4 rows, the 16 lanes of a row fetching its chunks in slot order.  FP8 K
+// is widened in registers and written to the same slots.  V is written
+// transposed (Vt[d][key], pitch VP) as stage_kv writes it.  Keys at or past
+// n_valid repeat key n_valid - 1; FULL blocks (all 128 keys cached, as every
+// non-local block is) skip that clamp.  The caller waits for vmcnt(0) and then
+// for the workgroup barrier before reading the block.
+template <bool KV8, bool FULL>
+__device__ __forceinline__ void stage_kv_fwd(unsigned char* Ks, uint16_t* Vt, const void* k, const void* v,
+                                             int64_t kv0, int n_valid) {
+  if constexpr (FULL) n_valid = kBk;
+  int tid = threadIdx.x;
+  // the per-lane addresses below are formed at each staging, not hoisted out
+  // of the tile loop into registers that would stay live all along it
+  asm volatile("" : "+v"(tid));
+  const int wave = tid >> 6, lane = tid & 63;
+  constexpr int VPER = 512 / kFThreads;  // 4-key x 8-dim V units per thread
+  if constexpr (!KV8) {
+    const unsigned char* kb = static_cast<const unsigned char*>(k) + kv0 * 2;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int g = 8 * wave + u;
+      const int row = 4 * g + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 15);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kb + (int64_t)min(row, n_valid - 1) * 256 + 16 * c),
+                                       (__attribute__((address_space(3))) void*)(Ks + 1024 * g), 16, 0, 0);
+    }
+    const uint16_t* vb = static_cast<const uint16_t*>(v) + kv0;
+    uint4 vr[4 * VPER];
+#pragma unroll
+    for (int u = 0; u < VPER; ++u) {
+      const int c = tid + kFThreads * u;
+      const int kq = c >> 4, od = c & 15;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        vr[4 * u + q4] = *reinterpret_cast<const uint4*>(vb + min(kq * 4 + q4, n_valid - 1) * kHeadDim + od * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < VPER; ++u) {
+      const int c = tid + kFThreads * u;
+      const int kq = c >> 4, od = c & 15;
+      const uint32_t* w[4] = {reinterpret_cast<const uint32_t*>(&vr[4 * u + 0]), reinterpret_cast<const uint32_t*>(&vr[4 * u + 1]),
+                              reinterpret_cast<const uint32_t*>(&vr[4 * u + 2]), reinterpret_cast<const uint32_t*>(&vr[4 * u + 3])};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        const uint32_t v0 = (w[0][e >> 1] >> sh) & 0xFFFFu, v1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t v2 = (w[2][e >> 1] >> sh) & 0xFFFFu, v3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
+        *reinterpret_cast<uint2*>(Vt + (od * 8 + e) * VP + kq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+      }
+    }
   } else {
-    total = ws.tile_off[ws.n_bins];
+    constexpr int KPER = 1024 / kFThreads;  // 16-byte pieces (16 codes) per thread
+    const unsigned char* kb = static_cast<const unsigned char*>(k) + kv0;
+    const unsigned char* vb = static_cast<const unsigned char*>(v) + kv0;
+    uint4 kr[KPER];
+    uint2 vr[4 * VPER];
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+      const int c = tid + kFThreads * u;
+      kr[u] = *reinterpret_cast<const uint4*>(kb + min(c >> 3, n_valid - 1) * kHeadDim + (c & 7) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < VPER; ++u) {
+      const int c = tid + kFThreads * u;
+      const int kq = c >> 4, od = c & 15;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        vr[4 * u + q4] = *reinterpret_cast<const uint2*>(vb + min(kq * 4 + q4, n_valid - 1) * kHeadDim + od * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+      const int c = tid + kFThreads * u;
+      const int row = c >> 3, oc = c & 7;
+      unsigned char* base = Ks + row * 256;
+      *reinterpret_cast<u32x4*>(base + 16 * ((2 * oc) ^ (row & 15))) = e4m3x8_to_bf16(make_uint2(kr[u].x, kr[u].y));
+      *reinterpret_cast<u32x4*>(base + 16 * ((2 * oc + 1) ^ (row & 15))) = e4m3x8_to_bf16(make_uint2(kr[u].z, kr[u].w));
+    }
+#pragma unroll
+    for (int u = 0; u < VPER; ++u) {
+      const int c = tid + kFThreads * u;
+      const int kq = c >> 4, od = c & 15;
+      const u32x4 w0 = e4m3x8_to_bf16(vr[4 * u + 0]), w1 = e4m3x8_to_bf16(vr[4 * u + 1]);
+      const u32x4 w2 = e4m3x8_to_bf16(vr[4 * u + 2]), w3 = e4m3x8_to_bf16(vr[4 * u + 3]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        const uint32_t v0 = (w0[e >> 1] >> sh) & 0xFFFFu, v1 = (w1[e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t v2 = (w2[e >> 1] >> sh) & 0xFFFFu, v3 = (w3[e >> 1] >> sh) & 0xFFFFu;
+        *reinterpret_cast<uint2*>(Vt + (od * 8 + e) * VP + kq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+      }
+    }
   }
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = gridDim.x / kXcds;
-  const int lo = (int)((int64_t)total * xcd / kXcds), hi = (int)((int64_t)total * (xcd + 1) / kXcds);
-  const int stride = per_xcd * kRun;  // >= kRun
-  Walk w0{lo + slot * kRun, lo + slot * kRun, min(lo + slot * kRun + kRun, hi)};
-  if (w0.tile >= hi) return;  // uniform over the workgroup
+}
+
+// S^T = K Q^T against query fragments held in registers, K in the swizzled
+// layout of stage_kv_fwd: the MFMA sequence of qk_block (same k-order, same
+// accumulation), so the scores are bit-identical.
+__device__ __forceinline__ void qk_block_q(const unsigned char* Ks, const uint4 (&qf)[8], int lane, f32x16 (&s)[4]) {
+  const int col = lane & 31, half = lane >> 5;
+  const unsigned char* kbase = Ks + col * 256;  // rows 32 T + col share col's swizzle
+  const int sw = col & 15;
+  uint4 kf[2][4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) kf[0][T] = *reinterpret_cast<const uint4*>(kbase + 32 * T * 256 + 16 * (half ^ sw));
+#pragma unroll
+  for (int T = 0; T < 4; ++T) s[T] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int cb = ks & 1, nb = cb ^ 1;
+    if (ks + 1 < 8) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+        kf[nb][T] = *reinterpret_cast<const uint4*>(kbase + 32 * T * 256 + 16 * ((2 * (ks + 1) + half) ^ sw));
+    }
+#pragma unroll
+    for (int T = 0; T < 4; ++T) s[T] = mfma_32x32x16(kf[cb][T], qf[ks], s[T]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int ks = 0; ks < 7; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+// softmax_pv<false> with the partial packed as it is produced: P is packed
+// to bf16 once, then O^T is formed one half of the head dim at a time (32
+// accumulator registers instead of 64) and each half is normalised into its
+// four packed chunks of w (the layout of pack_partial).  Every accumulator
+// sums the same MFMAs in the same order as softmax_pv, so m2, l and the
+// packed partial are bit-identical to softmax_pv followed by pack_partial.
+__device__ __forceinline__ void softmax_pv_packed(const uint16_t* Vt, f32x16 (&s)[4], int lane, float c,
+                                                  uint4 (&w)[8], float& m2, float& l) {
+  const float NEG_INF = -__builtin_huge_valf();
+  const int col = lane & 31, half = lane >> 5;
+  float ext;
+  if (c >= 0.f) {
+    ext = NEG_INF;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ext = fmaxf(ext, s[T][e]);
+    }
+    ext = fmaxf(ext, wave_xor32(ext));
+  } else {
+    ext = -NEG_INF;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ext = fminf(ext, s[T][e]);
+    }
+    ext = fminf(ext, wave_xor32(ext));
+  }
+  const float mref = ext * c;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[T][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[T][e], c, -mref));
+  }
+  m2 = mref;
+  float sum = 0.f;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sum += s[T][e];
+  }
+  sum += wave_xor32(sum);
+  l = sum;
+  const float inv = 1.f / sum;
+  uint4 pb[8];  // k-step j = 2T + u: keys 32T + 16u .. +15
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int T = j >> 1, u = j & 1;
+    pb[j] = make_uint4(pack_bf16x2(s[T][8 * u + 0], s[T][8 * u + 1]), pack_bf16x2(s[T][8 * u + 2], s[T][8 * u + 3]),
+                       pack_bf16x2(s[T][8 * u + 4], s[T][8 * u + 5]), pack_bf16x2(s[T][8 * u + 6], s[T][8 * u + 7]));
+  }
+  const uint16_t* vbase = Vt + col * VP + 4 * half;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    auto read_v2 = [&](int j, uint4 (&dst)[2]) {  // V^T rows of dims 32 (2h + d) + col at k-step j
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const uint16_t* vrow = vbase + 32 * (2 * h + d) * VP + 16 * j;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+        dst[d] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    };
+    f32x16 o[2] = {f32x16{}, f32x16{}};
+    uint4 vf[2][2];
+    read_v2(0, vf[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j + 1 < 8) read_v2(j + 1, vf[(j + 1) & 1]);
+#pragma unroll
+      for (int d = 0; d < 2; ++d) o[d] = mfma_32x32x16(vf[j & 1][d], pb[j], o[d]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      const int d = uu >> 1, e0 = (uu & 1) * 8;
+      w[4 * h + uu] = make_uint4(pack_bf16x2(o[d][e0 + 0] * inv, o[d][e0 + 1] * inv),
+                                 pack_bf16x2(o[d][e0 + 2] * inv, o[d][e0 + 3] * inv),
+                                 pack_bf16x2(o[d][e0 + 4] * inv, o[d][e0 + 5] * inv),
+                                 pack_bf16x2(o[d][e0 + 6] * inv, o[d][e0 + 7] * inv));
+    }
+  }
+}
+
+// Dynamic runs.  The tile range [0, total) is cut into kXcds slices; slice x
+// is first drained by the workgroups of XCD x (workgroup w runs on XCD
+// w % kXcds), which claim runs of kFRun consecutive tiles from the slice's
+// counter, so consecutive tiles (one K/V block as a rule) stay on one XCD's
+// L2.  A workgroup whose slice is empty moves on to the next slices in turn.
+// Workgroups that start late, or share their CU with other work, simply
+// claim fewer runs.  Only thread 0 of a workgroup uses it.
+struct RunQueue {
+  int32_t* ctr;
+  int total, slice, left;  // left: slices not yet found empty
+  int pend;                // claimed run of `slice`, not yet resolved
+  __device__ void init(int32_t* c, int tot) {
+    ctr = c;
+    total = tot;
+    slice = blockIdx.x % kXcds;
+    left = kXcds;
+    pend = 0;
+  }
+  __device__ int2 range(int s, int run) const {
+    const int64_t lo = (int64_t)total * s / kXcds, hi = (int64_t)total * (s + 1) / kXcds;
+    const int64_t st = lo + (int64_t)run * kFRun;
+    if (st >= hi) return make_int2(-1, -1);
+    return make_int2((int)st, (int)min<int64_t>(st + kFRun, hi));
+  }
+  __device__ int2 claim() {  // waits for each counter it reads
+    while (left > 0) {
+      const int2 r = range(slice, atomicAdd(&ctr[slice], 1));
+      if (r.x >= 0) return r;
+      slice = (slice + 1) % kXcds;
+      --left;
+    }
+    return make_int2(-1, -1);
+  }
+  __device__ void prefetch() {  // a claim whose result is looked at later
+    if (left > 0) pend = atomicAdd(&ctr[slice], 1);
+  }
+  __device__ int2 resolve() {
+    if (left <= 0) return make_int2(-1, -1);
+    const int2 r = range(slice, pend);
+    if (r.x >= 0) return r;
+    slice = (slice + 1) % kXcds;
+    --left;
+    return claim();
+  }
+};
+
+// a + b, never fused with the product that formed a or b.  The tile step is
+// inlined twice (the two query register sets) and a tile runs through either
+// copy, so its base-2 lse m2 + log2(l) must not be contracted into an fma in
+// one copy and not in the other.
+__device__ __forceinline__ float add_exact(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+
+__device__ __forceinline__ int2 uniform2(int2 x) {
+  return make_int2(__builtin_amdgcn_readfirstlane(x.x), __builtin_amdgcn_readfirstlane(x.y));
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete,
+// then s_barrier.  lds_barrier() also fences global memory, which waits
+// for every outstanding global load and store (the next tile's query rows,
+// the partials just stored).  Direct global-to-LDS loads are waited for
+// separately (vmcnt) before such a barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Runs are handed from thread 0 to the workgroup through three LDS slots: at
+// the barrier that starts run r every wave reads run r + 1 from slot
+// (r + 1) % 3; thread 0 writes run r + 2 into slot (r + 2) % 3 during run r,
+// before the barrier that starts run r + 1.  That slot was last read after
+// the barrier that started run r - 1, which every wave has left behind by
+// the barrier that started run r, so no wave can still be reading it.
+
+// Non-local tiles (KV-outer, persistent, dynamic runs).  Per tile and wave:
+// scores from the query rows in registers; decode of the next tile's list
+// entries; stores of the previous tile's partials; the next tile's query rows
+// loaded into the other register set; the list entries of the tile after it;
+// softmax and P.V, packed into the partial that is stored one tile later.
+// The run after next is claimed at the start of each run.
+template <bool VL, bool KV8>
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_tiles(
+    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, AttnWs ws, Dims D) {
+  __shared__ __align__(16) unsigned char Ks[kBk * 256];
+  __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
+  __shared__ int2 runs[3];
+  const bool leader = threadIdx.x == 0;
+  RunQueue rq;
+  if (leader) {
+    rq.init(ws.ctr, ws.tile_off[ws.n_bins]);
+    const int2 a = rq.claim();
+    runs[0] = a;
+    runs[1] = a.x >= 0 ? rq.claim() : make_int2(-1, -1);
+  }
+  lds_barrier();
+  int2 run = uniform2(runs[0]), nrun = uniform2(runs[1]);
+  if (run.x < 0) return;  // uniform over the workgroup
+  if (leader && nrun.x >= 0) rq.prefetch();
+  int ri = 0;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
   const int r = wave * 32 + col;
   const int ps = r / D.G, hh = r % D.G;
-  unsigned char* qw = Qs[wave];
   auto q_ptr = [&](const TileRow& tr) {  // rows that do not exist read row 0 of the group
     const int g = tr.bg % D.h_kv, b = tr.bg / D.h_kv;
     const int i = tr.valid ? tr.i : 0;
     return q + (qrow_of<VL>(D, b, i) * D.h_q + g * D.G + hh) * kHeadDim;
   };
+  // The tile after t1, the successor of tile t (-1: none; -2: the first tile
+  // of a run not yet known).  A run claimed from another slice can lie
+  // anywhere in the tile range, so whether t1 still belongs to t's run is
+  // told by t's place in that run, never by comparing tile numbers across runs.
+  auto after = [&](int t, int t1) {
+    if (t1 < 0) return -1;
+    if (t + 1 < run.y) return t1 + 1 < run.y ? t1 + 1 : nrun.x;  // t1 = t + 1, same run
+    return t1 + 1 < nrun.y ? t1 + 1 : -2;                       // t1 starts the next run
+  };
 
-  TileRow cur = tile_row<LOCAL, VL>(tile_raw<LOCAL>(ws, D, w0.tile, ps), D, ws, w0.tile, ps);
-  fetch_q_rows(qw, q_ptr(cur), lane);
-  Walk w1 = walk_next(w0, stride, hi);
-  TileRaw raw1 = tile_raw<LOCAL>(ws, D, min(w1.tile, hi - 1), ps);
+  int t = run.x;
+  TileRow cur = tile_row<false, VL>(tile_raw<false>(ws, D, t, ps), D, ws, t, ps);
+  int t1 = t + 1 < run.y ? t + 1 : nrun.x;
+  TileRaw raw1 = t1 >= 0 ? tile_raw<false>(ws, D, t1, ps) : TileRaw{-1, 0};
+  uint4 qa[8], qb[8];
+  load_q(q_ptr(cur), half, qa);
   uint4 pw[8];
   int64_t ppblk = 0;
   float plse = 0.f;
   bool pvalid = false, have = false;  // have: a packed partial waits in pw (uniform)
-  // outer loop: one staged K/V block; inner loop: the tiles that use it
-  while (w0.tile < hi) {
-    {
+  int staged_bg = -1, staged_t = -1;
+  bool fresh = true;  // a barrier was passed since the staged block was last read
+
+  auto step = [&](uint4 (&qc)[8], uint4 (&qn)[8]) -> bool {
+    if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform
+      if (!fresh) lds_barrier();                    // every wave is done with the staged block
       const int sb = cur.bg / D.h_kv;
       const int64_t kv0 = kvoff_of<VL>(D, sb, cur.bg % D.h_kv, cur.t);
-      stage_kv_any<KV8>(Ks, Vt, k, v, kv0, max(1, min(kBk, nkv_of<VL>(D, sb) - cur.t * kBk)));
-      __syncthreads();
+      stage_kv_fwd<KV8, true>(Ks, Vt, k, v, kv0, kBk);  // a non-local block lies wholly before the query
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);            // this wave's direct K loads have landed
+      lds_barrier();
+      staged_bg = cur.bg;
+      staged_t = cur.t;
     }
-    const int staged_bg = cur.bg, staged_t = cur.t;
-    bool same;
-    do {
-      f32x16 s[4];
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this tile's query rows have landed in LDS
-      __builtin_amdgcn_sched_barrier(0);
-      qk_block(Ks, qw, lane, s);
-      __builtin_amdgcn_sched_barrier(0);
-      const bool more = w1.tile < hi;
-      // past the last tile: a stand-in decode of the last one (loads stay in bounds, results unused)
-      const TileRow nxt = tile_row<LOCAL, VL>(raw1, D, ws, min(w1.tile, hi - 1), ps);
-      __builtin_amdgcn_sched_barrier(0);
-      if (have) store_partials(ws.part_o, ws.part_lse, pw, plse, pvalid, ppblk, hh, D.G, half);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // LDS reads of the region are done before it is refilled
-      __builtin_amdgcn_sched_barrier(0);
-      fetch_q_rows(qw, q_ptr(nxt), lane);
-      Walk w2 = w1;
-      if (more) w2 = walk_next(w1, stride, hi);
-      const TileRaw raw2 = tile_raw<LOCAL>(ws, D, min(w2.tile, hi - 1), ps);
-      f32x16 o[4];
-      float m2, l;
-      softmax_pv<LOCAL>(Vt, s, lane, D.scale_log2, (int64_t)cur.t * kBk, off_of<VL>(D, cur.bg / D.h_kv) + cur.i, o, m2,
-                        l);
-      pack_partial(o, 1.f / l, pw);
-      ppblk = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s;
-      plse = m2 + __log2f(l);
-      pvalid = cur.valid;
-      have = true;
-      w0 = w1;
-      w1 = w2;
-      raw1 = raw2;
-      cur = nxt;
-      same = more && cur.bg == staged_bg && cur.t == staged_t;  // uniform
-    } while (same);
-    __syncthreads();  // every wave is done with the staged block
+    fresh = false;
+    // the last tile of a run: the run after next, claimed when this run
+    // started, is resolved now (its counter value has long arrived) and
+    // handed over at the barrier that starts the next run
+    const bool last = t + 1 >= run.y;  // t ends its run (uniform)
+    if (leader && last && t1 >= 0) runs[(ri + 2) % 3] = rq.resolve();
+    f32x16 s[4];
+    __builtin_amdgcn_sched_barrier(0);
+    qk_block_q(Ks, qc, lane, s);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more = t1 >= 0;  // uniform
+    TileRow nxt = cur;
+    if (more) nxt = tile_row<false, VL>(raw1, D, ws, t1, ps);
+    __builtin_amdgcn_sched_barrier(0);
+    if (have) store_partials(ws.part_o, ws.part_lse, pw, plse, pvalid, ppblk, hh, D.G, half);
+    if (more) load_q(q_ptr(nxt), half, qn);
+    int t2 = after(t, t1);
+    TileRaw raw2{-1, 0};
+    if (t2 >= 0) raw2 = tile_raw<false>(ws, D, t2, ps);
+    float m2, l;
+    softmax_pv_packed(Vt, s, lane, D.scale_log2, pw, m2, l);
+    ppblk = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s;
+    plse = add_exact(m2, __log2f(l));
+    pvalid = cur.valid;
+    have = true;
+    if (!more) return false;
+    if (last) {  // t1 starts the next run
+      lds_barrier();
+      fresh = true;
+      run = nrun;
+      nrun = uniform2(runs[(ri + 2) % 3]);
+      ++ri;
+      if (leader && nrun.x >= 0) rq.prefetch();
+      if (t2 == -2) {  // the next run holds one tile: the one after it starts the run now known
+        t2 = nrun.x;
+        if (t2 >= 0) raw2 = tile_raw<false>(ws, D, t2, ps);
+      }
+    }
+    t = t1;
+    t1 = t2;
+    raw1 = raw2;
+    cur = nxt;
+    return true;
+  };
+  while (step(qa, qb) && step(qb, qa)) {
   }
   if (have) store_partials(ws.part_o, ws.part_lse, pw, plse, pvalid, ppblk, hh, D.G, half);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the last (unused) row fetch has landed before the workgroup ends
 }
 
-// Local tiles fused with the merge.  Each workgroup walks the local tiles (pt
-// consecutive positions sharing their local block; XCD-aware runs as above).
-// Per tile and wave: the query rows arrive by direct loads into the wave's LDS
-// region, the masked local block gives the unnormalised O^T, its max and sum
-// in registers, and the row's non-local partials (lse -inf: no partial) are
-// folded in two slots at a time with a running max.  Normalised, the result is
-// written to `out` (bf16) and `lse` (natural log).
+// Local tiles fused with the merge (persistent, dynamic runs).  Per tile and
+// wave: the query rows are loaded into registers, the masked local block gives
+// the unnormalised O^T, its max and sum, and the row's non-local partials
+// (lse -inf: no partial) are folded in two slots at a time.  Normalised, the
+// result is written to `out` (bf16) and `lse` (natural log).
 template <bool VL, bool KV8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_local_merge(
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_local_merge(
     const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, AttnWs ws,
     uint16_t* __restrict__ out, float* __restrict__ lse_out, Dims D) {
-  __shared__ __align__(16) uint16_t Ks[kBk * KP];
+  __shared__ __align__(16) unsigned char Ks[kBk * 256];
   __shared__ __align__(16) uint16_t Vt[kHeadDim * VP];
-  __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];
+  __shared__ int2 runs[3];
   const float NEG_INF = -__builtin_huge_valf();
-  const int total = D.B * D.h_kv * local_tiles<VL>(D);
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = gridDim.x / kXcds;
-  const int lo = (int)((int64_t)total * xcd / kXcds), hi = (int)((int64_t)total * (xcd + 1) / kXcds);
-  const int stride = per_xcd * kRun;
-  Walk w{lo + slot * kRun, lo + slot * kRun, min(lo + slot * kRun + kRun, hi)};
-  if (w.tile >= hi) return;  // uniform over the workgroup
+  const bool leader = threadIdx.x == 0;
+  RunQueue rq;
+  if (leader) {
+    rq.init(ws.ctr + kXcds, D.B * D.h_kv * local_tiles<VL>(D));
+    const int2 a = rq.claim();
+    runs[0] = a;
+    runs[1] = a.x >= 0 ? rq.claim() : make_int2(-1, -1);
+  }
+  lds_barrier();
+  int2 run = uniform2(runs[0]), nrun = uniform2(runs[1]);
+  if (run.x < 0) return;  // uniform over the workgroup
+  if (leader && nrun.x >= 0) rq.prefetch();
+  int ri = 0;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
   const int r = wave * 32 + col;
   const int ps = r / D.G, hh = r % D.G;
-  unsigned char* qw = Qs[wave];
   int staged_bg = -1, staged_t = -1;
-  for (; w.tile < hi; w = walk_next(w, stride, hi)) {
-    const TileRow cur = tile_row<true, VL>(TileRaw{-1, 0}, D, ws, w.tile, ps);
+  bool fresh = true;
+  for (int t = run.x;;) {
+    const TileRow cur = tile_row<true, VL>(TileRaw{-1, 0}, D, ws, t, ps);
     const int g = cur.bg % D.h_kv, b = cur.bg / D.h_kv;
     const int64_t qoff = (qrow_of<VL>(D, b, cur.valid ? cur.i : 0) * D.h_q + g * D.G + hh) * kHeadDim;
-    fetch_q_rows(qw, q + qoff, lane);
+    uint4 qf[8];
+    load_q(q + qoff, half, qf);
     // The row's non-local partials (chunk-major blocks, see store_partials):
     // this lane's 64 values of each are chunks 8 * half .. 8 * half + 7 of its
     // head, in accumulator order.  Their log-sum-exps are requested before the
@@ -347,7 +690,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // fold, which therefore never rescales; partial loads run one slot ahead of
     // the fold.
     const int64_t prow = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1);
-    const float* lse_p = ws.part_lse + prow * D.G + hh;                       // slot s at s * G
+    const float* lse_p = ws.part_lse + prow * D.G + hh;                                   // slot s at s * G
     const uint16_t* o_p = ws.part_o + prow * D.G * kHeadDim + (8 * half * D.G + hh) * 8;  // slot s at s * G * 128
     auto load_slot = [&](int s0, float& ls, uint4 (&x)[8]) {  // past slot k-1: weight 0
       const int sl = min(s0, D.k - 1);
@@ -367,23 +710,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 
     if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform
-      if (staged_bg >= 0) __syncthreads();
+      if (!fresh) lds_barrier();
       const int sb = cur.bg / D.h_kv;
       const int64_t kv0 = kvoff_of<VL>(D, sb, cur.bg % D.h_kv, cur.t);
-      stage_kv_any<KV8>(Ks, Vt, k, v, kv0, max(1, min(kBk, nkv_of<VL>(D, sb) - cur.t * kBk)));
-      __syncthreads();
+      stage_kv_fwd<KV8, false>(Ks, Vt, k, v, kv0, max(1, min(kBk, nkv_of<VL>(D, sb) - cur.t * kBk)));
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's direct K loads have landed
+      lds_barrier();
       staged_bg = cur.bg;
       staged_t = cur.t;
     }
+    fresh = false;
     f32x16 sc[4], o[4];
     float m2, l;
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the query rows have landed in LDS
-
-    float M = NEG_INF;  // the lse loads were issued after the row fetch: landed too
+    float M = NEG_INF;
 #pragma unroll
     for (int j = 0; j < 16; ++j) M = fmaxf(M, lv[j]);
     __builtin_amdgcn_sched_barrier(0);
-    qk_block(Ks, qw, lane, sc);
+    qk_block_q(Ks, qf, lane, sc);
     __builtin_amdgcn_sched_barrier(0);
     for (int s0 = 16; s0 < D.k; s0 += 8) {  // k > 16
       float lw[8];
@@ -446,32 +789,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (lse_out && half == 0)
         lse_out[((int64_t)b * D.h_q + g * D.G + hh) * D.n_q + cur.i] = (M + __log2f(L)) * 0.69314718055994531f;
     }
+    if (t + 1 < run.y) {
+      ++t;
+      continue;
+    }
+    if (nrun.x < 0) break;  // uniform
+    if (leader) runs[(ri + 2) % 3] = rq.resolve();
+    lds_barrier();
+    fresh = true;
+    run = nrun;
+    nrun = uniform2(runs[(ri + 2) % 3]);
+    ++ri;
+    if (leader && nrun.x >= 0) rq.prefetch();
+    t = run.x;
   }
 }
 
 }  // namespace
 
-hipError_t launch_sparse_attn(const uint16_t* q, const void* k, const void* v, const int32_t* block_idx,
-                              uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream) {
-  hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
-  if (e != hipSuccess) return e;
+Dims fwd_attn_dims(const Dims& D) {
+  Dims F = D;
+  int pt = 1;  // pt * G rows fill a tile of kFRows; pt <= Bk keeps a local tile inside one block
+  while (pt * 2 * D.G <= kFRows && pt * 2 <= kBk) pt *= 2;
+  F.pt = pt;
+  return F;
+}
+
+namespace {
+int fwd_attn_grid() { return 2 * persistent_grid(); }  // two four-wave workgroups per CU
+}  // namespace
+
+hipError_t launch_attn_kernels(const uint16_t* q, const void* k, const void* v, uint16_t* out, float* lse,
+                               const AttnWs& ws, const Dims& F, hipStream_t stream) {
   auto go = [&](auto vl, auto kv8) {
     constexpr bool VL = decltype(vl)::value, K8 = decltype(kv8)::value;
-    hipLaunchKernelGGL((k_attn_tiles<false, VL, K8>), dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws,
-                       D);
+    hipLaunchKernelGGL((k_attn_tiles<VL, K8>), dim3(fwd_attn_grid()), dim3(kFThreads), 0, stream, q, k, v, ws, F);
     mark("k_attn_tiles", stream);
-    hipLaunchKernelGGL((k_attn_local_merge<VL, K8>), dim3(persistent_grid()), dim3(kThreads), 0, stream, q, k, v, ws,
-                       out, lse, D);
+    hipLaunchKernelGGL((k_attn_local_merge<VL, K8>), dim3(fwd_attn_grid()), dim3(kFThreads), 0, stream, q, k, v, ws,
+                       out, lse, F);
     mark("k_attn_local_merge", stream);
   };
   using T = std::true_type;
-  using F = std::false_type;
-  if (dims_varlen(D)) {
-    if (D.kv_eb == 1) go(T{}, T{}); else go(T{}, F{});
+  using Fa = std::false_type;
+  if (dims_varlen(F)) {
+    if (F.kv_eb == 1) go(T{}, T{}); else go(T{}, Fa{});
   } else {
-    if (D.kv_eb == 1) go(F{}, T{}); else go(F{}, F{});
+    if (F.kv_eb == 1) go(Fa{}, T{}); else go(Fa{}, Fa{});
   }
   return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const uint16_t* q, const void* k, const void* v, const int32_t* block_idx,
+                              uint16_t* out, float* lse, const AttnWs& ws, const Dims& D, hipStream_t stream) {
+  const Dims F = fwd_attn_dims(D);
+  hipError_t e = launch_gather_plan(block_idx, ws, F, stream);
+  if (e != hipSuccess) return e;
+  return launch_attn_kernels(q, k, v, out, lse, ws, F, stream);
 }
 
 }  // namespace msa
