@@ -30,14 +30,15 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-MAX_MARKS = 64                 # events per marked step
+MAX_MARKS = 192                # events per marked step (overlapped passes mark ~100)
 
 # HBM bytes per launch from rocprofv3 counter runs of the 128K step (FETCH_SIZE
 # x2, calibrated on a 1 GiB copy, + WRITE_SIZE x1; see profiles/), with the
 # sha256 (first 16 hex digits) of the sources the kernel was built from when
 # they were taken.  A kernel whose sources have changed since reports null.
 COUNTER_TRAFFIC = {
-    # kernel name: (bytes per launch, {source file: sha16}); profiles/prefill_128k_decode_256k_counters.md
+    # kernel name: (bytes per step, summed over the step's launches, {source file: sha16});
+    # profiles/prefill_128k_decode_256k_counters.md
     "k_index_scores(top-k fused)": (2771779008, {"index_scores.hip": "d6c53c22822df47d"}),
     "k_attn_tiles": (66243421336, {"sparse_attn.hip": "d1e3aac4d416fd6f", "attn_tiles.h": "a115cc27501125f5"}),
     "k_attn_local_merge": (40917432688, {"sparse_attn.hip": "d1e3aac4d416fd6f", "attn_tiles.h": "a115cc27501125f5"}),
@@ -54,8 +55,9 @@ def source_sha16(name):
 
 
 def counter_traffic(kernel, workload):
-    """Counter bytes per launch recorded for this kernel on this workload with
-    its current sources, else None."""
+    """Counter bytes per step (over all of the step's launches of the kernel)
+    recorded for this kernel on this workload with its current sources, else
+    None."""
     rec = COUNTER_TRAFFIC.get(kernel)
     if rec is None or COUNTER_WORKLOAD.get(kernel, "prefill_128k") != workload:
         return None
@@ -198,19 +200,23 @@ def kernel_table(w, kernels, ms_step):
         e = {"avg_ms": round(ms, 4), "launches_per_step": d["launches_per_step"],
              "share_of_step": round(ms * d["launches_per_step"] / ms_step, 4)}
         bound, work, unit, design_bytes = kernel_work(name, w, wk)
-        if bound == "mfma" and d["launches_per_step"] == 1:
-            e["tflops"] = round(work / (ms * 1e-3) / 1e12, 1)
-            e["frac_mfma"] = round(work / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
-        elif bound == "hbm" and d["launches_per_step"] == 1:
-            e["gbs"] = round(work / (ms * 1e-3) / 1e9, 1)
-            e["frac_hbm"] = round(work / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-        if design_bytes is not None and d["launches_per_step"] == 1:
-            e["design_gbs"] = round(design_bytes / (ms * 1e-3) / 1e9, 1)
-            e["design_frac_hbm"] = round(design_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        # the step's work of this kernel over its time summed over the step's
+        # launches (the overlapped passes launch each attention and scoring
+        # kernel once per pass)
+        tot = ms * d["launches_per_step"]
+        if bound == "mfma":
+            e["tflops"] = round(work / (tot * 1e-3) / 1e12, 1)
+            e["frac_mfma"] = round(work / (tot * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        elif bound == "hbm":
+            e["gbs"] = round(work / (tot * 1e-3) / 1e9, 1)
+            e["frac_hbm"] = round(work / (tot * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        if design_bytes is not None:
+            e["design_gbs"] = round(design_bytes / (tot * 1e-3) / 1e9, 1)
+            e["design_frac_hbm"] = round(design_bytes / (tot * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         traffic = counter_traffic(name, w.name)
-        if traffic is not None and d["launches_per_step"] == 1:
+        if traffic is not None:
             e["counter_bytes"] = traffic
-            e["counter_frac_hbm"] = round(traffic / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            e["counter_frac_hbm"] = round(traffic / (tot * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         out[name] = e
     return out
 
@@ -221,13 +227,16 @@ def roofline_of(w, kernels):
     wk = algorithmic_work(w)
     name, d = max(kernels.items(), key=lambda kv: kv[1]["avg_ms"] * kv[1]["launches_per_step"])
     bound, work, unit, _ = kernel_work(name, w, wk)
-    ms = d["avg_ms"]
+    ms, n = d["avg_ms"], d["launches_per_step"]
+    work /= n  # per launch: the step's work spread over its launches
     if bound == "mfma":
         ach, peak, u = work / (ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
         ach, peak, u = work / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    traffic = counter_traffic(name, w.name)
     return {"bound": bound, "kernel": name, "achieved": round(ach, 2), "peak": peak, "unit": u,
-            "frac": round(ach / peak, 4), "traffic": counter_traffic(name, w.name), "avg_ms": round(ms, 4)}
+            "frac": round(ach / peak, 4), "traffic": None if traffic is None else traffic / n, "avg_ms": round(ms, 4),
+            "launches_per_step": n}
 
 
 def gpu_leg(w, steps, warmup, stream, paged=False, kl=False, stages=True, check=False):

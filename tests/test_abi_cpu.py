@@ -263,3 +263,13 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     # the 256K decode step and the 4K prefill fit
     assert msa.workspace_size(msa.Problem.make(64, 1, 262144, 64, 8), msa.OP_FORWARD) <= msa.NOALLOC_SCRATCH_BYTES
     assert msa.workspace_size(prob(), msa.OP_FORWARD) <= msa.NOALLOC_SCRATCH_BYTES
+
+
+def test_header_constants_match_binding():
+    """The binding's copies of the header's size constants."""
+    import re
+    defs = {m[0]: int(m[1]) << int(m[2] or 0)
+            for m in re.findall(r"#define (MSA_\w+) \(?(?:\(size_t\))?(\d+)(?: << (\d+))?", open(HEADER).read())}
+    assert defs["MSA_DEFAULT_CHUNK_ROWS"] == msa.DEFAULT_CHUNK_ROWS
+    assert defs["MSA_CHUNK_ALIGN"] == msa.CHUNK_ALIGN
+    assert defs["MSA_NOALLOC_SCRATCH_BYTES"] == msa.NOALLOC_SCRATCH_BYTES
