@@ -12,10 +12,12 @@
 //   0. the row's candidate scores (blocks t < l, l = the local block; block t
 //      = lane + 64 j) are loaded into registers through a buffer descriptor
 //      whose range is the row;
-//   1. each lane takes the max of its share of the row, and tau is the (k-1)-th
-//      largest of the 64 lane maxima (a sorting network, mostly DPP moves): at
-//      least k-1 scores of the row are >= tau, and for score rows of any shape
-//      only a handful more;
+//   1. each lane takes the max of its share of the row, and tau is a value
+//      that at least k-1 lane maxima reach: for k-1 <= 16 the smallest over the
+//      four rows of 16 lanes of each row's ceil((k-1)/4)-th largest (sorts of
+//      16 lanes, DPP moves only), else the (k-1)-th largest of all 64 (a
+//      sorting network, mostly DPP moves).  At least k-1 scores of the row are
+//      >= tau, and for score rows of any shape only a few dozen more;
 //   2. the scores >= tau are compacted into LDS in ascending block order with
 //      their block ids, one per lane, and T, the (k-1)-th largest of them, is
 //      read off a sorted copy (16, 32 or 64 lanes, as many as they need);
@@ -112,6 +114,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Number of the wave's lanes where pred holds (a scalar).
 __device__ __forceinline__ int count(bool pred) { return __popcll(__ballot(pred)); }
 
+// base + the number of set bits of m below this lane (two VALU ops).
+__device__ __forceinline__ int prefix(uint64_t m, int base = 0) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)base));
+}
+
 // PER > 0: a row's candidates (at most 64 * PER) are loaded once into
 // registers, the next row's while the current one is selected; PER == 0 (rows
 // beyond 2048 blocks): each of the two passes over the row streams it, eight
@@ -124,7 +131,6 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
   // live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int stride = gridDim.x * 4;
-  const uint64_t below = (1ull << lane) - 1ull;
   const float NEG_INF = -__builtin_huge_valf();
   const int k = D.k, kk = k - 1;  // kk blocks to pick among a row's `local` candidates
   constexpr int NREG = PER > 0 ? PER : 1;
@@ -185,11 +191,16 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
       const int nj = (local + 63) >> 6;  // score slots in use (uniform)
       // f(j, score of block lane + 64 j) for j = 0 .. nj-1, in order; only the
       // last slot can reach past the candidates
+      if constexpr (PER > 0) {  // the last slot's scores past the candidates become -inf, in place
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+          if (j == nj - 1) vc[j] = lane + 64 * j < local ? vc[j] : NEG_INF;
+      }
       auto each_score = [&](auto&& f) {
         if constexpr (PER > 0) {
 #pragma unroll
           for (int j = 0; j < PER; ++j)
-            if (j < nj) f(j, j < nj - 1 || lane + 64 * j < local ? vc[j] : NEG_INF);
+            if (j < nj) f(j, vc[j]);
         } else {
           for (int j0 = 0; j0 < nj; j0 += 8) {  // eight loads in flight per step
             float v[8];
@@ -202,10 +213,21 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
         }
       };
 
-      // 1. tau = kk-th largest lane maximum
+      // 1. tau: for kk <= 16, the smallest over the four rows of 16 lanes of
+      // the row's m-th largest lane maximum (m = ceil(kk / 4)): 4 m >= kk lane
+      // maxima are >= tau, and the 16-lane sorts are DPP moves only; else the
+      // kk-th largest lane maximum
       float mx = NEG_INF;
       each_score([&](int, float c) { mx = fmaxf(mx, c); });
-      const float tau = lane_f32(sort_lanes<64>(mx, lane), 64 - kk);
+      float tau;
+      if (kk <= 16) {
+        const float srt = sort_lanes<16>(mx, lane);
+        const int pos = 16 - ((kk + 3) >> 2);
+        tau = fminf(fminf(lane_f32(srt, pos), lane_f32(srt, 16 + pos)),
+                    fminf(lane_f32(srt, 32 + pos), lane_f32(srt, 48 + pos)));
+      } else {
+        tau = lane_f32(sort_lanes<64>(mx, lane), 64 - kk);
+      }
 
       // 2. scores >= tau, compacted in ascending block order (slot 63 takes
       // the overflow of a row with more than 64, whose list is not used)
@@ -214,7 +236,7 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
         const bool take = c >= tau;
         const uint64_t m = __ballot(take);
         if (m) {
-          const int slot = total + (int)__popcll(m & below);
+          const int slot = prefix(m, total);
           if (take) cand[wave][slot < 63 ? slot : 63] = make_uint2(__float_as_uint(c), (uint32_t)(lane + 64 * j));
           total += __popcll(m);
         }
@@ -236,9 +258,9 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
         // 3. emit: scores > T, then scores == T in block order until kk
         const uint64_t meq = __ballot(have && c == thr);
         const int need_eq = kk - count(have && c > thr);
-        const bool take = have && (c > thr || (c == thr && __popcll(meq & below) < need_eq));
+        const bool take = have && (c > thr || (c == thr && prefix(meq) < need_eq));
         const uint64_t m = __ballot(take);
-        if (take) dst[__popcll(m & below)] = (int)e.y;
+        if (take) dst[prefix(m)] = (int)e.y;
       } else {
         // many equal scores: T = the largest key x with #{keys >= x} >= kk, bit by bit
         uint32_t thr = 0;
@@ -256,9 +278,9 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
           const uint32_t u = sel_key(c);
           const bool eq = u == thr;
           const uint64_t meq = __ballot(eq);
-          const bool take = u > thr || (eq && eq_seen + __popcll(meq & below) < need_eq);
+          const bool take = u > thr || (eq && prefix(meq, eq_seen) < need_eq);
           const uint64_t m = __ballot(take);
-          if (take) dst[base + __popcll(m & below)] = lane + 64 * j;
+          if (take) dst[prefix(m, base)] = lane + 64 * j;
           base += __popcll(m);
           eq_seen += __popcll(meq);
         });
