@@ -13,7 +13,8 @@
 //      = lane + 64 j) are loaded into registers through a buffer descriptor
 //      whose range is the row;
 //   1. each lane takes the max of its share of the row, and tau is a value
-//      that at least k-1 lane maxima reach: for k-1 <= 16 the smallest over the
+//      that at least k-1 lane maxima reach: for k-1 <= 16 and rows held in
+//      registers the smallest over the
 //      four rows of 16 lanes of each row's ceil((k-1)/4)-th largest (sorts of
 //      16 lanes, DPP moves only), else the (k-1)-th largest of all 64 (a
 //      sorting network, mostly DPP moves).  At least k-1 scores of the row are
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
       float mx = NEG_INF;
       each_score([&](int, float c) { mx = fmaxf(mx, c); });
       float tau;
-      if (kk <= 16) {
+      if (PER > 0 && kk <= 16) {  // rows in registers (streamed rows keep the tighter tau: fewer candidates)
         const float srt = sort_lanes<16>(mx, lane);
         const int pos = 16 - ((kk + 3) >> 2);
         tau = fminf(fminf(lane_f32(srt, pos), lane_f32(srt, 16 + pos)),

@@ -217,7 +217,7 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, fl
 constexpr int kFWaves = 4;
 constexpr int kFThreads = 64 * kFWaves;
 constexpr int kFRows = 32 * kFWaves;
-constexpr int kFRun = 16;  // tiles per claimed run
+constexpr int kFRun = 16;  // most tiles per claimed run
 
 // Lane (column, half) of a wave's MFMA operand for query row `row`: dims
 // 16 ks + 8 half .. + 7 of k-step ks, the order qk_block reads from LDS.
@@ -450,27 +450,30 @@ __device__ __forceinline__ void softmax_pv_packed(const uint16_t* Vt, f32x16 (&s
 
 // Dynamic runs.  The tile range [0, total) is cut into kXcds slices; slice x
 // is first drained by the workgroups of XCD x (workgroup w runs on XCD
-// w % kXcds), which claim runs of kFRun consecutive tiles from the slice's
+// w % kXcds), which claim runs of consecutive tiles from the slice's
 // counter, so consecutive tiles (one K/V block as a rule) stay on one XCD's
-// L2.  A workgroup whose slice is empty moves on to the next slices in turn.
+// L2.  A run is kFRun tiles, or fewer when the grid would otherwise get under
+// four runs per workgroup (short tile lists: a chunk of a long context).  A
+// workgroup whose slice is empty moves on to the next slices in turn.
 // Workgroups that start late, or share their CU with other work, simply
 // claim fewer runs.  Only thread 0 of a workgroup uses it.
 struct RunQueue {
   int32_t* ctr;
-  int total, slice, left;  // left: slices not yet found empty
+  int total, len, slice, left;  // len: tiles per run; left: slices not yet found empty
   int pend;                // claimed run of `slice`, not yet resolved
   __device__ void init(int32_t* c, int tot) {
     ctr = c;
     total = tot;
+    len = max(1, min(kFRun, tot / (int)(gridDim.x * 4)));
     slice = blockIdx.x % kXcds;
     left = kXcds;
     pend = 0;
   }
   __device__ int2 range(int s, int run) const {
     const int64_t lo = (int64_t)total * s / kXcds, hi = (int64_t)total * (s + 1) / kXcds;
-    const int64_t st = lo + (int64_t)run * kFRun;
+    const int64_t st = lo + (int64_t)run * len;
     if (st >= hi) return make_int2(-1, -1);
-    return make_int2((int)st, (int)min<int64_t>(st + kFRun, hi));
+    return make_int2((int)st, (int)min<int64_t>(st + len, hi));
   }
   __device__ int2 claim() {  // waits for each counter it reads
     while (left > 0) {
