@@ -326,7 +326,16 @@ def gpu_leg(w, steps, warmup, stream, paged=False, kl=False, stages=True, check=
         run_klb = lambda: msa.index_kl_bwd(p, x["q"], x["k"], x["iq"], x["ik"], f["block_idx"], f["lse"], lse_index,
                                            d_iq, d_ik, workspace=kb_ws, stream=sp)
         res["ms_kl_bwd"] = timed_steps(run_klb, steps, warmup, stream)["ms"]
-        del d_iq, d_ik, kb_ws, lse_index
+        # the pair that keeps the teacher: the KL pass storing it (fp16 per
+        # (row, slot, key)), and the backward reading it instead of forming S
+        teacher = torch.empty(msa.teacher_shape(p), dtype=torch.float16, device="cuda")
+        run_klt = lambda: msa.index_kl_teacher(p, x["q"], x["k"], x["iq"], x["ik"], f["block_idx"], f["lse"], kl_out,
+                                               lse_index, teacher, kl_ws, stream=sp)
+        res["ms_kl_teacher"] = timed_steps(run_klt, steps, warmup, stream)["ms"]
+        run_klbt = lambda: msa.index_kl_bwd_teacher(p, x["iq"], x["ik"], f["block_idx"], teacher, lse_index, d_iq,
+                                                    d_ik, workspace=kb_ws, stream=sp)
+        res["ms_kl_bwd_teacher"] = timed_steps(run_klbt, steps, warmup, stream)["ms"]
+        del d_iq, d_ik, kb_ws, lse_index, teacher
         # dense mode (the indexer warmup): dense attention, then the KL over every visible token
         d_out = torch.empty_like(f["out"])
         d_lse = torch.empty_like(f["lse"])
@@ -651,6 +660,14 @@ def main():
         line["kl_backward"] = {"ms": round(g["ms_kl_bwd"], 4),
                                "tflops": round(f_klb / (g["ms_kl_bwd"] * 1e-3) / 1e12, 1),
                                "frac_mfma": round(f_klb / (g["ms_kl_bwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        # with the teacher stored: the KL pass also writes it (2 bytes per (row, slot, key));
+        # the backward reads it (no S), then Z, d_index_k and d_index_q for every group
+        t_bytes = 2.0 * w.batch * w.h_kv * w.n_q * (w.topk + 1) * w.block_size
+        f_klbt = 2.0 * 3 * w.index_dim * w.h_kv * w.batch * float(t_size.sum())
+        line["kl_teacher"] = {"ms": round(g["ms_kl_teacher"], 4), "teacher_gb": round(t_bytes / 1e9, 2),
+                              "kl_plus_bwd_ms": round(g["ms_kl_teacher"] + g["ms_kl_bwd_teacher"], 4)}
+        line["kl_backward_teacher"] = {"ms": round(g["ms_kl_bwd_teacher"], 4),
+                                       "tflops": round(f_klbt / (g["ms_kl_bwd_teacher"] * 1e-3) / 1e12, 1)}
         # dense mode: every visible token (sum over rows of p + 1)
         import numpy as np
         n_vis = float(np.sum(w.offset + np.arange(w.n_q, dtype=np.int64) + 1)) * w.batch

@@ -30,7 +30,8 @@ DEFAULT_CHUNK_ROWS, CHUNK_ALIGN = 131072, 8192  # MSA_DEFAULT_CHUNK_ROWS, MSA_CH
 EXPORTS = ("msa_workspace_size", "msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
            "msa_index_scores_v", "msa_block_topk_v", "msa_sparse_attn_fwd_v", "msa_forward_v", "msa_index_kl",
            "msa_dense_attn_fwd", "msa_dense_index_kl", "msa_sparse_attn_bwd", "msa_index_kl_bwd",
-           "msa_forward_noalloc", "msa_forward_marked", "msa_status_string")
+           "msa_index_kl_teacher", "msa_index_kl_bwd_teacher", "msa_forward_noalloc", "msa_forward_marked",
+           "msa_status_string")
 NOALLOC_SCRATCH_BYTES = 128 << 20  # MSA_NOALLOC_SCRATCH_BYTES
 
 
@@ -115,6 +116,8 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.msa_dense_index_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.msa_sparse_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_index_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.msa_index_kl_teacher.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.msa_index_kl_bwd_teacher.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.msa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.msa_forward_marked.argtypes = [P, V, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(vp),
                                            ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int)]
@@ -165,6 +168,7 @@ def _check(rc: int, what: str):
 # reaches the library.
 _BF16 = ("bfloat16",)
 _F32 = ("float32",)
+_F16 = ("float16",)
 _I32 = ("int32",)
 _FP8 = ("uint8", "float8_e4m3fn")
 
@@ -431,6 +435,55 @@ def index_kl(p: Problem, q, k, index_q, index_k, block_idx, lse, kl, workspace=N
                         _ptr(kl), _ptr(lse_index), _ptr(workspace), nb, st)
     _check(rc, "msa_index_kl")
     return kl
+
+
+def teacher_shape(p: Problem):
+    """Shape of index_kl_teacher's teacher (fp16): [B, H_kv, n_q, k + 1, block_size]."""
+    return (p.batch, p.h_kv, p.n_q, p.topk + 1, p.block_size)
+
+
+def index_kl_teacher(p: Problem, q, k, index_q, index_k, block_idx, lse, kl, lse_index, teacher, workspace=None,
+                     workspace_bytes=None, stream=None):
+    """index_kl, also storing the teacher's weight of every key of every
+    (row, slot) in teacher (fp16, teacher_shape(p)) for index_kl_bwd_teacher."""
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    a = _Args("index_kl_teacher")
+    _qkv_args(a, p, q, k, None, None, kv_dtypes=_BF16, with_v=False)
+    _index_args(a, p, index_q, index_k, None)
+    a.add(block_idx, "block_idx", _I32, _bidx_numel(p))
+    a.add(lse, "lse", _F32, _row_numel(p, p.h_q))
+    a.add(kl, "kl", _F32, _row_numel(p, p.h_kv))
+    a.add(lse_index, "lse_index", _F32, _row_numel(p, p.h_kv))
+    a.add(teacher, "teacher", _F16, _row_numel(p, p.h_kv) * (p.topk + 1) * p.block_size)
+    a.workspace(workspace, nb)
+    a.device()
+    L, st = library(), _stream(stream, q)
+    rc = L.msa_index_kl_teacher(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(index_q), _ptr(index_k), _ptr(block_idx),
+                                _ptr(lse), _ptr(kl), _ptr(lse_index), _ptr(teacher), _ptr(workspace), nb, st)
+    _check(rc, "msa_index_kl_teacher")
+    return kl, teacher
+
+
+def index_kl_bwd_teacher(p: Problem, index_q, index_k, block_idx, teacher, lse_index, d_index_q, d_index_k,
+                         dkl=None, workspace=None, workspace_bytes=None, stream=None):
+    """index_kl_bwd with the teacher index_kl_teacher stored (no q, k, lse)."""
+    nb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    a = _Args("index_kl_bwd_teacher")
+    _index_args(a, p, index_q, index_k, None)
+    a.add(block_idx, "block_idx", _I32, _bidx_numel(p))
+    a.add(teacher, "teacher", _F16, _row_numel(p, p.h_kv) * (p.topk + 1) * p.block_size)
+    a.add(lse_index, "lse_index", _F32, _row_numel(p, p.h_kv))
+    a.add(d_index_q, "d_index_q", _elem(p.index_dtype), p.batch * p.n_q * p.h_kv * p.index_dim)
+    a.add(d_index_k, "d_index_k", _elem(p.index_dtype), p.batch * p.n_kv * p.index_dim)
+    a.add(dkl, "dkl", _F32, _row_numel(p, p.h_kv), optional=True)
+    a.workspace(workspace, nb)
+    a.device()
+    L, st = library(), _stream(stream, index_q)
+    rc = L.msa_index_kl_bwd_teacher(ctypes.byref(p), _ptr(index_q), _ptr(index_k), _ptr(block_idx), _ptr(teacher),
+                                    _ptr(lse_index), _ptr(dkl), _ptr(d_index_q), _ptr(d_index_k), _ptr(workspace),
+                                    nb, st)
+    _check(rc, "msa_index_kl_bwd_teacher")
+    return d_index_q, d_index_k
 
 
 def sparse_attn_bwd(p: Problem, q, k, v, block_idx, out, lse, dout, dq, dk, dv, workspace=None,

@@ -506,8 +506,31 @@ msa_status msa_index_kl(const msa_problem* p, const void* q, const void* k, cons
   const size_t plan = attn_ws_layout(D, base, &ws, false);
   return hip_status(msa::launch_index_kl(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                          static_cast<const uint16_t*>(index_q), static_cast<const uint16_t*>(index_k),
-                                         block_idx, lse, kl, lse_index, ws, reinterpret_cast<float4*>(base + plan), D,
-                                         stream));
+                                         block_idx, lse, kl, lse_index, nullptr, ws,
+                                         reinterpret_cast<float4*>(base + plan), D, stream));
+}
+
+msa_status msa_index_kl_teacher(const msa_problem* p, const void* q, const void* k, const void* index_q,
+                                const void* index_k, const int32_t* block_idx, const float* lse, float* kl,
+                                float* lse_index, void* teacher, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !index_q || !index_k || !block_idx || !lse || !kl || !lse_index || !teacher || !workspace)
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(index_q) || !aligned16(index_k) || !aligned16(block_idx) ||
+      !aligned16(lse) || !aligned16(kl) || !aligned16(lse_index) || !aligned16(teacher) || !aligned16(workspace))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D)) return MSA_ERR_UNSUPPORTED;
+  if (kl_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  AttnWs ws;
+  char* base = static_cast<char*>(workspace);
+  const size_t plan = attn_ws_layout(D, base, &ws, false);
+  return hip_status(msa::launch_index_kl(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                         static_cast<const uint16_t*>(index_q), static_cast<const uint16_t*>(index_k),
+                                         block_idx, lse, kl, lse_index, static_cast<uint16_t*>(teacher), ws,
+                                         reinterpret_cast<float4*>(base + plan), D, stream));
 }
 
 msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, const void* index_q,
@@ -533,6 +556,32 @@ msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, 
   return hip_status(msa::launch_index_kl_bwd(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(index_q),
       static_cast<const uint16_t*>(index_k), block_idx, lse, lse_index, dkl, static_cast<uint16_t*>(d_index_q),
+      static_cast<uint16_t*>(d_index_k), ws, part, group, D, stream));
+}
+
+msa_status msa_index_kl_bwd_teacher(const msa_problem* p, const void* index_q, const void* index_k,
+                                    const int32_t* block_idx, const void* teacher, const float* lse_index,
+                                    const float* dkl, void* d_index_q, void* d_index_k, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  Dims D;
+  const msa_status st = derive(p, &D);
+  if (st != MSA_OK) return st;
+  if (!index_q || !index_k || !block_idx || !teacher || !lse_index || !d_index_q || !d_index_k || !workspace)
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(index_q) || !aligned16(index_k) || !aligned16(block_idx) || !aligned16(teacher) ||
+      !aligned16(lse_index) || (dkl && !aligned16(dkl)) || !aligned16(d_index_q) || !aligned16(d_index_k) ||
+      !aligned16(workspace))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (D.n_blk > msa::kMaxPlanBlocks || !msa::kl_supported(D) || !bwd_walk_ok(D)) return MSA_ERR_UNSUPPORTED;
+  if (klb_bytes(D) > workspace_bytes) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  AttnWs ws;
+  char* base = static_cast<char*>(workspace);
+  const size_t plan = attn_ws_layout(D, base, &ws, false);
+  auto part = reinterpret_cast<uint16_t*>(base + plan);
+  auto group = reinterpret_cast<float*>(base + plan + klb_part_bytes(D));
+  return hip_status(msa::launch_index_kl_bwd_teacher(
+      static_cast<const uint16_t*>(index_q), static_cast<const uint16_t*>(index_k), block_idx,
+      static_cast<const uint16_t*>(teacher), lse_index, dkl, static_cast<uint16_t*>(d_index_q),
       static_cast<uint16_t*>(d_index_k), ws, part, group, D, stream));
 }
 

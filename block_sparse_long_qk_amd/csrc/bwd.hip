@@ -747,6 +747,197 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
+// The same gradient from a stored teacher (msa_index_kl's optional output:
+// fp16 t per (row, slot, key of the block)), so S is not formed again: the
+// walk's rows are positions, not head rows (32 positions a chunk), and only
+// Z = IQ IK_w^T, g = w (s - t), d_ik^T += IQ^T g and d_iq^T = IK^T g^T remain,
+// on the operand layouts of k_kl_bwd.
+template <int DIDX>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_kl_bwd_t(
+    const uint16_t* __restrict__ iq, const uint16_t* __restrict__ ik, const _Float16* __restrict__ teacher,
+    const float* __restrict__ lse_index, const float* __restrict__ wrow, AttnWs ws, uint16_t* __restrict__ diq_part,
+    float* __restrict__ dik_group, Dims D) {
+  constexpr int CPI = DIDX / 8;       // 16-byte pieces of an index row
+  constexpr int RPI = 64 / CPI;       // index rows per wave instruction
+  constexpr int NI = 32 / RPI;        // waves that carry the chunk's index rows
+  constexpr int DT = DIDX / 16;       // 16-dim tiles of the index dim
+  constexpr int IKS = DIDX / 32;      // k-steps of Z
+  __shared__ __align__(16) uint16_t IKt[DIDX * kKtP];         // index keys of the block, transposed
+  __shared__ __align__(16) unsigned char IQs[32 * 2 * DIDX];  // each row's index-query row (swizzled)
+  __shared__ __align__(16) uint16_t IQt[DIDX * kTP];          // its transpose [d][row]
+  __shared__ __align__(16) unsigned char Ss[32 * 256];        // the chunk's g [row][key] (swizzled)
+  __shared__ WalkTab W;
+
+  Dims D1 = D;  // the walk over positions: one row per plan entry
+  D1.G = 1;
+  const int nbg = D.B * D.h_kv;
+  const int t = (int)(blockIdx.x / nbg);
+  const int bg = (int)(blockIdx.x % nbg);
+  const int b = bg / D.h_kv, g = bg % D.h_kv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, cgrp = lane >> 4;
+  const int nkv = D.n_kv;
+  const int n_valid = max(1, min(kBk, nkv - t * kBk));
+  const uint16_t* ikblk = ik + ((int64_t)b * nkv + (int64_t)t * kBk) * DIDX;
+
+  walk_setup(W, ws, D1, bg, t);
+  const int nch = W.n_chunks;
+  Builder bd;
+  const PartMul pm{1, 0};  // the (row, slot) index: d_iq partials DIDX apart, teacher rows kBk apart
+  if (wave == 0) bld_prologue(bd, W, ws, D1, bg, pm, lane);
+
+  // the block's index keys transposed into LDS: task = 4 keys x 8 dims
+  for (int task = threadIdx.x; task < 32 * CPI; task += kBwdThreads) {
+    const int kq = task / CPI, od = task % CPI;
+    u32x4 x[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      x[qq] = *reinterpret_cast<const u32x4*>(ikblk + min(4 * kq + qq, n_valid - 1) * DIDX + od * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) * 16;
+      const uint32_t v0 = (x[0][e >> 1] >> sh) & 0xFFFFu, v1 = (x[1][e >> 1] >> sh) & 0xFFFFu;
+      const uint32_t v2 = (x[2][e >> 1] >> sh) & 0xFFFFu, v3 = (x[3][e >> 1] >> sh) & 0xFFFFu;
+      *reinterpret_cast<uint2*>(IKt + (od * 8 + e) * kKtP + kq * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+    }
+  }
+  // this wave's 16 index keys as B operands
+  u32x4 ikf[IKS];
+  {
+    const int key = min(16 * wave + n, n_valid - 1);
+#pragma unroll
+    for (int ks = 0; ks < IKS; ++ks) ikf[ks] = *reinterpret_cast<const u32x4*>(ikblk + key * DIDX + 32 * ks + 8 * cgrp);
+  }
+  f32x4 dikT[DT];  // lane (key n, group c): dims 16dt + 4c + e of key 16w + n
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dikT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr float kL2e = 1.4426950408889634f;
+  const int key_abs = t * kBk + 16 * wave + n;
+  const bool has_w = wrow != nullptr;
+  const float* wsrc = has_w ? wrow : lse_index;  // read either way; 1 is used without weights
+  __syncthreads();  // row tables of chunks 0 and 1 are written
+
+  const uint16_t* iqb = iq + ((int64_t)b * D.n_q * D.h_kv + g) * DIDX;
+  const float* lzb = lse_index + (int64_t)bg * D.n_q;
+  const float* wb = wsrc + (int64_t)bg * D.n_q;
+  const _Float16* tk = teacher + 16 * wave + n;  // this lane's key in a (row, slot) of the teacher
+
+  // A chunk's index rows travel through registers: lane l of wave w < NI
+  // carries piece p of row RPI w + l / CPI, stored at byte 1024 w + 16 l and,
+  // element by element, into the transpose.
+  const int my_ri = RPI * wave + lane / CPI;
+  const int my_pi = (lane % CPI) ^ (my_ri % CPI);
+  u32x4 iq_next;
+  auto load_rows = [&](int slot) {
+    if (wave < NI) {
+      const int i = max(W.row[slot][my_ri].x - (int)D.offset, 0);
+      iq_next = *reinterpret_cast<const u32x4*>(iqb + (int64_t)i * D.h_kv * DIDX + 8 * my_pi);
+    }
+  };
+  auto store_rows = [&]() {
+    if (wave < NI) *reinterpret_cast<u32x4*>(IQs + 1024 * wave + 16 * lane) = iq_next;
+  };
+  // raw statistics of the next chunk for the lane's 8 rows 16 m + 4c + e (row
+  // 0's for rows that do not exist): the student's normaliser, the row weight
+  // and the teacher's weight of the lane's key
+  float lz_raw[8], w_raw[8];
+  _Float16 t_raw[8];
+  auto stats = [&](int slot) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = 16 * (u >> 2) + 4 * cgrp + (u & 3);
+      const int i = max(W.row[slot][r].x - (int)D.offset, 0);
+      lz_raw[u] = lzb[i];
+      w_raw[u] = wb[i];
+      t_raw[u] = tk[W.part[slot][r] * kBk];
+    }
+  };
+
+  load_rows(0);
+  stats(0);
+  store_rows();
+  for (int c = 0; c < nch; ++c) {
+    const int slot = c & (kRing - 1);
+    __syncthreads();  // chunk c's rows are in LDS; chunk c + 1's table is visible
+    if (wave < NI) tp_store8(IQt, iq_next, my_pi, my_ri);
+    float lz2[8], wg[8], tv[8];
+    int pos8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      pos8[u] = W.row[slot][16 * (u >> 2) + 4 * cgrp + (u & 3)].x;
+      lz2[u] = lz_raw[u] * kL2e;
+      wg[u] = has_w ? w_raw[u] : 1.f;
+      tv[u] = (float)t_raw[u];
+      asm volatile("" ::"v"(lz2[u]), "v"(wg[u]), "v"(tv[u]) : "memory");  // formed before the next chunk's loads
+    }
+    if (wave == 0) bld_step(bd, W, ws, D1, bg, pm, c, lane);
+    load_rows((c + 1) & (kRing - 1));
+    stats((c + 1) & (kRing - 1));
+    // Z (student), rows as M
+    f32x4 z4[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      z4[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * mt + n;
+#pragma unroll
+      for (int ks = 0; ks < IKS; ++ks) {
+        const u32x4 ia =
+            *reinterpret_cast<const u32x4*>(IQs + r * 2 * DIDX + 16 * ((4 * ks + cgrp) ^ (r % CPI)));
+        z4[mt] = mfma16(ia, ikf[ks], z4[mt]);
+      }
+    }
+    // g = w (s - t) on every visible (row, key); 0 for rows that do not exist
+    float gv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool vis = key_abs <= pos8[u] && key_abs < nkv;  // pos8 = -1: no row
+      const float sv = __builtin_amdgcn_exp2f(__builtin_fmaf(z4[u >> 2][u & 3], kL2e, -lz2[u]));
+      gv[u] = vis ? wg[u] * (sv - tv[u]) : 0.f;
+    }
+    const u32x4 gb = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]), pack_bf16x2(gv[4], gv[5]),
+                      pack_bf16x2(gv[6], gv[7])};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = 16 * (u >> 2) + 4 * cgrp + (u & 3);
+      const int key = 16 * wave + n;
+      const int sl = (key >> 3) ^ (r & 15);
+      *reinterpret_cast<uint16_t*>(Ss + r * 256 + sl * 16 + 2 * (key & 7)) =
+          (uint16_t)((u & 1) ? (gb[u >> 1] >> 16) : (gb[u >> 1] & 0xFFFFu));
+    }
+    __syncthreads();  // IQ^T and g are in LDS; the row buffers are free
+    // d_ik^T += IQ^T g (M = index dims, K = the 32 rows, N = this wave's keys)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dikT[dt] = mfma16(tp_operand(IQt, 16 * dt + n, cgrp), gb, dikT[dt]);
+    // d_iq^T (dims 16w .. 16w+15 x 32 rows) = IK^T g^T over the block's keys
+    if (wave < DT) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * nt + n;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(IKt + (16 * wave + n) * kKtP + 32 * ks + 8 * cgrp);
+          const u32x4 gbv = *reinterpret_cast<const u32x4*>(Ss + r * 256 + 16 * ((4 * ks + cgrp) ^ (r & 15)));
+          acc = mfma16(ka, gbv, acc);
+        }
+        if (W.row[slot][r].x >= 0) {
+          uint16_t* dst = diq_part + W.part[slot][r] * DIDX + 16 * wave + 4 * cgrp;
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        }
+      }
+    }
+    store_rows();  // chunk c + 1's rows, read after the next barrier
+  }
+  // this group's share of d_ik for the wave's keys (fp32; the groups are added next)
+  if (key_abs < nkv) {
+    float* dst = dik_group + (((int64_t)b * D.h_kv + g) * nkv + key_abs) * DIDX;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(dst + 16 * dt + 4 * cgrp) =
+          make_float4(dikT[dt][0], dikT[dt][1], dikT[dt][2], dikT[dt][3]);
+  }
+}
+
 // d_ik[b][j] = sum over groups of their shares (bf16): one thread per 4 dims.
 __global__ __launch_bounds__(256) void k_kl_bwd_dik(const float* __restrict__ dik_group, uint16_t* __restrict__ dik,
                                                     Dims D) {
@@ -826,6 +1017,30 @@ hipError_t launch_index_kl_bwd(const uint16_t* q, const uint16_t* k, const uint1
     }
   };
   if (D.d_idx == 128) by_g(std::integral_constant<int, 128>{}); else by_g(std::integral_constant<int, 64>{});
+  const int64_t n_ik = (int64_t)D.B * D.n_kv * (D.d_idx / 4);
+  hipLaunchKernelGGL(k_kl_bwd_dik, dim3((unsigned)((n_ik + 255) / 256)), dim3(256), 0, stream, dik_group, d_index_k, D);
+  const int64_t n_iq = (int64_t)D.B * D.h_kv * D.n_q * (D.d_idx / 8);
+  hipLaunchKernelGGL(k_kl_bwd_diq, dim3((unsigned)((n_iq + 255) / 256)), dim3(256), 0, stream, block_idx, diq_part,
+                     d_index_q, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_kl_bwd_teacher(const uint16_t* index_q, const uint16_t* index_k, const int32_t* block_idx,
+                                       const uint16_t* teacher, const float* lse_index, const float* wrow,
+                                       uint16_t* d_index_q, uint16_t* d_index_k, const AttnWs& ws,
+                                       uint16_t* diq_part, float* dik_group, const Dims& D, hipStream_t stream) {
+  if (ws.n_groups + 1 > kMaxSrc) return hipErrorInvalidValue;  // the walk's source table
+  hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
+  if (e == hipSuccess) e = launch_plan_sort(ws, D, stream);  // a fixed summation order
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((int64_t)D.B * D.h_kv * D.n_blk)), block(kBwdThreads);
+  const _Float16* t = reinterpret_cast<const _Float16*>(teacher);
+  if (D.d_idx == 128)
+    hipLaunchKernelGGL(k_kl_bwd_t<128>, grid, block, 0, stream, index_q, index_k, t, lse_index, wrow, ws, diq_part,
+                       dik_group, D);
+  else
+    hipLaunchKernelGGL(k_kl_bwd_t<64>, grid, block, 0, stream, index_q, index_k, t, lse_index, wrow, ws, diq_part,
+                       dik_group, D);
   const int64_t n_ik = (int64_t)D.B * D.n_kv * (D.d_idx / 4);
   hipLaunchKernelGGL(k_kl_bwd_dik, dim3((unsigned)((n_ik + 255) / 256)), dim3(256), 0, stream, dik_group, d_index_k, D);
   const int64_t n_iq = (int64_t)D.B * D.h_kv * D.n_q * (D.d_idx / 8);

@@ -22,7 +22,9 @@
 // in-lane sum plus one exchange.  Z is formed for every head row (the rows of a
 // position read the same index-query row), which keeps it in S's layout.  Each
 // (row, slot) gets a partial {sum p log2 p, sum p z, max z log2 e, sum 2^(z log2 e
-// - max)}; a merge adds a row's partials.
+// - max)}; a merge adds a row's partials.  Optionally the teacher itself is
+// stored, one fp16 value per (row, slot, key of the block), for a backward
+// that reads it instead of forming S again.
 #include "attn_tiles.h"
 
 namespace msa {
@@ -300,7 +302,7 @@ template <int DIDX, int G, bool LOCAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_kl_tiles(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ iq,
     const uint16_t* __restrict__ ik, const float* __restrict__ lse, AttnWs ws, float4* __restrict__ kl_part,
-    Dims D) {
+    _Float16* __restrict__ teacher, Dims D) {
   using PM = PosMap<G>;
   constexpr int IKP = DIDX + 8;
   __shared__ __align__(16) uint16_t Ks[kBk * KP];
@@ -388,6 +390,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       fetch_q_rows(qw, q_src(nxt), lane);
       lse_raw = lse_of(nxt);
       teacher_probs<G, LOCAL>(sc, lse2, lim, c, P);
+    }
+    if (teacher) {  // uniform
+      // P[T][j] at key 32T + col of the position's (row, slot); for G >= 8
+      // both halves hold the same values and split the four key ranges
+#pragma unroll
+      for (int j = 0; j < PM::NPL; ++j) {
+        if (!pv[j]) continue;
+        _Float16* dst = teacher + (((int64_t)cur.bg * D.n_q + pi[j]) * (D.k + 1) + pslot[j]) * kBk + col;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+          if (G == 4 || (T >> 1) == half) dst[32 * T] = (_Float16)P[T][j];
+      }
     }
     KlAcc acc[PM::NPL];
     {
@@ -597,17 +611,18 @@ bool kl_supported(const Dims& D) {
 }
 
 hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,
-                           const int32_t* block_idx, const float* lse, float* kl, float* lse_index, const AttnWs& ws,
-                           float4* kl_part, const Dims& D, hipStream_t stream) {
+                           const int32_t* block_idx, const float* lse, float* kl, float* lse_index, uint16_t* teacher,
+                           const AttnWs& ws, float4* kl_part, const Dims& D, hipStream_t stream) {
   hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
   if (e != hipSuccess) return e;
   const dim3 grid(persistent_grid()), block(kThreads);
   auto go = [&](auto didx, auto g) {
     constexpr int DI = decltype(didx)::value, GG = decltype(g)::value;
+    _Float16* t = reinterpret_cast<_Float16*>(teacher);
     hipLaunchKernelGGL((k_kl_tiles<DI, GG, false>), grid, block, 0, stream, q, k, index_q, index_k, lse, ws,
-                       kl_part, D);
+                       kl_part, t, D);
     hipLaunchKernelGGL((k_kl_tiles<DI, GG, true>), grid, block, 0, stream, q, k, index_q, index_k, lse, ws, kl_part,
-                       D);
+                       t, D);
   };
   using I128 = std::integral_constant<int, 128>;
   using I64 = std::integral_constant<int, 64>;

@@ -55,19 +55,29 @@ hipError_t launch_attn_kernels(const uint16_t* q, const void* k, const void* v, 
 // KL alignment of the index branch to the main branch's group-averaged
 // attention over the selected tokens (needs the forward's lse); kl_part holds
 // one float4 per (row, slot).  Supported for G in {4, 8, 16, 32}, bf16 index
-// inputs and uniform batches.
+// inputs and uniform batches.  teacher (optional): fp16 [B][H_kv][n_q][k+1][kBk],
+// the teacher's weight of each key of each (row, slot) that the row uses.
 bool kl_supported(const Dims& D);
 hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,
-                           const int32_t* block_idx, const float* lse, float* kl, float* lse_index, const AttnWs& ws,
-                           float4* kl_part, const Dims& D, hipStream_t stream);
+                           const int32_t* block_idx, const float* lse, float* kl, float* lse_index, uint16_t* teacher,
+                           const AttnWs& ws, float4* kl_part, const Dims& D, hipStream_t stream);
 
-// Main-branch backward over the forward's selection: dq, dk, dv (bf16) from
-// dout, out and lse; dq_part holds one bf16 partial per (row, slot, head),
-// delta the per-(row, head) dO . O.
+// KL backward into the index branch: d_index_q, d_index_k (bf16); diq_part
+// holds one bf16 partial per (row, slot), dik_group each group's fp32 share.
+// The first form forms the teacher again from q, k and lse; the second reads
+// the one launch_index_kl stored.
 hipError_t launch_index_kl_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,
                                const int32_t* block_idx, const float* lse, const float* lse_index, const float* wrow,
                                uint16_t* d_index_q, uint16_t* d_index_k, const AttnWs& ws, uint16_t* diq_part,
                                float* dik_group, const Dims& D, hipStream_t stream);
+hipError_t launch_index_kl_bwd_teacher(const uint16_t* index_q, const uint16_t* index_k, const int32_t* block_idx,
+                                       const uint16_t* teacher, const float* lse_index, const float* wrow,
+                                       uint16_t* d_index_q, uint16_t* d_index_k, const AttnWs& ws,
+                                       uint16_t* diq_part, float* dik_group, const Dims& D, hipStream_t stream);
+
+// Main-branch backward over the forward's selection: dq, dk, dv (bf16) from
+// dout, out and lse; dq_part holds one bf16 partial per (row, slot, head),
+// delta the per-(row, head) dO . O.
 hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* block_idx,
                                   const uint16_t* out, const float* lse, const uint16_t* dout, uint16_t* dq,
                                   uint16_t* dk, uint16_t* dv, const AttnWs& ws, uint16_t* dq_part, float* delta,

@@ -245,6 +245,36 @@ msa_status msa_index_kl_bwd(const msa_problem* p, const void* q, const void* k, 
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * msa_index_kl, and the teacher kept for the backward: teacher (fp16,
+ * [B][H_kv][n_q][k+1][Bk], caller-allocated, MSA_TEACHER_BYTES(p) bytes)
+ * receives t_j of every key of every block a row uses: element
+ * [b][g][i][s][j % Bk] for the block in slot s of block_idx[b][g][i] (s = k:
+ * the local block), 0 for keys outside T.  Entries of slots the row does not
+ * use (-1, or the local block listed again) are left as they were.  lse_index
+ * is required here.  Same support and workspace as msa_index_kl; kl and
+ * lse_index are the values msa_index_kl writes.
+ */
+#define MSA_TEACHER_BYTES(p) \
+  ((size_t)(p)->batch * (p)->h_kv * (p)->n_q * ((p)->topk + 1) * (p)->block_size * 2)
+msa_status msa_index_kl_teacher(const msa_problem* p, const void* q, const void* k, const void* index_q,
+                                const void* index_k, const int32_t* block_idx, const float* lse, float* kl,
+                                float* lse_index, void* teacher, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * msa_index_kl_bwd from the teacher msa_index_kl_teacher kept (for the same
+ * block_idx, and with its lse_index): the same g_j, d_index_q and d_index_k
+ * with t_j read instead of formed from q, k and lse, so no Main Branch input
+ * is read.  t_j enters as the fp16 value stored (relative error 2^-11).  Same
+ * support, workspace (MSA_OP_INDEX_KL_BWD) and reproducibility as
+ * msa_index_kl_bwd.
+ */
+msa_status msa_index_kl_bwd_teacher(const msa_problem* p, const void* index_q, const void* index_k,
+                                    const int32_t* block_idx, const void* teacher, const float* lse_index,
+                                    const float* dkl, void* d_index_q, void* d_index_k, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Backward of msa_sparse_attn_fwd: the gradients the language-model loss sends
  * into the Main Branch (section MSA 如何训练), over the same token sets T as
  * the forward (block_idx as the forward used it, the local block always in).

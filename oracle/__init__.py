@@ -57,8 +57,11 @@ def _L():
                                           _f64, _u16p, _f64p, _f64p, _f64p]
         lib.oracle_kl_bwd.argtypes = [_u16p, _i64, _i64p, _i32p, _i32, _i32, _u16p, _i64, _i32, _u16p, _u16p, _i32,
                                       _i32, _f64, _f64p, _f64p, _f64p]
+        lib.oracle_kl_teacher.argtypes = [_u16p, _i64, _i64p, _i32p, _i32, _i32, _u16p, _i64, _i32, _i32, _f64,
+                                           _f64p]
         for f in (lib.oracle_pool, lib.oracle_select, lib.oracle_attend, lib.oracle_dense_gqa, lib.oracle_merge,
-                  lib.oracle_e4m3_decode, lib.oracle_pool_f8, lib.oracle_kl, lib.oracle_attend_bwd, lib.oracle_kl_bwd):
+                  lib.oracle_e4m3_decode, lib.oracle_pool_f8, lib.oracle_kl, lib.oracle_attend_bwd, lib.oracle_kl_bwd,
+                  lib.oracle_kl_teacher):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -233,6 +236,18 @@ def kl(q_rows, pos, sel, K, iq_rows, ik, bk: int, scale: float) -> np.ndarray:
     out = np.empty(n)
     _check(_L().oracle_kl(q_rows, n, pos, sel, sel.shape[1], G, K, K.shape[0], d, iq_rows, ik, iq_rows.shape[1], bk,
                           scale, out), "oracle_kl")
+    return out
+
+
+def kl_teacher(q_rows, pos, sel, K, bk: int, scale: float) -> np.ndarray:
+    """The teacher of kl() per row as a dense [n, n_kv] array (0 outside T)."""
+    q_rows, K = _u16(q_rows), _u16(K)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    n, G, d = q_rows.shape
+    out = np.empty((n, K.shape[0]))
+    _check(_L().oracle_kl_teacher(q_rows, n, pos, sel, sel.shape[1], G, K, K.shape[0], d, bk, scale, out),
+           "oracle_kl_teacher")
     return out
 
 

@@ -323,6 +323,53 @@ int oracle_kl(const uint16_t* q, int64_t nrows, const int64_t* pos, const int32_
 }
 
 /*
+ * The teacher of oracle_kl on its own (the distribution the KL backward
+ * holds fixed): teach[r][j] = (1/G) sum_h softmax_j(scale * q_h . k_j) for j
+ * in T, 0 for every other key.  Rows as in oracle_kl -> teach [nrows][n_kv].
+ */
+int oracle_kl_teacher(const uint16_t* q, int64_t nrows, const int64_t* pos, const int32_t* sel, int32_t k, int32_t G,
+                      const uint16_t* K, int64_t n_kv, int32_t d, int32_t bk, double scale, double* teach) {
+  if (nrows < 0 || k < 1 || G < 1 || d <= 0 || bk <= 0) return -1;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (pos[r] < 0 || pos[r] >= n_kv) return -1;
+  const int64_t n_blk = (n_kv + bk - 1) / bk;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t p = pos[r];
+    double* tr = teach + r * n_kv;
+    for (int64_t j = 0; j < n_kv; ++j) tr[j] = 0.0;
+    int32_t* blocks = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    memcpy(blocks, sel + r * k, sizeof(int32_t) * (size_t)k);
+    qsort(blocks, (size_t)k, sizeof(int32_t), int_order);
+    int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)k * (size_t)bk);
+    int64_t nt = 0;
+    for (int32_t s = 0; s < k; ++s) {
+      const int32_t t = blocks[s];
+      if (t < 0 || t >= n_blk || (s > 0 && t == blocks[s - 1])) continue;
+      for (int64_t j = (int64_t)t * bk; j < ((int64_t)t + 1) * bk && j < n_kv && j <= p; ++j) tok[nt++] = j;
+    }
+    double* w = (double*)malloc(sizeof(double) * (size_t)(nt > 0 ? nt : 1));
+    for (int32_t h = 0; h < G; ++h) {
+      const uint16_t* qh = q + (r * G + h) * d;
+      double m = -INFINITY;
+      for (int64_t a = 0; a < nt; ++a) {
+        double dot = 0.0;
+        for (int32_t c = 0; c < d; ++c) dot += bf(qh[c]) * bf(K[tok[a] * d + c]);
+        w[a] = scale * dot;
+        if (w[a] > m) m = w[a];
+      }
+      double l = 0.0;
+      for (int64_t a = 0; a < nt; ++a) l += exp(w[a] - m);
+      for (int64_t a = 0; a < nt; ++a) tr[tok[a]] += exp(w[a] - m) / l / G;
+    }
+    free(w);
+    free(tok);
+    free(blocks);
+  }
+  return 0;
+}
+
+/*
  * Gradient of the KL alignment term with respect to the index projections'
  * outputs, the teacher held fixed (page "MiniMax 发布 MSA…", section MSA 如何训练:
  * gradient detach stops the KL gradient at the Index Branch's inputs, so it

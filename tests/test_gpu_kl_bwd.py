@@ -16,6 +16,13 @@ are exact bf16, sums run in fp32 and the results (and the d_index_q partials)
 are rounded to bf16: an element is off by about 2^-8 of the magnitude of the
 terms it sums.  The bound is the one of the attention backward: 2e-2 of the
 tensor's largest |value| for every element, 2e-3 of it on average.
+
+The stored-teacher pair (msa_index_kl_teacher, msa_index_kl_bwd_teacher): the
+KL pass with the teacher kept writes the same kl and lse_index bits as
+msa_index_kl; every stored weight of every used (row, slot) matches the
+oracle's teacher (oracle_kl_teacher) to fp16 rounding (2^-11 relative) plus
+the fp32 lse's error, and keys outside T hold 0; the backward from the stored
+teacher meets the same bound against oracle_kl_bwd as msa_index_kl_bwd.
 """
 import numpy as np
 import pytest
@@ -136,3 +143,128 @@ def test_kl_backward_is_deterministic():
     _, b_iq, b_ik = run_kl_bwd(w, res)
     assert torch.equal(a_iq.view(torch.int16), b_iq.view(torch.int16))
     assert torch.equal(a_ik.view(torch.int16), b_ik.view(torch.int16))
+
+
+# ---------------------------------------------------------------- stored teacher
+TEACHER_REL, TEACHER_ABS = 1e-3, 1e-7
+
+
+def run_kl_teacher(w, res):
+    import torch
+    p = problem(w)
+    x = res["inputs"]
+    kl = torch.empty((w.batch, w.h_kv, w.n_q), dtype=torch.float32, device="cuda")
+    lse_index = torch.full_like(kl, float("nan"))
+    teacher = torch.full(msa.teacher_shape(p), float("nan"), dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(msa.workspace_size(p, msa.OP_INDEX_KL), 256), dtype=torch.uint8, device="cuda")
+    msa.index_kl_teacher(p, x["q"], x["k"], x["iq"], x["ik"], res["block_idx"], res["lse"], kl, lse_index, teacher,
+                         ws)
+    torch.cuda.synchronize()
+    return kl, lse_index, teacher
+
+
+def run_kl_bwd_teacher(w, res, teacher, lse_index, dkl=None):
+    import torch
+    p = problem(w)
+    x = res["inputs"]
+    d_iq = torch.full_like(x["iq"], float("nan"))
+    d_ik = torch.full_like(x["ik"], float("nan"))
+    ws = torch.empty(msa.workspace_size(p, msa.OP_INDEX_KL_BWD), dtype=torch.uint8, device="cuda")
+    msa.index_kl_bwd_teacher(p, x["iq"], x["ik"], res["block_idx"], teacher, lse_index, d_iq, d_ik, dkl=dkl,
+                             workspace=ws)
+    torch.cuda.synchronize()
+    return d_iq, d_ik
+
+
+def used_slots(sel_row, local, k):
+    """Slots of a row the kernels use: listed non-local blocks (first of equal
+    neighbours) and slot k for the local block."""
+    out = [(s, int(t)) for s, t in enumerate(sel_row) if 0 <= t < local and (s == 0 or sel_row[s - 1] != t)]
+    return out + [(k, local)]
+
+
+def check_teacher(w, teacher_bg, ref, sel, rows):
+    """teacher_bg [n_q, k+1, Bk] (fp32 of the stored fp16) against the oracle's
+    dense teacher ref [len(rows), n_kv] over every used (row, slot)."""
+    bk = w.block_size
+    worst = 0.0
+    for r, i in enumerate(rows):
+        local = (w.offset + int(i)) // bk
+        for s, t in used_slots(sel[i], local, w.topk):
+            keys = t * bk + np.arange(bk)
+            got = teacher_bg[i, s]
+            inside = keys < w.n_kv
+            want = np.zeros(bk)
+            want[inside] = ref[r, keys[inside]]
+            err = np.abs(got - want)
+            assert np.all(np.isfinite(got)), (i, s)
+            bad = np.nonzero(err > TEACHER_REL * want + TEACHER_ABS)[0]
+            assert bad.size == 0, (int(i), s, int(t), [(int(j), float(got[j]), float(want[j])) for j in bad[:6]])
+            worst = max(worst, float((err / (want + TEACHER_ABS)).max()))
+    return worst
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_stored_teacher_and_its_backward_match_oracle(w):
+    import torch
+    say(f"[gpu] stored teacher {w.name}: B={w.batch} n_q={w.n_q} n_kv={w.n_kv} h={w.h_q}/{w.h_kv} "
+        f"d_idx={w.index_dim} k={w.topk}")
+    res = run_gpu(w, with_forward=False)
+    lz0, _, _ = run_kl_bwd(w, res)
+    kl, lse_index, teacher = run_kl_teacher(w, res)
+    assert torch.equal(lse_index, lz0), "the teacher-keeping pass gives the same lse_index bits"
+    dkl = None
+    if w.name in WEIGHTED:
+        gen = torch.Generator().manual_seed(w.seed)
+        dkl = (torch.rand((w.batch, w.h_kv, w.n_q), generator=gen) * 2 - 0.5).cuda()
+    d_iq, d_ik = run_kl_bwd_teacher(w, res, teacher, lse_index, dkl)
+    tf = teacher.float().cpu().numpy()
+    rows = np.arange(w.n_q)
+    for b in range(w.batch):
+        ref_ik = None
+        for g in range(w.h_kv):
+            x = oracle.inputs_for_rows(w, b, g, rows)
+            sel = res["block_idx"][b, g].cpu().numpy()
+            K = synth.host_kv(w, "k", b, g, 0, w.n_kv)
+            ref_t = oracle.kl_teacher(x["q"], x["pos"], sel, K, w.block_size, w.scale)
+            worst = check_teacher(w, tf[b, g], ref_t, sel, rows)
+            say(f"    teacher b{b} g{g}: worst relative error {worst:.2e}")
+            wr = None if dkl is None else dkl[b, g].double().cpu().numpy()
+            r_iq, r_ik = oracle.kl_bwd(x["q"], x["pos"], sel, K, x["iq"], x["ik"], w.block_size, w.scale, wr)
+            close(f"d_iq b{b} g{g}", as_float(d_iq[b][:, g]), r_iq)
+            ref_ik = r_ik if ref_ik is None else ref_ik + r_ik
+        got_ik = as_float(d_ik[b])
+        n_seen = ref_ik.shape[0]
+        close(f"d_ik b{b}", got_ik[:n_seen], ref_ik)
+        assert np.all(got_ik[n_seen:] == 0.0), "keys past every row's position must get 0"
+
+
+def test_stored_teacher_32k_sampled_sum_rule_and_determinism():
+    import torch
+    w = synth.WORKLOADS["prefill_32k"]
+    say(f"[gpu] stored teacher {w.name}")
+    res = run_gpu(w, with_forward=False)
+    _, lse_index, teacher = run_kl_teacher(w, res)
+    d_iq, d_ik = run_kl_bwd_teacher(w, res, teacher, lse_index)
+    rows = sample_rows(w, 32, seed=w.seed + 1, whole_blocks=0)
+    tf = teacher.float().cpu().numpy()
+    for g in range(w.h_kv):
+        x = oracle.inputs_for_rows(w, 0, g, rows)
+        sel_all = res["block_idx"][0, g].cpu().numpy()
+        sel = sel_all[rows]
+        K, _ = oracle.kv_for_blocks(w, 0, g, sel)
+        r_iq, _ = oracle.kl_bwd(x["q"], x["pos"], sel, K, x["iq"], x["ik"], w.block_size, w.scale)
+        got = as_float(d_iq[0].index_select(0, torch.from_numpy(rows).cuda())[:, g])
+        close(f"d_iq g{g}", got, r_iq)
+        if g == 0:
+            ref_t = oracle.kl_teacher(x["q"], x["pos"], sel, K, w.block_size, w.scale)
+            worst = check_teacher(w, tf[0, g], ref_t, sel_all, rows)
+            say(f"    teacher g0 (sampled rows): worst relative error {worst:.2e}")
+    dik = d_ik[0].view(torch.bfloat16).float()
+    total, mag = dik.sum(dim=0), dik.abs().sum(dim=0)
+    say(f"    sum rule: max |sum_j d_ik_j| / sum_j |d_ik_j| = {(total.abs() / mag).max().item():.2e}")
+    assert bool(torch.isfinite(dik).all())
+    assert bool((total.abs() <= 1e-2 * mag).all())
+    a_iq, a_ik = run_kl_bwd_teacher(w, res, teacher, lse_index)
+    assert torch.equal(a_iq.view(torch.int16), d_iq.view(torch.int16))
+    assert torch.equal(a_ik.view(torch.int16), d_ik.view(torch.int16))

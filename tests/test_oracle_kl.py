@@ -12,6 +12,10 @@ softmax of the raw index scores over the same tokens.  Pins:
   - invariance to the order of the group's heads and to a shift of every
     student logit;
   - torch's softmax and kl_div on the same tokens (a library computation).
+The teacher on its own (oracle_kl_teacher, which the stored-teacher backward
+is checked against): a hand-worked row, the weights of a row summing to 1 over
+T and 0 elsewhere, torch's head-averaged softmax, and the KL rebuilt from it
+and the student equal to oracle_kl.
 """
 import math
 
@@ -133,6 +137,51 @@ def test_matches_torch_softmax_and_kl_div(seed):
         log_student = torch.log_softmax(IQ[r] @ IK[idx].T, dim=-1)
         want = torch.nn.functional.kl_div(log_student, teacher, reduction="sum").item()
         assert abs(got[r] - want) < 1e-12 * max(1.0, abs(want))
+
+
+def test_teacher_by_hand():
+    # the two-token row of test_two_tokens_by_hand: weights (1/4, 3/4); a third key
+    # past the position gets 0
+    q = bf16_bits([[[1.0, 0.0]]])
+    K = bf16_bits([[0.0, 1.0], [1.0, 0.0], [1.0, 1.0]])
+    t = oracle.kl_teacher(q, [1], np.array([[0, 1]], np.int32), K, 2, math.log(3.0))
+    assert np.allclose(t[0], [0.25, 0.75, 0.0], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_teacher_sums_to_one_and_matches_torch(seed):
+    rng = np.random.default_rng(400 + seed)
+    n_kv, d, di, bk, G, k, n = 96, 16, 16, 8, 4, 3, 12
+    q, K = rand_bits(rng, (n, G, d)), rand_bits(rng, (n_kv, d))
+    iq, ik = rand_bits(rng, (n, di)), rand_bits(rng, (n_kv, di))
+    pos = rng.integers(0, n_kv, size=n)
+    sel = []
+    for p in pos:
+        loc = p // bk
+        others = sorted(rng.choice(loc, size=min(k - 1, loc), replace=False).tolist()) if loc else []
+        row = sorted(others + [loc])
+        sel.append(row + [-1] * (k - len(row)))
+    sel = np.array(sel, np.int32)
+    scale = 1.0 / math.sqrt(d)
+    t = oracle.kl_teacher(q, pos, sel, K, bk, scale)
+    kl = oracle.kl(q, pos, sel, K, iq, ik, bk, scale)
+    f = lambda b: torch.from_numpy(synth.bf16_to_f32(b).astype(np.float64))
+    Qt, Kt, IQ, IK = f(q), f(K), f(iq), f(ik)
+    for r in range(n):
+        toks = [j for tb in sel[r] if tb >= 0 for j in range(tb * bk, min((tb + 1) * bk, n_kv)) if j <= pos[r]]
+        outside = np.ones(n_kv, bool)
+        outside[toks] = False
+        assert np.all(t[r][outside] == 0.0)
+        assert abs(t[r].sum() - 1.0) < 1e-13
+        idx = torch.tensor(toks)
+        want = torch.softmax(scale * Qt[r] @ Kt[idx].T, dim=-1).mean(dim=0).numpy()
+        assert np.allclose(t[r][toks], want, rtol=1e-13, atol=1e-16)
+        # kl = sum t ln t - sum t z + ln sum exp z over T, with the teacher above
+        z = (IQ[r] @ IK[idx].T).numpy()
+        tt = t[r][toks]
+        nz = tt > 0
+        rebuilt = np.sum(tt[nz] * np.log(tt[nz])) - np.sum(tt * z) + (z.max() + np.log(np.exp(z - z.max()).sum()))
+        assert abs(rebuilt - kl[r]) < 1e-12 * max(1.0, abs(kl[r]))
 
 
 # ---------------------------------------------------------------- gradient (teacher detached)
