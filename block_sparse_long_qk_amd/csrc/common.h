@@ -181,13 +181,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+// x of lane l ^ 32 (v_permlane32_swap: the upper 32 lanes of one copy of x
+// trade places with the lower 32 of another; no LDS round trip).
+__device__ __forceinline__ float wave_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // {x of lanes 0-31, x of lanes 32-63}
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 // Reduction over the 32 lanes of each half-wave with DPP moves inside rows of
 // 16 lanes (xor 1 and xor 2 by quad permutes, then the half-row and row
-// mirrors), after which every lane of a row holds its row's total, and four
-// lane reads that combine the two rows of each half.  No LDS round trip; every
-// lane of a half gets the same value (from lanes 0 and 16, or 32 and 48).
+// mirrors), after which every lane of a row holds its row's total, and one
+// row swap that combines the two rows of each half.  No LDS round trip; every
+// lane of a half gets the same value (op is commutative and exact in either
+// order).
 // Needs all 64 lanes active.
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
@@ -209,12 +216,13 @@ __device__ __forceinline__ float half_reduce(float x, Op op) {
   x = op(x, dpp_move<0x4E>(x));   // quad_perm [2, 3, 0, 1]
   x = op(x, dpp_move<0x141>(x));  // row_half_mirror
   x = op(x, dpp_move<0x140>(x));  // row_mirror
-  const int xi = __builtin_bit_cast(int, x);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
-  return (threadIdx.x & 32) ? op(r2, r3) : op(r0, r1);
+  // the other row of the half: v_permlane16_swap trades the odd rows of one
+  // copy of x with the even rows of another ({rows 0, 0, 2, 2} and {rows 1,
+  // 1, 3, 3}); each lane takes the one that is not its own row (a select: the
+  // compiler is known to mistake the two results for one when both feed one op)
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return op(x, __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]));
 }
 __device__ __forceinline__ float half_max(float x) {
   return half_reduce(x, [](float a, float b) { return fmaxf(a, b); });

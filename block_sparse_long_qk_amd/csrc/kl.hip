@@ -25,7 +25,7 @@
 // - max)}; a merge adds a row's partials.  Optionally the teacher itself is
 // stored, one fp16 value per (row, slot, key of the block), for a backward
 // that reads it instead of forming S again.
-#include "attn_tiles.h"
+#include "fwd_tiles.h"
 
 namespace msa {
 namespace {
@@ -428,6 +428,337 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the last (unused) row fetch has landed before the workgroup ends
 }
 
+// ---------------------------------------------------------------- four-wave tiles
+// The same partials from four-wave workgroups on the forward's 128-row tiles
+// (pt * G = 128) and its dynamic per-XCD runs: each wave's query rows stay in
+// VGPRs (the next tile's loaded into the other register set while the current
+// one is computed), K and the index keys of a block arrive by direct
+// global-to-LDS loads, and Z is formed per position, not per head row: a
+// 16x16x32 product whose 16 M rows repeat the wave's 32 / G positions, so
+// that lane (key n, k-group c) holds Z of the positions its S registers
+// hold (see zpos), for the key the lane's S column is.
+
+// K (swizzled as in stage_kv_fwd) and the index keys (row r at r * 2 DIDX
+// bytes, its chunk c in slot c ^ (r % CPI)) of one block, by direct loads:
+// each wave issues 8 one-KB instructions of each.  Keys at or past n_valid
+// repeat key n_valid - 1.  The caller waits for vmcnt(0) and a barrier.
+template <int DIDX>
+__device__ __forceinline__ void stage_k_ik4(unsigned char* Ks, unsigned char* IKs, const uint16_t* k,
+                                            const uint16_t* ik, int64_t k0, int64_t ik0, int n_valid) {
+  constexpr int CPI = DIDX / 8;
+  constexpr int KPI = 64 / CPI;  // index keys per instruction
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // addresses formed at each staging, not kept live along the walk
+  const int wave = tid >> 6, lane = tid & 63;
+  const unsigned char* kb = reinterpret_cast<const unsigned char*>(k + k0);
+  const unsigned char* ib = reinterpret_cast<const unsigned char*>(ik + ik0);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int g = 8 * wave + u;
+    const int row = 4 * g + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 15);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kb + (int64_t)min(row, n_valid - 1) * 256 + 16 * c),
+                                     (__attribute__((address_space(3))) void*)(Ks + 1024 * g), 16, 0, 0);
+  }
+  constexpr int NIK = kBk * CPI / 64 / kFWaves;  // index-key instructions per wave
+#pragma unroll
+  for (int u = 0; u < NIK; ++u) {
+    const int g = NIK * wave + u;
+    const int key = KPI * g + lane / CPI;
+    const int c = (lane % CPI) ^ (key % CPI);
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const void*>(ib + (int64_t)min(key, n_valid - 1) * (2 * DIDX) + 16 * c),
+        (__attribute__((address_space(3))) void*)(IKs + 1024 * g), 16, 0, 0);
+  }
+}
+
+// S = Q K^T with the query rows (registers, load_q's layout) as the A
+// operand and K (swizzled LDS) as B: s[T] holds keys 32T .. 32T+31, lane
+// column = key, register e = query row 8(e/4) + 4 half + e%4 of the wave.
+// Same operands, order and accumulation as q_k_scores.
+__device__ __forceinline__ void qk_rows(const unsigned char* Ks, const uint4 (&qf)[8], int lane, f32x16 (&s)[4]) {
+  const int col = lane & 31, half = lane >> 5;
+  const unsigned char* kbase = Ks + col * 256;
+  const int sw = col & 15;
+  uint4 kf[2][4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) kf[0][T] = *reinterpret_cast<const uint4*>(kbase + 32 * T * 256 + 16 * (half ^ sw));
+#pragma unroll
+  for (int T = 0; T < 4; ++T) s[T] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int cb = ks & 1, nb = cb ^ 1;
+    if (ks + 1 < 8) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+        kf[nb][T] = *reinterpret_cast<const uint4*>(kbase + 32 * T * 256 + 16 * ((2 * (ks + 1) + half) ^ sw));
+    }
+#pragma unroll
+    for (int T = 0; T < 4; ++T) s[T] = mfma_32x32x16(qf[ks], kf[cb][T], s[T]);
+  }
+}
+
+typedef __bf16 bf16x8k __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma16k(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8k, a), __builtin_bit_cast(bf16x8k, b), c,
+                                                 0, 0, 0);
+}
+
+// Wave-local position of row m of the Z product: lane (n, c) gets rows 4c + i,
+// and its S registers hold lane-local positions j = i (PosMap::wpos(j, half),
+// with c = 2 half + (column >= 16)).
+template <int G>
+__device__ __forceinline__ int zpos(int m) {
+  constexpr int NP = 32 / G;
+  if constexpr (G == 4) return (m >> 3) + 2 * (m & 3);
+  return min(m & 3, NP - 1);
+}
+
+// z[T][j]: Z = IQ IK^T of lane-local position j and the lane's key 32T + col,
+// from the wave's index-query rows in LDS (row p at p * 2 DIDX, chunk c in
+// slot c ^ (p % CPI)) and the staged index keys.
+template <int DIDX, int G>
+__device__ __forceinline__ void z_scores(const unsigned char* IKs, const unsigned char* iqw, int lane,
+                                         float (&z)[4][PosMap<G>::NPL]) {
+  constexpr int CPI = DIDX / 8, IKS = DIDX / 32;
+  const int n = lane & 15, cg = lane >> 4;
+  const int pm = zpos<G>(n);
+  uint4 a[IKS];
+#pragma unroll
+  for (int ks = 0; ks < IKS; ++ks)
+    a[ks] = *reinterpret_cast<const uint4*>(iqw + pm * (2 * DIDX) + 16 * ((4 * ks + cg) ^ (pm % CPI)));
+  f32x4 zt[8];
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
+    const int key = 16 * kt + n;
+    zt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < IKS; ++ks) {
+      const uint4 b = *reinterpret_cast<const uint4*>(IKs + key * (2 * DIDX) + 16 * ((4 * ks + cg) ^ (key % CPI)));
+      zt[kt] = mfma16k(a[ks], b, zt[kt]);
+    }
+  }
+  const bool hi = (lane & 16) != 0;  // the lane's key 32T + col lies in key tile 2T + (col >= 16)
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+#pragma unroll
+    for (int j = 0; j < PosMap<G>::NPL; ++j) z[T][j] = hi ? zt[2 * T + 1][j] : zt[2 * T][j];
+  }
+}
+
+// student_tile with Z per lane-local position.
+template <int G, bool MASKED>
+__device__ __forceinline__ void student_tile_p(const float (&z)[4][PosMap<G>::NPL],
+                                               const float (&P)[4][PosMap<G>::NPL],
+                                               const int (&lim)[PosMap<G>::NPL], KlAcc (&out)[PosMap<G>::NPL]) {
+  using PM = PosMap<G>;
+  const float NEG_INF = -__builtin_huge_valf();
+#pragma unroll
+  for (int j = 0; j < PM::NPL; ++j) {
+    auto visible = [&](int T) { return 32 * T <= lim[j]; };
+    float m = NEG_INF;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+      if (visible(T)) m = fmaxf(m, z[T][j] * kLog2e);
+    m = half_max(m);
+    float a = 0.f, b = 0.f, l = 0.f;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const float zz = z[T][j], p = P[T][j];
+      if (p > 0.f) a += p * __log2f(p);
+      b += p * zz;
+      if (visible(T)) l += __builtin_amdgcn_exp2f(zz * kLog2e - m);
+    }
+    out[j] = KlAcc{half_sum(a), half_sum(b), m, half_sum(l)};
+  }
+}
+
+template <int DIDX, int G, bool LOCAL>
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_kl_tiles4(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ iq,
+    const uint16_t* __restrict__ ik, const float* __restrict__ lse, AttnWs ws, float4* __restrict__ kl_part,
+    _Float16* __restrict__ teacher, Dims D) {
+  using PM = PosMap<G>;
+  constexpr int NP = 32 / G;             // positions per wave
+  constexpr int CPI = DIDX / 8;          // 16-byte chunks of an index row
+  constexpr int IQB = NP * 2 * DIDX;     // bytes of one wave's index-query rows
+  constexpr int NPC = NP * CPI;          // their chunks
+  constexpr int NIQ = (NPC + 63) / 64;   // chunks per lane
+  __shared__ __align__(16) unsigned char Ks[kBk * 256];
+  __shared__ __align__(16) unsigned char IKs[kBk * 2 * DIDX];
+  __shared__ __align__(16) unsigned char IQs[kFWaves][2][IQB];
+  __shared__ __align__(16) float LSs[kFWaves][32];
+  __shared__ int2 runs[3];
+  const bool leader = threadIdx.x == 0;
+  RunQueue rq;
+  if (leader) {
+    if constexpr (LOCAL) rq.init(ws.ctr + kXcds, D.B * D.h_kv * local_tiles<false>(D));
+    else rq.init(ws.ctr, ws.tile_off[ws.n_bins]);
+    const int2 a = rq.claim();
+    runs[0] = a;
+    runs[1] = a.x >= 0 ? rq.claim() : make_int2(-1, -1);
+  }
+  lds_barrier();
+  int2 run = uniform2(runs[0]), nrun = uniform2(runs[1]);
+  if (run.x < 0) return;  // uniform over the workgroup
+  if (leader && nrun.x >= 0) rq.prefetch();
+  int ri = 0;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int r = wave * 32 + col;
+  const int ps = r / G, hh = r % G;
+  const float c = D.scale_log2;
+  auto q_ptr = [&](const TileRow& tr) {  // rows that do not exist read row 0 of the group
+    const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv, i = tr.valid ? tr.i : 0;
+    return q + (((int64_t)b * D.n_q + i) * D.h_q + g * G + hh) * kHeadDim;
+  };
+  auto lse_of = [&](const TileRow& tr) {
+    const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv, i = tr.valid ? tr.i : 0;
+    return lse[((int64_t)b * D.h_q + g * G + hh) * D.n_q + i];
+  };
+  // this lane's chunks of the wave's index-query rows of tile tr (position p's
+  // row from lane p G; rows that do not exist read row 0)
+  auto load_iq = [&](const TileRow& tr, uint4 (&x)[NIQ]) {
+    const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv;
+    const int i_mine = tr.valid ? tr.i : 0;
+#pragma unroll
+    for (int u = 0; u < NIQ; ++u) {
+      const int pc = min(lane + 64 * u, NPC - 1);
+      const int p = pc / CPI, ch = pc % CPI;
+      const int i = __shfl(i_mine, p * G, 64);
+      x[u] = *reinterpret_cast<const uint4*>(iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX + 8 * ch);
+    }
+  };
+  auto store_iq = [&](unsigned char* dst, const uint4 (&x)[NIQ]) {
+#pragma unroll
+    for (int u = 0; u < NIQ; ++u) {
+      const int pc = lane + 64 * u;
+      const int p = pc / CPI, ch = pc % CPI;
+      if (pc < NPC) *reinterpret_cast<uint4*>(dst + p * (2 * DIDX) + 16 * (ch ^ (p % CPI))) = x[u];
+    }
+  };
+  auto after = [&](int t, int t1) {  // as in k_attn_tiles
+    if (t1 < 0) return -1;
+    if (t + 1 < run.y) return t1 + 1 < run.y ? t1 + 1 : nrun.x;
+    return t1 + 1 < nrun.y ? t1 + 1 : -2;
+  };
+
+  int t = run.x;
+  TileRow cur = tile_row<LOCAL, false>(tile_raw<LOCAL>(ws, D, t, ps), D, ws, t, ps);
+  int t1 = t + 1 < run.y ? t + 1 : nrun.x;
+  TileRaw raw1 = t1 >= 0 ? tile_raw<LOCAL>(ws, D, t1, ps) : TileRaw{-1, 0};
+  uint4 qa[8], qb[8];
+  load_q(q_ptr(cur), half, qa);
+  float lse_cur = lse_of(cur);
+  {
+    uint4 x[NIQ];
+    load_iq(cur, x);
+    store_iq(IQs[wave][0], x);
+  }
+  int buf = 0;
+  int staged_bg = -1, staged_t = -1;
+  bool fresh = true;
+
+  auto step = [&](uint4 (&qc)[8], uint4 (&qn)[8]) -> bool {
+    if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform
+      if (!fresh) lds_barrier();                    // every wave is done with the staged block
+      const int b = cur.bg / D.h_kv, g = cur.bg % D.h_kv;
+      const int64_t k0 = (((int64_t)b * D.h_kv + g) * D.n_kv + (int64_t)cur.t * kBk) * kHeadDim;
+      const int64_t ik0 = ((int64_t)b * D.n_kv + (int64_t)cur.t * kBk) * DIDX;
+      stage_k_ik4<DIDX>(Ks, IKs, k, ik, k0, ik0, LOCAL ? max(1, min(kBk, D.n_kv - cur.t * kBk)) : kBk);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's direct loads have landed
+      lds_barrier();
+      staged_bg = cur.bg;
+      staged_t = cur.t;
+    }
+    fresh = false;
+    const bool last = t + 1 >= run.y;  // t ends its run (uniform)
+    if (leader && last && t1 >= 0) runs[(ri + 2) % 3] = rq.resolve();
+    // Z before S where that keeps the registers within two waves per SIMD
+    // (its 8 accumulator tiles are folded to the lane's values before S's are
+    // live); for d_idx 128 and G <= 8 after S and the next tile's loads,
+    // where that order does
+    constexpr bool kZFirst = !(DIDX == 128 && G <= 8);
+    float z[4][PM::NPL];
+    if constexpr (kZFirst) z_scores<DIDX, G>(IKs, IQs[wave][buf], lane, z);
+    f32x16 s[4];
+    qk_rows(Ks, qc, lane, s);
+    const bool more = t1 >= 0;  // uniform
+    TileRow nxt = cur;
+    if (more) nxt = tile_row<LOCAL, false>(raw1, D, ws, t1, ps);
+    uint4 xiq[NIQ];
+    float lse_nxt = 0.f;
+    if (more) {
+      load_q(q_ptr(nxt), half, qn);
+      load_iq(nxt, xiq);
+      lse_nxt = lse_of(nxt);
+    }
+    int t2 = after(t, t1);
+    TileRaw raw2{-1, 0};
+    if (t2 >= 0) raw2 = tile_raw<LOCAL>(ws, D, t2, ps);
+    if constexpr (!kZFirst) z_scores<DIDX, G>(IKs, IQs[wave][buf], lane, z);
+
+    float lse2[16];  // the lse of the 16 rows this lane's registers hold (+inf: no such row)
+    rows_lse(LSs[wave], cur.valid ? lse_cur * kLog2e : __builtin_huge_valf(), lane, lse2);
+    int lim[PM::NPL], pi[PM::NPL], pv[PM::NPL], pslot[PM::NPL];
+#pragma unroll
+    for (int j = 0; j < PM::NPL; ++j) {
+      pi[j] = pos_value<G>(cur.i, j, half);
+      pv[j] = pos_value<G>((int)cur.valid, j, half);
+      pslot[j] = pos_value<G>(cur.s, j, half);
+      lim[j] = key_limit<LOCAL>(pv[j], D.offset + pi[j], (int64_t)cur.t * kBk, col);
+    }
+    float P[4][PM::NPL];
+    teacher_probs<G, LOCAL>(s, lse2, lim, c, P);
+    if (teacher) {  // uniform; for G >= 8 both halves hold the same weights and split the key ranges
+#pragma unroll
+      for (int j = 0; j < PM::NPL; ++j) {
+        if (!pv[j]) continue;
+        _Float16* dst = teacher + (((int64_t)cur.bg * D.n_q + pi[j]) * (D.k + 1) + pslot[j]) * kBk + col;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+          if (G == 4 || (T >> 1) == half) dst[32 * T] = (_Float16)P[T][j];
+      }
+    }
+    KlAcc acc[PM::NPL];
+    student_tile_p<G, LOCAL>(z, P, lim, acc);
+#pragma unroll
+    for (int j = 0; j < PM::NPL; ++j) {
+      const bool writer = col == PM::wpos(j, half) * G && (G == 4 || half == 0);
+      if (writer && pv[j]) {
+        const int64_t row = (int64_t)cur.bg * D.n_q + pi[j];
+        kl_part[row * (D.k + 1) + pslot[j]] = make_float4(acc[j].a, acc[j].b, acc[j].m, acc[j].l);
+      }
+    }
+    if (!more) return false;
+    // the next tile's index-query rows into the other buffer (this wave's own
+    // region: its reads of this tile's rows, above, come first in LDS order)
+    buf ^= 1;
+    store_iq(IQs[wave][buf], xiq);
+    if (last) {  // t1 starts the next run
+      lds_barrier();
+      fresh = true;
+      run = nrun;
+      nrun = uniform2(runs[(ri + 2) % 3]);
+      ++ri;
+      if (leader && nrun.x >= 0) rq.prefetch();
+      if (t2 == -2) {  // the next run holds one tile: the one after it starts the run now known
+        t2 = nrun.x;
+        if (t2 >= 0) raw2 = tile_raw<LOCAL>(ws, D, t2, ps);
+      }
+    }
+    t = t1;
+    t1 = t2;
+    raw1 = raw2;
+    cur = nxt;
+    lse_cur = lse_nxt;
+    return true;
+  };
+  while (step(qa, qb) && step(qb, qa)) {
+  }
+}
+
 // One thread per (sequence, group, query): add the row's partials (the listed
 // non-local blocks and the local block, slot k) and form the KL value.
 __global__ __launch_bounds__(256) void k_kl_merge(const int32_t* __restrict__ block_idx,
@@ -613,16 +944,17 @@ bool kl_supported(const Dims& D) {
 hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t* index_q, const uint16_t* index_k,
                            const int32_t* block_idx, const float* lse, float* kl, float* lse_index, uint16_t* teacher,
                            const AttnWs& ws, float4* kl_part, const Dims& D, hipStream_t stream) {
-  hipError_t e = launch_gather_plan(block_idx, ws, D, stream);
+  const Dims F = fwd_attn_dims(D);  // 128-row tiles
+  hipError_t e = launch_gather_plan(block_idx, ws, F, stream);
   if (e != hipSuccess) return e;
-  const dim3 grid(persistent_grid()), block(kThreads);
+  const dim3 grid(2 * persistent_grid()), block(kFThreads);  // two four-wave workgroups per CU
   auto go = [&](auto didx, auto g) {
     constexpr int DI = decltype(didx)::value, GG = decltype(g)::value;
     _Float16* t = reinterpret_cast<_Float16*>(teacher);
-    hipLaunchKernelGGL((k_kl_tiles<DI, GG, false>), grid, block, 0, stream, q, k, index_q, index_k, lse, ws,
-                       kl_part, t, D);
-    hipLaunchKernelGGL((k_kl_tiles<DI, GG, true>), grid, block, 0, stream, q, k, index_q, index_k, lse, ws, kl_part,
-                       t, D);
+    hipLaunchKernelGGL((k_kl_tiles4<DI, GG, false>), grid, block, 0, stream, q, k, index_q, index_k, lse, ws,
+                       kl_part, t, F);
+    hipLaunchKernelGGL((k_kl_tiles4<DI, GG, true>), grid, block, 0, stream, q, k, index_q, index_k, lse, ws,
+                       kl_part, t, F);
   };
   using I128 = std::integral_constant<int, 128>;
   using I64 = std::integral_constant<int, 64>;

@@ -26,7 +26,7 @@
 // l % 32, so all softmax statistics of a row live in one lane pair (l, l ^ 32).
 #include <algorithm>
 
-#include "attn_tiles.h"
+#include "fwd_tiles.h"
 
 namespace msa {
 namespace {
@@ -207,24 +207,6 @@ __device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, fl
     for (int u = 0; u < 8; ++u)  // read once, by the merge: streamed past the caches
       __builtin_nontemporal_store(u32x4{w[u].x, w[u].y, w[u].z, w[u].w}, (gvec)(a + u * step));
   }
-}
-
-// The forward's tile workgroups are four waves (128 query rows per tile) and
-// hold only the K/V block in LDS (65 KB); each wave keeps its 32 query rows
-// in VGPRs.  Two such workgroups fill a CU, and one fits beside a scoring
-// workgroup, so the attention of one query pass can share CUs with the
-// scoring of the next.
-constexpr int kFWaves = 4;
-constexpr int kFThreads = 64 * kFWaves;
-constexpr int kFRows = 32 * kFWaves;
-constexpr int kFRun = 16;  // most tiles per claimed run
-
-// Lane (column, half) of a wave's MFMA operand for query row `row`: dims
-// 16 ks + 8 half .. + 7 of k-step ks, the order qk_block reads from LDS.
-__device__ __forceinline__ void load_q(const uint16_t* row, int half, uint4 (&qf)[8]) {
-  const uint16_t* p = row + 8 * half;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(p + 16 * ks);
 }
 
 // K/V staging of the forward kernels (kFThreads threads).  K rows are stored
@@ -448,55 +430,6 @@ __device__ __forceinline__ void softmax_pv_packed(const uint16_t* Vt, f32x16 (&s
   }
 }
 
-// Dynamic runs.  The tile range [0, total) is cut into kXcds slices; slice x
-// is first drained by the workgroups of XCD x (workgroup w runs on XCD
-// w % kXcds), which claim runs of consecutive tiles from the slice's
-// counter, so consecutive tiles (one K/V block as a rule) stay on one XCD's
-// L2.  A run is kFRun tiles, or fewer when the grid would otherwise get under
-// four runs per workgroup (short tile lists: a chunk of a long context).  A
-// workgroup whose slice is empty moves on to the next slices in turn.
-// Workgroups that start late, or share their CU with other work, simply
-// claim fewer runs.  Only thread 0 of a workgroup uses it.
-struct RunQueue {
-  int32_t* ctr;
-  int total, len, slice, left;  // len: tiles per run; left: slices not yet found empty
-  int pend;                // claimed run of `slice`, not yet resolved
-  __device__ void init(int32_t* c, int tot) {
-    ctr = c;
-    total = tot;
-    len = max(1, min(kFRun, tot / (int)(gridDim.x * 4)));
-    slice = blockIdx.x % kXcds;
-    left = kXcds;
-    pend = 0;
-  }
-  __device__ int2 range(int s, int run) const {
-    const int64_t lo = (int64_t)total * s / kXcds, hi = (int64_t)total * (s + 1) / kXcds;
-    const int64_t st = lo + (int64_t)run * len;
-    if (st >= hi) return make_int2(-1, -1);
-    return make_int2((int)st, (int)min<int64_t>(st + len, hi));
-  }
-  __device__ int2 claim() {  // waits for each counter it reads
-    while (left > 0) {
-      const int2 r = range(slice, atomicAdd(&ctr[slice], 1));
-      if (r.x >= 0) return r;
-      slice = (slice + 1) % kXcds;
-      --left;
-    }
-    return make_int2(-1, -1);
-  }
-  __device__ void prefetch() {  // a claim whose result is looked at later
-    if (left > 0) pend = atomicAdd(&ctr[slice], 1);
-  }
-  __device__ int2 resolve() {
-    if (left <= 0) return make_int2(-1, -1);
-    const int2 r = range(slice, pend);
-    if (r.x >= 0) return r;
-    slice = (slice + 1) % kXcds;
-    --left;
-    return claim();
-  }
-};
-
 // a + b, never fused with the product that formed a or b.  The tile step is
 // inlined twice (the two query register sets) and a tile runs through either
 // copy, so its base-2 lse m2 + log2(l) must not be contracted into an fma in
@@ -504,22 +437,6 @@ struct RunQueue {
 __device__ __forceinline__ float add_exact(float a, float b) {
 #pragma clang fp contract(off)
   return a + b;
-}
-
-__device__ __forceinline__ int2 uniform2(int2 x) {
-  return make_int2(__builtin_amdgcn_readfirstlane(x.x), __builtin_amdgcn_readfirstlane(x.y));
-}
-
-// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete,
-// then s_barrier.  lds_barrier() also fences global memory, which waits
-// for every outstanding global load and store (the next tile's query rows,
-// the partials just stored).  Direct global-to-LDS loads are waited for
-// separately (vmcnt) before such a barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // Runs are handed from thread 0 to the workgroup through three LDS slots: at
