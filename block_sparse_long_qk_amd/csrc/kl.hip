@@ -36,42 +36,6 @@ constexpr float kLn2 = 0.69314718055994531f;
 // Rows of index queries one wave keeps: 32 / G positions, at most 8 (G >= 4).
 constexpr int kIqRows = 8;
 
-// Stage the K block (row-major, pitch KP) and the index-key block (row-major,
-// pitch DIDX + 8) of one 128-key block.  Keys at or past n_valid repeat key
-// n_valid - 1 (finite data the causal mask drops).  All loads are issued
-// before the first LDS write.
-template <int DIDX>
-__device__ __forceinline__ void stage_k_ik(uint16_t* Ks, uint16_t* IKs, const uint16_t* __restrict__ kb,
-                                           const uint16_t* __restrict__ ikb, int n_valid) {
-  constexpr int IKP = DIDX + 8;
-  constexpr int CPI = DIDX / 8;                    // 16-byte chunks per index-key row
-  constexpr int KPER = 2048 / kThreads, IPER = kBk * CPI / kThreads;
-  const int tid = threadIdx.x;
-  uint4 kr[KPER], ir[IPER];
-#pragma unroll
-  for (int u = 0; u < KPER; ++u) {
-    const int c = tid + kThreads * u;
-    const int key = min(c >> 4, n_valid - 1), oc = c & 15;
-    kr[u] = *reinterpret_cast<const uint4*>(kb + key * kHeadDim + oc * 8);
-  }
-#pragma unroll
-  for (int u = 0; u < IPER; ++u) {
-    const int c = tid + kThreads * u;
-    const int key = min(c / CPI, n_valid - 1), oc = c % CPI;
-    ir[u] = *reinterpret_cast<const uint4*>(ikb + key * DIDX + oc * 8);
-  }
-#pragma unroll
-  for (int u = 0; u < KPER; ++u) {
-    const int c = tid + kThreads * u;
-    *reinterpret_cast<uint4*>(Ks + (c >> 4) * KP + (c & 15) * 8) = kr[u];
-  }
-#pragma unroll
-  for (int u = 0; u < IPER; ++u) {
-    const int c = tid + kThreads * u;
-    *reinterpret_cast<uint4*>(IKs + (c / CPI) * IKP + (c % CPI) * 8) = ir[u];
-  }
-}
-
 // The wave's index-query rows (one per position) by direct global-to-LDS loads:
 // row r at r * 2 * DIDX bytes, its 16-byte chunk c in slot c ^ (r % CPI), so the
 // rows of different positions read at one chunk index fall in different bank
@@ -251,36 +215,6 @@ __device__ __forceinline__ void student_fold(const f32x16 (&z)[4], const float (
   }
 }
 
-// One tile's KL partials for this lane's positions over the block's 128 keys
-// (the 32 lanes of a half hold 4 keys each): the max of the visible student
-// scores first (a max over the lanes), then the three sums with that common
-// max, added over the lanes (DPP reductions, no LDS).  Every lane of a half
-// ends with the totals; a position without visible keys gets m = -inf and l = 0.
-template <int G, bool MASKED>
-__device__ __forceinline__ void student_tile(const f32x16 (&z)[4], const float (&P)[4][PosMap<G>::NPL],
-                                             const int (&lim)[PosMap<G>::NPL], KlAcc (&out)[PosMap<G>::NPL]) {
-  using PM = PosMap<G>;
-  const float NEG_INF = -__builtin_huge_valf();
-#pragma unroll
-  for (int j = 0; j < PM::NPL; ++j) {
-    auto visible = [&](int T) { return 32 * T <= lim[j]; };
-    float m = NEG_INF;
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-      if (visible(T)) m = fmaxf(m, z[T][j * PM::RPP] * kLog2e);
-    m = half_max(m);
-    float a = 0.f, b = 0.f, l = 0.f;
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      const float zz = z[T][j * PM::RPP], p = P[T][j];
-      if (p > 0.f) a += p * __log2f(p);
-      b += p * zz;
-      if (visible(T)) l += __builtin_amdgcn_exp2f(zz * kLog2e - m);
-    }
-    out[j] = KlAcc{half_sum(a), half_sum(b), m, half_sum(l)};
-  }
-}
-
 // Sums over the 32 lanes of each half (the keys of a block): every lane of a
 // half ends with its positions' totals.
 template <int G>
@@ -296,147 +230,16 @@ __device__ __forceinline__ void lanes_reduce(KlAcc (&acc)[PosMap<G>::NPL]) {
   }
 }
 
-// Persistent, XCD-aware walk as in the attention tiles (non-local tiles from the
-// gather plan, LOCAL: the masked local tiles, slot k).
-template <int DIDX, int G, bool LOCAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_kl_tiles(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ iq,
-    const uint16_t* __restrict__ ik, const float* __restrict__ lse, AttnWs ws, float4* __restrict__ kl_part,
-    _Float16* __restrict__ teacher, Dims D) {
-  using PM = PosMap<G>;
-  constexpr int IKP = DIDX + 8;
-  __shared__ __align__(16) uint16_t Ks[kBk * KP];
-  __shared__ __align__(16) uint16_t IKs[kBk * IKP];
-  __shared__ __align__(16) unsigned char Qs[kWaves][kQRegion];
-  __shared__ __align__(16) unsigned char IQs[kWaves][kIqRows * 2 * DIDX];
-  __shared__ __align__(16) float LSs[kWaves][32];
-  int total;
-  if constexpr (LOCAL) {
-    total = D.B * D.h_kv * local_tiles<false>(D);
-  } else {
-    total = ws.tile_off[ws.n_bins];
-  }
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = gridDim.x / kXcds;
-  const int lo = (int)((int64_t)total * xcd / kXcds), hi = (int)((int64_t)total * (xcd + 1) / kXcds);
-  const int stride = per_xcd * kRun;
-  Walk w{lo + slot * kRun, lo + slot * kRun, min(lo + slot * kRun + kRun, hi)};
-  if (w.tile >= hi) return;  // uniform over the workgroup
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = lane & 31, half = lane >> 5;
-  const int r = wave * 32 + col;
-  const int ps = r / G, hh = r % G;
-  unsigned char* qw = Qs[wave];
-  unsigned char* iqw = IQs[wave];
-  const float c = D.scale_log2;
-
-  // A tile's query and index-query rows are fetched into the wave's LDS
-  // regions one tile ahead: each region is refilled as soon as the scores that
-  // read it are formed, so the fetch overlaps the teacher / student folds.
-  auto q_src = [&](const TileRow& tr) {  // rows that do not exist read row 0 of the group
-    const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv, i = tr.valid ? tr.i : 0;
-    return q + (((int64_t)b * D.n_q + i) * D.h_q + g * G + hh) * kHeadDim;
-  };
-  auto iq_src = [&](const TileRow& tr) {
-    const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv, i = tr.valid ? tr.i : 0;
-    return iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX;
-  };
-  auto lse_of = [&](const TileRow& tr) {
-    const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv, i = tr.valid ? tr.i : 0;
-    return lse[((int64_t)b * D.h_q + g * G + hh) * D.n_q + i];
-  };
-  TileRow cur = tile_row<LOCAL, false>(tile_raw<LOCAL>(ws, D, w.tile, ps), D, ws, w.tile, ps);
-  fetch_q_rows(qw, q_src(cur), lane);
-  fetch_iq_rows<DIDX, G>(iqw, iq_src(cur), lane);
-  float lse_raw = lse_of(cur);
-  // the list entry of the tile after next is loaded one tile ahead of its decode
-  Walk w1 = walk_next(w, stride, hi);
-  TileRaw raw1 = tile_raw<LOCAL>(ws, D, min(w1.tile, hi - 1), ps);
-  int staged_bg = -1, staged_t = -1;
-  while (w.tile < hi) {
-    const int b = cur.bg / D.h_kv, g = cur.bg % D.h_kv;
-    if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform: a new block for the workgroup
-      __syncthreads();  // every wave is done with the staged block
-      const int64_t kv0 = (((int64_t)b * D.h_kv + g) * D.n_kv + (int64_t)cur.t * kBk) * kHeadDim;
-      const int64_t ik0 = ((int64_t)b * D.n_kv + (int64_t)cur.t * kBk) * DIDX;
-      stage_k_ik<DIDX>(Ks, IKs, k + kv0, ik + ik0, max(1, min(kBk, D.n_kv - cur.t * kBk)));
-      staged_bg = cur.bg;
-      staged_t = cur.t;
-      __syncthreads();
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's query and index-query rows have landed
-    // the lse of the 16 rows this lane's registers hold (+inf: no such row)
-    float lse2[16];
-    rows_lse(LSs[wave], cur.valid ? lse_raw * kLog2e : __builtin_huge_valf(), lane, lse2);
-    int lim[PM::NPL];  // visibility limit of each lane-local position (see key_limit)
-    int pi[PM::NPL], pv[PM::NPL], pslot[PM::NPL];
-#pragma unroll
-    for (int j = 0; j < PM::NPL; ++j) {
-      pi[j] = pos_value<G>(cur.i, j, half);
-      pv[j] = pos_value<G>((int)cur.valid, j, half);
-      pslot[j] = pos_value<G>(cur.s, j, half);
-      lim[j] = key_limit<LOCAL>(pv[j], D.offset + pi[j], (int64_t)cur.t * kBk, col);
-    }
-    // the next tile (past the last: a stand-in decode of the last one, whose
-    // fetches stay in bounds and are never used), and the list entry after it
-    const TileRow nxt = tile_row<LOCAL, false>(raw1, D, ws, min(w1.tile, hi - 1), ps);
-    const Walk w2 = w1.tile < hi ? walk_next(w1, stride, hi) : w1;
-    const TileRaw raw2 = tile_raw<LOCAL>(ws, D, min(w2.tile, hi - 1), ps);
-    float P[4][PM::NPL];
-    {
-      f32x16 sc[4];
-      q_k_scores(Ks, qw, lane, sc);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the query region has been read
-      fetch_q_rows(qw, q_src(nxt), lane);
-      lse_raw = lse_of(nxt);
-      teacher_probs<G, LOCAL>(sc, lse2, lim, c, P);
-    }
-    if (teacher) {  // uniform
-      // P[T][j] at key 32T + col of the position's (row, slot); for G >= 8
-      // both halves hold the same values and split the four key ranges
-#pragma unroll
-      for (int j = 0; j < PM::NPL; ++j) {
-        if (!pv[j]) continue;
-        _Float16* dst = teacher + (((int64_t)cur.bg * D.n_q + pi[j]) * (D.k + 1) + pslot[j]) * kBk + col;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-          if (G == 4 || (T >> 1) == half) dst[32 * T] = (_Float16)P[T][j];
-      }
-    }
-    KlAcc acc[PM::NPL];
-    {
-      f32x16 zz[4];
-      iq_ik_scores<DIDX, G>(IKs, iqw, lane, zz);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the index-query region has been read
-      fetch_iq_rows<DIDX, G>(iqw, iq_src(nxt), lane);
-      student_tile<G, LOCAL>(zz, P, lim, acc);
-    }
-    // the lane of each position's first head row writes its partial
-#pragma unroll
-    for (int j = 0; j < PM::NPL; ++j) {
-      const bool writer = col == PM::wpos(j, half) * G && (G == 4 || half == 0);
-      if (writer && pv[j]) {
-        const int64_t row = (int64_t)cur.bg * D.n_q + pi[j];
-        kl_part[row * (D.k + 1) + pslot[j]] = make_float4(acc[j].a, acc[j].b, acc[j].m, acc[j].l);
-      }
-    }
-    w = w1;
-    w1 = w2;
-    raw1 = raw2;
-    cur = nxt;
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the last (unused) row fetch has landed before the workgroup ends
-}
-
 // ---------------------------------------------------------------- four-wave tiles
 // The same partials from four-wave workgroups on the forward's 128-row tiles
 // (pt * G = 128) and its dynamic per-XCD runs: each wave's query rows stay in
 // VGPRs (the next tile's loaded into the other register set while the current
 // one is computed), K and the index keys of a block arrive by direct
-// global-to-LDS loads, and Z is formed per position, not per head row: a
-// 16x16x32 product whose 16 M rows repeat the wave's 32 / G positions, so
-// that lane (key n, k-group c) holds Z of the positions its S registers
-// hold (see zpos), for the key the lane's S column is.
+// global-to-LDS loads, the rows are laid out so that a lane's S registers
+// hold whole positions (Rows4), and Z is formed per position, not per head
+// row: a 16x16x32 product whose 16 M rows repeat the wave's positions, so
+// that lane (key n, k-group c) holds Z of the positions its S registers hold
+// (see zpos), for the key the lane's S column is.
 
 // K (swizzled as in stage_kv_fwd) and the index keys (row r at r * 2 DIDX
 // bytes, its chunk c in slot c ^ (r % CPI)) of one block, by direct loads:
@@ -504,14 +307,51 @@ __device__ __forceinline__ f32x4 mfma16k(uint4 a, uint4 b, f32x4 c) {
                                                  0, 0, 0);
 }
 
-// Wave-local position of row m of the Z product: lane (n, c) gets rows 4c + i,
-// and its S registers hold lane-local positions j = i (PosMap::wpos(j, half),
-// with c = 2 half + (column >= 16)).
+// Rows of the four-wave tiles.  MFMA row m (lane column m of the query
+// operand) is (position, head) = ((16/G) h + e / G, e % G) of the wave, with
+// h = (m >> 2) & 1 and e = 4 (m >> 3) + (m & 3): accumulator register e of a
+// lane in half h is row 8 (e / 4) + 4 h + e % 4, so for G <= 16 every head of
+// a position sits in one lane's registers (the group average is an in-lane
+// sum) and the two halves hold different positions.  For G = 32 the one
+// position's heads are split over the halves (head 16 h + e).
+template <int G>
+struct Rows4 {
+  static constexpr int NPL = G <= 16 ? 16 / G : 1;  // positions per lane
+  static constexpr int RPP = G <= 16 ? G : 16;      // registers per position
+  static __device__ __forceinline__ int pos_of(int m) {
+    const int h = (m >> 2) & 1, e = 4 * (m >> 3) + (m & 3);
+    return G <= 16 ? (16 / G) * h + e / G : 0;
+  }
+  static __device__ __forceinline__ int head_of(int m) {
+    const int h = (m >> 2) & 1, e = 4 * (m >> 3) + (m & 3);
+    return G <= 16 ? e % G : 16 * h + e;
+  }
+  // wave-local position of lane-local position j in half h
+  static __device__ __forceinline__ int lpos(int j, int h) { return G <= 16 ? (16 / G) * h + j : 0; }
+  // the row of head 0 of wave-local position p
+  static __device__ __forceinline__ constexpr int row_of(int p) {
+    if (G > 16) return 0;
+    const int h = p / (16 / G), e = G * (p % (16 / G));
+    return 8 * (e >> 2) + 4 * h + (e & 3);
+  }
+};
+
+// Value x of head 0's row of lane-local position j (two lane reads with
+// constant lanes).
+template <int G>
+__device__ __forceinline__ int pos_value4(int x, int j, int half) {
+  const int v0 = __builtin_amdgcn_readlane(x, Rows4<G>::row_of(Rows4<G>::lpos(j, 0)));
+  const int v1 = __builtin_amdgcn_readlane(x, Rows4<G>::row_of(Rows4<G>::lpos(j, 1)));
+  return half ? v1 : v0;
+}
+
+// Row m of the Z product (lane (n, c) gets rows 4c + i): the wave-local
+// position whose values lane-local position i of the S registers needs
+// (c = 2 half + (column >= 16)); rows past a lane's positions repeat its last.
 template <int G>
 __device__ __forceinline__ int zpos(int m) {
-  constexpr int NP = 32 / G;
-  if constexpr (G == 4) return (m >> 3) + 2 * (m & 3);
-  return min(m & 3, NP - 1);
+  constexpr int NPL = Rows4<G>::NPL;
+  return Rows4<G>::lpos(min(m & 3, NPL - 1), (m >> 3) & 1);
 }
 
 // z[T][j]: Z = IQ IK^T of lane-local position j and the lane's key 32T + col,
@@ -519,7 +359,7 @@ __device__ __forceinline__ int zpos(int m) {
 // slot c ^ (p % CPI)) and the staged index keys.
 template <int DIDX, int G>
 __device__ __forceinline__ void z_scores(const unsigned char* IKs, const unsigned char* iqw, int lane,
-                                         float (&z)[4][PosMap<G>::NPL]) {
+                                         float (&z)[4][Rows4<G>::NPL]) {
   constexpr int CPI = DIDX / 8, IKS = DIDX / 32;
   const int n = lane & 15, cg = lane >> 4;
   const int pm = zpos<G>(n);
@@ -542,32 +382,61 @@ __device__ __forceinline__ void z_scores(const unsigned char* IKs, const unsigne
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
 #pragma unroll
-    for (int j = 0; j < PosMap<G>::NPL; ++j) z[T][j] = hi ? zt[2 * T + 1][j] : zt[2 * T][j];
+    for (int j = 0; j < Rows4<G>::NPL; ++j) z[T][j] = hi ? zt[2 * T + 1][j] : zt[2 * T][j];
   }
 }
 
-// student_tile with Z per lane-local position.
+// Teacher weights of the tile: P[T][j] is the group's average probability of
+// key key0 + 32T + col for lane-local position j (0 for keys after the
+// position and for rows that do not exist, whose lse2 is +inf).
 template <int G, bool MASKED>
-__device__ __forceinline__ void student_tile_p(const float (&z)[4][PosMap<G>::NPL],
-                                               const float (&P)[4][PosMap<G>::NPL],
-                                               const int (&lim)[PosMap<G>::NPL], KlAcc (&out)[PosMap<G>::NPL]) {
-  using PM = PosMap<G>;
+__device__ __forceinline__ void teacher_probs4(const f32x16 (&s)[4], const float (&lse2)[16],
+                                               const int (&lim)[Rows4<G>::NPL], float c,
+                                               float (&P)[4][Rows4<G>::NPL]) {
+  using R = Rows4<G>;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+#pragma unroll
+    for (int j = 0; j < R::NPL; ++j) {
+      float psum = 0.f;
+#pragma unroll
+      for (int e = j * R::RPP; e < (j + 1) * R::RPP; ++e)
+        psum += __builtin_amdgcn_exp2f(__builtin_fmaf(s[T][e], c, -lse2[e]));
+      if constexpr (G > 16) psum += wave_xor32(psum);
+      const bool vis = !MASKED || 32 * T <= lim[j];
+      P[T][j] = vis ? psum * (1.f / G) : 0.f;
+    }
+  }
+}
+
+// The tile's partials for the lane's positions over the block's 128 keys (the
+// 32 lanes of a half hold 4 keys each): the max of the visible student scores
+// first, then the three sums with that common max, added over the half's
+// lanes.  Every lane of a half ends with the totals; a position without
+// visible keys gets m = -inf and l = 0.
+template <int G, bool MASKED>
+__device__ __forceinline__ void student_tile4(const float (&z)[4][Rows4<G>::NPL], const float (&P)[4][Rows4<G>::NPL],
+                                              const int (&lim)[Rows4<G>::NPL], KlAcc (&out)[Rows4<G>::NPL]) {
+  using R = Rows4<G>;
   const float NEG_INF = -__builtin_huge_valf();
 #pragma unroll
-  for (int j = 0; j < PM::NPL; ++j) {
+  for (int j = 0; j < R::NPL; ++j) {
     auto visible = [&](int T) { return 32 * T <= lim[j]; };
+    float zl[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) zl[T] = z[T][j] * kLog2e;
     float m = NEG_INF;
 #pragma unroll
     for (int T = 0; T < 4; ++T)
-      if (visible(T)) m = fmaxf(m, z[T][j] * kLog2e);
+      if (visible(T)) m = fmaxf(m, zl[T]);
     m = half_max(m);
     float a = 0.f, b = 0.f, l = 0.f;
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      const float zz = z[T][j], p = P[T][j];
+      const float p = P[T][j];
       if (p > 0.f) a += p * __log2f(p);
-      b += p * zz;
-      if (visible(T)) l += __builtin_amdgcn_exp2f(zz * kLog2e - m);
+      b += p * z[T][j];
+      if (visible(T)) l += __builtin_amdgcn_exp2f(zl[T] - m);
     }
     out[j] = KlAcc{half_sum(a), half_sum(b), m, half_sum(l)};
   }
@@ -578,7 +447,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ iq,
     const uint16_t* __restrict__ ik, const float* __restrict__ lse, AttnWs ws, float4* __restrict__ kl_part,
     _Float16* __restrict__ teacher, Dims D) {
-  using PM = PosMap<G>;
+  using R = Rows4<G>;
   constexpr int NP = 32 / G;             // positions per wave
   constexpr int CPI = DIDX / 8;          // 16-byte chunks of an index row
   constexpr int IQB = NP * 2 * DIDX;     // bytes of one wave's index-query rows
@@ -606,8 +475,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
-  const int r = wave * 32 + col;
-  const int ps = r / G, hh = r % G;
+  const int ps = wave * NP + R::pos_of(col), hh = R::head_of(col);  // this lane's query row
   const float c = D.scale_log2;
   auto q_ptr = [&](const TileRow& tr) {  // rows that do not exist read row 0 of the group
     const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv, i = tr.valid ? tr.i : 0;
@@ -618,7 +486,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     return lse[((int64_t)b * D.h_q + g * G + hh) * D.n_q + i];
   };
   // this lane's chunks of the wave's index-query rows of tile tr (position p's
-  // row from lane p G; rows that do not exist read row 0)
+  // row from the lane of its head 0; rows that do not exist read row 0)
   auto load_iq = [&](const TileRow& tr, uint4 (&x)[NIQ]) {
     const int b = tr.bg / D.h_kv, g = tr.bg % D.h_kv;
     const int i_mine = tr.valid ? tr.i : 0;
@@ -626,7 +494,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     for (int u = 0; u < NIQ; ++u) {
       const int pc = min(lane + 64 * u, NPC - 1);
       const int p = pc / CPI, ch = pc % CPI;
-      const int i = __shfl(i_mine, p * G, 64);
+      const int i = __shfl(i_mine, R::row_of(p), 64);
       x[u] = *reinterpret_cast<const uint4*>(iq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * DIDX + 8 * ch);
     }
   };
@@ -680,7 +548,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     // live); for d_idx 128 and G <= 8 after S and the next tile's loads,
     // where that order does
     constexpr bool kZFirst = !(DIDX == 128 && G <= 8);
-    float z[4][PM::NPL];
+    float z[4][R::NPL];
     if constexpr (kZFirst) z_scores<DIDX, G>(IKs, IQs[wave][buf], lane, z);
     f32x16 s[4];
     qk_rows(Ks, qc, lane, s);
@@ -701,31 +569,31 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 
     float lse2[16];  // the lse of the 16 rows this lane's registers hold (+inf: no such row)
     rows_lse(LSs[wave], cur.valid ? lse_cur * kLog2e : __builtin_huge_valf(), lane, lse2);
-    int lim[PM::NPL], pi[PM::NPL], pv[PM::NPL], pslot[PM::NPL];
+    int lim[R::NPL], pi[R::NPL], pv[R::NPL], pslot[R::NPL];
 #pragma unroll
-    for (int j = 0; j < PM::NPL; ++j) {
-      pi[j] = pos_value<G>(cur.i, j, half);
-      pv[j] = pos_value<G>((int)cur.valid, j, half);
-      pslot[j] = pos_value<G>(cur.s, j, half);
+    for (int j = 0; j < R::NPL; ++j) {
+      pi[j] = pos_value4<G>(cur.i, j, half);
+      pv[j] = pos_value4<G>((int)cur.valid, j, half);
+      pslot[j] = pos_value4<G>(cur.s, j, half);
       lim[j] = key_limit<LOCAL>(pv[j], D.offset + pi[j], (int64_t)cur.t * kBk, col);
     }
-    float P[4][PM::NPL];
-    teacher_probs<G, LOCAL>(s, lse2, lim, c, P);
-    if (teacher) {  // uniform; for G >= 8 both halves hold the same weights and split the key ranges
+    float P[4][R::NPL];
+    teacher_probs4<G, LOCAL>(s, lse2, lim, c, P);
+    if (teacher) {  // uniform; for G = 32 both halves hold the same weights and split the key ranges
 #pragma unroll
-      for (int j = 0; j < PM::NPL; ++j) {
+      for (int j = 0; j < R::NPL; ++j) {
         if (!pv[j]) continue;
         _Float16* dst = teacher + (((int64_t)cur.bg * D.n_q + pi[j]) * (D.k + 1) + pslot[j]) * kBk + col;
 #pragma unroll
         for (int T = 0; T < 4; ++T)
-          if (G == 4 || (T >> 1) == half) dst[32 * T] = (_Float16)P[T][j];
+          if (G <= 16 || (T >> 1) == half) dst[32 * T] = (_Float16)P[T][j];
       }
     }
-    KlAcc acc[PM::NPL];
-    student_tile_p<G, LOCAL>(z, P, lim, acc);
+    KlAcc acc[R::NPL];
+    student_tile4<G, LOCAL>(z, P, lim, acc);
 #pragma unroll
-    for (int j = 0; j < PM::NPL; ++j) {
-      const bool writer = col == PM::wpos(j, half) * G && (G == 4 || half == 0);
+    for (int j = 0; j < R::NPL; ++j) {
+      const bool writer = col == 0 && (G <= 16 || half == 0);  // every lane of a half holds the totals
       if (writer && pv[j]) {
         const int64_t row = (int64_t)cur.bg * D.n_q + pi[j];
         kl_part[row * (D.k + 1) + pslot[j]] = make_float4(acc[j].a, acc[j].b, acc[j].m, acc[j].l);
