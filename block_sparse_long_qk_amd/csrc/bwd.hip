@@ -18,8 +18,8 @@
 //   S = Q K_w^T and dP = dO V_w^T with the rows as M: lane (key n, group c)
 //   holds rows {4c..4c+3} and {16+4c..16+4c+3}, which is exactly the k-group c
 //   that a 32-row contraction reads, so P and dS serve as B operands as they are;
-//   dV^T += dO^T P and dK^T += Q^T dS take dO^T and Q^T from transposed copies
-//   of the chunk in LDS;
+//   dV^T += dO^T P and dK^T += Q^T dS read dO^T and Q^T from the row-major chunk
+//   buffers by transposing loads (ds_read_b64_tr_b16);
 //   dQ^T = K^T dS^T needs every wave's dS: it goes through LDS once, and wave w
 //   forms head dims 16w .. 16w+15 of the chunk's dQ from the staged K^T.
 // dQ leaves as one bf16 partial per (row, slot); a merge adds a row's slots.
@@ -238,14 +238,37 @@ __device__ __forceinline__ u32x4 tp_operand(const uint16_t* src, int d, int c) {
   return u32x4{a.x, a.y, b.x, b.y};
 }
 
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+
+// Rows r0 .. r0+3 at dims dbase + (lane % 16), from a row-major chunk buffer
+// (row r at 256 r, its 16-byte chunk c in slot c ^ (r % 16)): lane 4e + j of
+// each 16-lane group reads row r0 + e, dims dbase + 4j .. +3, and the
+// transposing load hands lane i element i % 4 of lanes i / 4 + 4e.
+__device__ __forceinline__ uint2 tr_rows4(const unsigned char* buf, int r0, int dbase, int lane) {
+  const int e = (lane & 15) >> 2, j = lane & 3;
+  const int row = r0 + e, d = dbase + 4 * j;
+  const unsigned char* a = buf + row * 256 + 16 * ((d >> 3) ^ (row & 15)) + 2 * (d & 7);
+  const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s16*)a);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// The 16x16x32 A operand of dims 16 dt + (lane % 16) whose k-group c = lane / 16
+// is rows 4c .. 4c+3 and 16+4c .. 16+4c+3 of the chunk (the rows a lane of S
+// and dP holds for its key).
+__device__ __forceinline__ u32x4 tr_operand16(const unsigned char* buf, int dt, int lane) {
+  const int c = lane >> 4;
+  const uint2 a = tr_rows4(buf, 4 * c, 16 * dt, lane), b = tr_rows4(buf, 16 + 4 * c, 16 * dt, lane);
+  return u32x4{a.x, a.y, b.x, b.y};
+}
+
 template <bool VL>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta, AttnWs ws,
     uint16_t* __restrict__ dq_part, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, Dims D) {
   __shared__ __align__(16) uint16_t Kt[kHeadDim * kKtP];             // K^T of the block
-  __shared__ __align__(16) unsigned char Qs[32 * 256], Os[32 * 256];  // chunk rows of Q and dO (swizzled)
-  __shared__ __align__(16) uint16_t Qt[kHeadDim * kTP], Ot[kHeadDim * kTP];  // their transposes [d][row]
+  // chunk rows of Q and dO (swizzled), two chunks' worth: chunk c in buffer c % 2
+  __shared__ __align__(16) unsigned char Qs[2][32 * 256], Os[2][32 * 256];
   __shared__ __align__(16) unsigned char Ss[32 * 256];  // the chunk's dS [row][key] (swizzled)
   __shared__ WalkTab W;
 
@@ -313,7 +336,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // A chunk's rows travel through registers: lane l of wave w loads 16 bytes
   // of row r = 4w + l / 16, its piece p = (l % 16) ^ (r % 16) (dims 8p .. 8p+7),
   // and stores them at byte 1024 w + 16 l of the row buffer (so row r's piece
-  // p sits in slot p ^ (r % 16)) and, element by element, into the transposes.
+  // p sits in slot p ^ (r % 16)); dO^T and Q^T are read from these buffers by
+  // transposing loads.
   const int my_r = 4 * wave + (lane >> 4);
   const int my_p = (lane & 15) ^ (my_r & 15);
   u32x4 q_next, o_next;
@@ -322,13 +346,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     q_next = *reinterpret_cast<const u32x4*>(qb + qrow);
     o_next = *reinterpret_cast<const u32x4*>(ob + qrow);
   };
-  auto store_rows = [&]() {
-    *reinterpret_cast<u32x4*>(Qs + 1024 * wave + 16 * lane) = q_next;
-    *reinterpret_cast<u32x4*>(Os + 1024 * wave + 16 * lane) = o_next;
-  };
-  auto store_transposes = [&]() {
-    tp_store8(Qt, q_next, my_p, my_r);
-    tp_store8(Ot, o_next, my_p, my_r);
+  auto store_rows = [&](int buf) {
+    *reinterpret_cast<u32x4*>(Qs[buf] + 1024 * wave + 16 * lane) = q_next;
+    *reinterpret_cast<u32x4*>(Os[buf] + 1024 * wave + 16 * lane) = o_next;
   };
   // raw lse and delta of the next chunk's rows (row 0's for rows that do not
   // exist), first used in the next iteration
@@ -346,13 +366,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // and every path reaches the loop with the fragment loads above complete)
   load_rows(0);
   stats(0);
-  store_rows();
+  store_rows(0);
   for (int c = 0; c < nch; ++c) {
     const int slot = c & (kRing - 1);
+    const unsigned char* qs = Qs[c & 1];
+    const unsigned char* os = Os[c & 1];
     __syncthreads();  // chunk c's rows are in LDS; chunk c + 1's table is visible
-    // chunk c's transposes, from the registers that still hold its rows (the
-    // previous chunk's were last read before the barrier above)
-    store_transposes();
     float lse_c[8], dl_c[8];
     int pos8[8];
 #pragma unroll
@@ -381,8 +400,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int sl = (4 * ks + cgrp) ^ (r & 15);
-        const u32x4 qa = *reinterpret_cast<const u32x4*>(Qs + r * 256 + 16 * sl);
-        const u32x4 oa = *reinterpret_cast<const u32x4*>(Os + r * 256 + 16 * sl);
+        const u32x4 qa = *reinterpret_cast<const u32x4*>(qs + r * 256 + 16 * sl);
+        const u32x4 oa = *reinterpret_cast<const u32x4*>(os + r * 256 + 16 * sl);
         sc4[mt] = mfma16(qa, kf[ks], sc4[mt]);
         dp4[mt] = mfma16(oa, vf[ks], dp4[mt]);
       }
@@ -410,14 +429,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       *reinterpret_cast<uint16_t*>(Ss + r * 256 + sl * 16 + 2 * (key & 7)) =
           (uint16_t)((u & 1) ? (sb[u >> 1] >> 16) : (sb[u >> 1] & 0xFFFFu));
     }
-    __syncthreads();  // transposes and dS are in LDS; the row buffers are free
+    __syncthreads();  // dS is in LDS
     // dV^T += dO^T P, dK^T += Q^T dS: M = head dims (8 tiles), K = the 32 rows
     // (k-group c: rows 4c..4c+3 and 16+4c..16+4c+3), N = this wave's keys
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + n;
-      dvT[dt] = mfma16(tp_operand(Ot, d, cgrp), pb, dvT[dt]);
-      dkT[dt] = mfma16(tp_operand(Qt, d, cgrp), sb, dkT[dt]);
+      dvT[dt] = mfma16(tr_operand16(os, dt, lane), pb, dvT[dt]);
+      dkT[dt] = mfma16(tr_operand16(qs, dt, lane), sb, dkT[dt]);
     }
     // dQ^T (dims 16w .. 16w+15 x 32 rows) = K^T dS^T over the block's 128 keys;
     // lane (row 16nt + n, group c) holds dims 16w + 4c .. +3 of that row
@@ -438,7 +456,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
             make_uint2(pack_bf16x2(acc[0] * sc, acc[1] * sc), pack_bf16x2(acc[2] * sc, acc[3] * sc));
       }
     }
-    store_rows();  // chunk c + 1's rows, read after the next barrier
+    // chunk c + 1's rows into the other buffer (last read in chunk c - 1,
+    // which every wave left before this chunk's first barrier), read after
+    // the next barrier
+    store_rows((c + 1) & 1);
   }
   // write this wave's keys: lane (key n, group c) holds dims 16dt + 4c .. +3
   if (key_abs < nkv) {
@@ -471,8 +492,8 @@ __global__ __launch_bounds__(256) void k_bwd_dq_merge(const int32_t* __restrict_
   const int local = (int)((D.offset + i) / kBk);
   const int32_t* sel = block_idx + row * D.k;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto add = [&](int s) {
-    const uint4 x = *reinterpret_cast<const uint4*>(dq_part + ((row * (D.k + 1) + s) * D.G + h) * kHeadDim + 8 * part);
+  const uint16_t* src = dq_part + (row * (D.k + 1) * D.G + h) * kHeadDim + 8 * part;  // slot s at s G 128
+  auto add = [&](uint4 x) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -480,9 +501,20 @@ __global__ __launch_bounds__(256) void k_bwd_dq_merge(const int32_t* __restrict_
       acc[2 * u + 1] += __uint_as_float(w[u] & 0xFFFF0000u);
     }
   };
-  for (int s = 0; s < D.k; ++s)
-    if (nonlocal_slot(sel, s, local)) add(s);
-  add(D.k);
+  // the listed non-local slots in order, eight loads in flight at a time, then the local slot
+  for (int s0 = 0; s0 < D.k; s0 += 8) {
+    uint4 x[8];
+    bool use[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      use[u] = s0 + u < D.k && nonlocal_slot(sel, s0 + u, local);
+      x[u] = use[u] ? *reinterpret_cast<const uint4*>(src + (int64_t)(s0 + u) * D.G * kHeadDim) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (use[u]) add(x[u]);
+  }
+  add(*reinterpret_cast<const uint4*>(src + (int64_t)D.k * D.G * kHeadDim));
   uint16_t* dst = dq + (((int64_t)b * D.n_q + i) * D.h_q + g * D.G + h) * kHeadDim + 8 * part;
   *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                                               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
