@@ -1007,8 +1007,8 @@ __global__ __launch_bounds__(256) void k_kl_bwd_diq(const int32_t* __restrict__ 
   const int local = (int)((D.offset + i) / kBk);
   const int32_t* sel = block_idx + row * D.k;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto add = [&](int s) {
-    const uint4 x = *reinterpret_cast<const uint4*>(diq_part + (row * (D.k + 1) + s) * D.d_idx + 8 * part);
+  const uint16_t* src = diq_part + row * (D.k + 1) * D.d_idx + 8 * part;  // slot s at s d_idx
+  auto add = [&](uint4 x) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1016,9 +1016,20 @@ __global__ __launch_bounds__(256) void k_kl_bwd_diq(const int32_t* __restrict__ 
       acc[2 * u + 1] += __uint_as_float(w[u] & 0xFFFF0000u);
     }
   };
-  for (int s = 0; s < D.k; ++s)
-    if (nonlocal_slot(sel, s, local)) add(s);
-  add(D.k);
+  // the listed non-local slots in order, eight loads in flight at a time, then the local slot
+  for (int s0 = 0; s0 < D.k; s0 += 8) {
+    uint4 x[8];
+    bool use[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      use[u] = s0 + u < D.k && nonlocal_slot(sel, s0 + u, local);
+      x[u] = use[u] ? *reinterpret_cast<const uint4*>(src + (int64_t)(s0 + u) * D.d_idx) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (use[u]) add(x[u]);
+  }
+  add(*reinterpret_cast<const uint4*>(src + (int64_t)D.k * D.d_idx));
   uint16_t* dst = diq + (((int64_t)b * D.n_q + i) * D.h_kv + g) * D.d_idx + 8 * part;
   *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                                               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));

@@ -627,27 +627,49 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   }
 }
 
-// One thread per (sequence, group, query): add the row's partials (the listed
-// non-local blocks and the local block, slot k) and form the KL value.
+// 32 lanes per (sequence, group, query): lane j takes slots j, j + 32, .. of
+// the row's partials (the listed non-local blocks, and the local block, slot
+// k; the other slots add nothing), adds its own in slot order, and the 32
+// lanes' sums are added in a fixed tree order (the max first, then the
+// rescaled sums); lane 0 forms the KL value.
 __global__ __launch_bounds__(256) void k_kl_merge(const int32_t* __restrict__ block_idx,
                                                   const float4* __restrict__ kl_part, float* __restrict__ kl,
                                                   float* __restrict__ lse_index, Dims D) {
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= (int64_t)D.B * D.h_kv * D.n_q) return;
-  const int i = (int)(row % D.n_q);
-  const int local = (int)((D.offset + i) / kBk);
-  const int32_t* sel = block_idx + row * D.k;
-  const float4* part = kl_part + row * (D.k + 1);
-  KlAcc acc = kl_combine(KlAcc{0.f, 0.f, -__builtin_huge_valf(), 0.f},
-                         KlAcc{part[D.k].x, part[D.k].y, part[D.k].z, part[D.k].w});
-  for (int s = 0; s < D.k; ++s) {
-    if (!nonlocal_slot(sel, s, local)) continue;
-    const float4 x = part[s];
-    acc = kl_combine(acc, KlAcc{x.x, x.y, x.z, x.w});
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;
+  const int j = threadIdx.x & 31;
+  const int64_t rows = (int64_t)D.B * D.h_kv * D.n_q;
+  const bool live = row < rows;  // whole half-waves: a row's 32 lanes agree
+  const float NEG_INF = -__builtin_huge_valf();
+  KlAcc acc{0.f, 0.f, NEG_INF, 0.f};
+  if (live) {
+    const int i = (int)(row % D.n_q);
+    const int local = (int)((D.offset + i) / kBk);
+    const int32_t* sel = block_idx + row * D.k;
+    const float4* part = kl_part + row * (D.k + 1);
+    for (int s = j; s <= D.k; s += 32) {
+      if (s == D.k || nonlocal_slot(sel, s, local)) {
+        const float4 x = part[s];
+        acc = kl_combine(acc, KlAcc{x.x, x.y, x.z, x.w});
+      }
+    }
   }
-  const float lz = (acc.m + __log2f(acc.l)) * kLn2;  // the student's log-normaliser
-  kl[row] = acc.a * kLn2 - acc.b + lz;
-  if (lse_index) lse_index[row] = lz;
+  // the lanes' maximum, then every lane's sums at that maximum, added over the 32 lanes
+  float m = acc.m;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float l = acc.m == NEG_INF ? 0.f : acc.l * __builtin_amdgcn_exp2f(acc.m - m);
+  float a = acc.a, b = acc.b;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    a += __shfl_xor(a, o, 64);
+    b += __shfl_xor(b, o, 64);
+    l += __shfl_xor(l, o, 64);
+  }
+  if (live && j == 0) {
+    const float lz = (m + __log2f(l)) * kLn2;  // the student's log-normaliser
+    kl[row] = a * kLn2 - b + lz;
+    if (lse_index) lse_index[row] = lz;
+  }
 }
 
 // ---------------------------------------------------------------- dense mode
@@ -836,8 +858,8 @@ hipError_t launch_index_kl(const uint16_t* q, const uint16_t* k, const uint16_t*
   };
   if (D.d_idx == 128) by_g(I128{}); else by_g(I64{});
   const int64_t rows = (int64_t)D.B * D.h_kv * D.n_q;
-  hipLaunchKernelGGL(k_kl_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, block_idx, kl_part, kl,
-                     lse_index, D);
+  hipLaunchKernelGGL(k_kl_merge, dim3((unsigned)((rows * 32 + 255) / 256)), dim3(256), 0, stream, block_idx, kl_part,
+                     kl, lse_index, D);
   return hipGetLastError();
 }
 
