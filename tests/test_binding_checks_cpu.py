@@ -134,3 +134,33 @@ def test_training_calls_checked():
     with pytest.raises(ValueError, match="lse_index is required"):
         msa.index_kl_bwd(p, x["q"], x["k"], x["iq"], x["ik"], x["bidx"], x["lse"], None, x["iq"], x["ik"],
                          workspace=x["ws"], stream=0)
+
+
+def test_stored_teacher_calls_checked():
+    """The teacher-keeping KL pass and the backward that reads the teacher:
+    the teacher must be fp16 of teacher_shape(p), lse_index is required, and
+    host tensors of the right shapes get as far as the device check."""
+    p = prob(h_q=16, h_kv=2, index_dim=128)
+    x = inputs(p)
+    kl = torch.zeros((1, 2, 256), dtype=torch.float32)
+    lz = torch.zeros_like(kl)
+    assert msa.teacher_shape(p) == (1, 2, 256, 3, 128)
+    teacher = torch.zeros(msa.teacher_shape(p), dtype=torch.float16)
+    call = lambda t, l: msa.index_kl_teacher(p, x["q"], x["k"], x["iq"], x["ik"], x["bidx"], x["lse"], kl, l, t,
+                                             x["ws"], stream=0)
+    with pytest.raises(ValueError, match="teacher has dtype"):
+        call(teacher.to(torch.bfloat16), lz)
+    with pytest.raises(ValueError, match="teacher holds"):
+        call(teacher.reshape(-1)[:1000], lz)
+    with pytest.raises(ValueError, match="lse_index is required"):
+        call(teacher, None)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        call(teacher, lz)
+    bcall = lambda t, l: msa.index_kl_bwd_teacher(p, x["iq"], x["ik"], x["bidx"], t, l, x["iq"], x["ik"],
+                                                  workspace=x["ws"], stream=0)
+    with pytest.raises(ValueError, match="teacher has dtype"):
+        bcall(teacher.float(), lz)
+    with pytest.raises(ValueError, match="lse_index is required"):
+        bcall(teacher, None)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        bcall(teacher, lz)
