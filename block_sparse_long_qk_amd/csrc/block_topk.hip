@@ -49,8 +49,8 @@ __device__ __forceinline__ uint32_t sel_key(float f) {
 // row by 8, ^4 the half-row mirror followed by the quad flip.  Across rows:
 // ^16 and ^31 by ds_swizzle (xor within 32 lanes), ^63 by ds_bpermute.
 template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ float dpp_f32(float v) {  // every lane's source is in its row: no bound control needed
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 template <int M>
 __device__ __forceinline__ float xor_lane(float v) {
@@ -68,11 +68,14 @@ __device__ __forceinline__ float xor_lane(float v) {
   else return __shfl_xor(v, M, 64);
 }
 
-// Compare-exchange with lane ^ M: the lane whose `LOWBIT` is clear keeps the smaller.
+// Compare-exchange with lane ^ M: the lane whose `LOWBIT` is clear keeps the
+// smaller.  One median of three: med3(x, y, -inf) = min(x, y) and
+// med3(x, y, +inf) = max(x, y) (no NaNs here), the bound a per-lane constant.
 template <int M, int LOWBIT>
 __device__ __forceinline__ float cmpx(float x, int lane) {
   const float y = xor_lane<M>(x);
-  return (lane & LOWBIT) == 0 ? fminf(x, y) : fmaxf(x, y);
+  const float INF = __builtin_huge_valf();
+  return __builtin_amdgcn_fmed3f(x, y, (lane & LOWBIT) == 0 ? -INF : INF);
 }
 template <int S>
 __device__ __forceinline__ float half_clean(float x, int lane) {  // xor partners S, S/2, ..., 1
@@ -124,16 +127,20 @@ __device__ __forceinline__ int prefix(uint64_t m, int base = 0) {
 // registers, the next row's while the current one is selected; PER == 0 (rows
 // beyond 2048 blocks): each of the two passes over the row streams it, eight
 // loads in flight (the second pass mostly from L2).
-template <int PER, bool VL>
+template <int PER, bool VL, bool K16>
 __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ pooled, int32_t* __restrict__ out,
                                                     Dims D, int nrows) {
-  __shared__ uint2 cand[4][64];  // (score bits, block) of the row's scores >= tau
+  // scores >= tau ([w][0][i]) and their blocks' bits ([w][1][i]): a slot's
+  // scores are written from entry min(total, 64) on, so the list holds the
+  // first 64 in order and a row with more (whose list is not used) stays
+  // inside it
+  __shared__ float cand[4][2][128];
   // the wave index as a uniform value, so that the rows' buffer descriptors
   // live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int stride = gridDim.x * 4;
   const float NEG_INF = -__builtin_huge_valf();
-  const int k = D.k, kk = k - 1;  // kk blocks to pick among a row's `local` candidates
+  const int k = D.k, kk = k - 1;  // kk blocks to pick among a row's `local` candidates (K16: kk <= 16)
   constexpr int NREG = PER > 0 ? PER : 1;
 
   // A row (r < nrows: the launch's rows number below 2^31): its local block
@@ -160,146 +167,214 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
                                              max(x.local, 0) * 4, kRawBufferFlags);
     return x;
   };
-  auto load = [&](const Row& x, int j) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(x.rs, 4 * lane + 256 * j, 0, 0));
+  // `lane` as a value the compiler cannot see through (an empty asm per use
+  // site): per-slot values derived from it (offsets, block ids) are then
+  // formed where they are used, from one register, instead of being hoisted
+  // out of the row loop into one register per slot
+  auto opaque_lane = [&]() {
+    int v = lane;
+    asm volatile("" : "+v"(v));
+    return v;
   };
-  // registers of a row's scores: issued now, used later
+  // slot j's score: the lane's byte offset plus an immediate 256 j
+  auto load_at = [&](const Row& x, int off, int j) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(x.rs, off + 256 * j, 0, 0));
+  };
+  auto load = [&](const Row& x, int j) { return load_at(x, 4 * opaque_lane(), j); };
+  // registers of a row's scores: issued now, used later (all PER slots: the
+  // ones past the row read 0 through the descriptor and touch no memory)
   auto fetch = [&](const Row& x, float (&v)[NREG]) {
     if constexpr (PER > 0) {
-      const int nj = (x.local + 63) >> 6;
+      const int off = 4 * opaque_lane();
 #pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if (j < nj) v[j] = load(x, j);
+      for (int j = 0; j < PER; ++j) v[j] = load_at(x, off, j);
     }
   };
 
-  Row cur = row_at(blockIdx.x * 4 + wave);
-  float vc[NREG];
-  fetch(cur, vc);
-  while (cur.r < nrows) {
-    const Row nxt = row_at(cur.r + stride);
-    float vn[NREG];
-    fetch(nxt, vn);
-    const int local = cur.local;
-    int32_t* dst = out + (int64_t)cur.r * k;
-    if (local < 0) {
-      // not a row of this batch
-    } else if (local + 1 <= k) {  // every visible block is kept
+  // One row: its block list from its candidate scores (in vc for PER > 0).
+  auto select_row = [&](const Row& x, float (&vc)[NREG]) {
+    const int local = x.local;
+    int32_t* dst = out + (int64_t)x.r * k;
+    if (local < 0) return;  // not a row of this batch
+    if (local + 1 <= k) {  // every visible block is kept
       for (int s = lane; s < k; s += 64) dst[s] = s <= local ? s : -1;
-    } else if (kk == 0) {
+      return;
+    }
+    if (kk == 0) {
       if (lane == 0) dst[0] = local;
-    } else {
-      const int nj = (local + 63) >> 6;  // score slots in use (uniform)
-      // f(j, score of block lane + 64 j) for j = 0 .. nj-1, in order; only the
-      // last slot can reach past the candidates
-      if constexpr (PER > 0) {  // the last slot's scores past the candidates become -inf, in place
+      return;
+    }
+    const int nj = (local + 63) >> 6;  // score slots in use (uniform)
+    // the registers' scores past the candidates (they read 0) become -inf, in place
+    auto mask_tail = [&]() {
+      if constexpr (PER > 0) {
+        int lim = local;
+        asm volatile("" : "+s"(lim));  // keeps the compares on the paths that mask
+        const int lv = opaque_lane();
+#pragma unroll
+        for (int j = 0; j < PER; ++j) vc[j] = lv < lim - 64 * j ? vc[j] : NEG_INF;
+      }
+    };
+    // f(j, score of block lane + 64 j) for j = 0 .. nj-1, in order; only the
+    // last slot can reach past the candidates (registers: as they stand)
+    auto each_score = [&](auto&& f) {
+      if constexpr (PER > 0) {
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-          if (j == nj - 1) vc[j] = lane + 64 * j < local ? vc[j] : NEG_INF;
-      }
-      auto each_score = [&](auto&& f) {
-        if constexpr (PER > 0) {
+          if (j < nj) f(j, vc[j]);
+      } else {
+        for (int j0 = 0; j0 < nj; j0 += 8) {  // eight loads in flight per step
+          float v[8];
 #pragma unroll
-          for (int j = 0; j < PER; ++j)
-            if (j < nj) f(j, vc[j]);
-        } else {
-          for (int j0 = 0; j0 < nj; j0 += 8) {  // eight loads in flight per step
-            float v[8];
+          for (int u = 0; u < 8; ++u) v[u] = load(x, j0 + u);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = load(cur, j0 + u);
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-              if (j0 + u < nj) f(j0 + u, lane + 64 * (j0 + u) < local ? v[u] : NEG_INF);
-          }
+          for (int u = 0; u < 8; ++u)
+            if (j0 + u < nj) f(j0 + u, lane + 64 * (j0 + u) < local ? v[u] : NEG_INF);
         }
-      };
+      }
+    };
+    auto reg_max = [&]() {
+      float mx = vc[0];
+#pragma unroll
+      for (int j = 1; j < NREG; ++j) mx = fmaxf(mx, vc[j]);
+      return mx;
+    };
 
-      // 1. tau: for kk <= 16, the smallest over the four rows of 16 lanes of
-      // the row's m-th largest lane maximum (m = ceil(kk / 4)): 4 m >= kk lane
-      // maxima are >= tau, and the 16-lane sorts are DPP moves only; else the
-      // kk-th largest lane maximum
-      float mx = NEG_INF;
-      each_score([&](int, float c) { mx = fmaxf(mx, c); });
-      float tau;
-      if (PER > 0 && kk <= 16) {  // rows in registers (streamed rows keep the tighter tau: fewer candidates)
+    // 1. tau from the lane maxima mx: for kk <= 16, the smallest over the four
+    // rows of 16 lanes of the row's m-th largest lane maximum (m = ceil(kk /
+    // 4)): 4 m >= kk lane maxima are >= tau, and the 16-lane sorts are DPP
+    // moves only; else the kk-th largest lane maximum
+    auto tau_of = [&](float mx) {
+      if constexpr (PER > 0 && K16) {  // rows in registers (streamed rows keep the tighter tau: fewer candidates)
         const float srt = sort_lanes<16>(mx, lane);
         const int pos = 16 - ((kk + 3) >> 2);
-        tau = fminf(fminf(lane_f32(srt, pos), lane_f32(srt, 16 + pos)),
-                    fminf(lane_f32(srt, 32 + pos), lane_f32(srt, 48 + pos)));
-      } else {
-        tau = lane_f32(sort_lanes<64>(mx, lane), 64 - kk);
+        return fminf(fminf(lane_f32(srt, pos), lane_f32(srt, 16 + pos)),
+                     fminf(lane_f32(srt, 32 + pos), lane_f32(srt, 48 + pos)));
       }
-
-      // 2. scores >= tau, compacted in ascending block order (slot 63 takes
-      // the overflow of a row with more than 64, whose list is not used)
-      int total = 0;
-      each_score([&](int j, float c) {
-        const bool take = c >= tau;
-        const uint64_t m = __ballot(take);
-        if (m) {
-          const int slot = prefix(m, total);
-          if (take) cand[wave][slot < 63 ? slot : 63] = make_uint2(__float_as_uint(c), (uint32_t)(lane + 64 * j));
-          total += __popcll(m);
-        }
-      });
-      if (total <= 64) {
-        wave_lds_sync();
-        const bool have = lane < total;
-        const uint2 e = cand[wave][lane];
-        const float c = have ? __uint_as_float(e.x) : NEG_INF;
-        // T from a sorted copy of the candidates: a network over the first 16
-        // or 32 lanes when they hold them all (uniform branch on total)
-        float thr;
-        if (total <= 16 && kk <= 16)
-          thr = lane_f32(sort_lanes<16>(c, lane), 16 - kk);
-        else if (total <= 32 && kk <= 32)
-          thr = lane_f32(sort_lanes<32>(c, lane), 32 - kk);
-        else
-          thr = lane_f32(sort_lanes<64>(c, lane), 64 - kk);
-        // 3. emit: scores > T, then scores == T in block order until kk
-        const uint64_t meq = __ballot(have && c == thr);
-        const int need_eq = kk - count(have && c > thr);
-        const bool take = have && (c > thr || (c == thr && prefix(meq) < need_eq));
-        const uint64_t m = __ballot(take);
-        if (take) dst[prefix(m)] = (int)e.y;
-      } else {
-        // many equal scores: T = the largest key x with #{keys >= x} >= kk, bit by bit
-        uint32_t thr = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-          const uint32_t trial = thr | (1u << bit);
-          int n = 0;
-          each_score([&](int, float c) { n += count(sel_key(c) >= trial); });
-          if (n >= kk) thr = trial;
-        }
-        int n_gt = 0;
-        each_score([&](int, float c) { n_gt += count(sel_key(c) > thr); });
-        const int need_eq = kk - n_gt;  // >= 1 keys equal to T are taken
-        int base = 0, eq_seen = 0;
-        each_score([&](int j, float c) {
-          const uint32_t u = sel_key(c);
-          const bool eq = u == thr;
-          const uint64_t meq = __ballot(eq);
-          const bool take = u > thr || (eq && prefix(meq, eq_seen) < need_eq);
-          const uint64_t m = __ballot(take);
-          if (take) dst[prefix(m, base)] = lane + 64 * j;
-          base += __popcll(m);
-          eq_seen += __popcll(meq);
-        });
+      return lane_f32(sort_lanes<64>(mx, lane), 64 - kk);
+    };
+    float tau;
+    if constexpr (PER > 0) {
+      // First from the registers as loaded, the offsets past the candidates
+      // reading 0.  If tau > 0, each lane maximum >= tau is a candidate's
+      // score (so at least kk candidates reach tau) and no 0 passes `>= tau`:
+      // the row needs no masking.  Otherwise mask and take tau again.
+      tau = tau_of(reg_max());
+      if (!(tau > 0.0f)) {
+        mask_tail();
+        tau = tau_of(reg_max());
       }
-      if (lane == 0) dst[kk] = local;
-      wave_lds_sync();  // the list is read before the next row overwrites it
+    } else {
+      float mx = NEG_INF;
+      each_score([&](int, float c) { mx = fmaxf(mx, c); });
+      tau = tau_of(mx);
     }
-    cur = nxt;
-#pragma unroll
-    for (int j = 0; j < NREG; ++j) vc[j] = vn[j];
+
+    // 2. scores >= tau, compacted in ascending block order
+    int total = 0;
+    const int lane_v = opaque_lane();
+    each_score([&](int j, float c) {
+      const bool take = c >= tau;
+      const uint64_t m = __ballot(take);
+      float* at = &cand[wave][0][min(total, 64)];  // uniform
+      if (take) {
+        const int p = prefix(m);
+        at[p] = c;
+        at[128 + p] = __int_as_float(lane_v + 64 * j);
+      }
+      total += __popcll(m);
+    });
+    if (total <= 64) {
+      wave_lds_sync();
+      const bool have = lane < total;
+      const float c = have ? cand[wave][0][lane] : NEG_INF;
+      // T from a sorted copy of the candidates: a network over the first 16
+      // or 32 lanes when they hold them all (uniform branch on total)
+      float thr;
+      if (K16 && total <= 16)
+        thr = lane_f32(sort_lanes<16>(c, lane), 16 - kk);
+      else if (total <= 32 && kk <= 32)
+        thr = lane_f32(sort_lanes<32>(c, lane), 32 - kk);
+      else
+        thr = lane_f32(sort_lanes<64>(c, lane), 64 - kk);
+      // 3. emit: scores > T, then scores == T in block order until kk
+      const uint64_t meq = __ballot(have && c == thr);
+      const int need_eq = kk - count(have && c > thr);
+      const bool take = have && (c > thr || (c == thr && prefix(meq) < need_eq));
+      const uint64_t m = __ballot(take);
+      if (take) dst[prefix(m)] = __float_as_int(cand[wave][1][lane]);
+    } else {
+      // many equal scores: T = the largest key x with #{keys >= x} >= kk, bit by bit
+      mask_tail();
+      uint32_t thr = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t trial = thr | (1u << bit);
+        int n = 0;
+        each_score([&](int, float c) { n += count(sel_key(c) >= trial); });
+        if (n >= kk) thr = trial;
+      }
+      int n_gt = 0;
+      each_score([&](int, float c) { n_gt += count(sel_key(c) > thr); });
+      const int need_eq = kk - n_gt;  // >= 1 keys equal to T are taken
+      int base = 0, eq_seen = 0;
+      each_score([&](int j, float c) {
+        const uint32_t u = sel_key(c);
+        const bool eq = u == thr;
+        const uint64_t meq = __ballot(eq);
+        const bool take = u > thr || (eq && prefix(meq, eq_seen) < need_eq);
+        const uint64_t m = __ballot(take);
+        if (take) dst[prefix(m, base)] = lane_v + 64 * j;
+        base += __popcll(m);
+        eq_seen += __popcll(meq);
+      });
+    }
+    if (lane == 0) dst[kk] = local;
+    wave_lds_sync();  // the list is read before the next row overwrites it
+  };
+
+  // rows stride apart; with registers, two sets take turns (one selected
+  // while the other loads), so that no copy moves the next row's scores
+  Row cur = row_at(blockIdx.x * 4 + wave);
+  float va[NREG], vb[NREG];
+  if constexpr (PER > 0) {
+    fetch(cur, va);
+    while (cur.r < nrows) {
+      Row nxt = row_at(cur.r + stride);
+      fetch(nxt, vb);
+      select_row(cur, va);
+      cur = nxt;
+      if (cur.r >= nrows) break;
+      nxt = row_at(cur.r + stride);
+      fetch(nxt, va);
+      select_row(cur, vb);
+      cur = nxt;
+    }
+  } else {
+    for (; cur.r < nrows; cur = row_at(cur.r + stride)) select_row(cur, va);
   }
 }
 
 }  // namespace
 
+// Workgroups of one k_block_topk instantiation resident per CU (at most 8):
+// the grid is that many per CU, so that every wave is resident and walks its
+// share of the rows from the start.
+template <int P, bool V, bool K>
+int topk_blocks_per_cu() {
+  static int nb = 0;
+  if (nb == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void*>(&k_block_topk<P, V, K>), 256,
+                                                     0) != hipSuccess ||
+        v <= 0)
+      v = 1;
+    nb = std::min(v, 8);
+  }
+  return nb;
+}
+
 hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims& D, hipStream_t stream) {
   const int64_t nrows = (int64_t)D.B * D.h_kv * D.n_q;
-  // resident waves that walk the rows: up to 8 workgroups of 4 waves per CU
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, n = 0;
@@ -308,14 +383,22 @@ hipError_t launch_block_topk(const float* pooled, int32_t* block_idx, const Dims
       n = 256;
     cus = n;
   }
-  const dim3 grid((unsigned)std::min<int64_t>((nrows + 3) / 4, (int64_t)cus * 8)), block(256);
+  const dim3 block(256);
   const int n = (int)nrows;  // below 2^31 (the problem's row count is checked on the host)
   // scores per lane for the longest row (rows are at most n_blk - 1 candidates)
   const int per = (D.n_blk + 63) / 64;
-  auto go = [&](auto per_c, auto vl) {
-    hipLaunchKernelGGL((k_block_topk<decltype(per_c)::value, decltype(vl)::value>), grid, block, 0, stream, pooled,
-                       block_idx, D, n);
+  auto run = [&](auto per_c, auto vl, auto k16) {
+    constexpr int P = decltype(per_c)::value;
+    constexpr bool V = decltype(vl)::value, K = decltype(k16)::value;
+    const dim3 grid((unsigned)std::min<int64_t>((nrows + 3) / 4, (int64_t)cus * topk_blocks_per_cu<P, V, K>()));
+    hipLaunchKernelGGL((k_block_topk<P, V, K>), grid, block, 0, stream, pooled, block_idx, D, n);
     mark("k_block_topk", stream);
+  };
+  auto go = [&](auto per_c, auto vl) {
+    if (decltype(per_c)::value > 0 && D.k - 1 <= 16)
+      run(per_c, vl, std::integral_constant<bool, (decltype(per_c)::value > 0)>{});
+    else
+      run(per_c, vl, std::false_type{});
   };
   auto pick = [&](auto vl) {
     if (per <= 4) go(std::integral_constant<int, 4>{}, vl);
