@@ -47,7 +47,8 @@ __device__ __forceinline__ uint32_t sel_key(float f) {
 // Within a row of 16 lanes they are DPP moves (no LDS): ^1, ^2 and ^3 are
 // quad permutes, ^7 and ^15 the half-row and row mirrors, ^8 a rotate of the
 // row by 8, ^4 the half-row mirror followed by the quad flip.  Across rows:
-// ^16 and ^31 by ds_swizzle (xor within 32 lanes), ^63 by ds_bpermute.
+// ^16 and ^31 by ds_swizzle (xor within 32 lanes), ^63 by ds_bpermute (the
+// permlane swaps of gfx950 time the same here, with more VALU work).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {  // every lane's source is in its row: no bound control needed
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
@@ -127,8 +128,15 @@ __device__ __forceinline__ int prefix(uint64_t m, int base = 0) {
 // registers, the next row's while the current one is selected; PER == 0 (rows
 // beyond 2048 blocks): each of the two passes over the row streams it, eight
 // loads in flight (the second pass mostly from L2).
+// Waves per SIMD the register budget is fitted to: eight (64 VGPRs) while the
+// row fits 16 slots, four beyond (the 32-slot rows' two register sets).  The
+// kernel waits mostly on its loads, and eight waves keep twice the rows in
+// flight of the five or six the unconstrained allocation leaves room for.
+template <int PER>
+constexpr int topk_waves() { return PER > 16 ? 4 : 8; }
+
 template <int PER, bool VL, bool K16>
-__global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ pooled, int32_t* __restrict__ out,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(topk_waves<PER>(), 8))) void k_block_topk(const float* __restrict__ pooled, int32_t* __restrict__ out,
                                                     Dims D, int nrows) {
   // scores >= tau ([w][0][i]) and their blocks' bits ([w][1][i]): a slot's
   // scores are written from entry min(total, 64) on, so the list holds the
@@ -146,25 +154,52 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
   // A row (r < nrows: the launch's rows number below 2^31): its local block
   // (-1: nothing to do) and the descriptor of its candidate scores (offsets
   // past the candidates read 0 and never leave them).
+  // Rows carry their query index i = r mod n_q and, varlen, their sequence b
+  // and offset rb = r mod (h_kv n_q) inside it; the walk advances them by the
+  // stride's quotient and remainder instead of dividing each row.
   struct Row {
-    int r, local;
+    int r, i, b, rb, local;
     __amdgpu_buffer_rsrc_t rs;
+  };
+  const int per_seq = D.h_kv * D.n_q;  // rows of one sequence
+  const int step_i = stride % D.n_q, step_rb = stride % per_seq, step_b = stride / per_seq;
+  auto finish = [&](Row& x) {
+    x.local = -1;
+    if (x.r < nrows) {
+      if constexpr (VL) {
+        if (x.i < seq_nq(D, x.b)) x.local = (int)((seq_offset(D, x.b) + x.i) / kBk);  // rows past a sequence's queries: none
+      } else {
+        x.local = (int)((D.offset + x.i) / kBk);
+      }
+    }
+    x.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(pooled + (int64_t)x.r * D.n_blk), (short)0,
+                                             max(x.local, 0) * 4, kRawBufferFlags);
   };
   auto row_at = [&](int r) {
     Row x;
     x.r = r;
-    x.local = -1;
-    if (r < nrows) {
-      const int i = r % D.n_q;
-      if constexpr (VL) {
-        const int b = r / (D.h_kv * D.n_q);
-        if (i < seq_nq(D, b)) x.local = (int)((seq_offset(D, b) + i) / kBk);  // rows past a sequence's queries: none
-      } else {
-        x.local = (int)((D.offset + i) / kBk);
+    x.i = r % D.n_q;
+    x.b = r / per_seq;
+    x.rb = r % per_seq;
+    finish(x);
+    return x;
+  };
+  auto next_row = [&](const Row& c) {
+    Row x;
+    x.r = c.r + stride;
+    x.i = c.i + step_i;
+    if (x.i >= D.n_q) x.i -= D.n_q;
+    if constexpr (VL) {
+      x.rb = c.rb + step_rb;
+      x.b = c.b + step_b;
+      if (x.rb >= per_seq) {
+        x.rb -= per_seq;
+        ++x.b;
       }
+    } else {
+      x.b = x.rb = 0;
     }
-    x.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(pooled + (int64_t)r * D.n_blk), (short)0,
-                                             max(x.local, 0) * 4, kRawBufferFlags);
+    finish(x);
     return x;
   };
   // `lane` as a value the compiler cannot see through (an empty asm per use
@@ -339,18 +374,18 @@ __global__ __launch_bounds__(256) void k_block_topk(const float* __restrict__ po
   if constexpr (PER > 0) {
     fetch(cur, va);
     while (cur.r < nrows) {
-      Row nxt = row_at(cur.r + stride);
+      Row nxt = next_row(cur);
       fetch(nxt, vb);
       select_row(cur, va);
       cur = nxt;
       if (cur.r >= nrows) break;
-      nxt = row_at(cur.r + stride);
+      nxt = next_row(cur);
       fetch(nxt, va);
       select_row(cur, vb);
       cur = nxt;
     }
   } else {
-    for (; cur.r < nrows; cur = row_at(cur.r + stride)) select_row(cur, va);
+    for (; cur.r < nrows; cur = next_row(cur)) select_row(cur, va);
   }
 }
 
