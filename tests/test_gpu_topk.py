@@ -129,3 +129,59 @@ def test_ties_at_the_threshold():
         pooled[0, 0, r, perm[:10]] = 100.0 + np.arange(10)
         pooled[0, 0, r, perm[10:30]] = 50.0
     check(pooled, n_q, n_kv, 1, 16, name="threshold ties")
+
+
+# Rows of 2049 .. 8192 blocks are selected by a workgroup of eight waves, 1024
+# blocks each.  In one 5000-block launch: rows whose candidates end inside the
+# first wave (a few blocks, or hundreds), across the first wave boundary and in
+# later waves; with negative scores (the masked path), k above 17 (the 64-lane
+# threshold) and lane-periodic scores (the exact search, which one wave streams).
+@pytest.mark.parametrize("case", ["random", "negative", "k40", "periodic"])
+def test_workgroup_rows(case):
+    rng = np.random.default_rng(3800 + ["random", "negative", "k40", "periodic"].index(case))
+    n_blk, n_q = 5000, 192
+    n_kv = 128 * n_blk
+    k = 40 if case == "k40" else 16
+    for off_blk in (16, 900, 1024, 3000, 4800):
+        off = 128 * off_blk - 37
+        if case == "periodic":
+            row = -(np.arange(n_blk) % 64).astype(np.float32)
+            pooled = np.broadcast_to(row, (1, 2, n_q, n_blk)).copy()
+        else:
+            pooled = rng.standard_normal((1, 2, n_q, n_blk)).astype(np.float32) * 10
+            pooled[0, 1] = np.round(pooled[0, 1])   # ties in the second group
+            if case == "negative":
+                pooled = -np.abs(pooled) - 1.0
+        check(pooled, n_q, n_kv, 2, k, q_offset=off, name=f"workgroup rows, {case}, from block {off_blk}")
+
+
+def test_varlen_long_rows():
+    """msa_block_topk_v with caches of up to 5469 blocks (the workgroup path,
+    its variable-length instantiation): every sequence's rows equal the
+    oracle's selection, and rows past a sequence's queries stay untouched."""
+    import torch
+    seqs = [(100, 300000), (57, 700000), (0, 5000), (3, 400)]  # (queries, cache length) per sequence
+    B, h_kv, k = len(seqs), 2, 16
+    qo = [q for q, _ in seqs]
+    kv = [c for _, c in seqs]
+    p = msa.Problem.make(B, max(qo), max(kv), 8 * h_kv, h_kv, topk=k)
+    say(f"[gpu] top-k varlen long rows: seqs={seqs} n_blk={p.n_blk}")
+    rng = np.random.default_rng(3900)
+    pooled_np = (rng.standard_normal((B, h_kv, max(qo), p.n_blk)) * 10).astype(np.float32)
+    pooled_np[:, 1] = np.round(pooled_np[:, 1])  # ties in the second group
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    starts = np.concatenate([[0], np.cumsum(qo)[:-1]]).astype(int)
+    vl = msa.Varlen.make(qo_lens=i32(qo), kv_lens=i32(kv), q_starts=i32(starts.tolist()), total_q=int(sum(qo)))
+    bidx = torch.full((B, h_kv, max(qo), k), -77, dtype=torch.int32, device="cuda")
+    msa.block_topk(p, torch.from_numpy(pooled_np).cuda(), bidx, varlen=vl)
+    got = bidx.cpu().numpy()
+    for b, (q_b, kv_b) in enumerate(seqs):
+        assert (got[b, :, q_b:] == -77).all()
+        if q_b == 0:
+            continue
+        pos = kv_b - q_b + np.arange(q_b)
+        vis = np.arange(p.n_blk)[None, :] <= (pos // 128)[:, None]
+        for g in range(h_kv):
+            ref = oracle.select(np.where(vis, pooled_np[b, g, :q_b].astype(np.float64), np.nan), pos, 128, k)
+            bad = np.nonzero(np.any(ref != got[b, g, :q_b], axis=1))[0]
+            assert bad.size == 0, f"sequence {b} group {g} rows {bad[:5]}"
