@@ -5,20 +5,25 @@
 // the query is always included) and section 内核协同设计 (softmax preserves the
 // order, so the selection runs on the raw scores with no max, exp or sum).
 //
-// One wavefront per (sequence, group, query) row; the waves stay resident and
-// walk the rows, the next row's scores loading while the current one is
-// selected.  Scores are compared as fp32 values (-0 equals +0; lanes and slots
-// without a candidate hold -inf, and pooled scores are finite).  Selection:
+// One wavefront per (sequence, group, query) row for rows of up to 2048
+// blocks (k_block_topk), one workgroup of eight waves per row for rows of up
+// to 8192 (k_block_topk_wg), one wavefront streaming the row beyond that.  The
+// waves stay resident and walk the rows, the next row's scores loading while
+// the current one is selected.  Scores are compared as fp32 values (-0 equals
+// +0; lanes and slots without a candidate hold -inf, and pooled scores are
+// finite).  Selection:
 //   0. the row's candidate scores (blocks t < l, l = the local block; block t
 //      = lane + 64 j) are loaded into registers through a buffer descriptor
-//      whose range is the row;
+//      whose range is the row (offsets past it read 0);
 //   1. each lane takes the max of its share of the row, and tau is a value
 //      that at least k-1 lane maxima reach: for k-1 <= 16 and rows held in
-//      registers the smallest over the
-//      four rows of 16 lanes of each row's ceil((k-1)/4)-th largest (sorts of
-//      16 lanes, DPP moves only), else the (k-1)-th largest of all 64 (a
-//      sorting network, mostly DPP moves).  At least k-1 scores of the row are
-//      >= tau, and for score rows of any shape only a few dozen more;
+//      registers the smallest over the four rows of 16 lanes of each row's
+//      ceil((k-1)/4)-th largest (sorts of 16 lanes, DPP moves only), else the
+//      (k-1)-th largest of all 64 (a sorting network, mostly DPP moves).  At
+//      least k-1 scores of the row are >= tau, and for score rows of any shape
+//      only a few dozen more.  Tau is first taken over the registers as
+//      loaded; only a row whose tau is not positive has its tail set to -inf
+//      and tau taken again;
 //   2. the scores >= tau are compacted into LDS in ascending block order with
 //      their block ids, one per lane, and T, the (k-1)-th largest of them, is
 //      read off a sorted copy (16, 32 or 64 lanes, as many as they need);
