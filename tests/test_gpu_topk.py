@@ -134,14 +134,18 @@ def test_ties_at_the_threshold():
 # Rows of 2049 .. 8192 blocks are selected by a workgroup of eight waves, 1024
 # blocks each.  In one 5000-block launch: rows whose candidates end inside the
 # first wave (a few blocks, or hundreds), across the first wave boundary and in
-# later waves; with negative scores (the masked path), k above 17 (the 64-lane
-# threshold) and lane-periodic scores (the exact search, which one wave streams).
-@pytest.mark.parametrize("case", ["random", "negative", "k40", "periodic"])
+# later waves; with negative scores (the masked path), k of 1 (the local block
+# alone), 2, 40 and 64, and lane-periodic scores (the exact search, which one
+# wave streams).
+WG_CASES = ["random", "negative", "k40", "periodic", "k1", "k2", "k64"]
+
+
+@pytest.mark.parametrize("case", WG_CASES)
 def test_workgroup_rows(case):
-    rng = np.random.default_rng(3800 + ["random", "negative", "k40", "periodic"].index(case))
+    rng = np.random.default_rng(3800 + WG_CASES.index(case))
     n_blk, n_q = 5000, 192
     n_kv = 128 * n_blk
-    k = 40 if case == "k40" else 16
+    k = int(case[1:]) if case[0] == "k" else 16
     for off_blk in (16, 900, 1024, 3000, 4800):
         off = 128 * off_blk - 37
         if case == "periodic":
