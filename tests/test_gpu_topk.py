@@ -159,18 +159,29 @@ def test_workgroup_rows(case):
         check(pooled, n_q, n_kv, 2, k, q_offset=off, name=f"workgroup rows, {case}, from block {off_blk}")
 
 
-def test_varlen_long_rows():
-    """msa_block_topk_v with caches of up to 5469 blocks (the workgroup path,
-    its variable-length instantiation): every sequence's rows equal the
-    oracle's selection, and rows past a sequence's queries stay untouched."""
+# (queries, cache length) per sequence; the longest cache sets the row width:
+# 469 blocks (8 keys per lane), 1016 (16), 1954 (32), 5469 (the workgroup path)
+VARLEN_SEQS = {
+    "per8": [(60, 60000), (20, 33000), (2, 130)],
+    "per16": [(90, 130000), (41, 60000), (0, 5000), (3, 400)],
+    "per32": [(70, 250000), (33, 131000), (5, 900)],
+    "workgroup": [(100, 300000), (57, 700000), (0, 5000), (3, 400)],
+}
+
+
+@pytest.mark.parametrize("width", list(VARLEN_SEQS))
+def test_varlen_long_rows(width):
+    """msa_block_topk_v (the variable-length instantiations) on long caches:
+    every sequence's rows equal the oracle's selection, and rows past a
+    sequence's queries stay untouched."""
     import torch
-    seqs = [(100, 300000), (57, 700000), (0, 5000), (3, 400)]  # (queries, cache length) per sequence
+    seqs = VARLEN_SEQS[width]
     B, h_kv, k = len(seqs), 2, 16
     qo = [q for q, _ in seqs]
     kv = [c for _, c in seqs]
     p = msa.Problem.make(B, max(qo), max(kv), 8 * h_kv, h_kv, topk=k)
     say(f"[gpu] top-k varlen long rows: seqs={seqs} n_blk={p.n_blk}")
-    rng = np.random.default_rng(3900)
+    rng = np.random.default_rng(3900 + list(VARLEN_SEQS).index(width))
     pooled_np = (rng.standard_normal((B, h_kv, max(qo), p.n_blk)) * 10).astype(np.float32)
     pooled_np[:, 1] = np.round(pooled_np[:, 1])  # ties in the second group
     i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
