@@ -42,7 +42,7 @@ COUNTER_TRAFFIC = {
     "k_index_scores(top-k fused)": (3039874112, {"index_scores.hip": "d6c53c22822df47d", "common.h": "4c23e147ab3f19f0"}),
     "k_attn_tiles": (67269213640, {"sparse_attn.hip": "f272a14b21c87934", "fwd_tiles.h": "1f0a406284261b7e", "attn_tiles.h": "2f9107ca13d54488", "common.h": "4c23e147ab3f19f0"}),
     "k_attn_local_merge": (40981107304, {"sparse_attn.hip": "f272a14b21c87934", "fwd_tiles.h": "1f0a406284261b7e", "attn_tiles.h": "2f9107ca13d54488", "common.h": "4c23e147ab3f19f0"}),
-    "k_block_topk": (2286006155, {"block_topk.hip": "893cfd2da38a17f1", "common.h": "4c23e147ab3f19f0"}),
+    "k_block_topk": (2286006155, {"block_topk.hip": "52d43fa6ee7deeff", "common.h": "4c23e147ab3f19f0"}),
     "k_index_small": (4353107852, {"decode.hip": "6cb61b92818c32a7", "common.h": "4c23e147ab3f19f0"}),
     "k_attn_rows": (575066876, {"decode.hip": "6cb61b92818c32a7", "common.h": "4c23e147ab3f19f0"}),
 }

@@ -197,8 +197,8 @@ __device__ __forceinline__ void select_by_bits(EachScore&& each_score, int kk, i
 
 // PER > 0: a row's candidates (at most 64 * PER) are loaded once into
 // registers, the next row's while the current one is selected; PER == 0 (rows
-// beyond 2048 blocks): each of the two passes over the row streams it, eight
-// loads in flight (the second pass mostly from L2).
+// beyond 8192 blocks; k_block_topk_wg takes those of 2049 .. 8192): each of
+// the two passes over the row streams it, eight loads in flight.
 // Waves per SIMD the register budget is fitted to: eight (64 VGPRs) while the
 // row fits 16 slots, four beyond (the 32-slot rows' two register sets).  The
 // kernel waits mostly on its loads, and eight waves keep twice the rows in
@@ -207,8 +207,8 @@ template <int PER>
 constexpr int topk_waves() { return PER > 16 ? 4 : 8; }
 
 template <int PER, bool VL, bool K16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(topk_waves<PER>(), 8))) void k_block_topk(const float* __restrict__ pooled, int32_t* __restrict__ out,
-                                                    Dims D, int nrows) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(topk_waves<PER>(), 8))) void k_block_topk(
+    const float* __restrict__ pooled, int32_t* __restrict__ out, Dims D, int nrows) {
   // scores >= tau ([w][0][i]) and their blocks' bits ([w][1][i]): a slot's
   // scores are written from entry min(total, 64) on, so the list holds the
   // first 64 in order and a row with more (whose list is not used) stays
