@@ -30,6 +30,18 @@ struct KvRegs {
   u32x4 vr[4 * (512 / kThreads)];
 };
 
+// V unit c (0 .. 511): key quad kq (keys 4kq .. 4kq+3) and 16-byte dim chunk od
+// (dims 8od .. 8od+7).  A wave covers 8 key quads x 8 dim chunks, so that the
+// 32 lanes of each half-wave write their transposed words (row 8od + e of V^T,
+// keys 4kq ..) to 32 different bank pairs: with the rows 66 words apart, two
+// chunks 4 apart meet in a bank, and 16 chunks x 2 quads per half-wave met
+// four times in each.
+__device__ __forceinline__ void v_unit(int c, int& kq, int& od) {
+  const int w = c >> 6, l = c & 63;
+  kq = 8 * (w & 3) + (l & 7);
+  od = 8 * (w >> 2) + (l >> 3);
+}
+
 __device__ __forceinline__ void kv_load(KvRegs& x, const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
                                         int n_valid) {
   constexpr int KPER = 2048 / kThreads, VPER = 512 / kThreads;
@@ -45,7 +57,8 @@ __device__ __forceinline__ void kv_load(KvRegs& x, const uint16_t* __restrict__ 
 #pragma unroll
   for (int u = 0; u < VPER; ++u) {
     const int c = tid + kThreads * u;
-    const int kq = c >> 4, od = c & 15;
+    int kq, od;
+    v_unit(c, kq, od);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t off = (uint32_t)min(kq * 4 + q, n_valid - 1) * 256u + 16u * od;
@@ -65,7 +78,8 @@ __device__ __forceinline__ void kv_store(uint16_t* Ks, uint16_t* Vt, const KvReg
 #pragma unroll
   for (int u = 0; u < VPER; ++u) {  // transposed: Vt[d][key]
     const int c = tid + kThreads * u;
-    const int kq = c >> 4, od = c & 15;
+    int kq, od;
+    v_unit(c, kq, od);
     uint32_t w[4][4];  // by value: words of the four keys' 16-byte chunks
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
