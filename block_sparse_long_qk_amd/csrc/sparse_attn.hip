@@ -612,22 +612,33 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int64_t prow = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1);
     const float* lse_p = ws.part_lse + prow * D.G + hh;                                   // slot s at s * G
     const uint16_t* o_p = ws.part_o + prow * D.G * kHeadDim + (8 * half * D.G + hh) * 8;  // slot s at s * G * 128
-    auto load_slot = [&](int s0, float& ls, uint4 (&x)[8]) {  // past slot k-1: weight 0
-      const int sl = min(s0, D.k - 1);
-      ls = s0 < D.k ? lse_p[(int64_t)sl * D.G] : NEG_INF;
-      const uint16_t* src = o_p + (int64_t)sl * D.G * kHeadDim;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {  // read once: streamed past the caches
-        const u32x4 y = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + u * D.G * 8));
-        x[u] = make_uint4(y.x, y.y, y.z, y.w);
-      }
-    };
     float lv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float x = lse_p[(int64_t)min(j, D.k - 1) * D.G];
       lv[j] = j < D.k ? x : NEG_INF;
     }
+    // slots 0 .. 15 that hold a partial: the local block's slot, the padding
+    // and the slots past k-1 hold none, and their values are not read
+    uint32_t has = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) has |= (lv[j] != NEG_INF ? 1u : 0u) << j;
+    auto load_slot = [&](int s0, float& ls, uint4 (&x)[8]) {  // past slot k-1: weight 0
+      const int sl = min(s0, D.k - 1);
+      ls = s0 < D.k ? lse_p[(int64_t)sl * D.G] : NEG_INF;
+      const bool used = s0 < 16 ? ((has >> s0) & 1u) != 0 : ls != NEG_INF;
+      const uint16_t* src = o_p + (int64_t)sl * D.G * kHeadDim;
+      if (used) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {  // read once: streamed past the caches
+          const u32x4 y = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + u * D.G * 8));
+          x[u] = make_uint4(y.x, y.y, y.z, y.w);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    };
 
     if (cur.bg != staged_bg || cur.t != staged_t) {  // uniform
       if (!fresh) lds_barrier();
