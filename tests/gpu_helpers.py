@@ -1,7 +1,7 @@
 """Helpers of the GPU parity tests: run the HIP path through the C ABI and
 compare it with the fp64 oracle on the same seeded inputs.
 
-The tolerances are the ones the task fixes: block indices bit-exact where the
+The tolerances: block indices bit-exact where the
 gap between the (k-1)-th and k-th best non-local pooled score exceeds 1e-3
 (relative), epsilon-valid inside that gap; outputs within max |d| <= 1e-2 and
 mean |d| <= 1e-3 of the oracle run on the same block set.  Pooled scores must

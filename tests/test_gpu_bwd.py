@@ -4,8 +4,9 @@ fp64 oracle (oracle_attend_bwd, pinned to torch autograd).
 The forward runs on the GPU (block_idx, out, lse); the output gradient is a
 seeded synthetic tensor.  Small cases compare dq, dk and dv element by
 element with the oracle run over every row and head of each group (the
-GPU's own selection); the 32K workload compares dq on sampled rows and checks
-the exact sum rules sum_j dv_j = sum dO and sum_j dk_j = 0 per group.
+GPU's own selection); the 32K and 128K workloads compare dq on sampled rows,
+dk and dv of one key block against the oracle over every row that attends it,
+and check the exact sum rules sum_j dv_j = sum dO and sum_j dk_j = 0 per group.
 
 Tolerance: the kernels feed P and dS to the MFMA as bf16 (relative error
 2^-9 each), accumulate in fp32 and round the results (and the dq partials)
@@ -82,13 +83,36 @@ def test_backward_matches_oracle(w):
             close(f"dv b{b} g{g}", dv[b, g].float().cpu().numpy(), rdv)
 
 
-def test_backward_32k_sampled_and_sum_rules():
+def check_block_grads(w, res, dk, dv, t):
+    """dk and dv of key block t, exactly: the oracle over every row of each group
+    whose block set holds t (the rows that picked it and the block's own
+    positions), the only rows whose gradients reach its keys."""
+    G = w.group
+    j0, j1 = t * w.block_size, min((t + 1) * w.block_size, w.n_kv)
+    for g in range(w.h_kv):
+        sel_all = res["block_idx"][0, g].cpu().numpy()
+        rows = np.nonzero((sel_all == t).any(axis=1))[0]
+        assert len(rows) > 0
+        xr = oracle.inputs_for_rows(w, 0, g, rows)
+        sel = sel_all[rows]
+        K, V = oracle.kv_for_blocks(w, 0, g, sel)
+        dO = synth.host_do_rows(w, 0, rows)[:, g * G:(g + 1) * G, :]
+        _, rdk, rdv = oracle.attend_bwd(xr["q"], xr["pos"], sel, K, V, w.block_size, w.scale, dO)
+        close(f"dk block {t} g{g} ({len(rows)} rows)", dk[0, g, j0:j1].float().cpu().numpy(), rdk[j0:j1])
+        close(f"dv block {t} g{g}", dv[0, g, j0:j1].float().cpu().numpy(), rdv[j0:j1])
+
+
+@pytest.mark.parametrize("name,n_rand", [("prefill_32k", 32), ("prefill_128k", 16)])
+def test_backward_full_size_sampled_and_sum_rules(name, n_rand):
+    """At 32K and at the benchmarked 128K: dq on sampled rows, dk and dv of one
+    late key block exactly, and the sum rules over every key."""
     import torch
-    w = synth.WORKLOADS["prefill_32k"]
+    w = synth.WORKLOADS[name]
+    say(f"[gpu] backward {name}: dq on {n_rand} sampled rows, block {w.n_blk - 24} exactly, sum rules")
     res = run_gpu(w, with_forward=False)
     dout, dq, dk, dv = run_bwd(w, res)
     G = w.group
-    rows = sample_rows(w, 32, seed=w.seed, whole_blocks=0)
+    rows = sample_rows(w, n_rand, seed=w.seed, whole_blocks=0)
     # dq of sampled rows: the oracle over the rows' own blocks (dk, dv are not compared here)
     worst = 0.0
     for g in range(w.h_kv):
@@ -110,6 +134,8 @@ def test_backward_32k_sampled_and_sum_rules():
     assert bool(((dv_sum - do_sum).abs() <= 1e-2 * scale_v).all())
     assert bool((dk_sum.abs() <= 1e-2 * scale_k).all())
     assert bool(torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all())
+    # a late block: picked by few rows besides its own, so the exact check stays cheap
+    check_block_grads(w, res, dk, dv, w.n_blk - 24)
 
 
 def test_backward_is_deterministic():

@@ -2,8 +2,8 @@
 visible token) against the fp64 oracle.
 
 msa_dense_attn_fwd is compared with oracle.dense_gqa (itself pinned to
-torch's scaled_dot_product_attention on the CPU) under the task's output
-tolerances; msa_dense_index_kl, fed the dense lse, with oracle.kl over all
+torch's scaled_dot_product_attention on the CPU) under the attention's output
+tolerances, on seven shapes and on sampled rows of the benchmarked 128K call; msa_dense_index_kl, fed the dense lse, with oracle.kl over all
 visible blocks under the KL tolerance of the sparse pass.  Two consistency
 checks tie dense and sparse mode together: with k * Bk >= n_kv the sparse
 calls select every block, so they must agree with the dense ones.
@@ -65,6 +65,30 @@ def test_dense_attention_matches_oracle(w):
             ref_o, ref_l = oracle.dense_gqa(q_rows, w.offset + rows, K, V, w.scale)
             st.add_out(out[b].index_select(0, idx)[:, g * G:(g + 1) * G].float().cpu().numpy(), ref_o)
             st.add_lse(lse[b, g * G:(g + 1) * G].index_select(1, idx).cpu().numpy().T, ref_l)
+    st.check()
+
+
+def test_dense_attention_128k_sampled():
+    """The benchmarked 128K dense call on sampled rows, all groups and heads:
+    the first and last positions (one key and every key visible), both sides of
+    the first block edge, and random positions."""
+    import torch
+    w = synth.WORKLOADS["prefill_128k"]
+    say(f"[gpu] dense attention {w.name}: sampled rows")
+    x, out, lse = dense_gpu(w)
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([[0, 127, 128, w.n_q - 1], rng.integers(0, w.n_q, 3)])).astype(np.int64)
+    st = Stats()
+    idx = torch.from_numpy(rows).cuda()
+    G = w.group
+    for g in range(w.h_kv):
+        q_rows = synth.host_q_rows(w, 0, rows)[:, g * G:(g + 1) * G, :]
+        n_seen = int(w.offset + rows.max()) + 1
+        K = synth.host_kv(w, "k", 0, g, 0, n_seen)
+        V = synth.host_kv(w, "v", 0, g, 0, n_seen)
+        ref_o, ref_l = oracle.dense_gqa(q_rows, w.offset + rows, K, V, w.scale)
+        st.add_out(out[0].index_select(0, idx)[:, g * G:(g + 1) * G].float().cpu().numpy(), ref_o)
+        st.add_lse(lse[0, g * G:(g + 1) * G].index_select(1, idx).cpu().numpy().T, ref_l)
     st.check()
 
 

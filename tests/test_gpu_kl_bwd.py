@@ -7,8 +7,9 @@ the KL backward then takes them through the C ABI.  Small cases compare
 d_index_q and d_index_k element by element with the oracle over every row of
 each group (the GPU's own selection; d_index_k is the sum of the groups'
 contributions, since the index keys are shared); one case takes random row
-weights dkl.  The 32K workload compares d_index_q on sampled rows and checks
-the sum rule: every row's g_j = w (s_j - t_j) sums to zero over T (student
+weights dkl.  The 32K and 128K workloads compare d_index_q on sampled rows
+and d_index_k of one key block against the oracle over every row (of every
+group) that attends it, and check the sum rule: every row's g_j = w (s_j - t_j) sums to zero over T (student
 and teacher are both distributions over T), so sum_j d_index_k[j] = 0.
 
 Tolerance: g enters the MFMA as bf16 (relative error 2^-9), the index inputs
@@ -111,13 +112,39 @@ def test_kl_backward_matches_oracle(w):
         assert np.all(got_ik[n_seen:] == 0.0), "keys past every row's position must get 0"
 
 
-def test_kl_backward_32k_sampled_and_sum_rule():
+def check_block_dik(w, res, d_ik, t):
+    """d_index_k of key block t, exactly: the index keys are shared by the
+    groups, so the oracle runs over every row of every group whose block set
+    holds t (the only rows whose gradients reach those keys) and the groups'
+    contributions are added."""
     import torch
-    w = synth.WORKLOADS["prefill_32k"]
+    j0, j1 = t * w.block_size, min((t + 1) * w.block_size, w.n_kv)
+    ref = np.zeros((j1 - j0, w.index_dim))
+    n_rows = 0
+    for g in range(w.h_kv):
+        sel_all = res["block_idx"][0, g].cpu().numpy()
+        rows = np.nonzero((sel_all == t).any(axis=1))[0]
+        assert len(rows) > 0
+        n_rows += len(rows)
+        x = oracle.inputs_for_rows(w, 0, g, rows)
+        sel = sel_all[rows]
+        K, _ = oracle.kv_for_blocks(w, 0, g, sel)
+        _, r_ik = oracle.kl_bwd(x["q"], x["pos"], sel, K, x["iq"], x["ik"], w.block_size, w.scale)
+        ref += r_ik[j0:j1]
+    got = d_ik[0].view(torch.bfloat16)[j0:j1].float().cpu().numpy()
+    close(f"d_ik block {t} ({n_rows} rows over the groups)", got, ref)
+
+
+@pytest.mark.parametrize("name,n_rand", [("prefill_32k", 32), ("prefill_128k", 16)])
+def test_kl_backward_full_size_sampled_and_sum_rule(name, n_rand):
+    """At 32K and at the benchmarked 128K: d_index_q on sampled rows, d_index_k
+    of one late key block exactly, and the sum rule over every key."""
+    import torch
+    w = synth.WORKLOADS[name]
     say(f"[gpu] kl backward {w.name}")
     res = run_gpu(w, with_forward=False)
     _, d_iq, d_ik = run_kl_bwd(w, res)
-    rows = sample_rows(w, 32, seed=w.seed, whole_blocks=0)
+    rows = sample_rows(w, n_rand, seed=w.seed, whole_blocks=0)
     for g in range(w.h_kv):
         x = oracle.inputs_for_rows(w, 0, g, rows)
         sel = res["block_idx"][0, g].cpu().numpy()[rows]
@@ -131,6 +158,7 @@ def test_kl_backward_32k_sampled_and_sum_rule():
     say(f"    sum rule: max |sum_j d_ik_j| / sum_j |d_ik_j| = {(total.abs() / mag).max().item():.2e}")
     assert bool(torch.isfinite(dik).all())
     assert bool((total.abs() <= 1e-2 * mag).all())
+    check_block_dik(w, res, d_ik, w.n_blk - 24)
 
 
 def test_kl_backward_is_deterministic():
@@ -239,14 +267,15 @@ def test_stored_teacher_and_its_backward_match_oracle(w):
         assert np.all(got_ik[n_seen:] == 0.0), "keys past every row's position must get 0"
 
 
-def test_stored_teacher_32k_sampled_sum_rule_and_determinism():
+@pytest.mark.parametrize("name,n_rand", [("prefill_32k", 32), ("prefill_128k", 16)])
+def test_stored_teacher_full_size_sampled_sum_rule_and_determinism(name, n_rand):
     import torch
-    w = synth.WORKLOADS["prefill_32k"]
+    w = synth.WORKLOADS[name]
     say(f"[gpu] stored teacher {w.name}")
     res = run_gpu(w, with_forward=False)
     _, lse_index, teacher = run_kl_teacher(w, res)
     d_iq, d_ik = run_kl_bwd_teacher(w, res, teacher, lse_index)
-    rows = sample_rows(w, 32, seed=w.seed + 1, whole_blocks=0)
+    rows = sample_rows(w, n_rand, seed=w.seed + 1, whole_blocks=0)
     tf = teacher.float().cpu().numpy()
     for g in range(w.h_kv):
         x = oracle.inputs_for_rows(w, 0, g, rows)
@@ -265,6 +294,7 @@ def test_stored_teacher_32k_sampled_sum_rule_and_determinism():
     say(f"    sum rule: max |sum_j d_ik_j| / sum_j |d_ik_j| = {(total.abs() / mag).max().item():.2e}")
     assert bool(torch.isfinite(dik).all())
     assert bool((total.abs() <= 1e-2 * mag).all())
+    check_block_dik(w, res, d_ik, w.n_blk - 24)
     a_iq, a_ik = run_kl_bwd_teacher(w, res, teacher, lse_index)
     assert torch.equal(a_iq.view(torch.int16), d_iq.view(torch.int16))
     assert torch.equal(a_ik.view(torch.int16), d_ik.view(torch.int16))
