@@ -3,10 +3,12 @@ visible token) against the fp64 oracle.
 
 msa_dense_attn_fwd is compared with oracle.dense_gqa (itself pinned to
 torch's scaled_dot_product_attention on the CPU) under the attention's output
-tolerances, on seven shapes and on sampled rows of the benchmarked 128K call; msa_dense_index_kl, fed the dense lse, with oracle.kl over all
-visible blocks under the KL tolerance of the sparse pass.  Two consistency
-checks tie dense and sparse mode together: with k * Bk >= n_kv the sparse
-calls select every block, so they must agree with the dense ones.
+tolerances, on seven shapes and on sampled rows of the benchmarked 128K call;
+msa_dense_index_kl, fed the dense lse, with oracle.kl over all visible blocks
+under the KL tolerance of the sparse pass (four shapes, and sampled rows of
+the benchmarked 128K call).  Two consistency checks tie dense and sparse mode
+together: with k * Bk >= n_kv the sparse calls select every block, so they
+must agree with the dense ones.
 """
 import numpy as np
 import pytest
@@ -117,6 +119,37 @@ def test_dense_kl_matches_oracle(w):
             assert np.all(np.isfinite(got))
             assert np.all(err <= KL_ABS + KL_REL * np.abs(ref)), f"max |d| {err.max():.3e}"
             worst = max(worst, float(err.max()))
+    say(f"    dense KL max |d| = {worst:.3e}")
+
+
+def test_dense_kl_128k_sampled():
+    """The benchmarked 128K dense KL (fed the dense lse) on sampled rows of
+    every group: the first and last positions, both sides of the first block
+    edge, and random positions."""
+    import torch
+    w = synth.WORKLOADS["prefill_128k"]
+    say(f"[gpu] dense KL {w.name}: sampled rows")
+    x, out, lse = dense_gpu(w)
+    p = problem(w)
+    kl = torch.full((w.batch, w.h_kv, w.n_q), float("nan"), dtype=torch.float32, device="cuda")
+    msa.dense_index_kl(p, x["q"], x["k"], x["iq"], x["ik"], lse, kl)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed + 1)
+    rows = np.unique(np.concatenate([[0, 127, 128, w.n_q - 1], rng.integers(0, w.n_q, 3)])).astype(np.int64)
+    worst = 0.0
+    for g in range(w.h_kv):
+        xr = oracle.inputs_for_rows(w, 0, g, rows)
+        local = xr["pos"] // w.block_size
+        sel = np.full((len(rows), int(local.max()) + 1), -1, np.int32)
+        for r, l in enumerate(local):
+            sel[r, :l + 1] = np.arange(l + 1)
+        K = synth.host_kv(w, "k", 0, g, 0, int(xr["pos"].max()) + 1)
+        ref = oracle.kl(xr["q"], xr["pos"], sel, K, xr["iq"], xr["ik"], w.block_size, w.scale)
+        got = kl[0, g].cpu().numpy().astype(np.float64)[rows]
+        err = np.abs(got - ref)
+        assert np.all(np.isfinite(got))
+        assert np.all(err <= KL_ABS + KL_REL * np.abs(ref)), f"max |d| {err.max():.3e}"
+        worst = max(worst, float(err.max()))
     say(f"    dense KL max |d| = {worst:.3e}")
 
 

@@ -13,7 +13,7 @@ import pytest
 
 import block_sparse_long_qk_amd as msa
 import synth
-from gpu_helpers import Stats, check_rows, say
+from gpu_helpers import Stats, check_rows, problem, say
 
 pytestmark = pytest.mark.gpu
 
@@ -182,3 +182,45 @@ def test_varlen_uniform_equals_plain_call():
     assert torch.equal(outs[0]["block_idx"], outs[1]["block_idx"])
     assert torch.equal(outs[0]["out"].view(torch.int16), outs[1]["out"].view(torch.int16))
     assert torch.equal(outs[0]["lse"], outs[1]["lse"])
+
+
+def test_paged_128k_equals_contiguous():
+    """The benchmarked 128K prefill read from a page pool (k/v
+    [pages][h_kv][Bk][d], index_k [pages][Bk][d_idx], pages in a seeded random
+    order) gives the bits of the contiguous call, which test_gpu_parity checks
+    against the oracle at this size."""
+    import torch
+    w = synth.WORKLOADS["prefill_128k"]
+    say(f"[gpu] paged {w.name} against contiguous")
+    x = synth.device_inputs(w)
+    dev = x["q"].device
+    p = problem(w)
+    f = msa.alloc_outputs(p, dev)
+    msa.forward(p, x["q"], x["k"], x["v"], x["iq"], x["ik"], f["out"], f["block_idx"], f["lse"], f["workspace"])
+    torch.cuda.synchronize()
+    ref = {key: f[key].clone() for key in ("out", "block_idx", "lse")}
+    B, hk, bk, d, di, pps = w.batch, w.h_kv, w.block_size, w.head_dim, w.index_dim, w.n_blk
+    assert w.n_kv == pps * bk
+    perm = torch.from_numpy(np.random.default_rng(w.seed).permutation(B * pps)).to(dev)
+    pool = {}
+    for name, page_shape in (("k", (hk, bk, d)), ("v", (hk, bk, d)), ("ik", (bk, di))):
+        dst = torch.empty((B * pps,) + page_shape, dtype=torch.bfloat16, device=dev)
+        for b in range(B):
+            src = x[name][b].view(hk, pps, bk, d).transpose(0, 1) if name != "ik" else x[name][b].view(pps, bk, di)
+            dst.index_copy_(0, perm[b * pps:(b + 1) * pps], src)
+        pool[name] = dst
+    i32 = lambda a: a.to(torch.int32).contiguous()
+    vl = msa.Varlen.make(qo_lens=i32(torch.full((B,), w.n_q, device=dev)),
+                         kv_lens=i32(torch.full((B,), w.n_kv, device=dev)),
+                         q_starts=i32(torch.arange(B, device=dev) * w.n_q), total_q=B * w.n_q,
+                         page_table=i32(perm.view(B, pps)), num_pages=B * pps)
+    for key in ("out", "block_idx", "lse"):
+        f[key].fill_(-1)
+    msa.forward(p, x["q"], pool["k"], pool["v"], x["iq"], pool["ik"], f["out"], f["block_idx"], f["lse"],
+                f["workspace"], varlen=vl)
+    torch.cuda.synchronize()
+    assert torch.equal(ref["block_idx"], f["block_idx"])
+    assert torch.equal(ref["lse"], f["lse"])
+    assert torch.equal(ref["out"].view(torch.int16), f["out"].view(torch.int16))
+    del x, f, ref, pool
+    torch.cuda.empty_cache()
