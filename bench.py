@@ -104,11 +104,12 @@ def kernel_work(name, w, wk):
     Scoring and attention are MFMA-bound by the method (their FLOPs); the
     top-k is HBM-bound (its bytes).  The attention kernels also get the bytes
     their KV-outer design moves per (row, block) edge: the gathered query
-    rows (2 B x G x d) and the bf16 partial with its log-sum-exps, written by
-    the tiles and read by the merge."""
+    rows (2 B x G x d) and the partial (12-bit codes, 1.5 B x G x d) with its
+    exponents (4 B per head) and log-sum-exps (4 B per head), written by the
+    tiles and read by the merge."""
     G = w.h_q // w.h_kv
     edge_q = 2.0 * G * w.head_dim
-    edge_part = 2.0 * G * w.head_dim + 4.0 * G
+    edge_part = 1.5 * G * w.head_dim + 4.0 * G + 4.0 * G
     if name.startswith("k_index_scores"):
         return "mfma", wk["f_idx"], "flop", None
     if name == "k_index_small":   # decode: a stream over every index key

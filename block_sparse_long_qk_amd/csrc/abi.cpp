@@ -120,7 +120,9 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws, bool with_o = true)
   char* list = take(sizeof(int2) * max_tiles * D.pt);
   const int64_t pslots = (int64_t)D.B * D.h_kv * D.n_q * (D.k + 1);  // + the local slot
   char* part_lse = take(sizeof(float) * pslots * D.G);
-  char* part_o = with_o ? take(sizeof(uint16_t) * pslots * D.G * msa::kHeadDim) : nullptr;
+  // 12 bits per value (48 dwords per row and head) and two exponent bytes per lane pair
+  char* part_o = with_o ? take(sizeof(uint32_t) * pslots * D.G * (msa::kHeadDim * 12 / 32)) : nullptr;
+  char* part_ex = with_o ? take(sizeof(uint16_t) * pslots * D.G * 2) : nullptr;
   char* ctr = take(sizeof(int32_t) * msa::kWorkCounters);
   if (ws) {
     ws->hist = reinterpret_cast<int32_t*>(hist);
@@ -130,7 +132,8 @@ size_t attn_ws_layout(const Dims& D, char* base, AttnWs* ws, bool with_o = true)
     ws->tile_off = reinterpret_cast<int32_t*>(tile_off);
     ws->list = reinterpret_cast<int2*>(list);
     ws->part_lse = reinterpret_cast<float*>(part_lse);
-    ws->part_o = reinterpret_cast<uint16_t*>(part_o);
+    ws->part_o = reinterpret_cast<uint32_t*>(part_o);
+    ws->part_ex = reinterpret_cast<uint16_t*>(part_ex);
     ws->ctr = reinterpret_cast<int32_t*>(ctr);
     ws->max_tiles = max_tiles;
     ws->n_bins = nbgt;

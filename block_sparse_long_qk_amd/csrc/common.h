@@ -130,7 +130,8 @@ struct AttnWs {
   int32_t* tile_off;   // [bins+1] exclusive scan of ceil(cnt / pt); last = tile count
   int2* list;          // [max_tiles * pt] {row-slot id i * k + s (-1 = empty), bin of the tile}, tile-major
   float* part_lse;     // [B*h_kv*n_q*(k+1)][G]     base-2 log-sum-exp of each non-local partial (-inf: none)
-  uint16_t* part_o;    // [B*h_kv*n_q*(k+1)][16][G][8] normalised partials, bf16, chunk-major per block
+  uint32_t* part_o;    // [B*h_kv*n_q*(k+1)][12][G][4] normalised partials, 12-bit block-scaled codes, chunk-major
+  uint16_t* part_ex;   // [B*h_kv*n_q*(k+1)][G][2]     their exponents, one byte per 32-value group
   int32_t* ctr;        // [kWorkCounters] work counters of the forward attention kernels (zeroed by the plan)
   int64_t max_tiles;
   int64_t n_bins;      // B * h_kv * query groups * n_blk

@@ -17,8 +17,8 @@
 //   one tile ahead.  S^T = K Q^T and O^T = V^T P^T run on 32x32x16 bf16 MFMA.
 //   Non-local tiles need no mask (the block lies wholly before the query);
 //   local tiles (pt consecutive positions sharing their local block) apply
-//   the causal mask.  Each (row, slot) writes a normalised bf16 partial and
-//   its base-2 log-sum-exp.
+//   the causal mask.  Each (row, slot) writes a normalised partial (a 12-bit
+//   block-scaled code, see pack_group12) and its base-2 log-sum-exp.
 // Stage C, merge: LSE weighting of each row's partials into the bf16 output
 //   and the natural-log lse.
 //
@@ -172,39 +172,95 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* Vt, f32x16 (&s)[4], i
   l = sum;
 }
 
-// The wave's 32 normalised partials, bf16 in lane order: row q's 128 values
-// are lane q's 64 then lane q+32's 64, in accumulator order.
-__device__ __forceinline__ void pack_partial(const f32x16 (&o)[4], float inv, uint4 (&w)[8]) {
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int Dt = u >> 1, e0 = (u & 1) * 8;
-    w[u] = make_uint4(pack_bf16x2(o[Dt][e0 + 0] * inv, o[Dt][e0 + 1] * inv),
-                      pack_bf16x2(o[Dt][e0 + 2] * inv, o[Dt][e0 + 3] * inv),
-                      pack_bf16x2(o[Dt][e0 + 4] * inv, o[Dt][e0 + 5] * inv),
-                      pack_bf16x2(o[Dt][e0 + 6] * inv, o[Dt][e0 + 7] * inv));
-  }
+// Partials are stored in a 12-bit block-scaled fixed-point code.  The 32
+// values a lane holds of one half of the head dim form a group with one
+// power-of-two scale: E is the smallest integer with
+// max|value| * (1 + 2^-11) < 2^E, each value is stored as the nearest integer
+// of value * 2^(11-E), a 12-bit two's complement code that the margin keeps
+// within [-2047, 2047], and E as one signed byte.  A value is off by at most
+// half a step, 2^(E-12), which is under max|value| / 2047 of its group; bf16
+// would be off by up to |value| / 256.  Eight codes fill three dwords, low
+// bits first.
+//
+// One fma forms a code: x * sc + 1.5 * 2^23 lies in [2^23, 2^24), where the
+// float spacing is 1, so the sum is rounded to the nearest integer once and
+// the code sits in the low 12 mantissa bits.
+__device__ __forceinline__ uint32_t code12_bits(float x, float sc) {
+  return __float_as_uint(__builtin_fmaf(x, sc, 12582912.f));
 }
 
-// Store a wave's packed partials and their log-sum-exps.  The partials of one
-// (sequence, group, query, slot) form a block of G x 128 bf16 laid out
-// chunk-major: 16-byte chunk c of head h at (c * G + h) * 16 bytes, chunk
-// 8 * half + u holding w[u] of lane (column, half).  A wave's 32 rows are
-// whole query positions (all G heads) whenever G divides 32, so for each u
-// the lanes of one position write (or, in the merge, read) consecutive 16-byte
-// chunks straight from the MFMA layout, with no transposition.
-__device__ __forceinline__ void store_partials(uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-                                               const uint4 (&w)[8], float lse, bool valid, int64_t pblk, int hh,
-                                               int G, int half) {
+__device__ __forceinline__ void pack12x8(const uint32_t (&b)[8], uint32_t* d) {
+  constexpr uint32_t M = 0xFFFu;
+  d[0] = (b[0] & M) | ((b[1] & M) << 12) | (b[2] << 24);
+  d[1] = ((b[2] & M) >> 8) | ((b[3] & M) << 4) | ((b[4] & M) << 16) | (b[5] << 28);
+  d[2] = ((b[5] & M) >> 4) | ((b[6] & M) << 8) | (b[7] << 20);
+}
+
+__device__ __forceinline__ int sext12(uint32_t x, int lsb) { return (int32_t)(x << (20 - lsb)) >> 20; }
+
+__device__ __forceinline__ void unpack12x8(uint32_t d0, uint32_t d1, uint32_t d2, float (&x)[8]) {
+  x[0] = (float)sext12(d0, 0);
+  x[1] = (float)sext12(d0, 12);
+  x[2] = (float)sext12((d0 >> 24) | (d1 << 8), 0);
+  x[3] = (float)sext12(d1, 4);
+  x[4] = (float)sext12(d1, 16);
+  x[5] = (float)sext12((d1 >> 28) | (d2 << 4), 0);
+  x[6] = (float)sext12(d2, 8);
+  x[7] = (float)sext12(d2, 20);
+}
+
+// The code of one group: the 32 accumulators o[0..1][0..15] times inv (the
+// normalisation), as 12 dwords in accumulator order into w[0..2]; returns E.
+__device__ __forceinline__ int pack_group12(const f32x16 (&o)[2], float inv, uint4* w) {
+  float am = 0.f;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) am = fmaxf(am, fmaxf(fabsf(o[d][e]), fabsf(o[d][e + 1])));  // v_max3
+  }
+  // 0 for an all-zero group; kept within a signed byte, the lower bound only
+  // ever reached by values that code to 0
+  const int E = min(127, max(-100, __builtin_amdgcn_frexp_expf(am * (inv * 1.00048828125f))));
+  const float sc = __builtin_amdgcn_ldexpf(inv, 11 - E);  // exact: inv times a power of two
+  uint32_t dw[12];
+#pragma unroll
+  for (int uu = 0; uu < 4; ++uu) {
+    const int d = uu >> 1, e0 = (uu & 1) * 8;
+    uint32_t b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = code12_bits(o[d][e0 + j], sc);
+    pack12x8(b, dw + 3 * uu);
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) w[j] = make_uint4(dw[4 * j], dw[4 * j + 1], dw[4 * j + 2], dw[4 * j + 3]);
+  return E;
+}
+
+// Store a wave's packed partials, their scale exponents and log-sum-exps.
+// The partial of one (sequence, group, query, slot) is a block of G x 128
+// codes (192 bytes per head) laid out chunk-major: 16-byte chunk c (0..11) of
+// head h at (c * G + h) * 16 bytes, chunk 6 * half + u holding w[u] of lane
+// (column, half), groups (half of the head dim) h = u / 3.  The exponents of a
+// lane's two groups sit in one 16-bit word (group h in byte h) at
+// (slot * G + head) * 2 + half.  A wave's 32 rows are whole query positions
+// (all G heads) whenever G divides 32, so for each u the lanes of one
+// position write (or, in the merge, read) consecutive 16-byte chunks straight
+// from the MFMA layout, with no transposition.
+__device__ __forceinline__ void store_partials(uint32_t* __restrict__ part_o, uint16_t* __restrict__ part_ex,
+                                               float* __restrict__ part_lse, const uint4 (&w)[6], uint32_t ex,
+                                               float lse, bool valid, int64_t pblk, int hh, int G, int half) {
   if (valid) {
     if (half == 0) part_lse[pblk * G + hh] = lse;
-    uint64_t a = reinterpret_cast<uint64_t>(part_o + pblk * G * kHeadDim + (8 * half * G + hh) * 8);
-    // the eight addresses are formed here, one add each, rather than kept live
+    // read once, by the merge: streamed past the caches
+    __builtin_nontemporal_store((uint16_t)ex, part_ex + (pblk * G + hh) * 2 + half);
+    uint64_t a = reinterpret_cast<uint64_t>(part_o + (pblk * G * 12 + 6 * half * G + hh) * 4);
+    // the six addresses are formed here, one add each, rather than kept live
     // in registers since the partial was packed
     asm volatile("" : "+v"(a));
     const int64_t step = (int64_t)G * 16;  // bytes between consecutive chunks of one head
     typedef __attribute__((address_space(1))) u32x4* gvec;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)  // read once, by the merge: streamed past the caches
+    for (int u = 0; u < 6; ++u)
       __builtin_nontemporal_store(u32x4{w[u].x, w[u].y, w[u].z, w[u].w}, (gvec)(a + u * step));
   }
 }
@@ -343,11 +399,11 @@ __device__ __forceinline__ void qk_block_q(const unsigned char* Ks, const uint4 
 // softmax_pv<false> with the partial packed as it is produced: P is packed
 // to bf16 once, then O^T is formed one half of the head dim at a time (32
 // accumulator registers instead of 64) and each half is normalised into its
-// four packed chunks of w (the layout of pack_partial).  Every accumulator
-// sums the same MFMAs in the same order as softmax_pv, so m2, l and the
-// packed partial are bit-identical to softmax_pv followed by pack_partial.
+// group of three packed chunks of w (pack_group12), its exponent in byte h
+// of ex.  Every accumulator sums the same MFMAs in the same order as
+// softmax_pv.
 __device__ __forceinline__ void softmax_pv_packed(const uint16_t* Vt, f32x16 (&s)[4], int lane, float c,
-                                                  uint4 (&w)[8], float& m2, float& l) {
+                                                  uint4 (&w)[6], uint32_t& ex, float& m2, float& l) {
   const float NEG_INF = -__builtin_huge_valf();
   const int col = lane & 31, half = lane >> 5;
   float ext;
@@ -419,14 +475,8 @@ __device__ __forceinline__ void softmax_pv_packed(const uint16_t* Vt, f32x16 (&s
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-#pragma unroll
-    for (int uu = 0; uu < 4; ++uu) {
-      const int d = uu >> 1, e0 = (uu & 1) * 8;
-      w[4 * h + uu] = make_uint4(pack_bf16x2(o[d][e0 + 0] * inv, o[d][e0 + 1] * inv),
-                                 pack_bf16x2(o[d][e0 + 2] * inv, o[d][e0 + 3] * inv),
-                                 pack_bf16x2(o[d][e0 + 4] * inv, o[d][e0 + 5] * inv),
-                                 pack_bf16x2(o[d][e0 + 6] * inv, o[d][e0 + 7] * inv));
-    }
+    const int E = pack_group12(o, inv, w + 3 * h);
+    ex = h == 0 ? (uint32_t)(E & 0xFF) : ex | ((uint32_t)(E & 0xFF) << 8);
   }
 }
 
@@ -497,7 +547,8 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   TileRaw raw1 = t1 >= 0 ? tile_raw<false>(ws, D, t1, ps) : TileRaw{-1, 0};
   uint4 qa[8], qb[8];
   load_q(q_ptr(cur), half, qa);
-  uint4 pw[8];
+  uint4 pw[6];
+  uint32_t pex = 0;
   int64_t ppblk = 0;
   float plse = 0.f;
   bool pvalid = false, have = false;  // have: a packed partial waits in pw (uniform)
@@ -529,13 +580,13 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     TileRow nxt = cur;
     if (more) nxt = tile_row<false, VL>(raw1, D, ws, t1, ps);
     __builtin_amdgcn_sched_barrier(0);
-    if (have) store_partials(ws.part_o, ws.part_lse, pw, plse, pvalid, ppblk, hh, D.G, half);
+    if (have) store_partials(ws.part_o, ws.part_ex, ws.part_lse, pw, pex, plse, pvalid, ppblk, hh, D.G, half);
     if (more) load_q(q_ptr(nxt), half, qn);
     int t2 = after(t, t1);
     TileRaw raw2{-1, 0};
     if (t2 >= 0) raw2 = tile_raw<false>(ws, D, t2, ps);
     float m2, l;
-    softmax_pv_packed(Vt, s, lane, D.scale_log2, pw, m2, l);
+    softmax_pv_packed(Vt, s, lane, D.scale_log2, pw, pex, m2, l);
     ppblk = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1) + cur.s;
     plse = add_exact(m2, __log2f(l));
     pvalid = cur.valid;
@@ -561,7 +612,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   };
   while (step(qa, qb) && step(qb, qa)) {
   }
-  if (have) store_partials(ws.part_o, ws.part_lse, pw, plse, pvalid, ppblk, hh, D.G, half);
+  if (have) store_partials(ws.part_o, ws.part_ex, ws.part_lse, pw, pex, plse, pvalid, ppblk, hh, D.G, half);
 }
 
 // Local tiles fused with the merge (persistent, dynamic runs).  Per tile and
@@ -604,14 +655,15 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     uint4 qf[8];
     load_q(q + qoff, half, qf);
     // The row's non-local partials (chunk-major blocks, see store_partials):
-    // this lane's 64 values of each are chunks 8 * half .. 8 * half + 7 of its
-    // head, in accumulator order.  Their log-sum-exps are requested before the
+    // this lane's 64 values of each are chunks 6 * half .. 6 * half + 5 of its
+    // head, in accumulator order, with their two exponents in one word.  Their log-sum-exps are requested before the
     // local block is computed, so the max over all slots is known before the
     // fold, which therefore never rescales; partial loads run one slot ahead of
     // the fold.
     const int64_t prow = ((int64_t)cur.bg * D.n_q + cur.i) * (D.k + 1);
     const float* lse_p = ws.part_lse + prow * D.G + hh;                                   // slot s at s * G
-    const uint16_t* o_p = ws.part_o + prow * D.G * kHeadDim + (8 * half * D.G + hh) * 8;  // slot s at s * G * 128
+    const uint32_t* o_p = ws.part_o + (prow * D.G * 12 + 6 * half * D.G + hh) * 4;  // slot s at s * G * 48
+    const uint16_t* ex_p = ws.part_ex + (prow * D.G + hh) * 2 + half;              // slot s at s * G * 2
     float lv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -623,20 +675,22 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     uint32_t has = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) has |= (lv[j] != NEG_INF ? 1u : 0u) << j;
-    auto load_slot = [&](int s0, float& ls, uint4 (&x)[8]) {  // past slot k-1: weight 0
+    auto load_slot = [&](int s0, float& ls, uint4 (&x)[6], uint32_t& ex) {  // past slot k-1: weight 0
       const int sl = min(s0, D.k - 1);
       ls = s0 < D.k ? lse_p[(int64_t)sl * D.G] : NEG_INF;
       const bool used = s0 < 16 ? ((has >> s0) & 1u) != 0 : ls != NEG_INF;
-      const uint16_t* src = o_p + (int64_t)sl * D.G * kHeadDim;
+      const uint32_t* src = o_p + (int64_t)sl * D.G * 48;
       if (used) {
+        ex = __builtin_nontemporal_load(ex_p + (int64_t)sl * D.G * 2);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {  // read once: streamed past the caches
-          const u32x4 y = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + u * D.G * 8));
+        for (int u = 0; u < 6; ++u) {  // read once: streamed past the caches
+          const u32x4 y = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + u * D.G * 4));
           x[u] = make_uint4(y.x, y.y, y.z, y.w);
         }
       } else {
+        ex = 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = make_uint4(0u, 0u, 0u, 0u);
+        for (int u = 0; u < 6; ++u) x[u] = make_uint4(0u, 0u, 0u, 0u);
       }
     };
 
@@ -678,31 +732,37 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       l *= rs;
     }
     float L = l;
-    auto fold = [&](float ls, const uint4 (&x)[8]) {
-      const bool use = ls != NEG_INF;
-      const float wgt = use ? __builtin_amdgcn_exp2f(ls - M) : 0.f;
+    auto fold = [&](float ls, const uint4 (&x)[6], uint32_t ex) {  // a slot with no partial holds codes 0
+      const float wgt = ls != NEG_INF ? __builtin_amdgcn_exp2f(ls - M) : 0.f;
       L += wgt;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t xs[4] = {use ? x[u].x : 0u, use ? x[u].y : 0u, use ? x[u].z : 0u, use ? x[u].w : 0u};
+      for (int h = 0; h < 2; ++h) {
+        // group h's values are code * 2^(E - 11): the weight takes the scale
+        const int E = (int)(int8_t)(uint8_t)(ex >> (8 * h));
+        const float wq = __builtin_amdgcn_ldexpf(wgt, E - 11);
+        const uint32_t dw[12] = {x[3 * h].x,     x[3 * h].y,     x[3 * h].z,     x[3 * h].w,
+                                 x[3 * h + 1].x, x[3 * h + 1].y, x[3 * h + 1].z, x[3 * h + 1].w,
+                                 x[3 * h + 2].x, x[3 * h + 2].y, x[3 * h + 2].z, x[3 * h + 2].w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = (u & 1) * 8 + 2 * c;
-          o[u >> 1][e] += wgt * __uint_as_float(xs[c] << 16);
-          o[u >> 1][e + 1] += wgt * __uint_as_float(xs[c] & 0xFFFF0000u);
+        for (int uu = 0; uu < 4; ++uu) {
+          float c[8];
+          unpack12x8(dw[3 * uu], dw[3 * uu + 1], dw[3 * uu + 2], c);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[2 * h + (uu >> 1)][(uu & 1) * 8 + j] += wq * c[j];
         }
       }
     };
     {
       float la, lb;
-      uint4 xa[8], xb[8];
-      load_slot(0, la, xa);
+      uint32_t ea, eb;
+      uint4 xa[6], xb[6];
+      load_slot(0, la, xa, ea);
       for (int s0 = 0; s0 < D.k; s0 += 2) {
-        load_slot(s0 + 1, lb, xb);
-        fold(la, xa);
+        load_slot(s0 + 1, lb, xb, eb);
+        fold(la, xa, ea);
         if (s0 + 1 >= D.k) break;
-        load_slot(s0 + 2, la, xa);
-        fold(lb, xb);
+        load_slot(s0 + 2, la, xa, ea);
+        fold(lb, xb, eb);
       }
     }
     if (cur.valid) {

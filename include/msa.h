@@ -133,9 +133,10 @@ typedef enum {
  * calls that take none).  Host only; enqueues nothing.
  *
  * How the forward workspace grows (uniform batch, G = 8, k = 16, d = 128):
- * the attention's partial outputs take (k + 1) * G * d * 2 bytes plus a few
- * plan and lse bytes per (sequence, group, query row) of one pass, about
- * 278 KiB per query position at H_kv = 8, so at most ~36 GB for a pass of
+ * the attention's partial outputs take (k + 1) * G * (3 d / 2 + 8) bytes (a
+ * 12-bit code per value, a scale exponent byte per 32 values and an fp32 lse
+ * per head) plus a few plan bytes per (sequence, group, query row) of one
+ * pass, about 214 KiB per query position at H_kv = 8, so at most ~29 GB for a pass of
  * MSA_DEFAULT_CHUNK_ROWS rows whatever n_q is (a 1M-token prefill fits one
  * MI355X); the fp32 pooled scores [B][H_kv][rows][n_blk] are added only when
  * scoring and top-k cannot run as one launch (few rows against a long cache,
