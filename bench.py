@@ -39,12 +39,12 @@ MAX_MARKS = 192                # events per marked step (overlapped passes mark 
 COUNTER_TRAFFIC = {
     # kernel name: (bytes per step, summed over the step's launches, {source file: sha16});
     # profiles/prefill_128k_decode_256k_counters.md
-    "k_index_scores(top-k fused)": (3071411328, {"index_scores.hip": "d6c53c22822df47d", "common.h": "4c23e147ab3f19f0"}),
-    "k_attn_tiles": (67247282280, {"sparse_attn.hip": "9610578eace916e5", "fwd_tiles.h": "1f0a406284261b7e", "attn_tiles.h": "2f9107ca13d54488", "common.h": "4c23e147ab3f19f0"}),
-    "k_attn_local_merge": (37591660720, {"sparse_attn.hip": "9610578eace916e5", "fwd_tiles.h": "1f0a406284261b7e", "attn_tiles.h": "2f9107ca13d54488", "common.h": "4c23e147ab3f19f0"}),
-    "k_block_topk": (2286073835, {"block_topk.hip": "52d43fa6ee7deeff", "common.h": "4c23e147ab3f19f0"}),
-    "k_index_small": (4353003528, {"decode.hip": "6cb61b92818c32a7", "common.h": "4c23e147ab3f19f0"}),
-    "k_attn_rows": (575064556, {"decode.hip": "6cb61b92818c32a7", "common.h": "4c23e147ab3f19f0"}),
+    "k_index_scores(top-k fused)": (3135016960, {"index_scores.hip": "d6c53c22822df47d", "common.h": "ecb32c13321b9a30"}),
+    "k_attn_tiles": (59811840000, {"sparse_attn.hip": "531179aaf5e19eff", "fwd_tiles.h": "1f0a406284261b7e", "attn_tiles.h": "2f9107ca13d54488", "common.h": "ecb32c13321b9a30"}),
+    "k_attn_local_merge": (31339520000, {"sparse_attn.hip": "531179aaf5e19eff", "fwd_tiles.h": "1f0a406284261b7e", "attn_tiles.h": "2f9107ca13d54488", "common.h": "ecb32c13321b9a30"}),
+    "k_block_topk": (2285998080, {"block_topk.hip": "52d43fa6ee7deeff", "common.h": "ecb32c13321b9a30"}),
+    "k_index_small": (4354646016, {"decode.hip": "6cb61b92818c32a7", "common.h": "ecb32c13321b9a30"}),
+    "k_attn_rows": (575160320, {"decode.hip": "6cb61b92818c32a7", "common.h": "ecb32c13321b9a30"}),
 }
 COUNTER_WORKLOAD = {"k_index_small": "decode_256k", "k_attn_rows": "decode_256k"}  # the others: prefill_128k
 
