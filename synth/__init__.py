@@ -157,6 +157,7 @@ class Workload:
     plant_beta: float = 0.0     # amplitude added to that group's index queries
     index_dtype: str = "bf16"   # "fp8": index_q / index_k are the bf16 values rounded to OCP E4M3
     kv_dtype: str = "bf16"      # "fp8": k / v are the bf16 values rounded to OCP E4M3
+    v_outlier_shift: int = 0    # > 0: V channels V_OUTLIER_DIMS scaled by 2**shift (exact in bf16)
 
     @property
     def offset(self) -> int:
@@ -253,11 +254,29 @@ def host_q(w: Workload, b: int, i0: int, i1: int) -> np.ndarray:
     return gen_range(w.seed, T_Q, (b * w.n_q + i0) * row, (i1 - i0) * row).reshape(i1 - i0, w.h_q, w.head_dim)
 
 
+# Outlier channels of V (workloads with v_outlier_shift > 0): a few value
+# channels much larger than the rest, as activation outliers make them.  Their
+# bf16 values are multiplied by a power of two by adding to the exponent field,
+# which is exact; zeros stay zero.
+V_OUTLIER_DIMS = (0, 100)
+
+
+def _outlier_bits(x: np.ndarray, shift: int) -> np.ndarray:
+    x = x.copy()
+    cols = x[..., list(V_OUTLIER_DIMS)]
+    nz = (cols & 0x7F80) != 0
+    x[..., list(V_OUTLIER_DIMS)] = np.where(nz, cols + np.uint16(shift << 7), cols)
+    return x
+
+
 def host_kv(w: Workload, which: str, b: int, g: int, j0: int, j1: int) -> np.ndarray:
     """K or V[b, g, j0:j1] as bf16 bits, shape [j1-j0, d]."""
     tid = T_K if which == "k" else T_V
     base = ((b * w.h_kv + g) * w.n_kv + j0) * w.head_dim
-    return gen_range(w.seed, tid, base, (j1 - j0) * w.head_dim).reshape(j1 - j0, w.head_dim)
+    x = gen_range(w.seed, tid, base, (j1 - j0) * w.head_dim).reshape(j1 - j0, w.head_dim)
+    if which == "v" and w.v_outlier_shift > 0:
+        x = _outlier_bits(x, w.v_outlier_shift)
+    return x
 
 
 def host_kv_blocks(w: Workload, which: str, b: int, g: int, blocks) -> dict:
@@ -447,6 +466,11 @@ def device_inputs(w: Workload, device="cuda:0") -> dict:
     for name, shp in w.shapes().items():
         t = torch.empty(shp, dtype=torch.bfloat16, device=device)
         device_fill(w, name, t, nt_dev=nt)
+        if name == "v" and w.v_outlier_shift > 0:
+            bits = t.view(torch.int16)
+            for c in V_OUTLIER_DIMS:
+                col = bits[..., c]
+                col.copy_(torch.where((col & 0x7F80) != 0, col + (w.v_outlier_shift << 7), col))
         if (w.index_dtype == "fp8" and name in ("iq", "ik")) or (w.kv_dtype == "fp8" and name in ("k", "v")):
             t = t.to(torch.float8_e4m3fn).view(torch.uint8)
         out[name] = t

@@ -62,6 +62,46 @@ def test_edge_cases(w):
     _release()
 
 
+class BeyondOutputRounding(Stats):
+    """Stats whose max |d| counts only what exceeds the bf16 output's own
+    rounding of the exact value (half an ulp, at most 2^-8 |ref|): on channels
+    far larger than 1 every bf16 result rounds by more than the absolute
+    tolerance.  The mean stays the plain mean |d|."""
+
+    def __init__(self):
+        super().__init__()
+        self.raw_max = 0.0
+
+    def add_out(self, got, ref):
+        g, r = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+        d = np.abs(g - r)
+        if d.size:
+            self.raw_max = max(self.raw_max, float(d.max()))
+            self.max_abs = max(self.max_abs, float(np.maximum(d - np.abs(r) * 2.0 ** -8, 0.0).max()))
+        self.sum_abs += float(d.sum())
+        self.n += d.size
+
+
+def test_v_outlier_channels():
+    """Two value channels 8x larger than the rest (activation outliers).  The
+    non-local partials are stored as 12-bit codes with one power-of-two scale
+    per 32 values, so the groups holding an outlier channel take an exponent
+    three larger and their other values a coarser step.  On every row the
+    output must match the oracle within the tolerance beyond the bf16
+    output's own rounding (outputs on the outlier channels reach tens, where
+    that rounding alone exceeds the absolute bound)."""
+    w = synth.Workload("v_outlier", 1, 4096, 4096, 16, 2, topk=8, seed=4242, v_outlier_shift=3)
+    res = run_gpu(w)
+    check_forward_matches_stages(res)
+    st = BeyondOutputRounding()
+    for g in range(w.h_kv):
+        check_rows(w, res, 0, g, np.arange(w.n_q), st)
+    say(f"    raw max|d|={st.raw_max:.3e} (bf16 output rounding included)")
+    st.check()
+    del res
+    _release()
+
+
 def test_prefill_4k_all_rows():
     w = synth.WORKLOADS["prefill_4k"]
     res = run_gpu(w)

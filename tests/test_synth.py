@@ -103,3 +103,19 @@ def test_device_fill_samples_at_large_offsets():
                           np.arange(flat.numel() - 16, flat.numel())])
     got = flat[torch.from_numpy(idx).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, synth.gen_at(w.seed, synth.T_K, idx))
+
+
+def test_v_outlier_channels_are_exact_power_of_two_multiples():
+    """v_outlier_shift multiplies V's outlier channels by 2**shift exactly
+    (exponent field), leaves zeros and every other channel and tensor alone."""
+    w = synth.Workload("v_outlier", 1, 512, 512, 4, 2, seed=77, v_outlier_shift=3)
+    base = w.replace(v_outlier_shift=0)
+    a, b = synth.host_kv(w, "v", 0, 1, 0, 512), synth.host_kv(base, "v", 0, 1, 0, 512)
+    f = lambda x: (x.astype(np.uint32) << 16).view(np.float32)
+    others = [c for c in range(w.head_dim) if c not in synth.V_OUTLIER_DIMS]
+    assert np.array_equal(a[:, others], b[:, others])
+    for c in synth.V_OUTLIER_DIMS:
+        assert np.array_equal(f(a[:, c]), f(b[:, c]) * 8.0)
+    assert np.array_equal(synth.host_kv(w, "k", 0, 1, 0, 512), synth.host_kv(base, "k", 0, 1, 0, 512))
+    z = np.zeros((2, w.head_dim), np.uint16)
+    assert np.array_equal(synth._outlier_bits(z, 3), z)
