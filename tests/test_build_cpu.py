@@ -15,12 +15,11 @@ def report():
 
 
 def test_no_scratch_spills(report):
-    """No scratch in the uniform-batch kernels; the variable-length / paged
-    instantiations (template flag VL = true, "Lb1E" in the mangled name) may
-    spill a few loop-invariant registers."""
+    """No kernel uses scratch memory: neither the uniform-batch kernels nor
+    the variable-length / paged instantiations spill a register to it."""
     def scratch(v):
         return max(v.get("ScratchSize [bytes/lane]", 0), 4 * v.get("VGPRs Spill", 0))
-    bad = {k: v for k, v in report.items() if scratch(v) and not ("Lb1E" in k and scratch(v) <= 32)}
+    bad = {k: v for k, v in report.items() if scratch(v)}
     assert not bad, bad
 
 
